@@ -1,0 +1,101 @@
+"""Single-query decode attention over a paged KV cache, in float64.
+
+What is computed, and where the pages state it:
+  * [P5] section 4 (block table and locate()): a sequence's tokens live in
+    fixed blocks of `block_size` tokens; its block table lists the physical
+    block of each logical block, so logical position `pos` is found in block
+    table[pos // block_size] at offset pos % block_size.
+  * [P1] section 4.3: the attention kernel fetches K and V through the block
+    table from non-contiguous places; paging changes where bytes live, not
+    what is computed.
+  * [P1] section 2.1: attention is softmax(Q K^T / sqrt(d_head)) V; here the
+    scale is an argument (1/sqrt(head_dim) in every workload).
+  * [P1] section 2.2: at a decode step the single new query attends to the
+    keys of every cached position, the new token's own included.
+  * [P5] section 2 and [P3] section 3.3: with grouped-query attention every g
+    consecutive query heads share one K/V head (g = Hq / Hkv; MQA is Hkv = 1).
+  * [P5] section 7: quantised K/V carry one scale per head; here one fp32
+    scale per (physical block, KV head), and the value used is code * scale.
+
+Test infrastructure only (see the package docstring).
+"""
+
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+
+from .values import stored_to_f64
+
+
+def locate(table_row, pos, block_size: int = 16):
+    """Physical block and in-block offset of logical position(s) `pos`."""
+    table_row = np.asarray(table_row)
+    pos = np.asarray(pos)
+    return table_row[pos // block_size], pos % block_size
+
+
+def gather_sequence(cache, table_row, length: int, kv_tag: str, kv_heads=None,
+                    scales=None, block_size: int = 16) -> np.ndarray:
+    """Contiguous float64 [length, len(kv_heads), D] copy of one sequence.
+
+    `cache` is the raw storage array [num_blocks, Hkv, block_size, D] (uint16
+    bits for bf16, uint8 codes for fp8); `scales` ([num_blocks, Hkv] fp32) is
+    required for fp8 and multiplies every element of its (block, head) tile.
+    Only positions < length are touched.
+    """
+    nb = cache.shape[0]
+    if kv_heads is None:
+        kv_heads = np.arange(cache.shape[1])
+    kv_heads = np.asarray(kv_heads)
+    pos = np.arange(int(length))
+    blk, off = locate(table_row, pos, block_size)
+    if length and (blk.min() < 0 or blk.max() >= nb):
+        raise IndexError("block table entry outside the pool for a position < length")
+    raw = cache[blk[:, None], kv_heads[None, :], off[:, None], :]      # [L, h, D]
+    vals = stored_to_f64(raw, kv_tag)
+    if kv_tag == "fp8_e4m3":
+        if scales is None:
+            raise ValueError("fp8 caches need their per-(block, head) scales")
+        s = np.asarray(scales, dtype=np.float32).astype(np.float64)
+        vals = vals * s[blk[:, None], kv_heads[None, :]][:, :, None]
+    elif scales is not None:
+        raise ValueError("scales apply to fp8 caches only")
+    return vals
+
+
+def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                           *, q_tag: str, kv_tag: str, k_scales=None, v_scales=None,
+                           seqs: Optional[Sequence[int]] = None,
+                           q_heads: Optional[Sequence[int]] = None,
+                           block_size: int = 16) -> np.ndarray:
+    """out[b, i, :] for b in `seqs`, i in `q_heads` (all by default), float64.
+
+    q: [B, Hq, D] storage array; caches: [num_blocks, Hkv, block_size, D];
+    block_tables: int [B, max_blocks]; context_lens: int [B].
+    """
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    if Hq % Hkv:
+        raise ValueError("query heads must be a multiple of KV heads")
+    g = Hq // Hkv
+    seqs = list(range(B)) if seqs is None else list(seqs)
+    q_heads = list(range(Hq)) if q_heads is None else list(q_heads)
+    kv_for = [i // g for i in q_heads]
+    kv_needed = sorted(set(kv_for))
+    col = {h: c for c, h in enumerate(kv_needed)}
+    out = np.zeros((len(seqs), len(q_heads), D), dtype=np.float64)
+    qv = stored_to_f64(np.asarray(q)[seqs][:, q_heads], q_tag)       # [nb, nh, D]
+    for r, b in enumerate(seqs):
+        L = int(context_lens[b])
+        if L == 0:
+            continue
+        K = gather_sequence(k_cache, block_tables[b], L, kv_tag, kv_needed, k_scales, block_size)
+        V = gather_sequence(v_cache, block_tables[b], L, kv_tag, kv_needed, v_scales, block_size)
+        for c, i in enumerate(q_heads):
+            h = col[kv_for[c]]
+            s = scale * (K[:, h, :] @ qv[r, c])          # [L] scores
+            w = np.exp(s - s.max())                       # softmax numerator
+            out[r, c] = (w @ V[:, h, :]) / w.sum()
+    return out

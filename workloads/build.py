@@ -1,0 +1,234 @@
+"""Build block tables and seeded K/V/q tensors for a decode workload.
+
+Recipe (all seeded from the workload's seed):
+  * lengths: explicit, or uniform integers in the stated range (for a shared
+    prefix the range is that of the private suffix, added to the prefix);
+  * physical pool: `num_blocks` (or exactly what the batch needs); the free
+    list is a seeded random permutation of the block ids, so consecutive
+    logical blocks of a sequence land on scattered physical blocks;
+  * tables: sequence 0 takes its prefix blocks, the other sequences fork them
+    (reference count = number of sequences), then every sequence takes fresh
+    blocks for its private history, then the decode step reserves the slot of
+    each sequence's new token (a new block when the last one is full);
+  * values: q, K, V ~ N(0, 1) drawn in fp32 and rounded to the storage dtype;
+    every cache slot that holds no history token (block tails, unused blocks,
+    the slot the new token will be written to) is poisoned with NaN (float
+    caches) or the e4m3 NaN code 0x7F (fp8 caches), so a read of it shows up;
+  * fp8 caches: per (block, kv_head) tile, scale = amax|x| / 448 in fp32 (1.0
+    for an all-zero tile), code = round-to-nearest-even(x / scale) clamped to
+    +-448, done by torch's float8_e4m3fn cast.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from .pool import BlockPool
+from .specs import DecodeWorkload
+
+POISON_FP8_CODE = 0x7F
+FP8_MAX = 448.0
+
+_TORCH_DTYPE = {
+    "f32": torch.float32,
+    "f16": torch.float16,
+    "bf16": torch.bfloat16,
+    "fp8_e4m3": torch.uint8,
+}
+
+
+def torch_dtype(tag: str) -> torch.dtype:
+    return _TORCH_DTYPE[tag]
+
+
+@dataclass
+class DecodeLayout:
+    spec: DecodeWorkload
+    context_lens: np.ndarray        # int32 [B], post-append
+    block_tables: np.ndarray        # int32 [B, max_blocks], -1 padded
+    num_blocks: int
+    slot_mapping: Optional[np.ndarray]  # int64 [B] slot of the new token, or None
+    history_mask: np.ndarray        # bool [num_blocks, block_size]: slot holds a history token
+    refcount: np.ndarray            # int32 [num_blocks]
+    seq_slots: list                 # per sequence: int64 [L] flat slot of every position,
+                                    # in the order the pool handed them out
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_tables.shape[1])
+
+
+def _lengths(spec: DecodeWorkload, rng: np.random.Generator) -> np.ndarray:
+    if spec.context_lens is not None:
+        lens = np.asarray(spec.context_lens, dtype=np.int64)
+        if lens.shape[0] != spec.num_seqs:
+            raise ValueError("context_lens does not match num_seqs")
+    else:
+        lo, hi = spec.len_range
+        lens = rng.integers(lo, hi + 1, size=spec.num_seqs, dtype=np.int64)
+        lens = lens + spec.shared_prefix_tokens
+    return lens
+
+
+def _blocks_needed(spec: DecodeWorkload, lens: np.ndarray) -> int:
+    bs = spec.block_size
+    p = spec.shared_prefix_tokens
+    if p:
+        return p // bs + int(sum(-(-(int(L) - p) // bs) for L in lens))
+    return int(sum(-(-int(L) // bs) for L in lens))
+
+
+def build_layout(spec: DecodeWorkload) -> DecodeLayout:
+    bs = spec.block_size
+    rng = np.random.default_rng(spec.seed)
+    lens = _lengths(spec, rng)
+    if spec.shared_prefix_tokens % bs:
+        raise ValueError("a shared prefix must be whole blocks")
+    if spec.shared_prefix_tokens and int(lens.min()) <= spec.shared_prefix_tokens:
+        raise ValueError("every sequence must extend past the shared prefix")
+    need = _blocks_needed(spec, lens)
+    nb = spec.num_blocks if spec.num_blocks is not None else need
+    if nb < need:
+        raise ValueError(f"pool of {nb} blocks is smaller than the {need} needed")
+    pool = BlockPool(nb, rng.permutation(nb), block_size=bs)
+
+    hist = lens - 1 if spec.append else lens.copy()
+    history_mask = np.zeros((nb, bs), dtype=bool)
+
+    seq_slots = {b: [] for b in range(spec.num_seqs)}
+
+    def take(seq: int, count: int) -> None:
+        for _ in range(count):
+            slot = pool.append_token(seq)
+            seq_slots[seq].append(slot)
+            history_mask[slot // bs, slot % bs] = True
+
+    p = spec.shared_prefix_tokens
+    B = spec.num_seqs
+    pool.new_sequence(0)
+    if p:
+        take(0, p)
+        for b in range(1, B):
+            pool.fork(0, b, p)
+            seq_slots[b] = list(seq_slots[0][:p])
+    else:
+        for b in range(1, B):
+            pool.new_sequence(b)
+    for b in range(B):
+        take(b, int(hist[b]) - pool.num_tokens[b])
+
+    slot_mapping = None
+    if spec.append:
+        slot_mapping = np.array([pool.append_token(b) for b in range(B)], dtype=np.int64)
+        for b in range(B):
+            seq_slots[b].append(int(slot_mapping[b]))
+
+    max_blocks = max(len(pool.tables[b]) for b in range(B))
+    tables = np.full((B, max_blocks), -1, dtype=np.int32)
+    for b in range(B):
+        t = pool.tables[b]
+        tables[b, : len(t)] = t
+    return DecodeLayout(
+        spec=spec,
+        context_lens=lens.astype(np.int32),
+        block_tables=tables,
+        num_blocks=nb,
+        slot_mapping=slot_mapping,
+        history_mask=history_mask,
+        refcount=np.asarray(pool.refcount, dtype=np.int32),
+        seq_slots=[np.asarray(seq_slots[b], dtype=np.int64) for b in range(B)],
+    )
+
+
+# ---------------------------------------------------------------------------
+# tensors
+# ---------------------------------------------------------------------------
+
+def fp8_quantize_blocks(x: torch.Tensor, valid: Optional[torch.Tensor] = None):
+    """x: fp32 [NB, H, bs, D] -> (codes uint8 same shape, scales fp32 [NB, H]).
+
+    The scale of each (block, head) tile is its amax over valid slots / 448.
+    """
+    if valid is not None:
+        xm = x.masked_fill(~valid.view(valid.shape[0], 1, valid.shape[1], 1), 0.0)
+    else:
+        xm = x
+    amax = xm.abs().amax(dim=(2, 3))
+    scales = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax)).to(torch.float32)
+    y = (x / scales[:, :, None, None]).clamp_(-FP8_MAX, FP8_MAX)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, scales
+
+
+def _gen(device: str, seed: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def _normal(shape, gen, device, dtype_tag):
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    if dtype_tag == "fp8_e4m3":
+        return x
+    return x.to(torch_dtype(dtype_tag))
+
+
+def _make_inputs(layout: DecodeLayout, device: str, layers: Optional[int]) -> Dict[str, torch.Tensor]:
+    spec = layout.spec
+    nl = spec.num_layers if layers is None else layers
+    B, Hq, Hkv, D, bs = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.block_size
+    NB = layout.num_blocks
+    gen = _gen(device, spec.seed)
+    valid = torch.from_numpy(layout.history_mask).to(device)
+    poison = ~valid.view(NB, 1, bs, 1)
+    kv_tag = spec.kv_dtype
+    cache_dtype = torch_dtype(kv_tag)
+    out: Dict[str, torch.Tensor] = {}
+    out["q"] = _normal((nl, B, Hq, D), gen, device, spec.q_dtype)
+    k_cache = torch.empty((nl, NB, Hkv, bs, D), dtype=cache_dtype, device=device)
+    v_cache = torch.empty_like(k_cache)
+    scales = {}
+    for name, cache in (("k", k_cache), ("v", v_cache)):
+        if kv_tag == "fp8_e4m3":
+            sc = torch.empty((nl, NB, Hkv), dtype=torch.float32, device=device)
+            for layer in range(nl):
+                x = torch.randn((NB, Hkv, bs, D), generator=gen, device=device, dtype=torch.float32)
+                codes, s = fp8_quantize_blocks(x, valid)
+                del x
+                codes.masked_fill_(poison, POISON_FP8_CODE)
+                cache[layer].copy_(codes)
+                sc[layer].copy_(s)
+                del codes
+            scales[name] = sc
+        else:
+            for layer in range(nl):
+                x = torch.randn((NB, Hkv, bs, D), generator=gen, device=device, dtype=torch.float32)
+                cache[layer].copy_(x)        # rounds to the storage dtype (RNE)
+                del x
+                cache[layer].masked_fill_(poison, float("nan"))
+    out["k_cache"], out["v_cache"] = k_cache, v_cache
+    if kv_tag == "fp8_e4m3":
+        out["k_scales"], out["v_scales"] = scales["k"], scales["v"]
+    if spec.append:
+        if kv_tag == "fp8_e4m3":
+            raise NotImplementedError("this recipe appends only into 16/32-bit caches")
+        out["k_new"] = _normal((nl, B, Hkv, D), gen, device, kv_tag)
+        out["v_new"] = _normal((nl, B, Hkv, D), gen, device, kv_tag)
+        out["slot_mapping"] = torch.from_numpy(layout.slot_mapping).to(device)
+    out["block_tables"] = torch.from_numpy(layout.block_tables).to(device)
+    out["context_lens"] = torch.from_numpy(layout.context_lens).to(device)
+    return out
+
+
+def make_host_inputs(layout: DecodeLayout, layers: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """All tensors on the CPU (small workloads; the oracle reads these)."""
+    return _make_inputs(layout, "cpu", layers)
+
+
+def make_device_inputs(layout: DecodeLayout, device: str = "cuda", layers: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """All tensors drawn directly on `device` (full-size workloads)."""
+    return _make_inputs(layout, device, layers)
