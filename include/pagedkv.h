@@ -1,0 +1,154 @@
+/*
+ * pagedkv — single-query decode attention over a paged KV cache (gfx950).
+ *
+ * The operations follow the source pages:
+ *   - "KV Cache from first principles" (ldpk.cn/news/58971), 2.1: attention
+ *     is softmax(q K^T * scale) V; 2.2: at a decode step the one new query
+ *     attends to every cached position; 2.3: each step writes the new token's
+ *     K and V at the current length, which then grows by one; 4.3: the kernel
+ *     reads K and V through the block table from scattered places.
+ *   - "The KV Cache memory ledger: PagedAttention and continuous batching"
+ *     (gcssc.sfwss.com/posts/kv-cache-budget.html), 4: fixed 16-token blocks,
+ *     a per-sequence block table, locate(seq, pos) = table[pos / 16] * 16 +
+ *     pos % 16; prefix sharing points several tables at the same blocks;
+ *     2: grouped-query attention (g query heads share one K/V head);
+ *     7: 8-bit K/V with one scale per head.
+ *
+ * Memory layout (all row-major, contiguous, device memory):
+ *   k_cache, v_cache  [num_blocks][num_kv_heads][block_size=16][head_dim]
+ *                     one (block, kv_head) tile is a contiguous 16*head_dim run
+ *   block_tables      int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                     ceil(context_len / 16) are never read
+ *   context_lens      int32 [num_seqs]: tokens to attend, the new one included
+ *   q, out            [num_seqs][num_q_heads][head_dim]
+ *   k_scales,v_scales fp32 [num_blocks][num_kv_heads] (fp8 caches only)
+ *   slot_mapping      int64 [num_tokens]: flat slot = block * 16 + offset,
+ *                     -1 = skip this token
+ *   query head i reads KV head i / (num_q_heads / num_kv_heads).
+ *
+ * Ownership: the caller owns every buffer.  The library allocates nothing,
+ * keeps no mutable global state, and every call is asynchronous on `stream`
+ * (NULL = the default stream) with no host/device synchronisation inside.
+ *
+ * Errors: every call returns a pkv_status.  Arguments are checked on the host
+ * before anything is launched, so a non-zero status means nothing ran.
+ * Device-side faults surface at the caller's next synchronisation.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(PKV_BUILDING_LIBRARY)
+#define PKV_API __attribute__((visibility("default")))
+#else
+#define PKV_API
+#endif
+
+#define PKV_VERSION 100  /* 1.0.0 */
+#define PKV_BLOCK_SIZE 16
+
+typedef enum {
+  PKV_F32 = 0,
+  PKV_F16 = 1,
+  PKV_BF16 = 2,
+  PKV_FP8_E4M3 = 3 /* OCP e4m3fn: bias 7, max 448, no inf, NaN = S.1111.111 */
+} pkv_dtype;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = -1,      /* a required pointer is NULL */
+  PKV_ERR_SHAPE = -2,     /* non-positive size, Hq % Hkv != 0, g not in {1,2,4,8},
+                             head_dim not in {64,128}, block_size != 16 */
+  PKV_ERR_DTYPE = -3,     /* unsupported dtype or dtype combination */
+  PKV_ERR_WORKSPACE = -4, /* workspace missing or smaller than required */
+  PKV_ERR_LAUNCH = -5     /* the HIP runtime refused a launch */
+} pkv_status;
+
+typedef struct {
+  int32_t num_seqs;            /* B */
+  int32_t num_q_heads;         /* Hq */
+  int32_t num_kv_heads;        /* Hkv; Hq / Hkv in {1, 2, 4, 8} */
+  int32_t head_dim;            /* D in {64, 128} */
+  int32_t block_size;          /* must be 16 */
+  int32_t num_blocks;          /* physical blocks in the pool (per cache) */
+  int32_t max_blocks_per_seq;  /* row length of block_tables */
+  int32_t q_dtype;             /* pkv_dtype */
+  int32_t kv_dtype;            /* pkv_dtype */
+  int32_t out_dtype;           /* pkv_dtype */
+  int32_t partition_blocks;    /* blocks per context partition; 0 = automatic */
+} pkv_decode_dims;
+
+/*
+ * Per-step append ("KV Cache from first principles" 2.3; "The KV Cache memory
+ * ledger" 4, locate()).  For every t < num_tokens with slot_mapping[t] >= 0,
+ * copies k_new[t][h][:] to k_cache[slot / 16][h][slot % 16][:] and v_new to
+ * v_cache likewise, for every KV head h.  A bit-exact copy: no arithmetic.
+ *   k_new, v_new: [num_tokens][num_kv_heads][head_dim] of `dtype`.
+ *   Slots must be distinct (duplicates race).  Slots >= num_blocks * 16 are
+ *   skipped like -1.  dtype: F32, F16 or BF16.  head_dim: any multiple of
+ *   16 / sizeof(element) up to 1024 (the attention calls need 64 or 128).
+ *   Does not touch context lengths: the caller advances them.
+ */
+PKV_API int pkv_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                  void* k_cache, void* v_cache, int32_t num_tokens, int32_t num_kv_heads,
+                  int32_t head_dim, int32_t num_blocks, int32_t block_size, int32_t dtype,
+                  hipStream_t stream);
+
+/*
+ * Bytes of workspace pkv_paged_decode_attn(_fp8) needs for `dims`; 0 when the
+ * context is not split.  Depends only on `dims` (never on the device or on
+ * context_lens), so a caller can size it once.  Returns 0 for invalid dims.
+ */
+PKV_API size_t pkv_decode_workspace_bytes(const pkv_decode_dims* dims);
+
+/* Number of context partitions the attention call will use for `dims` (>= 1),
+ * or a negative pkv_status for invalid dims. */
+PKV_API int pkv_decode_num_partitions(const pkv_decode_dims* dims);
+
+/*
+ * Decode attention ("KV Cache from first principles" 2.1-2.2, 4.3; "The KV
+ * Cache memory ledger" 2, 4).  For each sequence b and query head i, with
+ * L = context_lens[b] and h = i / g:
+ *   out[b][i][:] = sum_t softmax_t(scale * <q[b][i], K_t>) V_t,  t < L,
+ * where K_t, V_t are read at locate(b, t).  L = 0 gives a zero row.  Block
+ * ids outside [0, num_blocks) and positions past max_blocks_per_seq * 16 are
+ * ignored (the caller must not pass them).
+ * Non-fp8 dtypes: q, caches and out all F32, or all F16, or all BF16.
+ * Arithmetic is fp32; the output is rounded once (nearest-even).
+ * workspace: device buffer of at least pkv_decode_workspace_bytes(dims)
+ * bytes (may be NULL when that is 0), used only during this call.
+ */
+PKV_API int pkv_paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens, float scale,
+                          void* out, const pkv_decode_dims* dims, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * FP8 variant ("The KV Cache memory ledger" 7: 8-bit K/V, one scale per head).
+ * kv_dtype must be FP8_E4M3; q and out are F16, BF16 or F32.  The value of a
+ * cached element is decode(code) * scale[block][kv_head].
+ */
+PKV_API int pkv_paged_decode_attn_fp8(const void* q, const void* k_cache, const void* v_cache,
+                              const float* k_scales, const float* v_scales,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              float scale, void* out, const pkv_decode_dims* dims,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static text for a status code. */
+PKV_API const char* pkv_status_string(int status);
+
+/* PKV_VERSION of the built library. */
+PKV_API int pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

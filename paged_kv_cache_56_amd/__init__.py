@@ -1,0 +1,227 @@
+"""pagedkv: paged-KV decode attention for MI355X (gfx950), Python binding.
+
+A thin ctypes layer over libpagedkv.so (include/pagedkv.h): it checks
+tensor shapes and dtypes, passes raw device pointers and the current HIP
+stream, and raises PagedKVError on a non-zero status.  All compute runs in
+the library's HIP kernels; there is no fallback path.  torch tensors only
+carry device memory and streams.
+
+    kv_append(k_new, v_new, slot_mapping, k_cache, v_cache)
+    paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                      k_scales=None, v_scales=None, workspace=None, partition_blocks=0)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "PagedKVError",
+    "library_path",
+    "load_library",
+    "kv_append",
+    "paged_decode_attn",
+    "decode_dims",
+    "decode_workspace_bytes",
+    "decode_num_partitions",
+    "DTYPE_CODES",
+    "BLOCK_SIZE",
+]
+
+BLOCK_SIZE = 16
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "lib", "libpagedkv.so")
+
+DTYPE_CODES = {
+    torch.float32: 0,
+    torch.float16: 1,
+    torch.bfloat16: 2,
+    torch.uint8: 3,               # fp8 e4m3fn codes, stored as raw bytes
+    torch.float8_e4m3fn: 3,
+}
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"pagedkv status {status}: {msg}")
+        self.status = status
+
+
+class DecodeDims(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("partition_blocks", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libpagedkv.so (built in-tree by paged_kv_cache_56_amd._build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with `python -m paged_kv_cache_56_amd._build` "
+            "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    dims_p = ctypes.POINTER(DecodeDims)
+    lib.pkv_kv_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.pkv_kv_append.restype = ctypes.c_int
+    lib.pkv_decode_workspace_bytes.argtypes = [dims_p]
+    lib.pkv_decode_workspace_bytes.restype = sz
+    lib.pkv_decode_num_partitions.argtypes = [dims_p]
+    lib.pkv_decode_num_partitions.restype = ctypes.c_int
+    lib.pkv_paged_decode_attn.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp, sz, vp]
+    lib.pkv_paged_decode_attn.restype = ctypes.c_int
+    lib.pkv_paged_decode_attn_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
+                                              dims_p, vp, sz, vp]
+    lib.pkv_paged_decode_attn_fp8.restype = ctypes.c_int
+    lib.pkv_status_string.argtypes = [ctypes.c_int]
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_version.argtypes = []
+    lib.pkv_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = load_library().pkv_status_string(status).decode()
+        raise PagedKVError(status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev(*ts) -> None:
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        _need(t.is_cuda, "all tensors must be on the GPU")
+        _need(t.is_contiguous(), "all tensors must be contiguous")
+        dev = dev or t.device
+        _need(t.device == dev, "all tensors must be on one device")
+
+
+def _code(t: torch.Tensor) -> int:
+    if t.dtype not in DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return DTYPE_CODES[t.dtype]
+
+
+def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+              k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+    """Write token t's K/V rows into slot slot_mapping[t] (-1 = skip).
+
+    k_new, v_new: [T, Hkv, D]; slot_mapping: int64 [T];
+    caches: [num_blocks, Hkv, 16, D] of the same dtype.
+    """
+    lib = load_library()
+    _dev(k_new, v_new, slot_mapping, k_cache, v_cache)
+    _need(k_new.shape == v_new.shape and k_new.dim() == 3, "k_new/v_new must be [T, Hkv, D]")
+    _need(k_cache.shape == v_cache.shape and k_cache.dim() == 4, "caches must be [NB, Hkv, 16, D]")
+    T, H, D = k_new.shape
+    _need(k_cache.shape[1] == H and k_cache.shape[3] == D, "cache and new-token shapes differ")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (T,), "slot_mapping must be int64 [T]")
+    _need(k_new.dtype == v_new.dtype == k_cache.dtype == v_cache.dtype, "dtype mismatch")
+    _check(lib.pkv_kv_append(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache),
+                             _ptr(v_cache), T, H, D, k_cache.shape[0], k_cache.shape[2],
+                             _code(k_cache), _stream(k_cache)))
+
+
+def decode_dims(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor,
+                out: torch.Tensor, partition_blocks: int = 0) -> DecodeDims:
+    B, Hq, D = q.shape
+    NB, Hkv, bs, Dk = k_cache.shape
+    _need(Dk == D, "head_dim of q and cache differ")
+    return DecodeDims(B, Hq, Hkv, D, bs, NB, block_tables.shape[1], _code(q), _code(k_cache),
+                      _code(out), partition_blocks)
+
+
+def decode_workspace_bytes(dims: DecodeDims) -> int:
+    return int(load_library().pkv_decode_workspace_bytes(ctypes.byref(dims)))
+
+
+def decode_num_partitions(dims: DecodeDims) -> int:
+    n = load_library().pkv_decode_num_partitions(ctypes.byref(dims))
+    _check(min(n, 0))
+    return n
+
+
+def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                      out: torch.Tensor, *, k_scales: Optional[torch.Tensor] = None,
+                      v_scales: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None,
+                      partition_blocks: int = 0) -> torch.Tensor:
+    """out[b, i] = softmax(scale * q[b, i] . K^T) V over the first context_lens[b]
+    tokens of sequence b, K/V read through block_tables.  Returns `out`.
+
+    q, out: [B, Hq, D]; caches: [NB, Hkv, 16, D]; block_tables: int32 [B, max_blocks];
+    context_lens: int32 [B].  FP8 caches (uint8 or float8_e4m3fn) need k_scales and
+    v_scales: fp32 [NB, Hkv].  `workspace` (uint8, on the device) is allocated here
+    when the call splits the context and none is given.
+    """
+    lib = load_library()
+    _dev(q, k_cache, v_cache, block_tables, context_lens, out, k_scales, v_scales, workspace)
+    _need(q.dim() == 3 and out.shape == q.shape, "q and out must be [B, Hq, D]")
+    _need(k_cache.shape == v_cache.shape and k_cache.dim() == 4, "caches must be [NB, Hkv, 16, D]")
+    _need(k_cache.dtype == v_cache.dtype, "K and V caches differ in dtype")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == q.shape[0], "block_tables must be int32 [B, max_blocks]")
+    _need(context_lens.dtype == torch.int32 and context_lens.shape == (q.shape[0],),
+          "context_lens must be int32 [B]")
+    dims = decode_dims(q, k_cache, block_tables, out, partition_blocks)
+    need = decode_workspace_bytes(dims)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _ptr(workspace) if need else None
+    ws_bytes = workspace.numel() * workspace.element_size() if (need and workspace is not None) else 0
+    fp8 = _code(k_cache) == 3
+    if fp8:
+        _need(k_scales is not None and v_scales is not None, "fp8 caches need k_scales and v_scales")
+        _need(k_scales.dtype == v_scales.dtype == torch.float32 and
+              k_scales.shape == v_scales.shape == k_cache.shape[:2], "scales must be fp32 [NB, Hkv]")
+        st = lib.pkv_paged_decode_attn_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales),
+                                           _ptr(v_scales), _ptr(block_tables), _ptr(context_lens),
+                                           float(scale), _ptr(out), ctypes.byref(dims), ws_ptr,
+                                           ws_bytes, _stream(q))
+    else:
+        _need(k_scales is None and v_scales is None, "scales apply to fp8 caches only")
+        st = lib.pkv_paged_decode_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                       _ptr(context_lens), float(scale), _ptr(out),
+                                       ctypes.byref(dims), ws_ptr, ws_bytes, _stream(q))
+    _check(st)
+    return out

@@ -1,0 +1,159 @@
+// C ABI of libpagedkv: argument checks on the host, then asynchronous launches.
+// Nothing here touches the device before every check has passed, so the
+// error paths can be exercised on a machine without a GPU.
+#include "pkv_internal.h"
+
+#include <cmath>
+
+using namespace pkv;
+
+namespace {
+
+int elem_bytes(int dt) {
+  switch (dt) {
+    case PKV_F32: return 4;
+    case PKV_F16: return 2;
+    case PKV_BF16: return 2;
+    case PKV_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+int check_dims(const pkv_decode_dims* d) {
+  if (!d) return PKV_ERR_NULL;
+  if (d->num_seqs <= 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0 ||
+      d->num_blocks <= 0 || d->max_blocks_per_seq <= 0 || d->partition_blocks < 0)
+    return PKV_ERR_SHAPE;
+  if (d->block_size != PKV_BLOCK_SIZE) return PKV_ERR_SHAPE;
+  if (d->num_q_heads % d->num_kv_heads) return PKV_ERR_SHAPE;
+  const int g = d->num_q_heads / d->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return PKV_ERR_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return PKV_ERR_SHAPE;
+  // grid dimensions: y = KV heads, z = sequences (HIP limits y, z to 65535)
+  if (d->num_kv_heads > 65535 || d->num_seqs > 65535) return PKV_ERR_SHAPE;
+  if (!elem_bytes(d->q_dtype) || !elem_bytes(d->kv_dtype) || !elem_bytes(d->out_dtype))
+    return PKV_ERR_DTYPE;
+  return PKV_OK;
+}
+
+int check_dtypes(const pkv_decode_dims* d, bool fp8) {
+  if (fp8) {
+    if (d->kv_dtype != PKV_FP8_E4M3) return PKV_ERR_DTYPE;
+    if (d->q_dtype == PKV_FP8_E4M3) return PKV_ERR_DTYPE;
+    const bool ok = (d->q_dtype == d->out_dtype) ||
+                    (d->out_dtype == PKV_F32 && (d->q_dtype == PKV_BF16 || d->q_dtype == PKV_F16));
+    return ok ? PKV_OK : PKV_ERR_DTYPE;
+  }
+  if (d->kv_dtype == PKV_FP8_E4M3) return PKV_ERR_DTYPE;
+  if (d->q_dtype != d->kv_dtype || d->out_dtype != d->kv_dtype) return PKV_ERR_DTYPE;
+  return PKV_OK;
+}
+
+int decode_common(const void* q, const void* k_cache, const void* v_cache, const float* k_scales,
+                  const float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
+                  float scale, void* out, const pkv_decode_dims* dims, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream, bool fp8) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
+  if (fp8 && (!k_scales || !v_scales)) return PKV_ERR_NULL;
+  st = check_dtypes(dims, fp8);
+  if (st) return st;
+  if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
+  int pb, np;
+  plan_partitions(*dims, &pb, &np);
+  const size_t need = workspace_bytes_for(*dims);
+  if (need && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+
+  DecodeArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.scale = scale * 1.4426950408889634f;  // scores are kept in log2 units
+  a.out = out;
+  const size_t rows = (size_t)dims->num_seqs * dims->num_q_heads;
+  a.o_part = need ? (float*)workspace : nullptr;
+  a.ml_part = need ? (float*)workspace + rows * np * dims->head_dim : nullptr;
+  a.num_seqs = dims->num_seqs;
+  a.num_q_heads = dims->num_q_heads;
+  a.num_kv_heads = dims->num_kv_heads;
+  a.head_dim = dims->head_dim;
+  a.num_blocks = dims->num_blocks;
+  a.max_blocks = dims->max_blocks_per_seq;
+  a.part_blocks = pb;
+  a.num_parts = np;
+  a.q_dtype = dims->q_dtype;
+  a.kv_dtype = dims->kv_dtype;
+  a.out_dtype = dims->out_dtype;
+  return launch_decode(a, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                  void* k_cache, void* v_cache, int32_t num_tokens, int32_t num_kv_heads,
+                  int32_t head_dim, int32_t num_blocks, int32_t block_size, int32_t dtype,
+                  hipStream_t stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0)
+    return PKV_ERR_SHAPE;
+  if (block_size != PKV_BLOCK_SIZE) return PKV_ERR_SHAPE;
+  if (dtype != PKV_F32 && dtype != PKV_F16 && dtype != PKV_BF16) return PKV_ERR_DTYPE;
+  const int row_bytes = head_dim * elem_bytes(dtype);
+  if (row_bytes % 16 || head_dim > 1024) return PKV_ERR_SHAPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKV_ERR_NULL;
+  return launch_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, num_tokens,
+                          num_kv_heads, row_bytes, num_blocks, stream);
+}
+
+size_t pkv_decode_workspace_bytes(const pkv_decode_dims* dims) {
+  if (check_dims(dims) != PKV_OK) return 0;
+  return workspace_bytes_for(*dims);
+}
+
+int pkv_decode_num_partitions(const pkv_decode_dims* dims) {
+  const int st = check_dims(dims);
+  if (st) return st;
+  int pb, np;
+  plan_partitions(*dims, &pb, &np);
+  return np;
+}
+
+int pkv_paged_decode_attn(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens, float scale,
+                          void* out, const pkv_decode_dims* dims, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  return decode_common(q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens, scale,
+                       out, dims, workspace, workspace_bytes, stream, false);
+}
+
+int pkv_paged_decode_attn_fp8(const void* q, const void* k_cache, const void* v_cache,
+                              const float* k_scales, const float* v_scales,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              float scale, void* out, const pkv_decode_dims* dims,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_common(q, k_cache, v_cache, k_scales, v_scales, block_tables, context_lens, scale,
+                       out, dims, workspace, workspace_bytes, stream, true);
+}
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "null pointer argument";
+    case PKV_ERR_SHAPE: return "invalid shape or size";
+    case PKV_ERR_DTYPE: return "unsupported dtype combination";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int pkv_version(void) { return PKV_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,621 @@
+// Paged decode attention for gfx950 (CDNA4, wave64), no MFMA.
+//
+// What is computed ("KV Cache from first principles" 2.1-2.2 and 4.3; "The
+// KV Cache memory ledger" 2 and 4): for every sequence b and query head i,
+//   out[b][i] = softmax_t(scale * <q[b][i], K_t>) . V_t  over t < L_b,
+// with K_t, V_t read through the block table (block table[t / 16], offset
+// t % 16), and query head i reading KV head i / g.
+//
+// Decode is a matrix-vector product per KV head, bound by HBM: every K/V
+// byte is used by only g query heads.  The kernel therefore streams each
+// (block, kv_head) tile once from HBM and makes that one read serve all g
+// query heads, with fp32 vector arithmetic (packed dot2 for 16-bit K).
+//
+// Work split.  Grid = (partition p, kv head h, sequence b); a workgroup of
+// four waves owns the blocks [p*PB, (p+1)*PB) of (b, h); wave w takes every
+// fourth of them.  Inside a wave, lane l covers token row r = l / LPT of
+// every tile and the 16-byte column c = l % LPT of that row, so one 16-byte
+// load per lane per (token row, column) reads a tile with fully contiguous
+// wave accesses, and each lane keeps its slice of all g query vectors in
+// registers for the whole partition.
+//
+// Scores.  A lane's partial dot products (g heads x its tokens) are summed
+// over the LPT lanes of its row with a DPP reduce-scatter: at every level a
+// lane keeps half of its partial sums and adds its partner's matching half.
+// Partners hold mirrored register orders (slot k of lane l holds quantity
+// k ^ M(l), M built from the lane's level bits), so each level is a plain
+// "s[k] += dpp(s[k + n/2])" with no selects.  After the reduce-scatter every
+// score exists once per row, so the exponentials are not duplicated; an
+// all-gather (the same exchange run backwards) then hands every lane the
+// probabilities it needs for its V slice.
+//
+// Softmax.  Online softmax with a lazily moved reference maximum per head:
+// probabilities are exp2(s - m_ref) and m_ref moves (rescaling the running
+// sum and accumulator) only when a score exceeds it by more than 2^8, which
+// after the first block is rare.  Every token row of every wave is its own
+// stream; streams are merged by log-sum-exp at the end of the partition, and
+// partitions by a second small kernel.
+//
+// Masking.  Positions >= L (the tail of the last block) get score -inf and a
+// zeroed V operand, so poisoned tail slots never reach the sums (0 * NaN
+// would).  Block ids outside the pool are treated as fully masked.
+#include "pkv_internal.h"
+
+#include <type_traits>
+#include <utility>
+
+namespace pkv {
+
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
+
+template <KV KT, int D, int G>
+struct Cfg {
+  static constexpr int EB = kv_bytes<KT>::value;
+  static constexpr int E = 16 / EB;                        // elements per 16-byte load
+  static constexpr int VPT = (D / E > 16) ? (D / E) / 16 : 1;  // loads per token per lane
+  static constexpr int LPT = D / (E * VPT);                // lanes sharing one token
+  static constexpr int R = 64 / LPT;                       // token rows per wave
+  static constexpr int TPL = 16 / R;                       // tokens per lane per block
+  static constexpr int NS = G * TPL;                       // score slots per lane
+  static constexpr int LEVELS = ilog2(LPT);
+  static constexpr int NRS = cmin(LEVELS, ilog2(NS));      // reduce-scatter levels
+  static constexpr int NF = NS >> NRS;                     // slots left after it
+  static constexpr int EL = E * VPT;                       // elements per lane per token
+  static constexpr int NW = 4;                             // waves per workgroup
+  static_assert(LPT >= 1 && LPT <= 16 && (LPT & (LPT - 1)) == 0, "lanes per token");
+  static_assert(TPL >= 1, "tokens per lane");
+};
+
+constexpr float kLazyMaxSlack = 8.0f;   // log2 units: probabilities stay <= 256
+
+// Exchange of level KIND (0: c^8, 1: half mirror, 2: c^2, 3: c^1).
+template <int KIND>
+__device__ __forceinline__ float xlevel(float v) {
+  if constexpr (KIND == 0) return dpp<DPP_ROW_ROR8>(v);
+  else if constexpr (KIND == 1) return dpp<DPP_ROW_HALF_MIRROR>(v);
+  else if constexpr (KIND == 2) return dpp<DPP_QUAD_XOR2>(v);
+  else return dpp<DPP_QUAD_XOR1>(v);
+}
+
+// Lane bit that flips exactly across the partners of level KIND and across
+// no other level's partners (solves m_k(F_j) = [k == j] for the flip sets
+// F = {8}, {0,1,2}, {1}, {0} of the four exchanges).
+template <int KIND, int LEVELS>
+__device__ __forceinline__ int level_bit(int c) {
+  const int b2 = LEVELS >= 3 ? (c >> 2) & 1 : 0;
+  if constexpr (KIND == 0) return (c >> 3) & 1;
+  else if constexpr (KIND == 1) return (c >> 2) & 1;
+  else if constexpr (KIND == 2) return ((c >> 1) & 1) ^ b2;
+  else return (c & 1) ^ b2;
+}
+
+// ---- per-dtype pieces ------------------------------------------------------
+// Query slice held by a lane: QW words per head (packed pairs for 16-bit K,
+// fp32 otherwise).
+template <KV KT, int EL> struct QSlice;
+template <int EL> struct QSlice<KV::F16, EL> { uint32_t w[EL / 2]; };
+template <int EL> struct QSlice<KV::BF16, EL> { uint32_t w[EL / 2]; };
+template <int EL> struct QSlice<KV::F32, EL> { float f[EL]; };
+template <int EL> struct QSlice<KV::FP8, EL> { float f[EL]; };
+
+template <KV T>
+__device__ __forceinline__ float load_elem_f32(const void* base, int64_t idx) {
+  if constexpr (T == KV::F32) return ((const float*)base)[idx];
+  else if constexpr (T == KV::F16) return (float)((const _Float16*)base)[idx];
+  else return __builtin_bit_cast(float, ((uint32_t)((const uint16_t*)base)[idx]) << 16);
+}
+
+// q row (already offset to the lane's head) -> the lane's slice.
+template <KV KT, KV QT, int D, int G, int EL, int LPT, int E, int VPT>
+__device__ __forceinline__ void load_q(QSlice<KT, EL>& qs, const void* qrow, int c) {
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    const int e0 = (v * LPT + c) * E;
+    if constexpr (KT == KV::F16 || KT == KV::BF16) {
+      static_assert(QT == KT, "16-bit caches take a query of the same type");
+      const uint4 x = *(const uint4*)((const uint16_t*)qrow + e0);
+      qs.w[v * 4 + 0] = x.x; qs.w[v * 4 + 1] = x.y; qs.w[v * 4 + 2] = x.z; qs.w[v * 4 + 3] = x.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) qs.f[v * E + e] = load_elem_f32<QT>(qrow, e0 + e);
+    }
+  }
+}
+
+// K/V words of one token for one lane: VPT * 4 dwords.
+template <int VPT> struct TokWords { uint4 x[VPT]; };
+
+template <KV KT, int EL, int VPT>
+__device__ __forceinline__ void to_f32(const TokWords<VPT>& t, float (&f)[EL]) {
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    const uint32_t w[4] = {t.x[v].x, t.x[v].y, t.x[v].z, t.x[v].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (KT == KV::F32) {
+        f[v * 4 + k] = __builtin_bit_cast(float, w[k]);
+      } else if constexpr (KT == KV::F16) {
+        f[v * 8 + 2 * k] = f16lo(w[k]);
+        f[v * 8 + 2 * k + 1] = f16hi(w[k]);
+      } else if constexpr (KT == KV::BF16) {
+        f[v * 8 + 2 * k] = bf16lo(w[k]);
+        f[v * 8 + 2 * k + 1] = bf16hi(w[k]);
+      } else {
+        const float2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
+        const float2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
+        f[v * 16 + 4 * k + 0] = lo.x;
+        f[v * 16 + 4 * k + 1] = lo.y;
+        f[v * 16 + 4 * k + 2] = hi.x;
+        f[v * 16 + 4 * k + 3] = hi.y;
+      }
+    }
+  }
+}
+
+// Partial <q_slice, K_slice> for one token.
+template <KV KT, int EL, int VPT>
+__device__ __forceinline__ float qk_partial(const QSlice<KT, EL>& qs, const TokWords<VPT>& t,
+                                            const float (&kf)[EL]) {
+  float s = 0.f;
+  if constexpr (KT == KV::F16) {
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      const uint32_t w[4] = {t.x[v].x, t.x[v].y, t.x[v].z, t.x[v].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qs.w[v * 4 + k]),
+                                   __builtin_bit_cast(half2_t, w[k]), s, false);
+    }
+  } else if constexpr (KT == KV::BF16) {
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      const uint32_t w[4] = {t.x[v].x, t.x[v].y, t.x[v].z, t.x[v].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, qs.w[v * 4 + k]),
+                                            __builtin_bit_cast(bf162_t, w[k]), s, false);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EL; ++e) s = __builtin_fmaf(qs.f[e], kf[e], s);
+  }
+  return s;
+}
+
+template <KV OT>
+__device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
+  if constexpr (OT == KV::F32) ((float*)out)[idx] = x;
+  else if constexpr (OT == KV::F16) ((_Float16*)out)[idx] = (_Float16)x;
+  else ((uint16_t*)out)[idx] = f32_to_bf16_rne(x);
+}
+
+__device__ __forceinline__ float exp2_safe_factor(float m_old, float m_new) {
+  // factor that moves a sum referenced to m_old onto m_new (m_new >= m_old)
+  return m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_old - m_new);
+}
+
+// ---------------------------------------------------------------------------
+template <KV KT, KV QT, KV OT, int D, int G>
+__global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
+  using C = Cfg<KT, D, G>;
+  constexpr int E = C::E, VPT = C::VPT, LPT = C::LPT, R = C::R, TPL = C::TPL;
+  constexpr int NS = C::NS, NRS = C::NRS, NF = C::NF, EL = C::EL, NW = C::NW;
+  constexpr int LEVELS = C::LEVELS;
+  constexpr int TILE = 16 * D;  // elements per (block, kv_head) tile
+
+  __shared__ float red_m[NW][G];
+  __shared__ float red_l[NW][G];
+  __shared__ float red_acc[NW][G][D];
+
+  const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int Hq = a.num_kv_heads * G;
+
+  int L = a.context_lens[b];
+  L = L < 0 ? 0 : (L > a.max_blocks * 16 ? a.max_blocks * 16 : L);
+  const int nblk = (L + 15) >> 4;
+  const int j0 = p * a.part_blocks;
+  const int j1 = min(j0 + a.part_blocks, nblk);
+  if (j0 >= j1) {
+    if (a.num_parts == 1) {
+      for (int idx = tid; idx < G * D; idx += 256)
+        store_out<OT>(a.out, ((int64_t)b * Hq + h * G) * D + idx, 0.f);
+    }
+    return;  // empty partitions of a split call are skipped by the merge
+  }
+
+  const int r = lane / LPT, c = lane % LPT;
+  int M = 0;
+  static_for<NRS>([&](auto l) {
+    constexpr int kind = 4 - LEVELS + decltype(l)::value;
+    M |= level_bit<kind, LEVELS>(c) * (NS >> (decltype(l)::value + 1));
+  });
+  const int hmask = M % G;   // register head hs holds query head h*G + (hs ^ hmask)
+  const int tmask = M / G;   // register token i holds tile row ((i ^ tmask) * R + r)
+
+  QSlice<KT, EL> qs[G];
+#pragma unroll
+  for (int hs = 0; hs < G; ++hs) {
+    const int qi = h * G + (hs ^ hmask);
+    const int64_t qoff = ((int64_t)b * Hq + qi) * D;
+    if constexpr (QT == KV::F32) load_q<KT, QT, D, G, EL, LPT, E, VPT>(qs[hs], (const float*)a.q + qoff, c);
+    else load_q<KT, QT, D, G, EL, LPT, E, VPT>(qs[hs], (const uint16_t*)a.q + qoff, c);
+  }
+
+  float acc[G][EL];
+  float mref[G];
+#pragma unroll
+  for (int hs = 0; hs < G; ++hs) {
+    mref[hs] = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) acc[hs][e] = 0.f;
+  }
+  float lpart[NF];
+#pragma unroll
+  for (int k = 0; k < NF; ++k) lpart[k] = 0.f;
+
+  const char* kbase = (const char*)a.k_cache;
+  const char* vbase = (const char*)a.v_cache;
+  const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
+  // byte offset of this lane's words inside a tile, per register token/load
+  int lane_off[TPL][VPT];
+#pragma unroll
+  for (int i = 0; i < TPL; ++i)
+#pragma unroll
+    for (int v = 0; v < VPT; ++v)
+      lane_off[i][v] = (((i ^ tmask) * R + r) * D + (v * LPT + c) * E) * C::EB;
+
+  auto load_block = [&](int j, TokWords<VPT> (&kr)[TPL], TokWords<VPT> (&vr)[TPL]) {
+    int phys = table[j];
+    phys = ((unsigned)phys < (unsigned)a.num_blocks) ? phys : 0;
+    const int64_t tile = ((int64_t)phys * a.num_kv_heads + h) * TILE * C::EB;
+#pragma unroll
+    for (int i = 0; i < TPL; ++i)
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) {
+        kr[i].x[v] = *(const uint4*)(kbase + tile + lane_off[i][v]);
+        vr[i].x[v] = *(const uint4*)(vbase + tile + lane_off[i][v]);
+      }
+  };
+
+  auto compute_block = [&](int j, const TokWords<VPT> (&kr)[TPL], const TokWords<VPT> (&vr)[TPL]) {
+    const int phys_raw = table[j];
+    const bool blk_ok = (unsigned)phys_raw < (unsigned)a.num_blocks;
+    const int nvalid = blk_ok ? min(16, L - j * 16) : 0;
+    float cs = a.scale;  // scale * log2(e), folded on the host
+    float vsc = 1.f;
+    if constexpr (KT == KV::FP8) {
+      const int64_t si = (int64_t)(blk_ok ? phys_raw : 0) * a.num_kv_heads + h;
+      cs *= a.k_scales[si];
+      vsc = a.v_scales[si];
+    }
+
+    // 1. partial scores: slot k = i * G + hs
+    float s[NS];
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+      float kf[EL];
+      if constexpr (KT == KV::F32 || KT == KV::FP8) to_f32<KT, EL, VPT>(kr[i], kf);
+#pragma unroll
+      for (int hs = 0; hs < G; ++hs) s[i * G + hs] = qk_partial<KT, EL, VPT>(qs[hs], kr[i], kf);
+    }
+    // 2. reduce-scatter over the row, then all-reduce for any levels left
+    static_for<NRS>([&](auto l) {
+      constexpr int lv = decltype(l)::value;
+      constexpr int half = NS >> (lv + 1);
+#pragma unroll
+      for (int k = 0; k < half; ++k) s[k] += xlevel<4 - LEVELS + lv>(s[k + half]);
+    });
+    static_for<LEVELS - NRS>([&](auto l) {
+      constexpr int lv = NRS + decltype(l)::value;
+      s[0] += xlevel<4 - LEVELS + lv>(s[0]);
+    });
+#pragma unroll
+    for (int k = 0; k < NF; ++k) s[k] *= cs;
+
+    // 3. mask the tail (and a block id outside the pool)
+    TokWords<VPT> vv[TPL];
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) vv[i] = vr[i];
+    if (nvalid < 16) {
+#pragma unroll
+      for (int k = 0; k < NF; ++k) {
+        const int tok = (((k / G) ^ tmask) * R + r);
+        if (tok >= nvalid) s[k] = -INFINITY;
+      }
+#pragma unroll
+      for (int i = 0; i < TPL; ++i) {
+        if (((i ^ tmask) * R + r) >= nvalid) {
+#pragma unroll
+          for (int v = 0; v < VPT; ++v) vv[i].x[v] = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+
+    // 4. move the reference maxima if some score passed them by > slack
+    bool need = false;
+#pragma unroll
+    for (int k = 0; k < NF; ++k) need |= s[k] > mref[k % G] + kLazyMaxSlack;
+    if (__any(need)) {
+      float sa[NS];
+#pragma unroll
+      for (int k = 0; k < NF; ++k) sa[k] = s[k];
+      static_for<NRS>([&](auto l) {
+        constexpr int lv = NRS - 1 - decltype(l)::value;
+        constexpr int half = NS >> (lv + 1);
+#pragma unroll
+        for (int k = 0; k < half; ++k) sa[k + half] = xlevel<4 - LEVELS + lv>(sa[k]);
+      });
+#pragma unroll
+      for (int hs = 0; hs < G; ++hs) {
+        float bm = sa[hs];
+#pragma unroll
+        for (int i = 1; i < TPL; ++i) bm = fmaxf(bm, sa[i * G + hs]);
+        const float mnew = fmaxf(mref[hs], bm);
+        const float f = exp2_safe_factor(mref[hs], mnew);
+#pragma unroll
+        for (int e = 0; e < EL; ++e) acc[hs][e] *= f;
+#pragma unroll
+        for (int k = 0; k < NF; ++k)
+          if (k % G == hs) lpart[k] *= f;
+        mref[hs] = mnew;
+      }
+    }
+
+    // 5. probabilities of the row's own scores, then all-gather them
+    float pf[NS];
+#pragma unroll
+    for (int k = 0; k < NF; ++k) {
+      const float m = mref[k % G];
+      const float pk = __builtin_amdgcn_exp2f(s[k] - (m == -INFINITY ? 0.f : m));
+      lpart[k] += pk;
+      pf[k] = pk * vsc;
+    }
+    static_for<NRS>([&](auto l) {
+      constexpr int lv = NRS - 1 - decltype(l)::value;
+      constexpr int half = NS >> (lv + 1);
+#pragma unroll
+      for (int k = 0; k < half; ++k) pf[k + half] = xlevel<4 - LEVELS + lv>(pf[k]);
+    });
+
+    // 6. accumulate p * V
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+      float vf[EL];
+      to_f32<KT, EL, VPT>(vv[i], vf);
+#pragma unroll
+      for (int hs = 0; hs < G; ++hs) {
+        const float pw = pf[i * G + hs];
+#pragma unroll
+        for (int e = 0; e < EL; ++e) acc[hs][e] = __builtin_fmaf(pw, vf[e], acc[hs][e]);
+      }
+    }
+  };
+
+  // software pipeline: the next block's loads are in flight during compute
+  {
+    int j = j0 + w;
+    if (j < j1) {
+      TokWords<VPT> ka[TPL], va[TPL], kb[TPL], vb[TPL];
+      load_block(j, ka, va);
+      while (true) {
+        if (j + NW < j1) load_block(j + NW, kb, vb);
+        compute_block(j, ka, va);
+        j += NW;
+        if (j >= j1) break;
+        if (j + NW < j1) load_block(j + NW, ka, va);
+        compute_block(j, kb, vb);
+        j += NW;
+        if (j >= j1) break;
+      }
+    }
+  }
+
+  // ---- combine: lanes of a row -> rows of a wave -> waves of the group ----
+  // per-head sum of probabilities over the row
+  float la[NS];
+#pragma unroll
+  for (int k = 0; k < NF; ++k) la[k] = lpart[k];
+  static_for<NRS>([&](auto l) {
+    constexpr int lv = NRS - 1 - decltype(l)::value;
+    constexpr int half = NS >> (lv + 1);
+#pragma unroll
+    for (int k = 0; k < half; ++k) la[k + half] = xlevel<4 - LEVELS + lv>(la[k]);
+  });
+  float lrow[G];
+#pragma unroll
+  for (int hs = 0; hs < G; ++hs) {
+    lrow[hs] = 0.f;
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) lrow[hs] += la[i * G + hs];
+  }
+  // rows of the wave: lanes with equal c hold the same heads and columns
+#pragma unroll
+  for (int hs = 0; hs < G; ++hs) {
+    float mw = mref[hs];
+#pragma unroll
+    for (int d = LPT; d < 64; d <<= 1) mw = fmaxf(mw, __shfl_xor(mw, d));
+    const float f = mref[hs] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref[hs] - mw);
+    lrow[hs] *= f;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) acc[hs][e] *= f;
+#pragma unroll
+    for (int d = LPT; d < 64; d <<= 1) {
+      lrow[hs] += __shfl_xor(lrow[hs], d);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) acc[hs][e] += __shfl_xor(acc[hs][e], d);
+    }
+    mref[hs] = mw;
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int hs = 0; hs < G; ++hs) {
+      const int ha = hs ^ hmask;
+#pragma unroll
+      for (int v = 0; v < VPT; ++v)
+#pragma unroll
+        for (int e = 0; e < E; ++e) red_acc[w][ha][(v * LPT + c) * E + e] = acc[hs][v * E + e];
+      if (c == 0) {
+        red_m[w][ha] = mref[hs];
+        red_l[w][ha] = lrow[hs];
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int ha = idx / D, d = idx % D;
+    float m = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) m = fmaxf(m, red_m[ww][ha]);
+    float lsum = 0.f, o = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float f = red_m[ww][ha] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(red_m[ww][ha] - m);
+      lsum += red_l[ww][ha] * f;
+      o += red_acc[ww][ha][d] * f;
+    }
+    const float res = lsum > 0.f ? o / lsum : 0.f;
+    const int64_t row = (int64_t)b * Hq + h * G + ha;
+    if (a.num_parts == 1) {
+      store_out<OT>(a.out, row * D + d, res);
+    } else {
+      a.o_part[(row * a.num_parts + p) * D + d] = res;
+      if (d == 0) {
+        a.ml_part[(row * a.num_parts + p) * 2 + 0] = m;
+        a.ml_part[(row * a.num_parts + p) * 2 + 1] = lsum;
+      }
+    }
+  }
+}
+
+// Log-sum-exp merge of the partitions of one (sequence, query head) row.
+// Partition p carries o_p (its normalised output), m_p (log2 reference) and
+// l_p (sum of exp2(s - m_p)); out = sum_p l_p 2^(m_p - M) o_p / sum_p l_p 2^(m_p - M).
+template <KV OT, int D>
+__global__ void __launch_bounds__(64) lse_merge_kernel(DecodeArgs a) {
+  const int row = blockIdx.x;
+  const int b = row / a.num_q_heads;
+  const int lane = threadIdx.x;
+  int L = a.context_lens[b];
+  L = L < 0 ? 0 : (L > a.max_blocks * 16 ? a.max_blocks * 16 : L);
+  const int nblk = (L + 15) >> 4;
+  const int np = min((nblk + a.part_blocks - 1) / a.part_blocks, a.num_parts);
+  const float* ml = a.ml_part + (int64_t)row * a.num_parts * 2;
+  const float* op = a.o_part + (int64_t)row * a.num_parts * D;
+  float m = -INFINITY;
+  for (int p = 0; p < np; ++p)
+    if (ml[2 * p + 1] > 0.f) m = fmaxf(m, ml[2 * p]);
+  constexpr int PER = D / 64;
+  float o[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) o[k] = 0.f;
+  float wsum = 0.f;
+  for (int p = 0; p < np; ++p) {
+    const float lp = ml[2 * p + 1];
+    if (!(lp > 0.f)) continue;
+    const float wgt = lp * __builtin_amdgcn_exp2f(ml[2 * p] - m);
+    wsum += wgt;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) o[k] = __builtin_fmaf(wgt, op[(int64_t)p * D + k * 64 + lane], o[k]);
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) store_out<OT>(a.out, (int64_t)row * D + k * 64 + lane, o[k] * inv);
+}
+
+// ---------------------------------------------------------------------------
+void plan_partitions(const pkv_decode_dims& d, int* part_blocks, int* num_parts) {
+  const int maxb = d.max_blocks_per_seq;
+  int pb;
+  if (d.partition_blocks > 0) {
+    pb = d.partition_blocks;
+  } else {
+    // aim for >= 1024 workgroups (4 per CU on 256 CUs), but never split
+    // below 16 blocks (256 tokens) per partition
+    const int64_t units = (int64_t)d.num_seqs * d.num_kv_heads;
+    int64_t want = (1024 + units - 1) / units;
+    if (want < 1) want = 1;
+    pb = (int)((maxb + want - 1) / want);
+    if (pb < 16) pb = 16;
+  }
+  if (pb > maxb) pb = maxb;
+  if (pb < 1) pb = 1;
+  *part_blocks = pb;
+  *num_parts = (maxb + pb - 1) / pb;
+}
+
+size_t workspace_bytes_for(const pkv_decode_dims& d) {
+  int pb, np;
+  plan_partitions(d, &pb, &np);
+  if (np <= 1) return 0;
+  return (size_t)d.num_seqs * d.num_q_heads * np * (d.head_dim + 2) * sizeof(float);
+}
+
+template <KV KT, KV QT, KV OT, int D, int G>
+static int launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
+  hipLaunchKernelGGL((decode_partition_kernel<KT, QT, OT, D, G>), grid, dim3(256), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return PKV_ERR_LAUNCH;
+  if (a.num_parts > 1) {
+    hipLaunchKernelGGL((lse_merge_kernel<OT, D>), dim3(a.num_seqs * a.num_q_heads), dim3(64), 0,
+                       stream, a);
+    if (hipGetLastError() != hipSuccess) return PKV_ERR_LAUNCH;
+  }
+  return PKV_OK;
+}
+
+template <KV KT, KV QT, KV OT, int D>
+static int dispatch_g(const DecodeArgs& a, hipStream_t s) {
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_typed<KT, QT, OT, D, 1>(a, s);
+    case 2: return launch_typed<KT, QT, OT, D, 2>(a, s);
+    case 4: return launch_typed<KT, QT, OT, D, 4>(a, s);
+    case 8: return launch_typed<KT, QT, OT, D, 8>(a, s);
+    default: return PKV_ERR_SHAPE;
+  }
+}
+
+template <KV KT, KV QT, KV OT>
+static int dispatch_d(const DecodeArgs& a, hipStream_t s) {
+  switch (a.head_dim) {
+    case 64: return dispatch_g<KT, QT, OT, 64>(a, s);
+    case 128: return dispatch_g<KT, QT, OT, 128>(a, s);
+    default: return PKV_ERR_SHAPE;
+  }
+}
+
+template <KV QT, KV OT>
+static int dispatch_fp8_out(const DecodeArgs& a, hipStream_t s) {
+  return dispatch_d<KV::FP8, QT, OT>(a, s);
+}
+
+int launch_decode(const DecodeArgs& a, hipStream_t s) {
+  const KV kt = (KV)a.kv_dtype, qt = (KV)a.q_dtype, ot = (KV)a.out_dtype;
+  if (kt != KV::FP8) {
+    if (qt != kt || ot != kt) return PKV_ERR_DTYPE;
+    switch (kt) {
+      case KV::F32: return dispatch_d<KV::F32, KV::F32, KV::F32>(a, s);
+      case KV::F16: return dispatch_d<KV::F16, KV::F16, KV::F16>(a, s);
+      case KV::BF16: return dispatch_d<KV::BF16, KV::BF16, KV::BF16>(a, s);
+      default: return PKV_ERR_DTYPE;
+    }
+  }
+#define PKV_FP8_CASE(Q, O)                                          \
+  if (qt == KV::Q && ot == KV::O) return dispatch_fp8_out<KV::Q, KV::O>(a, s);
+  PKV_FP8_CASE(BF16, BF16)
+  PKV_FP8_CASE(F16, F16)
+  PKV_FP8_CASE(F32, F32)
+  PKV_FP8_CASE(BF16, F32)
+  PKV_FP8_CASE(F16, F32)
+#undef PKV_FP8_CASE
+  return PKV_ERR_DTYPE;
+}
+
+}  // namespace pkv

@@ -1,0 +1,36 @@
+// Internal launcher declarations shared by the C-ABI shim and the kernels.
+#pragma once
+
+#include "../../include/pagedkv.h"
+#include "pkv_common.h"
+
+namespace pkv {
+
+int launch_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                     void* k_cache, void* v_cache, int num_tokens, int num_kv_heads,
+                     int row_bytes, int num_blocks, hipStream_t stream);
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const float* k_scales;   // fp8 only
+  const float* v_scales;   // fp8 only
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float scale;
+  void* out;
+  float* o_part;           // [B*Hq][P][D] when P > 1
+  float* ml_part;          // [B*Hq][P][2] when P > 1
+  int num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks;
+  int part_blocks, num_parts;
+  int q_dtype, kv_dtype, out_dtype;
+};
+
+// Partition plan: depends on dims only.
+void plan_partitions(const pkv_decode_dims& d, int* part_blocks, int* num_parts);
+size_t workspace_bytes_for(const pkv_decode_dims& d);
+
+int launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,141 @@
+"""The C ABI on a machine without a GPU: exports, status codes, sizing.
+
+Every call here fails validation (or needs no launch), so nothing reaches
+the device.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import paged_kv_cache_56_amd as pkv
+from paged_kv_cache_56_amd import DecodeDims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def _declared():
+    names = []
+    for fn in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            names += re.findall(r"^PKV_API\b[^;(]*?\b(pkv_\w+)\s*\(", text, flags=re.M)
+    return names
+
+
+def test_library_exports_every_declared_function():
+    names = _declared()
+    assert len(names) >= 7
+    lib = pkv.load_library()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.pkv_version() == 100
+
+
+def _dims(**kw):
+    base = dict(num_seqs=64, num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=16,
+                num_blocks=16384, max_blocks_per_seq=256, q_dtype=1, kv_dtype=1, out_dtype=1,
+                partition_blocks=0)
+    base.update(kw)
+    return DecodeDims(**base)
+
+
+def _attn(dims, q=FAKE, ws=None, ws_bytes=0):
+    lib = pkv.load_library()
+    return lib.pkv_paged_decode_attn(q, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.088), FAKE,
+                                     ctypes.byref(dims), ws, ws_bytes, None)
+
+
+def _attn_fp8(dims, ks=FAKE, vs=FAKE):
+    lib = pkv.load_library()
+    return lib.pkv_paged_decode_attn_fp8(FAKE, FAKE, FAKE, ks, vs, FAKE, FAKE, ctypes.c_float(0.088),
+                                         FAKE, ctypes.byref(dims), None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block_size=8), -2),
+    (dict(num_q_heads=60), -2),            # Hq % Hkv
+    (dict(num_q_heads=128), -2),           # g = 16
+    (dict(head_dim=96), -2),
+    (dict(num_seqs=0), -2),
+    (dict(max_blocks_per_seq=0), -2),
+    (dict(num_blocks=-1), -2),
+    (dict(partition_blocks=-3), -2),
+    (dict(q_dtype=2), -3),                 # q bf16, cache f16
+    (dict(out_dtype=0), -3),
+    (dict(kv_dtype=3, q_dtype=3, out_dtype=3), -3),  # fp8 through the non-fp8 entry
+    (dict(q_dtype=7), -3),
+])
+def test_attn_status_codes(kw, status):
+    assert _attn(_dims(**kw)) == status
+
+
+def test_attn_null_and_workspace():
+    assert _attn(_dims(), q=None) == -1
+    d = _dims()                            # 64 x 8 units -> split in two
+    need = pkv.decode_workspace_bytes(d)
+    assert need == 64 * 64 * 2 * (128 + 2) * 4
+    assert _attn(d, ws=None, ws_bytes=0) == -4
+    assert _attn(d, ws=FAKE, ws_bytes=need - 1) == -4
+    assert _attn(_dims(), ws=FAKE, ws_bytes=need - 4) == -4
+
+
+def test_fp8_status_codes():
+    ok = dict(kv_dtype=3, q_dtype=2, out_dtype=2, num_q_heads=32, max_blocks_per_seq=16)
+    assert _attn_fp8(_dims(**ok), ks=None) == -1
+    assert _attn_fp8(_dims(**ok), vs=None) == -1
+    assert _attn_fp8(_dims(**dict(ok, kv_dtype=1))) == -3
+    assert _attn_fp8(_dims(**dict(ok, q_dtype=3))) == -3
+    assert _attn_fp8(_dims(**dict(ok, out_dtype=1))) == -3        # bf16 q, f16 out
+
+
+def test_append_status_codes():
+    lib = pkv.load_library()
+    call = lambda *a: lib.pkv_kv_append(*a, None)
+    assert call(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 64, 8, 1) == -2     # block size
+    assert call(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 64, 16, 3) == -3    # fp8
+    assert call(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 12, 64, 16, 1) == -2     # 24-byte rows
+    assert call(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 8, 128, 64, 16, 1) == -2
+    assert call(None, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 64, 16, 1) == -1
+    assert call(None, None, None, None, None, 0, 8, 128, 64, 16, 1) == 0     # nothing to do
+
+
+@pytest.mark.parametrize("B,Hkv,maxb,parts", [
+    (64, 8, 256, 2),        # 70B-shaped step
+    (8, 8, 8192, 16),       # 131072-token fp8 case
+    (64, 40, 100, 1),       # MHA prefix batch
+    (4, 2, 7, 1),           # tiny
+    (32, 8, 498, 4),        # Llama-3-8B layer
+])
+def test_partition_plan(B, Hkv, maxb, parts):
+    d = _dims(num_seqs=B, num_kv_heads=Hkv, num_q_heads=Hkv * 4, max_blocks_per_seq=maxb)
+    assert pkv.decode_num_partitions(d) == parts
+    ws = pkv.decode_workspace_bytes(d)
+    assert ws == (0 if parts == 1 else B * Hkv * 4 * parts * (128 + 2) * 4)
+
+
+def test_explicit_partition_size():
+    d = _dims(partition_blocks=7)
+    assert pkv.decode_num_partitions(d) == -(-256 // 7)
+    d = _dims(partition_blocks=1000)
+    assert pkv.decode_num_partitions(d) == 1 and pkv.decode_workspace_bytes(d) == 0
+
+
+def test_status_strings():
+    lib = pkv.load_library()
+    for s in (0, -1, -2, -3, -4, -5, 9):
+        assert lib.pkv_status_string(s)
+
+
+def test_python_binding_rejects_host_tensors():
+    q = torch.zeros(1, 4, 64)
+    kc = torch.zeros(2, 1, 16, 64)
+    with pytest.raises(ValueError):
+        pkv.paged_decode_attn(q, kc, kc, torch.zeros(1, 2, dtype=torch.int32),
+                              torch.ones(1, dtype=torch.int32), 0.125, torch.zeros_like(q))
+    with pytest.raises(ValueError):
+        pkv.kv_append(torch.zeros(1, 1, 64), torch.zeros(1, 1, 64), torch.zeros(1, dtype=torch.int64), kc, kc)

@@ -1,0 +1,286 @@
+"""HIP path against the float64 oracle, element by element (needs a GPU).
+
+Tolerances (max-abs against the oracle run on the same stored values):
+fp32 1e-5, fp16/bf16 1e-2, fp8 5e-2; kv_append bit-exact.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_56_amd as pkv
+from workloads import WORKLOADS, DecodeWorkload, build_layout, make_host_inputs, make_device_inputs, scaled
+from gpu_common import TOL, say, host_storage, run_step, oracle_rows, host_layer, out_f64, max_err
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _to_dev(x):
+    return {k: v.to(DEV) for k, v in x.items()}
+
+
+def _out(spec, layers=None):
+    return torch.empty((spec.num_seqs, spec.num_q_heads, spec.head_dim),
+                       dtype=TORCH_DT[spec.out_dtype], device=DEV)
+
+
+# --------------------------------------------------------------------------
+# kv_append
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_kv_append_bit_exact(dt):
+    say(f"[kv_append] dtype={dt}")
+    spec = DecodeWorkload(name=f"append_{dt}", seed=77, num_layers=1, num_seqs=9, num_q_heads=8,
+                          num_kv_heads=4, head_dim=128, kv_dtype=dt, q_dtype=dt, out_dtype=dt,
+                          context_lens=(1, 16, 17, 32, 33, 100, 255, 256, 257), num_blocks=80)
+    lay = build_layout(spec)
+    x = make_host_inputs(lay)
+    slots = lay.slot_mapping.copy()
+    slots[3] = -1                                    # skipped token
+    xs = _to_dev(x)
+    sm = torch.from_numpy(slots).to(DEV)
+    pkv.kv_append(xs["k_new"][0], xs["v_new"][0], sm, xs["k_cache"][0], xs["v_cache"][0])
+    torch.cuda.synchronize()
+    for name, new in (("k_cache", "k_new"), ("v_cache", "v_new")):
+        ref = oracle.kv_append_bits(host_storage(x[name][0]), host_storage(x[new][0]), slots)
+        got = host_storage(xs[name][0])
+        assert np.array_equal(got.view(np.uint8), ref.view(np.uint8)), name
+
+
+def test_kv_append_skips_out_of_pool_slots():
+    say("[kv_append] out-of-pool slot")
+    kc = torch.zeros((2, 1, 16, 64), dtype=torch.float16, device=DEV)
+    vc = torch.zeros_like(kc)
+    new = torch.ones((3, 1, 64), dtype=torch.float16, device=DEV)
+    sm = torch.tensor([5, 2 * 16, 31], dtype=torch.int64, device=DEV)
+    pkv.kv_append(new, new, sm, kc, vc)
+    torch.cuda.synchronize()
+    flat = kc.view(32, 64).cpu()
+    assert (flat[5] == 1).all() and (flat[31] == 1).all()
+    assert flat.sum().item() == 2 * 64
+
+
+# --------------------------------------------------------------------------
+# decode attention, oracle-sized cases
+# --------------------------------------------------------------------------
+
+def _ragged(name, kv, q, out, D, G, lens, seed, hkv=2, append=False):
+    return DecodeWorkload(name=name, seed=seed, num_layers=1, num_seqs=len(lens), num_q_heads=hkv * G,
+                          num_kv_heads=hkv, head_dim=D, kv_dtype=kv, q_dtype=q, out_dtype=out,
+                          context_lens=tuple(lens), append=append)
+
+
+RAGGED = [1, 15, 16, 17, 31, 33, 100, 257, 0, 64, 511]
+SMALL = {
+    "tiny_f32": WORKLOADS["tiny_f32"],
+    "llama3_8b_bf16_small": scaled(WORKLOADS["llama3_8b_bf16"], num_seqs=4, len_range=(512, 2100)),
+    "llama70b_f16_small": scaled(WORKLOADS["llama70b_f16_80l"], num_layers=2, num_seqs=3),
+    "mha13b_prefix_small": scaled(WORKLOADS["mha13b_prefix_f16"], num_seqs=6),
+    "long_fp8_small": scaled(WORKLOADS["long_fp8"], num_seqs=2, len_range=(8192, 8192)),
+    "ragged_f16_g8_d128": _ragged("r1", "f16", "f16", "f16", 128, 8, RAGGED, 1),
+    "ragged_bf16_g4_d64": _ragged("r2", "bf16", "bf16", "bf16", 64, 4, RAGGED, 2),
+    "ragged_f32_g8_d128": _ragged("r3", "f32", "f32", "f32", 128, 8, RAGGED, 3),
+    "ragged_f16_g2_d64": _ragged("r4", "f16", "f16", "f16", 64, 2, RAGGED, 4),
+    "ragged_f32_g1_d64": _ragged("r5", "f32", "f32", "f32", 64, 1, RAGGED, 5),
+    "ragged_fp8_g8_d64_f32out": _ragged("r6", "fp8_e4m3", "bf16", "f32", 64, 8, RAGGED, 6),
+    "ragged_fp8_g1_d128_f16": _ragged("r7", "fp8_e4m3", "f16", "f16", 128, 1, RAGGED, 7),
+    "ragged_fp8_g2_d128_f32": _ragged("r8", "fp8_e4m3", "f32", "f32", 128, 2, RAGGED, 8),
+    "ragged_bf16_g8_d128_append": _ragged("r9", "bf16", "bf16", "bf16", 128, 8,
+                                          [1, 16, 17, 200, 33, 48, 49], 9, hkv=3, append=True),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_decode_matches_oracle(name):
+    spec = SMALL[name]
+    lay = build_layout(spec)
+    say(f"[decode] {name}: B={spec.num_seqs} Hq={spec.num_q_heads} Hkv={spec.num_kv_heads} "
+        f"D={spec.head_dim} kv={spec.kv_dtype} lens={list(lay.context_lens[:12])}")
+    x = make_host_inputs(lay)
+    xs = _to_dev(x)
+    tol = TOL[spec.kv_dtype]
+    for layer in range(spec.num_layers):
+        out = _out(spec)
+        run_step(xs, layer, spec, out)
+        torch.cuda.synchronize()
+        got = out_f64(out)
+        ref = oracle_rows(host_layer(x, layer), lay, spec)
+        assert np.isfinite(got).all()
+        err = max_err(got, ref)
+        say(f"    layer {layer}: max|err| = {err:.3e} (tol {tol})")
+        assert err <= tol
+        zero = lay.context_lens == 0
+        assert (got[zero] == 0).all()
+
+
+@pytest.mark.parametrize("pb", [1, 2, 3, 7])
+def test_split_size_invariance(pb):
+    say(f"[split] tiny_f32 partition_blocks={pb}")
+    spec = WORKLOADS["tiny_f32"]
+    lay = build_layout(spec)
+    x = make_host_inputs(lay)
+    xs = _to_dev(x)
+    whole = _out(spec)
+    run_step(xs, 0, spec, whole, partition_blocks=1000)
+    split = _out(spec)
+    run_step(xs, 0, spec, split, partition_blocks=pb, append=False)
+    torch.cuda.synchronize()
+    ref = oracle_rows(host_layer(x, 0), lay, spec)
+    assert max_err(out_f64(split), ref) <= 1e-5
+    assert max_err(out_f64(split), out_f64(whole)) <= 2e-6
+
+
+def test_shared_prefix_is_bit_identical_to_private_copies():
+    """Same values, once shared (refcount 6) and once copied into private
+    blocks: the kernel must give bit-identical outputs."""
+    spec = SMALL["mha13b_prefix_small"]
+    say("[prefix] shared vs private copies")
+    lay = build_layout(spec)
+    x = make_host_inputs(lay)
+    pb = spec.shared_prefix_tokens // 16
+    kc, vc = x["k_cache"][0], x["v_cache"][0]
+    NB = kc.shape[0]
+    extra = (spec.num_seqs - 1) * pb
+    kc2 = torch.cat([kc, torch.empty((extra,) + kc.shape[1:], dtype=kc.dtype)])
+    vc2 = torch.cat([vc, torch.empty((extra,) + vc.shape[1:], dtype=vc.dtype)])
+    tables2 = lay.block_tables.copy()
+    nxt = NB
+    for b in range(1, spec.num_seqs):
+        for j in range(pb):
+            src = lay.block_tables[b, j]
+            kc2[nxt], vc2[nxt] = kc[src], vc[src]
+            tables2[b, j] = nxt
+            nxt += 1
+    assert len(np.unique(tables2[tables2 >= 0])) == (tables2 >= 0).sum()
+    outs = []
+    for k_, v_, t_ in ((kc, vc, lay.block_tables), (kc2, vc2, tables2)):
+        out = _out(spec)
+        pkv.paged_decode_attn(x["q"][0].to(DEV), k_.to(DEV), v_.to(DEV),
+                              torch.from_numpy(t_).to(DEV), x["context_lens"].to(DEV),
+                              spec.scale, out)
+        outs.append(out.cpu())
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+def test_deterministic_run_to_run():
+    spec = SMALL["llama3_8b_bf16_small"]
+    say("[determinism] two identical calls")
+    lay = build_layout(spec)
+    xs = _to_dev(make_host_inputs(lay))
+    a, b = _out(spec), _out(spec)
+    run_step(xs, 0, spec, a)
+    run_step(xs, 0, spec, b)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_fp8_all_codes_decode_through_attention():
+    """With one token, out = V: every e4m3 code (scale 1) comes out exactly
+    as the OCP decoding (NaN codes as NaN)."""
+    say("[fp8] 256 codes through a length-1 attention")
+    D = 128
+    codes = np.arange(256, dtype=np.uint8).reshape(2, D)
+    vc = np.zeros((4, 1, 16, D), np.uint8)
+    vc[1, 0, 0] = codes[0]
+    vc[3, 0, 0] = codes[1]
+    kc = np.full((4, 1, 16, D), 0x38, np.uint8)
+    tables = np.array([[1], [3]], np.int32)
+    lens = np.array([1, 1], np.int32)
+    q = torch.randn((2, 1, D), device=DEV)
+    out = torch.empty((2, 1, D), device=DEV)
+    ones = torch.ones((4, 1), device=DEV)
+    pkv.paged_decode_attn(q, torch.from_numpy(kc).to(DEV), torch.from_numpy(vc).to(DEV),
+                          torch.from_numpy(tables).to(DEV), torch.from_numpy(lens).to(DEV), 0.1, out,
+                          k_scales=ones, v_scales=ones)
+    got = out.cpu().numpy()[:, 0, :].astype(np.float64)
+    ref = oracle.decode_e4m3fn(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+
+
+def test_block_ids_outside_pool_are_ignored():
+    say("[bounds] table entries outside the pool")
+    D, NB = 64, 3
+    kc = torch.randn((NB, 1, 16, D), device=DEV)
+    q = torch.randn((2, 4, D), device=DEV)
+    tables = torch.tensor([[-7, NB + 1], [0, 1]], dtype=torch.int32, device=DEV)
+    lens = torch.tensor([20, 20], dtype=torch.int32, device=DEV)
+    out = torch.empty_like(q)
+    pkv.paged_decode_attn(q, kc, kc, tables, lens, 0.125, out)
+    torch.cuda.synchronize()
+    assert (out[0] == 0).all() and torch.isfinite(out[1]).all()
+
+
+# --------------------------------------------------------------------------
+# full-size workloads (the bench's launch configuration), sampled rows
+# --------------------------------------------------------------------------
+
+def _compact_rows(x, layer, lay, seqs):
+    """Host copies of just the blocks `seqs` use, with tables remapped."""
+    nblk = -(-lay.context_lens // 16)
+    used = np.unique(np.concatenate([lay.block_tables[b, : nblk[b]] for b in seqs]))
+    remap = {int(o): i for i, o in enumerate(used)}
+    idx = torch.from_numpy(used.astype(np.int64)).to(DEV)
+    h = {"q": host_storage(x["q"][layer]),
+         "k_cache": host_storage(x["k_cache"][layer].index_select(0, idx)),
+         "v_cache": host_storage(x["v_cache"][layer].index_select(0, idx))}
+    if "k_scales" in x:
+        h["k_scales"] = host_storage(x["k_scales"][layer].index_select(0, idx))
+        h["v_scales"] = host_storage(x["v_scales"][layer].index_select(0, idx))
+    tables = np.full_like(lay.block_tables, -1)
+    for b in seqs:
+        tables[b, : nblk[b]] = [remap[int(o)] for o in lay.block_tables[b, : nblk[b]]]
+    slots = None
+    if lay.slot_mapping is not None:
+        h["k_new"] = host_storage(x["k_new"][layer])
+        h["v_new"] = host_storage(x["v_new"][layer])
+        slots = np.full_like(lay.slot_mapping, -1)
+        for b in seqs:
+            s = int(lay.slot_mapping[b])
+            slots[b] = remap[s // 16] * 16 + s % 16
+    return h, tables, slots
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_bf16", "mha13b_prefix_f16", "long_fp8", "llama70b_f16_80l"])
+def test_full_size_sampled_rows(name):
+    spec = WORKLOADS[name]
+    lay = build_layout(spec)
+    say(f"[full] {name}: B={spec.num_seqs} layers={spec.num_layers} blocks={lay.num_blocks} "
+        f"partitions={pkv.decode_num_partitions(pkv.DecodeDims(spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, 16, lay.num_blocks, lay.max_blocks_per_seq, 0, 0, 0, 0))}")
+    x = make_device_inputs(lay, DEV)
+    rng = np.random.default_rng(spec.seed)
+    layers = sorted({0, spec.num_layers // 2, spec.num_layers - 1})
+    seqs = sorted(rng.choice(spec.num_seqs, size=min(3, spec.num_seqs), replace=False).tolist())
+    heads = sorted(rng.choice(spec.num_q_heads, size=min(4, spec.num_q_heads), replace=False).tolist())
+    snaps = {l: _compact_rows(x, l, lay, seqs) for l in layers}        # before the step writes
+    outs = {}
+    for layer in range(spec.num_layers):                               # the whole step
+        out = _out(spec)
+        run_step(x, layer, spec, out)
+        if layer in snaps:
+            outs[layer] = out
+    torch.cuda.synchronize()
+    tol = TOL[spec.kv_dtype]
+    for layer in layers:
+        h, tables, slots = snaps[layer]
+        kc, vc = h["k_cache"], h["v_cache"]
+        if slots is not None:
+            kc = oracle.kv_append_bits(kc, h["k_new"], slots)
+            vc = oracle.kv_append_bits(vc, h["v_new"], slots)
+        ref = oracle.paged_decode_attention(h["q"], kc, vc, tables, lay.context_lens, spec.scale,
+                                            q_tag=spec.q_dtype, kv_tag=spec.kv_dtype,
+                                            k_scales=h.get("k_scales"), v_scales=h.get("v_scales"),
+                                            seqs=seqs, q_heads=heads)
+        got = out_f64(outs[layer])[seqs][:, heads]
+        err = max_err(got, ref)
+        say(f"    layer {layer} seqs {seqs} heads {heads}: max|err| = {err:.3e} (tol {tol})")
+        assert err <= tol
+        assert torch.isfinite(outs[layer].float()).all()
+    del x
+    torch.cuda.empty_cache()
