@@ -68,6 +68,16 @@ struct Cfg {
   static constexpr int NF = NS >> NRS;                     // slots left after it
   static constexpr int EL = E * VPT;                       // elements per lane per token
   static constexpr int NW = 4;                             // waves per workgroup
+  static constexpr int LPB = TPL * VPT;                    // 16-byte loads per lane per tile
+  static constexpr int TILE_B = 16 * D * EB;               // bytes of one (block, kv_head) tile
+  static constexpr int STAGE_B = 2 * TILE_B;               // K tile + V tile
+  // per-wave ring of staged blocks in LDS: about 16 KiB per wave, >= 2 stages
+  static constexpr int NBUF = (16384 / STAGE_B) >= 2 ? (16384 / STAGE_B) : 2;
+  static constexpr int RING_B = NW * NBUF * STAGE_B;
+  static constexpr int RED_B = NW * G * (D + 2) * 4;       // end-of-partition combine
+  static constexpr int SMEM_B = RING_B > RED_B ? RING_B : RED_B;
+  static_assert(LPB * 64 * 16 == TILE_B, "a tile is LPB wave-wide 16-byte loads");
+  static_assert(2 * LPB * (NBUF - 1) <= 63, "vmcnt range");
   static_assert(LPT >= 1 && LPT <= 16 && (LPT & (LPT - 1)) == 0, "lanes per token");
   static_assert(TPL >= 1, "tokens per lane");
 };
@@ -168,9 +178,15 @@ __device__ __forceinline__ float qk_partial(const QSlice<KT, EL>& qs, const TokW
     for (int v = 0; v < VPT; ++v) {
       const uint32_t w[4] = {t.x[v].x, t.x[v].y, t.x[v].z, t.x[v].w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qs.w[v * 4 + k]),
-                                   __builtin_bit_cast(half2_t, w[k]), s, false);
+      for (int k = 0; k < 4; ++k) {
+        if (v == 0 && k == 0) {
+          // three-operand form with an inline zero: no register to clear
+          asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(s) : "v"(qs.w[0]), "v"(w[0]));
+        } else {
+          s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qs.w[v * 4 + k]),
+                                     __builtin_bit_cast(half2_t, w[k]), s, false);
+        }
+      }
     }
   } else if constexpr (KT == KV::BF16) {
 #pragma unroll
@@ -209,12 +225,16 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
   constexpr int LEVELS = C::LEVELS;
   constexpr int TILE = 16 * D;  // elements per (block, kv_head) tile
 
-  __shared__ float red_m[NW][G];
-  __shared__ float red_l[NW][G];
-  __shared__ float red_acc[NW][G][D];
+  // LDS: while streaming, a ring of NBUF staged blocks per wave; at the end
+  // of the partition the same bytes hold the per-wave partial results.
+  __shared__ __attribute__((aligned(16))) char smem[C::SMEM_B];
+  float (*red_acc)[G][D] = reinterpret_cast<float (*)[G][D]>(smem);
+  float (*red_m)[G] = reinterpret_cast<float (*)[G]>(smem + NW * G * D * 4);
+  float (*red_l)[G] = reinterpret_cast<float (*)[G]>(smem + NW * G * D * 4 + NW * G * 4);
 
   const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int Hq = a.num_kv_heads * G;
 
   int L = a.context_lens[b];
@@ -262,7 +282,11 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
 
   const char* kbase = (const char*)a.k_cache;
   const char* vbase = (const char*)a.v_cache;
-  const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
+  // The table is read-only for the whole kernel: reading it through the
+  // constant address space makes every entry a scalar load (lgkmcnt), which
+  // never waits behind the in-flight tile copies (vmcnt).
+  const __attribute__((address_space(4))) int32_t* table =
+      (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)b * a.max_blocks);
   // byte offset of this lane's words inside a tile, per register token/load
   int lane_off[TPL][VPT];
 #pragma unroll
@@ -271,17 +295,44 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     for (int v = 0; v < VPT; ++v)
       lane_off[i][v] = (((i ^ tmask) * R + r) * D + (v * LPT + c) * E) * C::EB;
 
-  auto load_block = [&](int j, TokWords<VPT> (&kr)[TPL], TokWords<VPT> (&vr)[TPL]) {
+  constexpr int LPB = C::LPB, STAGE_B = C::STAGE_B, NBUF = C::NBUF;
+  const uint32_t ring = lds_offset(smem) + (uint32_t)(w * NBUF * STAGE_B);
+  // Start the copy of block j's K and V tiles into ring stage `st`.
+  auto issue_block = [&](int j, int st) {
     int phys = table[j];
     phys = ((unsigned)phys < (unsigned)a.num_blocks) ? phys : 0;
-    const int64_t tile = ((int64_t)phys * a.num_kv_heads + h) * TILE * C::EB;
+    const int64_t tile = ((int64_t)phys * a.num_kv_heads + h) * (int64_t)C::TILE_B;
+    const char* kt = kbase + tile;
+    const char* vt = vbase + tile;
+    const uint32_t dst = ring + (uint32_t)(st * STAGE_B);
+#pragma unroll
+    for (int i = 0; i < TPL; ++i)
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) lds_dma16(kt, (uint32_t)lane_off[i][v], dst + (i * VPT + v) * 1024);
+#pragma unroll
+    for (int i = 0; i < TPL; ++i)
+#pragma unroll
+      for (int v = 0; v < VPT; ++v)
+        lds_dma16(vt, (uint32_t)lane_off[i][v], dst + C::TILE_B + (i * VPT + v) * 1024);
+  };
+  // Registers <- the lane's own 16-byte pieces of stage `st`.
+  auto read_stage = [&](int st, TokWords<VPT> (&kr)[TPL], TokWords<VPT> (&vr)[TPL]) {
+    const char* src = smem + (w * NBUF + st) * STAGE_B + lane * 16;
 #pragma unroll
     for (int i = 0; i < TPL; ++i)
 #pragma unroll
       for (int v = 0; v < VPT; ++v) {
-        kr[i].x[v] = *(const uint4*)(kbase + tile + lane_off[i][v]);
-        vr[i].x[v] = *(const uint4*)(vbase + tile + lane_off[i][v]);
+        kr[i].x[v] = *(const uint4*)(src + (i * VPT + v) * 1024);
+        vr[i].x[v] = *(const uint4*)(src + C::TILE_B + (i * VPT + v) * 1024);
       }
+  };
+  // Wait until at most `later` stages' copies are still in flight.
+  auto wait_stages = [&](int later) {
+    constexpr int PER = 2 * LPB;
+    if constexpr (NBUF > 3) { if (later >= 3) { wait_vmcnt<(NBUF > 3 ? 3 : 0) * PER>(); return; } }
+    if constexpr (NBUF > 2) { if (later >= 2) { wait_vmcnt<(NBUF > 2 ? 2 : 0) * PER>(); return; } }
+    if (later >= 1) { wait_vmcnt<PER>(); return; }
+    wait_vmcnt<0>();
   };
 
   auto compute_block = [&](int j, const TokWords<VPT> (&kr)[TPL], const TokWords<VPT> (&vr)[TPL]) {
@@ -398,24 +449,24 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     }
   };
 
-  // software pipeline: the next block's loads are in flight during compute
+  // Pipeline: the wave's blocks are j0 + w, j0 + w + NW, ...; up to NBUF of
+  // them are being copied into the ring while one is computed from registers.
   {
-    int j = j0 + w;
-    if (j < j1) {
-      TokWords<VPT> ka[TPL], va[TPL], kb[TPL], vb[TPL];
-      load_block(j, ka, va);
-      while (true) {
-        if (j + NW < j1) load_block(j + NW, kb, vb);
-        compute_block(j, ka, va);
-        j += NW;
-        if (j >= j1) break;
-        if (j + NW < j1) load_block(j + NW, ka, va);
-        compute_block(j, kb, vb);
-        j += NW;
-        if (j >= j1) break;
-      }
+    const int first = j0 + w;
+    const int n_my = first < j1 ? (j1 - first + NW - 1) / NW : 0;
+    for (int t = 0; t < NBUF && t < n_my; ++t) issue_block(first + t * NW, t);
+    for (int t = 0; t < n_my; ++t) {
+      const int st = t % NBUF;
+      const int later = min(NBUF - 1, n_my - 1 - t);
+      wait_stages(later);
+      TokWords<VPT> kr[TPL], vr[TPL];
+      read_stage(st, kr, vr);
+      wait_lgkmcnt0();  // the stage is in registers: its buffer may be refilled
+      if (t + NBUF < n_my) issue_block(first + (t + NBUF) * NW, st);
+      compute_block(first + t * NW, kr, vr);
     }
   }
+  __syncthreads();  // every wave is done with its ring: the LDS is reused below
 
   // ---- combine: lanes of a row -> rows of a wave -> waves of the group ----
   // per-head sum of probabilities over the row

@@ -28,11 +28,39 @@ constexpr int DPP_QUAD_XOR2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int DPP_ROW_ROR8 = 0x128;      // row_ror:8  (lane c <-> c ^ 8)
 constexpr int DPP_ROW_HALF_MIRROR = 0x141;  // lane c <-> 7 - c inside each 8
 
+// Every control used here reads a valid lane for every lane, so the "old"
+// operand is never selected (bound_ctrl set: no register needs priming).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
+
+// ---- asynchronous global -> LDS copies (gfx950 LDS DMA) --------------------
+// One instruction moves 16 bytes per lane from `gbase + voff` (per lane) into
+// LDS at `lds + 16 * lane`.  The copy is tracked by vmcnt only, so the waits
+// below are explicit; the compiler is told nothing about the LDS write except
+// a memory clobber, which keeps LDS reads from moving across these points.
+__device__ __forceinline__ void lds_dma16(const void* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(gbase), "s"(lds)
+      : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
+
+// LDS byte offset of a __shared__ object (the low half of its flat address).
+__device__ __forceinline__ uint32_t lds_offset(const void* p) { return (uint32_t)(uintptr_t)p; }
 
 // ---- conversions ----------------------------------------------------------
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
