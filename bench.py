@@ -30,6 +30,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+CALIB_COPY_BYTES = 512 * 2**20
+CALIB_COPY_KERNEL = "__amd_rocclr_copyBuffer"
+PROBE_KERNEL = "pkv::hbm_read_kernel"
+ATTN_KERNEL = "pkv::decode_partition_kernel"
+CSRC = os.path.join(ROOT, "paged_kv_cache_56_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 METRIC = "paged decode attention KV GB/s and % of MI355X HBM peak (1 GPU)"
 ELT = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
 
@@ -55,7 +61,8 @@ def attention_bytes(spec, lay):
 
 
 def cpu_baseline(spec, lay, x, budget_s: float):
-    """Time the oracle on whole sequences of layer 0 until ~budget_s of CPU work."""
+    """Time the oracle on whole sequences (layer 0, then layer 1, ...) until
+    about budget_s seconds of CPU work have been spent."""
     import numpy as np
     import torch
 
@@ -71,25 +78,26 @@ def cpu_baseline(spec, lay, x, budget_s: float):
 
     nblk = -(-lay.context_lens.astype(int) // 16)
     done_bytes, elapsed, seqs = 0, 0.0, 0
+    order = [(layer, b) for layer in range(spec.num_layers) for b in range(spec.num_seqs)]
     with threadpool_limits(limits=cores):
-        for b in range(spec.num_seqs):
+        for layer, b in order:
             used = lay.block_tables[b, : nblk[b]].astype(np.int64)
             idx = torch.from_numpy(used).to(dev)
-            kc = host(x["k_cache"][0].index_select(0, idx))
-            vc = host(x["v_cache"][0].index_select(0, idx))
+            kc = host(x["k_cache"][layer].index_select(0, idx))
+            vc = host(x["v_cache"][layer].index_select(0, idx))
             table = np.arange(len(used), dtype=np.int32)[None, :]
             lens = lay.context_lens[b : b + 1]
-            q = host(x["q"][0][b : b + 1])
+            q = host(x["q"][layer][b : b + 1])
             kw = {}
             if "k_scales" in x:
-                kw = dict(k_scales=host(x["k_scales"][0].index_select(0, idx)),
-                          v_scales=host(x["v_scales"][0].index_select(0, idx)))
+                kw = dict(k_scales=host(x["k_scales"][layer].index_select(0, idx)),
+                          v_scales=host(x["v_scales"][layer].index_select(0, idx)))
             t0 = time.perf_counter()
             if spec.append:
                 s = int(lay.slot_mapping[b])
                 slot = np.array([int(np.nonzero(used == s // 16)[0][0]) * 16 + s % 16])
-                kc = oracle.kv_append_bits(kc, host(x["k_new"][0][b : b + 1]), slot)
-                vc = oracle.kv_append_bits(vc, host(x["v_new"][0][b : b + 1]), slot)
+                kc = oracle.kv_append_bits(kc, host(x["k_new"][layer][b : b + 1]), slot)
+                vc = oracle.kv_append_bits(vc, host(x["v_new"][layer][b : b + 1]), slot)
             oracle.paged_decode_attention(q, kc, vc, table, lens, spec.scale, q_tag=spec.q_dtype,
                                           kv_tag=spec.kv_dtype, **kw)
             elapsed += time.perf_counter() - t0
@@ -102,10 +110,157 @@ def cpu_baseline(spec, lay, x, budget_s: float):
         "unit": "GB/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"float64 numpy oracle (append + attention), layer 0, {seqs} of "
-                  f"{spec.num_seqs} sequences, all {spec.num_q_heads} query heads; "
+        "sample": f"float64 numpy oracle (append + attention) on {seqs} (layer, sequence) pairs "
+                  f"of {spec.num_layers * spec.num_seqs}, all {spec.num_q_heads} query heads each; "
                   f"{done_bytes / 1e9:.3f} GB of K/V in {elapsed:.1f} s",
     }
+
+
+def read_probe(dev, gib: int = 4):
+    """Plain streaming read (the library's hbm_read_probe) over `gib` GiB: the
+    rate a read-only kernel gets from HBM on this device.  Best of a few grid
+    sizes.  Also runs one 512 MiB device copy, a kernel of known traffic (512
+    MiB read + 512 MiB written) that counter runs use to scale FETCH_SIZE and
+    WRITE_SIZE."""
+    import torch
+
+    import paged_kv_cache_56_amd as pkv
+
+    buf = torch.empty(gib * 2**30, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    best = 0.0
+    for wgs in (1024, 2048, 4096, 8192):
+        sink = torch.zeros(wgs, dtype=torch.int32, device=dev)
+        pkv.hbm_read_probe(buf, sink)            # warm
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            pkv.hbm_read_probe(buf, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, 5 * buf.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9)
+    del buf
+    src = torch.ones(CALIB_COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    return {"gbs": best, "bytes": gib * 2**30}
+
+
+def kernel_source_sha() -> str:
+    """sha256 over the HIP sources and headers the library is built from."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for fn in sorted(os.listdir(CSRC)):
+        if fn.endswith((".hip", ".h", ".cpp")):
+            h.update(fn.encode())
+            h.update(open(os.path.join(CSRC, fn), "rb").read())
+    h.update(open(os.path.join(ROOT, "include", "pagedkv.h"), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _csv_rows(path):
+    import csv
+
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_counters(fetch_csv, write_csv, stats_csv, workload, probe_gib, out_md, command):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench plus
+    its --kernel-trace --stats run into the traffic summary bench.py reports.
+
+    Scale factors come from kernels of known traffic in the same runs: the
+    read probe (probe_gib GiB read) for FETCH_SIZE and a 512 MiB copy for
+    WRITE_SIZE (and as a FETCH_SIZE cross-check)."""
+    import statistics
+
+    def per_kernel(rows, counter):
+        d = {}
+        for r in rows:
+            if r["Counter_Name"] == counter:
+                d.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return d
+
+    fetch = per_kernel(_csv_rows(fetch_csv), "FETCH_SIZE")
+    write = per_kernel(_csv_rows(write_csv), "WRITE_SIZE")
+    pick = lambda d, key: [v for k, vals in d.items() if k.startswith(key) or key in k for v in vals]
+    probe_f = max(pick(fetch, PROBE_KERNEL))
+    copy_f = max(pick(fetch, CALIB_COPY_KERNEL))
+    copy_w = max(pick(write, CALIB_COPY_KERNEL))
+    fetch_scale = probe_gib * 2**30 / probe_f
+    write_scale = CALIB_COPY_BYTES / copy_w
+    attn_f = statistics.mean(pick(fetch, ATTN_KERNEL)) * fetch_scale
+    attn_w = statistics.mean(pick(write, ATTN_KERNEL)) * write_scale
+    stats = [r for r in _csv_rows(stats_csv)]
+    top = sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:6]
+    attn = [r for r in stats if ATTN_KERNEL in r["Name"]]
+    rec = {
+        "workload": workload,
+        "kernel": ATTN_KERNEL,
+        "kernel_source_sha": kernel_source_sha(),
+        "fetch_bytes_per_launch": round(attn_f),
+        "write_bytes_per_launch": round(attn_w),
+        "traffic_bytes_per_launch": round(attn_f + attn_w),
+        "fetch_scale": round(fetch_scale, 4),
+        "fetch_scale_check_copy": round(CALIB_COPY_BYTES / copy_f, 4),
+        "write_scale": round(write_scale, 4),
+        "trace_mean_launch_us": round(float(attn[0]["AverageNs"]) / 1e3, 2) if attn else None,
+        "trace_calls": int(attn[0]["Calls"]) if attn else 0,
+    }
+    lines = [
+        f"# {ATTN_KERNEL} on {workload}: rocprofv3 summary",
+        "",
+        "Commands (run from the repository root on one MI355X, `export TMPDIR=/tmp`):",
+        "",
+        "```",
+        *command,
+        "```",
+        "",
+        "## Kernel trace (--kernel-trace --stats), top kernels by total time",
+        "",
+        "| kernel | calls | mean us | min us | max us | share |",
+        "|---|---|---|---|---|---|",
+    ]
+    for r in top:
+        name = r["Name"].replace("|", "/")
+        name = name if len(name) < 90 else name[:87] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    lines += [
+        "",
+        "## HBM traffic (--pmc FETCH_SIZE, --pmc WRITE_SIZE; one run each)",
+        "",
+        f"FETCH_SIZE reads {probe_f / 2**30:.3f} GiB for the read probe that reads {probe_gib} GiB "
+        f"(scale {fetch_scale:.4f}); the 512 MiB copy gives {CALIB_COPY_BYTES / copy_f:.4f}.  "
+        f"WRITE_SIZE reads {copy_w / 2**20:.1f} MiB for the 512 MiB copy (scale {write_scale:.4f}).",
+        "",
+        "```json",
+        json.dumps(rec, indent=1),
+        "```",
+    ]
+    os.makedirs(os.path.dirname(out_md), exist_ok=True)
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return rec
+
+
+def traffic_for(workload: str):
+    """Counter-measured bytes per attention launch, if taken on these sources."""
+    import re
+
+    path = os.path.join(PROFILES, f"decode_partition_kernel__{workload}.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), flags=re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return rec
 
 
 def main():
@@ -116,7 +271,18 @@ def main():
     ap.add_argument("--workload", default="llama70b_f16_80l")
     ap.add_argument("--partition-blocks", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="0 skips the CPU baseline")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the plain-read bandwidth probe and the copy used to calibrate counters")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "STATS_CSV"),
+                    help="write profiles/decode_partition_kernel__<workload>.md from rocprofv3 output and exit")
+    ap.add_argument("--command", action="append", default=[],
+                    help="(with --summarize-counters) a command line to record in the summary")
     args = ap.parse_args()
+    if args.summarize_counters:
+        out = os.path.join(PROFILES, f"decode_partition_kernel__{args.workload}.md")
+        rec = summarize_counters(*args.summarize_counters, args.workload, 4, out, args.command)
+        print(json.dumps(rec))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
@@ -182,8 +348,15 @@ def main():
     value = kv_bytes * nl / (ms_per_step / 1e3) / 1e9
     achieved = alg_bytes / mean_launch_s / 1e9
     kernel = "decode_partition_kernel" + ("+lse_merge_kernel" if nparts > 1 else "")
+    trec = traffic_for(spec.name) if nparts == 1 else None
+    traffic = None if trec is None else trec["traffic_bytes_per_launch"]
     log(f"[bench] {ms_per_step:.3f} ms/step; attention launch {mean_launch_s * 1e6:.1f} us "
         f"-> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of peak)")
+
+    probe = None
+    if not args.no_probe:
+        probe = read_probe(dev)
+        log(f"[bench] plain read probe: {probe['gbs']:.0f} GB/s over {probe['bytes'] / 2**30:.0f} GiB")
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -222,9 +395,13 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "bytes_per_launch": alg_bytes,
             "mean_launch_us": round(mean_launch_s * 1e6, 2),
+            "traffic_over_algorithmic": None if traffic is None else round(traffic / alg_bytes, 4),
+            "kernel_source_sha": kernel_source_sha(),
+            "read_probe_gbs": None if probe is None else round(probe["gbs"], 1),
+            "frac_of_read_probe": None if probe is None else round(achieved / probe["gbs"], 4),
         },
         "cpu_baseline": cpu,
     }

@@ -141,6 +141,18 @@ PKV_API int pkv_paged_decode_attn_fp8(const void* q, const void* k_cache, const 
                               float scale, void* out, const pkv_decode_dims* dims,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Bandwidth reference ("KV Cache from first principles" 4.1: decode time is
+ * set by the bytes moved).  Reads the first `bytes` (rounded down to a
+ * multiple of 16) of device buffer `buf` once with 16-byte loads, using
+ * `sink_words` workgroups; each workgroup XORs what it read into
+ * sink[workgroup] (device, caller-zeroed if the value matters).  The rate
+ * of this call is what a read-only kernel achieves on the device.
+ * Errors: NULL buf/sink with bytes >= 16, sink_words < 1 -> status.
+ */
+PKV_API int pkv_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t sink_words,
+                               hipStream_t stream);
+
 /* Static text for a status code. */
 PKV_API const char* pkv_status_string(int status);
 

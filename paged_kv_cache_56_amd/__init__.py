@@ -28,6 +28,7 @@ __all__ = [
     "decode_dims",
     "decode_workspace_bytes",
     "decode_num_partitions",
+    "hbm_read_probe",
     "DTYPE_CODES",
     "BLOCK_SIZE",
 ]
@@ -97,6 +98,8 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_paged_decode_attn_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
                                               dims_p, vp, sz, vp]
     lib.pkv_paged_decode_attn_fp8.restype = ctypes.c_int
+    lib.pkv_hbm_read_probe.argtypes = [vp, sz, vp, i32, vp]
+    lib.pkv_hbm_read_probe.restype = ctypes.c_int
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_version.argtypes = []
@@ -178,6 +181,14 @@ def decode_num_partitions(dims: DecodeDims) -> int:
     n = load_library().pkv_decode_num_partitions(ctypes.byref(dims))
     _check(min(n, 0))
     return n
+
+
+def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Read every byte of `buf` once (bandwidth reference); sink: int32 [W] on the device."""
+    _dev(buf, sink)
+    _need(sink.dtype == torch.int32 and sink.dim() == 1, "sink must be int32 [workgroups]")
+    _check(load_library().pkv_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                             sink.numel(), _stream(buf)))
 
 
 def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

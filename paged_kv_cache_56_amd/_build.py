@@ -22,7 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libpagedkv.so")
-SOURCES = ["api.cpp", "kv_append.hip", "decode_attn.hip"]
+SOURCES = ["api.cpp", "kv_append.hip", "decode_attn.hip", "hbm_probe.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

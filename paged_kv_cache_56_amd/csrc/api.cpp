@@ -142,6 +142,14 @@ int pkv_paged_decode_attn_fp8(const void* q, const void* k_cache, const void* v_
                        out, dims, workspace, workspace_bytes, stream, true);
 }
 
+int pkv_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t sink_words,
+                       hipStream_t stream) {
+  if (sink_words < 1 || sink_words > 0x7FFFFFFF / 256) return PKV_ERR_SHAPE;
+  if (bytes < 16) return PKV_OK;
+  if (!buf || !sink) return PKV_ERR_NULL;
+  return launch_hbm_read(buf, bytes, sink, sink_words, stream);
+}
+
 const char* pkv_status_string(int status) {
   switch (status) {
     case PKV_OK: return "ok";

@@ -588,10 +588,12 @@ void plan_partitions(const pkv_decode_dims& d, int* part_blocks, int* num_parts)
   if (d.partition_blocks > 0) {
     pb = d.partition_blocks;
   } else {
-    // aim for >= 1024 workgroups (4 per CU on 256 CUs), but never split
-    // below 16 blocks (256 tokens) per partition
+    // Aim for about 512 workgroups: two per CU on 256 CUs, which is what the
+    // LDS ring allows resident at once.  Each extra split costs a workspace
+    // round trip and shortens the streaming loop, so split no further than
+    // that, and never below 16 blocks (256 tokens) per partition.
     const int64_t units = (int64_t)d.num_seqs * d.num_kv_heads;
-    int64_t want = (1024 + units - 1) / units;
+    int64_t want = (512 + units - 1) / units;
     if (want < 1) want = 1;
     pb = (int)((maxb + want - 1) / want);
     if (pb < 16) pb = 16;

@@ -33,4 +33,7 @@ size_t workspace_bytes_for(const pkv_decode_dims& d);
 
 int launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+int launch_hbm_read(const void* buf, size_t bytes, uint32_t* sink, int sink_words,
+                    hipStream_t stream);
+
 }  // namespace pkv

@@ -76,12 +76,13 @@ def test_attn_status_codes(kw, status):
 
 def test_attn_null_and_workspace():
     assert _attn(_dims(), q=None) == -1
-    d = _dims()                            # 64 x 8 units -> split in two
+    d = _dims(num_seqs=16)                 # 16 x 8 units -> split in four
     need = pkv.decode_workspace_bytes(d)
-    assert need == 64 * 64 * 2 * (128 + 2) * 4
+    assert need == 16 * 64 * 4 * (128 + 2) * 4
     assert _attn(d, ws=None, ws_bytes=0) == -4
     assert _attn(d, ws=FAKE, ws_bytes=need - 1) == -4
-    assert _attn(_dims(), ws=FAKE, ws_bytes=need - 4) == -4
+    assert _attn(_dims(num_seqs=16), ws=FAKE, ws_bytes=need - 4) == -4
+    assert pkv.decode_workspace_bytes(_dims()) == 0     # 512 units: no split
 
 
 def test_fp8_status_codes():
@@ -105,11 +106,12 @@ def test_append_status_codes():
 
 
 @pytest.mark.parametrize("B,Hkv,maxb,parts", [
-    (64, 8, 256, 2),        # 70B-shaped step
-    (8, 8, 8192, 16),       # 131072-token fp8 case
+    (64, 8, 256, 1),        # 70B-shaped step
+    (8, 8, 8192, 8),        # 131072-token fp8 case
     (64, 40, 100, 1),       # MHA prefix batch
     (4, 2, 7, 1),           # tiny
-    (32, 8, 498, 4),        # Llama-3-8B layer
+    (32, 8, 498, 2),        # Llama-3-8B layer
+    (2, 2, 300, 19),        # few units: split down to 16-block partitions
 ])
 def test_partition_plan(B, Hkv, maxb, parts):
     d = _dims(num_seqs=B, num_kv_heads=Hkv, num_q_heads=Hkv * 4, max_blocks_per_seq=maxb)

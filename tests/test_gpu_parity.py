@@ -217,6 +217,21 @@ def test_block_ids_outside_pool_are_ignored():
     assert (out[0] == 0).all() and torch.isfinite(out[1]).all()
 
 
+def test_hbm_read_probe_reads_every_word():
+    """The bandwidth probe folds every 16-byte word into its workgroup's sink."""
+    say("[probe] plain read fold")
+    n16, W = 64 * 1024 + 5, 8
+    x = torch.randint(0, 2**31 - 1, (n16 * 4,), dtype=torch.int32, device=DEV)
+    sink = torch.zeros(W, dtype=torch.int32, device=DEV)
+    pkv.hbm_read_probe(x, sink)
+    torch.cuda.synchronize()
+    words = x.cpu().numpy().view(np.uint32).reshape(n16, 4)
+    f = words[:, 0] ^ words[:, 1] ^ words[:, 2] ^ words[:, 3]
+    wg = (np.arange(n16) % (W * 256)) // 256
+    exp = [int(np.bitwise_xor.reduce(f[wg == w])) for w in range(W)]
+    assert sink.cpu().numpy().view(np.uint32).tolist() == exp
+
+
 # --------------------------------------------------------------------------
 # full-size workloads (the bench's launch configuration), sampled rows
 # --------------------------------------------------------------------------
