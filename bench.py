@@ -47,17 +47,27 @@ def log(*a):
 def attention_bytes(spec, lay):
     """Algorithmic bytes of one attention launch (one layer).
 
-    K and V of every attended (token, KV head) once, plus q, out, the block
-    table entries and lengths read, and the fp8 scales of every attended
-    (block, KV head)."""
+    K and V of every attended (token, KV head) once -- a physical block that
+    several sequences share (a common prefix) is counted once, since the
+    method needs to stream it only once -- plus q, out, the block table
+    entries and lengths read, and the fp8 scales of every attended (block,
+    KV head).  Returns (K/V bytes, all algorithmic bytes, logical K/V bytes
+    counting shared blocks once per sequence)."""
     L = lay.context_lens.astype(int)
     nblk = -(-L // 16)
-    kv = int(L.sum()) * spec.num_kv_heads * spec.head_dim * ELT[spec.kv_dtype] * 2
+    per_token = spec.num_kv_heads * spec.head_dim * ELT[spec.kv_dtype] * 2
+    logical = int(L.sum()) * per_token
+    used = {}
+    for b in range(spec.num_seqs):
+        for j in range(int(nblk[b])):
+            blk = int(lay.block_tables[b, j])
+            used[blk] = max(used.get(blk, 0), min(16, int(L[b]) - 16 * j))
+    kv = sum(used.values()) * per_token
     q = spec.num_seqs * spec.num_q_heads * spec.head_dim * ELT[spec.q_dtype]
     out = spec.num_seqs * spec.num_q_heads * spec.head_dim * ELT[spec.out_dtype]
     meta = int(nblk.sum()) * 4 + spec.num_seqs * 4
     scales = int(nblk.sum()) * spec.num_kv_heads * 4 * 2 if spec.kv_dtype == "fp8_e4m3" else 0
-    return kv, kv + q + out + meta + scales
+    return kv, kv + q + out + meta + scales, logical
 
 
 def cpu_baseline(spec, lay, x, budget_s: float):
@@ -344,7 +354,7 @@ def main():
     launch_ms = np.array([[e[0].elapsed_time(e[1]) for e in row] for row in events])
     mean_launch_s = float(launch_ms.mean()) / 1e3
 
-    kv_bytes, alg_bytes = attention_bytes(spec, lay)
+    kv_bytes, alg_bytes, logical_bytes = attention_bytes(spec, lay)
     value = kv_bytes * nl / (ms_per_step / 1e3) / 1e9
     achieved = alg_bytes / mean_launch_s / 1e9
     kernel = "decode_partition_kernel" + ("+lse_merge_kernel" if nparts > 1 else "")
@@ -387,6 +397,7 @@ def main():
             "block_size": 16,
             "partitions": nparts,
             "kv_bytes_per_step": kv_bytes * nl,
+            "logical_kv_bytes_per_step": logical_bytes * nl,
         },
         "roofline": {
             "bound": "hbm",
