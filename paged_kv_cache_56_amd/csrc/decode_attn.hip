@@ -9,15 +9,20 @@
 // Decode is a matrix-vector product per KV head, bound by HBM: every K/V
 // byte is used by only g query heads.  The kernel therefore streams each
 // (block, kv_head) tile once from HBM and makes that one read serve all g
-// query heads, with fp32 vector arithmetic (packed dot2 for 16-bit K).
+// query heads.  Scores use packed dot2 for f16/bf16 K (and for fp8 K after
+// widening it to f16; the query is held in f16 after a power-of-two
+// rescale of the KV group that the scores undo), fp32 FMA for fp32 K.  P.V accumulates in
+// fp32: for f16 and fp8 V it is a dot2 over pairs of tokens with the
+// probabilities rounded once to f16 (relative error <= 2^-11 per weight);
+// bf16 and fp32 V use fp32 FMA.
 //
 // Work split.  Grid = (partition p, kv head h, sequence b); a workgroup of
 // four waves owns the blocks [p*PB, (p+1)*PB) of (b, h); wave w takes every
-// fourth of them.  Inside a wave, lane l covers token row r = l / LPT of
-// every tile and the 16-byte column c = l % LPT of that row, so one 16-byte
-// load per lane per (token row, column) reads a tile with fully contiguous
-// wave accesses, and each lane keeps its slice of all g query vectors in
-// registers for the whole partition.
+// fourth of them.  Tiles are copied by LDS DMA into a per-wave ring, each
+// copy reading 1 KiB contiguously.  Inside a wave, lane l then takes token
+// rows of group r = l / LPT of every tile and the 16-byte column c = l % LPT,
+// and keeps its slice of all g query vectors in registers for the whole
+// partition.
 //
 // Scores.  A lane's partial dot products (g heads x its tokens) are summed
 // over the LPT lanes of its row with a DPP reduce-scatter: at every level a
@@ -106,13 +111,12 @@ __device__ __forceinline__ int level_bit(int c) {
 }
 
 // ---- per-dtype pieces ------------------------------------------------------
-// Query slice held by a lane: QW words per head (packed pairs for 16-bit K,
-// fp32 otherwise).
-template <KV KT, int EL> struct QSlice;
-template <int EL> struct QSlice<KV::F16, EL> { uint32_t w[EL / 2]; };
-template <int EL> struct QSlice<KV::BF16, EL> { uint32_t w[EL / 2]; };
+// The lane's slice of one query vector, kept in registers for the whole
+// partition: packed 16-bit pairs when K is f16/bf16 (dot2 with K directly),
+// packed f16 pairs when K is fp8 (dot2 with K converted to f16), fp32 when K
+// is fp32.
+template <KV KT, int EL> struct QSlice { uint32_t w[EL / 2]; };
 template <int EL> struct QSlice<KV::F32, EL> { float f[EL]; };
-template <int EL> struct QSlice<KV::FP8, EL> { float f[EL]; };
 
 template <KV T>
 __device__ __forceinline__ float load_elem_f32(const void* base, int64_t idx) {
@@ -121,9 +125,17 @@ __device__ __forceinline__ float load_elem_f32(const void* base, int64_t idx) {
   else return __builtin_bit_cast(float, ((uint32_t)((const uint16_t*)base)[idx]) << 16);
 }
 
-// q row (already offset to the lane's head) -> the lane's slice.
-template <KV KT, KV QT, int D, int G, int EL, int LPT, int E, int VPT>
-__device__ __forceinline__ void load_q(QSlice<KT, EL>& qs, const void* qrow, int c) {
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const half2_t h = {(_Float16)lo, (_Float16)hi};   // one v_cvt_pk_f16_f32 (round to nearest even)
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// q row (already offset to the lane's head) -> the lane's slice.  For fp8 K
+// the query is held in f16 after a power-of-two rescale `qexp` (applied here,
+// undone on the scores), chosen per KV group so its largest element is in
+// [2^14, 2^15).
+template <KV KT, KV QT, int EL, int LPT, int E, int VPT>
+__device__ __forceinline__ void load_q(QSlice<KT, EL>& qs, const void* qrow, int c, int qexp) {
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
     const int e0 = (v * LPT + c) * E;
@@ -131,77 +143,131 @@ __device__ __forceinline__ void load_q(QSlice<KT, EL>& qs, const void* qrow, int
       static_assert(QT == KT, "16-bit caches take a query of the same type");
       const uint4 x = *(const uint4*)((const uint16_t*)qrow + e0);
       qs.w[v * 4 + 0] = x.x; qs.w[v * 4 + 1] = x.y; qs.w[v * 4 + 2] = x.z; qs.w[v * 4 + 3] = x.w;
-    } else {
+    } else if constexpr (KT == KV::F32) {
 #pragma unroll
       for (int e = 0; e < E; ++e) qs.f[v * E + e] = load_elem_f32<QT>(qrow, e0 + e);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; e += 2)
+        qs.w[(v * E + e) / 2] = pack_f16x2(__builtin_ldexpf(load_elem_f32<QT>(qrow, e0 + e), qexp),
+                                           __builtin_ldexpf(load_elem_f32<QT>(qrow, e0 + e + 1), qexp));
     }
   }
+}
+
+// Largest |q| of the lane's slice (fp8 path only, before packing).
+template <KV QT, int EL, int LPT, int E, int VPT>
+__device__ __forceinline__ float slice_absmax(const void* qrow, int c) {
+  float m = 0.f;
+#pragma unroll
+  for (int v = 0; v < VPT; ++v)
+#pragma unroll
+    for (int e = 0; e < E; ++e) m = fmaxf(m, fabsf(load_elem_f32<QT>(qrow, (v * LPT + c) * E + e)));
+  return m;
 }
 
 // K/V words of one token for one lane: VPT * 4 dwords.
 template <int VPT> struct TokWords { uint4 x[VPT]; };
 
-template <KV KT, int EL, int VPT>
-__device__ __forceinline__ void to_f32(const TokWords<VPT>& t, float (&f)[EL]) {
+template <int VPT>
+__device__ __forceinline__ void words_of(const TokWords<VPT>& t, uint32_t (&w)[4 * VPT]) {
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
-    const uint32_t w[4] = {t.x[v].x, t.x[v].y, t.x[v].z, t.x[v].w};
+    w[4 * v + 0] = t.x[v].x; w[4 * v + 1] = t.x[v].y; w[4 * v + 2] = t.x[v].z; w[4 * v + 3] = t.x[v].w;
+  }
+}
+
+template <KV KT, int EL, int VPT>
+__device__ __forceinline__ void to_f32(const TokWords<VPT>& t, float (&f)[EL]) {
+  uint32_t w[4 * VPT];
+  words_of(t, w);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if constexpr (KT == KV::F32) {
-        f[v * 4 + k] = __builtin_bit_cast(float, w[k]);
-      } else if constexpr (KT == KV::F16) {
-        f[v * 8 + 2 * k] = f16lo(w[k]);
-        f[v * 8 + 2 * k + 1] = f16hi(w[k]);
-      } else if constexpr (KT == KV::BF16) {
-        f[v * 8 + 2 * k] = bf16lo(w[k]);
-        f[v * 8 + 2 * k + 1] = bf16hi(w[k]);
-      } else {
-        const float2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
-        const float2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
-        f[v * 16 + 4 * k + 0] = lo.x;
-        f[v * 16 + 4 * k + 1] = lo.y;
-        f[v * 16 + 4 * k + 2] = hi.x;
-        f[v * 16 + 4 * k + 3] = hi.y;
-      }
+  for (int k = 0; k < 4 * VPT; ++k) {
+    if constexpr (KT == KV::F32) {
+      f[k] = __builtin_bit_cast(float, w[k]);
+    } else if constexpr (KT == KV::F16) {
+      f[2 * k] = f16lo(w[k]);
+      f[2 * k + 1] = f16hi(w[k]);
+    } else if constexpr (KT == KV::BF16) {
+      f[2 * k] = bf16lo(w[k]);
+      f[2 * k + 1] = bf16hi(w[k]);
+    } else {
+      const float2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
+      const float2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
+      f[4 * k + 0] = lo.x; f[4 * k + 1] = lo.y; f[4 * k + 2] = hi.x; f[4 * k + 3] = hi.y;
     }
+  }
+}
+
+// fp8 token words -> f16 pairs of adjacent elements (same token): EL / 2 words.
+template <int EL, int VPT>
+__device__ __forceinline__ void fp8_to_f16_pairs(const TokWords<VPT>& t, uint32_t (&h)[EL / 2]) {
+  uint32_t w[4 * VPT];
+  words_of(t, w);
+#pragma unroll
+  for (int k = 0; k < 4 * VPT; ++k) {
+    h[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[k], 1.0f, false));
+    h[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[k], 1.0f, true));
   }
 }
 
 // Partial <q_slice, K_slice> for one token.
 template <KV KT, int EL, int VPT>
 __device__ __forceinline__ float qk_partial(const QSlice<KT, EL>& qs, const TokWords<VPT>& t,
-                                            const float (&kf)[EL]) {
-  float s = 0.f;
-  if constexpr (KT == KV::F16) {
+                                            const float (&kf)[EL], const uint32_t (&kh)[EL / 2]) {
+  float s;
+  if constexpr (KT == KV::F16 || KT == KV::FP8) {
+    uint32_t w[EL / 2];
+    if constexpr (KT == KV::F16) words_of(t, w);
+    else {
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      const uint32_t w[4] = {t.x[v].x, t.x[v].y, t.x[v].z, t.x[v].w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (v == 0 && k == 0) {
-          // three-operand form with an inline zero: no register to clear
-          asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(s) : "v"(qs.w[0]), "v"(w[0]));
-        } else {
-          s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qs.w[v * 4 + k]),
-                                     __builtin_bit_cast(half2_t, w[k]), s, false);
-        }
-      }
+      for (int k = 0; k < EL / 2; ++k) w[k] = kh[k];
     }
+    // three-operand form with an inline zero: no register to clear
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(s) : "v"(qs.w[0]), "v"(w[0]));
+#pragma unroll
+    for (int k = 1; k < EL / 2; ++k)
+      s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qs.w[k]), __builtin_bit_cast(half2_t, w[k]),
+                                 s, false);
   } else if constexpr (KT == KV::BF16) {
+    uint32_t w[EL / 2];
+    words_of(t, w);
+    s = 0.f;
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      const uint32_t w[4] = {t.x[v].x, t.x[v].y, t.x[v].z, t.x[v].w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, qs.w[v * 4 + k]),
-                                            __builtin_bit_cast(bf162_t, w[k]), s, false);
-    }
+    for (int k = 0; k < EL / 2; ++k)
+      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, qs.w[k]),
+                                          __builtin_bit_cast(bf162_t, w[k]), s, false);
   } else {
+    s = 0.f;
 #pragma unroll
     for (int e = 0; e < EL; ++e) s = __builtin_fmaf(qs.f[e], kf[e], s);
   }
   return s;
+}
+
+// V of two tokens -> per element, an f16 pair (token 0, token 1) for dot2.
+template <KV KT, int EL, int VPT>
+__device__ __forceinline__ void v_token_pairs(const TokWords<VPT>& t0, const TokWords<VPT>& t1,
+                                              uint32_t (&vp)[EL]) {
+  uint32_t a[4 * VPT], b[4 * VPT];
+  words_of(t0, a);
+  words_of(t1, b);
+#pragma unroll
+  for (int k = 0; k < 4 * VPT; ++k) {
+    if constexpr (KT == KV::F16) {
+      // word k holds elements 2k, 2k+1 of each token
+      vp[2 * k] = __builtin_amdgcn_perm(b[k], a[k], 0x05040100u);
+      vp[2 * k + 1] = __builtin_amdgcn_perm(b[k], a[k], 0x07060302u);
+    } else {
+      // word k holds fp8 elements 4k..4k+3: interleave bytes, then widen
+      const uint32_t lo = __builtin_amdgcn_perm(b[k], a[k], 0x05010400u);
+      const uint32_t hi = __builtin_amdgcn_perm(b[k], a[k], 0x07030602u);
+      vp[4 * k + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false));
+      vp[4 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true));
+      vp[4 * k + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false));
+      vp[4 * k + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true));
+    }
+  }
 }
 
 template <KV OT>
@@ -223,7 +289,8 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
   constexpr int E = C::E, VPT = C::VPT, LPT = C::LPT, R = C::R, TPL = C::TPL;
   constexpr int NS = C::NS, NRS = C::NRS, NF = C::NF, EL = C::EL, NW = C::NW;
   constexpr int LEVELS = C::LEVELS;
-  constexpr int TILE = 16 * D;  // elements per (block, kv_head) tile
+  // P.V as f16 dot2 over pairs of tokens (probabilities rounded to f16)
+  constexpr bool PV_DOT2 = (KT == KV::F16 || KT == KV::FP8) && TPL >= 2;
 
   // LDS: while streaming, a ring of NBUF staged blocks per wave; at the end
   // of the partition the same bytes hold the per-wave partial results.
@@ -250,23 +317,40 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     return;  // empty partitions of a split call are skipped by the merge
   }
 
+  // Register slot k = hs * TPL + i holds (query head hs ^ hmask, tile token
+  // row ((i ^ tmask) * R + r)); the masks mirror partners' orders (see above).
   const int r = lane / LPT, c = lane % LPT;
   int M = 0;
   static_for<NRS>([&](auto l) {
     constexpr int kind = 4 - LEVELS + decltype(l)::value;
     M |= level_bit<kind, LEVELS>(c) * (NS >> (decltype(l)::value + 1));
   });
-  const int hmask = M % G;   // register head hs holds query head h*G + (hs ^ hmask)
-  const int tmask = M / G;   // register token i holds tile row ((i ^ tmask) * R + r)
+  const int hmask = M / TPL;
+  const int tmask = M % TPL;
 
+  auto qrow_of = [&](int hs) {
+    const int64_t qoff = ((int64_t)b * Hq + h * G + (hs ^ hmask)) * D;
+    return (QT == KV::F32) ? (const void*)((const float*)a.q + qoff)
+                           : (const void*)((const uint16_t*)a.q + qoff);
+  };
+  // fp8: one power-of-two rescale for the whole KV group, from the largest
+  // |q| over all g heads (every lane of a row sees all of them, so every lane
+  // derives the same exponent), so the partial sums the rows combine agree.
+  int qexp = 0;
+  if constexpr (KT == KV::FP8) {
+    float m = 0.f;
+#pragma unroll
+    for (int hs = 0; hs < G; ++hs) m = fmaxf(m, slice_absmax<QT, EL, LPT, E, VPT>(qrow_of(hs), c));
+    static_for<LEVELS>([&](auto l) { m = fmaxf(m, xlevel<4 - LEVELS + decltype(l)::value>(m)); });
+    int ex;
+    (void)__builtin_frexpf(m, &ex);             // m = f * 2^ex, f in [0.5, 1)
+    qexp = m > 0.f ? 15 - ex : 0;               // largest element lands in [2^14, 2^15)
+    qexp = qexp > 100 ? 100 : (qexp < -100 ? -100 : qexp);
+  }
+  const float qfac = __builtin_ldexpf(1.0f, -qexp);   // undoes the rescale on the scores
   QSlice<KT, EL> qs[G];
 #pragma unroll
-  for (int hs = 0; hs < G; ++hs) {
-    const int qi = h * G + (hs ^ hmask);
-    const int64_t qoff = ((int64_t)b * Hq + qi) * D;
-    if constexpr (QT == KV::F32) load_q<KT, QT, D, G, EL, LPT, E, VPT>(qs[hs], (const float*)a.q + qoff, c);
-    else load_q<KT, QT, D, G, EL, LPT, E, VPT>(qs[hs], (const uint16_t*)a.q + qoff, c);
-  }
+  for (int hs = 0; hs < G; ++hs) load_q<KT, QT, EL, LPT, E, VPT>(qs[hs], qrow_of(hs), c, qexp);
 
   float acc[G][EL];
   float mref[G];
@@ -287,16 +371,17 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
   // never waits behind the in-flight tile copies (vmcnt).
   const __attribute__((address_space(4))) int32_t* table =
       (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)b * a.max_blocks);
-  // byte offset of this lane's words inside a tile, per register token/load
-  int lane_off[TPL][VPT];
+
+  constexpr int LPB = C::LPB, STAGE_B = C::STAGE_B, NBUF = C::NBUF;
+  const uint32_t ring = lds_offset(smem) + (uint32_t)(w * NBUF * STAGE_B);
+  // Copy n of a tile moves token rows n / VPT * R .. + R - 1, 16-byte column
+  // (n % VPT) * LPT + c, in lane order: every copy reads 1 KiB contiguously.
+  uint32_t dma_off[LPB];
 #pragma unroll
   for (int i = 0; i < TPL; ++i)
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
-      lane_off[i][v] = (((i ^ tmask) * R + r) * D + (v * LPT + c) * E) * C::EB;
-
-  constexpr int LPB = C::LPB, STAGE_B = C::STAGE_B, NBUF = C::NBUF;
-  const uint32_t ring = lds_offset(smem) + (uint32_t)(w * NBUF * STAGE_B);
+      dma_off[i * VPT + v] = (uint32_t)(((i * R + r) * D + (v * LPT + c) * E) * C::EB);
   // Start the copy of block j's K and V tiles into ring stage `st`.
   auto issue_block = [&](int j, int st) {
     int phys = table[j];
@@ -306,24 +391,21 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     const char* vt = vbase + tile;
     const uint32_t dst = ring + (uint32_t)(st * STAGE_B);
 #pragma unroll
-    for (int i = 0; i < TPL; ++i)
+    for (int n = 0; n < LPB; ++n) lds_dma16(kt, dma_off[n], dst + n * 1024);
 #pragma unroll
-      for (int v = 0; v < VPT; ++v) lds_dma16(kt, (uint32_t)lane_off[i][v], dst + (i * VPT + v) * 1024);
-#pragma unroll
-    for (int i = 0; i < TPL; ++i)
-#pragma unroll
-      for (int v = 0; v < VPT; ++v)
-        lds_dma16(vt, (uint32_t)lane_off[i][v], dst + C::TILE_B + (i * VPT + v) * 1024);
+    for (int n = 0; n < LPB; ++n) lds_dma16(vt, dma_off[n], dst + C::TILE_B + n * 1024);
   };
-  // Registers <- the lane's own 16-byte pieces of stage `st`.
+  // Registers <- stage `st`: register token i reads the copy of row group
+  // (i ^ tmask) at the lane's own position (conflict-free LDS reads).
   auto read_stage = [&](int st, TokWords<VPT> (&kr)[TPL], TokWords<VPT> (&vr)[TPL]) {
     const char* src = smem + (w * NBUF + st) * STAGE_B + lane * 16;
 #pragma unroll
     for (int i = 0; i < TPL; ++i)
 #pragma unroll
       for (int v = 0; v < VPT; ++v) {
-        kr[i].x[v] = *(const uint4*)(src + (i * VPT + v) * 1024);
-        vr[i].x[v] = *(const uint4*)(src + C::TILE_B + (i * VPT + v) * 1024);
+        const int n = (i ^ tmask) * VPT + v;
+        kr[i].x[v] = *(const uint4*)(src + n * 1024);
+        vr[i].x[v] = *(const uint4*)(src + C::TILE_B + n * 1024);
       }
   };
   // Wait until at most `later` stages' copies are still in flight.
@@ -347,14 +429,16 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
       vsc = a.v_scales[si];
     }
 
-    // 1. partial scores: slot k = i * G + hs
+    // 1. partial scores: slot k = hs * TPL + i
     float s[NS];
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
       float kf[EL];
-      if constexpr (KT == KV::F32 || KT == KV::FP8) to_f32<KT, EL, VPT>(kr[i], kf);
+      uint32_t kh[EL / 2];
+      if constexpr (KT == KV::F32) to_f32<KT, EL, VPT>(kr[i], kf);
+      if constexpr (KT == KV::FP8) fp8_to_f16_pairs<EL, VPT>(kr[i], kh);
 #pragma unroll
-      for (int hs = 0; hs < G; ++hs) s[i * G + hs] = qk_partial<KT, EL, VPT>(qs[hs], kr[i], kf);
+      for (int hs = 0; hs < G; ++hs) s[hs * TPL + i] = qk_partial<KT, EL, VPT>(qs[hs], kr[i], kf, kh);
     }
     // 2. reduce-scatter over the row, then all-reduce for any levels left
     static_for<NRS>([&](auto l) {
@@ -367,6 +451,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
       constexpr int lv = NRS + decltype(l)::value;
       s[0] += xlevel<4 - LEVELS + lv>(s[0]);
     });
+    if constexpr (KT == KV::FP8) cs *= qfac;
 #pragma unroll
     for (int k = 0; k < NF; ++k) s[k] *= cs;
 
@@ -377,7 +462,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     if (nvalid < 16) {
 #pragma unroll
       for (int k = 0; k < NF; ++k) {
-        const int tok = (((k / G) ^ tmask) * R + r);
+        const int tok = (((k % TPL) ^ tmask) * R + r);
         if (tok >= nvalid) s[k] = -INFINITY;
       }
 #pragma unroll
@@ -392,7 +477,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     // 4. move the reference maxima if some score passed them by > slack
     bool need = false;
 #pragma unroll
-    for (int k = 0; k < NF; ++k) need |= s[k] > mref[k % G] + kLazyMaxSlack;
+    for (int k = 0; k < NF; ++k) need |= s[k] > mref[k / TPL] + kLazyMaxSlack;
     if (__any(need)) {
       float sa[NS];
 #pragma unroll
@@ -405,16 +490,16 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
       });
 #pragma unroll
       for (int hs = 0; hs < G; ++hs) {
-        float bm = sa[hs];
+        float bm = sa[hs * TPL];
 #pragma unroll
-        for (int i = 1; i < TPL; ++i) bm = fmaxf(bm, sa[i * G + hs]);
+        for (int i = 1; i < TPL; ++i) bm = fmaxf(bm, sa[hs * TPL + i]);
         const float mnew = fmaxf(mref[hs], bm);
         const float f = exp2_safe_factor(mref[hs], mnew);
 #pragma unroll
         for (int e = 0; e < EL; ++e) acc[hs][e] *= f;
 #pragma unroll
         for (int k = 0; k < NF; ++k)
-          if (k % G == hs) lpart[k] *= f;
+          if (k / TPL == hs) lpart[k] *= f;
         mref[hs] = mnew;
       }
     }
@@ -423,7 +508,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     float pf[NS];
 #pragma unroll
     for (int k = 0; k < NF; ++k) {
-      const float m = mref[k % G];
+      const float m = mref[k / TPL];
       const float pk = __builtin_amdgcn_exp2f(s[k] - (m == -INFINITY ? 0.f : m));
       lpart[k] += pk;
       pf[k] = pk * vsc;
@@ -436,15 +521,31 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     });
 
     // 6. accumulate p * V
+    if constexpr (PV_DOT2) {
 #pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-      float vf[EL];
-      to_f32<KT, EL, VPT>(vv[i], vf);
+      for (int m2 = 0; m2 < TPL / 2; ++m2) {
+        uint32_t vp[EL];
+        v_token_pairs<KT, EL, VPT>(vv[2 * m2], vv[2 * m2 + 1], vp);
 #pragma unroll
-      for (int hs = 0; hs < G; ++hs) {
-        const float pw = pf[i * G + hs];
+        for (int hs = 0; hs < G; ++hs) {
+          const half2_t pp = __builtin_bit_cast(
+              half2_t, pack_f16x2(pf[hs * TPL + 2 * m2], pf[hs * TPL + 2 * m2 + 1]));
 #pragma unroll
-        for (int e = 0; e < EL; ++e) acc[hs][e] = __builtin_fmaf(pw, vf[e], acc[hs][e]);
+          for (int e = 0; e < EL; ++e)
+            acc[hs][e] = __builtin_amdgcn_fdot2(pp, __builtin_bit_cast(half2_t, vp[e]), acc[hs][e], false);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TPL; ++i) {
+        float vf[EL];
+        to_f32<KT, EL, VPT>(vv[i], vf);
+#pragma unroll
+        for (int hs = 0; hs < G; ++hs) {
+          const float pw = pf[hs * TPL + i];
+#pragma unroll
+          for (int e = 0; e < EL; ++e) acc[hs][e] = __builtin_fmaf(pw, vf[e], acc[hs][e]);
+        }
       }
     }
   };
@@ -484,7 +585,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
   for (int hs = 0; hs < G; ++hs) {
     lrow[hs] = 0.f;
 #pragma unroll
-    for (int i = 0; i < TPL; ++i) lrow[hs] += la[i * G + hs];
+    for (int i = 0; i < TPL; ++i) lrow[hs] += la[hs * TPL + i];
   }
   // rows of the wave: lanes with equal c hold the same heads and columns
 #pragma unroll
