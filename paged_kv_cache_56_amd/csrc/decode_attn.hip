@@ -75,14 +75,21 @@ struct Cfg {
   static constexpr int NW = 4;                             // waves per workgroup
   static constexpr int LPB = TPL * VPT;                    // 16-byte loads per lane per tile
   static constexpr int TILE_B = 16 * D * EB;               // bytes of one (block, kv_head) tile
-  static constexpr int STAGE_B = 2 * TILE_B;               // K tile + V tile
-  // per-wave ring of staged blocks in LDS: about 16 KiB per wave, >= 2 stages
-  static constexpr int NBUF = (16384 / STAGE_B) >= 2 ? (16384 / STAGE_B) : 2;
-  static constexpr int RING_B = NW * NBUF * STAGE_B;
+  // Per-wave rings of staged tiles in LDS: NK K tiles and NV V tiles
+  // (NK >= NV: K is needed first).  About 16 KiB per wave: two 4-wave
+  // workgroups per CU; 20 KiB (NK = 3) measured no faster.
+#ifndef PKV_LDS_WAVE_B
+#define PKV_LDS_WAVE_B 16384
+#endif
+  static constexpr int TILES = PKV_LDS_WAVE_B / TILE_B;
+  static constexpr int NV = (TILES / 2) >= 2 ? (TILES / 2) : 2;
+  static constexpr int NK = (TILES - NV) >= NV ? (TILES - NV) : NV;
+  static constexpr int WAVE_RING_B = (NK + NV) * TILE_B;
+  static constexpr int RING_B = NW * WAVE_RING_B;
   static constexpr int RED_B = NW * G * (D + 2) * 4;       // end-of-partition combine
   static constexpr int SMEM_B = RING_B > RED_B ? RING_B : RED_B;
   static_assert(LPB * 64 * 16 == TILE_B, "a tile is LPB wave-wide 16-byte loads");
-  static_assert(2 * LPB * (NBUF - 1) <= 63, "vmcnt range");
+  static_assert(2 * LPB * (NV - 1) <= 63, "vmcnt range");
   static_assert(LPT >= 1 && LPT <= 16 && (LPT & (LPT - 1)) == 0, "lanes per token");
   static_assert(TPL >= 1, "tokens per lane");
 };
@@ -292,7 +299,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
   // P.V as f16 dot2 over pairs of tokens (probabilities rounded to f16)
   constexpr bool PV_DOT2 = (KT == KV::F16 || KT == KV::FP8) && TPL >= 2;
 
-  // LDS: while streaming, a ring of NBUF staged blocks per wave; at the end
+  // LDS: while streaming, per-wave rings of staged K and V tiles; at the end
   // of the partition the same bytes hold the per-wave partial results.
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM_B];
   float (*red_acc)[G][D] = reinterpret_cast<float (*)[G][D]>(smem);
@@ -372,8 +379,9 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
   const __attribute__((address_space(4))) int32_t* table =
       (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)b * a.max_blocks);
 
-  constexpr int LPB = C::LPB, STAGE_B = C::STAGE_B, NBUF = C::NBUF;
-  const uint32_t ring = lds_offset(smem) + (uint32_t)(w * NBUF * STAGE_B);
+  constexpr int LPB = C::LPB, NK = C::NK, NV = C::NV, TILE_B = C::TILE_B;
+  const uint32_t kring = lds_offset(smem) + (uint32_t)(w * C::WAVE_RING_B);
+  const uint32_t vring = kring + (uint32_t)(NK * TILE_B);
   // Copy n of a tile moves token rows n / VPT * R .. + R - 1, 16-byte column
   // (n % VPT) * LPT + c, in lane order: every copy reads 1 KiB contiguously.
   uint32_t dma_off[LPB];
@@ -382,39 +390,44 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
       dma_off[i * VPT + v] = (uint32_t)(((i * R + r) * D + (v * LPT + c) * E) * C::EB);
-  // Start the copy of block j's K and V tiles into ring stage `st`.
-  auto issue_block = [&](int j, int st) {
+  auto tile_of = [&](int j) {
     int phys = table[j];
     phys = ((unsigned)phys < (unsigned)a.num_blocks) ? phys : 0;
-    const int64_t tile = ((int64_t)phys * a.num_kv_heads + h) * (int64_t)C::TILE_B;
-    const char* kt = kbase + tile;
-    const char* vt = vbase + tile;
-    const uint32_t dst = ring + (uint32_t)(st * STAGE_B);
-#pragma unroll
-    for (int n = 0; n < LPB; ++n) lds_dma16(kt, dma_off[n], dst + n * 1024);
-#pragma unroll
-    for (int n = 0; n < LPB; ++n) lds_dma16(vt, dma_off[n], dst + C::TILE_B + n * 1024);
+    return ((int64_t)phys * a.num_kv_heads + h) * (int64_t)TILE_B;
   };
-  // Registers <- stage `st`: register token i reads the copy of row group
+  // Start copying block j's K tile into K slot `sk`, or its V tile into V slot `sv`.
+  auto issue_k = [&](int j, int sk) {
+    const char* src = kbase + tile_of(j);
+    const uint32_t dst = kring + (uint32_t)(sk * TILE_B);
+#pragma unroll
+    for (int n = 0; n < LPB; ++n) lds_dma16(src, dma_off[n], dst + n * 1024);
+  };
+  auto issue_v = [&](int j, int sv) {
+    const char* src = vbase + tile_of(j);
+    const uint32_t dst = vring + (uint32_t)(sv * TILE_B);
+#pragma unroll
+    for (int n = 0; n < LPB; ++n) lds_dma16(src, dma_off[n], dst + n * 1024);
+  };
+  // Registers <- slots: register token i reads the copy of row group
   // (i ^ tmask) at the lane's own position (conflict-free LDS reads).
-  auto read_stage = [&](int st, TokWords<VPT> (&kr)[TPL], TokWords<VPT> (&vr)[TPL]) {
-    const char* src = smem + (w * NBUF + st) * STAGE_B + lane * 16;
+  auto read_slots = [&](int sk, int sv, TokWords<VPT> (&kr)[TPL], TokWords<VPT> (&vr)[TPL]) {
+    const char* ks = smem + w * C::WAVE_RING_B + sk * TILE_B + lane * 16;
+    const char* vs = smem + w * C::WAVE_RING_B + (NK + sv) * TILE_B + lane * 16;
 #pragma unroll
     for (int i = 0; i < TPL; ++i)
 #pragma unroll
       for (int v = 0; v < VPT; ++v) {
         const int n = (i ^ tmask) * VPT + v;
-        kr[i].x[v] = *(const uint4*)(src + n * 1024);
-        vr[i].x[v] = *(const uint4*)(src + C::TILE_B + n * 1024);
+        kr[i].x[v] = *(const uint4*)(ks + n * 1024);
+        vr[i].x[v] = *(const uint4*)(vs + n * 1024);
       }
   };
-  // Wait until at most `later` stages' copies are still in flight.
-  auto wait_stages = [&](int later) {
-    constexpr int PER = 2 * LPB;
-    if constexpr (NBUF > 3) { if (later >= 3) { wait_vmcnt<(NBUF > 3 ? 3 : 0) * PER>(); return; } }
-    if constexpr (NBUF > 2) { if (later >= 2) { wait_vmcnt<(NBUF > 2 ? 2 : 0) * PER>(); return; } }
-    if (later >= 1) { wait_vmcnt<PER>(); return; }
-    wait_vmcnt<0>();
+  // Wait until at most `tiles` tile copies (of LPB loads each) are in flight.
+  auto wait_tiles = [&](int tiles) {
+    static_for<2 * NV - 1>([&](auto u) {
+      constexpr int c2 = 2 * NV - 2 - decltype(u)::value;   // tries 2NV-2 down to 0
+      if (tiles == c2) wait_vmcnt<c2 * LPB>();
+    });
   };
 
   auto compute_block = [&](int j, const TokWords<VPT> (&kr)[TPL], const TokWords<VPT> (&vr)[TPL]) {
@@ -550,20 +563,28 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     }
   };
 
-  // Pipeline: the wave's blocks are j0 + w, j0 + w + NW, ...; up to NBUF of
-  // them are being copied into the ring while one is computed from registers.
+  // Pipeline: the wave's blocks are j0 + w, j0 + w + NW, ... (index t).  K of
+  // block t + NK and V of block t + NV are copied while block t is computed.
+  // Copies complete in issue order, so block t is ready once no more than the
+  // copies issued after V(t) -- K(t+NK-NV+1 .. t+NK-1), V(t+1 .. t+NV-1) --
+  // are outstanding.
   {
     const int first = j0 + w;
     const int n_my = first < j1 ? (j1 - first + NW - 1) / NW : 0;
-    for (int t = 0; t < NBUF && t < n_my; ++t) issue_block(first + t * NW, t);
+    for (int u = 0; u < NK; ++u) {
+      if (u < n_my) issue_k(first + u * NW, u);
+      if (u < NV && u < n_my) issue_v(first + u * NW, u);
+    }
     for (int t = 0; t < n_my; ++t) {
-      const int st = t % NBUF;
-      const int later = min(NBUF - 1, n_my - 1 - t);
-      wait_stages(later);
+      const int sk = t % NK, sv = t % NV;
+      const int k_after = max(0, min(n_my, t + NK) - max(t + NK - NV + 1, 0));
+      const int v_after = max(0, min(n_my, t + NV) - (t + 1));
+      wait_tiles(k_after + v_after);
       TokWords<VPT> kr[TPL], vr[TPL];
-      read_stage(st, kr, vr);
-      wait_lgkmcnt0();  // the stage is in registers: its buffer may be refilled
-      if (t + NBUF < n_my) issue_block(first + (t + NBUF) * NW, st);
+      read_slots(sk, sv, kr, vr);
+      wait_lgkmcnt0();  // the slots are in registers: they may be refilled
+      if (t + NK < n_my) issue_k(first + (t + NK) * NW, sk);
+      if (t + NV < n_my) issue_v(first + (t + NV) * NW, sv);
       compute_block(first + t * NW, kr, vr);
     }
   }
