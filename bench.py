@@ -25,6 +25,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -44,7 +46,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def attention_bytes(spec, lay):
+def attended(L: int, window: int, sinks: int):
+    """Positions a length-L sequence attends (the oracle's definition, restated
+    here so the byte count does not import the oracle)."""
+    if window <= 0 or L <= window:
+        return range(L)
+    return sorted(set(range(min(sinks, L))) | set(range(L - window, L)))
+
+
+def attention_bytes(spec, lay, window: int = 0, sinks: int = 0):
     """Algorithmic bytes of one attention launch (one layer).
 
     K and V of every attended (token, KV head) once -- a physical block that
@@ -54,15 +64,16 @@ def attention_bytes(spec, lay):
     KV head).  Returns (K/V bytes, all algorithmic bytes, logical K/V bytes
     counting shared blocks once per sequence)."""
     L = lay.context_lens.astype(int)
-    nblk = -(-L // 16)
     per_token = spec.num_kv_heads * spec.head_dim * ELT[spec.kv_dtype] * 2
-    logical = int(L.sum()) * per_token
-    used = {}
+    logical = 0
+    used = {}                        # physical block -> attended token offsets
     for b in range(spec.num_seqs):
-        for j in range(int(nblk[b])):
-            blk = int(lay.block_tables[b, j])
-            used[blk] = max(used.get(blk, 0), min(16, int(L[b]) - 16 * j))
-    kv = sum(used.values()) * per_token
+        pos = attended(int(L[b]), window, sinks)
+        logical += len(pos) * per_token
+        for p in pos:
+            used.setdefault(int(lay.block_tables[b, p // 16]), set()).add(p % 16)
+    kv = sum(len(v) for v in used.values()) * per_token
+    nblk = np.array([len({p // 16 for p in attended(int(l), window, sinks)}) for l in L])
     q = spec.num_seqs * spec.num_q_heads * spec.head_dim * ELT[spec.q_dtype]
     out = spec.num_seqs * spec.num_q_heads * spec.head_dim * ELT[spec.out_dtype]
     meta = int(nblk.sum()) * 4 + spec.num_seqs * 4
@@ -280,6 +291,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama70b_f16_80l")
     ap.add_argument("--partition-blocks", type=int, default=0)
+    ap.add_argument("--window", type=int, default=0, help="sliding window W (0 = whole context)")
+    ap.add_argument("--sinks", type=int, default=0, help="attention-sink tokens kept with a window")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="0 skips the CPU baseline")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the plain-read bandwidth probe and the copy used to calibrate counters")
@@ -317,7 +330,8 @@ def main():
     nl = spec.num_layers
     odt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[spec.out_dtype]
     outs = torch.empty((nl, spec.num_seqs, spec.num_q_heads, spec.head_dim), dtype=odt, device=dev)
-    dims = pkv.decode_dims(x["q"][0], x["k_cache"][0], x["block_tables"], outs[0], args.partition_blocks)
+    dims = pkv.decode_dims(x["q"][0], x["k_cache"][0], x["block_tables"], outs[0], args.partition_blocks,
+                           args.window, args.sinks)
     nparts = pkv.decode_num_partitions(dims)
     ws_bytes = pkv.decode_workspace_bytes(dims)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -333,7 +347,8 @@ def main():
             kw = dict(k_scales=x["k_scales"][layer], v_scales=x["v_scales"][layer]) if fp8 else {}
             pkv.paged_decode_attn(x["q"][layer], kc, vc, x["block_tables"], x["context_lens"],
                                   spec.scale, outs[layer], workspace=ws,
-                                  partition_blocks=args.partition_blocks, **kw)
+                                  partition_blocks=args.partition_blocks, window=args.window,
+                                  sinks=args.sinks, **kw)
             if ev is not None:
                 ev[layer][1].record()
 
@@ -354,11 +369,11 @@ def main():
     launch_ms = np.array([[e[0].elapsed_time(e[1]) for e in row] for row in events])
     mean_launch_s = float(launch_ms.mean()) / 1e3
 
-    kv_bytes, alg_bytes, logical_bytes = attention_bytes(spec, lay)
+    kv_bytes, alg_bytes, logical_bytes = attention_bytes(spec, lay, args.window, args.sinks)
     value = kv_bytes * nl / (ms_per_step / 1e3) / 1e9
     achieved = alg_bytes / mean_launch_s / 1e9
     kernel = "decode_partition_kernel" + ("+lse_merge_kernel" if nparts > 1 else "")
-    trec = traffic_for(spec.name) if nparts == 1 else None
+    trec = traffic_for(spec.name) if (nparts == 1 and args.window == 0) else None
     traffic = None if trec is None else trec["traffic_bytes_per_launch"]
     log(f"[bench] {ms_per_step:.3f} ms/step; attention launch {mean_launch_s * 1e6:.1f} us "
         f"-> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of peak)")
@@ -396,6 +411,8 @@ def main():
             "head_dim": spec.head_dim,
             "block_size": 16,
             "partitions": nparts,
+            "window": args.window,
+            "sinks": args.sinks if args.window > 0 else 0,
             "kv_bytes_per_step": kv_bytes * nl,
             "logical_kv_bytes_per_step": logical_bytes * nl,
         },

@@ -65,7 +65,8 @@ typedef enum {
   PKV_OK = 0,
   PKV_ERR_NULL = -1,      /* a required pointer is NULL */
   PKV_ERR_SHAPE = -2,     /* non-positive size, Hq % Hkv != 0, g not in {1,2,4,8},
-                             head_dim not in {64,128}, block_size != 16 */
+                             head_dim not in {64,128}, block_size != 16,
+                             negative window or sinks */
   PKV_ERR_DTYPE = -3,     /* unsupported dtype or dtype combination */
   PKV_ERR_WORKSPACE = -4, /* workspace missing or smaller than required */
   PKV_ERR_LAUNCH = -5     /* the HIP runtime refused a launch */
@@ -83,6 +84,9 @@ typedef struct {
   int32_t kv_dtype;            /* pkv_dtype */
   int32_t out_dtype;           /* pkv_dtype */
   int32_t partition_blocks;    /* blocks per context partition; 0 = automatic */
+  int32_t window;              /* sliding window W: attend only the last W positions
+                                  (0 = the whole context) */
+  int32_t sinks;               /* with W > 0, also attend the first `sinks` positions */
 } pkv_decode_dims;
 
 /*
@@ -117,7 +121,10 @@ PKV_API int pkv_decode_num_partitions(const pkv_decode_dims* dims);
  * Cache memory ledger" 2, 4).  For each sequence b and query head i, with
  * L = context_lens[b] and h = i / g:
  *   out[b][i][:] = sum_t softmax_t(scale * <q[b][i], K_t>) V_t,  t < L,
- * where K_t, V_t are read at locate(b, t).  L = 0 gives a zero row.  Block
+ * where K_t, V_t are read at locate(b, t).  With dims->window = W > 0 the
+ * positions are restricted to t >= L - W plus t < dims->sinks ("KV Cache
+ * from first principles" 5.3: sliding window and attention-sink tokens).
+ * L = 0 gives a zero row.  Block
  * ids outside [0, num_blocks) and positions past max_blocks_per_seq * 16 are
  * ignored (the caller must not pass them).
  * Non-fp8 dtypes: q, caches and out all F32, or all F16, or all BF16.

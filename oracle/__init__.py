@@ -9,7 +9,7 @@ Pages cited (by title and section):
   [P1] "KV Cache from first principles" (ldpk.cn/news/58971): 2.1 scaled
        dot-product attention; 2.2 decode attends over cached K/V; 2.3 append
        at the current length; 3.1 bytes per token; 3.2 worked model table;
-       4.3 paging; 5.1 GQA/MQA.
+       4.3 paging; 5.1 GQA/MQA; 5.3 sliding window and attention sinks.
   [P2] "Large-model inference KV Cache memory optimisation: from PagedAttention
        to AI memory systems" (wmrh.cn/news/79784): 1.1 KV size formula and the
        13B example; 2.2 fixed-size blocks and block tables; 3.1-3.2 sharing.
@@ -21,7 +21,7 @@ Pages cited (by title and section):
   [P5] "The KV Cache memory ledger: PagedAttention and continuous batching"
        (gcssc.sfwss.com/posts/kv-cache-budget.html): 1 bytes per token (70B);
        2 GQA table; 4 block table and locate(); 4 prefix sharing; 7 quantized
-       KV with per-head scales.
+       KV with per-head scales; sink tokens kept out of coarse quantisation.
 
 Readings taken where the pages are silent (each is also a test):
   * cache memory order is [num_blocks, kv_heads, block_size, head_dim];
@@ -38,7 +38,7 @@ pages print); none is "parity unpinned".
 
 from .fp8_e4m3 import decode_e4m3fn, encode_e4m3fn_rne, E4M3_MAX, E4M3_NAN_CODES
 from .values import stored_to_f64
-from .paged_attention import locate, gather_sequence, paged_decode_attention
+from .paged_attention import locate, gather_sequence, paged_decode_attention, attended_positions
 from .kv_append import kv_append_bits
 from .kv_bytes import kv_bytes_per_token, kv_bytes
 
@@ -51,6 +51,7 @@ __all__ = [
     "locate",
     "gather_sequence",
     "paged_decode_attention",
+    "attended_positions",
     "kv_append_bits",
     "kv_bytes_per_token",
     "kv_bytes",

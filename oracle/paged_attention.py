@@ -16,6 +16,10 @@ What is computed, and where the pages state it:
     consecutive query heads share one K/V head (g = Hq / Hkv; MQA is Hkv = 1).
   * [P5] section 7: quantised K/V carry one scale per head; here one fp32
     scale per (physical block, KV head), and the value used is code * scale.
+  * [P1] section 5.3: with a sliding window of W, a position attends only to
+    the most recent W tokens (itself included), optionally together with the
+    first few tokens of the sequence (attention sinks), which [P1] 5.3 and
+    [P5] section 7 single out as tokens that must not be dropped.
 
 Test infrastructure only (see the package docstring).
 """
@@ -36,22 +40,38 @@ def locate(table_row, pos, block_size: int = 16):
     return table_row[pos // block_size], pos % block_size
 
 
+def attended_positions(length: int, window: int = 0, sinks: int = 0) -> np.ndarray:
+    """Positions the query of a sequence of `length` tokens attends to.
+
+    window = 0: all of them.  window > 0: the last `window` positions, plus
+    the first `sinks` positions (sinks only matter together with a window).
+    """
+    L = int(length)
+    if window <= 0:
+        return np.arange(L)
+    recent = np.arange(max(0, L - int(window)), L)
+    first = np.arange(min(int(sinks), L))
+    return np.union1d(first, recent)
+
+
 def gather_sequence(cache, table_row, length: int, kv_tag: str, kv_heads=None,
-                    scales=None, block_size: int = 16) -> np.ndarray:
-    """Contiguous float64 [length, len(kv_heads), D] copy of one sequence.
+                    scales=None, block_size: int = 16, positions=None) -> np.ndarray:
+    """Contiguous float64 [n, len(kv_heads), D] copy of one sequence's tokens.
 
     `cache` is the raw storage array [num_blocks, Hkv, block_size, D] (uint16
     bits for bf16, uint8 codes for fp8); `scales` ([num_blocks, Hkv] fp32) is
     required for fp8 and multiplies every element of its (block, head) tile.
-    Only positions < length are touched.
+    The tokens are `positions` (default: 0 .. length-1), all < length.
     """
     nb = cache.shape[0]
     if kv_heads is None:
         kv_heads = np.arange(cache.shape[1])
     kv_heads = np.asarray(kv_heads)
-    pos = np.arange(int(length))
+    pos = np.arange(int(length)) if positions is None else np.asarray(positions, dtype=np.int64)
+    if len(pos) and (pos.min() < 0 or pos.max() >= length):
+        raise IndexError("position outside the sequence")
     blk, off = locate(table_row, pos, block_size)
-    if length and (blk.min() < 0 or blk.max() >= nb):
+    if len(pos) and (blk.min() < 0 or blk.max() >= nb):
         raise IndexError("block table entry outside the pool for a position < length")
     raw = cache[blk[:, None], kv_heads[None, :], off[:, None], :]      # [L, h, D]
     vals = stored_to_f64(raw, kv_tag)
@@ -69,11 +89,12 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
                            *, q_tag: str, kv_tag: str, k_scales=None, v_scales=None,
                            seqs: Optional[Sequence[int]] = None,
                            q_heads: Optional[Sequence[int]] = None,
-                           block_size: int = 16) -> np.ndarray:
+                           block_size: int = 16, window: int = 0, sinks: int = 0) -> np.ndarray:
     """out[b, i, :] for b in `seqs`, i in `q_heads` (all by default), float64.
 
     q: [B, Hq, D] storage array; caches: [num_blocks, Hkv, block_size, D];
-    block_tables: int [B, max_blocks]; context_lens: int [B].
+    block_tables: int [B, max_blocks]; context_lens: int [B].  window/sinks
+    restrict the attended positions (see attended_positions).
     """
     B, Hq, D = q.shape
     Hkv = k_cache.shape[1]
@@ -89,10 +110,11 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
     qv = stored_to_f64(np.asarray(q)[seqs][:, q_heads], q_tag)       # [nb, nh, D]
     for r, b in enumerate(seqs):
         L = int(context_lens[b])
-        if L == 0:
+        pos = attended_positions(L, window, sinks)
+        if len(pos) == 0:
             continue
-        K = gather_sequence(k_cache, block_tables[b], L, kv_tag, kv_needed, k_scales, block_size)
-        V = gather_sequence(v_cache, block_tables[b], L, kv_tag, kv_needed, v_scales, block_size)
+        K = gather_sequence(k_cache, block_tables[b], L, kv_tag, kv_needed, k_scales, block_size, pos)
+        V = gather_sequence(v_cache, block_tables[b], L, kv_tag, kv_needed, v_scales, block_size, pos)
         for c, i in enumerate(q_heads):
             h = col[kv_for[c]]
             s = scale * (K[:, h, :] @ qv[r, c])          # [L] scores

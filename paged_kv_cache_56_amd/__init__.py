@@ -8,7 +8,8 @@ carry device memory and streams.
 
     kv_append(k_new, v_new, slot_mapping, k_cache, v_cache)
     paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, scale, out,
-                      k_scales=None, v_scales=None, workspace=None, partition_blocks=0)
+                      k_scales=None, v_scales=None, workspace=None, partition_blocks=0,
+                      window=0, sinks=0)
 """
 
 from __future__ import annotations
@@ -65,6 +66,8 @@ class DecodeDims(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32),
         ("out_dtype", ctypes.c_int32),
         ("partition_blocks", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("sinks", ctypes.c_int32),
     ]
 
 
@@ -165,12 +168,13 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tens
 
 
 def decode_dims(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor,
-                out: torch.Tensor, partition_blocks: int = 0) -> DecodeDims:
+                out: torch.Tensor, partition_blocks: int = 0, window: int = 0,
+                sinks: int = 0) -> DecodeDims:
     B, Hq, D = q.shape
     NB, Hkv, bs, Dk = k_cache.shape
     _need(Dk == D, "head_dim of q and cache differ")
     return DecodeDims(B, Hq, Hkv, D, bs, NB, block_tables.shape[1], _code(q), _code(k_cache),
-                      _code(out), partition_blocks)
+                      _code(out), partition_blocks, window, sinks)
 
 
 def decode_workspace_bytes(dims: DecodeDims) -> int:
@@ -196,14 +200,15 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       out: torch.Tensor, *, k_scales: Optional[torch.Tensor] = None,
                       v_scales: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None,
-                      partition_blocks: int = 0) -> torch.Tensor:
+                      partition_blocks: int = 0, window: int = 0, sinks: int = 0) -> torch.Tensor:
     """out[b, i] = softmax(scale * q[b, i] . K^T) V over the first context_lens[b]
     tokens of sequence b, K/V read through block_tables.  Returns `out`.
 
     q, out: [B, Hq, D]; caches: [NB, Hkv, 16, D]; block_tables: int32 [B, max_blocks];
     context_lens: int32 [B].  FP8 caches (uint8 or float8_e4m3fn) need k_scales and
     v_scales: fp32 [NB, Hkv].  `workspace` (uint8, on the device) is allocated here
-    when the call splits the context and none is given.
+    when the call splits the context and none is given.  window > 0 limits each
+    query to the last `window` positions plus the first `sinks` positions.
     """
     lib = load_library()
     _dev(q, k_cache, v_cache, block_tables, context_lens, out, k_scales, v_scales, workspace)
@@ -214,7 +219,7 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
           and block_tables.shape[0] == q.shape[0], "block_tables must be int32 [B, max_blocks]")
     _need(context_lens.dtype == torch.int32 and context_lens.shape == (q.shape[0],),
           "context_lens must be int32 [B]")
-    dims = decode_dims(q, k_cache, block_tables, out, partition_blocks)
+    dims = decode_dims(q, k_cache, block_tables, out, partition_blocks, window, sinks)
     need = decode_workspace_bytes(dims)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

@@ -22,7 +22,8 @@ int elem_bytes(int dt) {
 int check_dims(const pkv_decode_dims* d) {
   if (!d) return PKV_ERR_NULL;
   if (d->num_seqs <= 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0 ||
-      d->num_blocks <= 0 || d->max_blocks_per_seq <= 0 || d->partition_blocks < 0)
+      d->num_blocks <= 0 || d->max_blocks_per_seq <= 0 || d->partition_blocks < 0 ||
+      d->window < 0 || d->sinks < 0)
     return PKV_ERR_SHAPE;
   if (d->block_size != PKV_BLOCK_SIZE) return PKV_ERR_SHAPE;
   if (d->num_q_heads % d->num_kv_heads) return PKV_ERR_SHAPE;
@@ -86,6 +87,8 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
   a.max_blocks = dims->max_blocks_per_seq;
   a.part_blocks = pb;
   a.num_parts = np;
+  a.window = dims->window;
+  a.sinks = dims->window > 0 ? dims->sinks : 0;
   a.q_dtype = dims->q_dtype;
   a.kv_dtype = dims->kv_dtype;
   a.out_dtype = dims->out_dtype;

@@ -41,9 +41,11 @@
 // stream; streams are merged by log-sum-exp at the end of the partition, and
 // partitions by a second small kernel.
 //
-// Masking.  Positions >= L (the tail of the last block) get score -inf and a
-// zeroed V operand, so poisoned tail slots never reach the sums (0 * NaN
-// would).  Block ids outside the pool are treated as fully masked.
+// Masking.  Positions >= L (the tail of the last block), and with a sliding
+// window the positions outside it, get score -inf and a zeroed V operand, so
+// poisoned slots never reach the sums (0 * NaN would).  Block ids outside
+// the pool are treated as fully masked.  A window skips whole blocks: a
+// partition walks only the attended blocks (sink blocks, then window blocks).
 #include "pkv_internal.h"
 
 #include <type_traits>
@@ -289,6 +291,48 @@ __device__ __forceinline__ float exp2_safe_factor(float m_old, float m_new) {
   return m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_old - m_new);
 }
 
+// The blocks one sequence's query attends, as a compressed list: with a
+// sliding window of W and S sink tokens ("KV Cache from first principles"
+// 5.3) they are the sink blocks [0, nsb) then the window blocks [wb0, nblk);
+// without a window, or when the two ranges touch, simply [0, nblk).
+// Position pos of block j is attended iff pos < L and (no window, or
+// pos < se, or pos >= ws).
+struct SeqSpan {
+  int L, nblk, natt, nsb, wb0, se, ws;
+  bool windowed;
+  __device__ __forceinline__ SeqSpan(int len, int max_blocks, int window, int sinks) {
+    L = len < 0 ? 0 : (len > max_blocks * 16 ? max_blocks * 16 : len);
+    nblk = (L + 15) >> 4;
+    windowed = window > 0 && L > window;
+    ws = windowed ? L - window : 0;
+    se = windowed ? min(sinks, L) : 0;
+    if (se >= ws) windowed = false;      // sinks reach the window: everything
+    nsb = 0;
+    wb0 = 0;
+    if (windowed) {
+      nsb = (se + 15) >> 4;
+      wb0 = ws >> 4;
+      if (nsb >= wb0) { nsb = 0; wb0 = 0; }  // the ranges touch: one range
+    }
+    natt = nsb + nblk - wb0;
+  }
+  __device__ __forceinline__ int logical(int cidx) const { return cidx < nsb ? cidx : cidx - nsb + wb0; }
+  // bit t set: token t of logical block j is attended
+  __device__ __forceinline__ uint32_t valid_bits(int j) const {
+    const int base = j * 16;
+    const int nv = min(16, L - base);
+    uint32_t m = nv >= 16 ? 0xFFFFu : (nv > 0 ? ((1u << nv) - 1u) : 0u);
+    if (windowed) {
+      const int lo = ws - base;                    // tokens >= lo are in the window
+      const int hi = se - base;                    // tokens < hi are sinks
+      const uint32_t win = lo <= 0 ? 0xFFFFu : (lo >= 16 ? 0u : (0xFFFFu & ~((1u << lo) - 1u)));
+      const uint32_t snk = hi <= 0 ? 0u : (hi >= 16 ? 0xFFFFu : ((1u << hi) - 1u));
+      m &= (win | snk);
+    }
+    return m;
+  }
+};
+
 // ---------------------------------------------------------------------------
 template <KV KT, KV QT, KV OT, int D, int G>
 __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
@@ -311,11 +355,10 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int Hq = a.num_kv_heads * G;
 
-  int L = a.context_lens[b];
-  L = L < 0 ? 0 : (L > a.max_blocks * 16 ? a.max_blocks * 16 : L);
-  const int nblk = (L + 15) >> 4;
+  const SeqSpan span(a.context_lens[b], a.max_blocks, a.window, a.sinks);
+  // this partition: entries [j0, j1) of the sequence's attended-block list
   const int j0 = p * a.part_blocks;
-  const int j1 = min(j0 + a.part_blocks, nblk);
+  const int j1 = min(j0 + a.part_blocks, span.natt);
   if (j0 >= j1) {
     if (a.num_parts == 1) {
       for (int idx = tid; idx < G * D; idx += 256)
@@ -391,7 +434,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     for (int v = 0; v < VPT; ++v)
       dma_off[i * VPT + v] = (uint32_t)(((i * R + r) * D + (v * LPT + c) * E) * C::EB);
   auto tile_of = [&](int j) {
-    int phys = table[j];
+    int phys = table[span.logical(j)];
     phys = ((unsigned)phys < (unsigned)a.num_blocks) ? phys : 0;
     return ((int64_t)phys * a.num_kv_heads + h) * (int64_t)TILE_B;
   };
@@ -431,9 +474,10 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
   };
 
   auto compute_block = [&](int j, const TokWords<VPT> (&kr)[TPL], const TokWords<VPT> (&vr)[TPL]) {
-    const int phys_raw = table[j];
+    const int jl = span.logical(j);
+    const int phys_raw = table[jl];
     const bool blk_ok = (unsigned)phys_raw < (unsigned)a.num_blocks;
-    const int nvalid = blk_ok ? min(16, L - j * 16) : 0;
+    const uint32_t vbits = blk_ok ? span.valid_bits(jl) : 0u;
     float cs = a.scale;  // scale * log2(e), folded on the host
     float vsc = 1.f;
     if constexpr (KT == KV::FP8) {
@@ -472,15 +516,15 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     TokWords<VPT> vv[TPL];
 #pragma unroll
     for (int i = 0; i < TPL; ++i) vv[i] = vr[i];
-    if (nvalid < 16) {
+    if (vbits != 0xFFFFu) {
 #pragma unroll
       for (int k = 0; k < NF; ++k) {
         const int tok = (((k % TPL) ^ tmask) * R + r);
-        if (tok >= nvalid) s[k] = -INFINITY;
+        if (!((vbits >> tok) & 1u)) s[k] = -INFINITY;
       }
 #pragma unroll
       for (int i = 0; i < TPL; ++i) {
-        if (((i ^ tmask) * R + r) >= nvalid) {
+        if (!((vbits >> ((i ^ tmask) * R + r)) & 1u)) {
 #pragma unroll
           for (int v = 0; v < VPT; ++v) vv[i].x[v] = make_uint4(0, 0, 0, 0);
         }
@@ -676,10 +720,8 @@ __global__ void __launch_bounds__(64) lse_merge_kernel(DecodeArgs a) {
   const int row = blockIdx.x;
   const int b = row / a.num_q_heads;
   const int lane = threadIdx.x;
-  int L = a.context_lens[b];
-  L = L < 0 ? 0 : (L > a.max_blocks * 16 ? a.max_blocks * 16 : L);
-  const int nblk = (L + 15) >> 4;
-  const int np = min((nblk + a.part_blocks - 1) / a.part_blocks, a.num_parts);
+  const SeqSpan span(a.context_lens[b], a.max_blocks, a.window, a.sinks);
+  const int np = min((span.natt + a.part_blocks - 1) / a.part_blocks, a.num_parts);
   const float* ml = a.ml_part + (int64_t)row * a.num_parts * 2;
   const float* op = a.o_part + (int64_t)row * a.num_parts * D;
   float m = -INFINITY;
@@ -705,7 +747,12 @@ __global__ void __launch_bounds__(64) lse_merge_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 void plan_partitions(const pkv_decode_dims& d, int* part_blocks, int* num_parts) {
-  const int maxb = d.max_blocks_per_seq;
+  // longest attended-block list any sequence can have
+  int maxb = d.max_blocks_per_seq;
+  if (d.window > 0) {
+    const int64_t att = (int64_t)(d.window + 15) / 16 + 1 + (d.sinks + 15) / 16;
+    if (att < maxb) maxb = (int)att;
+  }
   int pb;
   if (d.partition_blocks > 0) {
     pb = d.partition_blocks;

@@ -24,6 +24,7 @@ struct DecodeArgs {
   float* ml_part;          // [B*Hq][P][2] when P > 1
   int num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks;
   int part_blocks, num_parts;
+  int window, sinks;       // sliding window (0 = off) and attention-sink tokens
   int q_dtype, kv_dtype, out_dtype;
 };
 

@@ -31,7 +31,7 @@ def host_storage(t: torch.Tensor) -> np.ndarray:
 
 
 def run_step(x, layer: int, spec, out: torch.Tensor, partition_blocks: int = 0,
-             workspace=None, append: bool = True):
+             workspace=None, append: bool = True, window: int = 0, sinks: int = 0):
     """One layer of the decode step on the device: append, then attend."""
     kc, vc = x["k_cache"][layer], x["v_cache"][layer]
     if spec.append and append:
@@ -41,10 +41,10 @@ def run_step(x, layer: int, spec, out: torch.Tensor, partition_blocks: int = 0,
         kw = dict(k_scales=x["k_scales"][layer], v_scales=x["v_scales"][layer])
     return pkv.paged_decode_attn(x["q"][layer], kc, vc, x["block_tables"], x["context_lens"],
                                  spec.scale, out, workspace=workspace,
-                                 partition_blocks=partition_blocks, **kw)
+                                 partition_blocks=partition_blocks, window=window, sinks=sinks, **kw)
 
 
-def oracle_rows(x_host_layer, layout, spec, seqs=None, q_heads=None):
+def oracle_rows(x_host_layer, layout, spec, seqs=None, q_heads=None, window=0, sinks=0):
     """Oracle output for the given rows from host copies of one layer's inputs.
 
     x_host_layer: dict with numpy storage arrays q, k_cache, v_cache (pre-append),
@@ -58,7 +58,7 @@ def oracle_rows(x_host_layer, layout, spec, seqs=None, q_heads=None):
         x_host_layer["q"], kc, vc, layout.block_tables, layout.context_lens, spec.scale,
         q_tag=spec.q_dtype, kv_tag=spec.kv_dtype,
         k_scales=x_host_layer.get("k_scales"), v_scales=x_host_layer.get("v_scales"),
-        seqs=seqs, q_heads=q_heads)
+        seqs=seqs, q_heads=q_heads, window=window, sinks=sinks)
 
 
 def host_layer(x, layer: int):

@@ -65,6 +65,8 @@ def _attn_fp8(dims, ks=FAKE, vs=FAKE):
     (dict(max_blocks_per_seq=0), -2),
     (dict(num_blocks=-1), -2),
     (dict(partition_blocks=-3), -2),
+    (dict(window=-1), -2),
+    (dict(window=64, sinks=-1), -2),
     (dict(q_dtype=2), -3),                 # q bf16, cache f16
     (dict(out_dtype=0), -3),
     (dict(kv_dtype=3, q_dtype=3, out_dtype=3), -3),  # fp8 through the non-fp8 entry
@@ -118,6 +120,16 @@ def test_partition_plan(B, Hkv, maxb, parts):
     assert pkv.decode_num_partitions(d) == parts
     ws = pkv.decode_workspace_bytes(d)
     assert ws == (0 if parts == 1 else B * Hkv * 4 * parts * (128 + 2) * 4)
+
+
+def test_window_shrinks_the_partition_plan():
+    # 16 sequences x 8 KV heads = 128 units -> 4 partitions of the full context
+    d = _dims(num_seqs=16)
+    assert pkv.decode_num_partitions(d) == 4
+    # a 256-token window with 4 sinks attends at most 16 + 1 + 1 = 18 blocks
+    d = _dims(num_seqs=16, window=256, sinks=4)
+    assert pkv.decode_num_partitions(d) == 2          # 18 blocks, >= 16 per partition
+    assert pkv.decode_workspace_bytes(d) == 16 * 64 * 2 * (128 + 2) * 4
 
 
 def test_explicit_partition_size():

@@ -118,6 +118,40 @@ def test_decode_matches_oracle(name):
         assert (got[zero] == 0).all()
 
 
+WINDOWED = [
+    # (case, window, sinks, partition_blocks)
+    ("ragged_f16_g8_d128", 1, 0, 0),
+    ("ragged_f16_g8_d128", 16, 0, 0),
+    ("ragged_f16_g8_d128", 17, 4, 1),
+    ("ragged_f16_g8_d128", 100, 20, 2),
+    ("ragged_bf16_g4_d64", 33, 1, 0),
+    ("ragged_bf16_g4_d64", 48, 64, 1),       # sinks overlap the window
+    ("ragged_f32_g1_d64", 5, 3, 0),
+    ("ragged_fp8_g2_d128_f32", 64, 16, 1),
+    ("ragged_bf16_g8_d128_append", 30, 2, 0),
+    ("long_fp8_small", 1024, 32, 0),
+    ("llama3_8b_bf16_small", 700, 4, 0),
+]
+
+
+@pytest.mark.parametrize("case,window,sinks,pb", WINDOWED)
+def test_sliding_window_and_sinks(case, window, sinks, pb):
+    spec = SMALL[case]
+    lay = build_layout(spec)
+    say(f"[window] {case}: W={window} S={sinks} partition_blocks={pb} lens={list(lay.context_lens[:12])}")
+    x = make_host_inputs(lay)
+    xs = _to_dev(x)
+    out = _out(spec)
+    run_step(xs, 0, spec, out, partition_blocks=pb, window=window, sinks=sinks)
+    torch.cuda.synchronize()
+    got = out_f64(out)
+    ref = oracle_rows(host_layer(x, 0), lay, spec, window=window, sinks=sinks)
+    err = max_err(got, ref)
+    say(f"    max|err| = {err:.3e} (tol {TOL[spec.kv_dtype]})")
+    assert np.isfinite(got).all()
+    assert err <= TOL[spec.kv_dtype]
+
+
 @pytest.mark.parametrize("pb", [1, 2, 3, 7])
 def test_split_size_invariance(pb):
     say(f"[split] tiny_f32 partition_blocks={pb}")

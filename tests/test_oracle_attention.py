@@ -191,7 +191,35 @@ def check_invariances(mod):
                                run_oracle(mod, q, kd, vd, td, Ld, 0.3), atol=1e-13)
 
 
-PINS = [check_against_sdpa, check_closed_forms, check_invariances]
+def check_window_against_masked_sdpa(mod):
+    """Sliding window + sinks against float64 SDPA with an explicit mask built
+    from the definition (the last W positions and the first S positions)."""
+    rng = np.random.default_rng(11)
+    D, Hkv, g = 16, 2, 2
+    lens = [1, 7, 16, 17, 40, 70]
+    q, sk, sv = random_case(rng, len(lens), Hkv * g, Hkv, D, lens)
+    q = q.astype(np.float32).astype(np.float64)
+    sk = [k.astype(np.float32).astype(np.float64) for k in sk]
+    sv = [v.astype(np.float32).astype(np.float64) for v in sv]
+    kc, vc, t, L = paged_from_contiguous(sk, sv, 20, seed=21)
+    for W, S in [(1, 0), (5, 0), (16, 1), (17, 4), (33, 2), (500, 3), (3, 50)]:
+        got = run_oracle(mod, q, kc, vc, t, L, 0.25, window=W, sinks=S)
+        for b, Lb in enumerate(lens):
+            pos = np.arange(Lb)
+            keep = (pos >= Lb - W) | (pos < S)
+            K = torch.from_numpy(sk[b]).permute(1, 0, 2).repeat_interleave(g, 0).contiguous()
+            V = torch.from_numpy(sv[b]).permute(1, 0, 2).repeat_interleave(g, 0).contiguous()
+            qq = torch.from_numpy(q[b])[:, None, :]
+            mask = torch.from_numpy(keep)[None, None, :]
+            ref = F.scaled_dot_product_attention(qq, K, V, attn_mask=mask, scale=0.25)[:, 0, :].numpy()
+            np.testing.assert_allclose(got[b], ref, atol=1e-12)
+    # window 1 without sinks: the newest token's V exactly
+    got = run_oracle(mod, q, kc, vc, t, L, 0.25, window=1)
+    for b, Lb in enumerate(lens):
+        np.testing.assert_array_equal(got[b], np.repeat(sv[b][Lb - 1], g, axis=0))
+
+
+PINS = [check_against_sdpa, check_closed_forms, check_invariances, check_window_against_masked_sdpa]
 
 
 # --------------------------------------------------------------------------
@@ -264,6 +292,16 @@ def test_locate_matches_pool_bookkeeping_on_workloads():
             assert len(slots) == lay.context_lens[b]
 
 
+def test_attended_positions_definition():
+    from oracle import attended_positions
+    assert list(attended_positions(10)) == list(range(10))
+    assert list(attended_positions(10, window=3)) == [7, 8, 9]
+    assert list(attended_positions(10, window=3, sinks=2)) == [0, 1, 7, 8, 9]
+    assert list(attended_positions(4, window=3, sinks=2)) == [0, 1, 2, 3]
+    assert list(attended_positions(0, window=3, sinks=2)) == []
+    assert list(attended_positions(5, window=0, sinks=2)) == list(range(5))
+
+
 def test_sequence_subset_selection():
     rng = np.random.default_rng(5)
     q, sk, sv = random_case(rng, 3, 8, 2, 16, [9, 20, 33])
@@ -312,6 +350,9 @@ MUTANTS = {
     "normalise_by_length": ("out[r, c] = (w @ V[:, h, :]) / w.sum()", "out[r, c] = (w @ V[:, h, :]) / len(w)"),
     "exponent_sign": ("w = np.exp(s - s.max())", "w = np.exp(s.max() - s)"),
     "fp8_scale_ignored": ("vals = vals * s[blk[:, None], kv_heads[None, :]][:, :, None]", "vals = vals"),
+    "window_off_by_one": ("recent = np.arange(max(0, L - int(window)), L)",
+                          "recent = np.arange(max(0, L - int(window) + 1), L)"),
+    "sinks_ignored": ("first = np.arange(min(int(sinks), L))", "first = np.arange(0)"),
     "query_head_index": ("qv = stored_to_f64(np.asarray(q)[seqs][:, q_heads], q_tag)",
                          "qv = stored_to_f64(np.asarray(q)[seqs][:, q_heads][:, ::-1], q_tag)"),
 }
