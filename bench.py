@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Decode-step benchmark: paged decode attention KV GB/s on one MI355X.
 
-One step = for every layer: kv_append of each sequence's new token, then
-paged_decode_attn over all cached tokens (the whole hot path), on synthetic
+One step = for every layer: kv_append of each sequence's new token (fp8
+caches quantise it on write), then paged_decode_attn over all cached tokens
+(the whole hot path), on synthetic
 seeded inputs already resident in HBM.  Default workload: the 70B-shaped
 fp16 step (80 layers, 64 sequences x 4096 tokens, 64 query / 8 KV heads,
 head_dim 128).
@@ -117,8 +118,16 @@ def cpu_baseline(spec, lay, x, budget_s: float):
             if spec.append:
                 s = int(lay.slot_mapping[b])
                 slot = np.array([int(np.nonzero(used == s // 16)[0][0]) * 16 + s % 16])
-                kc = oracle.kv_append_bits(kc, host(x["k_new"][layer][b : b + 1]), slot)
-                vc = oracle.kv_append_bits(vc, host(x["v_new"][layer][b : b + 1]), slot)
+                kn = host(x["k_new"][layer][b : b + 1])
+                vn = host(x["v_new"][layer][b : b + 1])
+                if "k_scales" in x:
+                    kn = oracle.stored_to_f64(kn, spec.q_dtype).astype(np.float32)
+                    vn = oracle.stored_to_f64(vn, spec.q_dtype).astype(np.float32)
+                    kc, kw["k_scales"] = oracle.kv_append_fp8(kc, kw["k_scales"], kn, slot, first_write=False)
+                    vc, kw["v_scales"] = oracle.kv_append_fp8(vc, kw["v_scales"], vn, slot, first_write=False)
+                else:
+                    kc = oracle.kv_append_bits(kc, kn, slot)
+                    vc = oracle.kv_append_bits(vc, vn, slot)
             oracle.paged_decode_attention(q, kc, vc, table, lens, spec.scale, q_tag=spec.q_dtype,
                                           kv_tag=spec.kv_dtype, **kw)
             elapsed += time.perf_counter() - t0
@@ -340,11 +349,14 @@ def main():
     def step(ev=None):
         for layer in range(nl):
             kc, vc = x["k_cache"][layer], x["v_cache"][layer]
-            if spec.append:
+            kw = dict(k_scales=x["k_scales"][layer], v_scales=x["v_scales"][layer]) if fp8 else {}
+            if spec.append and fp8:
+                pkv.kv_append_fp8(x["k_new"][layer], x["v_new"][layer], x["slot_mapping"], kc, vc,
+                                  kw["k_scales"], kw["v_scales"])
+            elif spec.append:
                 pkv.kv_append(x["k_new"][layer], x["v_new"][layer], x["slot_mapping"], kc, vc)
             if ev is not None:
                 ev[layer][0].record()
-            kw = dict(k_scales=x["k_scales"][layer], v_scales=x["v_scales"][layer]) if fp8 else {}
             pkv.paged_decode_attn(x["q"][layer], kc, vc, x["block_tables"], x["context_lens"],
                                   spec.scale, outs[layer], workspace=ws,
                                   partition_blocks=args.partition_blocks, window=args.window,

@@ -105,6 +105,32 @@ PKV_API int pkv_kv_append(const void* k_new, const void* v_new, const int64_t* s
                   int32_t head_dim, int32_t num_blocks, int32_t block_size, int32_t dtype,
                   hipStream_t stream);
 
+typedef enum {
+  PKV_SCALE_GIVEN = 0,      /* scales are set by the caller (e.g. calibrated) */
+  PKV_SCALE_FIRST_WRITE = 1 /* a block's first token (offset 0) sets its scale */
+} pkv_scale_mode;
+
+/*
+ * FP8 append, quantising on write ("The KV Cache memory ledger" 7: 8-bit
+ * K/V with one scale per head; "Why does KV Cache eat GPU memory?": FP8 KV
+ * needs calibrated scales).  Caches hold e4m3fn codes [NB][Hkv][16][D];
+ * k_scales, v_scales are fp32 [NB][Hkv] (device, read and, in first-write
+ * mode, written).  k_new, v_new: [T][Hkv][D] of src_dtype (F32/F16/BF16).
+ * For every t with 0 <= slot < NB*16, blk = slot/16, off = slot%16, head h:
+ *   - PKV_SCALE_FIRST_WRITE and off == 0: scale[blk][h] = max_d |x| / 448 in
+ *     fp32 (1.0 if that max is 0), set for all such tokens of the call before
+ *     any token is quantised;
+ *   - code = round-to-nearest-even(clamp(x / scale[blk][h], -448, 448)), the
+ *     quotient a correctly rounded fp32 division; values beyond 448*scale
+ *     saturate; NaN stays NaN.
+ * head_dim must be a multiple of 16 (<= 1024).  Slots must be distinct.
+ */
+PKV_API int pkv_kv_append_fp8(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                              void* k_cache, void* v_cache, float* k_scales, float* v_scales,
+                              int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t num_blocks, int32_t block_size, int32_t src_dtype,
+                              int32_t scale_mode, hipStream_t stream);
+
 /*
  * Bytes of workspace pkv_paged_decode_attn(_fp8) needs for `dims`; 0 when the
  * context is not split.  Depends only on `dims` (never on the device or on

@@ -39,7 +39,7 @@ pages print); none is "parity unpinned".
 from .fp8_e4m3 import decode_e4m3fn, encode_e4m3fn_rne, E4M3_MAX, E4M3_NAN_CODES
 from .values import stored_to_f64
 from .paged_attention import locate, gather_sequence, paged_decode_attention, attended_positions
-from .kv_append import kv_append_bits
+from .kv_append import kv_append_bits, kv_append_fp8
 from .kv_bytes import kv_bytes_per_token, kv_bytes
 
 __all__ = [
@@ -53,6 +53,7 @@ __all__ = [
     "paged_decode_attention",
     "attended_positions",
     "kv_append_bits",
+    "kv_append_fp8",
     "kv_bytes_per_token",
     "kv_bytes",
 ]

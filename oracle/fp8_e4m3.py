@@ -44,25 +44,27 @@ def encode_e4m3fn_rne(x) -> np.ndarray:
     """float64 values -> uint8 codes: nearest finite code, ties to even code.
 
     Values beyond +-448 saturate to +-448 (the inputs are clamped first, as
-    the quantiser does); NaN maps to 0x7F.  Brute force over all finite codes:
-    slow, but it follows the definition of round-to-nearest-even directly.
+    the quantiser does); NaN maps to 0x7F.  Brute force over all finite codes
+    of the input's sign: slow, but it follows the definition of
+    round-to-nearest-even directly.
     """
     v = np.asarray(x, dtype=np.float64)
     flat = v.reshape(-1)
     # Candidates carry the sign of the input, so a value that rounds to zero
     # keeps its sign (-0 is the code 0x80).
     pos_codes = np.arange(0x00, 0x7F, dtype=np.int64)      # 0x7F is NaN
-    neg_codes = pos_codes | 0x80
     out = np.empty(flat.shape, dtype=np.uint8)
-    for idx, val in enumerate(flat):
-        if np.isnan(val):
-            out[idx] = 0x7F
-            continue
-        val = min(max(val, -E4M3_MAX), E4M3_MAX)
-        cands_all = neg_codes if np.signbit(val) else pos_codes
-        dist = np.abs(_TABLE[cands_all] - val)
-        cands = cands_all[dist == dist.min()]
-        # At most two codes tie (neighbours); the even one has mantissa LSB 0.
-        even = cands[(cands & 1) == 0]
-        out[idx] = int(even[0] if len(even) else cands[0])
+    chunk = 1 << 16
+    for lo in range(0, flat.size, chunk):
+        val = flat[lo:lo + chunk]
+        nan = np.isnan(val)
+        mag = np.minimum(np.abs(np.where(nan, 0.0, val)), E4M3_MAX)
+        dist = np.abs(_TABLE[pos_codes][None, :] - mag[:, None])          # [n, 127]
+        best = dist.min(axis=1, keepdims=True)
+        tie = dist == best
+        # at most two neighbouring codes tie; prefer the even one (mantissa LSB 0)
+        even = tie & ((pos_codes[None, :] & 1) == 0)
+        pick = np.where(even.any(axis=1), even.argmax(axis=1), tie.argmax(axis=1))
+        code = pos_codes[pick] | np.where(np.signbit(val), 0x80, 0x00)
+        out[lo:lo + chunk] = np.where(nan, 0x7F, code).astype(np.uint8)
     return out.reshape(v.shape)

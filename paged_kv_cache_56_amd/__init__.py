@@ -25,6 +25,7 @@ __all__ = [
     "library_path",
     "load_library",
     "kv_append",
+    "kv_append_fp8",
     "paged_decode_attn",
     "decode_dims",
     "decode_workspace_bytes",
@@ -92,6 +93,8 @@ def load_library() -> ctypes.CDLL:
     dims_p = ctypes.POINTER(DecodeDims)
     lib.pkv_kv_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.pkv_kv_append.restype = ctypes.c_int
+    lib.pkv_kv_append_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.pkv_kv_append_fp8.restype = ctypes.c_int
     lib.pkv_decode_workspace_bytes.argtypes = [dims_p]
     lib.pkv_decode_workspace_bytes.restype = sz
     lib.pkv_decode_num_partitions.argtypes = [dims_p]
@@ -165,6 +168,35 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tens
     _check(lib.pkv_kv_append(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache),
                              _ptr(v_cache), T, H, D, k_cache.shape[0], k_cache.shape[2],
                              _code(k_cache), _stream(k_cache)))
+
+
+SCALE_GIVEN, SCALE_FIRST_WRITE = 0, 1
+
+
+def kv_append_fp8(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                  k_cache: torch.Tensor, v_cache: torch.Tensor, k_scales: torch.Tensor,
+                  v_scales: torch.Tensor, *, first_write: bool = False) -> None:
+    """Quantise token t's K/V rows (f32/f16/bf16) into fp8 e4m3 caches at its slot.
+
+    k_new, v_new: [T, Hkv, D]; caches: uint8 or float8_e4m3fn [NB, Hkv, 16, D];
+    scales: fp32 [NB, Hkv].  With first_write=True the token that opens a block
+    sets that block's scale to max|x|/448 first; otherwise the given scales are used.
+    """
+    lib = load_library()
+    _dev(k_new, v_new, slot_mapping, k_cache, v_cache, k_scales, v_scales)
+    _need(k_new.shape == v_new.shape and k_new.dim() == 3, "k_new/v_new must be [T, Hkv, D]")
+    _need(k_cache.shape == v_cache.shape and k_cache.dim() == 4 and _code(k_cache) == 3,
+          "caches must be fp8 [NB, Hkv, 16, D]")
+    T, H, D = k_new.shape
+    _need(k_cache.shape[1] == H and k_cache.shape[3] == D, "cache and new-token shapes differ")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (T,), "slot_mapping must be int64 [T]")
+    _need(k_scales.dtype == v_scales.dtype == torch.float32 and
+          k_scales.shape == v_scales.shape == k_cache.shape[:2], "scales must be fp32 [NB, Hkv]")
+    _need(k_new.dtype == v_new.dtype and _code(k_new) in (0, 1, 2), "k_new/v_new must be f32/f16/bf16")
+    _check(lib.pkv_kv_append_fp8(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache),
+                                 _ptr(v_cache), _ptr(k_scales), _ptr(v_scales), T, H, D,
+                                 k_cache.shape[0], k_cache.shape[2], _code(k_new),
+                                 SCALE_FIRST_WRITE if first_write else SCALE_GIVEN, _stream(k_cache)))
 
 
 def decode_dims(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor,

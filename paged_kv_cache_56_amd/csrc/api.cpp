@@ -115,6 +115,24 @@ int pkv_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapp
                           num_kv_heads, row_bytes, num_blocks, stream);
 }
 
+int pkv_kv_append_fp8(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                      void* k_cache, void* v_cache, float* k_scales, float* v_scales,
+                      int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t num_blocks, int32_t block_size, int32_t src_dtype,
+                      int32_t scale_mode, hipStream_t stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0)
+    return PKV_ERR_SHAPE;
+  if (block_size != PKV_BLOCK_SIZE || head_dim % 16 || head_dim > 1024) return PKV_ERR_SHAPE;
+  if (src_dtype != PKV_F32 && src_dtype != PKV_F16 && src_dtype != PKV_BF16) return PKV_ERR_DTYPE;
+  if (scale_mode != PKV_SCALE_GIVEN && scale_mode != PKV_SCALE_FIRST_WRITE) return PKV_ERR_SHAPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache || !k_scales || !v_scales)
+    return PKV_ERR_NULL;
+  return launch_kv_append_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scales, v_scales,
+                              num_tokens, num_kv_heads, head_dim, num_blocks, src_dtype,
+                              scale_mode == PKV_SCALE_FIRST_WRITE, stream);
+}
+
 size_t pkv_decode_workspace_bytes(const pkv_decode_dims* dims) {
   if (check_dims(dims) != PKV_OK) return 0;
   return workspace_bytes_for(*dims);

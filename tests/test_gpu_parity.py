@@ -11,7 +11,8 @@ import torch
 import oracle
 import paged_kv_cache_56_amd as pkv
 from workloads import WORKLOADS, DecodeWorkload, build_layout, make_host_inputs, make_device_inputs, scaled
-from gpu_common import TOL, say, host_storage, run_step, oracle_rows, host_layer, out_f64, max_err
+from gpu_common import (TOL, say, host_storage, run_step, oracle_rows, oracle_append, host_layer,
+                        out_f64, max_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,6 +51,68 @@ def test_kv_append_bit_exact(dt):
         ref = oracle.kv_append_bits(host_storage(x[name][0]), host_storage(x[new][0]), slots)
         got = host_storage(xs[name][0])
         assert np.array_equal(got.view(np.uint8), ref.view(np.uint8)), name
+
+
+@pytest.mark.parametrize("src", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("first_write", [False, True])
+def test_kv_append_fp8_bit_exact(src, first_write):
+    """Codes and scales equal the oracle's bit for bit, including several
+    tokens of one call landing in one fresh block (first-write ordering)."""
+    say(f"[kv_append_fp8] src={src} first_write={first_write}")
+    rng = np.random.default_rng(5)
+    NB, H, D, T = 12, 4, 128, 21
+    codes = rng.integers(0, 0x7E, size=(NB, H, 16, D)).astype(np.uint8)
+    scales = rng.uniform(0.002, 0.05, size=(NB, H)).astype(np.float32)
+    x = torch.from_numpy(rng.standard_normal((T, H, D)).astype(np.float32) * 2).to(TORCH_DT[src])
+    x[3] *= 40                                           # exceeds 448 * scale somewhere
+    slots = np.array([0, 1, 2, 3, 4, 5, 16, 33, -1, 48, 49, 50, 51, 52, 53, 54, 55, 56, 57, 190,
+                      NB * 16 + 3], dtype=np.int64)
+    xs = host_storage(x)
+    xf = oracle.stored_to_f64(xs, src).astype(np.float32)
+    ref_c, ref_s = oracle.kv_append_fp8(codes, scales, xf, slots, first_write=first_write)
+    dc = torch.from_numpy(codes).to(DEV)
+    dv = torch.from_numpy(codes).to(DEV)
+    ks = torch.from_numpy(scales).to(DEV)
+    vs = torch.from_numpy(scales).to(DEV)
+    xd = x.to(DEV)
+    pkv.kv_append_fp8(xd, xd, torch.from_numpy(slots).to(DEV), dc, dv, ks, vs, first_write=first_write)
+    torch.cuda.synchronize()
+    for c_, s_ in ((dc, ks), (dv, vs)):
+        assert np.array_equal(c_.cpu().numpy(), ref_c)
+        assert np.array_equal(s_.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+
+
+def test_fp8_quantise_ties_saturation_and_subnormals():
+    """Scale 1: the codes are the hardware's RNE e4m3 of the clamped values --
+    every tie between neighbouring codes and both fp32 neighbours of it,
+    the subnormal range, zeros, and values past 448 (including infinity)."""
+    say("[kv_append_fp8] rounding edge cases")
+    vals = np.sort(oracle.decode_e4m3fn(np.arange(0, 0x7F, dtype=np.uint8)))
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)
+    edge = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(np.inf)),
+                           np.float32([0.0, -0.0, 447.9, 448.0, 449.0, 464.0, 465.0, 1e6, np.inf, 2.0**-10,
+                                       2.0**-11, 3 * 2.0**-11, 1e-30])]).astype(np.float32)
+    edge = np.concatenate([edge, -edge])
+    D, H = 128, 1
+    T = -(-edge.size // D)
+    x = np.zeros((T * D,), np.float32)
+    x[: edge.size] = edge
+    x = x.reshape(T, H, D)
+    NB = -(-T // 16)
+    slots = np.arange(T, dtype=np.int64)
+    codes = np.zeros((NB, H, 16, D), np.uint8)
+    ones = np.ones((NB, H), np.float32)
+    ref_c, _ = oracle.kv_append_fp8(codes, ones, x, slots, first_write=False)
+    dc = torch.zeros((NB, H, 16, D), dtype=torch.uint8, device=DEV)
+    dv = torch.zeros_like(dc)
+    s1 = torch.ones((NB, H), device=DEV)
+    s2 = torch.ones((NB, H), device=DEV)
+    xd = torch.from_numpy(x).to(DEV)
+    pkv.kv_append_fp8(xd, xd, torch.from_numpy(slots).to(DEV), dc, dv, s1, s2)
+    torch.cuda.synchronize()
+    got = dc.cpu().numpy()
+    bad = np.argwhere(got != ref_c)
+    assert bad.size == 0, [(tuple(i), int(got[tuple(i)]), int(ref_c[tuple(i)])) for i in bad[:8]]
 
 
 def test_kv_append_skips_out_of_pool_slots():
@@ -318,14 +381,10 @@ def test_full_size_sampled_rows(name):
     tol = TOL[spec.kv_dtype]
     for layer in layers:
         h, tables, slots = snaps[layer]
-        kc, vc = h["k_cache"], h["v_cache"]
-        if slots is not None:
-            kc = oracle.kv_append_bits(kc, h["k_new"], slots)
-            vc = oracle.kv_append_bits(vc, h["v_new"], slots)
+        kc, vc, ks, vs = oracle_append(h, spec, slots)
         ref = oracle.paged_decode_attention(h["q"], kc, vc, tables, lay.context_lens, spec.scale,
                                             q_tag=spec.q_dtype, kv_tag=spec.kv_dtype,
-                                            k_scales=h.get("k_scales"), v_scales=h.get("v_scales"),
-                                            seqs=seqs, q_heads=heads)
+                                            k_scales=ks, v_scales=vs, seqs=seqs, q_heads=heads)
         got = out_f64(outs[layer])[seqs][:, heads]
         err = max_err(got, ref)
         say(f"    layer {layer} seqs {seqs} heads {heads}: max|err| = {err:.3e} (tol {tol})")

@@ -80,3 +80,73 @@ def test_matches_torch_index_copy():
     t.index_copy_(0, torch.from_numpy(slots), torch.from_numpy(new))
     ref = t.reshape(NB, BS, H, D).permute(0, 2, 1, 3).numpy()
     assert np.array_equal(ours.view(np.uint16), ref.view(np.uint16))
+
+
+# --------------------------------------------------------------------------
+# FP8 quantise-on-write
+# --------------------------------------------------------------------------
+
+from oracle import kv_append_fp8, decode_e4m3fn
+
+
+def _fp8_case(seed=3, T=6, H=2, D=8, NB=5):
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 0x70, size=(NB, H, BS, D)).astype(np.uint8)
+    scales = rng.uniform(0.01, 0.1, size=(NB, H)).astype(np.float32)
+    x = (rng.standard_normal((T, H, D)) * 3).astype(np.float32)
+    return codes, scales, x
+
+
+def test_fp8_append_given_scales_matches_torch_cast():
+    """Codes = torch's float8_e4m3fn cast of the clamped fp32 quotient."""
+    codes, scales, x = _fp8_case()
+    slots = np.array([0, 17, 33, -1, 50, 79])
+    out, sc = kv_append_fp8(codes, scales, x, slots, first_write=False)
+    assert np.array_equal(sc, scales)
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        q = np.clip(x[t] / scales[s // BS][:, None], -448, 448).astype(np.float32)
+        ref = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(out[s // BS, :, s % BS, :], ref)
+    # untouched elsewhere
+    mask = np.ones(codes.shape, bool)
+    for s in slots[slots >= 0]:
+        mask[s // BS, :, s % BS, :] = False
+    assert np.array_equal(out[mask], codes[mask])
+
+
+def test_fp8_append_first_write_sets_scale_then_saturates():
+    codes, scales, x = _fp8_case(T=3)
+    x[1] = x[0] * 4                     # a later token of the same block, 4x larger
+    slots = np.array([32, 33, 48])      # block 2 starts with token 0; block 3 with token 2
+    out, sc = kv_append_fp8(codes, scales, x, slots, first_write=True)
+    for t, blk in ((0, 2), (2, 3)):
+        amax = np.abs(x[t]).max(axis=1)
+        assert np.array_equal(sc[blk], (amax / np.float32(448)).astype(np.float32))
+        row = decode_e4m3fn(out[blk, :, 0 if t == 0 else 0, :])
+        assert np.array_equal(np.abs(row).max(axis=1), [448.0, 448.0])
+    # token 1 reused block 2's scale and saturated where it exceeded 448 * scale
+    dec = decode_e4m3fn(out[2, :, 1, :])
+    big = np.abs(x[1]) / sc[2][:, None] > 448
+    assert big.any() and np.all(np.abs(dec[big]) == 448.0)
+    assert np.array_equal(sc[[0, 1, 4]], scales[[0, 1, 4]])
+
+
+def test_fp8_append_exact_values_round_trip():
+    """x = decode(c) * 2^k is stored as c exactly (power-of-two scales)."""
+    rng = np.random.default_rng(4)
+    c = rng.integers(0, 0x7F, size=(2, 1, 8)).astype(np.uint8)
+    c[c == 0x7F] = 0
+    scales = np.array([[0.25], [8.0]], np.float32)
+    x = (decode_e4m3fn(c)[:, :, :] * scales[[0, 1]][:, :, None]).astype(np.float32)
+    codes = np.zeros((2, 1, BS, 8), np.uint8)
+    out, _ = kv_append_fp8(codes, scales, x, np.array([3, 16 + 5]), first_write=False)
+    assert np.array_equal(out[0, :, 3, :], c[0]) and np.array_equal(out[1, :, 5, :], c[1])
+
+
+def test_fp8_append_zero_token_first_write_scale_is_one():
+    codes, scales, x = _fp8_case(T=1)
+    x[:] = 0
+    out, sc = kv_append_fp8(codes, scales, x, np.array([16]), first_write=True)
+    assert np.all(sc[1] == 1.0) and np.all(out[1, :, 0, :] == 0)

@@ -107,11 +107,15 @@ def test_fp8_quantisation_recipe():
     vals = decode_e4m3fn(codes)
     hist = lay.history_mask
     assert not np.isnan(vals.transpose(0, 2, 1, 3)[hist]).any()
-    # every tile reaches +-448 exactly once scaled: amax code is 0x7E/0xFE
+    # every tile's history reaches +-448 exactly once scaled: amax code is 0x7E/0xFE
     for blk in range(lay.num_blocks):
         for h in range(w.num_kv_heads):
-            assert np.abs(vals[blk, h]).max() == 448.0
+            assert np.abs(vals[blk, h][hist[blk]]).max() == 448.0
             assert scales[blk, h] > 0
+    # the slot the new token goes to is poisoned until the step quantises it
+    s = lay.slot_mapping[0]
+    assert (codes[s // 16, :, s % 16, :] == POISON_FP8_CODE).all()
+    assert x["k_new"].dtype == torch.bfloat16
     assert x["q"].dtype == torch.bfloat16
 
 

@@ -15,8 +15,10 @@ Recipe (all seeded from the workload's seed):
     the slot the new token will be written to) is poisoned with NaN (float
     caches) or the e4m3 NaN code 0x7F (fp8 caches), so a read of it shows up;
   * fp8 caches: per (block, kv_head) tile, scale = amax|x| / 448 in fp32 (1.0
-    for an all-zero tile), code = round-to-nearest-even(x / scale) clamped to
-    +-448, done by torch's float8_e4m3fn cast.
+    for an all-zero tile) over the tile's history tokens, code =
+    round-to-nearest-even(x / scale) clamped to +-448, done by torch's
+    float8_e4m3fn cast; the new token's K/V are drawn in the query dtype and
+    quantised on write, with its block's existing scale, by the step itself.
 """
 
 from __future__ import annotations
@@ -214,10 +216,11 @@ def _make_inputs(layout: DecodeLayout, device: str, layers: Optional[int]) -> Di
     if kv_tag == "fp8_e4m3":
         out["k_scales"], out["v_scales"] = scales["k"], scales["v"]
     if spec.append:
-        if kv_tag == "fp8_e4m3":
-            raise NotImplementedError("this recipe appends only into 16/32-bit caches")
-        out["k_new"] = _normal((nl, B, Hkv, D), gen, device, kv_tag)
-        out["v_new"] = _normal((nl, B, Hkv, D), gen, device, kv_tag)
+        # fp8 caches quantise the new token on write; its K/V arrive in the
+        # query's dtype
+        src_tag = spec.q_dtype if kv_tag == "fp8_e4m3" else kv_tag
+        out["k_new"] = _normal((nl, B, Hkv, D), gen, device, src_tag)
+        out["v_new"] = _normal((nl, B, Hkv, D), gen, device, src_tag)
         out["slot_mapping"] = torch.from_numpy(layout.slot_mapping).to(device)
     out["block_tables"] = torch.from_numpy(layout.block_tables).to(device)
     out["context_lens"] = torch.from_numpy(layout.context_lens).to(device)

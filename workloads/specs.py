@@ -78,7 +78,7 @@ WORKLOADS = {
         name="long_fp8", seed=56004, num_layers=1, num_seqs=8,
         num_q_heads=32, num_kv_heads=8, head_dim=128,
         kv_dtype="fp8_e4m3", q_dtype="bf16", out_dtype="bf16",
-        len_range=(131072, 131072), append=False,
+        len_range=(131072, 131072), append=True,
         description="long-context FP8 e4m3 KV, GQA-4, B=8 x 131072, bf16 q/out, split + merge",
     ),
 }
