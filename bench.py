@@ -178,6 +178,36 @@ def read_probe(dev, gib: int = 4):
     return {"gbs": best, "bytes": gib * 2**30}
 
 
+def copy_blocks_rate(x, spec, pairs: int):
+    """Copy-on-write block copies on layer 0's caches: `pairs` random
+    (src, dst) pairs with distinct destinations, each moving a whole block of
+    K and V (every head) -- read once, written once."""
+    import torch
+
+    import paged_kv_cache_56_amd as pkv
+
+    kc, vc = x["k_cache"][0], x["v_cache"][0]
+    nb = kc.shape[0]
+    pairs = min(pairs, nb // 2, 65535)
+    g = torch.Generator().manual_seed(spec.seed)
+    perm = torch.randperm(nb, generator=g)
+    src = perm[:pairs].to(torch.int32).to(kc.device)
+    dst = perm[pairs:2 * pairs].to(torch.int32).to(kc.device)
+    kw = dict(k_scales=x["k_scales"][0], v_scales=x["v_scales"][0]) if "k_scales" in x else {}
+    pkv.copy_blocks(kc, vc, src, dst, **kw)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        pkv.copy_blocks(kc, vc, src, dst, **kw)
+    e1.record()
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) / 1e3 / reps
+    moved = 2 * pairs * kc[0].numel() * kc.element_size() * 2      # K and V, read + write
+    return {"pairs": pairs, "block_bytes": kc[0].numel() * kc.element_size(), "us": round(s * 1e6, 2),
+            "gbs": round(moved / s / 1e9, 1)}
+
+
 def kernel_source_sha() -> str:
     """sha256 over the HIP sources and headers the library is built from."""
     import hashlib
@@ -303,6 +333,8 @@ def main():
     ap.add_argument("--window", type=int, default=0, help="sliding window W (0 = whole context)")
     ap.add_argument("--sinks", type=int, default=0, help="attention-sink tokens kept with a window")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="0 skips the CPU baseline")
+    ap.add_argument("--copy-pairs", type=int, default=0,
+                    help="also time copy-on-write copies of this many random block pairs")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the plain-read bandwidth probe and the copy used to calibrate counters")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "STATS_CSV"),
@@ -390,6 +422,11 @@ def main():
     log(f"[bench] {ms_per_step:.3f} ms/step; attention launch {mean_launch_s * 1e6:.1f} us "
         f"-> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of peak)")
 
+    copy_rec = None
+    if args.copy_pairs > 0:
+        copy_rec = copy_blocks_rate(x, spec, args.copy_pairs)
+        log(f"[bench] copy-on-write copies: {copy_rec['pairs']} block pairs, {copy_rec['gbs']:.0f} GB/s")
+
     probe = None
     if not args.no_probe:
         probe = read_probe(dev)
@@ -445,6 +482,8 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if copy_rec is not None:
+        rec["copy_blocks"] = copy_rec
     print(json.dumps(rec), flush=True)
 
 

@@ -69,7 +69,9 @@ typedef enum {
                              negative window or sinks */
   PKV_ERR_DTYPE = -3,     /* unsupported dtype or dtype combination */
   PKV_ERR_WORKSPACE = -4, /* workspace missing or smaller than required */
-  PKV_ERR_LAUNCH = -5     /* the HIP runtime refused a launch */
+  PKV_ERR_LAUNCH = -5,    /* the HIP runtime refused a launch */
+  PKV_ERR_NO_BLOCKS = -6, /* block manager: not enough free blocks (nothing changed) */
+  PKV_ERR_SEQUENCE = -7   /* block manager: unknown or duplicate sequence id */
 } pkv_status;
 
 typedef struct {
@@ -185,6 +187,59 @@ PKV_API int pkv_paged_decode_attn_fp8(const void* q, const void* k_cache, const 
  */
 PKV_API int pkv_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t sink_words,
                                hipStream_t stream);
+
+/*
+ * Copy-on-write block copies ("Large-model inference KV Cache memory
+ * optimisation" 3.2: copy a shared block before writing into it).  For every
+ * i < num_pairs, block dst_blocks[i] of both caches receives a bit copy of
+ * block src_blocks[i] (every KV head, all 16 slots), and for fp8 caches the
+ * scales k_scales/v_scales[dst][h] receive those of src (pass NULL scales for
+ * other dtypes).  src_blocks, dst_blocks: int32 device arrays.  Destinations
+ * must be distinct and not also sources in the same call; ids outside
+ * [0, num_blocks) are skipped.  num_pairs <= 65535.
+ */
+PKV_API int pkv_copy_blocks(void* k_cache, void* v_cache, float* k_scales, float* v_scales,
+                            const int32_t* src_blocks, const int32_t* dst_blocks, int32_t num_pairs,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                            int32_t dtype, hipStream_t stream);
+
+/*
+ * Host block manager ("Large-model inference KV Cache memory optimisation"
+ * 2.2-2.3 pool and recycling, 3.1-3.2 shared blocks, reference counts and
+ * copy-on-write; "The KV Cache memory ledger" 4).  Host memory only; every
+ * call is thread-safe (one internal lock; reference counts are atomic).
+ *   create: `num_blocks` blocks of 16 tokens; free_order (may be NULL =
+ *     0, 1, 2, ...) is the order in which fresh blocks are handed out; freed
+ *     blocks are handed out again first, most recently freed first.
+ *     Returns NULL for bad arguments.
+ *   fork: `child` references every block of `parent` (the partial last one
+ *     too) and has its length.
+ *   append_slots: reserves the next position of each of seqs[0..n) (distinct)
+ *     and writes its flat slot to slots_out[i].  A new block is taken when
+ *     the position opens a block; when it falls in a partial last block that
+ *     other sequences still reference, a fresh block replaces it and the pair
+ *     (old, fresh) is written to copy_src/copy_dst (capacity >= n): run
+ *     pkv_copy_blocks on those pairs before appending.  Fails with
+ *     PKV_ERR_NO_BLOCKS, changing nothing, if the pool is short.
+ *   free_sequence: drops one reference from each of its blocks; blocks at
+ *     zero return to the pool.
+ *   block_tables: rows of max_blocks int32 (padded with -1) and lengths for
+ *     seqs[0..n), ready for pkv_paged_decode_attn after a copy to the device.
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+PKV_API pkv_block_manager* pkv_bm_create(int32_t num_blocks, int32_t block_size,
+                                         const int32_t* free_order);
+PKV_API void pkv_bm_destroy(pkv_block_manager* bm);
+PKV_API int pkv_bm_add_sequence(pkv_block_manager* bm, int64_t seq);
+PKV_API int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child);
+PKV_API int pkv_bm_append_slots(pkv_block_manager* bm, const int64_t* seqs, int32_t n,
+                                int64_t* slots_out, int32_t* copy_src, int32_t* copy_dst,
+                                int32_t copy_capacity, int32_t* num_copies);
+PKV_API int pkv_bm_free_sequence(pkv_block_manager* bm, int64_t seq);
+PKV_API int pkv_bm_num_free(pkv_block_manager* bm);
+PKV_API int pkv_bm_refcount(pkv_block_manager* bm, int32_t block);
+PKV_API int pkv_bm_block_tables(pkv_block_manager* bm, const int64_t* seqs, int32_t n,
+                                int32_t max_blocks, int32_t* tables_out, int32_t* lens_out);
 
 /* Static text for a status code. */
 PKV_API const char* pkv_status_string(int status);

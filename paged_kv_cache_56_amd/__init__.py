@@ -26,6 +26,8 @@ __all__ = [
     "load_library",
     "kv_append",
     "kv_append_fp8",
+    "copy_blocks",
+    "BlockManager",
     "paged_decode_attn",
     "decode_dims",
     "decode_workspace_bytes",
@@ -106,6 +108,23 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_paged_decode_attn_fp8.restype = ctypes.c_int
     lib.pkv_hbm_read_probe.argtypes = [vp, sz, vp, i32, vp]
     lib.pkv_hbm_read_probe.restype = ctypes.c_int
+    i64, i32p, i64p = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    lib.pkv_copy_blocks.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    lib.pkv_copy_blocks.restype = ctypes.c_int
+    lib.pkv_bm_create.argtypes = [i32, i32, i32p]
+    lib.pkv_bm_create.restype = vp
+    lib.pkv_bm_destroy.argtypes = [vp]
+    lib.pkv_bm_destroy.restype = None
+    lib.pkv_bm_add_sequence.argtypes = [vp, i64]
+    lib.pkv_bm_fork.argtypes = [vp, i64, i64]
+    lib.pkv_bm_append_slots.argtypes = [vp, i64p, i32, i64p, i32p, i32p, i32, i32p]
+    lib.pkv_bm_free_sequence.argtypes = [vp, i64]
+    lib.pkv_bm_num_free.argtypes = [vp]
+    lib.pkv_bm_refcount.argtypes = [vp, i32]
+    lib.pkv_bm_block_tables.argtypes = [vp, i64p, i32, i32, i32p, i32p]
+    for f in ("pkv_bm_add_sequence", "pkv_bm_fork", "pkv_bm_append_slots", "pkv_bm_free_sequence",
+              "pkv_bm_num_free", "pkv_bm_refcount", "pkv_bm_block_tables"):
+        getattr(lib, f).restype = ctypes.c_int
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_version.argtypes = []
@@ -197,6 +216,88 @@ def kv_append_fp8(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.
                                  _ptr(v_cache), _ptr(k_scales), _ptr(v_scales), T, H, D,
                                  k_cache.shape[0], k_cache.shape[2], _code(k_new),
                                  SCALE_FIRST_WRITE if first_write else SCALE_GIVEN, _stream(k_cache)))
+
+
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src: torch.Tensor, dst: torch.Tensor,
+                k_scales: Optional[torch.Tensor] = None, v_scales: Optional[torch.Tensor] = None) -> None:
+    """Copy-on-write: blocks dst[i] of both caches (and fp8 scales) become bit
+    copies of blocks src[i].  src, dst: int32 [n] on the device."""
+    lib = load_library()
+    _dev(k_cache, v_cache, src, dst, k_scales, v_scales)
+    _need(k_cache.shape == v_cache.shape and k_cache.dim() == 4, "caches must be [NB, Hkv, 16, D]")
+    _need(src.dtype == dst.dtype == torch.int32 and src.shape == dst.shape and src.dim() == 1,
+          "src/dst must be int32 [n]")
+    NB, H, _, D = k_cache.shape
+    _check(lib.pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales), _ptr(src),
+                               _ptr(dst), src.numel(), H, D, NB, _code(k_cache), _stream(k_cache)))
+
+
+class BlockManager:
+    """The library's host block manager (pool, reference counts, fork,
+    copy-on-write).  See pkv_bm_* in include/pagedkv.h."""
+
+    def __init__(self, num_blocks: int, free_order=None, block_size: int = BLOCK_SIZE):
+        self._lib = load_library()
+        order = None
+        if free_order is not None:
+            arr = (ctypes.c_int32 * num_blocks)(*[int(b) for b in free_order])
+            order = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+        self._h = self._lib.pkv_bm_create(num_blocks, block_size, order)
+        if not self._h:
+            raise ValueError("bad block manager arguments")
+        self.num_blocks = num_blocks
+
+    def close(self) -> None:
+        if self._h:
+            self._lib.pkv_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_sequence(self, seq: int) -> None:
+        _check(self._lib.pkv_bm_add_sequence(self._h, seq))
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(self._lib.pkv_bm_fork(self._h, parent, child))
+
+    def append_slots(self, seqs):
+        """-> (slots list, [(src_block, dst_block), ...] to copy first)."""
+        n = len(seqs)
+        sq = (ctypes.c_int64 * max(n, 1))(*seqs)
+        slots = (ctypes.c_int64 * max(n, 1))()
+        cs = (ctypes.c_int32 * max(n, 1))()
+        cd = (ctypes.c_int32 * max(n, 1))()
+        nc = ctypes.c_int32(0)
+        _check(self._lib.pkv_bm_append_slots(self._h, sq, n, slots, cs, cd, max(n, 1), ctypes.byref(nc)))
+        return list(slots[:n]), [(cs[i], cd[i]) for i in range(nc.value)]
+
+    def free_sequence(self, seq: int) -> None:
+        _check(self._lib.pkv_bm_free_sequence(self._h, seq))
+
+    def num_free(self) -> int:
+        n = self._lib.pkv_bm_num_free(self._h)
+        _check(min(n, 0))
+        return n
+
+    def refcount(self, block: int) -> int:
+        n = self._lib.pkv_bm_refcount(self._h, block)
+        _check(min(n, 0))
+        return n
+
+    def block_tables(self, seqs, max_blocks: int):
+        """-> (int32 tensor [n, max_blocks] padded with -1, int32 tensor [n] lengths), on the CPU."""
+        n = len(seqs)
+        tables = torch.empty((max(n, 1), max_blocks), dtype=torch.int32)
+        lens = torch.empty((max(n, 1),), dtype=torch.int32)
+        sq = (ctypes.c_int64 * max(n, 1))(*seqs)
+        _check(self._lib.pkv_bm_block_tables(
+            self._h, sq, n, max_blocks, ctypes.cast(tables.data_ptr(), ctypes.POINTER(ctypes.c_int32)),
+            ctypes.cast(lens.data_ptr(), ctypes.POINTER(ctypes.c_int32))))
+        return tables[:n], lens[:n]
 
 
 def decode_dims(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor,

@@ -133,6 +133,24 @@ int pkv_kv_append_fp8(const void* k_new, const void* v_new, const int64_t* slot_
                               scale_mode == PKV_SCALE_FIRST_WRITE, stream);
 }
 
+int pkv_copy_blocks(void* k_cache, void* v_cache, float* k_scales, float* v_scales,
+                    const int32_t* src_blocks, const int32_t* dst_blocks, int32_t num_pairs,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t dtype,
+                    hipStream_t stream) {
+  if (num_pairs < 0 || num_pairs > 65535 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0)
+    return PKV_ERR_SHAPE;
+  const int eb = elem_bytes(dtype);
+  if (!eb) return PKV_ERR_DTYPE;
+  const int64_t block_bytes = (int64_t)num_kv_heads * PKV_BLOCK_SIZE * head_dim * eb;
+  if (block_bytes % 16 || block_bytes > (1 << 30)) return PKV_ERR_SHAPE;
+  if (dtype == PKV_FP8_E4M3 ? (!k_scales || !v_scales) : (k_scales || v_scales)) return PKV_ERR_DTYPE;
+  if (dtype == PKV_FP8_E4M3 && num_kv_heads > 256) return PKV_ERR_SHAPE;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !src_blocks || !dst_blocks) return PKV_ERR_NULL;
+  return launch_copy_blocks(k_cache, v_cache, k_scales, v_scales, src_blocks, dst_blocks,
+                            num_pairs, num_kv_heads, (int)block_bytes, num_blocks, stream);
+}
+
 size_t pkv_decode_workspace_bytes(const pkv_decode_dims* dims) {
   if (check_dims(dims) != PKV_OK) return 0;
   return workspace_bytes_for(*dims);
@@ -179,6 +197,8 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_DTYPE: return "unsupported dtype combination";
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_LAUNCH: return "kernel launch failed";
+    case PKV_ERR_NO_BLOCKS: return "block pool exhausted";
+    case PKV_ERR_SEQUENCE: return "unknown or duplicate sequence id";
     default: return "unknown status";
   }
 }

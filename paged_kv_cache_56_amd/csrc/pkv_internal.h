@@ -15,6 +15,10 @@ int launch_kv_append_fp8(const void* k_new, const void* v_new, const int64_t* sl
                          int num_tokens, int num_kv_heads, int head_dim, int num_blocks,
                          int src_dtype, bool first_write, hipStream_t stream);
 
+int launch_copy_blocks(void* k_cache, void* v_cache, float* k_scales, float* v_scales,
+                       const int32_t* src, const int32_t* dst, int n, int num_kv_heads,
+                       int block_bytes, int num_blocks, hipStream_t stream);
+
 struct DecodeArgs {
   const void* q;
   const void* k_cache;

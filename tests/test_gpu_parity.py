@@ -115,6 +115,98 @@ def test_fp8_quantise_ties_saturation_and_subnormals():
     assert bad.size == 0, [(tuple(i), int(got[tuple(i)]), int(ref_c[tuple(i)])) for i in bad[:8]]
 
 
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16", "fp8_e4m3"])
+def test_copy_blocks_bit_exact(dt):
+    say(f"[copy_blocks] dtype={dt}")
+    rng = np.random.default_rng(9)
+    NB, H, D = 40, 4, 128
+    nbytes = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}[dt]
+    raw = rng.integers(0, 256, size=(2, NB, H, 16, D * nbytes), dtype=np.uint8)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "fp8_e4m3": torch.uint8}[dt]
+    kc = torch.from_numpy(raw[0].copy()).view(tdt).to(DEV)
+    vc = torch.from_numpy(raw[1].copy()).view(tdt).to(DEV)
+    src = np.array([3, 7, 11, 0, 39, 5, 2], np.int32)
+    dst = np.array([20, 21, 22, 23, 24, 99, 2], np.int32)     # 99 outside the pool, 2 -> 2 no-op
+    ks = vs = None
+    sc = rng.uniform(size=(2, NB, H)).astype(np.float32)
+    if dt == "fp8_e4m3":
+        ks, vs = torch.from_numpy(sc[0].copy()).to(DEV), torch.from_numpy(sc[1].copy()).to(DEV)
+    pkv.copy_blocks(kc, vc, torch.from_numpy(src).to(DEV), torch.from_numpy(dst).to(DEV), ks, vs)
+    torch.cuda.synchronize()
+    for t, c_ in enumerate((kc, vc)):
+        exp = raw[t].copy()
+        for s_, d_ in zip(src, dst):
+            if d_ < NB and s_ != d_:
+                exp[d_] = raw[t][s_]
+        got = c_.cpu().contiguous().view(torch.uint8).numpy().reshape(exp.shape)
+        assert np.array_equal(got, exp)
+        if ks is not None:
+            e2 = sc[t].copy()
+            for s_, d_ in zip(src, dst):
+                if d_ < NB and s_ != d_:
+                    e2[d_] = sc[t][s_]
+            assert np.array_equal((ks, vs)[t].cpu().numpy(), e2)
+
+
+def test_fork_copy_on_write_end_to_end():
+    """A parent with a partial last block is forked three times; parent and
+    children then append different tokens.  The manager asks for copies, the
+    device copies and appends, and attention for every sequence equals the
+    oracle on each sequence's own contiguous history."""
+    say("[cow] fork + copy-on-write + append + attention")
+    rng = np.random.default_rng(12)
+    NB, H, G, D = 24, 2, 4, 64
+    bm = pkv.BlockManager(NB, free_order=rng.permutation(NB).tolist())
+    kc = torch.full((NB, H, 16, D), float("nan"), dtype=torch.float16, device=DEV)
+    vc = torch.full_like(kc, float("nan"))
+    hist_k, hist_v = {0: []}, {0: []}
+    bm.add_sequence(0)
+
+    def step(seqs):
+        slots, copies = bm.append_slots(seqs)
+        if copies:
+            cs = torch.tensor([c[0] for c in copies], dtype=torch.int32, device=DEV)
+            cd = torch.tensor([c[1] for c in copies], dtype=torch.int32, device=DEV)
+            pkv.copy_blocks(kc, vc, cs, cd)
+        kn = torch.randn((len(seqs), H, D), dtype=torch.float16, device=DEV)
+        vn = torch.randn_like(kn)
+        pkv.kv_append(kn, vn, torch.tensor(slots, dtype=torch.int64, device=DEV), kc, vc)
+        for i, s_ in enumerate(seqs):
+            hist_k[s_].append(kn[i].cpu().float().numpy())
+            hist_v[s_].append(vn[i].cpu().float().numpy())
+        return copies
+
+    for _ in range(20):
+        step([0])
+    for c in (1, 2, 3):
+        bm.fork(0, c)
+        hist_k[c], hist_v[c] = list(hist_k[0]), list(hist_v[0])
+    ncopies = 0
+    for r in range(17):
+        ncopies += len(step([3, 0, 1, 2] if r % 2 else [1, 2, 3, 0]))
+    # the partial block was shared four ways: the first three writers copy it,
+    # the last one is then its only holder and writes in place
+    assert ncopies == 3
+    seqs = [0, 1, 2, 3]
+    tables, lens = bm.block_tables(seqs, 4)
+    q = torch.randn((4, H * G, D), dtype=torch.float16, device=DEV)
+    out = torch.empty_like(q)
+    pkv.paged_decode_attn(q, kc, vc, tables.to(DEV), lens.to(DEV), 0.125, out)
+    torch.cuda.synchronize()
+    got = out_f64(out)
+    for i, s_ in enumerate(seqs):
+        K = np.stack(hist_k[s_]).astype(np.float64)          # [L, H, D]
+        V = np.stack(hist_v[s_]).astype(np.float64)
+        assert int(lens[i]) == len(K)
+        qv = q[i].cpu().double().numpy()
+        for hq in range(H * G):
+            sc = 0.125 * (K[:, hq // G, :] @ qv[hq])
+            w = np.exp(sc - sc.max())
+            ref = (w @ V[:, hq // G, :]) / w.sum()
+            assert np.abs(got[i, hq] - ref).max() <= TOL["f16"]
+    bm.close()
+
+
 def test_kv_append_skips_out_of_pool_slots():
     say("[kv_append] out-of-pool slot")
     kc = torch.zeros((2, 1, 16, 64), dtype=torch.float16, device=DEV)
