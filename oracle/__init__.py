@@ -28,8 +28,10 @@ Readings taken where the pages are silent (each is also a test):
   * query head i uses KV head i // g (contiguous groups of g = Hq / Hkv);
   * the new token is appended first and attended to (lengths count it);
   * a sequence of length 0 yields a zero output row;
-  * fp8 is OCP e4m3fn (bias 7, max 448, no inf, NaN = S.1111.111), and a
-    stored value is code_value * scale with one fp32 scale per (block, head).
+  * fp8 is OCP e4m3fn (bias 7, max 448, no inf, NaN = S.1111.111), int8 is
+    symmetric (codes -127..127), and a stored value is code_value * scale
+    with one fp32 scale per (block, head), times an optional per-(head,
+    channel) factor for K.
 
 Every function here is pinned by a -m "not gpu" test against something other
 than itself (a library routine, a closed form, an invariant, or a number the
@@ -39,7 +41,7 @@ pages print); none is "parity unpinned".
 from .fp8_e4m3 import decode_e4m3fn, encode_e4m3fn_rne, E4M3_MAX, E4M3_NAN_CODES
 from .values import stored_to_f64
 from .paged_attention import locate, gather_sequence, paged_decode_attention, attended_positions
-from .kv_append import kv_append_bits, kv_append_fp8
+from .kv_append import kv_append_bits, kv_append_fp8, kv_append_int8, kv_append_quant
 from .kv_bytes import kv_bytes_per_token, kv_bytes
 
 __all__ = [
@@ -54,6 +56,8 @@ __all__ = [
     "attended_positions",
     "kv_append_bits",
     "kv_append_fp8",
+    "kv_append_int8",
+    "kv_append_quant",
     "kv_bytes_per_token",
     "kv_bytes",
 ]

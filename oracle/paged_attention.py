@@ -16,6 +16,11 @@ What is computed, and where the pages state it:
     consecutive query heads share one K/V head (g = Hq / Hkv; MQA is Hkv = 1).
   * [P5] section 7: quantised K/V carry one scale per head; here one fp32
     scale per (physical block, KV head), and the value used is code * scale.
+  * [P5] section 7: K is the more sensitive of the two, so K may stay in FP8
+    while V goes to INT8 (symmetric integer codes, value = code * scale);
+    [P1] section 5.2: K has outlier channels, which per-channel scaling
+    absorbs -- here an optional fp32 factor per (KV head, channel) applied on
+    top of the per-(block, head) scale.
   * [P1] section 5.3: with a sliding window of W, a position attends only to
     the most recent W tokens (itself included), optionally together with the
     first few tokens of the sequence (attention sinks), which [P1] 5.3 and
@@ -54,14 +59,20 @@ def attended_positions(length: int, window: int = 0, sinks: int = 0) -> np.ndarr
     return np.union1d(first, recent)
 
 
+QUANTISED = ("fp8_e4m3", "int8")
+
+
 def gather_sequence(cache, table_row, length: int, kv_tag: str, kv_heads=None,
-                    scales=None, block_size: int = 16, positions=None) -> np.ndarray:
+                    scales=None, block_size: int = 16, positions=None,
+                    channel_scales=None) -> np.ndarray:
     """Contiguous float64 [n, len(kv_heads), D] copy of one sequence's tokens.
 
     `cache` is the raw storage array [num_blocks, Hkv, block_size, D] (uint16
-    bits for bf16, uint8 codes for fp8); `scales` ([num_blocks, Hkv] fp32) is
-    required for fp8 and multiplies every element of its (block, head) tile.
-    The tokens are `positions` (default: 0 .. length-1), all < length.
+    bits for bf16, uint8 codes for fp8, int8 codes for int8); `scales`
+    ([num_blocks, Hkv] fp32) is required for the quantised tags and multiplies
+    every element of its (block, head) tile; `channel_scales` ([Hkv, D] fp32,
+    optional) multiplies channel d of head h.  The tokens are `positions`
+    (default: 0 .. length-1), all < length.
     """
     nb = cache.shape[0]
     if kv_heads is None:
@@ -75,13 +86,16 @@ def gather_sequence(cache, table_row, length: int, kv_tag: str, kv_heads=None,
         raise IndexError("block table entry outside the pool for a position < length")
     raw = cache[blk[:, None], kv_heads[None, :], off[:, None], :]      # [L, h, D]
     vals = stored_to_f64(raw, kv_tag)
-    if kv_tag == "fp8_e4m3":
+    if kv_tag in QUANTISED:
         if scales is None:
-            raise ValueError("fp8 caches need their per-(block, head) scales")
+            raise ValueError("quantised caches need their per-(block, head) scales")
         s = np.asarray(scales, dtype=np.float32).astype(np.float64)
         vals = vals * s[blk[:, None], kv_heads[None, :]][:, :, None]
     elif scales is not None:
-        raise ValueError("scales apply to fp8 caches only")
+        raise ValueError("scales apply to quantised caches only")
+    if channel_scales is not None:
+        c = np.asarray(channel_scales, dtype=np.float32).astype(np.float64)
+        vals = vals * c[kv_heads][None, :, :]
     return vals
 
 
@@ -89,13 +103,17 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
                            *, q_tag: str, kv_tag: str, k_scales=None, v_scales=None,
                            seqs: Optional[Sequence[int]] = None,
                            q_heads: Optional[Sequence[int]] = None,
-                           block_size: int = 16, window: int = 0, sinks: int = 0) -> np.ndarray:
+                           block_size: int = 16, window: int = 0, sinks: int = 0,
+                           v_tag: Optional[str] = None, k_channel_scales=None) -> np.ndarray:
     """out[b, i, :] for b in `seqs`, i in `q_heads` (all by default), float64.
 
     q: [B, Hq, D] storage array; caches: [num_blocks, Hkv, block_size, D];
     block_tables: int [B, max_blocks]; context_lens: int [B].  window/sinks
-    restrict the attended positions (see attended_positions).
+    restrict the attended positions (see attended_positions).  v_tag (default
+    kv_tag) is the V cache's format when it differs from K's;
+    k_channel_scales ([Hkv, D]) multiplies K's channels.
     """
+    v_tag = kv_tag if v_tag is None else v_tag
     B, Hq, D = q.shape
     Hkv = k_cache.shape[1]
     if Hq % Hkv:
@@ -113,8 +131,9 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
         pos = attended_positions(L, window, sinks)
         if len(pos) == 0:
             continue
-        K = gather_sequence(k_cache, block_tables[b], L, kv_tag, kv_needed, k_scales, block_size, pos)
-        V = gather_sequence(v_cache, block_tables[b], L, kv_tag, kv_needed, v_scales, block_size, pos)
+        K = gather_sequence(k_cache, block_tables[b], L, kv_tag, kv_needed, k_scales, block_size, pos,
+                            k_channel_scales)
+        V = gather_sequence(v_cache, block_tables[b], L, v_tag, kv_needed, v_scales, block_size, pos)
         for c, i in enumerate(q_heads):
             h = col[kv_for[c]]
             s = scale * (K[:, h, :] @ qv[r, c])          # [L] scores

@@ -150,3 +150,119 @@ def test_fp8_append_zero_token_first_write_scale_is_one():
     x[:] = 0
     out, sc = kv_append_fp8(codes, scales, x, np.array([16]), first_write=True)
     assert np.all(sc[1] == 1.0) and np.all(out[1, :, 0, :] == 0)
+
+
+# --------------------------------------------------------------------------
+# INT8 quantise-on-write, per-channel factors
+# --------------------------------------------------------------------------
+
+from oracle import kv_append_int8, kv_append_quant
+
+
+def _nearest_int8_brute(q):
+    """Nearest of -127..127 to each fp32 value, ties to the even code, by
+    scanning every candidate (NaN -> 0)."""
+    cand = np.arange(-127, 128, dtype=np.float64)
+    out = np.zeros(q.shape, np.int8)
+    for idx, v in np.ndenumerate(q.astype(np.float64)):
+        if np.isnan(v):
+            continue
+        dist = np.abs(cand - v)
+        best = np.flatnonzero(dist == dist.min())
+        if len(best) == 2:                       # a tie: the even code wins
+            best = best[(cand[best] % 2) == 0]
+        out[idx] = int(cand[best[0]])
+    return out
+
+
+def _int8_case(seed=5, T=6, H=2, D=8, NB=5):
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(-127, 128, size=(NB, H, BS, D)).astype(np.int8)
+    scales = rng.uniform(0.01, 0.1, size=(NB, H)).astype(np.float32)
+    x = (rng.standard_normal((T, H, D)) * 3).astype(np.float32)
+    return codes, scales, x
+
+
+def test_int8_append_given_scales_is_nearest_code():
+    codes, scales, x = _int8_case()
+    x[0, 0, :4] = np.array([0.5, 1.5, -2.5, 126.5], np.float32) * scales[0, 0]   # halves
+    x[1, 1, :3] = np.array([1000.0, -1000.0, np.nan], np.float32)               # saturate, NaN
+    slots = np.array([0, 17, 33, -1, 50, 79])
+    out, sc = kv_append_int8(codes, scales, x, slots, first_write=False)
+    assert np.array_equal(sc, scales)
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        q = np.clip(x[t] / scales[s // BS][:, None], -127, 127).astype(np.float32)
+        assert np.array_equal(out[s // BS, :, s % BS, :], _nearest_int8_brute(q))
+    assert list(out[0, 0, 0, :4]) == [0, 2, -2, 126]
+    assert list(out[1, 1, 1, :3]) == [127, -127, 0]
+    mask = np.ones(codes.shape, bool)
+    for s in slots[slots >= 0]:
+        mask[s // BS, :, s % BS, :] = False
+    assert np.array_equal(out[mask], codes[mask])
+
+
+def test_int8_append_first_write_sets_scale_then_saturates():
+    codes, scales, x = _int8_case(T=3)
+    x[1] = x[0] * 4
+    slots = np.array([32, 33, 48])
+    out, sc = kv_append_int8(codes, scales, x, slots, first_write=True)
+    for t, blk in ((0, 2), (2, 3)):
+        amax = np.abs(x[t]).max(axis=1)
+        assert np.array_equal(sc[blk], (amax / np.float32(127)).astype(np.float32))
+        assert np.array_equal(np.abs(out[blk, :, 0, :].astype(int)).max(axis=1), [127, 127])
+    big = np.abs(x[1]) / sc[2][:, None] > 127.5
+    assert big.any() and np.all(np.abs(out[2, :, 1, :][big].astype(int)) == 127)
+    # dequantisation error of the unsaturated elements is at most half a step
+    ok = ~big
+    err = np.abs(out[2, :, 1, :].astype(np.float64) * sc[2][:, None] - x[1])
+    assert np.all(err[ok] <= 0.5 * np.broadcast_to(sc[2][:, None], err.shape)[ok] * (1 + 1e-6))
+    assert np.array_equal(sc[[0, 1, 4]], scales[[0, 1, 4]])
+
+
+def test_int8_append_exact_values_round_trip_and_zero_row():
+    rng = np.random.default_rng(6)
+    c = rng.integers(-127, 128, size=(2, 1, 8)).astype(np.int8)
+    scales = np.array([[0.25], [8.0]], np.float32)
+    x = (c.astype(np.float32) * scales[:, :, None]).astype(np.float32)
+    out, _ = kv_append_int8(np.zeros((2, 1, BS, 8), np.int8), scales, x, np.array([3, 21]),
+                            first_write=False)
+    assert np.array_equal(out[0, :, 3, :], c[0]) and np.array_equal(out[1, :, 5, :], c[1])
+    z = np.zeros((1, 1, 8), np.float32)
+    out, sc = kv_append_int8(np.ones((2, 1, BS, 8), np.int8), scales, z, np.array([16]), first_write=True)
+    assert sc[1, 0] == 1.0 and np.all(out[1, :, 0, :] == 0)
+
+
+@pytest.mark.parametrize("code", ["fp8_e4m3", "int8"])
+def test_channel_scales_divide_before_quantising(code):
+    """Power-of-two channel factors divide exactly, so appending x with factors
+    c equals appending x / c without them; unit factors change nothing."""
+    rng = np.random.default_rng(7)
+    H, D, NB = 2, 8, 3
+    dt = np.uint8 if code == "fp8_e4m3" else np.int8
+    codes = np.zeros((NB, H, BS, D), dt)
+    scales = np.ones((NB, H), np.float32)
+    c = (2.0 ** rng.integers(-3, 5, size=(H, D))).astype(np.float32)
+    x = (rng.standard_normal((4, H, D)) * 5 * c).astype(np.float32)
+    slots = np.array([16, 17, 32, 2])
+    for fw in (False, True):
+        got = kv_append_quant(codes, scales, x, slots, code=code, first_write=fw, channel_scales=c)
+        ref = kv_append_quant(codes, scales, x / c, slots, code=code, first_write=fw)
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+        one = kv_append_quant(codes, scales, x, slots, code=code, first_write=fw,
+                              channel_scales=np.ones((H, D), np.float32))
+        plain = kv_append_quant(codes, scales, x, slots, code=code, first_write=fw)
+        assert np.array_equal(one[0], plain[0]) and np.array_equal(one[1], plain[1])
+    # an outlier channel no longer flattens the others: every channel of a
+    # first-written int8 row spans the code range it has
+    x2 = rng.standard_normal((1, H, D)).astype(np.float32)
+    x2[0, :, 3] *= 64
+    cs = np.ones((H, D), np.float32); cs[:, 3] = 64
+    out_c, _ = kv_append_int8(np.zeros((NB, H, BS, D), np.int8), scales, x2, np.array([0]),
+                              first_write=True, channel_scales=cs)
+    out_n, _ = kv_append_int8(np.zeros((NB, H, BS, D), np.int8), scales, x2, np.array([0]),
+                              first_write=True)
+    others = [d for d in range(D) if d != 3]
+    assert (np.abs(out_c[0, :, 0, others].astype(int)).max() >
+            4 * np.abs(out_n[0, :, 0, others].astype(int)).max())

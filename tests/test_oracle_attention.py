@@ -353,6 +353,11 @@ MUTANTS = {
     "window_off_by_one": ("recent = np.arange(max(0, L - int(window)), L)",
                           "recent = np.arange(max(0, L - int(window) + 1), L)"),
     "sinks_ignored": ("first = np.arange(min(int(sinks), L))", "first = np.arange(0)"),
+    "channel_factors_dropped": ("vals = vals * c[kv_heads][None, :, :]", "vals = vals"),
+    "channel_factors_transposed": ("vals = vals * c[kv_heads][None, :, :]",
+                                   "vals = vals * c[kv_heads][None, :, ::-1]"),
+    "v_read_in_k_format": ("V = gather_sequence(v_cache, block_tables[b], L, v_tag,",
+                           "V = gather_sequence(v_cache, block_tables[b], L, kv_tag,"),
     "query_head_index": ("qv = stored_to_f64(np.asarray(q)[seqs][:, q_heads], q_tag)",
                          "qv = stored_to_f64(np.asarray(q)[seqs][:, q_heads][:, ::-1], q_tag)"),
 }
@@ -387,13 +392,48 @@ def _fp8_pin(mod):
     np.testing.assert_allclose(got, ref, atol=1e-12)
 
 
+def _mixed_pin(mod):
+    """fp8 K with per-channel factors and int8 V: the dense reference uses
+    K = decode(code) * block scale * channel factor and V = code * block
+    scale, built position by position (torch's fp8 decode, numpy's int8)."""
+    rng = np.random.default_rng(9)
+    lens = [19, 35]
+    Hkv, D = 2, 8
+    codes_k = [rng.integers(0, 0x70, size=(L, Hkv, D)).astype(np.uint8) for L in lens]
+    codes_v = [rng.integers(-127, 128, size=(L, Hkv, D)).astype(np.int8) for L in lens]
+    kc, _, t, Ls = paged_from_contiguous(codes_k, codes_k, 6, seed=18, storage=np.uint8, fill=0x7F)
+    vc, _, t2, _ = paged_from_contiguous(codes_v, codes_v, 6, seed=18, storage=np.int8, fill=0)
+    assert np.array_equal(t, t2)
+    ks = rng.uniform(0.01, 0.1, size=(6, Hkv)).astype(np.float32)
+    vs = rng.uniform(0.01, 0.1, size=(6, Hkv)).astype(np.float32)
+    cs = rng.uniform(0.5, 4.0, size=(Hkv, D)).astype(np.float32)
+    q = rng.standard_normal((2, 4, D)).astype(np.float32)
+    got = mod.paged_decode_attention(q, kc, vc, t, Ls, 0.4, q_tag="f32", kv_tag="fp8_e4m3",
+                                     v_tag="int8", k_scales=ks, v_scales=vs, k_channel_scales=cs)
+    dec = lambda a: torch.from_numpy(a).view(torch.float8_e4m3fn).double().numpy()
+    sk_d, sv_d = [], []
+    for b, L in enumerate(lens):
+        kd = np.zeros((L, Hkv, D)); vd = np.zeros_like(kd)
+        for pos in range(L):
+            blk = t[b][pos // BS]
+            kd[pos] = dec(codes_k[b][pos]) * ks[blk][:, None] * cs
+            vd[pos] = codes_v[b][pos].astype(np.float64) * vs[blk][:, None]
+        sk_d.append(kd); sv_d.append(vd)
+    ref = sdpa_reference(q.astype(np.float64), sk_d, sv_d, 0.4)
+    np.testing.assert_allclose(got, ref, atol=1e-12)
+
+
+def test_mixed_precision_pin():
+    _mixed_pin(oracle)
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(name):
     mod = _mutant_module(name)
     caught = []
-    for pin in PINS + [_fp8_pin]:
+    for pin in PINS + [_fp8_pin, _mixed_pin]:
         try:
             pin(mod)
-        except (AssertionError, IndexError, ValueError):
+        except (AssertionError, IndexError, ValueError, TypeError):
             caught.append(pin.__name__)
     assert caught, f"no pin catches the planted mistake {name}"
