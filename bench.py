@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Decode-step benchmark: paged decode attention KV GB/s on one MI355X.
 
-One step = for every layer: kv_append of each sequence's new token (fp8
+One step = for every layer: kv_append of each sequence's new token (8-bit
 caches quantise it on write), then paged_decode_attn over all cached tokens
 (the whole hot path), on synthetic
 seeded inputs already resident in HBM.  Default workload: the 70B-shaped
@@ -40,7 +40,7 @@ ATTN_KERNEL = "pkv::decode_partition_kernel"
 CSRC = os.path.join(ROOT, "paged_kv_cache_56_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 METRIC = "paged decode attention KV GB/s and % of MI355X HBM peak (1 GPU)"
-ELT = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
+ELT = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1, "int8": 1}
 
 
 def log(*a):
@@ -61,11 +61,11 @@ def attention_bytes(spec, lay, window: int = 0, sinks: int = 0):
     K and V of every attended (token, KV head) once -- a physical block that
     several sequences share (a common prefix) is counted once, since the
     method needs to stream it only once -- plus q, out, the block table
-    entries and lengths read, and the fp8 scales of every attended (block,
-    KV head).  Returns (K/V bytes, all algorithmic bytes, logical K/V bytes
+    entries and lengths read, the 8-bit scales of every attended (block, KV
+    head) and K's channel factors.  Returns (K/V bytes, all algorithmic bytes, logical K/V bytes
     counting shared blocks once per sequence)."""
     L = lay.context_lens.astype(int)
-    per_token = spec.num_kv_heads * spec.head_dim * ELT[spec.kv_dtype] * 2
+    per_token = spec.num_kv_heads * spec.head_dim * (ELT[spec.kv_dtype] + ELT[spec.v_tag])
     logical = 0
     used = {}                        # physical block -> attended token offsets
     for b in range(spec.num_seqs):
@@ -78,8 +78,9 @@ def attention_bytes(spec, lay, window: int = 0, sinks: int = 0):
     q = spec.num_seqs * spec.num_q_heads * spec.head_dim * ELT[spec.q_dtype]
     out = spec.num_seqs * spec.num_q_heads * spec.head_dim * ELT[spec.out_dtype]
     meta = int(nblk.sum()) * 4 + spec.num_seqs * 4
-    scales = int(nblk.sum()) * spec.num_kv_heads * 4 * 2 if spec.kv_dtype == "fp8_e4m3" else 0
-    return kv, kv + q + out + meta + scales, logical
+    scales = int(nblk.sum()) * spec.num_kv_heads * 4 * 2 if spec.quantised else 0
+    chan = spec.num_kv_heads * spec.head_dim * 4 if spec.k_outliers else 0
+    return kv, kv + q + out + meta + scales + chan, logical
 
 
 def cpu_baseline(spec, lay, x, budget_s: float):
@@ -98,6 +99,7 @@ def cpu_baseline(spec, lay, x, budget_s: float):
         t = t.detach().cpu()
         return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
 
+
     nblk = -(-lay.context_lens.astype(int) // 16)
     done_bytes, elapsed, seqs = 0, 0.0, 0
     order = [(layer, b) for layer in range(spec.num_layers) for b in range(spec.num_seqs)]
@@ -114,6 +116,7 @@ def cpu_baseline(spec, lay, x, budget_s: float):
             if "k_scales" in x:
                 kw = dict(k_scales=host(x["k_scales"][layer].index_select(0, idx)),
                           v_scales=host(x["v_scales"][layer].index_select(0, idx)))
+            chan = host(x["k_channel_scales"]) if "k_channel_scales" in x else None
             t0 = time.perf_counter()
             if spec.append:
                 s = int(lay.slot_mapping[b])
@@ -123,15 +126,20 @@ def cpu_baseline(spec, lay, x, budget_s: float):
                 if "k_scales" in x:
                     kn = oracle.stored_to_f64(kn, spec.q_dtype).astype(np.float32)
                     vn = oracle.stored_to_f64(vn, spec.q_dtype).astype(np.float32)
-                    kc, kw["k_scales"] = oracle.kv_append_fp8(kc, kw["k_scales"], kn, slot, first_write=False)
-                    vc, kw["v_scales"] = oracle.kv_append_fp8(vc, kw["v_scales"], vn, slot, first_write=False)
+                    kc, kw["k_scales"] = oracle.kv_append_quant(kc, kw["k_scales"], kn, slot,
+                                                                code=spec.kv_dtype, first_write=False,
+                                                                channel_scales=chan)
+                    vc, kw["v_scales"] = oracle.kv_append_quant(vc, kw["v_scales"], vn, slot,
+                                                                code=spec.v_tag, first_write=False)
                 else:
                     kc = oracle.kv_append_bits(kc, kn, slot)
                     vc = oracle.kv_append_bits(vc, vn, slot)
             oracle.paged_decode_attention(q, kc, vc, table, lens, spec.scale, q_tag=spec.q_dtype,
-                                          kv_tag=spec.kv_dtype, **kw)
+                                          kv_tag=spec.kv_dtype, v_tag=spec.v_tag,
+                                          k_channel_scales=chan, **kw)
             elapsed += time.perf_counter() - t0
-            done_bytes += int(lens[0]) * spec.num_kv_heads * spec.head_dim * ELT[spec.kv_dtype] * 2
+            done_bytes += int(lens[0]) * spec.num_kv_heads * spec.head_dim * (ELT[spec.kv_dtype] +
+                                                                              ELT[spec.v_tag])
             seqs += 1
             if elapsed >= budget_s:
                 break
@@ -376,15 +384,24 @@ def main():
     nparts = pkv.decode_num_partitions(dims)
     ws_bytes = pkv.decode_workspace_bytes(dims)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    fp8 = spec.kv_dtype == "fp8_e4m3"
+    chan = x.get("k_channel_scales")
+    both_fp8 = spec.kv_dtype == spec.v_tag == "fp8_e4m3" and chan is None
 
     def step(ev=None):
         for layer in range(nl):
             kc, vc = x["k_cache"][layer], x["v_cache"][layer]
-            kw = dict(k_scales=x["k_scales"][layer], v_scales=x["v_scales"][layer]) if fp8 else {}
-            if spec.append and fp8:
+            kw = {}
+            if spec.quantised:
+                kw = dict(k_scales=x["k_scales"][layer], v_scales=x["v_scales"][layer])
+                if chan is not None:
+                    kw["k_channel_scales"] = chan
+            if spec.append and both_fp8:
                 pkv.kv_append_fp8(x["k_new"][layer], x["v_new"][layer], x["slot_mapping"], kc, vc,
                                   kw["k_scales"], kw["v_scales"])
+            elif spec.append and spec.quantised:
+                pkv.kv_append_quant(x["k_new"][layer], x["slot_mapping"], kc, kw["k_scales"],
+                                    channel_scales=chan)
+                pkv.kv_append_quant(x["v_new"][layer], x["slot_mapping"], vc, kw["v_scales"])
             elif spec.append:
                 pkv.kv_append(x["k_new"][layer], x["v_new"][layer], x["slot_mapping"], kc, vc)
             if ev is not None:
@@ -448,7 +465,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f32": "f32", "f16": "f16", "bf16": "bf16", "fp8_e4m3": "fp8_e4m3"}[spec.kv_dtype],
+        "dtype": spec.kv_dtype if spec.v_tag == spec.kv_dtype else f"{spec.kv_dtype}+{spec.v_tag}",
         "data": "synthetic",
         "config": {
             "workload": spec.name,

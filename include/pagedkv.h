@@ -12,7 +12,10 @@
  *     a per-sequence block table, locate(seq, pos) = table[pos / 16] * 16 +
  *     pos % 16; prefix sharing points several tables at the same blocks;
  *     2: grouped-query attention (g query heads share one K/V head);
- *     7: 8-bit K/V with one scale per head.
+ *     7: 8-bit K/V with one scale per head, K (the more sensitive) in FP8
+ *     with V in INT8 as a mixed form.
+ *   - "KV Cache from first principles" 5.2: K has outlier channels, which
+ *     per-channel factors absorb.
  *
  * Memory layout (all row-major, contiguous, device memory):
  *   k_cache, v_cache  [num_blocks][num_kv_heads][block_size=16][head_dim]
@@ -21,7 +24,8 @@
  *                     ceil(context_len / 16) are never read
  *   context_lens      int32 [num_seqs]: tokens to attend, the new one included
  *   q, out            [num_seqs][num_q_heads][head_dim]
- *   k_scales,v_scales fp32 [num_blocks][num_kv_heads] (fp8 caches only)
+ *   k_scales,v_scales fp32 [num_blocks][num_kv_heads] (8-bit caches only)
+ *   k_channel_scales  fp32 [num_kv_heads][head_dim] (8-bit K, optional)
  *   slot_mapping      int64 [num_tokens]: flat slot = block * 16 + offset,
  *                     -1 = skip this token
  *   query head i reads KV head i / (num_q_heads / num_kv_heads).
@@ -51,14 +55,15 @@ extern "C" {
 #define PKV_API
 #endif
 
-#define PKV_VERSION 100  /* 1.0.0 */
+#define PKV_VERSION 110  /* 1.1.0 */
 #define PKV_BLOCK_SIZE 16
 
 typedef enum {
   PKV_F32 = 0,
   PKV_F16 = 1,
   PKV_BF16 = 2,
-  PKV_FP8_E4M3 = 3 /* OCP e4m3fn: bias 7, max 448, no inf, NaN = S.1111.111 */
+  PKV_FP8_E4M3 = 3, /* OCP e4m3fn: bias 7, max 448, no inf, NaN = S.1111.111 */
+  PKV_INT8 = 4      /* symmetric two's-complement codes -127..127 (-128 unused) */
 } pkv_dtype;
 
 typedef enum {
@@ -83,7 +88,7 @@ typedef struct {
   int32_t num_blocks;          /* physical blocks in the pool (per cache) */
   int32_t max_blocks_per_seq;  /* row length of block_tables */
   int32_t q_dtype;             /* pkv_dtype */
-  int32_t kv_dtype;            /* pkv_dtype */
+  int32_t kv_dtype;            /* pkv_dtype (of K, where V may differ) */
   int32_t out_dtype;           /* pkv_dtype */
   int32_t partition_blocks;    /* blocks per context partition; 0 = automatic */
   int32_t window;              /* sliding window W: attend only the last W positions
@@ -134,7 +139,29 @@ PKV_API int pkv_kv_append_fp8(const void* k_new, const void* v_new, const int64_
                               int32_t scale_mode, hipStream_t stream);
 
 /*
- * Bytes of workspace pkv_paged_decode_attn(_fp8) needs for `dims`; 0 when the
+ * 8-bit append into ONE cache (K or V), quantising on write, for the fp8,
+ * int8 and mixed (K fp8, V int8) layouts ("The KV Cache memory ledger" 7;
+ * "KV Cache from first principles" 5.2: per-channel factors for K).
+ * cache: codes of cache_dtype (FP8_E4M3 or INT8) [NB][Hkv][16][D]; scales:
+ * fp32 [NB][Hkv] (read and, in first-write mode, written); channel_scales:
+ * NULL or fp32 [Hkv][D] (device).  x_new: [T][Hkv][D] of src_dtype.  With
+ * QMAX = 448 (fp8) or 127 (int8), for every t with 0 <= slot < NB*16:
+ *   - y = x / channel_scales[h][d] (correctly rounded fp32), or y = x;
+ *   - PKV_SCALE_FIRST_WRITE and off == 0: scale[blk][h] = max_d |y| / QMAX
+ *     (1.0 if that max is 0), set for all such tokens before any is quantised;
+ *   - code = nearest code, ties to even, of clamp(y / scale, -QMAX, QMAX)
+ *     (correctly rounded fp32 quotient); NaN stays NaN (fp8) or becomes 0
+ *     (int8).
+ * head_dim must be a multiple of 16 (<= 1024).  Slots must be distinct.
+ */
+PKV_API int pkv_kv_append_quant(const void* x_new, const int64_t* slot_mapping, void* cache,
+                                float* scales, const float* channel_scales, int32_t num_tokens,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                int32_t block_size, int32_t src_dtype, int32_t cache_dtype,
+                                int32_t scale_mode, hipStream_t stream);
+
+/*
+ * Bytes of workspace pkv_paged_decode_attn(_fp8, _quant) needs for `dims`; 0 when the
  * context is not split.  Depends only on `dims` (never on the device or on
  * context_lens), so a caller can size it once.  Returns 0 for invalid dims.
  */
@@ -177,6 +204,25 @@ PKV_API int pkv_paged_decode_attn_fp8(const void* q, const void* k_cache, const 
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * 8-bit variant with mixed formats and per-channel K factors ("The KV Cache
+ * memory ledger" 7: K in FP8 with V in INT8; "KV Cache from first
+ * principles" 5.2: per-channel factors for K's outlier channels).
+ * dims->kv_dtype is K's format and v_dtype V's: (FP8_E4M3, FP8_E4M3) with
+ * the q/out pairs of pkv_paged_decode_attn_fp8, or (FP8_E4M3, INT8) and
+ * (INT8, INT8) with q and out both F16 or both BF16.  A cached K element is
+ * decode(code) * k_scales[block][h] * k_channel_scales[h][d] (the last factor
+ * 1 when k_channel_scales is NULL), a V element decode(code) *
+ * v_scales[block][h]; int8 codes decode to their integer value.
+ */
+PKV_API int pkv_paged_decode_attn_quant(const void* q, const void* k_cache, const void* v_cache,
+                                        const float* k_scales, const float* v_scales,
+                                        const float* k_channel_scales, int32_t v_dtype,
+                                        const int32_t* block_tables, const int32_t* context_lens,
+                                        float scale, void* out, const pkv_decode_dims* dims,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+
+/*
  * Bandwidth reference ("KV Cache from first principles" 4.1: decode time is
  * set by the bytes moved).  Reads the first `bytes` (rounded down to a
  * multiple of 16) of device buffer `buf` once with 16-byte loads, using
@@ -192,9 +238,9 @@ PKV_API int pkv_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, in
  * Copy-on-write block copies ("Large-model inference KV Cache memory
  * optimisation" 3.2: copy a shared block before writing into it).  For every
  * i < num_pairs, block dst_blocks[i] of both caches receives a bit copy of
- * block src_blocks[i] (every KV head, all 16 slots), and for fp8 caches the
- * scales k_scales/v_scales[dst][h] receive those of src (pass NULL scales for
- * other dtypes).  src_blocks, dst_blocks: int32 device arrays.  Destinations
+ * block src_blocks[i] (every KV head, all 16 slots), and for 8-bit caches
+ * the scales k_scales/v_scales[dst][h] receive those of src (pass NULL scales
+ * for other dtypes; a mixed fp8 K / int8 V pair passes either 8-bit dtype).  src_blocks, dst_blocks: int32 device arrays.  Destinations
  * must be distinct and not also sources in the same call; ids outside
  * [0, num_blocks) are skipped.  num_pairs <= 65535.
  */

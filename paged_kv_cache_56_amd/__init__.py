@@ -7,9 +7,11 @@ the library's HIP kernels; there is no fallback path.  torch tensors only
 carry device memory and streams.
 
     kv_append(k_new, v_new, slot_mapping, k_cache, v_cache)
+    kv_append_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scales, v_scales)
+    kv_append_quant(x_new, slot_mapping, cache, scales, channel_scales=None)
     paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, scale, out,
-                      k_scales=None, v_scales=None, workspace=None, partition_blocks=0,
-                      window=0, sinks=0)
+                      k_scales=None, v_scales=None, k_channel_scales=None,
+                      workspace=None, partition_blocks=0, window=0, sinks=0)
 """
 
 from __future__ import annotations
@@ -26,6 +28,7 @@ __all__ = [
     "load_library",
     "kv_append",
     "kv_append_fp8",
+    "kv_append_quant",
     "copy_blocks",
     "BlockManager",
     "paged_decode_attn",
@@ -47,7 +50,9 @@ DTYPE_CODES = {
     torch.bfloat16: 2,
     torch.uint8: 3,               # fp8 e4m3fn codes, stored as raw bytes
     torch.float8_e4m3fn: 3,
+    torch.int8: 4,                # symmetric int8 codes
 }
+_Q8 = (3, 4)
 
 
 class PagedKVError(RuntimeError):
@@ -97,6 +102,8 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_kv_append.restype = ctypes.c_int
     lib.pkv_kv_append_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.pkv_kv_append_fp8.restype = ctypes.c_int
+    lib.pkv_kv_append_quant.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.pkv_kv_append_quant.restype = ctypes.c_int
     lib.pkv_decode_workspace_bytes.argtypes = [dims_p]
     lib.pkv_decode_workspace_bytes.restype = sz
     lib.pkv_decode_num_partitions.argtypes = [dims_p]
@@ -106,6 +113,9 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_paged_decode_attn_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
                                               dims_p, vp, sz, vp]
     lib.pkv_paged_decode_attn_fp8.restype = ctypes.c_int
+    lib.pkv_paged_decode_attn_quant.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, ctypes.c_float, vp,
+                                                dims_p, vp, sz, vp]
+    lib.pkv_paged_decode_attn_quant.restype = ctypes.c_int
     lib.pkv_hbm_read_probe.argtypes = [vp, sz, vp, i32, vp]
     lib.pkv_hbm_read_probe.restype = ctypes.c_int
     i64, i32p, i64p = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
@@ -218,13 +228,41 @@ def kv_append_fp8(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.
                                  SCALE_FIRST_WRITE if first_write else SCALE_GIVEN, _stream(k_cache)))
 
 
+def kv_append_quant(x_new: torch.Tensor, slot_mapping: torch.Tensor, cache: torch.Tensor,
+                    scales: torch.Tensor, *, channel_scales: Optional[torch.Tensor] = None,
+                    first_write: bool = False) -> None:
+    """Quantise token t's rows (f32/f16/bf16) into ONE 8-bit cache at its slot.
+
+    x_new: [T, Hkv, D]; cache: fp8 (uint8 / float8_e4m3fn) or int8 [NB, Hkv, 16, D];
+    scales: fp32 [NB, Hkv]; channel_scales: optional fp32 [Hkv, D] that each
+    element is divided by first.  first_write as in kv_append_fp8 (QMAX 448 for
+    fp8, 127 for int8).
+    """
+    lib = load_library()
+    _dev(x_new, slot_mapping, cache, scales, channel_scales)
+    _need(x_new.dim() == 3 and cache.dim() == 4 and _code(cache) in _Q8,
+          "x_new must be [T, Hkv, D] and the cache 8-bit [NB, Hkv, 16, D]")
+    T, H, D = x_new.shape
+    _need(cache.shape[1] == H and cache.shape[3] == D, "cache and new-token shapes differ")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (T,), "slot_mapping must be int64 [T]")
+    _need(scales.dtype == torch.float32 and scales.shape == cache.shape[:2], "scales must be fp32 [NB, Hkv]")
+    _need(channel_scales is None or (channel_scales.dtype == torch.float32 and
+                                     channel_scales.shape == (H, D)), "channel_scales must be fp32 [Hkv, D]")
+    _need(_code(x_new) in (0, 1, 2), "x_new must be f32/f16/bf16")
+    _check(lib.pkv_kv_append_quant(_ptr(x_new), _ptr(slot_mapping), _ptr(cache), _ptr(scales),
+                                   _ptr(channel_scales), T, H, D, cache.shape[0], cache.shape[2],
+                                   _code(x_new), _code(cache),
+                                   SCALE_FIRST_WRITE if first_write else SCALE_GIVEN, _stream(cache)))
+
+
 def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src: torch.Tensor, dst: torch.Tensor,
                 k_scales: Optional[torch.Tensor] = None, v_scales: Optional[torch.Tensor] = None) -> None:
-    """Copy-on-write: blocks dst[i] of both caches (and fp8 scales) become bit
+    """Copy-on-write: blocks dst[i] of both caches (and 8-bit scales) become bit
     copies of blocks src[i].  src, dst: int32 [n] on the device."""
     lib = load_library()
     _dev(k_cache, v_cache, src, dst, k_scales, v_scales)
     _need(k_cache.shape == v_cache.shape and k_cache.dim() == 4, "caches must be [NB, Hkv, 16, D]")
+    _need(k_cache.element_size() == v_cache.element_size(), "K and V elements differ in width")
     _need(src.dtype == dst.dtype == torch.int32 and src.shape == dst.shape and src.dim() == 1,
           "src/dst must be int32 [n]")
     NB, H, _, D = k_cache.shape
@@ -332,22 +370,26 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
                       out: torch.Tensor, *, k_scales: Optional[torch.Tensor] = None,
                       v_scales: Optional[torch.Tensor] = None,
+                      k_channel_scales: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None,
                       partition_blocks: int = 0, window: int = 0, sinks: int = 0) -> torch.Tensor:
     """out[b, i] = softmax(scale * q[b, i] . K^T) V over the first context_lens[b]
     tokens of sequence b, K/V read through block_tables.  Returns `out`.
 
     q, out: [B, Hq, D]; caches: [NB, Hkv, 16, D]; block_tables: int32 [B, max_blocks];
-    context_lens: int32 [B].  FP8 caches (uint8 or float8_e4m3fn) need k_scales and
-    v_scales: fp32 [NB, Hkv].  `workspace` (uint8, on the device) is allocated here
+    context_lens: int32 [B].  8-bit caches -- fp8 (uint8 or float8_e4m3fn) or
+    int8, K fp8 with V int8 allowed -- need k_scales and v_scales: fp32 [NB, Hkv],
+    and may give k_channel_scales: fp32 [Hkv, D] for K.  `workspace` (uint8, on the device) is allocated here
     when the call splits the context and none is given.  window > 0 limits each
     query to the last `window` positions plus the first `sinks` positions.
     """
     lib = load_library()
-    _dev(q, k_cache, v_cache, block_tables, context_lens, out, k_scales, v_scales, workspace)
+    _dev(q, k_cache, v_cache, block_tables, context_lens, out, k_scales, v_scales, k_channel_scales,
+         workspace)
     _need(q.dim() == 3 and out.shape == q.shape, "q and out must be [B, Hq, D]")
     _need(k_cache.shape == v_cache.shape and k_cache.dim() == 4, "caches must be [NB, Hkv, 16, D]")
-    _need(k_cache.dtype == v_cache.dtype, "K and V caches differ in dtype")
+    kc, vc = _code(k_cache), _code(v_cache)
+    _need(kc == vc or (kc in _Q8 and vc in _Q8), "K and V caches differ in dtype")
     _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
           and block_tables.shape[0] == q.shape[0], "block_tables must be int32 [B, max_blocks]")
     _need(context_lens.dtype == torch.int32 and context_lens.shape == (q.shape[0],),
@@ -358,17 +400,27 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _ptr(workspace) if need else None
     ws_bytes = workspace.numel() * workspace.element_size() if (need and workspace is not None) else 0
-    fp8 = _code(k_cache) == 3
-    if fp8:
-        _need(k_scales is not None and v_scales is not None, "fp8 caches need k_scales and v_scales")
+    if kc in _Q8:
+        _need(k_scales is not None and v_scales is not None, "8-bit caches need k_scales and v_scales")
         _need(k_scales.dtype == v_scales.dtype == torch.float32 and
               k_scales.shape == v_scales.shape == k_cache.shape[:2], "scales must be fp32 [NB, Hkv]")
-        st = lib.pkv_paged_decode_attn_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales),
-                                           _ptr(v_scales), _ptr(block_tables), _ptr(context_lens),
-                                           float(scale), _ptr(out), ctypes.byref(dims), ws_ptr,
-                                           ws_bytes, _stream(q))
+        _need(k_channel_scales is None or (k_channel_scales.dtype == torch.float32 and
+                                           k_channel_scales.shape == (k_cache.shape[1], k_cache.shape[3])),
+              "k_channel_scales must be fp32 [Hkv, D]")
+        if kc == vc == 3 and k_channel_scales is None:
+            st = lib.pkv_paged_decode_attn_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales),
+                                               _ptr(v_scales), _ptr(block_tables), _ptr(context_lens),
+                                               float(scale), _ptr(out), ctypes.byref(dims), ws_ptr,
+                                               ws_bytes, _stream(q))
+        else:
+            st = lib.pkv_paged_decode_attn_quant(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales),
+                                                 _ptr(v_scales), _ptr(k_channel_scales), vc,
+                                                 _ptr(block_tables), _ptr(context_lens), float(scale),
+                                                 _ptr(out), ctypes.byref(dims), ws_ptr, ws_bytes,
+                                                 _stream(q))
     else:
-        _need(k_scales is None and v_scales is None, "scales apply to fp8 caches only")
+        _need(k_scales is None and v_scales is None and k_channel_scales is None,
+              "scales apply to 8-bit caches only")
         st = lib.pkv_paged_decode_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                        _ptr(context_lens), float(scale), _ptr(out),
                                        ctypes.byref(dims), ws_ptr, ws_bytes, _stream(q))

@@ -15,6 +15,7 @@ int elem_bytes(int dt) {
     case PKV_F16: return 2;
     case PKV_BF16: return 2;
     case PKV_FP8_E4M3: return 1;
+    case PKV_INT8: return 1;
     default: return 0;
   }
 }
@@ -37,28 +38,36 @@ int check_dims(const pkv_decode_dims* d) {
   return PKV_OK;
 }
 
-int check_dtypes(const pkv_decode_dims* d, bool fp8) {
-  if (fp8) {
-    if (d->kv_dtype != PKV_FP8_E4M3) return PKV_ERR_DTYPE;
-    if (d->q_dtype == PKV_FP8_E4M3) return PKV_ERR_DTYPE;
-    const bool ok = (d->q_dtype == d->out_dtype) ||
-                    (d->out_dtype == PKV_F32 && (d->q_dtype == PKV_BF16 || d->q_dtype == PKV_F16));
-    return ok ? PKV_OK : PKV_ERR_DTYPE;
+bool is_q8(int dt) { return dt == PKV_FP8_E4M3 || dt == PKV_INT8; }
+
+// v_dtype < 0: the unquantised entry point (q, K, V, out of one float type).
+int check_dtypes(const pkv_decode_dims* d, int v_dtype) {
+  if (v_dtype >= 0) {
+    const int k = d->kv_dtype, q = d->q_dtype, o = d->out_dtype;
+    if (is_q8(q) || is_q8(o)) return PKV_ERR_DTYPE;
+    if (k == PKV_FP8_E4M3 && v_dtype == PKV_FP8_E4M3) {
+      const bool ok = (q == o) || (o == PKV_F32 && (q == PKV_BF16 || q == PKV_F16));
+      return ok ? PKV_OK : PKV_ERR_DTYPE;
+    }
+    const bool pair = (k == PKV_FP8_E4M3 && v_dtype == PKV_INT8) ||
+                      (k == PKV_INT8 && v_dtype == PKV_INT8);
+    const bool qo = (q == PKV_BF16 || q == PKV_F16) && o == q;
+    return pair && qo ? PKV_OK : PKV_ERR_DTYPE;
   }
-  if (d->kv_dtype == PKV_FP8_E4M3) return PKV_ERR_DTYPE;
+  if (is_q8(d->kv_dtype)) return PKV_ERR_DTYPE;
   if (d->q_dtype != d->kv_dtype || d->out_dtype != d->kv_dtype) return PKV_ERR_DTYPE;
   return PKV_OK;
 }
 
 int decode_common(const void* q, const void* k_cache, const void* v_cache, const float* k_scales,
-                  const float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
-                  float scale, void* out, const pkv_decode_dims* dims, void* workspace,
-                  size_t workspace_bytes, hipStream_t stream, bool fp8) {
+                  const float* v_scales, const float* k_chan, const int32_t* block_tables,
+                  const int32_t* context_lens, float scale, void* out, const pkv_decode_dims* dims,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream, int v_dtype) {
   int st = check_dims(dims);
   if (st) return st;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
-  if (fp8 && (!k_scales || !v_scales)) return PKV_ERR_NULL;
-  st = check_dtypes(dims, fp8);
+  if (v_dtype >= 0 && (!k_scales || !v_scales)) return PKV_ERR_NULL;
+  st = check_dtypes(dims, v_dtype);
   if (st) return st;
   if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
   int pb, np;
@@ -72,6 +81,7 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
   a.v_cache = v_cache;
   a.k_scales = k_scales;
   a.v_scales = v_scales;
+  a.k_chan = k_chan;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.scale = scale * 1.4426950408889634f;  // scores are kept in log2 units
@@ -91,8 +101,19 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
   a.sinks = dims->window > 0 ? dims->sinks : 0;
   a.q_dtype = dims->q_dtype;
   a.kv_dtype = dims->kv_dtype;
+  a.v_dtype = v_dtype >= 0 ? v_dtype : dims->kv_dtype;
   a.out_dtype = dims->out_dtype;
   return launch_decode(a, stream);
+}
+
+int check_q8_append(int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                    int32_t block_size, int32_t src_dtype, int32_t scale_mode) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0)
+    return PKV_ERR_SHAPE;
+  if (block_size != PKV_BLOCK_SIZE || head_dim % 16 || head_dim > 1024) return PKV_ERR_SHAPE;
+  if (src_dtype != PKV_F32 && src_dtype != PKV_F16 && src_dtype != PKV_BF16) return PKV_ERR_DTYPE;
+  if (scale_mode != PKV_SCALE_GIVEN && scale_mode != PKV_SCALE_FIRST_WRITE) return PKV_ERR_SHAPE;
+  return PKV_OK;
 }
 
 }  // namespace
@@ -120,17 +141,31 @@ int pkv_kv_append_fp8(const void* k_new, const void* v_new, const int64_t* slot_
                       int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
                       int32_t num_blocks, int32_t block_size, int32_t src_dtype,
                       int32_t scale_mode, hipStream_t stream) {
-  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0)
-    return PKV_ERR_SHAPE;
-  if (block_size != PKV_BLOCK_SIZE || head_dim % 16 || head_dim > 1024) return PKV_ERR_SHAPE;
-  if (src_dtype != PKV_F32 && src_dtype != PKV_F16 && src_dtype != PKV_BF16) return PKV_ERR_DTYPE;
-  if (scale_mode != PKV_SCALE_GIVEN && scale_mode != PKV_SCALE_FIRST_WRITE) return PKV_ERR_SHAPE;
+  const int st = check_q8_append(num_tokens, num_kv_heads, head_dim, num_blocks, block_size,
+                                 src_dtype, scale_mode);
+  if (st) return st;
   if (num_tokens == 0) return PKV_OK;
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache || !k_scales || !v_scales)
     return PKV_ERR_NULL;
-  return launch_kv_append_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scales, v_scales,
-                              num_tokens, num_kv_heads, head_dim, num_blocks, src_dtype,
-                              scale_mode == PKV_SCALE_FIRST_WRITE, stream);
+  const QTargetArgs tg[2] = {{k_new, k_cache, k_scales, nullptr}, {v_new, v_cache, v_scales, nullptr}};
+  return launch_kv_append_q8(tg, 2, slot_mapping, num_tokens, num_kv_heads, head_dim, num_blocks,
+                             src_dtype, PKV_FP8_E4M3, scale_mode == PKV_SCALE_FIRST_WRITE, stream);
+}
+
+int pkv_kv_append_quant(const void* x_new, const int64_t* slot_mapping, void* cache, float* scales,
+                        const float* channel_scales, int32_t num_tokens, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                        int32_t src_dtype, int32_t cache_dtype, int32_t scale_mode,
+                        hipStream_t stream) {
+  const int st = check_q8_append(num_tokens, num_kv_heads, head_dim, num_blocks, block_size,
+                                 src_dtype, scale_mode);
+  if (st) return st;
+  if (!is_q8(cache_dtype)) return PKV_ERR_DTYPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!x_new || !slot_mapping || !cache || !scales) return PKV_ERR_NULL;
+  const QTargetArgs tg[1] = {{x_new, cache, scales, channel_scales}};
+  return launch_kv_append_q8(tg, 1, slot_mapping, num_tokens, num_kv_heads, head_dim, num_blocks,
+                             src_dtype, cache_dtype, scale_mode == PKV_SCALE_FIRST_WRITE, stream);
 }
 
 int pkv_copy_blocks(void* k_cache, void* v_cache, float* k_scales, float* v_scales,
@@ -143,8 +178,8 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, float* k_scales, float* v_scal
   if (!eb) return PKV_ERR_DTYPE;
   const int64_t block_bytes = (int64_t)num_kv_heads * PKV_BLOCK_SIZE * head_dim * eb;
   if (block_bytes % 16 || block_bytes > (1 << 30)) return PKV_ERR_SHAPE;
-  if (dtype == PKV_FP8_E4M3 ? (!k_scales || !v_scales) : (k_scales || v_scales)) return PKV_ERR_DTYPE;
-  if (dtype == PKV_FP8_E4M3 && num_kv_heads > 256) return PKV_ERR_SHAPE;
+  if (is_q8(dtype) ? (!k_scales || !v_scales) : (k_scales || v_scales)) return PKV_ERR_DTYPE;
+  if (is_q8(dtype) && num_kv_heads > 256) return PKV_ERR_SHAPE;
   if (num_pairs == 0) return PKV_OK;
   if (!k_cache || !v_cache || !src_blocks || !dst_blocks) return PKV_ERR_NULL;
   return launch_copy_blocks(k_cache, v_cache, k_scales, v_scales, src_blocks, dst_blocks,
@@ -168,8 +203,8 @@ int pkv_paged_decode_attn(const void* q, const void* k_cache, const void* v_cach
                           const int32_t* block_tables, const int32_t* context_lens, float scale,
                           void* out, const pkv_decode_dims* dims, void* workspace,
                           size_t workspace_bytes, hipStream_t stream) {
-  return decode_common(q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens, scale,
-                       out, dims, workspace, workspace_bytes, stream, false);
+  return decode_common(q, k_cache, v_cache, nullptr, nullptr, nullptr, block_tables, context_lens,
+                       scale, out, dims, workspace, workspace_bytes, stream, -1);
 }
 
 int pkv_paged_decode_attn_fp8(const void* q, const void* k_cache, const void* v_cache,
@@ -177,8 +212,19 @@ int pkv_paged_decode_attn_fp8(const void* q, const void* k_cache, const void* v_
                               const int32_t* block_tables, const int32_t* context_lens,
                               float scale, void* out, const pkv_decode_dims* dims,
                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return decode_common(q, k_cache, v_cache, k_scales, v_scales, block_tables, context_lens, scale,
-                       out, dims, workspace, workspace_bytes, stream, true);
+  return decode_common(q, k_cache, v_cache, k_scales, v_scales, nullptr, block_tables, context_lens,
+                       scale, out, dims, workspace, workspace_bytes, stream, PKV_FP8_E4M3);
+}
+
+int pkv_paged_decode_attn_quant(const void* q, const void* k_cache, const void* v_cache,
+                                const float* k_scales, const float* v_scales,
+                                const float* k_channel_scales, int32_t v_dtype,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                float scale, void* out, const pkv_decode_dims* dims,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!is_q8(v_dtype)) return PKV_ERR_DTYPE;
+  return decode_common(q, k_cache, v_cache, k_scales, v_scales, k_channel_scales, block_tables,
+                       context_lens, scale, out, dims, workspace, workspace_bytes, stream, v_dtype);
 }
 
 int pkv_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t sink_words,

@@ -9,12 +9,18 @@
 // Decode is a matrix-vector product per KV head, bound by HBM: every K/V
 // byte is used by only g query heads.  The kernel therefore streams each
 // (block, kv_head) tile once from HBM and makes that one read serve all g
-// query heads.  Scores use packed dot2 for f16/bf16 K (and for fp8 K after
-// widening it to f16; the query is held in f16 after a power-of-two
-// rescale of the KV group that the scores undo), fp32 FMA for fp32 K.  P.V accumulates in
-// fp32: for f16 and fp8 V it is a dot2 over pairs of tokens with the
-// probabilities rounded once to f16 (relative error <= 2^-11 per weight);
-// bf16 and fp32 V use fp32 FMA.
+// query heads.  Scores use packed dot2 for f16/bf16 K (and for fp8 or int8
+// K after widening it to f16, both exact; the query is held in f16 after a
+// power-of-two rescale of the KV group that the scores undo), fp32 FMA for
+// fp32 K.  P.V accumulates in fp32: for f16, fp8 and int8 V it is a dot2
+// over pairs of tokens with the probabilities rounded once to f16 (relative
+// error <= 2^-11 per weight); bf16 and fp32 V use fp32 FMA.
+//
+// 8-bit caches ("The KV Cache memory ledger" 7; "KV Cache from first
+// principles" 5.2): K and V may use different code sets (K fp8 with V int8)
+// of the same width, each with a scale per (block, KV head); K may also have
+// one factor per (KV head, channel), which is folded into the query once:
+// <q, k * c> = <q * c, k>.
 //
 // Work split.  Grid = (partition p, kv head h, sequence b); a workgroup of
 // four waves owns the blocks [p*PB, (p+1)*PB) of (b, h); wave w takes every
@@ -122,8 +128,8 @@ __device__ __forceinline__ int level_bit(int c) {
 // ---- per-dtype pieces ------------------------------------------------------
 // The lane's slice of one query vector, kept in registers for the whole
 // partition: packed 16-bit pairs when K is f16/bf16 (dot2 with K directly),
-// packed f16 pairs when K is fp8 (dot2 with K converted to f16), fp32 when K
-// is fp32.
+// packed f16 pairs when K is 8-bit (dot2 with K converted to f16), fp32 when
+// K is fp32.
 template <KV KT, int EL> struct QSlice { uint32_t w[EL / 2]; };
 template <int EL> struct QSlice<KV::F32, EL> { float f[EL]; };
 
@@ -139,12 +145,21 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// q row (already offset to the lane's head) -> the lane's slice.  For fp8 K
-// the query is held in f16 after a power-of-two rescale `qexp` (applied here,
-// undone on the scores), chosen per KV group so its largest element is in
-// [2^14, 2^15).
+// Query element idx times K's channel factor (8-bit K only; `chan` may be
+// NULL: no factors).
+template <KV QT>
+__device__ __forceinline__ float q_elem(const void* qrow, const float* chan, int idx) {
+  const float x = load_elem_f32<QT>(qrow, idx);
+  return chan ? x * chan[idx] : x;
+}
+
+// q row (already offset to the lane's head) -> the lane's slice.  For 8-bit K
+// the query (times K's channel factors) is held in f16 after a power-of-two
+// rescale `qexp` (applied here, undone on the scores), chosen per KV group
+// so its largest element is in [2^14, 2^15).
 template <KV KT, KV QT, int EL, int LPT, int E, int VPT>
-__device__ __forceinline__ void load_q(QSlice<KT, EL>& qs, const void* qrow, int c, int qexp) {
+__device__ __forceinline__ void load_q(QSlice<KT, EL>& qs, const void* qrow, const float* chan,
+                                       int c, int qexp) {
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
     const int e0 = (v * LPT + c) * E;
@@ -158,20 +173,20 @@ __device__ __forceinline__ void load_q(QSlice<KT, EL>& qs, const void* qrow, int
     } else {
 #pragma unroll
       for (int e = 0; e < E; e += 2)
-        qs.w[(v * E + e) / 2] = pack_f16x2(__builtin_ldexpf(load_elem_f32<QT>(qrow, e0 + e), qexp),
-                                           __builtin_ldexpf(load_elem_f32<QT>(qrow, e0 + e + 1), qexp));
+        qs.w[(v * E + e) / 2] = pack_f16x2(__builtin_ldexpf(q_elem<QT>(qrow, chan, e0 + e), qexp),
+                                           __builtin_ldexpf(q_elem<QT>(qrow, chan, e0 + e + 1), qexp));
     }
   }
 }
 
-// Largest |q| of the lane's slice (fp8 path only, before packing).
+// Largest |q * c| of the lane's slice (8-bit K only, before packing).
 template <KV QT, int EL, int LPT, int E, int VPT>
-__device__ __forceinline__ float slice_absmax(const void* qrow, int c) {
+__device__ __forceinline__ float slice_absmax(const void* qrow, const float* chan, int c) {
   float m = 0.f;
 #pragma unroll
   for (int v = 0; v < VPT; ++v)
 #pragma unroll
-    for (int e = 0; e < E; ++e) m = fmaxf(m, fabsf(load_elem_f32<QT>(qrow, (v * LPT + c) * E + e)));
+    for (int e = 0; e < E; ++e) m = fmaxf(m, fabsf(q_elem<QT>(qrow, chan, (v * LPT + c) * E + e)));
   return m;
 }
 
@@ -200,10 +215,13 @@ __device__ __forceinline__ void to_f32(const TokWords<VPT>& t, float (&f)[EL]) {
     } else if constexpr (KT == KV::BF16) {
       f[2 * k] = bf16lo(w[k]);
       f[2 * k + 1] = bf16hi(w[k]);
-    } else {
+    } else if constexpr (KT == KV::FP8) {
       const float2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
       const float2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
       f[4 * k + 0] = lo.x; f[4 * k + 1] = lo.y; f[4 * k + 2] = hi.x; f[4 * k + 3] = hi.y;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f[4 * k + j] = (float)(int)(int8_t)(w[k] >> (8 * j));
     }
   }
 }
@@ -220,12 +238,35 @@ __device__ __forceinline__ void fp8_to_f16_pairs(const TokWords<VPT>& t, uint32_
   }
 }
 
+// int8 -> f16, exactly: a byte u placed under the f16 exponent of 1024 reads
+// as 1024 + u; with the sign bit flipped first, u = x + 128, so subtracting
+// 1152 leaves x (all values involved are integers below 2048: exact).
+constexpr uint32_t kI8Bias = 0x64806480u;   // f16 0x6400 (1024) in each half, byte sign flip
+__device__ __forceinline__ uint32_t i8_biased_to_f16(uint32_t u) {
+  const half2_t b = {(_Float16)1152.0f, (_Float16)1152.0f};
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, u) - b);
+}
+
+// int8 token words -> f16 pairs of adjacent elements (same token): EL / 2 words.
+template <int EL, int VPT>
+__device__ __forceinline__ void int8_to_f16_pairs(const TokWords<VPT>& t, uint32_t (&h)[EL / 2]) {
+  uint32_t w[4 * VPT];
+  words_of(t, w);
+#pragma unroll
+  for (int k = 0; k < 4 * VPT; ++k) {
+    // bytes x0..x3 -> halves (x0, x1) and (x2, x3), each byte under 0x64
+    const uint32_t x = w[k] ^ 0x80808080u;
+    h[2 * k] = i8_biased_to_f16(__builtin_amdgcn_perm(0x64646464u, x, 0x04010400u));
+    h[2 * k + 1] = i8_biased_to_f16(__builtin_amdgcn_perm(0x64646464u, x, 0x04030402u));
+  }
+}
+
 // Partial <q_slice, K_slice> for one token.
 template <KV KT, int EL, int VPT>
 __device__ __forceinline__ float qk_partial(const QSlice<KT, EL>& qs, const TokWords<VPT>& t,
                                             const float (&kf)[EL], const uint32_t (&kh)[EL / 2]) {
   float s;
-  if constexpr (KT == KV::F16 || KT == KV::FP8) {
+  if constexpr (KT == KV::F16 || is_quantised<KT>()) {
     uint32_t w[EL / 2];
     if constexpr (KT == KV::F16) words_of(t, w);
     else {
@@ -267,6 +308,14 @@ __device__ __forceinline__ void v_token_pairs(const TokWords<VPT>& t0, const Tok
       // word k holds elements 2k, 2k+1 of each token
       vp[2 * k] = __builtin_amdgcn_perm(b[k], a[k], 0x05040100u);
       vp[2 * k + 1] = __builtin_amdgcn_perm(b[k], a[k], 0x07060302u);
+    } else if constexpr (KT == KV::INT8) {
+      // word k holds int8 elements 4k..4k+3: element j of both tokens under
+      // the f16 bias, then unbias
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t sel = 0x0c000c00u | ((uint32_t)(4 + j) << 16) | (uint32_t)j;
+        vp[4 * k + j] = i8_biased_to_f16(__builtin_amdgcn_perm(b[k], a[k], sel) ^ kI8Bias);
+      }
     } else {
       // word k holds fp8 elements 4k..4k+3: interleave bytes, then widen
       const uint32_t lo = __builtin_amdgcn_perm(b[k], a[k], 0x05010400u);
@@ -334,14 +383,17 @@ struct SeqSpan {
 };
 
 // ---------------------------------------------------------------------------
-template <KV KT, KV QT, KV OT, int D, int G>
+template <KV KT, KV VT, KV QT, KV OT, int D, int G>
 __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
+  static_assert(kv_bytes<KT>::value == kv_bytes<VT>::value, "K and V share the tile layout");
+  static_assert(is_quantised<KT>() == is_quantised<VT>(), "8-bit K goes with 8-bit V");
+  constexpr bool KQ = is_quantised<KT>();
   using C = Cfg<KT, D, G>;
   constexpr int E = C::E, VPT = C::VPT, LPT = C::LPT, R = C::R, TPL = C::TPL;
   constexpr int NS = C::NS, NRS = C::NRS, NF = C::NF, EL = C::EL, NW = C::NW;
   constexpr int LEVELS = C::LEVELS;
   // P.V as f16 dot2 over pairs of tokens (probabilities rounded to f16)
-  constexpr bool PV_DOT2 = (KT == KV::F16 || KT == KV::FP8) && TPL >= 2;
+  constexpr bool PV_DOT2 = (VT == KV::F16 || is_quantised<VT>()) && TPL >= 2;
 
   // LDS: while streaming, per-wave rings of staged K and V tiles; at the end
   // of the partition the same bytes hold the per-wave partial results.
@@ -383,14 +435,16 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     return (QT == KV::F32) ? (const void*)((const float*)a.q + qoff)
                            : (const void*)((const uint16_t*)a.q + qoff);
   };
-  // fp8: one power-of-two rescale for the whole KV group, from the largest
-  // |q| over all g heads (every lane of a row sees all of them, so every lane
-  // derives the same exponent), so the partial sums the rows combine agree.
+  // 8-bit K: one power-of-two rescale for the whole KV group, from the
+  // largest |q * c| over all g heads (every lane of a row sees all of them,
+  // so every lane derives the same exponent), so the partial sums the rows
+  // combine agree.
+  const float* chan = (KQ && a.k_chan) ? a.k_chan + (int64_t)h * D : nullptr;
   int qexp = 0;
-  if constexpr (KT == KV::FP8) {
+  if constexpr (KQ) {
     float m = 0.f;
 #pragma unroll
-    for (int hs = 0; hs < G; ++hs) m = fmaxf(m, slice_absmax<QT, EL, LPT, E, VPT>(qrow_of(hs), c));
+    for (int hs = 0; hs < G; ++hs) m = fmaxf(m, slice_absmax<QT, EL, LPT, E, VPT>(qrow_of(hs), chan, c));
     static_for<LEVELS>([&](auto l) { m = fmaxf(m, xlevel<4 - LEVELS + decltype(l)::value>(m)); });
     int ex;
     (void)__builtin_frexpf(m, &ex);             // m = f * 2^ex, f in [0.5, 1)
@@ -400,7 +454,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
   const float qfac = __builtin_ldexpf(1.0f, -qexp);   // undoes the rescale on the scores
   QSlice<KT, EL> qs[G];
 #pragma unroll
-  for (int hs = 0; hs < G; ++hs) load_q<KT, QT, EL, LPT, E, VPT>(qs[hs], qrow_of(hs), c, qexp);
+  for (int hs = 0; hs < G; ++hs) load_q<KT, QT, EL, LPT, E, VPT>(qs[hs], qrow_of(hs), chan, c, qexp);
 
   float acc[G][EL];
   float mref[G];
@@ -480,7 +534,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     const uint32_t vbits = blk_ok ? span.valid_bits(jl) : 0u;
     float cs = a.scale;  // scale * log2(e), folded on the host
     float vsc = 1.f;
-    if constexpr (KT == KV::FP8) {
+    if constexpr (KQ) {
       const int64_t si = (int64_t)(blk_ok ? phys_raw : 0) * a.num_kv_heads + h;
       cs *= a.k_scales[si];
       vsc = a.v_scales[si];
@@ -494,6 +548,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
       uint32_t kh[EL / 2];
       if constexpr (KT == KV::F32) to_f32<KT, EL, VPT>(kr[i], kf);
       if constexpr (KT == KV::FP8) fp8_to_f16_pairs<EL, VPT>(kr[i], kh);
+      if constexpr (KT == KV::INT8) int8_to_f16_pairs<EL, VPT>(kr[i], kh);
 #pragma unroll
       for (int hs = 0; hs < G; ++hs) s[hs * TPL + i] = qk_partial<KT, EL, VPT>(qs[hs], kr[i], kf, kh);
     }
@@ -508,7 +563,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
       constexpr int lv = NRS + decltype(l)::value;
       s[0] += xlevel<4 - LEVELS + lv>(s[0]);
     });
-    if constexpr (KT == KV::FP8) cs *= qfac;
+    if constexpr (KQ) cs *= qfac;
 #pragma unroll
     for (int k = 0; k < NF; ++k) s[k] *= cs;
 
@@ -582,7 +637,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
       for (int m2 = 0; m2 < TPL / 2; ++m2) {
         uint32_t vp[EL];
-        v_token_pairs<KT, EL, VPT>(vv[2 * m2], vv[2 * m2 + 1], vp);
+        v_token_pairs<VT, EL, VPT>(vv[2 * m2], vv[2 * m2 + 1], vp);
 #pragma unroll
         for (int hs = 0; hs < G; ++hs) {
           const half2_t pp = __builtin_bit_cast(
@@ -596,7 +651,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < TPL; ++i) {
         float vf[EL];
-        to_f32<KT, EL, VPT>(vv[i], vf);
+        to_f32<VT, EL, VPT>(vv[i], vf);
 #pragma unroll
         for (int hs = 0; hs < G; ++hs) {
           const float pw = pf[hs * TPL + i];
@@ -780,10 +835,10 @@ size_t workspace_bytes_for(const pkv_decode_dims& d) {
   return (size_t)d.num_seqs * d.num_q_heads * np * (d.head_dim + 2) * sizeof(float);
 }
 
-template <KV KT, KV QT, KV OT, int D, int G>
+template <KV KT, KV VT, KV QT, KV OT, int D, int G>
 static int launch_typed(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((decode_partition_kernel<KT, QT, OT, D, G>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((decode_partition_kernel<KT, VT, QT, OT, D, G>), grid, dim3(256), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return PKV_ERR_LAUNCH;
   if (a.num_parts > 1) {
     hipLaunchKernelGGL((lse_merge_kernel<OT, D>), dim3(a.num_seqs * a.num_q_heads), dim3(64), 0,
@@ -793,50 +848,51 @@ static int launch_typed(const DecodeArgs& a, hipStream_t stream) {
   return PKV_OK;
 }
 
-template <KV KT, KV QT, KV OT, int D>
+template <KV KT, KV VT, KV QT, KV OT, int D>
 static int dispatch_g(const DecodeArgs& a, hipStream_t s) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_typed<KT, QT, OT, D, 1>(a, s);
-    case 2: return launch_typed<KT, QT, OT, D, 2>(a, s);
-    case 4: return launch_typed<KT, QT, OT, D, 4>(a, s);
-    case 8: return launch_typed<KT, QT, OT, D, 8>(a, s);
+    case 1: return launch_typed<KT, VT, QT, OT, D, 1>(a, s);
+    case 2: return launch_typed<KT, VT, QT, OT, D, 2>(a, s);
+    case 4: return launch_typed<KT, VT, QT, OT, D, 4>(a, s);
+    case 8: return launch_typed<KT, VT, QT, OT, D, 8>(a, s);
     default: return PKV_ERR_SHAPE;
   }
 }
 
-template <KV KT, KV QT, KV OT>
+template <KV KT, KV VT, KV QT, KV OT>
 static int dispatch_d(const DecodeArgs& a, hipStream_t s) {
   switch (a.head_dim) {
-    case 64: return dispatch_g<KT, QT, OT, 64>(a, s);
-    case 128: return dispatch_g<KT, QT, OT, 128>(a, s);
+    case 64: return dispatch_g<KT, VT, QT, OT, 64>(a, s);
+    case 128: return dispatch_g<KT, VT, QT, OT, 128>(a, s);
     default: return PKV_ERR_SHAPE;
   }
-}
-
-template <KV QT, KV OT>
-static int dispatch_fp8_out(const DecodeArgs& a, hipStream_t s) {
-  return dispatch_d<KV::FP8, QT, OT>(a, s);
 }
 
 int launch_decode(const DecodeArgs& a, hipStream_t s) {
-  const KV kt = (KV)a.kv_dtype, qt = (KV)a.q_dtype, ot = (KV)a.out_dtype;
-  if (kt != KV::FP8) {
-    if (qt != kt || ot != kt) return PKV_ERR_DTYPE;
+  const KV kt = (KV)a.kv_dtype, vt = (KV)a.v_dtype, qt = (KV)a.q_dtype, ot = (KV)a.out_dtype;
+  if (kt == KV::F32 || kt == KV::F16 || kt == KV::BF16) {
+    if (vt != kt || qt != kt || ot != kt) return PKV_ERR_DTYPE;
     switch (kt) {
-      case KV::F32: return dispatch_d<KV::F32, KV::F32, KV::F32>(a, s);
-      case KV::F16: return dispatch_d<KV::F16, KV::F16, KV::F16>(a, s);
-      case KV::BF16: return dispatch_d<KV::BF16, KV::BF16, KV::BF16>(a, s);
-      default: return PKV_ERR_DTYPE;
+      case KV::F32: return dispatch_d<KV::F32, KV::F32, KV::F32, KV::F32>(a, s);
+      case KV::F16: return dispatch_d<KV::F16, KV::F16, KV::F16, KV::F16>(a, s);
+      default: return dispatch_d<KV::BF16, KV::BF16, KV::BF16, KV::BF16>(a, s);
     }
   }
-#define PKV_FP8_CASE(Q, O)                                          \
-  if (qt == KV::Q && ot == KV::O) return dispatch_fp8_out<KV::Q, KV::O>(a, s);
-  PKV_FP8_CASE(BF16, BF16)
-  PKV_FP8_CASE(F16, F16)
-  PKV_FP8_CASE(F32, F32)
-  PKV_FP8_CASE(BF16, F32)
-  PKV_FP8_CASE(F16, F32)
-#undef PKV_FP8_CASE
+#define PKV_Q8_CASE(K, V, Q, O)                                                  \
+  if (kt == KV::K && vt == KV::V && qt == KV::Q && ot == KV::O)                  \
+    return dispatch_d<KV::K, KV::V, KV::Q, KV::O>(a, s);
+  // fp8 K and V: every query / output pairing
+  PKV_Q8_CASE(FP8, FP8, BF16, BF16)
+  PKV_Q8_CASE(FP8, FP8, F16, F16)
+  PKV_Q8_CASE(FP8, FP8, F32, F32)
+  PKV_Q8_CASE(FP8, FP8, BF16, F32)
+  PKV_Q8_CASE(FP8, FP8, F16, F32)
+  // mixed and int8 caches: 16-bit query and output of one type
+  PKV_Q8_CASE(FP8, INT8, BF16, BF16)
+  PKV_Q8_CASE(FP8, INT8, F16, F16)
+  PKV_Q8_CASE(INT8, INT8, BF16, BF16)
+  PKV_Q8_CASE(INT8, INT8, F16, F16)
+#undef PKV_Q8_CASE
   return PKV_ERR_DTYPE;
 }
 

@@ -38,15 +38,29 @@ __global__ void __launch_bounds__(256) kv_append_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// FP8 append: quantise on write ("The KV Cache memory ledger" 7: 8-bit K/V
-// with one scale per head; "Why does KV Cache eat GPU memory?": FP8 KV needs
-// calibrated scales).  Scales are per (block, KV head).  In first-write mode
-// the token that opens a block (offset 0) sets that block's scale to
-// max|x| / 448 of its own row; the pass that does so runs before the one
-// that quantises, so tokens of one call that land later in the same block
-// already see it.  Codes are RNE(clamp(x / scale, +-448)) with the quotient
-// a correctly rounded fp32 division and the conversion the hardware's
-// round-to-nearest-even e4m3 (OCP) convert.
+// 8-bit append: quantise on write ("The KV Cache memory ledger" 7: 8-bit K/V
+// with one scale per head, K in FP8 with V in INT8 as the mixed form; "Why
+// does KV Cache eat GPU memory?": FP8 KV needs calibrated scales; "KV Cache
+// from first principles" 5.2: per-channel factors for K's outlier channels).
+// Scales are per (block, KV head).  With channel factors the source is first
+// divided by its channel's factor.  In first-write mode the token that opens
+// a block (offset 0) sets that block's scale to max|y| / QMAX of its own row;
+// the pass that does so runs before the one that quantises, so tokens of one
+// call that land later in the same block already see it.  Codes are the
+// nearest code (ties to even) of clamp(y / scale, +-QMAX), every quotient a
+// correctly rounded fp32 division: for fp8 the hardware's round-to-nearest-
+// even e4m3 (OCP) convert, for int8 rint (NaN gives 0).
+//
+// grid.y selects one of up to two (source, cache, scales, factors) targets:
+// K and V in one launch, or a single cache.
+
+struct QTarget {
+  const void* src;       // [T][Hkv][D] of the source dtype
+  uint8_t* cache;        // [NB][Hkv][16][D] codes
+  float* scales;         // [NB][Hkv]
+  const float* chan;     // [Hkv][D] or NULL
+};
+struct QTargets { QTarget t[2]; };
 
 template <KV ST>
 __device__ __forceinline__ float src_elem(const void* base, int64_t i) {
@@ -55,37 +69,56 @@ __device__ __forceinline__ float src_elem(const void* base, int64_t i) {
   else return __builtin_bit_cast(float, ((uint32_t)((const uint16_t*)base)[i]) << 16);
 }
 
+template <KV CT> constexpr float qmax() { return CT == KV::FP8 ? 448.0f : 127.0f; }
+
+// Source element divided by its channel factor (if any).
 template <KV ST>
-__global__ void __launch_bounds__(256) fp8_first_write_scale_kernel(
-    const void* __restrict__ k_new, const void* __restrict__ v_new,
-    const int64_t* __restrict__ slot_mapping, float* __restrict__ k_scales,
-    float* __restrict__ v_scales, int num_tokens, int num_kv_heads, int head_dim,
-    int64_t num_slots) {
+__device__ __forceinline__ float scaled_src(const QTarget& q, int64_t row, int h, int d, int head_dim) {
+  const float x = src_elem<ST>(q.src, row * head_dim + d);
+  return q.chan ? x / q.chan[(int64_t)h * head_dim + d] : x;
+}
+
+template <KV ST, KV CT>
+__global__ void __launch_bounds__(256) q8_first_write_scale_kernel(
+    QTargets tg, const int64_t* __restrict__ slot_mapping, int num_tokens, int num_kv_heads,
+    int head_dim, int64_t num_slots) {
   const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // t * Hkv + h
   if (row >= (int64_t)num_tokens * num_kv_heads) return;
-  const bool is_v = blockIdx.y != 0;
+  const QTarget q = blockIdx.y ? tg.t[1] : tg.t[0];   // uniform: no indexed copy
   const int64_t t = row / num_kv_heads;
   const int h = (int)(row % num_kv_heads);
   const int64_t slot = slot_mapping[t];
   if (slot < 0 || slot >= num_slots || slot % PKV_BLOCK_SIZE != 0) return;
-  const void* src = is_v ? v_new : k_new;
   float amax = 0.f;
-  for (int d = 0; d < head_dim; ++d) amax = fmaxf(amax, fabsf(src_elem<ST>(src, row * head_dim + d)));
-  float* scales = is_v ? v_scales : k_scales;
-  scales[(slot / PKV_BLOCK_SIZE) * num_kv_heads + h] = amax > 0.f ? amax / 448.0f : 1.0f;
+  for (int d = 0; d < head_dim; ++d) amax = fmaxf(amax, fabsf(scaled_src<ST>(q, row, h, d, head_dim)));
+  q.scales[(slot / PKV_BLOCK_SIZE) * num_kv_heads + h] = amax > 0.f ? amax / qmax<CT>() : 1.0f;
 }
 
-template <KV ST>
-__global__ void __launch_bounds__(256) fp8_quantize_append_kernel(
-    const void* __restrict__ k_new, const void* __restrict__ v_new,
-    const int64_t* __restrict__ slot_mapping, uint8_t* __restrict__ k_cache,
-    uint8_t* __restrict__ v_cache, const float* __restrict__ k_scales,
-    const float* __restrict__ v_scales, int num_tokens, int num_kv_heads, int head_dim,
-    int64_t num_slots) {
+// Four clamped quotients -> four codes in one word (element 0 in the low byte).
+template <KV CT>
+__device__ __forceinline__ uint32_t encode4(const float (&v)[4]) {
+  if constexpr (CT == KV::FP8) {
+    int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
+  } else {
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float r = v[e] == v[e] ? __builtin_rintf(v[e]) : 0.f;   // ties to even; NaN -> 0
+      word |= ((uint32_t)(int)r & 0xFFu) << (8 * e);
+    }
+    return word;
+  }
+}
+
+template <KV ST, KV CT>
+__global__ void __launch_bounds__(256) q8_quantize_append_kernel(
+    QTargets tg, const int64_t* __restrict__ slot_mapping, int num_tokens, int num_kv_heads,
+    int head_dim, int64_t num_slots) {
   const int groups = head_dim / 16;                         // 16 elements per thread
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)num_tokens * num_kv_heads * groups) return;
-  const bool is_v = blockIdx.y != 0;
+  const QTarget q = blockIdx.y ? tg.t[1] : tg.t[0];   // uniform: no indexed copy
   const int gi = (int)(idx % groups);
   const int64_t row = idx / groups;                         // t * Hkv + h
   const int h = (int)(row % num_kv_heads);
@@ -93,54 +126,60 @@ __global__ void __launch_bounds__(256) fp8_quantize_append_kernel(
   const int64_t slot = slot_mapping[t];
   if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot / PKV_BLOCK_SIZE, off = slot % PKV_BLOCK_SIZE;
-  const float scale = (is_v ? v_scales : k_scales)[blk * num_kv_heads + h];
-  const void* src = is_v ? v_new : k_new;
+  const float scale = q.scales[blk * num_kv_heads + h];
+  constexpr float QM = qmax<CT>();
   uint32_t packed[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    float q[4];
+    float v4[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float v = src_elem<ST>(src, row * head_dim + gi * 16 + w * 4 + e) / scale;
-      v = v > 448.0f ? 448.0f : (v < -448.0f ? -448.0f : v);   // NaN passes through
-      q[e] = v;
+      float v = scaled_src<ST>(q, row, h, gi * 16 + w * 4 + e, head_dim) / scale;
+      v4[e] = v > QM ? QM : (v < -QM ? -QM : v);   // NaN passes through
     }
-    int word = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-    word = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], word, true);
-    packed[w] = (uint32_t)word;
+    packed[w] = encode4<CT>(v4);
   }
-  uint8_t* dst = (is_v ? v_cache : k_cache) +
-                 ((blk * num_kv_heads + h) * PKV_BLOCK_SIZE + off) * head_dim + gi * 16;
+  uint8_t* dst = q.cache + ((blk * num_kv_heads + h) * PKV_BLOCK_SIZE + off) * head_dim + gi * 16;
   *(uint4*)dst = make_uint4(packed[0], packed[1], packed[2], packed[3]);
 }
 
-int launch_kv_append_fp8(const void* k_new, const void* v_new, const int64_t* slot_mapping,
-                         void* k_cache, void* v_cache, float* k_scales, float* v_scales,
-                         int num_tokens, int num_kv_heads, int head_dim, int num_blocks,
-                         int src_dtype, bool first_write, hipStream_t stream) {
+int launch_kv_append_q8(const QTargetArgs* targets, int num_targets, const int64_t* slot_mapping,
+                        int num_tokens, int num_kv_heads, int head_dim, int num_blocks,
+                        int src_dtype, int code_dtype, bool first_write, hipStream_t stream) {
   const int64_t rows = (int64_t)num_tokens * num_kv_heads;
   if (rows == 0) return PKV_OK;
   const int64_t slots = (int64_t)num_blocks * PKV_BLOCK_SIZE;
   const int64_t threads = rows * (head_dim / 16);
   if ((rows + 255) / 256 > 0x7FFFFFFF || (threads + 255) / 256 > 0x7FFFFFFF) return PKV_ERR_SHAPE;
-  const dim3 g1((unsigned)((rows + 255) / 256), 2), g2((unsigned)((threads + 255) / 256), 2);
-#define PKV_FP8_APPEND(ST)                                                                        \
+  QTargets tg{};
+  for (int i = 0; i < num_targets; ++i)
+    tg.t[i] = QTarget{targets[i].src, (uint8_t*)targets[i].cache, targets[i].scales, targets[i].chan};
+  const dim3 g1((unsigned)((rows + 255) / 256), num_targets);
+  const dim3 g2((unsigned)((threads + 255) / 256), num_targets);
+#define PKV_Q8_APPEND(ST, CT)                                                                     \
   do {                                                                                            \
     if (first_write)                                                                              \
-      hipLaunchKernelGGL(fp8_first_write_scale_kernel<ST>, g1, dim3(256), 0, stream, k_new,      \
-                         v_new, slot_mapping, k_scales, v_scales, num_tokens, num_kv_heads,       \
-                         head_dim, slots);                                                        \
-    hipLaunchKernelGGL(fp8_quantize_append_kernel<ST>, g2, dim3(256), 0, stream, k_new, v_new,   \
-                       slot_mapping, (uint8_t*)k_cache, (uint8_t*)v_cache, k_scales, v_scales,   \
-                       num_tokens, num_kv_heads, head_dim, slots);                                \
+      hipLaunchKernelGGL((q8_first_write_scale_kernel<ST, CT>), g1, dim3(256), 0, stream, tg,     \
+                         slot_mapping, num_tokens, num_kv_heads, head_dim, slots);                \
+    hipLaunchKernelGGL((q8_quantize_append_kernel<ST, CT>), g2, dim3(256), 0, stream, tg,        \
+                       slot_mapping, num_tokens, num_kv_heads, head_dim, slots);                  \
   } while (0)
-  switch ((KV)src_dtype) {
-    case KV::F32: PKV_FP8_APPEND(KV::F32); break;
-    case KV::F16: PKV_FP8_APPEND(KV::F16); break;
-    case KV::BF16: PKV_FP8_APPEND(KV::BF16); break;
-    default: return PKV_ERR_DTYPE;
+#define PKV_Q8_SRC(CT)                                       \
+  switch ((KV)src_dtype) {                                   \
+    case KV::F32: PKV_Q8_APPEND(KV::F32, CT); break;         \
+    case KV::F16: PKV_Q8_APPEND(KV::F16, CT); break;         \
+    case KV::BF16: PKV_Q8_APPEND(KV::BF16, CT); break;       \
+    default: return PKV_ERR_DTYPE;                           \
   }
-#undef PKV_FP8_APPEND
+  if ((KV)code_dtype == KV::FP8) {
+    PKV_Q8_SRC(KV::FP8)
+  } else if ((KV)code_dtype == KV::INT8) {
+    PKV_Q8_SRC(KV::INT8)
+  } else {
+    return PKV_ERR_DTYPE;
+  }
+#undef PKV_Q8_SRC
+#undef PKV_Q8_APPEND
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 

@@ -6,13 +6,17 @@
 
 namespace pkv {
 
-enum class KV : int { F32 = 0, F16 = 1, BF16 = 2, FP8 = 3 };
+enum class KV : int { F32 = 0, F16 = 1, BF16 = 2, FP8 = 3, INT8 = 4 };
+
+// 8-bit codes with a per-(block, head) scale
+template <KV T> constexpr bool is_quantised() { return T == KV::FP8 || T == KV::INT8; }
 
 template <KV T> struct kv_bytes;
 template <> struct kv_bytes<KV::F32> { static constexpr int value = 4; };
 template <> struct kv_bytes<KV::F16> { static constexpr int value = 2; };
 template <> struct kv_bytes<KV::BF16> { static constexpr int value = 2; };
 template <> struct kv_bytes<KV::FP8> { static constexpr int value = 1; };
+template <> struct kv_bytes<KV::INT8> { static constexpr int value = 1; };
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
@@ -79,7 +83,5 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
-
-template <KV T> struct out_store;
 
 }  // namespace pkv

@@ -10,10 +10,19 @@ int launch_kv_append(const void* k_new, const void* v_new, const int64_t* slot_m
                      void* k_cache, void* v_cache, int num_tokens, int num_kv_heads,
                      int row_bytes, int num_blocks, hipStream_t stream);
 
-int launch_kv_append_fp8(const void* k_new, const void* v_new, const int64_t* slot_mapping,
-                         void* k_cache, void* v_cache, float* k_scales, float* v_scales,
-                         int num_tokens, int num_kv_heads, int head_dim, int num_blocks,
-                         int src_dtype, bool first_write, hipStream_t stream);
+// One cache to quantise into: source rows, codes, per-(block, head) scales
+// and optional per-(head, channel) factors.
+struct QTargetArgs {
+  const void* src;
+  void* cache;
+  float* scales;
+  const float* chan;
+};
+
+// 8-bit append into one or two caches of the same code set (grid.y picks).
+int launch_kv_append_q8(const QTargetArgs* targets, int num_targets, const int64_t* slot_mapping,
+                        int num_tokens, int num_kv_heads, int head_dim, int num_blocks,
+                        int src_dtype, int code_dtype, bool first_write, hipStream_t stream);
 
 int launch_copy_blocks(void* k_cache, void* v_cache, float* k_scales, float* v_scales,
                        const int32_t* src, const int32_t* dst, int n, int num_kv_heads,
@@ -23,8 +32,9 @@ struct DecodeArgs {
   const void* q;
   const void* k_cache;
   const void* v_cache;
-  const float* k_scales;   // fp8 only
-  const float* v_scales;   // fp8 only
+  const float* k_scales;   // 8-bit caches only: [num_blocks][num_kv_heads]
+  const float* v_scales;   // 8-bit caches only
+  const float* k_chan;     // 8-bit K only, may be NULL: [num_kv_heads][head_dim]
   const int32_t* block_tables;
   const int32_t* context_lens;
   float scale;
@@ -34,7 +44,7 @@ struct DecodeArgs {
   int num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks;
   int part_blocks, num_parts;
   int window, sinks;       // sliding window (0 = off) and attention-sink tokens
-  int q_dtype, kv_dtype, out_dtype;
+  int q_dtype, kv_dtype, v_dtype, out_dtype;   // kv_dtype is K's
 };
 
 // Partition plan: depends on dims only.

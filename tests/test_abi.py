@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
     lib = pkv.load_library()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pkv_version() == 100
+    assert lib.pkv_version() == 110
 
 
 def _dims(**kw):
@@ -94,6 +94,43 @@ def test_fp8_status_codes():
     assert _attn_fp8(_dims(**dict(ok, kv_dtype=1))) == -3
     assert _attn_fp8(_dims(**dict(ok, q_dtype=3))) == -3
     assert _attn_fp8(_dims(**dict(ok, out_dtype=1))) == -3        # bf16 q, f16 out
+
+
+def _attn_quant(dims, v_dtype, ks=FAKE, vs=FAKE, q=FAKE):
+    lib = pkv.load_library()
+    return lib.pkv_paged_decode_attn_quant(q, FAKE, FAKE, ks, vs, None, v_dtype, FAKE, FAKE,
+                                           ctypes.c_float(0.088), FAKE, ctypes.byref(dims), None, 0,
+                                           None)
+
+
+def test_quant_status_codes():
+    """Pairs outside (fp8, fp8), (fp8, int8), (int8, int8), or with a query /
+    output pairing those pairs do not take, are refused before any launch."""
+    ok = dict(q_dtype=2, out_dtype=2, num_q_heads=32, max_blocks_per_seq=16)
+    for k, v in ((4, 3), (1, 4), (3, 1), (4, 2)):          # int8 K + fp8 V, f16 K, ...
+        assert _attn_quant(_dims(**dict(ok, kv_dtype=k)), v) == -3, (k, v)
+    assert _attn_quant(_dims(**dict(ok, kv_dtype=3, out_dtype=0)), 4) == -3    # mixed, f32 out
+    assert _attn_quant(_dims(**dict(ok, kv_dtype=4, q_dtype=0, out_dtype=0)), 4) == -3
+    assert _attn_quant(_dims(**dict(ok, kv_dtype=4, q_dtype=4, out_dtype=4)), 4) == -3
+    assert _attn_quant(_dims(**dict(ok, kv_dtype=3)), 4, ks=None) == -1
+    assert _attn_quant(_dims(**dict(ok, kv_dtype=4)), 4, vs=None) == -1
+    assert _attn_quant(_dims(**dict(ok, kv_dtype=4)), 4, q=None) == -1
+    assert _attn_quant(_dims(**dict(ok, kv_dtype=4, head_dim=96)), 4) == -2
+    # int8 through the other entry points
+    assert _attn(_dims(kv_dtype=4, q_dtype=4, out_dtype=4)) == -3
+    assert _attn_fp8(_dims(kv_dtype=4, q_dtype=2, out_dtype=2)) == -3
+
+
+def test_append_quant_status_codes():
+    lib = pkv.load_library()
+    call = lambda *a: lib.pkv_kv_append_quant(*a, None)
+    # x, slots, cache, scales, chan, T, Hkv, D, NB, bs, src, cache_dtype, mode
+    assert call(FAKE, FAKE, FAKE, FAKE, None, 4, 8, 128, 64, 16, 2, 1, 0) == -3    # f16 cache
+    assert call(FAKE, FAKE, FAKE, FAKE, None, 4, 8, 128, 64, 16, 3, 4, 0) == -3    # fp8 source
+    assert call(FAKE, FAKE, FAKE, FAKE, None, 4, 8, 120, 64, 16, 2, 4, 0) == -2    # D % 16
+    assert call(FAKE, FAKE, FAKE, FAKE, None, 4, 8, 128, 64, 16, 2, 4, 2) == -2    # scale mode
+    assert call(FAKE, FAKE, FAKE, None, None, 4, 8, 128, 64, 16, 2, 4, 0) == -1    # no scales
+    assert call(None, None, None, None, None, 0, 8, 128, 64, 16, 2, 4, 0) == 0     # nothing to do
 
 
 def test_append_status_codes():

@@ -1,7 +1,8 @@
 """HIP path against the float64 oracle, element by element (needs a GPU).
 
 Tolerances (max-abs against the oracle run on the same stored values):
-fp32 1e-5, fp16/bf16 1e-2, fp8 5e-2; kv_append bit-exact.
+fp32 1e-5, fp16/bf16 1e-2, 8-bit caches (fp8, int8, mixed) 5e-2; every
+append (plain or quantising) bit-exact.
 """
 
 import numpy as np
@@ -115,21 +116,107 @@ def test_fp8_quantise_ties_saturation_and_subnormals():
     assert bad.size == 0, [(tuple(i), int(got[tuple(i)]), int(ref_c[tuple(i)])) for i in bad[:8]]
 
 
-@pytest.mark.parametrize("dt", ["f32", "f16", "bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("code", ["int8", "fp8_e4m3"])
+@pytest.mark.parametrize("src", ["f32", "bf16"])
+@pytest.mark.parametrize("first_write", [False, True])
+@pytest.mark.parametrize("chan", [False, True])
+def test_kv_append_quant_bit_exact(code, src, first_write, chan):
+    """One cache at a time, with or without per-channel factors: codes and
+    scales equal the oracle's bit for bit."""
+    say(f"[kv_append_quant] code={code} src={src} first_write={first_write} chan={chan}")
+    rng = np.random.default_rng(11)
+    NB, H, D, T = 12, 4, 128, 21
+    npdt = np.uint8 if code == "fp8_e4m3" else np.int8
+    codes = rng.integers(0, 0x7E, size=(NB, H, 16, D)).astype(npdt)
+    scales = rng.uniform(0.002, 0.05, size=(NB, H)).astype(np.float32)
+    cs = None
+    if chan:
+        cs = rng.uniform(0.25, 20.0, size=(H, D)).astype(np.float32)
+        cs[:, ::7] = 16.0
+    x = torch.from_numpy(rng.standard_normal((T, H, D)).astype(np.float32) * 2).to(TORCH_DT[src])
+    x[3] *= 40
+    slots = np.array([0, 1, 2, 3, 4, 5, 16, 33, -1, 48, 49, 50, 51, 52, 53, 54, 55, 56, 57, 190,
+                      NB * 16 + 3], dtype=np.int64)
+    xf = oracle.stored_to_f64(host_storage(x), src).astype(np.float32)
+    ref_c, ref_s = oracle.kv_append_quant(codes, scales, xf, slots, code=code, first_write=first_write,
+                                          channel_scales=cs)
+    dc = torch.from_numpy(codes).to(DEV)
+    ds = torch.from_numpy(scales).to(DEV)
+    dcs = None if cs is None else torch.from_numpy(cs).to(DEV)
+    pkv.kv_append_quant(x.to(DEV), torch.from_numpy(slots).to(DEV), dc, ds, channel_scales=dcs,
+                        first_write=first_write)
+    torch.cuda.synchronize()
+    assert np.array_equal(dc.cpu().numpy(), ref_c)
+    assert np.array_equal(ds.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+
+
+def test_int8_quantise_ties_saturation_and_nan():
+    """Scale 1: every half-integer tie in range, both fp32 neighbours of it,
+    +-127.5 and beyond, infinities and NaN."""
+    say("[kv_append_quant] int8 rounding edge cases")
+    half = np.arange(-127, 127, dtype=np.float32) + np.float32(0.5)
+    edge = np.concatenate([half, np.nextafter(half, np.float32(-np.inf)), np.nextafter(half, np.float32(np.inf)),
+                           np.float32([0.0, -0.0, 126.9, 127.0, 127.49, 127.5, 128.0, 1e6, np.inf, -np.inf,
+                                       np.nan, 1e-30, -1e-30])]).astype(np.float32)
+    D, H = 128, 1
+    T = -(-edge.size // D)
+    x = np.zeros((T * D,), np.float32)
+    x[: edge.size] = edge
+    x = x.reshape(T, H, D)
+    NB = -(-T // 16)
+    slots = np.arange(T, dtype=np.int64)
+    codes = np.zeros((NB, H, 16, D), np.int8)
+    ones = np.ones((NB, H), np.float32)
+    ref_c, _ = oracle.kv_append_int8(codes, ones, x, slots, first_write=False)
+    dc = torch.zeros((NB, H, 16, D), dtype=torch.int8, device=DEV)
+    pkv.kv_append_quant(torch.from_numpy(x).to(DEV), torch.from_numpy(slots).to(DEV), dc,
+                        torch.ones((NB, H), device=DEV))
+    torch.cuda.synchronize()
+    got = dc.cpu().numpy()
+    bad = np.argwhere(got != ref_c)
+    assert bad.size == 0, [(tuple(i), int(got[tuple(i)]), int(ref_c[tuple(i)])) for i in bad[:8]]
+
+
+def test_int8_all_codes_decode_through_attention():
+    """With one token, out = V * scale: every int8 code (scale 1, and a
+    power-of-two scale) comes out exactly, under fp8 and int8 K."""
+    say("[int8] 256 codes through a length-1 attention")
+    D = 128
+    codes = np.arange(-128, 128, dtype=np.int16).astype(np.int8).reshape(2, D)
+    vc = np.zeros((4, 1, 16, D), np.int8)
+    vc[1, 0, 0] = codes[0]
+    vc[3, 0, 0] = codes[1]
+    tables = np.array([[1], [3]], np.int32)
+    lens = np.array([1, 1], np.int32)
+    q = torch.randn((2, 1, D), device=DEV).to(torch.bfloat16)
+    for kdt, kfill in ((torch.uint8, 0x38), (torch.int8, 5)):
+        kc = torch.full((4, 1, 16, D), kfill, dtype=kdt, device=DEV)
+        for vscale in (1.0, 0.25):
+            out = torch.empty((2, 1, D), device=DEV, dtype=torch.bfloat16)
+            vs = torch.full((4, 1), vscale, device=DEV)
+            pkv.paged_decode_attn(q, kc, torch.from_numpy(vc).to(DEV), torch.from_numpy(tables).to(DEV),
+                                  torch.from_numpy(lens).to(DEV), 0.1, out,
+                                  k_scales=torch.ones((4, 1), device=DEV), v_scales=vs)
+            got = out.float().cpu().numpy()[:, 0, :].astype(np.float64)
+            assert np.array_equal(got, codes.astype(np.float64) * vscale), (kdt, vscale)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16", "fp8_e4m3", "int8"])
 def test_copy_blocks_bit_exact(dt):
     say(f"[copy_blocks] dtype={dt}")
     rng = np.random.default_rng(9)
     NB, H, D = 40, 4, 128
-    nbytes = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}[dt]
+    nbytes = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1, "int8": 1}[dt]
     raw = rng.integers(0, 256, size=(2, NB, H, 16, D * nbytes), dtype=np.uint8)
-    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "fp8_e4m3": torch.uint8}[dt]
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "fp8_e4m3": torch.uint8,
+           "int8": torch.int8}[dt]
     kc = torch.from_numpy(raw[0].copy()).view(tdt).to(DEV)
     vc = torch.from_numpy(raw[1].copy()).view(tdt).to(DEV)
     src = np.array([3, 7, 11, 0, 39, 5, 2], np.int32)
     dst = np.array([20, 21, 22, 23, 24, 99, 2], np.int32)     # 99 outside the pool, 2 -> 2 no-op
     ks = vs = None
     sc = rng.uniform(size=(2, NB, H)).astype(np.float32)
-    if dt == "fp8_e4m3":
+    if dt in ("fp8_e4m3", "int8"):
         ks, vs = torch.from_numpy(sc[0].copy()).to(DEV), torch.from_numpy(sc[1].copy()).to(DEV)
     pkv.copy_blocks(kc, vc, torch.from_numpy(src).to(DEV), torch.from_numpy(dst).to(DEV), ks, vs)
     torch.cuda.synchronize()
@@ -224,10 +311,10 @@ def test_kv_append_skips_out_of_pool_slots():
 # decode attention, oracle-sized cases
 # --------------------------------------------------------------------------
 
-def _ragged(name, kv, q, out, D, G, lens, seed, hkv=2, append=False):
+def _ragged(name, kv, q, out, D, G, lens, seed, hkv=2, append=False, v=None, outliers=0):
     return DecodeWorkload(name=name, seed=seed, num_layers=1, num_seqs=len(lens), num_q_heads=hkv * G,
                           num_kv_heads=hkv, head_dim=D, kv_dtype=kv, q_dtype=q, out_dtype=out,
-                          context_lens=tuple(lens), append=append)
+                          context_lens=tuple(lens), append=append, v_dtype=v, k_outliers=outliers)
 
 
 RAGGED = [1, 15, 16, 17, 31, 33, 100, 257, 0, 64, 511]
@@ -247,6 +334,18 @@ SMALL = {
     "ragged_fp8_g2_d128_f32": _ragged("r8", "fp8_e4m3", "f32", "f32", 128, 2, RAGGED, 8),
     "ragged_bf16_g8_d128_append": _ragged("r9", "bf16", "bf16", "bf16", 128, 8,
                                           [1, 16, 17, 200, 33, 48, 49], 9, hkv=3, append=True),
+    # 8-bit mixed and int8 caches (K fp8 + V int8; int8 K with channel factors)
+    "long_fp8k_int8v_small": scaled(WORKLOADS["long_fp8k_int8v"], num_seqs=2, len_range=(8192, 8192)),
+    "long_int8_kchan_small": scaled(WORKLOADS["long_int8_kchan"], num_seqs=2, len_range=(8192, 8192)),
+    "ragged_fp8k_int8v_g8_d64": _ragged("r10", "fp8_e4m3", "bf16", "bf16", 64, 8, RAGGED, 10, v="int8"),
+    "ragged_fp8k_int8v_g1_d128_f16": _ragged("r11", "fp8_e4m3", "f16", "f16", 128, 1, RAGGED, 11, v="int8"),
+    "ragged_int8_g4_d64_chan": _ragged("r12", "int8", "f16", "f16", 64, 4, RAGGED, 12, outliers=3),
+    "ragged_int8_g2_d128_chan_append": _ragged("r13", "int8", "bf16", "bf16", 128, 2,
+                                               [1, 16, 17, 200, 33, 48, 49], 13, hkv=3, append=True,
+                                               outliers=5),
+    "ragged_fp8k_int8v_g4_d128_chan_append": _ragged("r14", "fp8_e4m3", "bf16", "bf16", 128, 4,
+                                                     [2, 15, 16, 64, 65, 300], 14, hkv=2, append=True,
+                                                     v="int8", outliers=4),
 }
 
 
@@ -286,6 +385,8 @@ WINDOWED = [
     ("ragged_bf16_g8_d128_append", 30, 2, 0),
     ("long_fp8_small", 1024, 32, 0),
     ("llama3_8b_bf16_small", 700, 4, 0),
+    ("ragged_fp8k_int8v_g8_d64", 40, 8, 1),
+    ("long_int8_kchan_small", 2000, 16, 0),
 ]
 
 
@@ -437,6 +538,8 @@ def _compact_rows(x, layer, lay, seqs):
     if "k_scales" in x:
         h["k_scales"] = host_storage(x["k_scales"][layer].index_select(0, idx))
         h["v_scales"] = host_storage(x["v_scales"][layer].index_select(0, idx))
+    if "k_channel_scales" in x:
+        h["k_channel_scales"] = host_storage(x["k_channel_scales"])
     tables = np.full_like(lay.block_tables, -1)
     for b in seqs:
         tables[b, : nblk[b]] = [remap[int(o)] for o in lay.block_tables[b, : nblk[b]]]
@@ -451,7 +554,8 @@ def _compact_rows(x, layer, lay, seqs):
     return h, tables, slots
 
 
-@pytest.mark.parametrize("name", ["llama3_8b_bf16", "mha13b_prefix_f16", "long_fp8", "llama70b_f16_80l"])
+@pytest.mark.parametrize("name", ["llama3_8b_bf16", "mha13b_prefix_f16", "long_fp8", "llama70b_f16_80l",
+                                  "long_fp8k_int8v", "long_int8_kchan"])
 def test_full_size_sampled_rows(name):
     spec = WORKLOADS[name]
     lay = build_layout(spec)
@@ -475,8 +579,10 @@ def test_full_size_sampled_rows(name):
         h, tables, slots = snaps[layer]
         kc, vc, ks, vs = oracle_append(h, spec, slots)
         ref = oracle.paged_decode_attention(h["q"], kc, vc, tables, lay.context_lens, spec.scale,
-                                            q_tag=spec.q_dtype, kv_tag=spec.kv_dtype,
-                                            k_scales=ks, v_scales=vs, seqs=seqs, q_heads=heads)
+                                            q_tag=spec.q_dtype, kv_tag=spec.kv_dtype, v_tag=spec.v_tag,
+                                            k_scales=ks, v_scales=vs,
+                                            k_channel_scales=h.get("k_channel_scales"),
+                                            seqs=seqs, q_heads=heads)
         got = out_f64(outs[layer])[seqs][:, heads]
         err = max_err(got, ref)
         say(f"    layer {layer} seqs {seqs} heads {heads}: max|err| = {err:.3e} (tol {tol})")

@@ -5,7 +5,8 @@ import pytest
 import torch
 
 from workloads import (WORKLOADS, BlockPool, PoolExhausted, build_layout, make_host_inputs,
-                       scaled, fp8_quantize_blocks, POISON_FP8_CODE)
+                       scaled, fp8_quantize_blocks, quantize_blocks, POISON_FP8_CODE,
+                       POISON_INT8_CODE)
 from oracle import decode_e4m3fn
 
 BS = 16
@@ -45,7 +46,7 @@ def test_pool_refcount_fork_and_free():
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_layout_shapes(name):
     w = WORKLOADS[name]
-    if name == "long_fp8":
+    if name.startswith("long_"):
         w = scaled(w, num_seqs=2, len_range=(4096, 4096))
     lay = build_layout(w)
     nblk = -(-lay.context_lens // BS)
@@ -123,3 +124,37 @@ def test_fp8_quantise_zero_tile_scale_is_one():
     x = torch.zeros((1, 1, BS, 4))
     codes, s = fp8_quantize_blocks(x)
     assert s.item() == 1.0 and (codes == 0).all()
+
+
+def test_mixed_and_int8_recipes():
+    """K fp8 / V int8, and int8 K with outlier channels: the codes, scales,
+    poison and channel factors the recipe states."""
+    w = scaled(WORKLOADS["long_fp8k_int8v"], num_seqs=2, len_range=(64, 64))
+    lay = build_layout(w)
+    x = make_host_inputs(lay)
+    hist = lay.history_mask
+    assert x["k_cache"].dtype == torch.uint8 and x["v_cache"].dtype == torch.int8
+    v = x["v_cache"][0].numpy().transpose(0, 2, 1, 3)
+    assert (np.abs(v[hist].astype(int)).max(axis=-1) <= 127).all()
+    assert (v[~hist] == POISON_INT8_CODE).all()
+    # every (block, head) tile's history reaches +-127
+    vt = x["v_cache"][0].numpy()
+    for blk in range(lay.num_blocks):
+        assert (np.abs(vt[blk][:, hist[blk]].astype(int)).max(axis=(1, 2)) == 127).all()
+    assert "k_channel_scales" not in x
+
+    w = scaled(WORKLOADS["long_int8_kchan"], num_seqs=2, len_range=(64, 64))
+    lay = build_layout(w)
+    x = make_host_inputs(lay)
+    c = x["k_channel_scales"].numpy()
+    assert c.shape == (w.num_kv_heads, w.head_dim)
+    assert ((c == 16).sum(axis=1) == w.k_outliers).all() and ((c == 1) | (c == 16)).all()
+    # the new token carries the outliers: its outlier channels are ~16x larger
+    kn = x["k_new"][0].float().numpy()
+    for h in range(w.num_kv_heads):
+        ratio = np.abs(kn[:, h, c[h] == 16]).mean() / np.abs(kn[:, h, c[h] == 1]).mean()
+        assert 4 < ratio < 64
+    # int8 rounding of the recipe: halves to even
+    codes, s = quantize_blocks(torch.tensor([0.5, 1.5, 2.5, -0.5, 127.0]).view(1, 1, 1, 5),
+                               code="int8")
+    assert s.item() == 1.0 and codes.flatten().tolist() == [0, 2, 2, 0, 127]

@@ -14,11 +14,17 @@ Recipe (all seeded from the workload's seed):
     every cache slot that holds no history token (block tails, unused blocks,
     the slot the new token will be written to) is poisoned with NaN (float
     caches) or the e4m3 NaN code 0x7F (fp8 caches), so a read of it shows up;
-  * fp8 caches: per (block, kv_head) tile, scale = amax|x| / 448 in fp32 (1.0
-    for an all-zero tile) over the tile's history tokens, code =
-    round-to-nearest-even(x / scale) clamped to +-448, done by torch's
-    float8_e4m3fn cast; the new token's K/V are drawn in the query dtype and
-    quantised on write, with its block's existing scale, by the step itself.
+  * 8-bit caches: per (block, kv_head) tile, scale = amax|x| / QMAX in fp32
+    (1.0 for an all-zero tile; QMAX 448 for fp8 e4m3, 127 for int8) over the
+    tile's history tokens, code = round-to-nearest-even(x / scale) clamped to
+    +-QMAX, done by torch (float8_e4m3fn cast, or round then int8); poisoned
+    slots hold 0x7F (fp8 NaN) or -128 (the unused int8 code); the new token's
+    K/V are drawn in the query dtype and quantised on write, with its block's
+    existing scale, by the step itself;
+  * K outlier channels (k_outliers > 0): in each KV head that many channels,
+    chosen at random, are 16x larger, in the history and in the new token
+    alike; K then has per-channel factors c[h][d] (16 on those channels, 1
+    elsewhere) that every K value is divided by before quantising.
 """
 
 from __future__ import annotations
@@ -33,14 +39,20 @@ from .pool import BlockPool
 from .specs import DecodeWorkload
 
 POISON_FP8_CODE = 0x7F
+POISON_INT8_CODE = -128
 FP8_MAX = 448.0
+INT8_MAX = 127.0
+OUTLIER_GAIN = 16.0
 
 _TORCH_DTYPE = {
     "f32": torch.float32,
     "f16": torch.float16,
     "bf16": torch.bfloat16,
     "fp8_e4m3": torch.uint8,
+    "int8": torch.int8,
 }
+_QMAX = {"fp8_e4m3": FP8_MAX, "int8": INT8_MAX}
+_POISON = {"fp8_e4m3": POISON_FP8_CODE, "int8": POISON_INT8_CODE}
 
 
 def torch_dtype(tag: str) -> torch.dtype:
@@ -150,20 +162,38 @@ def build_layout(spec: DecodeWorkload) -> DecodeLayout:
 # tensors
 # ---------------------------------------------------------------------------
 
-def fp8_quantize_blocks(x: torch.Tensor, valid: Optional[torch.Tensor] = None):
-    """x: fp32 [NB, H, bs, D] -> (codes uint8 same shape, scales fp32 [NB, H]).
+def quantize_blocks(x: torch.Tensor, valid: Optional[torch.Tensor] = None, code: str = "fp8_e4m3"):
+    """x: fp32 [NB, H, bs, D] -> (codes same shape, scales fp32 [NB, H]).
 
-    The scale of each (block, head) tile is its amax over valid slots / 448.
+    The scale of each (block, head) tile is its amax over valid slots / QMAX;
+    codes are uint8 e4m3fn bits or int8 integers.
     """
+    qmax = _QMAX[code]
     if valid is not None:
         xm = x.masked_fill(~valid.view(valid.shape[0], 1, valid.shape[1], 1), 0.0)
     else:
         xm = x
     amax = xm.abs().amax(dim=(2, 3))
-    scales = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax)).to(torch.float32)
-    y = (x / scales[:, :, None, None]).clamp_(-FP8_MAX, FP8_MAX)
-    codes = y.to(torch.float8_e4m3fn).view(torch.uint8)
-    return codes, scales
+    scales = torch.where(amax > 0, amax / qmax, torch.ones_like(amax)).to(torch.float32)
+    y = (x / scales[:, :, None, None]).clamp_(-qmax, qmax)
+    if code == "fp8_e4m3":
+        return y.to(torch.float8_e4m3fn).view(torch.uint8), scales
+    return torch.round(y).to(torch.int8), scales          # round: halves to even
+
+
+def fp8_quantize_blocks(x: torch.Tensor, valid: Optional[torch.Tensor] = None):
+    return quantize_blocks(x, valid, "fp8_e4m3")
+
+
+def outlier_factors(spec: DecodeWorkload, device: str) -> Optional[torch.Tensor]:
+    """fp32 [Hkv, D]: OUTLIER_GAIN on spec.k_outliers seeded channels per head, else 1."""
+    if not spec.k_outliers:
+        return None
+    rng = np.random.default_rng(spec.seed + 7919)
+    c = np.ones((spec.num_kv_heads, spec.head_dim), np.float32)
+    for h in range(spec.num_kv_heads):
+        c[h, rng.choice(spec.head_dim, spec.k_outliers, replace=False)] = OUTLIER_GAIN
+    return torch.from_numpy(c).to(device)
 
 
 def _gen(device: str, seed: int) -> torch.Generator:
@@ -187,21 +217,24 @@ def _make_inputs(layout: DecodeLayout, device: str, layers: Optional[int]) -> Di
     gen = _gen(device, spec.seed)
     valid = torch.from_numpy(layout.history_mask).to(device)
     poison = ~valid.view(NB, 1, bs, 1)
-    kv_tag = spec.kv_dtype
-    cache_dtype = torch_dtype(kv_tag)
+    tags = {"k": spec.kv_dtype, "v": spec.v_tag}
+    chan = outlier_factors(spec, device)
     out: Dict[str, torch.Tensor] = {}
     out["q"] = _normal((nl, B, Hq, D), gen, device, spec.q_dtype)
-    k_cache = torch.empty((nl, NB, Hkv, bs, D), dtype=cache_dtype, device=device)
-    v_cache = torch.empty_like(k_cache)
+    k_cache = torch.empty((nl, NB, Hkv, bs, D), dtype=torch_dtype(tags["k"]), device=device)
+    v_cache = torch.empty((nl, NB, Hkv, bs, D), dtype=torch_dtype(tags["v"]), device=device)
     scales = {}
     for name, cache in (("k", k_cache), ("v", v_cache)):
-        if kv_tag == "fp8_e4m3":
+        tag = tags[name]
+        if tag in _QMAX:
             sc = torch.empty((nl, NB, Hkv), dtype=torch.float32, device=device)
             for layer in range(nl):
                 x = torch.randn((NB, Hkv, bs, D), generator=gen, device=device, dtype=torch.float32)
-                codes, s = fp8_quantize_blocks(x, valid)
+                # with outlier channels x is already K / c: the history's K is
+                # code * scale * c, its outliers carried by c
+                codes, s = quantize_blocks(x, valid, tag)
                 del x
-                codes.masked_fill_(poison, POISON_FP8_CODE)
+                codes.masked_fill_(poison, _POISON[tag])
                 cache[layer].copy_(codes)
                 sc[layer].copy_(s)
                 del codes
@@ -213,14 +246,18 @@ def _make_inputs(layout: DecodeLayout, device: str, layers: Optional[int]) -> Di
                 del x
                 cache[layer].masked_fill_(poison, float("nan"))
     out["k_cache"], out["v_cache"] = k_cache, v_cache
-    if kv_tag == "fp8_e4m3":
+    if spec.quantised:
         out["k_scales"], out["v_scales"] = scales["k"], scales["v"]
+    if chan is not None:
+        out["k_channel_scales"] = chan
     if spec.append:
-        # fp8 caches quantise the new token on write; its K/V arrive in the
+        # 8-bit caches quantise the new token on write; its K/V arrive in the
         # query's dtype
-        src_tag = spec.q_dtype if kv_tag == "fp8_e4m3" else kv_tag
+        src_tag = spec.q_dtype if spec.quantised else spec.kv_dtype
         out["k_new"] = _normal((nl, B, Hkv, D), gen, device, src_tag)
         out["v_new"] = _normal((nl, B, Hkv, D), gen, device, src_tag)
+        if chan is not None:
+            out["k_new"] = (out["k_new"].float() * chan).to(out["k_new"].dtype)
         out["slot_mapping"] = torch.from_numpy(layout.slot_mapping).to(device)
     out["block_tables"] = torch.from_numpy(layout.block_tables).to(device)
     out["context_lens"] = torch.from_numpy(layout.context_lens).to(device)

@@ -21,7 +21,7 @@ class DecodeWorkload:
     num_q_heads: int
     num_kv_heads: int
     head_dim: int
-    kv_dtype: str            # "f32" | "f16" | "bf16" | "fp8_e4m3"
+    kv_dtype: str            # K's (and by default V's): "f32" | "f16" | "bf16" | "fp8_e4m3" | "int8"
     q_dtype: str             # "f32" | "f16" | "bf16"
     out_dtype: str           # "f32" | "f16" | "bf16"
     # Length mix: either explicit lengths, or uniform integers in [lo, hi].
@@ -35,6 +35,19 @@ class DecodeWorkload:
     append: bool = True
     block_size: int = 16
     description: str = ""
+    # V's format when it differs from K's (8-bit caches only)
+    v_dtype: Optional[str] = None
+    # Outlier channels per KV head in K (x16); > 0 also gives K per-channel
+    # factors equal to each channel's magnitude
+    k_outliers: int = 0
+
+    @property
+    def v_tag(self) -> str:
+        return self.v_dtype or self.kv_dtype
+
+    @property
+    def quantised(self) -> bool:
+        return self.kv_dtype in ("fp8_e4m3", "int8")
 
     @property
     def group(self) -> int:
@@ -80,6 +93,21 @@ WORKLOADS = {
         kv_dtype="fp8_e4m3", q_dtype="bf16", out_dtype="bf16",
         len_range=(131072, 131072), append=True,
         description="long-context FP8 e4m3 KV, GQA-4, B=8 x 131072, bf16 q/out, split + merge",
+    ),
+    "long_fp8k_int8v": DecodeWorkload(
+        name="long_fp8k_int8v", seed=56005, num_layers=1, num_seqs=8,
+        num_q_heads=32, num_kv_heads=8, head_dim=128,
+        kv_dtype="fp8_e4m3", v_dtype="int8", q_dtype="bf16", out_dtype="bf16",
+        len_range=(131072, 131072), append=True,
+        description="long-context mixed KV: K fp8 e4m3, V int8, GQA-4, B=8 x 131072, bf16 q/out",
+    ),
+    "long_int8_kchan": DecodeWorkload(
+        name="long_int8_kchan", seed=56006, num_layers=1, num_seqs=8,
+        num_q_heads=32, num_kv_heads=8, head_dim=128,
+        kv_dtype="int8", q_dtype="bf16", out_dtype="bf16",
+        len_range=(131072, 131072), append=True, k_outliers=4,
+        description="long-context int8 KV, 4 outlier K channels per head with per-channel K "
+                    "factors, GQA-4, B=8 x 131072, bf16 q/out",
     ),
 }
 
