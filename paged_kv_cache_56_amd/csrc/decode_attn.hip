@@ -10,7 +10,7 @@
 // byte is used by only g query heads.  The kernel therefore streams each
 // (block, kv_head) tile once from HBM and makes that one read serve all g
 // query heads.  Scores use packed dot2 for f16/bf16 K (and for fp8 or int8
-// K after widening it to f16, both exact; the query is held in f16 after a
+// K after widening it to f16, both exact -- int8 by SDWA converts; the query is held in f16 after a
 // power-of-two rescale of the KV group that the scores undo), fp32 FMA for
 // fp32 K.  P.V accumulates in fp32: for f16, fp8 and int8 V it is a dot2
 // over pairs of tokens with the probabilities rounded once to f16 (relative
@@ -145,21 +145,39 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// Query element idx times K's channel factor (8-bit K only; `chan` may be
-// NULL: no factors).
-template <KV QT>
-__device__ __forceinline__ float q_elem(const void* qrow, const float* chan, int idx) {
-  const float x = load_elem_f32<QT>(qrow, idx);
-  return chan ? x * chan[idx] : x;
+// The lane's slice of one query row as fp32: elements (v * LPT + c) * E + e
+// for v < VPT, e < E (E consecutive elements per v, read 16 bytes at a time).
+template <KV QT, int EL, int LPT, int E, int VPT>
+__device__ __forceinline__ void q_slice_f32(const void* qrow, int c, float (&f)[EL]) {
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    const int e0 = (v * LPT + c) * E;
+    if constexpr (QT == KV::F32) {
+#pragma unroll
+      for (int u = 0; u < E / 4; ++u) {
+        const float4 x = *(const float4*)((const float*)qrow + e0 + 4 * u);
+        f[v * E + 4 * u + 0] = x.x; f[v * E + 4 * u + 1] = x.y;
+        f[v * E + 4 * u + 2] = x.z; f[v * E + 4 * u + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < E / 8; ++u) {
+        const uint4 x = *(const uint4*)((const uint16_t*)qrow + e0 + 8 * u);
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          f[v * E + 8 * u + 2 * k] = QT == KV::F16 ? f16lo(w[k]) : bf16lo(w[k]);
+          f[v * E + 8 * u + 2 * k + 1] = QT == KV::F16 ? f16hi(w[k]) : bf16hi(w[k]);
+        }
+      }
+    }
+  }
 }
 
-// q row (already offset to the lane's head) -> the lane's slice.  For 8-bit K
-// the query (times K's channel factors) is held in f16 after a power-of-two
-// rescale `qexp` (applied here, undone on the scores), chosen per KV group
-// so its largest element is in [2^14, 2^15).
+// q row (already offset to the lane's head) -> the lane's slice, for f16,
+// bf16 and fp32 K (the query is read as stored).
 template <KV KT, KV QT, int EL, int LPT, int E, int VPT>
-__device__ __forceinline__ void load_q(QSlice<KT, EL>& qs, const void* qrow, const float* chan,
-                                       int c, int qexp) {
+__device__ __forceinline__ void load_q(QSlice<KT, EL>& qs, const void* qrow, int c) {
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
     const int e0 = (v * LPT + c) * E;
@@ -167,27 +185,22 @@ __device__ __forceinline__ void load_q(QSlice<KT, EL>& qs, const void* qrow, con
       static_assert(QT == KT, "16-bit caches take a query of the same type");
       const uint4 x = *(const uint4*)((const uint16_t*)qrow + e0);
       qs.w[v * 4 + 0] = x.x; qs.w[v * 4 + 1] = x.y; qs.w[v * 4 + 2] = x.z; qs.w[v * 4 + 3] = x.w;
-    } else if constexpr (KT == KV::F32) {
+    } else {
+      static_assert(KT == KV::F32, "8-bit K packs its query with q8_pack");
 #pragma unroll
       for (int e = 0; e < E; ++e) qs.f[v * E + e] = load_elem_f32<QT>(qrow, e0 + e);
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; e += 2)
-        qs.w[(v * E + e) / 2] = pack_f16x2(__builtin_ldexpf(q_elem<QT>(qrow, chan, e0 + e), qexp),
-                                           __builtin_ldexpf(q_elem<QT>(qrow, chan, e0 + e + 1), qexp));
     }
   }
 }
 
-// Largest |q * c| of the lane's slice (8-bit K only, before packing).
-template <KV QT, int EL, int LPT, int E, int VPT>
-__device__ __forceinline__ float slice_absmax(const void* qrow, const float* chan, int c) {
-  float m = 0.f;
+// 8-bit K: the slice times K's channel factors `cf`, rescaled by 2^qexp and
+// packed into f16 pairs.
+template <KV KT, int EL>
+__device__ __forceinline__ void q8_pack(QSlice<KT, EL>& qs, const float (&f)[EL], const float (&cf)[EL],
+                                        int qexp) {
 #pragma unroll
-  for (int v = 0; v < VPT; ++v)
-#pragma unroll
-    for (int e = 0; e < E; ++e) m = fmaxf(m, fabsf(q_elem<QT>(qrow, chan, (v * LPT + c) * E + e)));
-  return m;
+  for (int e = 0; e < EL; e += 2)
+    qs.w[e / 2] = pack_f16x2(__builtin_ldexpf(f[e] * cf[e], qexp), __builtin_ldexpf(f[e + 1] * cf[e + 1], qexp));
 }
 
 // K/V words of one token for one lane: VPT * 4 dwords.
@@ -238,14 +251,30 @@ __device__ __forceinline__ void fp8_to_f16_pairs(const TokWords<VPT>& t, uint32_
   }
 }
 
-// int8 -> f16, exactly: a byte u placed under the f16 exponent of 1024 reads
-// as 1024 + u; with the sign bit flipped first, u = x + 128, so subtracting
-// 1152 leaves x (all values involved are integers below 2048: exact).
-constexpr uint32_t kI8Bias = 0x64806480u;   // f16 0x6400 (1024) in each half, byte sign flip
-__device__ __forceinline__ uint32_t i8_biased_to_f16(uint32_t u) {
-  const half2_t b = {(_Float16)1152.0f, (_Float16)1152.0f};
-  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, u) - b);
+// int8 -> f16 pair, exactly (|x| <= 128 is an f16 integer): byte BL of `lo`
+// and byte BH of `hi`, each sign-extended and converted by one SDWA convert
+// that writes its half of the result (the second keeps the first's half).
+#define PKV_CVT_I8_LO(B)                                                            \
+  asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD "       \
+      "src0_sel:BYTE_" #B : "=v"(r) : "v"(lo))
+#define PKV_CVT_I8_HI(B)                                                            \
+  asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE "  \
+      "src0_sel:BYTE_" #B : "+v"(r) : "v"(hi))
+template <int BL, int BH>
+__device__ __forceinline__ uint32_t i8_pair_to_f16(uint32_t lo, uint32_t hi) {
+  uint32_t r;
+  if constexpr (BL == 0) PKV_CVT_I8_LO(0);
+  else if constexpr (BL == 1) PKV_CVT_I8_LO(1);
+  else if constexpr (BL == 2) PKV_CVT_I8_LO(2);
+  else PKV_CVT_I8_LO(3);
+  if constexpr (BH == 0) PKV_CVT_I8_HI(0);
+  else if constexpr (BH == 1) PKV_CVT_I8_HI(1);
+  else if constexpr (BH == 2) PKV_CVT_I8_HI(2);
+  else PKV_CVT_I8_HI(3);
+  return r;
 }
+#undef PKV_CVT_I8_LO
+#undef PKV_CVT_I8_HI
 
 // int8 token words -> f16 pairs of adjacent elements (same token): EL / 2 words.
 template <int EL, int VPT>
@@ -254,10 +283,8 @@ __device__ __forceinline__ void int8_to_f16_pairs(const TokWords<VPT>& t, uint32
   words_of(t, w);
 #pragma unroll
   for (int k = 0; k < 4 * VPT; ++k) {
-    // bytes x0..x3 -> halves (x0, x1) and (x2, x3), each byte under 0x64
-    const uint32_t x = w[k] ^ 0x80808080u;
-    h[2 * k] = i8_biased_to_f16(__builtin_amdgcn_perm(0x64646464u, x, 0x04010400u));
-    h[2 * k + 1] = i8_biased_to_f16(__builtin_amdgcn_perm(0x64646464u, x, 0x04030402u));
+    h[2 * k] = i8_pair_to_f16<0, 1>(w[k], w[k]);
+    h[2 * k + 1] = i8_pair_to_f16<2, 3>(w[k], w[k]);
   }
 }
 
@@ -309,13 +336,11 @@ __device__ __forceinline__ void v_token_pairs(const TokWords<VPT>& t0, const Tok
       vp[2 * k] = __builtin_amdgcn_perm(b[k], a[k], 0x05040100u);
       vp[2 * k + 1] = __builtin_amdgcn_perm(b[k], a[k], 0x07060302u);
     } else if constexpr (KT == KV::INT8) {
-      // word k holds int8 elements 4k..4k+3: element j of both tokens under
-      // the f16 bias, then unbias
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t sel = 0x0c000c00u | ((uint32_t)(4 + j) << 16) | (uint32_t)j;
-        vp[4 * k + j] = i8_biased_to_f16(__builtin_amdgcn_perm(b[k], a[k], sel) ^ kI8Bias);
-      }
+      // word k holds int8 elements 4k..4k+3: element j of both tokens
+      vp[4 * k + 0] = i8_pair_to_f16<0, 0>(a[k], b[k]);
+      vp[4 * k + 1] = i8_pair_to_f16<1, 1>(a[k], b[k]);
+      vp[4 * k + 2] = i8_pair_to_f16<2, 2>(a[k], b[k]);
+      vp[4 * k + 3] = i8_pair_to_f16<3, 3>(a[k], b[k]);
     } else {
       // word k holds fp8 elements 4k..4k+3: interleave bytes, then widen
       const uint32_t lo = __builtin_amdgcn_perm(b[k], a[k], 0x05010400u);
@@ -435,26 +460,44 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     return (QT == KV::F32) ? (const void*)((const float*)a.q + qoff)
                            : (const void*)((const uint16_t*)a.q + qoff);
   };
-  // 8-bit K: one power-of-two rescale for the whole KV group, from the
-  // largest |q * c| over all g heads (every lane of a row sees all of them,
-  // so every lane derives the same exponent), so the partial sums the rows
-  // combine agree.
-  const float* chan = (KQ && a.k_chan) ? a.k_chan + (int64_t)h * D : nullptr;
+  // 8-bit K: the query times K's channel factors (1 without them), with one
+  // power-of-two rescale for the whole KV group, from the largest |q * c|
+  // over all g heads (every lane of a row sees all of them, so every lane
+  // derives the same exponent), so the partial sums the rows combine agree.
+  QSlice<KT, EL> qs[G];
   int qexp = 0;
   if constexpr (KQ) {
+    float cf[EL];
+    if (a.k_chan) {
+      q_slice_f32<KV::F32, EL, LPT, E, VPT>(a.k_chan + (int64_t)h * D, c, cf);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EL; ++e) cf[e] = 1.0f;
+    }
     float m = 0.f;
 #pragma unroll
-    for (int hs = 0; hs < G; ++hs) m = fmaxf(m, slice_absmax<QT, EL, LPT, E, VPT>(qrow_of(hs), chan, c));
+    for (int hs = 0; hs < G; ++hs) {
+      float f[EL];
+      q_slice_f32<QT, EL, LPT, E, VPT>(qrow_of(hs), c, f);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) m = fmaxf(m, fabsf(f[e] * cf[e]));
+    }
     static_for<LEVELS>([&](auto l) { m = fmaxf(m, xlevel<4 - LEVELS + decltype(l)::value>(m)); });
     int ex;
     (void)__builtin_frexpf(m, &ex);             // m = f * 2^ex, f in [0.5, 1)
     qexp = m > 0.f ? 15 - ex : 0;               // largest element lands in [2^14, 2^15)
     qexp = qexp > 100 ? 100 : (qexp < -100 ? -100 : qexp);
+#pragma unroll
+    for (int hs = 0; hs < G; ++hs) {
+      float f[EL];
+      q_slice_f32<QT, EL, LPT, E, VPT>(qrow_of(hs), c, f);
+      q8_pack<KT, EL>(qs[hs], f, cf, qexp);
+    }
+  } else {
+#pragma unroll
+    for (int hs = 0; hs < G; ++hs) load_q<KT, QT, EL, LPT, E, VPT>(qs[hs], qrow_of(hs), c);
   }
   const float qfac = __builtin_ldexpf(1.0f, -qexp);   // undoes the rescale on the scores
-  QSlice<KT, EL> qs[G];
-#pragma unroll
-  for (int hs = 0; hs < G; ++hs) load_q<KT, QT, EL, LPT, E, VPT>(qs[hs], qrow_of(hs), chan, c, qexp);
 
   float acc[G][EL];
   float mref[G];
@@ -535,9 +578,11 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     float cs = a.scale;  // scale * log2(e), folded on the host
     float vsc = 1.f;
     if constexpr (KQ) {
+      // uniform index, read-only data: scalar loads, which do not wait
+      // behind the tile copies in flight (those count on vmcnt)
       const int64_t si = (int64_t)(blk_ok ? phys_raw : 0) * a.num_kv_heads + h;
-      cs *= a.k_scales[si];
-      vsc = a.v_scales[si];
+      cs *= ((const __attribute__((address_space(4))) float*)a.k_scales)[si];
+      vsc = ((const __attribute__((address_space(4))) float*)a.v_scales)[si];
     }
 
     // 1. partial scores: slot k = hs * TPL + i
