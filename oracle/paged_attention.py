@@ -24,7 +24,9 @@ What is computed, and where the pages state it:
   * [P1] section 5.3: with a sliding window of W, a position attends only to
     the most recent W tokens (itself included), optionally together with the
     first few tokens of the sequence (attention sinks), which [P1] 5.3 and
-    [P5] section 7 single out as tokens that must not be dropped.
+    [P5] section 7 single out as tokens that must not be dropped; [P5]
+    section 7 also keeps them in their original precision when the rest of
+    the cache is quantised (optional full-precision side tiles here).
 
 Test infrastructure only (see the package docstring).
 """
@@ -104,7 +106,9 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
                            seqs: Optional[Sequence[int]] = None,
                            q_heads: Optional[Sequence[int]] = None,
                            block_size: int = 16, window: int = 0, sinks: int = 0,
-                           v_tag: Optional[str] = None, k_channel_scales=None) -> np.ndarray:
+                           v_tag: Optional[str] = None, k_channel_scales=None,
+                           sink_k=None, sink_v=None, sink_blocks=None,
+                           sink_tag: Optional[str] = None) -> np.ndarray:
     """out[b, i, :] for b in `seqs`, i in `q_heads` (all by default), float64.
 
     q: [B, Hq, D] storage array; caches: [num_blocks, Hkv, block_size, D];
@@ -112,8 +116,19 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
     restrict the attended positions (see attended_positions).  v_tag (default
     kv_tag) is the V cache's format when it differs from K's;
     k_channel_scales ([Hkv, D]) multiplies K's channels.
+
+    Full-precision sinks ([P5] section 7: attention-sink tokens keep their
+    original precision, since their magnitudes would spoil a shared scale):
+    with sink_k/sink_v ([num_sink_tiles, Hkv, block_size, D] of sink_tag,
+    default q_tag) and sink_blocks ([B]), position p < `sinks` of sequence b
+    is read, as stored, from tile sink_blocks[b], offset p, instead of the
+    cache; the attended positions are unchanged.
     """
     v_tag = kv_tag if v_tag is None else v_tag
+    sink_tag = q_tag if sink_tag is None else sink_tag
+    side = sink_k is not None
+    if side and not (1 <= sinks <= block_size and sink_v is not None and sink_blocks is not None):
+        raise ValueError("full-precision sinks need 1 <= sinks <= block_size, both tiles and sink_blocks")
     B, Hq, D = q.shape
     Hkv = k_cache.shape[1]
     if Hq % Hkv:
@@ -131,9 +146,17 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
         pos = attended_positions(L, window, sinks)
         if len(pos) == 0:
             continue
+        if side:
+            first, pos = pos[pos < sinks], pos[pos >= sinks]
         K = gather_sequence(k_cache, block_tables[b], L, kv_tag, kv_needed, k_scales, block_size, pos,
                             k_channel_scales)
         V = gather_sequence(v_cache, block_tables[b], L, v_tag, kv_needed, v_scales, block_size, pos)
+        if side and len(first):
+            tile = int(sink_blocks[b])
+            sk = np.asarray(sink_k)[tile][kv_needed][:, first, :].transpose(1, 0, 2)   # [n, h, D]
+            sv = np.asarray(sink_v)[tile][kv_needed][:, first, :].transpose(1, 0, 2)
+            K = np.concatenate([stored_to_f64(sk, sink_tag), K])
+            V = np.concatenate([stored_to_f64(sv, sink_tag), V])
         for c, i in enumerate(q_heads):
             h = col[kv_for[c]]
             s = scale * (K[:, h, :] @ qv[r, c])          # [L] scores

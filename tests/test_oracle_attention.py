@@ -358,6 +358,9 @@ MUTANTS = {
                                    "vals = vals * c[kv_heads][None, :, ::-1]"),
     "v_read_in_k_format": ("V = gather_sequence(v_cache, block_tables[b], L, v_tag,",
                            "V = gather_sequence(v_cache, block_tables[b], L, kv_tag,"),
+    "side_sinks_ignored": ("        if side and len(first):", "        if False:"),
+    "side_sink_offset": ("[kv_needed][:, first, :].transpose(1, 0, 2)   # [n, h, D]",
+                         "[kv_needed][:, first[::-1], :].transpose(1, 0, 2)   # [n, h, D]"),
     "query_head_index": ("qv = stored_to_f64(np.asarray(q)[seqs][:, q_heads], q_tag)",
                          "qv = stored_to_f64(np.asarray(q)[seqs][:, q_heads][:, ::-1], q_tag)"),
 }
@@ -427,11 +430,51 @@ def test_mixed_precision_pin():
     _mixed_pin(oracle)
 
 
+def _side_sink_pin(mod):
+    """int8 cache with the first S positions of each sequence in f16 side
+    tiles: the dense reference takes positions < S from the tile, as stored,
+    and the rest from the int8 cache, with and without a window."""
+    rng = np.random.default_rng(10)
+    lens = [3, 16, 40]
+    Hkv, D, S = 2, 8, 5
+    codes_k = [rng.integers(-127, 128, size=(L, Hkv, D)).astype(np.int8) for L in lens]
+    codes_v = [rng.integers(-127, 128, size=(L, Hkv, D)).astype(np.int8) for L in lens]
+    kc, vc, t, Ls = paged_from_contiguous(codes_k, codes_v, 8, seed=19, storage=np.int8, fill=-128)
+    ks = rng.uniform(0.01, 0.1, size=(8, Hkv)).astype(np.float32)
+    vs = rng.uniform(0.01, 0.1, size=(8, Hkv)).astype(np.float32)
+    tiles = (rng.standard_normal((2, 5, Hkv, BS, D)) * 8).astype(np.float16)     # K, V side tiles
+    sink_blocks = np.array([4, 0, 2])
+    q = rng.standard_normal((3, 4, D)).astype(np.float16)
+    for window in (0, 12):
+        got = mod.paged_decode_attention(q, kc, vc, t, Ls, 0.3, q_tag="f16", kv_tag="int8",
+                                         k_scales=ks, v_scales=vs, window=window, sinks=S,
+                                         sink_k=tiles[0], sink_v=tiles[1], sink_blocks=sink_blocks)
+        sk_d, sv_d = [], []
+        for b, L in enumerate(lens):
+            keep = [p for p in range(L) if window == 0 or p >= L - window or p < S]
+            kd = np.zeros((len(keep), Hkv, D)); vd = np.zeros_like(kd)
+            for r, pos in enumerate(keep):
+                blk = t[b][pos // BS]
+                if pos < S:
+                    kd[r] = tiles[0][sink_blocks[b], :, pos, :].astype(np.float64)
+                    vd[r] = tiles[1][sink_blocks[b], :, pos, :].astype(np.float64)
+                else:
+                    kd[r] = codes_k[b][pos].astype(np.float64) * ks[blk][:, None]
+                    vd[r] = codes_v[b][pos].astype(np.float64) * vs[blk][:, None]
+            sk_d.append(kd); sv_d.append(vd)
+        ref = sdpa_reference(q.astype(np.float64), sk_d, sv_d, 0.3)
+        np.testing.assert_allclose(got, ref, atol=1e-12)
+
+
+def test_full_precision_sink_pin():
+    _side_sink_pin(oracle)
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(name):
     mod = _mutant_module(name)
     caught = []
-    for pin in PINS + [_fp8_pin, _mixed_pin]:
+    for pin in PINS + [_fp8_pin, _mixed_pin, _side_sink_pin]:
         try:
             pin(mod)
         except (AssertionError, IndexError, ValueError, TypeError):
