@@ -66,14 +66,20 @@ def attention_bytes(spec, lay, window: int = 0, sinks: int = 0):
     counting shared blocks once per sequence)."""
     L = lay.context_lens.astype(int)
     per_token = spec.num_kv_heads * spec.head_dim * (ELT[spec.kv_dtype] + ELT[spec.v_tag])
+    side_token = spec.num_kv_heads * spec.head_dim * 2 * ELT[spec.q_dtype]   # full-precision sinks
+    S = spec.fp_sinks
     logical = 0
+    side = 0
     used = {}                        # physical block -> attended token offsets
     for b in range(spec.num_seqs):
-        pos = attended(int(L[b]), window, sinks)
+        pos = attended(int(L[b]), window, S or sinks)
         logical += len(pos) * per_token
         for p in pos:
+            if p < S:
+                side += side_token
+                continue
             used.setdefault(int(lay.block_tables[b, p // 16]), set()).add(p % 16)
-    kv = sum(len(v) for v in used.values()) * per_token
+    kv = sum(len(v) for v in used.values()) * per_token + side
     nblk = np.array([len({p // 16 for p in attended(int(l), window, sinks)}) for l in L])
     q = spec.num_seqs * spec.num_q_heads * spec.head_dim * ELT[spec.q_dtype]
     out = spec.num_seqs * spec.num_q_heads * spec.head_dim * ELT[spec.out_dtype]
@@ -117,6 +123,11 @@ def cpu_baseline(spec, lay, x, budget_s: float):
                 kw = dict(k_scales=host(x["k_scales"][layer].index_select(0, idx)),
                           v_scales=host(x["v_scales"][layer].index_select(0, idx)))
             chan = host(x["k_channel_scales"]) if "k_channel_scales" in x else None
+            if spec.fp_sinks:
+                tile = int(x["sink_tiles_of_seq"][b])
+                kw.update(sink_k=host(x["sink_k"][layer][tile:tile + 1]),
+                          sink_v=host(x["sink_v"][layer][tile:tile + 1]),
+                          sink_blocks=np.zeros(1, np.int64), sinks=spec.fp_sinks)
             t0 = time.perf_counter()
             if spec.append:
                 s = int(lay.slot_mapping[b])
@@ -334,12 +345,17 @@ def traffic_for(workload: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=0,
+                    help="timed steps (default: enough for >= 200 attention launches, at least 10)")
+    ap.add_argument("--warmup", type=int, default=-1,
+                    help="untimed steps first (default: enough for >= 100 launches, at least 3); "
+                         "the GPU needs a few dozen launches to reach its steady clocks")
     ap.add_argument("--workload", default="llama70b_f16_80l")
     ap.add_argument("--partition-blocks", type=int, default=0)
     ap.add_argument("--window", type=int, default=0, help="sliding window W (0 = whole context)")
     ap.add_argument("--sinks", type=int, default=0, help="attention-sink tokens kept with a window")
+    ap.add_argument("--fp-sinks", type=int, default=0,
+                    help="8-bit workloads: keep this many leading tokens in full-precision side tiles")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="0 skips the CPU baseline")
     ap.add_argument("--copy-pairs", type=int, default=0,
                     help="also time copy-on-write copies of this many random block pairs")
@@ -364,7 +380,7 @@ def main():
     import torch
 
     import paged_kv_cache_56_amd as pkv
-    from workloads import WORKLOADS, build_layout, make_device_inputs
+    from workloads import WORKLOADS, build_layout, make_device_inputs, scaled
 
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a GPU")
@@ -372,6 +388,13 @@ def main():
     torch.cuda.set_device(dev)
     pkv.load_library()
     spec = WORKLOADS[args.workload]
+    if args.warmup < 0:
+        args.warmup = max(3, -(-100 // spec.num_layers))
+    if args.steps <= 0:
+        args.steps = max(10, -(-200 // spec.num_layers))
+    if args.fp_sinks:
+        spec = scaled(spec, fp_sinks=args.fp_sinks)
+        args.sinks = args.fp_sinks
     lay = build_layout(spec)
     log(f"[bench] {spec.description}: generating inputs on the device")
     x = make_device_inputs(lay, "cuda")
@@ -380,12 +403,12 @@ def main():
     odt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[spec.out_dtype]
     outs = torch.empty((nl, spec.num_seqs, spec.num_q_heads, spec.head_dim), dtype=odt, device=dev)
     dims = pkv.decode_dims(x["q"][0], x["k_cache"][0], x["block_tables"], outs[0], args.partition_blocks,
-                           args.window, args.sinks)
+                           args.window, args.sinks, bool(spec.fp_sinks))
     nparts = pkv.decode_num_partitions(dims)
     ws_bytes = pkv.decode_workspace_bytes(dims)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     chan = x.get("k_channel_scales")
-    both_fp8 = spec.kv_dtype == spec.v_tag == "fp8_e4m3" and chan is None
+    both_fp8 = spec.kv_dtype == spec.v_tag == "fp8_e4m3" and chan is None and not spec.fp_sinks
 
     def step(ev=None):
         for layer in range(nl):
@@ -395,6 +418,12 @@ def main():
                 kw = dict(k_scales=x["k_scales"][layer], v_scales=x["v_scales"][layer])
                 if chan is not None:
                     kw["k_channel_scales"] = chan
+            if spec.fp_sinks:
+                kw.update(sink_k=x["sink_k"][layer], sink_v=x["sink_v"][layer],
+                          sink_tiles_of_seq=x["sink_tiles_of_seq"])
+                if spec.append:
+                    pkv.kv_append(x["k_new"][layer], x["v_new"][layer], x["sink_slot_mapping"],
+                                  x["sink_k"][layer], x["sink_v"][layer])
             if spec.append and both_fp8:
                 pkv.kv_append_fp8(x["k_new"][layer], x["v_new"][layer], x["slot_mapping"], kc, vc,
                                   kw["k_scales"], kw["v_scales"])
@@ -478,7 +507,8 @@ def main():
             "block_size": 16,
             "partitions": nparts,
             "window": args.window,
-            "sinks": args.sinks if args.window > 0 else 0,
+            "sinks": args.sinks if (args.window > 0 or spec.fp_sinks) else 0,
+            "fp_sinks": spec.fp_sinks,
             "kv_bytes_per_step": kv_bytes * nl,
             "logical_kv_bytes_per_step": logical_bytes * nl,
         },

@@ -55,7 +55,7 @@ extern "C" {
 #define PKV_API
 #endif
 
-#define PKV_VERSION 110  /* 1.1.0 */
+#define PKV_VERSION 120  /* 1.2.0 */
 #define PKV_BLOCK_SIZE 16
 
 typedef enum {
@@ -94,6 +94,9 @@ typedef struct {
   int32_t window;              /* sliding window W: attend only the last W positions
                                   (0 = the whole context) */
   int32_t sinks;               /* with W > 0, also attend the first `sinks` positions */
+  int32_t sink_tiles;          /* 1: positions < sinks come from full-precision side tiles
+                                  (pkv_paged_decode_attn_quant only; 1 <= sinks <= 16,
+                                  with or without a window); 0: from the cache */
 } pkv_decode_dims;
 
 /*
@@ -203,24 +206,44 @@ PKV_API int pkv_paged_decode_attn_fp8(const void* q, const void* k_cache, const 
                               float scale, void* out, const pkv_decode_dims* dims,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Arguments of the 8-bit decode entry point beyond those of the others. */
+typedef struct {
+  const float* k_scales;          /* fp32 [num_blocks][num_kv_heads], required */
+  const float* v_scales;          /* fp32 [num_blocks][num_kv_heads], required */
+  const float* k_channel_scales;  /* fp32 [num_kv_heads][head_dim], or NULL */
+  int32_t v_dtype;                /* V's pkv_dtype (dims->kv_dtype is K's) */
+  /* With dims->sink_tiles = 1: full-precision sink tiles, q's dtype,
+   * [num_sink_tiles][num_kv_heads][16][head_dim]; sequence b's position
+   * p < dims->sinks is read from tile sink_tiles_of_seq[b], offset p
+   * (write it there with pkv_kv_append).  A tile id outside
+   * [0, num_sink_tiles) leaves that sequence without sink tokens. */
+  const void* k_sink;
+  const void* v_sink;
+  const int32_t* sink_tiles_of_seq;  /* int32 [num_seqs] */
+  int32_t num_sink_tiles;
+} pkv_quant_params;
+
 /*
- * 8-bit variant with mixed formats and per-channel K factors ("The KV Cache
- * memory ledger" 7: K in FP8 with V in INT8; "KV Cache from first
- * principles" 5.2: per-channel factors for K's outlier channels).
- * dims->kv_dtype is K's format and v_dtype V's: (FP8_E4M3, FP8_E4M3) with
+ * 8-bit variant with mixed formats, per-channel K factors and full-precision
+ * sink tokens ("The KV Cache memory ledger" 7: K in FP8 with V in INT8, and
+ * attention-sink tokens kept at their original precision; "KV Cache from
+ * first principles" 5.2: per-channel factors for K's outlier channels).
+ * dims->kv_dtype is K's format and p->v_dtype V's: (FP8_E4M3, FP8_E4M3) with
  * the q/out pairs of pkv_paged_decode_attn_fp8, or (FP8_E4M3, INT8) and
  * (INT8, INT8) with q and out both F16 or both BF16.  A cached K element is
  * decode(code) * k_scales[block][h] * k_channel_scales[h][d] (the last factor
  * 1 when k_channel_scales is NULL), a V element decode(code) *
- * v_scales[block][h]; int8 codes decode to their integer value.
+ * v_scales[block][h]; int8 codes decode to their integer value.  With
+ * dims->sink_tiles = 1 the first dims->sinks positions are read as stored
+ * from the side tiles (see pkv_quant_params); the attended positions are
+ * those of pkv_paged_decode_attn, and the call always splits the context
+ * (pkv_decode_workspace_bytes > 0).
  */
 PKV_API int pkv_paged_decode_attn_quant(const void* q, const void* k_cache, const void* v_cache,
-                                        const float* k_scales, const float* v_scales,
-                                        const float* k_channel_scales, int32_t v_dtype,
-                                        const int32_t* block_tables, const int32_t* context_lens,
-                                        float scale, void* out, const pkv_decode_dims* dims,
-                                        void* workspace, size_t workspace_bytes,
-                                        hipStream_t stream);
+                                        const pkv_quant_params* p, const int32_t* block_tables,
+                                        const int32_t* context_lens, float scale, void* out,
+                                        const pkv_decode_dims* dims, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Bandwidth reference ("KV Cache from first principles" 4.1: decode time is

@@ -11,6 +11,7 @@ carry device memory and streams.
     kv_append_quant(x_new, slot_mapping, cache, scales, channel_scales=None)
     paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, scale, out,
                       k_scales=None, v_scales=None, k_channel_scales=None,
+                      sink_k=None, sink_v=None, sink_tiles_of_seq=None,
                       workspace=None, partition_blocks=0, window=0, sinks=0)
 """
 
@@ -76,6 +77,20 @@ class DecodeDims(ctypes.Structure):
         ("partition_blocks", ctypes.c_int32),
         ("window", ctypes.c_int32),
         ("sinks", ctypes.c_int32),
+        ("sink_tiles", ctypes.c_int32),
+    ]
+
+
+class QuantParams(ctypes.Structure):
+    _fields_ = [
+        ("k_scales", ctypes.c_void_p),
+        ("v_scales", ctypes.c_void_p),
+        ("k_channel_scales", ctypes.c_void_p),
+        ("v_dtype", ctypes.c_int32),
+        ("k_sink", ctypes.c_void_p),
+        ("v_sink", ctypes.c_void_p),
+        ("sink_tiles_of_seq", ctypes.c_void_p),
+        ("num_sink_tiles", ctypes.c_int32),
     ]
 
 
@@ -113,8 +128,8 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_paged_decode_attn_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
                                               dims_p, vp, sz, vp]
     lib.pkv_paged_decode_attn_fp8.restype = ctypes.c_int
-    lib.pkv_paged_decode_attn_quant.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, ctypes.c_float, vp,
-                                                dims_p, vp, sz, vp]
+    lib.pkv_paged_decode_attn_quant.argtypes = [vp, vp, vp, ctypes.POINTER(QuantParams), vp, vp,
+                                                ctypes.c_float, vp, dims_p, vp, sz, vp]
     lib.pkv_paged_decode_attn_quant.restype = ctypes.c_int
     lib.pkv_hbm_read_probe.argtypes = [vp, sz, vp, i32, vp]
     lib.pkv_hbm_read_probe.restype = ctypes.c_int
@@ -340,12 +355,12 @@ class BlockManager:
 
 def decode_dims(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor,
                 out: torch.Tensor, partition_blocks: int = 0, window: int = 0,
-                sinks: int = 0) -> DecodeDims:
+                sinks: int = 0, sink_tiles: bool = False) -> DecodeDims:
     B, Hq, D = q.shape
     NB, Hkv, bs, Dk = k_cache.shape
     _need(Dk == D, "head_dim of q and cache differ")
     return DecodeDims(B, Hq, Hkv, D, bs, NB, block_tables.shape[1], _code(q), _code(k_cache),
-                      _code(out), partition_blocks, window, sinks)
+                      _code(out), partition_blocks, window, sinks, int(sink_tiles))
 
 
 def decode_workspace_bytes(dims: DecodeDims) -> int:
@@ -371,6 +386,8 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       out: torch.Tensor, *, k_scales: Optional[torch.Tensor] = None,
                       v_scales: Optional[torch.Tensor] = None,
                       k_channel_scales: Optional[torch.Tensor] = None,
+                      sink_k: Optional[torch.Tensor] = None, sink_v: Optional[torch.Tensor] = None,
+                      sink_tiles_of_seq: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None,
                       partition_blocks: int = 0, window: int = 0, sinks: int = 0) -> torch.Tensor:
     """out[b, i] = softmax(scale * q[b, i] . K^T) V over the first context_lens[b]
@@ -379,13 +396,16 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     q, out: [B, Hq, D]; caches: [NB, Hkv, 16, D]; block_tables: int32 [B, max_blocks];
     context_lens: int32 [B].  8-bit caches -- fp8 (uint8 or float8_e4m3fn) or
     int8, K fp8 with V int8 allowed -- need k_scales and v_scales: fp32 [NB, Hkv],
-    and may give k_channel_scales: fp32 [Hkv, D] for K.  `workspace` (uint8, on the device) is allocated here
+    and may give k_channel_scales: fp32 [Hkv, D] for K, and full-precision sink
+    tiles sink_k, sink_v: [num_tiles, Hkv, 16, D] of q's dtype with
+    sink_tiles_of_seq: int32 [B] (positions < sinks of sequence b are read from
+    its tile; 1 <= sinks <= 16, with or without a window).  `workspace` (uint8, on the device) is allocated here
     when the call splits the context and none is given.  window > 0 limits each
     query to the last `window` positions plus the first `sinks` positions.
     """
     lib = load_library()
     _dev(q, k_cache, v_cache, block_tables, context_lens, out, k_scales, v_scales, k_channel_scales,
-         workspace)
+         sink_k, sink_v, sink_tiles_of_seq, workspace)
     _need(q.dim() == 3 and out.shape == q.shape, "q and out must be [B, Hq, D]")
     _need(k_cache.shape == v_cache.shape and k_cache.dim() == 4, "caches must be [NB, Hkv, 16, D]")
     kc, vc = _code(k_cache), _code(v_cache)
@@ -394,7 +414,15 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
           and block_tables.shape[0] == q.shape[0], "block_tables must be int32 [B, max_blocks]")
     _need(context_lens.dtype == torch.int32 and context_lens.shape == (q.shape[0],),
           "context_lens must be int32 [B]")
-    dims = decode_dims(q, k_cache, block_tables, out, partition_blocks, window, sinks)
+    side = sink_k is not None or sink_v is not None or sink_tiles_of_seq is not None
+    if side:
+        _need(sink_k is not None and sink_v is not None and sink_tiles_of_seq is not None,
+              "full-precision sinks need sink_k, sink_v and sink_tiles_of_seq")
+        _need(sink_k.shape == sink_v.shape and sink_k.dim() == 4 and sink_k.shape[1:] == k_cache.shape[1:]
+              and sink_k.dtype == sink_v.dtype == q.dtype, "sink tiles must be [n, Hkv, 16, D] of q's dtype")
+        _need(sink_tiles_of_seq.dtype == torch.int32 and sink_tiles_of_seq.shape == (q.shape[0],),
+              "sink_tiles_of_seq must be int32 [B]")
+    dims = decode_dims(q, k_cache, block_tables, out, partition_blocks, window, sinks, side)
     need = decode_workspace_bytes(dims)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -407,20 +435,22 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         _need(k_channel_scales is None or (k_channel_scales.dtype == torch.float32 and
                                            k_channel_scales.shape == (k_cache.shape[1], k_cache.shape[3])),
               "k_channel_scales must be fp32 [Hkv, D]")
-        if kc == vc == 3 and k_channel_scales is None:
+        if kc == vc == 3 and k_channel_scales is None and not side:
             st = lib.pkv_paged_decode_attn_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales),
                                                _ptr(v_scales), _ptr(block_tables), _ptr(context_lens),
                                                float(scale), _ptr(out), ctypes.byref(dims), ws_ptr,
                                                ws_bytes, _stream(q))
         else:
-            st = lib.pkv_paged_decode_attn_quant(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales),
-                                                 _ptr(v_scales), _ptr(k_channel_scales), vc,
+            qp = QuantParams(_ptr(k_scales), _ptr(v_scales), _ptr(k_channel_scales), vc,
+                             _ptr(sink_k), _ptr(sink_v), _ptr(sink_tiles_of_seq),
+                             sink_k.shape[0] if side else 0)
+            st = lib.pkv_paged_decode_attn_quant(_ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(qp),
                                                  _ptr(block_tables), _ptr(context_lens), float(scale),
                                                  _ptr(out), ctypes.byref(dims), ws_ptr, ws_bytes,
                                                  _stream(q))
     else:
-        _need(k_scales is None and v_scales is None and k_channel_scales is None,
-              "scales apply to 8-bit caches only")
+        _need(k_scales is None and v_scales is None and k_channel_scales is None and not side,
+              "scales and sink tiles apply to 8-bit caches only")
         st = lib.pkv_paged_decode_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                        _ptr(context_lens), float(scale), _ptr(out),
                                        ctypes.byref(dims), ws_ptr, ws_bytes, _stream(q))

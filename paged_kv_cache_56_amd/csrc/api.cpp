@@ -26,6 +26,8 @@ int check_dims(const pkv_decode_dims* d) {
       d->num_blocks <= 0 || d->max_blocks_per_seq <= 0 || d->partition_blocks < 0 ||
       d->window < 0 || d->sinks < 0)
     return PKV_ERR_SHAPE;
+  if (d->sink_tiles != 0 && d->sink_tiles != 1) return PKV_ERR_SHAPE;
+  if (d->sink_tiles && (d->sinks < 1 || d->sinks > PKV_BLOCK_SIZE)) return PKV_ERR_SHAPE;
   if (d->block_size != PKV_BLOCK_SIZE) return PKV_ERR_SHAPE;
   if (d->num_q_heads % d->num_kv_heads) return PKV_ERR_SHAPE;
   const int g = d->num_q_heads / d->num_kv_heads;
@@ -59,14 +61,22 @@ int check_dtypes(const pkv_decode_dims* d, int v_dtype) {
   return PKV_OK;
 }
 
-int decode_common(const void* q, const void* k_cache, const void* v_cache, const float* k_scales,
-                  const float* v_scales, const float* k_chan, const int32_t* block_tables,
-                  const int32_t* context_lens, float scale, void* out, const pkv_decode_dims* dims,
-                  void* workspace, size_t workspace_bytes, hipStream_t stream, int v_dtype) {
+// qp: the 8-bit arguments (NULL for the f32/f16/bf16 entry point).
+int decode_common(const void* q, const void* k_cache, const void* v_cache, const pkv_quant_params* qp,
+                  const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
+                  const pkv_decode_dims* dims, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
   int st = check_dims(dims);
   if (st) return st;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
-  if (v_dtype >= 0 && (!k_scales || !v_scales)) return PKV_ERR_NULL;
+  if (qp && (!qp->k_scales || !qp->v_scales)) return PKV_ERR_NULL;
+  if (dims->sink_tiles) {
+    if (!qp) return PKV_ERR_SHAPE;            // side tiles exist for 8-bit caches only
+    if (!qp->k_sink || !qp->v_sink || !qp->sink_tiles_of_seq) return PKV_ERR_NULL;
+    if (qp->num_sink_tiles <= 0) return PKV_ERR_SHAPE;
+  }
+  const int v_dtype = qp ? qp->v_dtype : -1;
+  if (qp && !is_q8(v_dtype)) return PKV_ERR_DTYPE;
   st = check_dtypes(dims, v_dtype);
   if (st) return st;
   if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
@@ -79,14 +89,15 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
-  a.k_scales = k_scales;
-  a.v_scales = v_scales;
-  a.k_chan = k_chan;
+  a.k_scales = qp ? qp->k_scales : nullptr;
+  a.v_scales = qp ? qp->v_scales : nullptr;
+  a.k_chan = qp ? qp->k_channel_scales : nullptr;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.scale = scale * 1.4426950408889634f;  // scores are kept in log2 units
   a.out = out;
   const size_t rows = (size_t)dims->num_seqs * dims->num_q_heads;
+  a.split = need ? 1 : 0;
   a.o_part = need ? (float*)workspace : nullptr;
   a.ml_part = need ? (float*)workspace + rows * np * dims->head_dim : nullptr;
   a.num_seqs = dims->num_seqs;
@@ -98,7 +109,14 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
   a.part_blocks = pb;
   a.num_parts = np;
   a.window = dims->window;
-  a.sinks = dims->window > 0 ? dims->sinks : 0;
+  a.sinks = (dims->window > 0 || dims->sink_tiles) ? dims->sinks : 0;
+  a.sink_tiles = dims->sink_tiles;
+  if (dims->sink_tiles) {
+    a.sink_k = qp->k_sink;
+    a.sink_v = qp->v_sink;
+    a.sink_of_seq = qp->sink_tiles_of_seq;
+    a.num_sink_tiles = qp->num_sink_tiles;
+  }
   a.q_dtype = dims->q_dtype;
   a.kv_dtype = dims->kv_dtype;
   a.v_dtype = v_dtype >= 0 ? v_dtype : dims->kv_dtype;
@@ -203,8 +221,8 @@ int pkv_paged_decode_attn(const void* q, const void* k_cache, const void* v_cach
                           const int32_t* block_tables, const int32_t* context_lens, float scale,
                           void* out, const pkv_decode_dims* dims, void* workspace,
                           size_t workspace_bytes, hipStream_t stream) {
-  return decode_common(q, k_cache, v_cache, nullptr, nullptr, nullptr, block_tables, context_lens,
-                       scale, out, dims, workspace, workspace_bytes, stream, -1);
+  return decode_common(q, k_cache, v_cache, nullptr, block_tables, context_lens, scale, out, dims,
+                       workspace, workspace_bytes, stream);
 }
 
 int pkv_paged_decode_attn_fp8(const void* q, const void* k_cache, const void* v_cache,
@@ -212,19 +230,23 @@ int pkv_paged_decode_attn_fp8(const void* q, const void* k_cache, const void* v_
                               const int32_t* block_tables, const int32_t* context_lens,
                               float scale, void* out, const pkv_decode_dims* dims,
                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return decode_common(q, k_cache, v_cache, k_scales, v_scales, nullptr, block_tables, context_lens,
-                       scale, out, dims, workspace, workspace_bytes, stream, PKV_FP8_E4M3);
+  if (dims && dims->sink_tiles) return PKV_ERR_SHAPE;   // side tiles: the _quant entry point
+  pkv_quant_params qp{};
+  qp.k_scales = k_scales;
+  qp.v_scales = v_scales;
+  qp.v_dtype = PKV_FP8_E4M3;
+  return decode_common(q, k_cache, v_cache, &qp, block_tables, context_lens, scale, out, dims,
+                       workspace, workspace_bytes, stream);
 }
 
 int pkv_paged_decode_attn_quant(const void* q, const void* k_cache, const void* v_cache,
-                                const float* k_scales, const float* v_scales,
-                                const float* k_channel_scales, int32_t v_dtype,
-                                const int32_t* block_tables, const int32_t* context_lens,
-                                float scale, void* out, const pkv_decode_dims* dims,
-                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!is_q8(v_dtype)) return PKV_ERR_DTYPE;
-  return decode_common(q, k_cache, v_cache, k_scales, v_scales, k_channel_scales, block_tables,
-                       context_lens, scale, out, dims, workspace, workspace_bytes, stream, v_dtype);
+                                const pkv_quant_params* p, const int32_t* block_tables,
+                                const int32_t* context_lens, float scale, void* out,
+                                const pkv_decode_dims* dims, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  if (!p) return PKV_ERR_NULL;
+  return decode_common(q, k_cache, v_cache, p, block_tables, context_lens, scale, out, dims,
+                       workspace, workspace_bytes, stream);
 }
 
 int pkv_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t sink_words,

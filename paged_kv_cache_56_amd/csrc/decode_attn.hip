@@ -365,21 +365,28 @@ __device__ __forceinline__ float exp2_safe_factor(float m_old, float m_new) {
   return m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_old - m_new);
 }
 
-// The blocks one sequence's query attends, as a compressed list: with a
-// sliding window of W and S sink tokens ("KV Cache from first principles"
-// 5.3) they are the sink blocks [0, nsb) then the window blocks [wb0, nblk);
-// without a window, or when the two ranges touch, simply [0, nblk).
-// Position pos of block j is attended iff pos < L and (no window, or
-// pos < se, or pos >= ws).
+// The blocks one sequence's query attends in the cache, as a compressed
+// list: with a sliding window of W and S sink tokens ("KV Cache from first
+// principles" 5.3) they are the sink blocks [0, nsb) then the window blocks
+// [wb0, nblk); without a window, or when the two ranges touch, simply
+// [0, nblk).  Position pos of block j is attended iff pos < L and (no
+// window, or pos < se, or pos >= ws).  With full-precision sink tiles
+// (`skip` = S > 0) the sinks are attended elsewhere: the cache serves only
+// positions >= S (and inside the window).
 struct SeqSpan {
   int L, nblk, natt, nsb, wb0, se, ws;
   bool windowed;
-  __device__ __forceinline__ SeqSpan(int len, int max_blocks, int window, int sinks) {
+  __device__ __forceinline__ SeqSpan(int len, int max_blocks, int window, int sinks, int skip) {
     L = len < 0 ? 0 : (len > max_blocks * 16 ? max_blocks * 16 : len);
     nblk = (L + 15) >> 4;
     windowed = window > 0 && L > window;
     ws = windowed ? L - window : 0;
     se = windowed ? min(sinks, L) : 0;
+    if (skip > 0) {                      // sinks come from their own tiles
+      se = 0;
+      ws = max(ws, min(skip, L));
+      windowed = ws > 0;
+    }
     if (se >= ws) windowed = false;      // sinks reach the window: everything
     nsb = 0;
     wb0 = 0;
@@ -432,12 +439,12 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int Hq = a.num_kv_heads * G;
 
-  const SeqSpan span(a.context_lens[b], a.max_blocks, a.window, a.sinks);
+  const SeqSpan span(a.context_lens[b], a.max_blocks, a.window, a.sinks, a.sink_tiles ? a.sinks : 0);
   // this partition: entries [j0, j1) of the sequence's attended-block list
   const int j0 = p * a.part_blocks;
   const int j1 = min(j0 + a.part_blocks, span.natt);
   if (j0 >= j1) {
-    if (a.num_parts == 1) {
+    if (!a.split) {
       for (int idx = tid; idx < G * D; idx += 256)
         store_out<OT>(a.out, ((int64_t)b * Hq + h * G) * D + idx, 0.f);
     }
@@ -800,7 +807,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     }
     const float res = lsum > 0.f ? o / lsum : 0.f;
     const int64_t row = (int64_t)b * Hq + h * G + ha;
-    if (a.num_parts == 1) {
+    if (!a.split) {
       store_out<OT>(a.out, row * D + d, res);
     } else {
       a.o_part[(row * a.num_parts + p) * D + d] = res;
@@ -815,23 +822,66 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
 // Log-sum-exp merge of the partitions of one (sequence, query head) row.
 // Partition p carries o_p (its normalised output), m_p (log2 reference) and
 // l_p (sum of exp2(s - m_p)); out = sum_p l_p 2^(m_p - M) o_p / sum_p l_p 2^(m_p - M).
-template <KV OT, int D>
+// Only the partitions the cache pass wrote are read (the sequence's own
+// count).
+//
+// Full-precision sink tokens ("The KV Cache memory ledger" 7: attention-sink
+// tokens keep their original precision when the rest is quantised) join
+// here as one more term: the first min(S, L) positions of the sequence,
+// read as stored (q's dtype) from its side tile, attended with an online
+// softmax over at most 16 tokens (lane l holds elements l + 64k).
+template <KV QT, KV OT, int D>
 __global__ void __launch_bounds__(64) lse_merge_kernel(DecodeArgs a) {
+  constexpr int PER = D / 64;
   const int row = blockIdx.x;
   const int b = row / a.num_q_heads;
   const int lane = threadIdx.x;
-  const SeqSpan span(a.context_lens[b], a.max_blocks, a.window, a.sinks);
+  const SeqSpan span(a.context_lens[b], a.max_blocks, a.window, a.sinks, a.sink_tiles ? a.sinks : 0);
   const int np = min((span.natt + a.part_blocks - 1) / a.part_blocks, a.num_parts);
   const float* ml = a.ml_part + (int64_t)row * a.num_parts * 2;
   const float* op = a.o_part + (int64_t)row * a.num_parts * D;
-  float m = -INFINITY;
+
+  float ms = -INFINITY, ls = 0.f, os[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) os[k] = 0.f;
+  if (a.sink_tiles) {
+    const int tile = a.sink_of_seq[b];
+    const int n = ((unsigned)tile < (unsigned)a.num_sink_tiles) ? min(a.sinks, span.L) : 0;
+    const int h = (row % a.num_q_heads) / (a.num_q_heads / a.num_kv_heads);
+    const int64_t tbase = ((int64_t)(n > 0 ? tile : 0) * a.num_kv_heads + h) * 16 * D;
+    float qv[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) qv[k] = load_elem_f32<QT>(a.q, (int64_t)row * D + k * 64 + lane);
+    for (int t = 0; t < n; ++t) {
+      float part = 0.f;
+#pragma unroll
+      for (int k = 0; k < PER; ++k)
+        part = __builtin_fmaf(qv[k], load_elem_f32<QT>(a.sink_k, tbase + t * D + k * 64 + lane), part);
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) part += __shfl_xor(part, d);
+      const float s = part * a.scale;                   // log2 units, same on every lane
+      const float mnew = fmaxf(ms, s);
+      const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - mnew);
+      const float w = __builtin_amdgcn_exp2f(s - mnew);
+      ls = __builtin_fmaf(ls, f, w);
+#pragma unroll
+      for (int k = 0; k < PER; ++k)
+        os[k] = __builtin_fmaf(os[k], f, w * load_elem_f32<QT>(a.sink_v, tbase + t * D + k * 64 + lane));
+      ms = mnew;
+    }
+  }
+
+  float m = ls > 0.f ? ms : -INFINITY;
   for (int p = 0; p < np; ++p)
     if (ml[2 * p + 1] > 0.f) m = fmaxf(m, ml[2 * p]);
-  constexpr int PER = D / 64;
   float o[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) o[k] = 0.f;
   float wsum = 0.f;
+  {
+    const float f = ls > 0.f ? __builtin_amdgcn_exp2f(ms - m) : 0.f;   // the sink term, unnormalised
+    wsum = ls * f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) o[k] = os[k] * f;
+  }
   for (int p = 0; p < np; ++p) {
     const float lp = ml[2 * p + 1];
     if (!(lp > 0.f)) continue;
@@ -876,7 +926,7 @@ void plan_partitions(const pkv_decode_dims& d, int* part_blocks, int* num_parts)
 size_t workspace_bytes_for(const pkv_decode_dims& d) {
   int pb, np;
   plan_partitions(d, &pb, &np);
-  if (np <= 1) return 0;
+  if (np <= 1 && !d.sink_tiles) return 0;    // sink tiles are merged in: always split
   return (size_t)d.num_seqs * d.num_q_heads * np * (d.head_dim + 2) * sizeof(float);
 }
 
@@ -885,8 +935,8 @@ static int launch_typed(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
   hipLaunchKernelGGL((decode_partition_kernel<KT, VT, QT, OT, D, G>), grid, dim3(256), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return PKV_ERR_LAUNCH;
-  if (a.num_parts > 1) {
-    hipLaunchKernelGGL((lse_merge_kernel<OT, D>), dim3(a.num_seqs * a.num_q_heads), dim3(64), 0,
+  if (a.split) {
+    hipLaunchKernelGGL((lse_merge_kernel<QT, OT, D>), dim3(a.num_seqs * a.num_q_heads), dim3(64), 0,
                        stream, a);
     if (hipGetLastError() != hipSuccess) return PKV_ERR_LAUNCH;
   }

@@ -39,11 +39,20 @@ struct DecodeArgs {
   const int32_t* context_lens;
   float scale;
   void* out;
-  float* o_part;           // [B*Hq][P][D] when P > 1
-  float* ml_part;          // [B*Hq][P][2] when P > 1
+  float* o_part;           // [B*Hq][num_parts][D] when split
+  float* ml_part;          // [B*Hq][num_parts][2] when split
   int num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks;
   int part_blocks, num_parts;
+  int split;               // partial results go to the workspace (then merged)
   int window, sinks;       // sliding window (0 = off) and attention-sink tokens
+  // full-precision sink tiles (q's dtype, [num_sink_tiles][Hkv][16][D]); when
+  // set, positions < sinks are attended from them by the merge kernel and
+  // the cache pass skips them
+  const void* sink_k;
+  const void* sink_v;
+  const int32_t* sink_of_seq;
+  int num_sink_tiles;
+  int sink_tiles;
   int q_dtype, kv_dtype, v_dtype, out_dtype;   // kv_dtype is K's
 };
 

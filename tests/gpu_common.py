@@ -42,6 +42,13 @@ def run_step(x, layer: int, spec, out: torch.Tensor, partition_blocks: int = 0,
         kw = dict(k_scales=x["k_scales"][layer], v_scales=x["v_scales"][layer])
         if chan is not None:
             kw["k_channel_scales"] = chan
+    if spec.fp_sinks:
+        kw.update(sink_k=x["sink_k"][layer], sink_v=x["sink_v"][layer],
+                  sink_tiles_of_seq=x["sink_tiles_of_seq"])
+        sinks = spec.fp_sinks
+        if spec.append and append:      # a new token among the first S goes to its tile
+            pkv.kv_append(x["k_new"][layer], x["v_new"][layer], x["sink_slot_mapping"],
+                          x["sink_k"][layer], x["sink_v"][layer])
     if spec.append and append:
         if spec.kv_dtype == spec.v_tag == "fp8_e4m3" and chan is None:
             pkv.kv_append_fp8(x["k_new"][layer], x["v_new"][layer], x["slot_mapping"], kc, vc,
@@ -64,11 +71,25 @@ def oracle_rows(x_host_layer, layout, spec, seqs=None, q_heads=None, window=0, s
     k_new, v_new (if appending), k_scales, v_scales (8-bit), k_channel_scales.
     """
     kc, vc, ks, vs = oracle_append(x_host_layer, spec, layout.slot_mapping)
+    return oracle_attend(x_host_layer, spec, kc, vc, ks, vs, layout.block_tables, layout.context_lens,
+                         seqs=seqs, q_heads=q_heads, window=window, sinks=sinks)
+
+
+def oracle_attend(h, spec, kc, vc, ks, vs, tables, lens, seqs=None, q_heads=None, window=0, sinks=0):
+    """The oracle's attention on one layer's (appended) host copies."""
+    side = {}
+    if spec.fp_sinks:
+        sk, sv = h["sink_k"], h["sink_v"]
+        if spec.append:
+            sk = oracle.kv_append_bits(sk, h["k_new"], h["sink_slot_mapping"])
+            sv = oracle.kv_append_bits(sv, h["v_new"], h["sink_slot_mapping"])
+        side = dict(sink_k=sk, sink_v=sv, sink_blocks=h["sink_tiles_of_seq"])
+        sinks = spec.fp_sinks
     return oracle.paged_decode_attention(
-        x_host_layer["q"], kc, vc, layout.block_tables, layout.context_lens, spec.scale,
+        h["q"], kc, vc, tables, lens, spec.scale,
         q_tag=spec.q_dtype, kv_tag=spec.kv_dtype, v_tag=spec.v_tag, k_scales=ks, v_scales=vs,
-        k_channel_scales=x_host_layer.get("k_channel_scales"),
-        seqs=seqs, q_heads=q_heads, window=window, sinks=sinks)
+        k_channel_scales=h.get("k_channel_scales"),
+        seqs=seqs, q_heads=q_heads, window=window, sinks=sinks, **side)
 
 
 def oracle_append(h, spec, slot_mapping):
@@ -98,11 +119,32 @@ def host_layer(x, layer: int):
             h[k] = host_storage(x[k][layer])
     if "k_channel_scales" in x:
         h["k_channel_scales"] = host_storage(x["k_channel_scales"])
+    if "sink_k" in x:
+        h["sink_k"] = host_storage(x["sink_k"][layer])
+        h["sink_v"] = host_storage(x["sink_v"][layer])
+        h["sink_tiles_of_seq"] = host_storage(x["sink_tiles_of_seq"])
+        if "sink_slot_mapping" in x:
+            h["sink_slot_mapping"] = host_storage(x["sink_slot_mapping"])
     return h
 
 
 def out_f64(out: torch.Tensor) -> np.ndarray:
     return out.detach().float().cpu().numpy().astype(np.float64)
+
+
+def half_ulp(ref: np.ndarray, tag: str) -> np.ndarray:
+    """Half a unit in the last place of the output type at |ref|: the one
+    rounding of the result to that type, which no kernel can avoid."""
+    mant = {"f32": 23, "f16": 10, "bf16": 7}[tag]
+    e = np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126)))
+    return np.ldexp(0.5, (e - mant).astype(int))
+
+
+def err_beyond_rounding(got: np.ndarray, ref: np.ndarray, tag: str) -> float:
+    """max |got - ref| after discounting the final rounding to the output type."""
+    if not got.size:
+        return 0.0
+    return float(np.max(np.abs(got - ref) - half_ulp(ref, tag)))
 
 
 def max_err(a: np.ndarray, b: np.ndarray) -> float:

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
     lib = pkv.load_library()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pkv_version() == 110
+    assert lib.pkv_version() == 120
 
 
 def _dims(**kw):
@@ -96,11 +96,12 @@ def test_fp8_status_codes():
     assert _attn_fp8(_dims(**dict(ok, out_dtype=1))) == -3        # bf16 q, f16 out
 
 
-def _attn_quant(dims, v_dtype, ks=FAKE, vs=FAKE, q=FAKE):
+def _attn_quant(dims, v_dtype, ks=FAKE, vs=FAKE, q=FAKE, sink=None, ntiles=0, params=True):
     lib = pkv.load_library()
-    return lib.pkv_paged_decode_attn_quant(q, FAKE, FAKE, ks, vs, None, v_dtype, FAKE, FAKE,
-                                           ctypes.c_float(0.088), FAKE, ctypes.byref(dims), None, 0,
-                                           None)
+    qp = pkv.QuantParams(ks and ks.value, vs and vs.value, None, v_dtype, sink, sink, sink, ntiles)
+    return lib.pkv_paged_decode_attn_quant(q, FAKE, FAKE, ctypes.byref(qp) if params else None, FAKE,
+                                           FAKE, ctypes.c_float(0.088), FAKE, ctypes.byref(dims), None,
+                                           0, None)
 
 
 def test_quant_status_codes():
@@ -116,9 +117,27 @@ def test_quant_status_codes():
     assert _attn_quant(_dims(**dict(ok, kv_dtype=4)), 4, vs=None) == -1
     assert _attn_quant(_dims(**dict(ok, kv_dtype=4)), 4, q=None) == -1
     assert _attn_quant(_dims(**dict(ok, kv_dtype=4, head_dim=96)), 4) == -2
+    assert _attn_quant(_dims(**dict(ok, kv_dtype=4)), 4, params=False) == -1
     # int8 through the other entry points
     assert _attn(_dims(kv_dtype=4, q_dtype=4, out_dtype=4)) == -3
     assert _attn_fp8(_dims(kv_dtype=4, q_dtype=2, out_dtype=2)) == -3
+
+
+def test_sink_tile_status_codes_and_workspace():
+    ok = dict(kv_dtype=4, q_dtype=2, out_dtype=2, num_q_heads=32, max_blocks_per_seq=16, sinks=4,
+              sink_tiles=1)
+    assert _attn_quant(_dims(**ok), 4) == -1                          # tiles missing
+    assert _attn_quant(_dims(**ok), 4, sink=FAKE.value, ntiles=0) == -2
+    assert _attn_quant(_dims(**dict(ok, sinks=0)), 4, sink=FAKE.value, ntiles=3) == -2
+    assert _attn_quant(_dims(**dict(ok, sinks=17)), 4, sink=FAKE.value, ntiles=3) == -2
+    assert _attn_quant(_dims(**dict(ok, sink_tiles=2)), 4, sink=FAKE.value, ntiles=3) == -2
+    assert _attn(_dims(sinks=4, sink_tiles=1)) == -2                  # not on the 16-bit entry
+    assert _attn_fp8(_dims(**dict(ok, kv_dtype=3))) == -2             # nor on the fp8 one
+    # always split (the merge kernel attends the sink tiles), even when P = 1
+    d = _dims(**ok)
+    assert pkv.decode_num_partitions(d) == 1
+    assert pkv.decode_workspace_bytes(d) == 64 * 32 * 1 * (128 + 2) * 4
+    assert _attn_quant(d, 4, sink=FAKE.value, ntiles=3) == -4        # no workspace given
 
 
 def test_append_quant_status_codes():

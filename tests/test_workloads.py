@@ -158,3 +158,27 @@ def test_mixed_and_int8_recipes():
     codes, s = quantize_blocks(torch.tensor([0.5, 1.5, 2.5, -0.5, 127.0]).view(1, 1, 1, 5),
                                code="int8")
     assert s.item() == 1.0 and codes.flatten().tolist() == [0, 2, 2, 0, 127]
+
+
+def test_full_precision_sink_recipe():
+    """Side tiles hold positions < S in q's dtype (x4 draws), the rest of each
+    tile is NaN, and the cache slots of those positions are poisoned."""
+    w = scaled(WORKLOADS["long_fp8k_int8v"], num_seqs=3, len_range=(3, 40), fp_sinks=5, num_layers=2)
+    lay = build_layout(w)
+    x = make_host_inputs(lay)
+    S = 5
+    order = x["sink_tiles_of_seq"].numpy()
+    assert sorted(order.tolist()) == [0, 1, 2]
+    for layer in range(2):
+        for b in range(3):
+            t = x["sink_k"][layer][order[b]].float().numpy()          # [Hkv, 16, D]
+            assert np.isfinite(t[:, :S]).all() and np.isnan(t[:, S:]).all()
+            assert np.abs(t[:, :S]).std() > 2
+            for pos, slot in enumerate(lay.seq_slots[b][:S]):
+                slot = int(slot)
+                assert (x["k_cache"][layer][slot // 16, :, slot % 16] == POISON_FP8_CODE).all()
+                assert (x["v_cache"][layer][slot // 16, :, slot % 16] == POISON_INT8_CODE).all()
+    pos = lay.context_lens - 1
+    side = x["sink_slot_mapping"].numpy()
+    for b in range(3):
+        assert side[b] == (order[b] * 16 + pos[b] if pos[b] < S else -1)

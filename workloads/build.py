@@ -24,7 +24,13 @@ Recipe (all seeded from the workload's seed):
   * K outlier channels (k_outliers > 0): in each KV head that many channels,
     chosen at random, are 16x larger, in the history and in the new token
     alike; K then has per-channel factors c[h][d] (16 on those channels, 1
-    elsewhere) that every K value is divided by before quantising.
+    elsewhere) that every K value is divided by before quantising;
+  * full-precision sinks (fp_sinks = S > 0): sequence b's first S positions
+    live in side tile sink_tiles_of_seq[b] (a seeded permutation of the B
+    tiles), in q's dtype, drawn N(0, 1) x 8 (sink tokens stand apart in
+    magnitude); the rest of each tile, and the cache slots of those
+    positions, are poisoned; a new token at a position < S goes to its tile
+    (sink_slot_mapping = tile * 16 + position, else -1).
 """
 
 from __future__ import annotations
@@ -250,6 +256,31 @@ def _make_inputs(layout: DecodeLayout, device: str, layers: Optional[int]) -> Di
         out["k_scales"], out["v_scales"] = scales["k"], scales["v"]
     if chan is not None:
         out["k_channel_scales"] = chan
+    if spec.fp_sinks:
+        S = spec.fp_sinks
+        if not (spec.quantised and 1 <= S <= bs):
+            raise ValueError("full-precision sinks need an 8-bit cache and 1..16 positions")
+        order = torch.from_numpy(np.random.default_rng(spec.seed + 104729).permutation(B).astype(np.int32))
+        qdt = torch_dtype(spec.q_dtype)
+        tiles = {}
+        for name in ("k", "v"):
+            t = torch.full((nl, B, Hkv, bs, D), float("nan"), dtype=qdt, device=device)
+            for layer in range(nl):
+                x = torch.randn((B, Hkv, S, D), generator=gen, device=device, dtype=torch.float32) * 4
+                t[layer][order.to(device).long(), :, :S, :] = x.to(qdt)
+            tiles[name] = t
+        out["sink_k"], out["sink_v"] = tiles["k"], tiles["v"]
+        out["sink_tiles_of_seq"] = order.to(device)
+        # the cache never serves these positions: poison them there
+        for b in range(B):
+            for slot in layout.seq_slots[b][:S]:
+                slot = int(slot)
+                for name, cache in (("k", k_cache), ("v", v_cache)):
+                    cache[:, slot // bs, :, slot % bs, :] = _POISON[tags[name]]
+        if spec.append:
+            pos = layout.context_lens.astype(np.int64) - 1
+            side = np.where(pos < S, order.numpy().astype(np.int64) * bs + pos, -1)
+            out["sink_slot_mapping"] = torch.from_numpy(side).to(device)
     if spec.append:
         # 8-bit caches quantise the new token on write; its K/V arrive in the
         # query's dtype

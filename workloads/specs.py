@@ -40,6 +40,9 @@ class DecodeWorkload:
     # Outlier channels per KV head in K (x16); > 0 also gives K per-channel
     # factors equal to each channel's magnitude
     k_outliers: int = 0
+    # 8-bit caches: the first this-many positions (<= 16) of every sequence
+    # live in full-precision side tiles (q's dtype) instead of the cache
+    fp_sinks: int = 0
 
     @property
     def v_tag(self) -> str:
