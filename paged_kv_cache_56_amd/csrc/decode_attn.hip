@@ -24,8 +24,9 @@
 //
 // Work split.  Grid = (partition p, kv head h, sequence b); a workgroup of
 // four waves owns the blocks [p*PB, (p+1)*PB) of (b, h); wave w takes every
-// fourth of them.  Tiles are copied by LDS DMA into a per-wave ring, each
-// copy reading 1 KiB contiguously.  Inside a wave, lane l then takes token
+// fourth of them.  K tiles are copied by LDS DMA into a per-wave ring, each
+// copy reading 1 KiB contiguously; V tiles are loaded straight into
+// registers (see "Staging" below).  Inside a wave, lane l then takes token
 // rows of group r = l / LPT of every tile and the 16-byte column c = l % LPT,
 // and keeps its slice of all g query vectors in registers for the whole
 // partition.
@@ -83,21 +84,13 @@ struct Cfg {
   static constexpr int NW = 4;                             // waves per workgroup
   static constexpr int LPB = TPL * VPT;                    // 16-byte loads per lane per tile
   static constexpr int TILE_B = 16 * D * EB;               // bytes of one (block, kv_head) tile
-  // Per-wave rings of staged tiles in LDS: NK K tiles and NV V tiles
-  // (NK >= NV: K is needed first).  About 16 KiB per wave: two 4-wave
-  // workgroups per CU; 20 KiB (NK = 3) measured no faster.
-#ifndef PKV_LDS_WAVE_B
-#define PKV_LDS_WAVE_B 16384
-#endif
-  static constexpr int TILES = PKV_LDS_WAVE_B / TILE_B;
-  static constexpr int NV = (TILES / 2) >= 2 ? (TILES / 2) : 2;
-  static constexpr int NK = (TILES - NV) >= NV ? (TILES - NV) : NV;
-  static constexpr int WAVE_RING_B = (NK + NV) * TILE_B;
-  static constexpr int RING_B = NW * WAVE_RING_B;
+  // K tiles are staged in LDS, two slots per wave (deeper rings measured
+  // slower); V tiles go straight to registers.
+  static constexpr int KR = 2;
+  static constexpr int KRING_B = NW * KR * TILE_B;
   static constexpr int RED_B = NW * G * (D + 2) * 4;       // end-of-partition combine
-  static constexpr int SMEM_B = RING_B > RED_B ? RING_B : RED_B;
+  static constexpr int SMEM_B = KRING_B > RED_B ? KRING_B : RED_B;
   static_assert(LPB * 64 * 16 == TILE_B, "a tile is LPB wave-wide 16-byte loads");
-  static_assert(2 * LPB * (NV - 1) <= 63, "vmcnt range");
   static_assert(LPT >= 1 && LPT <= 16 && (LPT & (LPT - 1)) == 0, "lanes per token");
   static_assert(TPL >= 1, "tokens per lane");
 };
@@ -526,9 +519,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
   const __attribute__((address_space(4))) int32_t* table =
       (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)b * a.max_blocks);
 
-  constexpr int LPB = C::LPB, NK = C::NK, NV = C::NV, TILE_B = C::TILE_B;
-  const uint32_t kring = lds_offset(smem) + (uint32_t)(w * C::WAVE_RING_B);
-  const uint32_t vring = kring + (uint32_t)(NK * TILE_B);
+  constexpr int LPB = C::LPB, KR = C::KR, TILE_B = C::TILE_B;
   // Copy n of a tile moves token rows n / VPT * R .. + R - 1, 16-byte column
   // (n % VPT) * LPT + c, in lane order: every copy reads 1 KiB contiguously.
   uint32_t dma_off[LPB];
@@ -537,47 +528,14 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
       dma_off[i * VPT + v] = (uint32_t)(((i * R + r) * D + (v * LPT + c) * E) * C::EB);
-  auto tile_of = [&](int j) {
+  auto tile_of = [&](int j) __attribute__((always_inline)) {
     int phys = table[span.logical(j)];
     phys = ((unsigned)phys < (unsigned)a.num_blocks) ? phys : 0;
     return ((int64_t)phys * a.num_kv_heads + h) * (int64_t)TILE_B;
   };
-  // Start copying block j's K tile into K slot `sk`, or its V tile into V slot `sv`.
-  auto issue_k = [&](int j, int sk) {
-    const char* src = kbase + tile_of(j);
-    const uint32_t dst = kring + (uint32_t)(sk * TILE_B);
-#pragma unroll
-    for (int n = 0; n < LPB; ++n) lds_dma16(src, dma_off[n], dst + n * 1024);
-  };
-  auto issue_v = [&](int j, int sv) {
-    const char* src = vbase + tile_of(j);
-    const uint32_t dst = vring + (uint32_t)(sv * TILE_B);
-#pragma unroll
-    for (int n = 0; n < LPB; ++n) lds_dma16(src, dma_off[n], dst + n * 1024);
-  };
-  // Registers <- slots: register token i reads the copy of row group
-  // (i ^ tmask) at the lane's own position (conflict-free LDS reads).
-  auto read_slots = [&](int sk, int sv, TokWords<VPT> (&kr)[TPL], TokWords<VPT> (&vr)[TPL]) {
-    const char* ks = smem + w * C::WAVE_RING_B + sk * TILE_B + lane * 16;
-    const char* vs = smem + w * C::WAVE_RING_B + (NK + sv) * TILE_B + lane * 16;
-#pragma unroll
-    for (int i = 0; i < TPL; ++i)
-#pragma unroll
-      for (int v = 0; v < VPT; ++v) {
-        const int n = (i ^ tmask) * VPT + v;
-        kr[i].x[v] = *(const uint4*)(ks + n * 1024);
-        vr[i].x[v] = *(const uint4*)(vs + n * 1024);
-      }
-  };
-  // Wait until at most `tiles` tile copies (of LPB loads each) are in flight.
-  auto wait_tiles = [&](int tiles) {
-    static_for<2 * NV - 1>([&](auto u) {
-      constexpr int c2 = 2 * NV - 2 - decltype(u)::value;   // tries 2NV-2 down to 0
-      if (tiles == c2) wait_vmcnt<c2 * LPB>();
-    });
-  };
-
-  auto compute_block = [&](int j, const TokWords<VPT> (&kr)[TPL], const TokWords<VPT> (&vr)[TPL]) {
+  // vr is consumed: tokens outside the sequence (or window) are zeroed in it.
+  auto compute_block = [&](int j, const TokWords<VPT> (&kr)[TPL], TokWords<VPT> (&vr)[TPL])
+                           __attribute__((always_inline)) {
     const int jl = span.logical(j);
     const int phys_raw = table[jl];
     const bool blk_ok = (unsigned)phys_raw < (unsigned)a.num_blocks;
@@ -620,9 +578,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     for (int k = 0; k < NF; ++k) s[k] *= cs;
 
     // 3. mask the tail (and a block id outside the pool)
-    TokWords<VPT> vv[TPL];
-#pragma unroll
-    for (int i = 0; i < TPL; ++i) vv[i] = vr[i];
+    TokWords<VPT> (&vv)[TPL] = vr;
     if (vbits != 0xFFFFu) {
 #pragma unroll
       for (int k = 0; k < NF; ++k) {
@@ -714,30 +670,79 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     }
   };
 
-  // Pipeline: the wave's blocks are j0 + w, j0 + w + NW, ... (index t).  K of
-  // block t + NK and V of block t + NV are copied while block t is computed.
-  // Copies complete in issue order, so block t is ready once no more than the
-  // copies issued after V(t) -- K(t+NK-NV+1 .. t+NK-1), V(t+1 .. t+NV-1) --
-  // are outstanding.
+  // Staging.  K tiles go through a two-slot per-wave LDS ring by LDS DMA; V
+  // tiles go straight to registers.  The LDS DMA path alone tops out near
+  // 6.0 TB/s on this chip while plain 16-byte loads reach ~6.7, and splitting
+  // the stream between the two paths reaches the latter.  Block t + 1's K
+  // copy and V loads are in flight while block t is computed.  The V loads
+  // are ordinary loads, so the compiler knows when their registers are
+  // valid; the one wait per block is a waitcnt it can see (vmcnt(0), which
+  // also covers the K copies it cannot see), so it places no waits of its
+  // own on V(t) behind the newer loads.  V's register slot (i, v) is token
+  // row ((i ^ tmask) * R + r), the order the reduce-scatter's mirrored masks
+  // ask for.
+  uint32_t roff[TPL][VPT];
+#pragma unroll
+  for (int i = 0; i < TPL; ++i)
+#pragma unroll
+    for (int v = 0; v < VPT; ++v)
+      roff[i][v] = (uint32_t)((((i ^ tmask) * R + r) * D + (v * LPT + c) * E) * C::EB);
+  auto issue_vregs = [&](int j, TokWords<VPT> (&vr)[TPL]) __attribute__((always_inline)) {
+    const char* src = vbase + tile_of(j);
+#pragma unroll
+    for (int i = 0; i < TPL; ++i)
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) vr[i].x[v] = *(const uint4*)(src + roff[i][v]);
+  };
+  auto read_k = [&](int sk, TokWords<VPT> (&kr)[TPL]) __attribute__((always_inline)) {
+    const char* ks = smem + w * KR * TILE_B + sk * TILE_B + lane * 16;
+#pragma unroll
+    for (int i = 0; i < TPL; ++i)
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) kr[i].x[v] = *(const uint4*)(ks + ((i ^ tmask) * VPT + v) * 1024);
+  };
   {
+    const uint32_t kslot0 = lds_offset(smem) + (uint32_t)(w * KR * TILE_B);
+    auto issue_k2 = [&](int j, int sk) __attribute__((always_inline)) {
+      const char* src = kbase + tile_of(j);
+      const uint32_t dst = kslot0 + (uint32_t)(sk * TILE_B);
+#pragma unroll
+      for (int n = 0; n < LPB; ++n) lds_dma16(src, dma_off[n], dst + n * 1024);
+    };
     const int first = j0 + w;
     const int n_my = first < j1 ? (j1 - first + NW - 1) / NW : 0;
-    for (int u = 0; u < NK; ++u) {
-      if (u < n_my) issue_k(first + u * NW, u);
-      if (u < NV && u < n_my) issue_v(first + u * NW, u);
+    TokWords<VPT> va[TPL], vb[TPL];
+    // A wait the compiler sees: the query loads are complete, so it places
+    // none of its own inside the loop, where they would also wait for the
+    // prefetches in flight.
+    constexpr unsigned kWaitVm0 = 0x0F70;     // vmcnt(0), expcnt(7), lgkmcnt(15)
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    static_assert(KR == 2, "one block in flight: K(t+1) and V(t+1) while t is computed");
+    if (n_my > 0) {
+      issue_vregs(first, va);
+      issue_k2(first, 0);
     }
-    for (int t = 0; t < n_my; ++t) {
-      const int sk = t % NK, sv = t % NV;
-      const int k_after = max(0, min(n_my, t + NK) - max(t + NK - NV + 1, 0));
-      const int v_after = max(0, min(n_my, t + NV) - (t + 1));
-      wait_tiles(k_after + v_after);
-      TokWords<VPT> kr[TPL], vr[TPL];
-      read_slots(sk, sv, kr, vr);
-      wait_lgkmcnt0();  // the slots are in registers: they may be refilled
-      if (t + NK < n_my) issue_k(first + (t + NK) * NW, sk);
-      if (t + NV < n_my) issue_v(first + (t + NV) * NW, sv);
-      compute_block(first + t * NW, kr, vr);
+    // Step t: K(t) and V(t) are the newest loads in flight, so wait for all.
+    auto step = [&](int t, TokWords<VPT> (&vcur)[TPL], TokWords<VPT> (&vnext)[TPL])
+                    __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      wait_vmcnt<0>();                      // (asm, memory clobber) the LDS reads stay below
+      TokWords<VPT> kr[TPL];
+      read_k(t & 1, kr);
+      wait_lgkmcnt0();                      // K(t)'s slot may be refilled from here on
+      if (t + 1 < n_my) {
+        issue_vregs(first + (t + 1) * NW, vnext);
+        issue_k2(first + (t + 1) * NW, (t + 1) & 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);    // the loads stay ahead of the compute
+      compute_block(first + t * NW, kr, vcur);
+    };
+    int t = 0;
+    for (; t + 1 < n_my; t += 2) {
+      step(t, va, vb);
+      step(t + 1, vb, va);
     }
+    if (t < n_my) step(t, va, vb);
   }
   __syncthreads();  // every wave is done with its ring: the LDS is reused below
 

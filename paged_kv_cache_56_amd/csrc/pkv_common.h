@@ -21,6 +21,7 @@ template <> struct kv_bytes<KV::INT8> { static constexpr int value = 1; };
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x >> 1); }
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
