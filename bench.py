@@ -326,6 +326,29 @@ def summarize_counters(fetch_csv, write_csv, stats_csv, workload, probe_gib, out
     return rec
 
 
+def summarize_trace(stats_csv, workload, out_md, command):
+    """A rocprofv3 --kernel-trace --stats summary (top kernels) for one workload."""
+    stats = _csv_rows(stats_csv)
+    top = sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:8]
+    attn = [r for r in stats if ATTN_KERNEL in r["Name"]]
+    lines = [f"# {ATTN_KERNEL} on {workload}: rocprofv3 kernel trace", "",
+             "Command (run from the repository root on one MI355X, `export TMPDIR=/tmp`):", "",
+             "```", *command, "```", "",
+             "| kernel | calls | mean us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in top:
+        name = r["Name"].replace("|", "/")
+        name = name if len(name) < 90 else name[:87] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    rec = {"workload": workload, "kernel": ATTN_KERNEL, "kernel_source_sha": kernel_source_sha(),
+           "trace_mean_launch_us": round(float(attn[0]["AverageNs"]) / 1e3, 2) if attn else None,
+           "trace_calls": int(attn[0]["Calls"]) if attn else 0}
+    lines += ["", "```json", json.dumps(rec, indent=1), "```"]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return rec
+
+
 def traffic_for(workload: str):
     """Counter-measured bytes per attention launch, if taken on these sources."""
     import re
@@ -363,9 +386,16 @@ def main():
                     help="skip the plain-read bandwidth probe and the copy used to calibrate counters")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "STATS_CSV"),
                     help="write profiles/decode_partition_kernel__<workload>.md from rocprofv3 output and exit")
+    ap.add_argument("--summarize-trace", metavar="STATS_CSV",
+                    help="write profiles/decode_partition_kernel__<workload>__trace.md from a rocprofv3 "
+                         "--kernel-trace --stats run and exit")
     ap.add_argument("--command", action="append", default=[],
                     help="(with --summarize-counters) a command line to record in the summary")
     args = ap.parse_args()
+    if args.summarize_trace:
+        out = os.path.join(PROFILES, f"decode_partition_kernel__{args.workload}__trace.md")
+        print(json.dumps(summarize_trace(args.summarize_trace, args.workload, out, args.command)))
+        return
     if args.summarize_counters:
         out = os.path.join(PROFILES, f"decode_partition_kernel__{args.workload}.md")
         rec = summarize_counters(*args.summarize_counters, args.workload, 4, out, args.command)
