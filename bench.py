@@ -432,8 +432,11 @@ def main():
     nl = spec.num_layers
     odt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[spec.out_dtype]
     outs = torch.empty((nl, spec.num_seqs, spec.num_q_heads, spec.head_dim), dtype=odt, device=dev)
+    # a scheduler knows its batch's lengths on the host: pass their block count
+    # so the split plan can balance uneven sequences
+    total_blocks = int((-(-lay.context_lens.astype(np.int64) // 16)).sum())
     dims = pkv.decode_dims(x["q"][0], x["k_cache"][0], x["block_tables"], outs[0], args.partition_blocks,
-                           args.window, args.sinks, bool(spec.fp_sinks))
+                           args.window, args.sinks, bool(spec.fp_sinks), total_blocks)
     nparts = pkv.decode_num_partitions(dims)
     ws_bytes = pkv.decode_workspace_bytes(dims)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -468,7 +471,7 @@ def main():
             pkv.paged_decode_attn(x["q"][layer], kc, vc, x["block_tables"], x["context_lens"],
                                   spec.scale, outs[layer], workspace=ws,
                                   partition_blocks=args.partition_blocks, window=args.window,
-                                  sinks=args.sinks, **kw)
+                                  sinks=args.sinks, total_blocks=total_blocks, **kw)
             if ev is not None:
                 ev[layer][1].record()
 

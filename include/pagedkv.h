@@ -55,7 +55,7 @@ extern "C" {
 #define PKV_API
 #endif
 
-#define PKV_VERSION 120  /* 1.2.0 */
+#define PKV_VERSION 130  /* 1.3.0 */
 #define PKV_BLOCK_SIZE 16
 
 typedef enum {
@@ -97,6 +97,10 @@ typedef struct {
   int32_t sink_tiles;          /* 1: positions < sinks come from full-precision side tiles
                                   (pkv_paged_decode_attn_quant only; 1 <= sinks <= 16,
                                   with or without a window); 0: from the cache */
+  int32_t total_blocks;        /* optional hint, 0 = unknown: sum over the sequences of
+                                  ceil(context_len / 16).  When the batch is much lighter
+                                  than max_blocks_per_seq suggests, the split plan sizes
+                                  its pieces from it; results do not depend on it */
 } pkv_decode_dims;
 
 /*

@@ -78,6 +78,7 @@ class DecodeDims(ctypes.Structure):
         ("window", ctypes.c_int32),
         ("sinks", ctypes.c_int32),
         ("sink_tiles", ctypes.c_int32),
+        ("total_blocks", ctypes.c_int32),
     ]
 
 
@@ -355,12 +356,12 @@ class BlockManager:
 
 def decode_dims(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor,
                 out: torch.Tensor, partition_blocks: int = 0, window: int = 0,
-                sinks: int = 0, sink_tiles: bool = False) -> DecodeDims:
+                sinks: int = 0, sink_tiles: bool = False, total_blocks: int = 0) -> DecodeDims:
     B, Hq, D = q.shape
     NB, Hkv, bs, Dk = k_cache.shape
     _need(Dk == D, "head_dim of q and cache differ")
     return DecodeDims(B, Hq, Hkv, D, bs, NB, block_tables.shape[1], _code(q), _code(k_cache),
-                      _code(out), partition_blocks, window, sinks, int(sink_tiles))
+                      _code(out), partition_blocks, window, sinks, int(sink_tiles), int(total_blocks))
 
 
 def decode_workspace_bytes(dims: DecodeDims) -> int:
@@ -389,7 +390,8 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       sink_k: Optional[torch.Tensor] = None, sink_v: Optional[torch.Tensor] = None,
                       sink_tiles_of_seq: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None,
-                      partition_blocks: int = 0, window: int = 0, sinks: int = 0) -> torch.Tensor:
+                      partition_blocks: int = 0, window: int = 0, sinks: int = 0,
+                      total_blocks: int = 0) -> torch.Tensor:
     """out[b, i] = softmax(scale * q[b, i] . K^T) V over the first context_lens[b]
     tokens of sequence b, K/V read through block_tables.  Returns `out`.
 
@@ -399,7 +401,9 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     and may give k_channel_scales: fp32 [Hkv, D] for K, and full-precision sink
     tiles sink_k, sink_v: [num_tiles, Hkv, 16, D] of q's dtype with
     sink_tiles_of_seq: int32 [B] (positions < sinks of sequence b are read from
-    its tile; 1 <= sinks <= 16, with or without a window).  `workspace` (uint8, on the device) is allocated here
+    its tile; 1 <= sinks <= 16, with or without a window).  total_blocks (the
+    batch's sum of ceil(len / 16), known to a scheduler on the host) lets the
+    split plan balance uneven lengths.  `workspace` (uint8, on the device) is allocated here
     when the call splits the context and none is given.  window > 0 limits each
     query to the last `window` positions plus the first `sinks` positions.
     """
@@ -422,7 +426,7 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
               and sink_k.dtype == sink_v.dtype == q.dtype, "sink tiles must be [n, Hkv, 16, D] of q's dtype")
         _need(sink_tiles_of_seq.dtype == torch.int32 and sink_tiles_of_seq.shape == (q.shape[0],),
               "sink_tiles_of_seq must be int32 [B]")
-    dims = decode_dims(q, k_cache, block_tables, out, partition_blocks, window, sinks, side)
+    dims = decode_dims(q, k_cache, block_tables, out, partition_blocks, window, sinks, side, total_blocks)
     need = decode_workspace_bytes(dims)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

@@ -24,7 +24,7 @@ int check_dims(const pkv_decode_dims* d) {
   if (!d) return PKV_ERR_NULL;
   if (d->num_seqs <= 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0 ||
       d->num_blocks <= 0 || d->max_blocks_per_seq <= 0 || d->partition_blocks < 0 ||
-      d->window < 0 || d->sinks < 0)
+      d->window < 0 || d->sinks < 0 || d->total_blocks < 0)
     return PKV_ERR_SHAPE;
   if (d->sink_tiles != 0 && d->sink_tiles != 1) return PKV_ERR_SHAPE;
   if (d->sink_tiles && (d->sinks < 1 || d->sinks > PKV_BLOCK_SIZE)) return PKV_ERR_SHAPE;

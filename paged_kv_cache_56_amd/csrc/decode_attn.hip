@@ -407,6 +407,19 @@ struct SeqSpan {
   }
 };
 
+// A sequence with `natt` attended blocks uses min(ceil(natt / T), P) of the
+// P partitions, cut into equal pieces (T = the planned partition size):
+// partition p covers entries [j0, j1) of the attended-block list.
+struct SeqParts {
+  int n, j0, j1;
+  __device__ __forceinline__ SeqParts(int natt, int T, int P, int p) {
+    n = natt > 0 ? min((natt + T - 1) / T, P) : 0;
+    const int pb = n > 0 ? (natt + n - 1) / n : 0;
+    j0 = p * pb;
+    j1 = min(j0 + pb, natt);
+  }
+};
+
 // ---------------------------------------------------------------------------
 template <KV KT, KV VT, KV QT, KV OT, int D, int G>
 __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
@@ -434,8 +447,8 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
 
   const SeqSpan span(a.context_lens[b], a.max_blocks, a.window, a.sinks, a.sink_tiles ? a.sinks : 0);
   // this partition: entries [j0, j1) of the sequence's attended-block list
-  const int j0 = p * a.part_blocks;
-  const int j1 = min(j0 + a.part_blocks, span.natt);
+  const SeqParts parts(span.natt, a.part_blocks, a.num_parts, p);
+  const int j0 = parts.j0, j1 = parts.j1;
   if (j0 >= j1) {
     if (!a.split) {
       for (int idx = tid; idx < G * D; idx += 256)
@@ -842,7 +855,7 @@ __global__ void __launch_bounds__(64) lse_merge_kernel(DecodeArgs a) {
   const int b = row / a.num_q_heads;
   const int lane = threadIdx.x;
   const SeqSpan span(a.context_lens[b], a.max_blocks, a.window, a.sinks, a.sink_tiles ? a.sinks : 0);
-  const int np = min((span.natt + a.part_blocks - 1) / a.part_blocks, a.num_parts);
+  const int np = SeqParts(span.natt, a.part_blocks, a.num_parts, 0).n;
   const float* ml = a.ml_part + (int64_t)row * a.num_parts * 2;
   const float* op = a.o_part + (int64_t)row * a.num_parts * D;
 
@@ -921,6 +934,20 @@ void plan_partitions(const pkv_decode_dims& d, int* part_blocks, int* num_parts)
     if (want < 1) want = 1;
     pb = (int)((maxb + want - 1) / want);
     if (pb < 16) pb = 16;
+    // The table width only bounds the lengths.  When the batch's real size
+    // is known and the plan above would keep fewer than 256 workgroups busy
+    // (one per CU), size the pieces from the real size instead (sequences
+    // are cut evenly into ceil(len / pb) pieces).  Finer splits of a batch
+    // that already fills the chip measured slower, so they are not made.
+    if (d.total_blocks > 0) {
+      const int64_t total = d.total_blocks < units / d.num_kv_heads * (int64_t)maxb
+                                ? d.total_blocks
+                                : units / d.num_kv_heads * (int64_t)maxb;
+      if (total * d.num_kv_heads < 256 * (int64_t)pb) {
+        const int64_t t = (total * d.num_kv_heads + 511) / 512;
+        pb = (int)(t < 16 ? 16 : (t > maxb ? maxb : t));
+      }
+    }
   }
   if (pb > maxb) pb = maxb;
   if (pb < 1) pb = 1;

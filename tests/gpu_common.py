@@ -33,8 +33,11 @@ def host_storage(t: torch.Tensor) -> np.ndarray:
 
 
 def run_step(x, layer: int, spec, out: torch.Tensor, partition_blocks: int = 0,
-             workspace=None, append: bool = True, window: int = 0, sinks: int = 0):
-    """One layer of the decode step on the device: append, then attend."""
+             workspace=None, append: bool = True, window: int = 0, sinks: int = 0,
+             balanced: bool = False):
+    """One layer of the decode step on the device: append, then attend.
+    balanced: pass the batch's block count, as a scheduler would."""
+    total_blocks = int(((x["context_lens"].cpu().long() + 15) // 16).sum()) if balanced else 0
     kc, vc = x["k_cache"][layer], x["v_cache"][layer]
     kw = {}
     chan = x.get("k_channel_scales")
@@ -61,7 +64,8 @@ def run_step(x, layer: int, spec, out: torch.Tensor, partition_blocks: int = 0,
             pkv.kv_append(x["k_new"][layer], x["v_new"][layer], x["slot_mapping"], kc, vc)
     return pkv.paged_decode_attn(x["q"][layer], kc, vc, x["block_tables"], x["context_lens"],
                                  spec.scale, out, workspace=workspace,
-                                 partition_blocks=partition_blocks, window=window, sinks=sinks, **kw)
+                                 partition_blocks=partition_blocks, window=window, sinks=sinks,
+                                 total_blocks=total_blocks, **kw)
 
 
 def oracle_rows(x_host_layer, layout, spec, seqs=None, q_heads=None, window=0, sinks=0):

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
     lib = pkv.load_library()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pkv_version() == 120
+    assert lib.pkv_version() == 130
 
 
 def _dims(**kw):
@@ -186,6 +186,25 @@ def test_window_shrinks_the_partition_plan():
     d = _dims(num_seqs=16, window=256, sinks=4)
     assert pkv.decode_num_partitions(d) == 2          # 18 blocks, >= 16 per partition
     assert pkv.decode_workspace_bytes(d) == 16 * 64 * 2 * (128 + 2) * 4
+
+
+def test_plan_uses_the_batch_size_hint_for_light_batches():
+    # a table 8192 blocks wide, but the 8 sequences hold ~1000 blocks each:
+    # sized for the width, 8 x 8 units would keep only 64 workgroups busy
+    d = _dims(num_seqs=8, num_kv_heads=8, num_q_heads=32, max_blocks_per_seq=8192)
+    assert pkv.decode_num_partitions(d) == 8                     # pieces of 1024
+    d = _dims(num_seqs=8, num_kv_heads=8, num_q_heads=32, max_blocks_per_seq=8192, total_blocks=8000)
+    assert pkv.decode_num_partitions(d) == -(-8192 // 125)       # pieces of 125
+    # a batch that fills the chip keeps the default plan (Llama-3-8B-shaped)
+    d = _dims(num_seqs=32, num_kv_heads=8, num_q_heads=32, max_blocks_per_seq=498, total_blocks=8704)
+    assert pkv.decode_num_partitions(d) == 2
+    # a uniform 70B-shaped batch is not split either way
+    d = _dims(total_blocks=64 * 256)
+    assert pkv.decode_num_partitions(d) == 1 and pkv.decode_workspace_bytes(d) == 0
+    # a hint larger than the batch can hold is clamped to it
+    d = _dims(num_seqs=8, num_kv_heads=8, num_q_heads=32, max_blocks_per_seq=8192, total_blocks=10 ** 9)
+    assert pkv.decode_num_partitions(d) == 8
+    assert _attn(_dims(total_blocks=-1)) == -2
 
 
 def test_explicit_partition_size():

@@ -357,6 +357,8 @@ SMALL = {
                                                          [1, 2, 3, 4, 17, 100], 17, hkv=2, append=True,
                                                          v="int8", outliers=2, fp_sinks=3),
     "long_fp8_fpsinks_small": scaled(WORKLOADS["long_fp8"], num_seqs=2, len_range=(8192, 8192), fp_sinks=4),
+    # one long sequence among short ones: the batch-size hint changes the split plan
+    "one_long_many_short_f16": _ragged("r18", "f16", "f16", "f16", 128, 4, [8192] + [20, 3, 47, 16] * 4, 18),
 }
 
 
@@ -420,6 +422,27 @@ def test_sliding_window_and_sinks(case, window, sinks, pb):
     say(f"    max|err| = {err:.3e} (tol {TOL[spec.kv_dtype]})")
     assert np.isfinite(got).all()
     assert err <= TOL[spec.kv_dtype]
+
+
+@pytest.mark.parametrize("name", ["one_long_many_short_f16", "llama3_8b_bf16_small", "ragged_f16_g8_d128",
+                                  "ragged_fp8_g2_d128_f32", "ragged_int8_g8_d128_fpsinks4", "long_fp8_small"])
+def test_balanced_plan_matches_oracle(name):
+    """With the batch's block count passed, the split plan may change (for a
+    light batch: pieces sized from the real total); the result still matches
+    the oracle."""
+    spec = SMALL[name]
+    lay = build_layout(spec)
+    say(f"[balanced] {name}: lens={list(lay.context_lens[:12])}")
+    x = make_host_inputs(lay)
+    xs = _to_dev(x)
+    out = _out(spec)
+    run_step(xs, 0, spec, out, balanced=True)
+    torch.cuda.synchronize()
+    got = out_f64(out)
+    ref = oracle_rows(host_layer(x, 0), lay, spec)
+    err = err_beyond_rounding(got, ref, spec.out_dtype)
+    say(f"    max|err| = {err:.3e} (tol {TOL[spec.kv_dtype]})")
+    assert np.isfinite(got).all() and err <= TOL[spec.kv_dtype]
 
 
 @pytest.mark.parametrize("pb", [1, 2, 3, 7])
