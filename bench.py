@@ -382,6 +382,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="0 skips the CPU baseline")
     ap.add_argument("--copy-pairs", type=int, default=0,
                     help="also time copy-on-write copies of this many random block pairs")
+    ap.add_argument("--no-groups", action="store_true",
+                    help="attend shared prefixes per sequence instead of once per group")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the plain-read bandwidth probe and the copy used to calibrate counters")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "STATS_CSV"),
@@ -435,8 +437,18 @@ def main():
     # a scheduler knows its batch's lengths on the host: pass their block count
     # so the split plan can balance uneven sequences
     total_blocks = int((-(-lay.context_lens.astype(np.int64) // 16)).sum())
+    # shared prefixes: read once per group (the scheduler knows the groups)
+    grouped = (lay.group_starts is not None and not args.no_groups and args.window == 0
+               and spec.kv_dtype in ("f16", "bf16"))
+    gkw = {}
+    if grouped:
+        gkw = dict(prefix_group_starts=x["group_starts"], prefix_group_blocks=x["group_blocks"],
+                   prefix_max_seqs=int(np.diff(lay.group_starts).max()),
+                   prefix_max_blocks=int(lay.group_blocks.max()))
     dims = pkv.decode_dims(x["q"][0], x["k_cache"][0], x["block_tables"], outs[0], args.partition_blocks,
-                           args.window, args.sinks, bool(spec.fp_sinks), total_blocks)
+                           args.window, args.sinks, bool(spec.fp_sinks), total_blocks,
+                           len(lay.group_blocks) if grouped else 0, gkw.get("prefix_max_seqs", 0),
+                           gkw.get("prefix_max_blocks", 0))
     nparts = pkv.decode_num_partitions(dims)
     ws_bytes = pkv.decode_workspace_bytes(dims)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -471,7 +483,7 @@ def main():
             pkv.paged_decode_attn(x["q"][layer], kc, vc, x["block_tables"], x["context_lens"],
                                   spec.scale, outs[layer], workspace=ws,
                                   partition_blocks=args.partition_blocks, window=args.window,
-                                  sinks=args.sinks, total_blocks=total_blocks, **kw)
+                                  sinks=args.sinks, total_blocks=total_blocks, **kw, **gkw)
             if ev is not None:
                 ev[layer][1].record()
 
@@ -495,8 +507,9 @@ def main():
     kv_bytes, alg_bytes, logical_bytes = attention_bytes(spec, lay, args.window, args.sinks)
     value = kv_bytes * nl / (ms_per_step / 1e3) / 1e9
     achieved = alg_bytes / mean_launch_s / 1e9
-    kernel = "decode_partition_kernel" + ("+lse_merge_kernel" if nparts > 1 else "")
-    trec = traffic_for(spec.name) if (nparts == 1 and args.window == 0) else None
+    kernel = ("group_prefix_kernel+" if grouped else "") + "decode_partition_kernel" + (
+        "+lse_merge_kernel" if (nparts > 1 or grouped) else "")
+    trec = traffic_for(spec.name) if (nparts == 1 and args.window == 0 and not grouped) else None
     traffic = None if trec is None else trec["traffic_bytes_per_launch"]
     log(f"[bench] {ms_per_step:.3f} ms/step; attention launch {mean_launch_s * 1e6:.1f} us "
         f"-> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of peak)")
@@ -542,6 +555,7 @@ def main():
             "window": args.window,
             "sinks": args.sinks if (args.window > 0 or spec.fp_sinks) else 0,
             "fp_sinks": spec.fp_sinks,
+            "prefix_groups": len(lay.group_blocks) if grouped else 0,
             "kv_bytes_per_step": kv_bytes * nl,
             "logical_kv_bytes_per_step": logical_bytes * nl,
         },

@@ -55,7 +55,7 @@ extern "C" {
 #define PKV_API
 #endif
 
-#define PKV_VERSION 130  /* 1.3.0 */
+#define PKV_VERSION 140  /* 1.4.0 */
 #define PKV_BLOCK_SIZE 16
 
 typedef enum {
@@ -101,6 +101,11 @@ typedef struct {
                                   ceil(context_len / 16).  When the batch is much lighter
                                   than max_blocks_per_seq suggests, the split plan sizes
                                   its pieces from it; results do not depend on it */
+  int32_t prefix_groups;       /* G >= 0 shared-prefix groups (pkv_paged_decode_attn_prefix
+                                  only; 0 everywhere else) */
+  int32_t prefix_max_seqs;     /* with G > 0: >= the sequence count of every group */
+  int32_t prefix_max_blocks;   /* with G > 0: >= every group's shared block count,
+                                  <= max_blocks_per_seq */
 } pkv_decode_dims;
 
 /*
@@ -248,6 +253,37 @@ PKV_API int pkv_paged_decode_attn_quant(const void* q, const void* k_cache, cons
                                         const int32_t* context_lens, float scale, void* out,
                                         const pkv_decode_dims* dims, void* workspace,
                                         size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Decode attention for batches whose sequences share prefix blocks ("The KV
+ * Cache memory ledger" 4: prefix sharing points several block tables at the
+ * same physical blocks; "Large-model inference KV Cache memory
+ * optimisation" 3.1-3.3: shared blocks are stored once, whole blocks only).
+ * The result is that of pkv_paged_decode_attn; only the order of the reads
+ * changes: a group's shared blocks are read once and scored against the
+ * queries of all its sequences together (a matrix product on the matrix
+ * cores), the rest of each sequence as usual, and the two parts are merged
+ * by log-sum-exp.
+ *   group_seq_start: int32 device [G + 1], nondecreasing: group g is the
+ *     sequences [group_seq_start[g], group_seq_start[g + 1]);
+ *   group_prefix_blocks: int32 device [G]: every sequence of group g has the
+ *     same first group_prefix_blocks[g] block-table entries (those of the
+ *     group's first sequence are read), each a full block: 16 * that count
+ *     <= context_lens[b] for every b of the group.
+ * Sequences outside every group, and past dims->prefix_max_seqs in a group,
+ * are attended as usual; counts are clamped to [0, dims->prefix_max_blocks].
+ * Tables that break the sharing promise, or unsorted starts, give undefined
+ * results but never out-of-bounds accesses.  dims->prefix_groups = G with
+ * G * ceil(prefix_max_seqs * g / 64) <= 65535; window and sink tiles must be
+ * off; q, caches and out all F16 or all BF16.  Always splits (workspace > 0).
+ */
+PKV_API int pkv_paged_decode_attn_prefix(const void* q, const void* k_cache, const void* v_cache,
+                                         const int32_t* group_seq_start,
+                                         const int32_t* group_prefix_blocks,
+                                         const int32_t* block_tables, const int32_t* context_lens,
+                                         float scale, void* out, const pkv_decode_dims* dims,
+                                         void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
 
 /*
  * Bandwidth reference ("KV Cache from first principles" 4.1: decode time is

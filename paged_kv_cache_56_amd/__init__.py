@@ -12,7 +12,9 @@ carry device memory and streams.
     paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, scale, out,
                       k_scales=None, v_scales=None, k_channel_scales=None,
                       sink_k=None, sink_v=None, sink_tiles_of_seq=None,
-                      workspace=None, partition_blocks=0, window=0, sinks=0)
+                      workspace=None, partition_blocks=0, window=0, sinks=0,
+                      total_blocks=0, prefix_group_starts=None, prefix_group_blocks=None,
+                      prefix_max_seqs=0, prefix_max_blocks=0)
 """
 
 from __future__ import annotations
@@ -79,6 +81,9 @@ class DecodeDims(ctypes.Structure):
         ("sinks", ctypes.c_int32),
         ("sink_tiles", ctypes.c_int32),
         ("total_blocks", ctypes.c_int32),
+        ("prefix_groups", ctypes.c_int32),
+        ("prefix_max_seqs", ctypes.c_int32),
+        ("prefix_max_blocks", ctypes.c_int32),
     ]
 
 
@@ -132,6 +137,9 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_paged_decode_attn_quant.argtypes = [vp, vp, vp, ctypes.POINTER(QuantParams), vp, vp,
                                                 ctypes.c_float, vp, dims_p, vp, sz, vp]
     lib.pkv_paged_decode_attn_quant.restype = ctypes.c_int
+    lib.pkv_paged_decode_attn_prefix.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
+                                                 dims_p, vp, sz, vp]
+    lib.pkv_paged_decode_attn_prefix.restype = ctypes.c_int
     lib.pkv_hbm_read_probe.argtypes = [vp, sz, vp, i32, vp]
     lib.pkv_hbm_read_probe.restype = ctypes.c_int
     i64, i32p, i64p = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
@@ -356,12 +364,15 @@ class BlockManager:
 
 def decode_dims(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor,
                 out: torch.Tensor, partition_blocks: int = 0, window: int = 0,
-                sinks: int = 0, sink_tiles: bool = False, total_blocks: int = 0) -> DecodeDims:
+                sinks: int = 0, sink_tiles: bool = False, total_blocks: int = 0,
+                prefix_groups: int = 0, prefix_max_seqs: int = 0,
+                prefix_max_blocks: int = 0) -> DecodeDims:
     B, Hq, D = q.shape
     NB, Hkv, bs, Dk = k_cache.shape
     _need(Dk == D, "head_dim of q and cache differ")
     return DecodeDims(B, Hq, Hkv, D, bs, NB, block_tables.shape[1], _code(q), _code(k_cache),
-                      _code(out), partition_blocks, window, sinks, int(sink_tiles), int(total_blocks))
+                      _code(out), partition_blocks, window, sinks, int(sink_tiles), int(total_blocks),
+                      int(prefix_groups), int(prefix_max_seqs), int(prefix_max_blocks))
 
 
 def decode_workspace_bytes(dims: DecodeDims) -> int:
@@ -391,7 +402,10 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       sink_tiles_of_seq: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None,
                       partition_blocks: int = 0, window: int = 0, sinks: int = 0,
-                      total_blocks: int = 0) -> torch.Tensor:
+                      total_blocks: int = 0,
+                      prefix_group_starts: Optional[torch.Tensor] = None,
+                      prefix_group_blocks: Optional[torch.Tensor] = None,
+                      prefix_max_seqs: int = 0, prefix_max_blocks: int = 0) -> torch.Tensor:
     """out[b, i] = softmax(scale * q[b, i] . K^T) V over the first context_lens[b]
     tokens of sequence b, K/V read through block_tables.  Returns `out`.
 
@@ -406,10 +420,17 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     split plan balance uneven lengths.  `workspace` (uint8, on the device) is allocated here
     when the call splits the context and none is given.  window > 0 limits each
     query to the last `window` positions plus the first `sinks` positions.
+
+    Shared prefixes (f16 or bf16 throughout): prefix_group_starts int32 [G + 1]
+    (nondecreasing; group g = sequences [starts[g], starts[g + 1])) and
+    prefix_group_blocks int32 [G] (the group's shared leading table entries,
+    full blocks) on the device, with host bounds prefix_max_seqs (>= every
+    group's size) and prefix_max_blocks (>= every count); the shared blocks
+    are then read once per group.  The result is the same attention.
     """
     lib = load_library()
     _dev(q, k_cache, v_cache, block_tables, context_lens, out, k_scales, v_scales, k_channel_scales,
-         sink_k, sink_v, sink_tiles_of_seq, workspace)
+         sink_k, sink_v, sink_tiles_of_seq, workspace, prefix_group_starts, prefix_group_blocks)
     _need(q.dim() == 3 and out.shape == q.shape, "q and out must be [B, Hq, D]")
     _need(k_cache.shape == v_cache.shape and k_cache.dim() == 4, "caches must be [NB, Hkv, 16, D]")
     kc, vc = _code(k_cache), _code(v_cache)
@@ -426,7 +447,18 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
               and sink_k.dtype == sink_v.dtype == q.dtype, "sink tiles must be [n, Hkv, 16, D] of q's dtype")
         _need(sink_tiles_of_seq.dtype == torch.int32 and sink_tiles_of_seq.shape == (q.shape[0],),
               "sink_tiles_of_seq must be int32 [B]")
-    dims = decode_dims(q, k_cache, block_tables, out, partition_blocks, window, sinks, side, total_blocks)
+    grouped = prefix_group_starts is not None or prefix_group_blocks is not None
+    G = 0
+    if grouped:
+        _need(prefix_group_starts is not None and prefix_group_blocks is not None,
+              "shared prefixes need prefix_group_starts and prefix_group_blocks")
+        G = prefix_group_blocks.numel()
+        _need(prefix_group_starts.dtype == prefix_group_blocks.dtype == torch.int32
+              and prefix_group_blocks.dim() == 1 and prefix_group_starts.shape == (G + 1,),
+              "prefix_group_starts must be int32 [G + 1] and prefix_group_blocks int32 [G]")
+        _need(kc in (1, 2), "shared prefixes need f16 or bf16 caches")
+    dims = decode_dims(q, k_cache, block_tables, out, partition_blocks, window, sinks, side, total_blocks,
+                       G, prefix_max_seqs if grouped else 0, prefix_max_blocks if grouped else 0)
     need = decode_workspace_bytes(dims)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -455,8 +487,15 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     else:
         _need(k_scales is None and v_scales is None and k_channel_scales is None and not side,
               "scales and sink tiles apply to 8-bit caches only")
-        st = lib.pkv_paged_decode_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                                       _ptr(context_lens), float(scale), _ptr(out),
-                                       ctypes.byref(dims), ws_ptr, ws_bytes, _stream(q))
+        if grouped:
+            st = lib.pkv_paged_decode_attn_prefix(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                                  _ptr(prefix_group_starts), _ptr(prefix_group_blocks),
+                                                  _ptr(block_tables), _ptr(context_lens), float(scale),
+                                                  _ptr(out), ctypes.byref(dims), ws_ptr, ws_bytes,
+                                                  _stream(q))
+        else:
+            st = lib.pkv_paged_decode_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                           _ptr(context_lens), float(scale), _ptr(out),
+                                           ctypes.byref(dims), ws_ptr, ws_bytes, _stream(q))
     _check(st)
     return out

@@ -35,6 +35,14 @@ int check_dims(const pkv_decode_dims* d) {
   if (d->head_dim != 64 && d->head_dim != 128) return PKV_ERR_SHAPE;
   // grid dimensions: y = KV heads, z = sequences (HIP limits y, z to 65535)
   if (d->num_kv_heads > 65535 || d->num_seqs > 65535) return PKV_ERR_SHAPE;
+  if (d->prefix_groups < 0 || d->prefix_max_seqs < 0 || d->prefix_max_blocks < 0)
+    return PKV_ERR_SHAPE;
+  if (d->prefix_groups > 0) {
+    if (d->prefix_max_seqs < 1 || d->prefix_max_blocks > d->max_blocks_per_seq) return PKV_ERR_SHAPE;
+    if (d->window != 0 || d->sink_tiles) return PKV_ERR_SHAPE;
+    const int64_t z = (int64_t)d->prefix_groups * (((int64_t)d->prefix_max_seqs * g + 63) / 64);
+    if (z > 65535) return PKV_ERR_SHAPE;   // grid z of the shared-prefix pass
+  }
   if (!elem_bytes(d->q_dtype) || !elem_bytes(d->kv_dtype) || !elem_bytes(d->out_dtype))
     return PKV_ERR_DTYPE;
   return PKV_OK;
@@ -61,13 +69,25 @@ int check_dtypes(const pkv_decode_dims* d, int v_dtype) {
   return PKV_OK;
 }
 
-// qp: the 8-bit arguments (NULL for the f32/f16/bf16 entry point).
+// Shared-prefix group arguments (both NULL: the entry points without groups).
+struct GroupPtrs {
+  const int32_t* seq_start;
+  const int32_t* blocks;
+};
+
+// qp: the 8-bit arguments (NULL for the f32/f16/bf16 entry points).
 int decode_common(const void* q, const void* k_cache, const void* v_cache, const pkv_quant_params* qp,
-                  const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
-                  const pkv_decode_dims* dims, void* workspace, size_t workspace_bytes,
-                  hipStream_t stream) {
+                  const GroupPtrs* gp, const int32_t* block_tables, const int32_t* context_lens,
+                  float scale, void* out, const pkv_decode_dims* dims, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
   int st = check_dims(dims);
   if (st) return st;
+  if (!gp && dims->prefix_groups != 0) return PKV_ERR_SHAPE;   // groups: the _prefix entry point
+  if (gp) {
+    if (dims->prefix_groups > 0 && (!gp->seq_start || !gp->blocks)) return PKV_ERR_NULL;
+    if (qp) return PKV_ERR_DTYPE;
+    if (dims->kv_dtype != PKV_F16 && dims->kv_dtype != PKV_BF16) return PKV_ERR_DTYPE;
+  }
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
   if (qp && (!qp->k_scales || !qp->v_scales)) return PKV_ERR_NULL;
   if (dims->sink_tiles) {
@@ -80,8 +100,9 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
   st = check_dtypes(dims, v_dtype);
   if (st) return st;
   if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
-  int pb, np;
+  int pb, np, gpb = 1, gnp = 0, qchunks = 0;
   plan_partitions(*dims, &pb, &np);
+  if (dims->prefix_groups > 0) plan_groups(*dims, &gpb, &gnp, &qchunks);
   const size_t need = workspace_bytes_for(*dims);
   if (need && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
 
@@ -99,7 +120,7 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
   const size_t rows = (size_t)dims->num_seqs * dims->num_q_heads;
   a.split = need ? 1 : 0;
   a.o_part = need ? (float*)workspace : nullptr;
-  a.ml_part = need ? (float*)workspace + rows * np * dims->head_dim : nullptr;
+  a.ml_part = need ? (float*)workspace + rows * (np + gnp) * dims->head_dim : nullptr;
   a.num_seqs = dims->num_seqs;
   a.num_q_heads = dims->num_q_heads;
   a.num_kv_heads = dims->num_kv_heads;
@@ -108,6 +129,17 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
   a.max_blocks = dims->max_blocks_per_seq;
   a.part_blocks = pb;
   a.num_parts = np;
+  a.part_stride = np + gnp;
+  if (dims->prefix_groups > 0) {
+    a.group_seq_start = gp->seq_start;
+    a.group_blocks = gp->blocks;
+    a.num_groups = dims->prefix_groups;
+    a.group_max_seqs = dims->prefix_max_seqs;
+    a.group_max_blocks = dims->prefix_max_blocks;
+    a.group_part_blocks = gpb;
+    a.group_num_parts = gnp;
+    a.group_qchunks = qchunks;
+  }
   a.window = dims->window;
   a.sinks = (dims->window > 0 || dims->sink_tiles) ? dims->sinks : 0;
   a.sink_tiles = dims->sink_tiles;
@@ -221,8 +253,8 @@ int pkv_paged_decode_attn(const void* q, const void* k_cache, const void* v_cach
                           const int32_t* block_tables, const int32_t* context_lens, float scale,
                           void* out, const pkv_decode_dims* dims, void* workspace,
                           size_t workspace_bytes, hipStream_t stream) {
-  return decode_common(q, k_cache, v_cache, nullptr, block_tables, context_lens, scale, out, dims,
-                       workspace, workspace_bytes, stream);
+  return decode_common(q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens, scale, out,
+                       dims, workspace, workspace_bytes, stream);
 }
 
 int pkv_paged_decode_attn_fp8(const void* q, const void* k_cache, const void* v_cache,
@@ -235,8 +267,8 @@ int pkv_paged_decode_attn_fp8(const void* q, const void* k_cache, const void* v_
   qp.k_scales = k_scales;
   qp.v_scales = v_scales;
   qp.v_dtype = PKV_FP8_E4M3;
-  return decode_common(q, k_cache, v_cache, &qp, block_tables, context_lens, scale, out, dims,
-                       workspace, workspace_bytes, stream);
+  return decode_common(q, k_cache, v_cache, &qp, nullptr, block_tables, context_lens, scale, out,
+                       dims, workspace, workspace_bytes, stream);
 }
 
 int pkv_paged_decode_attn_quant(const void* q, const void* k_cache, const void* v_cache,
@@ -245,8 +277,18 @@ int pkv_paged_decode_attn_quant(const void* q, const void* k_cache, const void* 
                                 const pkv_decode_dims* dims, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
   if (!p) return PKV_ERR_NULL;
-  return decode_common(q, k_cache, v_cache, p, block_tables, context_lens, scale, out, dims,
-                       workspace, workspace_bytes, stream);
+  return decode_common(q, k_cache, v_cache, p, nullptr, block_tables, context_lens, scale, out,
+                       dims, workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_decode_attn_prefix(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* group_seq_start, const int32_t* group_prefix_blocks,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 float scale, void* out, const pkv_decode_dims* dims,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const GroupPtrs gp{group_seq_start, group_prefix_blocks};
+  return decode_common(q, k_cache, v_cache, nullptr, &gp, block_tables, context_lens, scale, out,
+                       dims, workspace, workspace_bytes, stream);
 }
 
 int pkv_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t sink_words,

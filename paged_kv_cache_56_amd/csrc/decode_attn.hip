@@ -407,19 +407,6 @@ struct SeqSpan {
   }
 };
 
-// A sequence with `natt` attended blocks uses min(ceil(natt / T), P) of the
-// P partitions, cut into equal pieces (T = the planned partition size):
-// partition p covers entries [j0, j1) of the attended-block list.
-struct SeqParts {
-  int n, j0, j1;
-  __device__ __forceinline__ SeqParts(int natt, int T, int P, int p) {
-    n = natt > 0 ? min((natt + T - 1) / T, P) : 0;
-    const int pb = n > 0 ? (natt + n - 1) / n : 0;
-    j0 = p * pb;
-    j1 = min(j0 + pb, natt);
-  }
-};
-
 // ---------------------------------------------------------------------------
 template <KV KT, KV VT, KV QT, KV OT, int D, int G>
 __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
@@ -445,7 +432,10 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int Hq = a.num_kv_heads * G;
 
-  const SeqSpan span(a.context_lens[b], a.max_blocks, a.window, a.sinks, a.sink_tiles ? a.sinks : 0);
+  // positions covered elsewhere (sink tiles, or a shared prefix read by the
+  // group pass) are skipped here
+  const SeqSpan span(a.context_lens[b], a.max_blocks, a.window, a.sinks,
+                     a.sink_tiles ? a.sinks : 16 * prefix_blocks_of_seq(a, b));
   // this partition: entries [j0, j1) of the sequence's attended-block list
   const SeqParts parts(span.natt, a.part_blocks, a.num_parts, p);
   const int j0 = parts.j0, j1 = parts.j1;
@@ -828,10 +818,10 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     if (!a.split) {
       store_out<OT>(a.out, row * D + d, res);
     } else {
-      a.o_part[(row * a.num_parts + p) * D + d] = res;
+      a.o_part[(row * a.part_stride + p) * D + d] = res;
       if (d == 0) {
-        a.ml_part[(row * a.num_parts + p) * 2 + 0] = m;
-        a.ml_part[(row * a.num_parts + p) * 2 + 1] = lsum;
+        a.ml_part[(row * a.part_stride + p) * 2 + 0] = m;
+        a.ml_part[(row * a.part_stride + p) * 2 + 1] = lsum;
       }
     }
   }
@@ -854,10 +844,15 @@ __global__ void __launch_bounds__(64) lse_merge_kernel(DecodeArgs a) {
   const int row = blockIdx.x;
   const int b = row / a.num_q_heads;
   const int lane = threadIdx.x;
-  const SeqSpan span(a.context_lens[b], a.max_blocks, a.window, a.sinks, a.sink_tiles ? a.sinks : 0);
+  const int pre = a.sink_tiles ? 0 : prefix_blocks_of_seq(a, b);
+  const SeqSpan span(a.context_lens[b], a.max_blocks, a.window, a.sinks,
+                     a.sink_tiles ? a.sinks : 16 * pre);
+  // slots [0, np) hold the per-sequence pieces, [num_parts, num_parts + ng)
+  // those of the shared-prefix pass
   const int np = SeqParts(span.natt, a.part_blocks, a.num_parts, 0).n;
-  const float* ml = a.ml_part + (int64_t)row * a.num_parts * 2;
-  const float* op = a.o_part + (int64_t)row * a.num_parts * D;
+  const int ng = pre > 0 ? SeqParts(pre, a.group_part_blocks, a.group_num_parts, 0).n : 0;
+  const float* ml = a.ml_part + (int64_t)row * a.part_stride * 2;
+  const float* op = a.o_part + (int64_t)row * a.part_stride * D;
 
   float ms = -INFINITY, ls = 0.f, os[PER];
 #pragma unroll
@@ -890,8 +885,10 @@ __global__ void __launch_bounds__(64) lse_merge_kernel(DecodeArgs a) {
   }
 
   float m = ls > 0.f ? ms : -INFINITY;
-  for (int p = 0; p < np; ++p)
+  for (int i = 0; i < np + ng; ++i) {
+    const int p = i < np ? i : a.num_parts + (i - np);
     if (ml[2 * p + 1] > 0.f) m = fmaxf(m, ml[2 * p]);
+  }
   float o[PER];
   float wsum = 0.f;
   {
@@ -900,7 +897,8 @@ __global__ void __launch_bounds__(64) lse_merge_kernel(DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) o[k] = os[k] * f;
   }
-  for (int p = 0; p < np; ++p) {
+  for (int i = 0; i < np + ng; ++i) {
+    const int p = i < np ? i : a.num_parts + (i - np);
     const float lp = ml[2 * p + 1];
     if (!(lp > 0.f)) continue;
     const float wgt = lp * __builtin_amdgcn_exp2f(ml[2 * p] - m);
@@ -956,10 +954,12 @@ void plan_partitions(const pkv_decode_dims& d, int* part_blocks, int* num_parts)
 }
 
 size_t workspace_bytes_for(const pkv_decode_dims& d) {
-  int pb, np;
+  int pb, np, gpb, gnp = 0, qc;
   plan_partitions(d, &pb, &np);
-  if (np <= 1 && !d.sink_tiles) return 0;    // sink tiles are merged in: always split
-  return (size_t)d.num_seqs * d.num_q_heads * np * (d.head_dim + 2) * sizeof(float);
+  if (d.prefix_groups > 0) plan_groups(d, &gpb, &gnp, &qc);
+  // sink tiles and shared-prefix groups are merged in: always split
+  if (np <= 1 && !d.sink_tiles && d.prefix_groups <= 0) return 0;
+  return (size_t)d.num_seqs * d.num_q_heads * (np + gnp) * (d.head_dim + 2) * sizeof(float);
 }
 
 template <KV KT, KV VT, KV QT, KV OT, int D, int G>
@@ -996,6 +996,10 @@ static int dispatch_d(const DecodeArgs& a, hipStream_t s) {
 }
 
 int launch_decode(const DecodeArgs& a, hipStream_t s) {
+  if (a.num_groups > 0) {
+    const int st = launch_group_prefix(a, s);   // before the merge that reads it
+    if (st != PKV_OK) return st;
+  }
   const KV kt = (KV)a.kv_dtype, vt = (KV)a.v_dtype, qt = (KV)a.q_dtype, ot = (KV)a.out_dtype;
   if (kt == KV::F32 || kt == KV::F16 || kt == KV::BF16) {
     if (vt != kt || qt != kt || ot != kt) return PKV_ERR_DTYPE;

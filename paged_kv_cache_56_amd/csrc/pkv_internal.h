@@ -39,10 +39,13 @@ struct DecodeArgs {
   const int32_t* context_lens;
   float scale;
   void* out;
-  float* o_part;           // [B*Hq][num_parts][D] when split
-  float* ml_part;          // [B*Hq][num_parts][2] when split
+  float* o_part;           // [B*Hq][part_stride][D] when split
+  float* ml_part;          // [B*Hq][part_stride][2] when split
   int num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks;
   int part_blocks, num_parts;
+  // workspace slots per row: num_parts for the per-sequence pass, then
+  // group_num_parts for the shared-prefix pass
+  int part_stride;
   int split;               // partial results go to the workspace (then merged)
   int window, sinks;       // sliding window (0 = off) and attention-sink tokens
   // full-precision sink tiles (q's dtype, [num_sink_tiles][Hkv][16][D]); when
@@ -54,13 +57,69 @@ struct DecodeArgs {
   int num_sink_tiles;
   int sink_tiles;
   int q_dtype, kv_dtype, v_dtype, out_dtype;   // kv_dtype is K's
+  // shared-prefix groups (num_groups = 0: none): sequences
+  // [group_seq_start[g], group_seq_start[g+1]) share their first
+  // group_blocks[g] table entries, which one pass reads once for all of them
+  const int32_t* group_seq_start;
+  const int32_t* group_blocks;
+  int num_groups, group_max_seqs, group_max_blocks;
+  int group_part_blocks, group_num_parts;   // split of a group's shared blocks
+  int group_qchunks;                        // 64-row chunks of a group's queries
 };
+
+// A list of `natt` blocks uses min(ceil(natt / T), P) of P pieces, cut
+// equally (T = the planned piece size): piece p covers entries [j0, j1).
+struct SeqParts {
+  int n, j0, j1;
+  __device__ __forceinline__ SeqParts(int natt, int T, int P, int p) {
+    n = natt > 0 ? min((natt + T - 1) / T, P) : 0;
+    const int pb = n > 0 ? (natt + n - 1) / n : 0;
+    j0 = p * pb;
+    j1 = min(j0 + pb, natt);
+  }
+};
+
+// One group as both passes see it, clamped so that they always agree on
+// which blocks of which sequence the group pass covers.
+struct PrefixGroup {
+  int s0, nseq, nblk;   // first sequence, sequences covered, shared blocks
+};
+
+__device__ __forceinline__ PrefixGroup prefix_group(const DecodeArgs& a, int g) {
+  PrefixGroup r;
+  const int s0 = min(max(a.group_seq_start[g], 0), a.num_seqs);
+  const int s1 = min(max(a.group_seq_start[g + 1], s0), a.num_seqs);
+  r.s0 = s0;
+  r.nseq = min(s1 - s0, a.group_max_seqs);
+  r.nblk = r.nseq > 0 ? min(max(a.group_blocks[g], 0), a.group_max_blocks) : 0;
+  return r;
+}
+
+// Leading blocks of sequence b that the group pass covers (0 outside every
+// group): the last group starting at or before b, if b is among its
+// covered sequences.
+__device__ __forceinline__ int prefix_blocks_of_seq(const DecodeArgs& a, int b) {
+  if (a.num_groups <= 0) return 0;
+  int lo = 0, hi = a.num_groups;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.group_seq_start[mid] <= b) lo = mid; else hi = mid;
+  }
+  const PrefixGroup pg = prefix_group(a, lo);
+  return (b >= pg.s0 && b < pg.s0 + pg.nseq) ? pg.nblk : 0;
+}
 
 // Partition plan: depends on dims only.
 void plan_partitions(const pkv_decode_dims& d, int* part_blocks, int* num_parts);
+// Shared-prefix plan (dims->prefix_groups > 0): blocks per piece, pieces,
+// 64-row query chunks per group.
+void plan_groups(const pkv_decode_dims& d, int* part_blocks, int* num_parts, int* qchunks);
 size_t workspace_bytes_for(const pkv_decode_dims& d);
 
 int launch_decode(const DecodeArgs& a, hipStream_t stream);
+// the shared-prefix pass (F16 or BF16 throughout); writes its partial
+// results into workspace slots [num_parts, part_stride) of each row
+int launch_group_prefix(const DecodeArgs& a, hipStream_t stream);
 
 int launch_hbm_read(const void* buf, size_t bytes, uint32_t* sink, int sink_words,
                     hipStream_t stream);

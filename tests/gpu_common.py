@@ -32,11 +32,22 @@ def host_storage(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
+def group_args(x) -> dict:
+    """Shared-prefix group arguments of the attention call, from the tensors'
+    group descriptors (host bounds as a scheduler would know them)."""
+    starts, blocks = x["group_starts"], x["group_blocks"]
+    hs = starts.cpu().numpy()
+    return dict(prefix_group_starts=starts, prefix_group_blocks=blocks,
+                prefix_max_seqs=max(1, int((hs[1:] - hs[:-1]).max(initial=0))),
+                prefix_max_blocks=int(blocks.cpu().numpy().max(initial=0)))
+
+
 def run_step(x, layer: int, spec, out: torch.Tensor, partition_blocks: int = 0,
              workspace=None, append: bool = True, window: int = 0, sinks: int = 0,
-             balanced: bool = False):
+             balanced: bool = False, grouped: bool = False):
     """One layer of the decode step on the device: append, then attend.
-    balanced: pass the batch's block count, as a scheduler would."""
+    balanced: pass the batch's block count, as a scheduler would.
+    grouped: read shared prefixes once per group (the tensors' descriptors)."""
     total_blocks = int(((x["context_lens"].cpu().long() + 15) // 16).sum()) if balanced else 0
     kc, vc = x["k_cache"][layer], x["v_cache"][layer]
     kw = {}
@@ -62,6 +73,8 @@ def run_step(x, layer: int, spec, out: torch.Tensor, partition_blocks: int = 0,
             pkv.kv_append_quant(x["v_new"][layer], x["slot_mapping"], vc, kw["v_scales"])
         else:
             pkv.kv_append(x["k_new"][layer], x["v_new"][layer], x["slot_mapping"], kc, vc)
+    if grouped:
+        kw.update(group_args(x))
     return pkv.paged_decode_attn(x["q"][layer], kc, vc, x["block_tables"], x["context_lens"],
                                  spec.scale, out, workspace=workspace,
                                  partition_blocks=partition_blocks, window=window, sinks=sinks,

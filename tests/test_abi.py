@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
     lib = pkv.load_library()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pkv_version() == 130
+    assert lib.pkv_version() == 140
 
 
 def _dims(**kw):
@@ -138,6 +138,46 @@ def test_sink_tile_status_codes_and_workspace():
     assert pkv.decode_num_partitions(d) == 1
     assert pkv.decode_workspace_bytes(d) == 64 * 32 * 1 * (128 + 2) * 4
     assert _attn_quant(d, 4, sink=FAKE.value, ntiles=3) == -4        # no workspace given
+
+
+def _attn_prefix(dims, starts=FAKE, blocks=FAKE, ws=None, ws_bytes=0):
+    lib = pkv.load_library()
+    return lib.pkv_paged_decode_attn_prefix(FAKE, FAKE, FAKE, starts, blocks, FAKE, FAKE,
+                                            ctypes.c_float(0.088), FAKE, ctypes.byref(dims), ws,
+                                            ws_bytes, None)
+
+
+def test_prefix_group_status_codes_and_plan():
+    # the MHA prefix batch: 64 sequences x 40 heads, one group sharing 75 blocks
+    ok = dict(num_seqs=64, num_q_heads=40, num_kv_heads=40, max_blocks_per_seq=100,
+              prefix_groups=1, prefix_max_seqs=64, prefix_max_blocks=75)
+    d = _dims(**ok)
+    # per-sequence pass: 1 piece; group pass: ~256 workgroups over 40 heads
+    # -> 7 pieces of 11 blocks; every row gets 1 + 7 workspace slots
+    assert pkv.decode_num_partitions(d) == 1
+    assert pkv.decode_workspace_bytes(d) == 64 * 40 * (1 + 7) * (128 + 2) * 4
+    assert _attn_prefix(d) == -4                                   # valid, but no workspace
+    assert _attn_prefix(d, starts=None) == -1
+    assert _attn_prefix(d, blocks=None) == -1
+    for bad in (dict(prefix_groups=-1), dict(prefix_max_seqs=0), dict(prefix_max_blocks=101),
+                dict(prefix_max_blocks=-1), dict(window=256), dict(sinks=4, sink_tiles=1),
+                dict(prefix_groups=65535, prefix_max_seqs=65)):    # grid z: 65535 x 2 chunks
+        assert _attn_prefix(_dims(**dict(ok, **bad))) == -2, bad
+    for dt in (dict(q_dtype=0, kv_dtype=0, out_dtype=0), dict(kv_dtype=3, q_dtype=2, out_dtype=2),
+               dict(kv_dtype=2)):
+        assert _attn_prefix(_dims(**dict(ok, **dt))) == -3, dt
+    # groups only through their own entry point
+    assert _attn(d) == -2
+    assert _attn_fp8(_dims(**dict(ok, kv_dtype=3, q_dtype=2, out_dtype=2))) == -2
+    assert _attn_quant(_dims(**dict(ok, kv_dtype=4, q_dtype=2, out_dtype=2)), 4) == -2
+    # no groups: the entry point behaves like pkv_paged_decode_attn (no split here)
+    d0 = _dims(**dict(ok, prefix_groups=0))
+    assert pkv.decode_workspace_bytes(d0) == 0
+    # more query rows than one chunk: the group pass needs no more slots
+    d8 = _dims(num_seqs=64, num_q_heads=64, num_kv_heads=8, max_blocks_per_seq=256,
+               prefix_groups=2, prefix_max_seqs=40, prefix_max_blocks=200)
+    # group pass: 2 groups x 8 heads x 5 chunks = 80 units -> 4 pieces of 50
+    assert pkv.decode_workspace_bytes(d8) == 64 * 64 * (1 + 4) * (128 + 2) * 4
 
 
 def test_append_quant_status_codes():

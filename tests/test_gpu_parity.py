@@ -13,7 +13,8 @@ import torch
 
 import oracle
 import paged_kv_cache_56_amd as pkv
-from workloads import WORKLOADS, DecodeWorkload, build_layout, make_host_inputs, make_device_inputs, scaled
+from workloads import (WORKLOADS, DecodeWorkload, build_layout, make_host_inputs, make_device_inputs, scaled,
+                       share_prefixes)
 from gpu_common import (TOL, say, host_storage, run_step, oracle_rows, oracle_append, oracle_attend,
                         host_layer, out_f64, max_err, err_beyond_rounding)
 
@@ -445,6 +446,81 @@ def test_balanced_plan_matches_oracle(name):
     assert np.isfinite(got).all() and err <= TOL[spec.kv_dtype]
 
 
+# Shared-prefix groups: (case, group starts, shared blocks per group).  The
+# ragged lengths are chosen so that every member extends past its group's
+# shared blocks; sequences after the last start belong to no group.
+GROUPED = {
+    "prefix_one_group_f16_g1": ("mha13b_prefix_small", None, None),
+    "prefix_groups_f16_g8_d128": (
+        _ragged("p1", "f16", "f16", "f16", 128, 8, [300, 200, 180, 50, 260, 90, 40, 20, 600, 17, 1, 33],
+                31, append=True),
+        [0, 3, 3, 6, 9], [10, 0, 2, 1]),
+    "prefix_groups_bf16_g4_d64": (
+        _ragged("p2", "bf16", "bf16", "bf16", 64, 4, [700, 650, 601, 599, 1000, 70, 35, 17, 16],
+                32, hkv=3),
+        [0, 4, 6], [37, 2]),
+    "prefix_two_chunks_f16_g8_d128": (       # 10 sequences x 8 heads = 80 query rows
+        _ragged("p3", "f16", "f16", "f16", 128, 8, [400 + 37 * i for i in range(10)] + [5, 300],
+                33, append=True),
+        [0, 10], [23]),
+    "prefix_groups_bf16_g2_d128_one_seq": (  # a one-sequence group and a 1-block group
+        _ragged("p4", "bf16", "bf16", "bf16", 128, 2, [90, 130, 33, 34, 18, 257], 34, hkv=4),
+        [0, 1, 2, 6], [5, 1, 1]),
+    "prefix_groups_f16_g1_d64": (
+        _ragged("p5", "f16", "f16", "f16", 64, 1, [130, 145, 161, 177, 193, 1], 35, hkv=5, append=True),
+        [0, 5, 5], [8, 0]),
+}
+
+
+def _grouped_layout(case):
+    src, starts, blocks = GROUPED[case]
+    spec = SMALL[src] if isinstance(src, str) else src
+    lay = build_layout(spec)
+    if starts is not None:
+        lay = share_prefixes(lay, starts, blocks)
+    return spec, lay
+
+
+@pytest.mark.parametrize("case", list(GROUPED))
+def test_prefix_groups_match_oracle(case):
+    """Shared prefixes read once per group (matrix-core pass) and merged with
+    each sequence's own blocks: the oracle's attention, which knows nothing
+    of groups, and the per-sequence path's result, to the same tolerance."""
+    spec, lay = _grouped_layout(case)
+    say(f"[groups] {case}: B={spec.num_seqs} g={spec.num_q_heads // spec.num_kv_heads} D={spec.head_dim} "
+        f"starts={list(lay.group_starts)} blocks={list(lay.group_blocks)} lens={list(lay.context_lens)}")
+    x = make_host_inputs(lay)
+    xs = _to_dev(x)
+    plain = _out(spec)
+    if not spec.append:
+        run_step(xs, 0, spec, plain)                     # the per-sequence path
+    grouped = _out(spec)
+    run_step(xs, 0, spec, grouped, grouped=True)
+    torch.cuda.synchronize()
+    got = out_f64(grouped)
+    ref = oracle_rows(host_layer(x, 0), lay, spec)
+    tol = TOL[spec.kv_dtype]
+    err = err_beyond_rounding(got, ref, spec.out_dtype)
+    say(f"    max|err| = {err:.3e} (tol {tol})")
+    assert np.isfinite(got).all() and err <= tol
+    assert (got[lay.context_lens == 0] == 0).all()
+    if not spec.append:                                  # same cache: the two paths agree
+        assert max_err(got, out_f64(plain)) <= tol
+
+
+def test_prefix_groups_deterministic():
+    spec, lay = _grouped_layout("prefix_groups_f16_g8_d128")
+    say("[groups] run-to-run")
+    xs = _to_dev(make_host_inputs(lay))
+    outs = []
+    for i in range(3):
+        o = _out(spec)
+        run_step(xs, 0, spec, o, append=(i == 0), grouped=True)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[1], outs[2])
+
+
 @pytest.mark.parametrize("pb", [1, 2, 3, 7])
 def test_split_size_invariance(pb):
     say(f"[split] tiny_f32 partition_blocks={pb}")
@@ -591,9 +667,11 @@ def _compact_rows(x, layer, lay, seqs):
     return h, tables, slots
 
 
-@pytest.mark.parametrize("name", ["llama3_8b_bf16", "mha13b_prefix_f16", "long_fp8", "llama70b_f16_80l",
-                                  "long_fp8k_int8v", "long_int8_kchan"])
+@pytest.mark.parametrize("name", ["llama3_8b_bf16", "mha13b_prefix_f16", "mha13b_prefix_f16:grouped", "long_fp8",
+                                  "llama70b_f16_80l", "long_fp8k_int8v", "long_int8_kchan"])
 def test_full_size_sampled_rows(name):
+    name, _, mode = name.partition(":")
+    grouped = mode == "grouped"
     spec = WORKLOADS[name]
     lay = build_layout(spec)
     say(f"[full] {name}: B={spec.num_seqs} layers={spec.num_layers} blocks={lay.num_blocks} "
@@ -607,7 +685,7 @@ def test_full_size_sampled_rows(name):
     outs = {}
     for layer in range(spec.num_layers):                               # the whole step
         out = _out(spec)
-        run_step(x, layer, spec, out)
+        run_step(x, layer, spec, out, grouped=grouped)
         if layer in snaps:
             outs[layer] = out
     torch.cuda.synchronize()

@@ -17,6 +17,7 @@ from .pool import BlockPool, PoolExhausted
 from .build import (
     DecodeLayout,
     build_layout,
+    share_prefixes,
     make_host_inputs,
     make_device_inputs,
     fp8_quantize_blocks,
@@ -35,6 +36,7 @@ __all__ = [
     "PoolExhausted",
     "DecodeLayout",
     "build_layout",
+    "share_prefixes",
     "make_host_inputs",
     "make_device_inputs",
     "fp8_quantize_blocks",

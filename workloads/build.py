@@ -25,6 +25,11 @@ Recipe (all seeded from the workload's seed):
     chosen at random, are 16x larger, in the history and in the new token
     alike; K then has per-channel factors c[h][d] (16 on those channels, 1
     elsewhere) that every K value is divided by before quantising;
+  * shared-prefix groups: a shared prefix makes one group of all sequences
+    (group_starts [0, B], group_blocks [prefix / 16]); share_prefixes()
+    rewrites a layout's tables into several groups, each member pointing
+    its first blocks at those of the group's first sequence, and releases
+    (poisons) the blocks that were replaced;
   * full-precision sinks (fp_sinks = S > 0): sequence b's first S positions
     live in side tile sink_tiles_of_seq[b] (a seeded permutation of the B
     tiles), in q's dtype, drawn N(0, 1) x 8 (sink tokens stand apart in
@@ -76,6 +81,11 @@ class DecodeLayout:
     refcount: np.ndarray            # int32 [num_blocks]
     seq_slots: list                 # per sequence: int64 [L] flat slot of every position,
                                     # in the order the pool handed them out
+    # shared-prefix groups: group g is the sequences [group_starts[g],
+    # group_starts[g + 1]), whose first group_blocks[g] table entries are the
+    # same physical blocks (None: no groups)
+    group_starts: Optional[np.ndarray] = None   # int32 [G + 1]
+    group_blocks: Optional[np.ndarray] = None   # int32 [G]
 
     @property
     def max_blocks_per_seq(self) -> int:
@@ -161,7 +171,50 @@ def build_layout(spec: DecodeWorkload) -> DecodeLayout:
         history_mask=history_mask,
         refcount=np.asarray(pool.refcount, dtype=np.int32),
         seq_slots=[np.asarray(seq_slots[b], dtype=np.int64) for b in range(B)],
+        group_starts=np.array([0, B], dtype=np.int32) if p else None,
+        group_blocks=np.array([p // bs], dtype=np.int32) if p else None,
     )
+
+
+def share_prefixes(layout: DecodeLayout, starts, blocks) -> DecodeLayout:
+    """A copy of `layout` in which the sequences of group g = [starts[g],
+    starts[g + 1]) all point their first blocks[g] table entries at the
+    blocks of the group's first sequence (a fork of that sequence's prefix).
+
+    The blocks the other members held there are released: no longer
+    history, so the tensors poison them.  Every member must keep at least
+    one private history position past the shared blocks (the new token then
+    never lands in a shared block).
+    """
+    bs = layout.spec.block_size
+    starts = np.asarray(starts, dtype=np.int32)
+    blocks = np.asarray(blocks, dtype=np.int32)
+    if starts.shape != (blocks.shape[0] + 1,) or (np.diff(starts) < 0).any():
+        raise ValueError("starts must be nondecreasing [G + 1], blocks [G]")
+    tables = layout.block_tables.copy()
+    mask = layout.history_mask.copy()
+    ref = layout.refcount.copy()
+    slots = [s.copy() for s in layout.seq_slots]
+    hist = layout.context_lens.astype(np.int64) - (1 if layout.slot_mapping is not None else 0)
+    for g in range(blocks.shape[0]):
+        s0, s1, n = int(starts[g]), int(starts[g + 1]), int(blocks[g])
+        for b in range(s0 + 1, s1):
+            if hist[b] <= n * bs or hist[s0] <= n * bs:
+                raise ValueError("a group member would not extend past the shared blocks")
+            for j in range(n):
+                old, new = int(tables[b, j]), int(tables[s0, j])
+                if old == new:
+                    continue
+                ref[old] -= 1
+                if ref[old] == 0:
+                    mask[old] = False
+                ref[new] += 1
+                tables[b, j] = new
+            slots[b][: n * bs] = slots[s0][: n * bs]
+    return DecodeLayout(spec=layout.spec, context_lens=layout.context_lens, block_tables=tables,
+                        num_blocks=layout.num_blocks, slot_mapping=layout.slot_mapping,
+                        history_mask=mask, refcount=ref, seq_slots=slots,
+                        group_starts=starts, group_blocks=blocks)
 
 
 # ---------------------------------------------------------------------------
@@ -292,6 +345,9 @@ def _make_inputs(layout: DecodeLayout, device: str, layers: Optional[int]) -> Di
         out["slot_mapping"] = torch.from_numpy(layout.slot_mapping).to(device)
     out["block_tables"] = torch.from_numpy(layout.block_tables).to(device)
     out["context_lens"] = torch.from_numpy(layout.context_lens).to(device)
+    if layout.group_starts is not None:
+        out["group_starts"] = torch.from_numpy(layout.group_starts).to(device)
+        out["group_blocks"] = torch.from_numpy(layout.group_blocks).to(device)
     return out
 
 
