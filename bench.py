@@ -326,12 +326,12 @@ def summarize_counters(fetch_csv, write_csv, stats_csv, workload, probe_gib, out
     return rec
 
 
-def summarize_trace(stats_csv, workload, out_md, command):
+def summarize_trace(stats_csv, workload, out_md, command, kernel=ATTN_KERNEL):
     """A rocprofv3 --kernel-trace --stats summary (top kernels) for one workload."""
     stats = _csv_rows(stats_csv)
     top = sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:8]
-    attn = [r for r in stats if ATTN_KERNEL in r["Name"]]
-    lines = [f"# {ATTN_KERNEL} on {workload}: rocprofv3 kernel trace", "",
+    attn = [r for r in stats if kernel in r["Name"]]
+    lines = [f"# {kernel} on {workload}: rocprofv3 kernel trace", "",
              "Command (run from the repository root on one MI355X, `export TMPDIR=/tmp`):", "",
              "```", *command, "```", "",
              "| kernel | calls | mean us | min us | max us | share |", "|---|---|---|---|---|---|"]
@@ -340,7 +340,7 @@ def summarize_trace(stats_csv, workload, out_md, command):
         name = name if len(name) < 90 else name[:87] + "..."
         lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
-    rec = {"workload": workload, "kernel": ATTN_KERNEL, "kernel_source_sha": kernel_source_sha(),
+    rec = {"workload": workload, "kernel": kernel, "kernel_source_sha": kernel_source_sha(),
            "trace_mean_launch_us": round(float(attn[0]["AverageNs"]) / 1e3, 2) if attn else None,
            "trace_calls": int(attn[0]["Calls"]) if attn else 0}
     lines += ["", "```json", json.dumps(rec, indent=1), "```"]
@@ -389,14 +389,17 @@ def main():
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "STATS_CSV"),
                     help="write profiles/decode_partition_kernel__<workload>.md from rocprofv3 output and exit")
     ap.add_argument("--summarize-trace", metavar="STATS_CSV",
-                    help="write profiles/decode_partition_kernel__<workload>__trace.md from a rocprofv3 "
+                    help="write profiles/<kernel>__<workload>__trace.md from a rocprofv3 "
                          "--kernel-trace --stats run and exit")
+    ap.add_argument("--trace-kernel", default=ATTN_KERNEL,
+                    help="kernel whose mean launch --summarize-trace records")
     ap.add_argument("--command", action="append", default=[],
                     help="(with --summarize-counters) a command line to record in the summary")
     args = ap.parse_args()
     if args.summarize_trace:
-        out = os.path.join(PROFILES, f"decode_partition_kernel__{args.workload}__trace.md")
-        print(json.dumps(summarize_trace(args.summarize_trace, args.workload, out, args.command)))
+        out = os.path.join(PROFILES, f"{args.trace_kernel.split('::')[-1]}__{args.workload}__trace.md")
+        print(json.dumps(summarize_trace(args.summarize_trace, args.workload, out, args.command,
+                                         args.trace_kernel)))
         return
     if args.summarize_counters:
         out = os.path.join(PROFILES, f"decode_partition_kernel__{args.workload}.md")

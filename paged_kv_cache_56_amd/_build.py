@@ -23,7 +23,7 @@ OBJ = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libpagedkv.so")
 SOURCES = ["api.cpp", "block_manager.cpp", "kv_append.hip", "decode_attn.hip", "hbm_probe.hip",
-           "copy_blocks.hip", "prefix_attn.hip"]
+           "copy_blocks.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -139,6 +139,10 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
     a.group_part_blocks = gpb;
     a.group_num_parts = gnp;
     a.group_qchunks = qchunks;
+    const int64_t gw = (int64_t)gnp * dims->num_kv_heads * dims->prefix_groups * qchunks;
+    const int64_t dw = (int64_t)np * dims->num_kv_heads * dims->num_seqs;
+    if (gw + dw > 0x7FFFFFFF) return PKV_ERR_SHAPE;   // one-dimensional grid
+    a.group_wgs = (int)gw;
   }
   a.window = dims->window;
   a.sinks = (dims->window > 0 || dims->sink_tiles) ? dims->sinks : 0;

@@ -54,6 +54,7 @@
 // the pool are treated as fully masked.  A window skips whole blocks: a
 // partition walks only the attended blocks (sink blocks, then window blocks).
 #include "pkv_internal.h"
+#include "group_prefix.h"
 
 #include <type_traits>
 #include <utility>
@@ -408,8 +409,10 @@ struct SeqSpan {
 };
 
 // ---------------------------------------------------------------------------
+// One workgroup of the cache pass: partition p of (sequence b, KV head h);
+// smem is the workgroup's LDS (Cfg::SMEM_B bytes).
 template <KV KT, KV VT, KV QT, KV OT, int D, int G>
-__global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, int b, char* smem) {
   static_assert(kv_bytes<KT>::value == kv_bytes<VT>::value, "K and V share the tile layout");
   static_assert(is_quantised<KT>() == is_quantised<VT>(), "8-bit K goes with 8-bit V");
   constexpr bool KQ = is_quantised<KT>();
@@ -422,29 +425,44 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
 
   // LDS: while streaming, per-wave rings of staged K and V tiles; at the end
   // of the partition the same bytes hold the per-wave partial results.
-  __shared__ __attribute__((aligned(16))) char smem[C::SMEM_B];
   float (*red_acc)[G][D] = reinterpret_cast<float (*)[G][D]>(smem);
   float (*red_m)[G] = reinterpret_cast<float (*)[G]>(smem + NW * G * D * 4);
   float (*red_l)[G] = reinterpret_cast<float (*)[G]>(smem + NW * G * D * 4 + NW * G * 4);
 
-  const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int Hq = a.num_kv_heads * G;
 
   // positions covered elsewhere (sink tiles, or a shared prefix read by the
   // group pass) are skipped here
+  const int pre = a.sink_tiles ? 0 : prefix_blocks_of_seq(a, b);
   const SeqSpan span(a.context_lens[b], a.max_blocks, a.window, a.sinks,
-                     a.sink_tiles ? a.sinks : 16 * prefix_blocks_of_seq(a, b));
+                     a.sink_tiles ? a.sinks : 16 * pre);
   // this partition: entries [j0, j1) of the sequence's attended-block list
   const SeqParts parts(span.natt, a.part_blocks, a.num_parts, p);
   const int j0 = parts.j0, j1 = parts.j1;
-  if (j0 >= j1) {
+
+  // Writes row (b, h*G + ha), channel d, from this partition's (m, l, o),
+  // o being the unnormalised sum.
+  auto finish = [&](int ha, int d, float m, float lsum, float o) __attribute__((always_inline)) {
+    const int64_t row = (int64_t)b * Hq + h * G + ha;
+    const float res = lsum > 0.f ? o / lsum : 0.f;
     if (!a.split) {
-      for (int idx = tid; idx < G * D; idx += 256)
-        store_out<OT>(a.out, ((int64_t)b * Hq + h * G) * D + idx, 0.f);
+      store_out<OT>(a.out, row * D + d, res);
+    } else {
+      a.o_part[(row * a.part_stride + p) * D + d] = res;
+      if (d == 0) {
+        a.ml_part[(row * a.part_stride + p) * 2 + 0] = m;
+        a.ml_part[(row * a.part_stride + p) * 2 + 1] = lsum;
+      }
     }
-    return;  // empty partitions of a split call are skipped by the merge
+  };
+  if (j0 >= j1) {
+    // nothing of the cache here: a zero row; empty partitions of a split
+    // call are skipped by the merge
+    if (!a.split)
+      for (int idx = tid; idx < G * D; idx += 256) finish(idx / D, idx % D, -INFINITY, 0.f, 0.f);
+    return;
   }
 
   // Register slot k = hs * TPL + i holds (query head hs ^ hmask, tile token
@@ -813,25 +831,40 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
       lsum += red_l[ww][ha] * f;
       o += red_acc[ww][ha][d] * f;
     }
-    const float res = lsum > 0.f ? o / lsum : 0.f;
-    const int64_t row = (int64_t)b * Hq + h * G + ha;
-    if (!a.split) {
-      store_out<OT>(a.out, row * D + d, res);
-    } else {
-      a.o_part[(row * a.part_stride + p) * D + d] = res;
-      if (d == 0) {
-        a.ml_part[(row * a.part_stride + p) * 2 + 0] = m;
-        a.ml_part[(row * a.part_stride + p) * 2 + 1] = lsum;
-      }
-    }
+    finish(ha, d, m, lsum, o);
+  }
+}
+
+template <KV KT, KV VT, KV QT, KV OT, int D, int G>
+__global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[Cfg<KT, D, G>::SMEM_B];
+  decode_body<KT, VT, QT, OT, D, G>(a, blockIdx.x, blockIdx.y, blockIdx.z, smem);
+}
+
+// Cache pass and shared-prefix group pass in one launch: the first
+// group_wgs workgroups run the group pass (matrix cores, latency-bound at
+// this size) while the rest stream the sequences' own blocks, so neither
+// waits for the other.  Both parts use the same LDS buffer.
+template <KV T, int D, int G>
+__global__ void __launch_bounds__(256) decode_group_kernel(DecodeArgs a) {
+  static_assert(Cfg<T, D, G>::SMEM_B >= GroupLds<D>::BYTES, "one LDS buffer serves both parts");
+  __shared__ __attribute__((aligned(16))) char smem[Cfg<T, D, G>::SMEM_B];
+  const int id = blockIdx.x;
+  if (id < a.group_wgs) {
+    const int pp = id % a.group_num_parts, rest = id / a.group_num_parts;
+    group_body<T, D>(a, pp, rest % a.num_kv_heads, rest / a.num_kv_heads, smem);
+  } else {
+    const int k = id - a.group_wgs;
+    const int p = k % a.num_parts, rest = k / a.num_parts;
+    decode_body<T, T, T, T, D, G>(a, p, rest % a.num_kv_heads, rest / a.num_kv_heads, smem);
   }
 }
 
 // Log-sum-exp merge of the partitions of one (sequence, query head) row.
 // Partition p carries o_p (its normalised output), m_p (log2 reference) and
 // l_p (sum of exp2(s - m_p)); out = sum_p l_p 2^(m_p - M) o_p / sum_p l_p 2^(m_p - M).
-// Only the partitions the cache pass wrote are read (the sequence's own
-// count).
+// Only the slots written for this row are read: the sequence's own
+// partitions, then the pieces of the shared-prefix group pass, if any.
 //
 // Full-precision sink tokens ("The KV Cache memory ledger" 7: attention-sink
 // tokens keep their original precision when the rest is quantised) join
@@ -884,27 +917,40 @@ __global__ void __launch_bounds__(64) lse_merge_kernel(DecodeArgs a) {
     }
   }
 
+  // One pass with a running reference (the sink term first): every
+  // partition joins as l_p 2^(m_p - M) o_p, the sum rescaled when M moves.
+  // Slots are read four at a time with unconditional loads (an index past
+  // the end re-reads the last slot and is then ignored), so their latencies
+  // overlap.
+  const int n = np + ng;
   float m = ls > 0.f ? ms : -INFINITY;
-  for (int i = 0; i < np + ng; ++i) {
-    const int p = i < np ? i : a.num_parts + (i - np);
-    if (ml[2 * p + 1] > 0.f) m = fmaxf(m, ml[2 * p]);
-  }
+  float wsum = ls > 0.f ? ls : 0.f;
   float o[PER];
-  float wsum = 0.f;
-  {
-    const float f = ls > 0.f ? __builtin_amdgcn_exp2f(ms - m) : 0.f;   // the sink term, unnormalised
-    wsum = ls * f;
 #pragma unroll
-    for (int k = 0; k < PER; ++k) o[k] = os[k] * f;
-  }
-  for (int i = 0; i < np + ng; ++i) {
-    const int p = i < np ? i : a.num_parts + (i - np);
-    const float lp = ml[2 * p + 1];
-    if (!(lp > 0.f)) continue;
-    const float wgt = lp * __builtin_amdgcn_exp2f(ml[2 * p] - m);
-    wsum += wgt;
+  for (int k = 0; k < PER; ++k) o[k] = ls > 0.f ? os[k] : 0.f;
+  constexpr int U = 4;
+  for (int i0 = 0; i0 < n; i0 += U) {
+    float mi[U], li[U], oi[U][PER];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) o[k] = __builtin_fmaf(wgt, op[(int64_t)p * D + k * 64 + lane], o[k]);
+    for (int u = 0; u < U; ++u) {
+      const int i = min(i0 + u, n - 1);
+      const int p = i < np ? i : a.num_parts + (i - np);
+      mi[u] = ml[2 * p];
+      li[u] = ml[2 * p + 1];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) oi[u][k] = op[(int64_t)p * D + k * 64 + lane];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i0 + u >= n || !(li[u] > 0.f)) continue;
+      const float mn = fmaxf(m, mi[u]);
+      const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+      const float g = li[u] * __builtin_amdgcn_exp2f(mi[u] - mn);
+      wsum = __builtin_fmaf(wsum, f, g);
+#pragma unroll
+      for (int k = 0; k < PER; ++k) o[k] = __builtin_fmaf(o[k], f, g * oi[u][k]);
+      m = mn;
+    }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
@@ -953,6 +999,28 @@ void plan_partitions(const pkv_decode_dims& d, int* part_blocks, int* num_parts)
   *num_parts = (maxb + pb - 1) / pb;
 }
 
+void plan_groups(const pkv_decode_dims& d, int* part_blocks, int* num_parts, int* qchunks) {
+  const int g = d.num_q_heads / d.num_kv_heads;
+  *qchunks = (int)(((int64_t)d.prefix_max_seqs * g + 63) / 64);
+  const int maxb = d.prefix_max_blocks < d.max_blocks_per_seq ? d.prefix_max_blocks
+                                                              : d.max_blocks_per_seq;
+  if (d.prefix_groups <= 0 || maxb <= 0) {
+    *part_blocks = 1;
+    *num_parts = 0;
+    return;
+  }
+  // About PKV_GROUP_WGS workgroups for the whole pass, never fewer than
+  // PKV_GROUP_MIN_PB blocks per piece: each piece adds a partial result per
+  // query row.
+  const int64_t units = (int64_t)d.prefix_groups * d.num_kv_heads * *qchunks;
+  const int64_t want = units >= PKV_GROUP_WGS ? 1 : (PKV_GROUP_WGS + units - 1) / units;
+  int pb = (int)((maxb + want - 1) / want);
+  if (pb < PKV_GROUP_MIN_PB) pb = PKV_GROUP_MIN_PB;
+  if (pb > maxb) pb = maxb;
+  *part_blocks = pb;
+  *num_parts = (maxb + pb - 1) / pb;
+}
+
 size_t workspace_bytes_for(const pkv_decode_dims& d) {
   int pb, np, gpb, gnp = 0, qc;
   plan_partitions(d, &pb, &np);
@@ -964,6 +1032,18 @@ size_t workspace_bytes_for(const pkv_decode_dims& d) {
 
 template <KV KT, KV VT, KV QT, KV OT, int D, int G>
 static int launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  constexpr bool plain16 = (KT == KV::F16 || KT == KV::BF16) && VT == KT && QT == KT && OT == KT;
+  if constexpr (plain16) {
+    if (a.group_wgs > 0) {
+      const int64_t n = (int64_t)a.group_wgs + (int64_t)a.num_parts * a.num_kv_heads * a.num_seqs;
+      hipLaunchKernelGGL((decode_group_kernel<KT, D, G>), dim3((unsigned)n), dim3(256), 0, stream, a);
+      if (hipGetLastError() != hipSuccess) return PKV_ERR_LAUNCH;
+      hipLaunchKernelGGL((lse_merge_kernel<QT, OT, D>), dim3(a.num_seqs * a.num_q_heads), dim3(64), 0,
+                         stream, a);
+      return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+    }
+  }
+  if (a.group_wgs > 0) return PKV_ERR_DTYPE;   // groups run with 16-bit caches only
   dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
   hipLaunchKernelGGL((decode_partition_kernel<KT, VT, QT, OT, D, G>), grid, dim3(256), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return PKV_ERR_LAUNCH;
@@ -996,10 +1076,6 @@ static int dispatch_d(const DecodeArgs& a, hipStream_t s) {
 }
 
 int launch_decode(const DecodeArgs& a, hipStream_t s) {
-  if (a.num_groups > 0) {
-    const int st = launch_group_prefix(a, s);   // before the merge that reads it
-    if (st != PKV_OK) return st;
-  }
   const KV kt = (KV)a.kv_dtype, vt = (KV)a.v_dtype, qt = (KV)a.q_dtype, ot = (KV)a.out_dtype;
   if (kt == KV::F32 || kt == KV::F16 || kt == KV::BF16) {
     if (vt != kt || qt != kt || ot != kt) return PKV_ERR_DTYPE;

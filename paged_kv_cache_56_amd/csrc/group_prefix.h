@@ -13,12 +13,16 @@
 // row) go to the workspace next to those of the per-sequence pass, which
 // skips the shared blocks, and the merge kernel combines both by log-sum-exp.
 //
-// Work split.  Grid = (piece p of the group's shared blocks, KV head h,
-// group x 64-row chunk of its queries).  Query row r of a group is sequence
-// s0 + r / g, query head h * g + r % g.  Each of the four waves owns 16 rows;
-// the workgroup stages 32 tokens (two blocks) of K and V in LDS per step:
-// K row-major, V transposed (column d holds the tokens), so that both
-// products read 16-byte operands.
+// Work split.  A workgroup takes (piece p of the group's shared blocks,
+// KV head h, 64-row chunk of the group's queries).  Query row r of a group
+// is sequence s0 + r / g, query head h * g + r % g.  Each of the four waves
+// owns 16 rows; the workgroup stages 32 tokens (two blocks) of K and V in
+// LDS per step: K row-major, V transposed (column d holds the tokens), so
+// that both products read 16-byte operands.  These workgroups lead the
+// launch of the per-sequence pass (decode_group_kernel): a piece is a chain
+// of dependent memory round trips (descriptor, table, tiles, one step after
+// another), which the other workgroups' streaming hides; pieces are long
+// (32 blocks or more) so that few partial results are written and merged.
 //
 // Orientation.  Scores are computed transposed, S^T = K Q^T (A = K tile,
 // B = Q^T), so the result leaves lane l with query l % 16 and tokens
@@ -30,14 +34,28 @@
 // leaves lane l with query l % 16, so the softmax rescale stays in-lane.
 //
 // Precision.  q, K and V are read as stored; products accumulate in fp32.
-// The probabilities are rounded once to the operand type (f16 or bf16) and
-// the running sum adds the rounded values, so the result is an exact convex
-// combination of V rows with weights off by at most half an ulp of that
-// type.
+// The probabilities exp2(s - m) (m: a reference at most 8 below the largest
+// score so far, so they stay <= 256) are rounded once to the operand type
+// (f16 or bf16), and the running sum adds the rounded values, so the result
+// is an exact convex combination of V rows with weights off by at most half
+// an ulp of that type.
+#pragma once
+
 #include "pkv_internal.h"
 
+// Loads in flight per workgroup (32-token steps), and the split plan: about
+// PKV_GROUP_WGS workgroups, pieces of at least PKV_GROUP_MIN_PB blocks.
+#ifndef PKV_GROUP_PF
+#define PKV_GROUP_PF 1
+#endif
+#ifndef PKV_GROUP_WGS
+#define PKV_GROUP_WGS 256
+#endif
+#ifndef PKV_GROUP_MIN_PB
+#define PKV_GROUP_MIN_PB 32
+#endif
+
 namespace pkv {
-namespace {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -75,20 +93,28 @@ __device__ __forceinline__ int vt_col(int t) {
   return ((t & 15) >> 2) * 8 + (t >> 4) * 4 + (t & 3);
 }
 
+// LDS of one group workgroup: the K tile of a step, then the transposed V tile.
+template <int D> struct GroupLds {
+  static constexpr int KS = D + 8;     // K tile row stride (elements)
+  static constexpr int VS = 40;        // transposed V tile row stride (elements)
+  static constexpr int BYTES = (32 * KS + D * VS) * 2;
+};
+
+// One workgroup of the group pass: piece pp of the shared blocks of group
+// z / group_qchunks, KV head h, query chunk z % group_qchunks; smem holds
+// at least GroupLds<D>::BYTES bytes.
 template <KV T, int D>
-__global__ void __launch_bounds__(256) group_prefix_kernel(DecodeArgs a) {
-  constexpr int KS = D + 8;            // K tile row stride in LDS (elements)
-  constexpr int VS = 40;               // transposed V tile row stride (elements)
+__device__ __forceinline__ void group_body(const DecodeArgs& a, int pp, int h, int z, char* smem) {
+  constexpr int KS = GroupLds<D>::KS, VS = GroupLds<D>::VS;
   constexpr int CH = D / 8;            // 16-byte chunks per token row
   constexpr int NL = 32 * CH / 256;    // chunks per thread per 32-token step
   constexpr int KK = D / 32;           // contraction steps over the head dimension
   constexpr int DT = D / 16;           // 16-channel output tiles
   static_assert(NL >= 1 && 32 * CH == 256 * NL, "whole chunks per thread");
-  __shared__ __attribute__((aligned(16))) uint16_t ks[32 * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[D * VS];
+  uint16_t* ks = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* vt = ks + 32 * KS;
 
-  const int qc = blockIdx.z % a.group_qchunks, g = blockIdx.z / a.group_qchunks;
-  const int h = blockIdx.y, pp = blockIdx.x;
+  const int qc = z % a.group_qchunks, g = z / a.group_qchunks;
   const PrefixGroup pg = prefix_group(a, g);
   const int gq = a.num_q_heads / a.num_kv_heads;
   const int nrows = pg.nseq * gq;
@@ -116,55 +142,67 @@ __global__ void __launch_bounds__(256) group_prefix_kernel(DecodeArgs a) {
   }
 
   const int32_t* table = a.block_tables + (int64_t)pg.s0 * a.max_blocks;
-  auto block_ok = [&](int j) __attribute__((always_inline)) {
-    return j < parts.j1 && (unsigned)table[j] < (unsigned)a.num_blocks;
-  };
 
-  // staging: chunk c = tid + 256*e is token c % 32, channels (c / 32)*8 .. +7
-  u32x4_t kreg[NL], vreg[NL];
-  auto load_step = [&](int j) __attribute__((always_inline)) {
+  // Staging: chunk c = tid + 256*e is token c % 32, channels (c / 32)*8 .. +7
+  // of a step: the 32 lanes that write one channel octet of the transposed
+  // V tile then cover one LDS row, free of bank conflicts (a wave's load
+  // still reads 32-byte runs of 32 token rows).  PF steps of loads are in flight in a register ring.  Loads
+  // are never conditional (a missing block reads block 0, a step past the
+  // end re-reads the last one) so the compiler's waits stay exact; missing
+  // blocks turn into zeros when the ring slot is written to LDS.
+  constexpr int PF = PKV_GROUP_PF;
+  const int nsteps = (parts.j1 - parts.j0 + 1) >> 1;
+  // A ring slot also carries its step's block validity (bit 0: first
+  // block, bit 1: second), taken when its table entries are read, so that
+  // no table read (a scalar load, counted with the LDS reads) sits in the
+  // compute.
+  u32x4_t kreg[PF][NL], vreg[PF][NL];
+  int okb[PF];
+  auto load_step = [&](int i, u32x4_t (&kr)[NL], u32x4_t (&vr)[NL], int& ok) __attribute__((always_inline)) {
+    const int j = parts.j0 + 2 * min(i, nsteps - 1);
     const int ph0 = table[j];
     const int ph1 = j + 1 < parts.j1 ? table[j + 1] : -1;
+    ok = ((unsigned)ph0 < (unsigned)a.num_blocks ? 1 : 0) | ((unsigned)ph1 < (unsigned)a.num_blocks ? 2 : 0);
 #pragma unroll
     for (int e = 0; e < NL; ++e) {
       const int c = tid + 256 * e, t = c & 31, col = c >> 5;
-      const int ph = t < 16 ? ph0 : ph1;
-      if ((unsigned)ph < (unsigned)a.num_blocks) {
-        const int64_t off = (((int64_t)ph * a.num_kv_heads + h) * 16 + (t & 15)) * D + col * 8;
-        kreg[e] = *(const u32x4_t*)((const uint16_t*)a.k_cache + off);
-        vreg[e] = *(const u32x4_t*)((const uint16_t*)a.v_cache + off);
-      } else {
-        kreg[e] = u32x4_t{0u, 0u, 0u, 0u};   // missing block: zeros, never NaN
-        vreg[e] = u32x4_t{0u, 0u, 0u, 0u};
-      }
+      int ph = t < 16 ? ph0 : ph1;
+      ph = (unsigned)ph < (unsigned)a.num_blocks ? ph : 0;
+      const int64_t off = (((int64_t)ph * a.num_kv_heads + h) * 16 + (t & 15)) * D + col * 8;
+      kr[e] = *(const u32x4_t*)((const uint16_t*)a.k_cache + off);
+      vr[e] = *(const u32x4_t*)((const uint16_t*)a.v_cache + off);
     }
   };
-  auto store_step = [&]() __attribute__((always_inline)) {
+  auto store_step = [&](int ok, const u32x4_t (&kr)[NL], const u32x4_t (&vr)[NL]) __attribute__((always_inline)) {
+    const bool ok0 = ok & 1, ok1 = ok & 2;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < NL; ++e) {
       const int c = tid + 256 * e, t = c & 31, col = c >> 5;
-      *(u32x4_t*)&ks[t * KS + col * 8] = kreg[e];
+      const bool ok = t < 16 ? ok0 : ok1;            // a missing block: zeros, never NaN
+      *(u32x4_t*)&ks[t * KS + col * 8] = ok ? kr[e] : zero;
+      const u32x4_t v = ok ? vr[e] : zero;
       const int vc = vt_col(t);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        vt[(col * 8 + 2 * k) * VS + vc] = (uint16_t)(vreg[e][k] & 0xFFFFu);
-        vt[(col * 8 + 2 * k + 1) * VS + vc] = (uint16_t)(vreg[e][k] >> 16);
+        vt[(col * 8 + 2 * k) * VS + vc] = (uint16_t)(v[k] & 0xFFFFu);
+        vt[(col * 8 + 2 * k + 1) * VS + vc] = (uint16_t)(v[k] >> 16);
       }
     }
   };
 
+  // Online softmax with a lazily moved reference: probabilities are
+  // exp2(s - m) with m shared by the four lanes of a query, and m moves
+  // (one cross-lane max, one rescale of the sums) only when a score passes
+  // it by more than 2^8 -- on the first scores, and rarely after.  A lane
+  // keeps the sum of its own probabilities; the four are added at the end.
+  constexpr float SLACK = 8.f;           // log2 units: probabilities stay <= 256
   float m = -INFINITY, l = 0.f;
   f32x4_t acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  load_step(parts.j0);
-  for (int j = parts.j0; j < parts.j1; j += 2) {
-    __syncthreads();                     // the previous step's LDS reads are done
-    store_step();
-    __syncthreads();
-    if (j + 2 < parts.j1) load_step(j + 2);
-    if (!wave_on) continue;
+  auto compute_step = [&](int j, int ok) __attribute__((always_inline)) {
 
     // S^T tiles: lane holds (token 16*tt + 4*lg + i, query lq) in s[tt][i]
     f32x4_t s[2];
@@ -172,12 +210,10 @@ __global__ void __launch_bounds__(256) group_prefix_kernel(DecodeArgs a) {
     for (int tt = 0; tt < 2; ++tt) {
       s[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const u32x4_t ka = *(const u32x4_t*)&ks[(tt * 16 + lq) * KS + kk * 32 + 8 * lg];
-        s[tt] = Mma<T>::run(ka, qf[kk], s[tt]);
-      }
+      for (int kk = 0; kk < KK; ++kk)
+        s[tt] = Mma<T>::run(*(const u32x4_t*)&ks[(tt * 16 + lq) * KS + kk * 32 + 8 * lg], qf[kk], s[tt]);
     }
-    const bool ok0 = block_ok(j), ok1 = block_ok(j + 1);
+    const bool ok0 = ok & 1, ok1 = ok & 2;
     float sv[8];
     float mx = -INFINITY;
 #pragma unroll
@@ -189,35 +225,58 @@ __global__ void __launch_bounds__(256) group_prefix_kernel(DecodeArgs a) {
         sv[tt * 4 + i] = ok ? s[tt][i] * a.scale : -INFINITY;   // log2 units
         mx = fmaxf(mx, sv[tt * 4 + i]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(m, mx);
-    const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+    if (__builtin_amdgcn_ballot_w64(mx > m + SLACK)) {         // uniform over the wave
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m, mx);
+      const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+      m = mn;
+    }
 
     // B operand of O^T = V^T P^T: the lane's 8 tokens of query lq, rounded
     uint32_t pw[4];
-    float ps = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       float r0, r1;
-      const float p0 = sv[2 * k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[2 * k] - mn);
-      const float p1 = sv[2 * k + 1] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[2 * k + 1] - mn);
+      const float p0 = sv[2 * k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[2 * k] - m);
+      const float p1 = sv[2 * k + 1] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[2 * k + 1] - m);
       pw[k] = Mma<T>::round(p0, &r0) | (Mma<T>::round(p1, &r1) << 16);
-      ps += r0 + r1;
+      l += r0 + r1;
     }
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
-    l = l * alpha + ps;
-    m = mn;
     const u32x4_t pb = {pw[0], pw[1], pw[2], pw[3]};
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const u32x4_t va = *(const u32x4_t*)&vt[(dt * 16 + lq) * VS + 8 * lg];
-      acc[dt] = Mma<T>::run(va, pb, acc[dt] * alpha);
-    }
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = Mma<T>::run(*(const u32x4_t*)&vt[(dt * 16 + lq) * VS + 8 * lg], pb, acc[dt]);
+  };
+
+  // step i uses ring slot i % PF and refills it with step i + PF
+  auto step = [&](int i, u32x4_t (&kr)[NL], u32x4_t (&vr)[NL], int& okr) __attribute__((always_inline)) {
+    const int j = parts.j0 + 2 * i;
+    const int ok = okr;
+    __syncthreads();                      // the previous step's LDS reads are done
+    store_step(ok, kr, vr);
+    __syncthreads();
+    load_step(i + PF, kr, vr, okr);
+    if (wave_on) compute_step(j, ok);
+  };
+#pragma unroll
+  for (int s = 0; s < PF; ++s) load_step(s, kreg[s], vreg[s], okb[s]);
+  // whole rounds of PF steps carry no conditions, so every wait for a ring
+  // slot leaves the PF - 1 younger slots in flight
+  int i0 = 0;
+  for (; i0 + PF <= nsteps; i0 += PF) {
+#pragma unroll
+    for (int s = 0; s < PF; ++s) step(i0 + s, kreg[s], vreg[s], okb[s]);
   }
+#pragma unroll
+  for (int s = 0; s < PF - 1; ++s)
+    if (i0 + s < nsteps) step(i0 + s, kreg[s], vreg[s], okb[s]);   // uniform over the workgroup
 
   // partial result of this piece: lane holds channels dt*16 + 4*lg + 0..3
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
   if (wave_on && rv) {
     const int64_t slot =
         ((int64_t)b * a.num_q_heads + head) * a.part_stride + a.num_parts + pp;
@@ -230,48 +289,6 @@ __global__ void __launch_bounds__(256) group_prefix_kernel(DecodeArgs a) {
       a.ml_part[slot * 2 + 1] = l;
     }
   }
-}
-
-template <KV T>
-int launch_t(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(a.group_num_parts, a.num_kv_heads, a.num_groups * a.group_qchunks);
-  if (a.head_dim == 128)
-    hipLaunchKernelGGL((group_prefix_kernel<T, 128>), grid, dim3(256), 0, s, a);
-  else if (a.head_dim == 64)
-    hipLaunchKernelGGL((group_prefix_kernel<T, 64>), grid, dim3(256), 0, s, a);
-  else
-    return PKV_ERR_SHAPE;
-  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
-}
-
-}  // namespace
-
-void plan_groups(const pkv_decode_dims& d, int* part_blocks, int* num_parts, int* qchunks) {
-  const int g = d.num_q_heads / d.num_kv_heads;
-  *qchunks = (int)(((int64_t)d.prefix_max_seqs * g + 63) / 64);
-  const int maxb = d.prefix_max_blocks < d.max_blocks_per_seq ? d.prefix_max_blocks
-                                                              : d.max_blocks_per_seq;
-  if (d.prefix_groups <= 0 || maxb <= 0) {
-    *part_blocks = 1;
-    *num_parts = 0;
-    return;
-  }
-  // About 256 workgroups (one per CU) for the whole pass, never fewer than
-  // 8 blocks per piece: each piece adds a partial result per query row.
-  const int64_t units = (int64_t)d.prefix_groups * d.num_kv_heads * *qchunks;
-  const int64_t want = units >= 256 ? 1 : (256 + units - 1) / units;
-  int pb = (int)((maxb + want - 1) / want);
-  if (pb < 8) pb = 8;
-  if (pb > maxb) pb = maxb;
-  *part_blocks = pb;
-  *num_parts = (maxb + pb - 1) / pb;
-}
-
-int launch_group_prefix(const DecodeArgs& a, hipStream_t s) {
-  if (a.num_groups <= 0 || a.group_num_parts <= 0) return PKV_OK;
-  if (a.kv_dtype == (int)KV::F16) return launch_t<KV::F16>(a, s);
-  if (a.kv_dtype == (int)KV::BF16) return launch_t<KV::BF16>(a, s);
-  return PKV_ERR_DTYPE;
 }
 
 }  // namespace pkv

@@ -65,6 +65,9 @@ struct DecodeArgs {
   int num_groups, group_max_seqs, group_max_blocks;
   int group_part_blocks, group_num_parts;   // split of a group's shared blocks
   int group_qchunks;                        // 64-row chunks of a group's queries
+  // workgroups of the group pass (0: none); they lead the combined launch
+  // and write workspace slots [num_parts, part_stride) of their rows
+  int group_wgs;
 };
 
 // A list of `natt` blocks uses min(ceil(natt / T), P) of P pieces, cut
@@ -117,9 +120,6 @@ void plan_groups(const pkv_decode_dims& d, int* part_blocks, int* num_parts, int
 size_t workspace_bytes_for(const pkv_decode_dims& d);
 
 int launch_decode(const DecodeArgs& a, hipStream_t stream);
-// the shared-prefix pass (F16 or BF16 throughout); writes its partial
-// results into workspace slots [num_parts, part_stride) of each row
-int launch_group_prefix(const DecodeArgs& a, hipStream_t stream);
 
 int launch_hbm_read(const void* buf, size_t bytes, uint32_t* sink, int sink_words,
                     hipStream_t stream);

@@ -152,10 +152,10 @@ def test_prefix_group_status_codes_and_plan():
     ok = dict(num_seqs=64, num_q_heads=40, num_kv_heads=40, max_blocks_per_seq=100,
               prefix_groups=1, prefix_max_seqs=64, prefix_max_blocks=75)
     d = _dims(**ok)
-    # per-sequence pass: 1 piece; group pass: ~256 workgroups over 40 heads
-    # -> 7 pieces of 11 blocks; every row gets 1 + 7 workspace slots
+    # per-sequence pass: 1 piece; group pass: pieces of at least 32 blocks
+    # -> 3 pieces of 25; every row gets 1 + 3 workspace slots
     assert pkv.decode_num_partitions(d) == 1
-    assert pkv.decode_workspace_bytes(d) == 64 * 40 * (1 + 7) * (128 + 2) * 4
+    assert pkv.decode_workspace_bytes(d) == 64 * 40 * (1 + 3) * (128 + 2) * 4
     assert _attn_prefix(d) == -4                                   # valid, but no workspace
     assert _attn_prefix(d, starts=None) == -1
     assert _attn_prefix(d, blocks=None) == -1
@@ -176,7 +176,8 @@ def test_prefix_group_status_codes_and_plan():
     # more query rows than one chunk: the group pass needs no more slots
     d8 = _dims(num_seqs=64, num_q_heads=64, num_kv_heads=8, max_blocks_per_seq=256,
                prefix_groups=2, prefix_max_seqs=40, prefix_max_blocks=200)
-    # group pass: 2 groups x 8 heads x 5 chunks = 80 units -> 4 pieces of 50
+    # group pass: 2 groups x 8 heads x 5 chunks = 80 units -> ~256 workgroups
+    # would take 4 pieces of 50 blocks (above the 32-block floor)
     assert pkv.decode_workspace_bytes(d8) == 64 * 64 * (1 + 4) * (128 + 2) * 4
 
 
