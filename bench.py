@@ -227,16 +227,27 @@ def copy_blocks_rate(x, spec, pairs: int):
             "gbs": round(moved / s / 1e9, 1)}
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace collapsed, so that
+    comment edits do not count as kernel changes."""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_sha() -> str:
-    """sha256 over the HIP sources and headers the library is built from."""
+    """sha256 over the code (comments dropped) of the HIP sources and headers
+    the library is built from."""
     import hashlib
 
     h = hashlib.sha256()
     for fn in sorted(os.listdir(CSRC)):
         if fn.endswith((".hip", ".h", ".cpp")):
             h.update(fn.encode())
-            h.update(open(os.path.join(CSRC, fn), "rb").read())
-    h.update(open(os.path.join(ROOT, "include", "pagedkv.h"), "rb").read())
+            h.update(_code_only(open(os.path.join(CSRC, fn)).read()).encode())
+    h.update(_code_only(open(os.path.join(ROOT, "include", "pagedkv.h")).read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,4 +1,6 @@
-// Paged decode attention for gfx950 (CDNA4, wave64), no MFMA.
+// Paged decode attention for gfx950 (CDNA4, wave64).  The per-sequence pass
+// below uses no MFMA; the shared-prefix group pass (group_prefix.h), which
+// it can carry in the same launch, does.
 //
 // What is computed ("KV Cache from first principles" 2.1-2.2 and 4.3; "The
 // KV Cache memory ledger" 2 and 4): for every sequence b and query head i,
