@@ -393,6 +393,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="0 skips the CPU baseline")
     ap.add_argument("--copy-pairs", type=int, default=0,
                     help="also time copy-on-write copies of this many random block pairs")
+    ap.add_argument("--event-stride", type=int, default=8,
+                    help="bracket every N-th attention launch with HIP events (1 = all)")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="append with its own launch instead of inside the attention launch")
     ap.add_argument("--no-groups", action="store_true",
                     help="attend shared prefixes per sequence instead of once per group")
     ap.add_argument("--no-probe", action="store_true",
@@ -468,6 +472,8 @@ def main():
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     chan = x.get("k_channel_scales")
     both_fp8 = spec.kv_dtype == spec.v_tag == "fp8_e4m3" and chan is None and not spec.fp_sinks
+    # 16-bit and f32 caches: the append rides in the attention launch
+    fused = spec.append and not spec.quantised and not spec.fp_sinks and not grouped and not args.separate_append
 
     def step(ev=None):
         for layer in range(nl):
@@ -490,23 +496,34 @@ def main():
                 pkv.kv_append_quant(x["k_new"][layer], x["slot_mapping"], kc, kw["k_scales"],
                                     channel_scales=chan)
                 pkv.kv_append_quant(x["v_new"][layer], x["slot_mapping"], vc, kw["v_scales"])
-            elif spec.append:
+            elif spec.append and not fused:
                 pkv.kv_append(x["k_new"][layer], x["v_new"][layer], x["slot_mapping"], kc, vc)
-            if ev is not None:
+            if ev is not None and layer in ev:
                 ev[layer][0].record()
-            pkv.paged_decode_attn(x["q"][layer], kc, vc, x["block_tables"], x["context_lens"],
-                                  spec.scale, outs[layer], workspace=ws,
-                                  partition_blocks=args.partition_blocks, window=args.window,
-                                  sinks=args.sinks, total_blocks=total_blocks, **kw, **gkw)
-            if ev is not None:
+            if fused:
+                pkv.paged_decode_step(x["k_new"][layer], x["v_new"][layer], x["slot_mapping"], x["q"][layer],
+                                      kc, vc, x["block_tables"], x["context_lens"], spec.scale, outs[layer],
+                                      workspace=ws, partition_blocks=args.partition_blocks,
+                                      window=args.window, sinks=args.sinks, total_blocks=total_blocks)
+            else:
+                pkv.paged_decode_attn(x["q"][layer], kc, vc, x["block_tables"], x["context_lens"],
+                                      spec.scale, outs[layer], workspace=ws,
+                                      partition_blocks=args.partition_blocks, window=args.window,
+                                      sinks=args.sinks, total_blocks=total_blocks, **kw, **gkw)
+            if ev is not None and layer in ev:
                 ev[layer][1].record()
 
     log(f"[bench] warmup {args.warmup} steps (partitions per sequence: {nparts})")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nl)]
-              for _ in range(args.steps)]
+    # HIP events bracket a sample of the launches (every event_stride-th,
+    # rotating over layers): each event is a packet the command processor
+    # handles between kernels, so bracketing all of them would lengthen the
+    # step that `value` is computed from.
+    stride = max(1, args.event_stride)
+    events = [{layer: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for layer in range(nl) if (k + layer) % stride == 0} for k in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -515,10 +532,13 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    launch_ms = np.array([[e[0].elapsed_time(e[1]) for e in row] for row in events])
+    launch_ms = np.array([e[0].elapsed_time(e[1]) for row in events for e in row.values()])
     mean_launch_s = float(launch_ms.mean()) / 1e3
 
     kv_bytes, alg_bytes, logical_bytes = attention_bytes(spec, lay, args.window, args.sinks)
+    if fused:
+        # the launch also reads each new K/V row and writes it to its slot
+        alg_bytes += 4 * spec.num_seqs * spec.num_kv_heads * spec.head_dim * ELT[spec.kv_dtype]
     value = kv_bytes * nl / (ms_per_step / 1e3) / 1e9
     achieved = alg_bytes / mean_launch_s / 1e9
     kernel = ("group_prefix_kernel+" if grouped else "") + "decode_partition_kernel" + (
@@ -570,6 +590,7 @@ def main():
             "sinks": args.sinks if (args.window > 0 or spec.fp_sinks) else 0,
             "fp_sinks": spec.fp_sinks,
             "prefix_groups": len(lay.group_blocks) if grouped else 0,
+            "append": ("in the attention launch" if fused else "own launch") if spec.append else "none",
             "kv_bytes_per_step": kv_bytes * nl,
             "logical_kv_bytes_per_step": logical_bytes * nl,
         },
@@ -583,6 +604,7 @@ def main():
             "traffic": traffic,
             "bytes_per_launch": alg_bytes,
             "mean_launch_us": round(mean_launch_s * 1e6, 2),
+            "launches_timed": int(launch_ms.size),
             "traffic_over_algorithmic": None if traffic is None else round(traffic / alg_bytes, 4),
             "kernel_source_sha": kernel_source_sha(),
             "read_probe_gbs": None if probe is None else round(probe["gbs"], 1),

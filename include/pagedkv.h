@@ -55,7 +55,7 @@ extern "C" {
 #define PKV_API
 #endif
 
-#define PKV_VERSION 140  /* 1.4.0 */
+#define PKV_VERSION 150  /* 1.5.0 */
 #define PKV_BLOCK_SIZE 16
 
 typedef enum {
@@ -253,6 +253,27 @@ PKV_API int pkv_paged_decode_attn_quant(const void* q, const void* k_cache, cons
                                         const int32_t* context_lens, float scale, void* out,
                                         const pkv_decode_dims* dims, void* workspace,
                                         size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One decode step in one launch: pkv_kv_append of each sequence's new token
+ * followed by pkv_paged_decode_attn ("KV Cache from first principles" 2.2-2.3:
+ * the new token's K and V are written at the current length, which then
+ * counts it, and the new query attends to every cached position, its own
+ * included).  Results and cache contents equal those of the two calls.
+ *   k_new, v_new: [num_seqs][num_kv_heads][head_dim] of the caches' dtype:
+ *     token b is sequence b's new token;
+ *   slot_mapping: int64 [num_seqs], the slot of sequence b's position
+ *     context_lens[b] - 1 (its last), or -1 for no new token; slots outside
+ *     the pool are skipped.  A slot elsewhere in the sequence gives
+ *     undefined results (its block may be read before it is written).
+ * Caches F32, F16 or BF16 (q, caches and out of one type, as for
+ * pkv_paged_decode_attn); no sink tiles or prefix groups.
+ */
+PKV_API int pkv_paged_decode_step(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                                  const void* q, void* k_cache, void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  float scale, void* out, const pkv_decode_dims* dims,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Decode attention for batches whose sequences share prefix blocks ("The KV

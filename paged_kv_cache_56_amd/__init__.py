@@ -9,6 +9,9 @@ carry device memory and streams.
     kv_append(k_new, v_new, slot_mapping, k_cache, v_cache)
     kv_append_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scales, v_scales)
     kv_append_quant(x_new, slot_mapping, cache, scales, channel_scales=None)
+    paged_decode_step(k_new, v_new, slot_mapping, q, k_cache, v_cache, block_tables,
+                      context_lens, scale, out, workspace=None, partition_blocks=0,
+                      window=0, sinks=0, total_blocks=0)
     paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, scale, out,
                       k_scales=None, v_scales=None, k_channel_scales=None,
                       sink_k=None, sink_v=None, sink_tiles_of_seq=None,
@@ -35,6 +38,7 @@ __all__ = [
     "copy_blocks",
     "BlockManager",
     "paged_decode_attn",
+    "paged_decode_step",
     "decode_dims",
     "decode_workspace_bytes",
     "decode_num_partitions",
@@ -137,6 +141,9 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_paged_decode_attn_quant.argtypes = [vp, vp, vp, ctypes.POINTER(QuantParams), vp, vp,
                                                 ctypes.c_float, vp, dims_p, vp, sz, vp]
     lib.pkv_paged_decode_attn_quant.restype = ctypes.c_int
+    lib.pkv_paged_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp,
+                                          sz, vp]
+    lib.pkv_paged_decode_step.restype = ctypes.c_int
     lib.pkv_paged_decode_attn_prefix.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
                                                  dims_p, vp, sz, vp]
     lib.pkv_paged_decode_attn_prefix.restype = ctypes.c_int
@@ -498,4 +505,40 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                                            _ptr(context_lens), float(scale), _ptr(out),
                                            ctypes.byref(dims), ws_ptr, ws_bytes, _stream(q))
     _check(st)
+    return out
+
+
+def paged_decode_step(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                      q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                      out: torch.Tensor, *, workspace: Optional[torch.Tensor] = None,
+                      partition_blocks: int = 0, window: int = 0, sinks: int = 0,
+                      total_blocks: int = 0) -> torch.Tensor:
+    """kv_append of each sequence's new token, then paged_decode_attn, in one launch.
+
+    k_new, v_new: [B, Hkv, D] (row b is sequence b's new token); slot_mapping:
+    int64 [B], the slot of sequence b's last position (-1: none).  Caches and
+    q/out f32, f16 or bf16 of one type.  Returns `out`.
+    """
+    lib = load_library()
+    _dev(k_new, v_new, slot_mapping, q, k_cache, v_cache, block_tables, context_lens, out, workspace)
+    _need(q.dim() == 3 and out.shape == q.shape, "q and out must be [B, Hq, D]")
+    _need(k_cache.shape == v_cache.shape and k_cache.dim() == 4, "caches must be [NB, Hkv, 16, D]")
+    B = q.shape[0]
+    _need(k_new.shape == v_new.shape == (B, k_cache.shape[1], k_cache.shape[3]),
+          "k_new/v_new must be [B, Hkv, D]")
+    _need(k_new.dtype == v_new.dtype == k_cache.dtype == v_cache.dtype, "dtype mismatch")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (B,), "slot_mapping must be int64 [B]")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == B,
+          "block_tables must be int32 [B, max_blocks]")
+    _need(context_lens.dtype == torch.int32 and context_lens.shape == (B,), "context_lens must be int32 [B]")
+    dims = decode_dims(q, k_cache, block_tables, out, partition_blocks, window, sinks, False, total_blocks)
+    need = decode_workspace_bytes(dims)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _ptr(workspace) if need else None
+    ws_bytes = workspace.numel() * workspace.element_size() if (need and workspace is not None) else 0
+    _check(lib.pkv_paged_decode_step(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(q), _ptr(k_cache),
+                                     _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), float(scale),
+                                     _ptr(out), ctypes.byref(dims), ws_ptr, ws_bytes, _stream(q)))
     return out

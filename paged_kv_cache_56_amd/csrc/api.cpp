@@ -75,13 +75,27 @@ struct GroupPtrs {
   const int32_t* blocks;
 };
 
+// The step's append carried by the attention launch (pkv_paged_decode_step).
+struct StepAppend {
+  const void* k_new;
+  const void* v_new;
+  const int64_t* slots;
+  void* k_cache;
+  void* v_cache;
+};
+
 // qp: the 8-bit arguments (NULL for the f32/f16/bf16 entry points).
 int decode_common(const void* q, const void* k_cache, const void* v_cache, const pkv_quant_params* qp,
                   const GroupPtrs* gp, const int32_t* block_tables, const int32_t* context_lens,
                   float scale, void* out, const pkv_decode_dims* dims, void* workspace,
-                  size_t workspace_bytes, hipStream_t stream) {
+                  size_t workspace_bytes, hipStream_t stream, const StepAppend* ap = nullptr) {
   int st = check_dims(dims);
   if (st) return st;
+  if (ap) {
+    if (qp || gp || dims->sink_tiles) return PKV_ERR_SHAPE;   // 16-bit and f32 caches, no groups
+    if (is_q8(dims->kv_dtype)) return PKV_ERR_DTYPE;
+    if (!ap->k_new || !ap->v_new || !ap->slots) return PKV_ERR_NULL;
+  }
   if (!gp && dims->prefix_groups != 0) return PKV_ERR_SHAPE;   // groups: the _prefix entry point
   if (gp) {
     if (dims->prefix_groups > 0 && (!gp->seq_start || !gp->blocks)) return PKV_ERR_NULL;
@@ -152,6 +166,13 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
     a.sink_v = qp->v_sink;
     a.sink_of_seq = qp->sink_tiles_of_seq;
     a.num_sink_tiles = qp->num_sink_tiles;
+  }
+  if (ap) {
+    a.k_new = ap->k_new;
+    a.v_new = ap->v_new;
+    a.new_slots = ap->slots;
+    a.k_cache_rw = ap->k_cache;
+    a.v_cache_rw = ap->v_cache;
   }
   a.q_dtype = dims->q_dtype;
   a.kv_dtype = dims->kv_dtype;
@@ -283,6 +304,16 @@ int pkv_paged_decode_attn_quant(const void* q, const void* k_cache, const void* 
   if (!p) return PKV_ERR_NULL;
   return decode_common(q, k_cache, v_cache, p, nullptr, block_tables, context_lens, scale, out,
                        dims, workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_decode_step(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                          const void* q, void* k_cache, void* v_cache, const int32_t* block_tables,
+                          const int32_t* context_lens, float scale, void* out,
+                          const pkv_decode_dims* dims, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  const StepAppend ap{k_new, v_new, slot_mapping, k_cache, v_cache};
+  return decode_common(q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens, scale, out,
+                       dims, workspace, workspace_bytes, stream, &ap);
 }
 
 int pkv_paged_decode_attn_prefix(const void* q, const void* k_cache, const void* v_cache,

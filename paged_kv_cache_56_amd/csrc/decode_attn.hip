@@ -444,6 +444,33 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
   const SeqParts parts(span.natt, a.part_blocks, a.num_parts, p);
   const int j0 = parts.j0, j1 = parts.j1;
 
+  // The step's append, when the call carries it ("KV Cache from first
+  // principles" 2.3: the new token's K and V are written at the current
+  // length before it is attended).  The partition holding the sequence's
+  // last attended block -- the new token's -- writes head h's new rows into
+  // the slot, and within it the wave that will read that block, so the
+  // write needs no barrier: the wave's read of the block is issued after a
+  // wait for all its memory operations (the per-step wait, or the explicit
+  // one below when that block is the wave's first).  No other workgroup
+  // reads the block.  Partition 0 writes when nothing is attended.
+  const bool appends = !KQ && a.new_slots != nullptr && p == (parts.n > 0 ? parts.n - 1 : 0);
+  const int append_wave = j1 > j0 ? (j1 - 1 - j0) % NW : 0;
+  auto append_rows = [&]() __attribute__((always_inline)) {
+    if constexpr (!KQ) {
+      const int64_t slot = a.new_slots[b];
+      constexpr int ROWC = D * C::EB / 16;   // 16-byte chunks of one row
+      static_assert(2 * ROWC <= 64, "one wave copies a K row and a V row");
+      if (slot >= 0 && slot < (int64_t)a.num_blocks * 16 && lane < 2 * ROWC) {
+        const bool isv = lane >= ROWC;
+        const int ch = isv ? lane - ROWC : lane;
+        const int64_t src = ((int64_t)b * a.num_kv_heads + h) * ROWC + ch;
+        const int64_t dst = (((slot >> 4) * a.num_kv_heads + h) * 16 + (slot & 15)) * ROWC + ch;
+        reinterpret_cast<u32x4_t*>(isv ? a.v_cache_rw : a.k_cache_rw)[dst] =
+            reinterpret_cast<const u32x4_t*>(isv ? a.v_new : a.k_new)[src];
+      }
+    }
+  };
+
   // Writes row (b, h*G + ha), channel d, from this partition's (m, l, o),
   // o being the unnormalised sum.
   auto finish = [&](int ha, int d, float m, float lsum, float o) __attribute__((always_inline)) {
@@ -462,6 +489,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
   if (j0 >= j1) {
     // nothing of the cache here: a zero row; empty partitions of a split
     // call are skipped by the merge
+    if (appends && w == 0) append_rows();
     if (!a.split)
       for (int idx = tid; idx < G * D; idx += 256) finish(idx / D, idx % D, -INFINITY, 0.f, 0.f);
     return;
@@ -741,6 +769,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
     constexpr unsigned kWaitVm0 = 0x0F70;     // vmcnt(0), expcnt(7), lgkmcnt(15)
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     static_assert(KR == 2, "one block in flight: K(t+1) and V(t+1) while t is computed");
+    if (appends && w == append_wave) {
+      append_rows();
+      if (n_my == 1) wait_vmcnt<0>();    // the new token's block is this wave's first
+    }
     if (n_my > 0) {
       issue_vregs(first, va);
       issue_k2(first, 0);

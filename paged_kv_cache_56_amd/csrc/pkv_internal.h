@@ -65,6 +65,14 @@ struct DecodeArgs {
   int num_groups, group_max_seqs, group_max_blocks;
   int group_part_blocks, group_num_parts;   // split of a group's shared blocks
   int group_qchunks;                        // 64-row chunks of a group's queries
+  // the step's append carried by the attention launch (new_slots NULL:
+  // none): k_new, v_new [B][Hkv][D]; sequence b's token goes to slot
+  // new_slots[b] of the caches, which are then also written
+  const void* k_new;
+  const void* v_new;
+  const int64_t* new_slots;
+  void* k_cache_rw;
+  void* v_cache_rw;
   // workgroups of the group pass (0: none); they lead the combined launch
   // and write workspace slots [num_parts, part_stride) of their rows
   int group_wgs;

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
     lib = pkv.load_library()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pkv_version() == 140
+    assert lib.pkv_version() == 150
 
 
 def _dims(**kw):
@@ -179,6 +179,26 @@ def test_prefix_group_status_codes_and_plan():
     # group pass: 2 groups x 8 heads x 5 chunks = 80 units -> ~256 workgroups
     # would take 4 pieces of 50 blocks (above the 32-block floor)
     assert pkv.decode_workspace_bytes(d8) == 64 * 64 * (1 + 4) * (128 + 2) * 4
+
+
+def _step(dims, k_new=FAKE, v_new=FAKE, slots=FAKE, ws=None, ws_bytes=0):
+    lib = pkv.load_library()
+    return lib.pkv_paged_decode_step(k_new, v_new, slots, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.088),
+                                     FAKE, ctypes.byref(dims), ws, ws_bytes, None)
+
+
+def test_fused_step_status_codes():
+    d = _dims(num_seqs=16)                       # 16 x 8 units -> 4 partitions: needs a workspace
+    assert pkv.decode_num_partitions(d) == 4
+    assert _step(d) == -4
+    assert _step(d, k_new=None) == -1
+    assert _step(d, slots=None) == -1
+    assert _step(_dims(kv_dtype=3, q_dtype=2, out_dtype=2)) == -3          # 8-bit caches: separate calls
+    assert _step(_dims(kv_dtype=4, q_dtype=2, out_dtype=2)) == -3
+    assert _step(_dims(kv_dtype=1, q_dtype=2, out_dtype=2)) == -3          # q, caches, out of one type
+    assert _step(_dims(sinks=4, sink_tiles=1)) == -2
+    assert _step(_dims(prefix_groups=1, prefix_max_seqs=4, prefix_max_blocks=8)) == -2
+    assert _step(_dims(block_size=8)) == -2
 
 
 def test_append_quant_status_codes():

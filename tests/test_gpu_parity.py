@@ -521,6 +521,54 @@ def test_prefix_groups_deterministic():
     assert torch.equal(outs[1], outs[2])
 
 
+# Append and attention in one launch: (case, partition_blocks, window, sinks, skip)
+STEP_CASES = [
+    ("tiny_f32", 0, 0, 0, None),
+    ("tiny_f32", 2, 0, 0, 1),                      # split; sequence 1's token skipped
+    ("ragged_bf16_g8_d128_append", 0, 0, 0, None),
+    ("ragged_bf16_g8_d128_append", 1, 0, 0, None),  # every block its own partition
+    ("ragged_bf16_g8_d128_append", 0, 30, 2, None),
+    ("llama70b_f16_small", 0, 0, 0, None),
+    ("mha13b_prefix_small", 0, 0, 0, 3),
+    ("llama3_8b_bf16_small", 3, 700, 4, None),
+]
+
+
+@pytest.mark.parametrize("case,pb,window,sinks,skip", STEP_CASES)
+def test_fused_step_matches_append_then_attend(case, pb, window, sinks, skip):
+    """pkv_paged_decode_step: the caches equal the oracle's append bit for
+    bit, and the output the oracle's attention over them."""
+    spec = SMALL[case]
+    assert spec.append
+    lay = build_layout(spec)
+    say(f"[step] {case}: pb={pb} window={window} sinks={sinks} skip={skip} lens={list(lay.context_lens[:12])}")
+    x = make_host_inputs(lay)
+    xs = _to_dev(x)
+    slots = lay.slot_mapping.copy()
+    if skip is not None:
+        slots[skip] = -1
+    sm = torch.from_numpy(slots).to(DEV)
+    tol = TOL[spec.kv_dtype]
+    for layer in range(spec.num_layers):
+        out = _out(spec)
+        pkv.paged_decode_step(xs["k_new"][layer], xs["v_new"][layer], sm, xs["q"][layer], xs["k_cache"][layer],
+                              xs["v_cache"][layer], xs["block_tables"], xs["context_lens"], spec.scale, out,
+                              partition_blocks=pb, window=window, sinks=sinks)
+        torch.cuda.synchronize()
+        h = host_layer(x, layer)
+        kc, vc, _, _ = oracle_append(h, spec, slots)
+        for name, ref in (("k_cache", kc), ("v_cache", vc)):
+            got = host_storage(xs[name][layer])
+            assert np.array_equal(got.view(np.uint8), ref.view(np.uint8)), (layer, name)
+        keep = [b for b in range(spec.num_seqs) if b != skip]
+        ref = oracle_attend(h, spec, kc, vc, None, None, lay.block_tables, lay.context_lens, seqs=keep,
+                            window=window, sinks=sinks)
+        got = out_f64(out)[keep]
+        err = err_beyond_rounding(got, ref, spec.out_dtype)
+        say(f"    layer {layer}: max|err| = {err:.3e} (tol {tol})")
+        assert np.isfinite(got).all() and err <= tol
+
+
 @pytest.mark.parametrize("pb", [1, 2, 3, 7])
 def test_split_size_invariance(pb):
     say(f"[split] tiny_f32 partition_blocks={pb}")
