@@ -745,12 +745,26 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
 #pragma unroll
       for (int v = 0; v < VPT; ++v) vr[i].x[v] = *(const uint4*)(src + roff[i][v]);
   };
+  // K(t) from its ring slot: the 16 bytes each lane's DMA copy wrote, read
+  // back with ds_read_b128 (consecutive lanes, consecutive 16-byte columns:
+  // no bank conflicts) and waited for in the same statement.
+  const uint32_t kread0 = lds_offset(smem) + (uint32_t)(w * KR * TILE_B + lane * 16);
   auto read_k = [&](int sk, TokWords<VPT> (&kr)[TPL]) __attribute__((always_inline)) {
-    const char* ks = smem + w * KR * TILE_B + sk * TILE_B + lane * 16;
+    uint32_t addr[TPL * VPT];
 #pragma unroll
     for (int i = 0; i < TPL; ++i)
 #pragma unroll
-      for (int v = 0; v < VPT; ++v) kr[i].x[v] = *(const uint4*)(ks + ((i ^ tmask) * VPT + v) * 1024);
+      for (int v = 0; v < VPT; ++v)
+        addr[i * VPT + v] = kread0 + (uint32_t)(sk * TILE_B + ((i ^ tmask) * VPT + v) * 1024);
+    u32x4_t got[TPL * VPT];
+    lds_read16_wait<TPL * VPT>(got, addr);
+#pragma unroll
+    for (int i = 0; i < TPL; ++i)
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) {
+        const u32x4_t g = got[i * VPT + v];
+        kr[i].x[v] = make_uint4(g[0], g[1], g[2], g[3]);
+      }
   };
   {
     const uint32_t kslot0 = lds_offset(smem) + (uint32_t)(w * KR * TILE_B);
@@ -783,8 +797,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       wait_vmcnt<0>();                      // (asm, memory clobber) the LDS reads stay below
       TokWords<VPT> kr[TPL];
-      read_k(t & 1, kr);
-      wait_lgkmcnt0();                      // K(t)'s slot may be refilled from here on
+      read_k(t & 1, kr);                    // waits for its reads: K(t)'s slot may be refilled
       if (t + 1 < n_my) {
         issue_vregs(first + (t + 1) * NW, vnext);
         issue_k2(first + (t + 1) * NW, (t + 1) & 1);

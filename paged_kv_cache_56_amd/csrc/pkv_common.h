@@ -64,6 +64,43 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
+// N 16-byte LDS reads (ds_read_b128) and the wait for them, in one asm
+// statement: the outputs are defined only when the statement ends, after
+// the wait, so the compiler cannot use them while they are in flight.  The
+// compiler would otherwise split each read into two ds_read2_b32, which
+// puts four lanes on every bank when the 64 lanes read consecutive 16-byte
+// columns.  addr: LDS byte addresses, 16-byte aligned.
+template <int N>
+__device__ __forceinline__ void lds_read16_wait(u32x4_t (&out)[N], const uint32_t (&addr)[N]) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8, "1, 2, 4 or 8 reads");
+  if constexpr (N == 1) {
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(out[0]) : "v"(addr[0]) : "memory");
+  } else if constexpr (N == 2) {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(out[0]), "=&v"(out[1])
+        : "v"(addr[0]), "v"(addr[1])
+        : "memory");
+  } else if constexpr (N == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3])
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3])
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\tds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3]), "=&v"(out[4]), "=&v"(out[5]),
+          "=&v"(out[6]), "=&v"(out[7])
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]),
+          "v"(addr[7])
+        : "memory");
+  }
+}
+
 // LDS byte offset of a __shared__ object (the low half of its flat address).
 __device__ __forceinline__ uint32_t lds_offset(const void* p) { return (uint32_t)(uintptr_t)p; }
 
