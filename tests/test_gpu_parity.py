@@ -407,6 +407,25 @@ WINDOWED = [
 ]
 
 
+@pytest.mark.parametrize("case,window,sinks", [(c, w, s) for c, w, s, pb in WINDOWED if pb == 0])
+def test_balanced_split_with_window(case, window, sinks):
+    """The batch-size hint counts whole lengths; with a window the kernels
+    still attend only the window's blocks."""
+    spec = SMALL[case]
+    lay = build_layout(spec)
+    say(f"[window+balanced] {case}: W={window} S={sinks} lens={list(lay.context_lens[:12])}")
+    x = make_host_inputs(lay)
+    xs = _to_dev(x)
+    out = _out(spec)
+    run_step(xs, 0, spec, out, window=window, sinks=sinks, balanced=True)
+    torch.cuda.synchronize()
+    got = out_f64(out)
+    ref = oracle_rows(host_layer(x, 0), lay, spec, window=window, sinks=sinks)
+    err = err_beyond_rounding(got, ref, spec.out_dtype)
+    say(f"    max|err| = {err:.3e} (tol {TOL[spec.kv_dtype]})")
+    assert np.isfinite(got).all() and err <= TOL[spec.kv_dtype]
+
+
 @pytest.mark.parametrize("case,window,sinks,pb", WINDOWED)
 def test_sliding_window_and_sinks(case, window, sinks, pb):
     spec = SMALL[case]
@@ -426,11 +445,13 @@ def test_sliding_window_and_sinks(case, window, sinks, pb):
 
 
 @pytest.mark.parametrize("name", ["one_long_many_short_f16", "llama3_8b_bf16_small", "ragged_f16_g8_d128",
-                                  "ragged_fp8_g2_d128_f32", "ragged_int8_g8_d128_fpsinks4", "long_fp8_small"])
+                                  "ragged_fp8_g2_d128_f32", "ragged_int8_g8_d128_fpsinks4", "long_fp8_small",
+                                  "ragged_bf16_g4_d64", "ragged_f32_g1_d64", "ragged_fp8k_int8v_g8_d64",
+                                  "ragged_int8_g4_d64_chan", "ragged_bf16_g8_d128_append"])
 def test_balanced_plan_matches_oracle(name):
     """With the batch's block count passed, the split plan may change (for a
     light batch: pieces sized from the real total); the result still matches
-    the oracle."""
+    the oracle (sequences of length 0, 8-bit and mixed caches included)."""
     spec = SMALL[name]
     lay = build_layout(spec)
     say(f"[balanced] {name}: lens={list(lay.context_lens[:12])}")
@@ -521,16 +542,22 @@ def test_prefix_groups_deterministic():
     assert torch.equal(outs[1], outs[2])
 
 
-# Append and attention in one launch: (case, partition_blocks, window, sinks, skip)
+# Append and attention in one launch: (case, partition_blocks, window, sinks,
+# skip); pb = -1 passes the batch's block count instead (the batch-size hint)
 STEP_CASES = [
     ("tiny_f32", 0, 0, 0, None),
     ("tiny_f32", 2, 0, 0, 1),                      # split; sequence 1's token skipped
+    ("tiny_f32", -1, 0, 0, 2),
     ("ragged_bf16_g8_d128_append", 0, 0, 0, None),
     ("ragged_bf16_g8_d128_append", 1, 0, 0, None),  # every block its own partition
     ("ragged_bf16_g8_d128_append", 0, 30, 2, None),
+    ("ragged_bf16_g8_d128_append", -1, 0, 0, None),
+    ("ragged_bf16_g8_d128_append", -1, 30, 2, 4),
     ("llama70b_f16_small", 0, 0, 0, None),
     ("mha13b_prefix_small", 0, 0, 0, 3),
+    ("mha13b_prefix_small", -1, 0, 0, None),
     ("llama3_8b_bf16_small", 3, 700, 4, None),
+    ("llama3_8b_bf16_small", -1, 0, 0, None),
 ]
 
 
@@ -551,9 +578,10 @@ def test_fused_step_matches_append_then_attend(case, pb, window, sinks, skip):
     tol = TOL[spec.kv_dtype]
     for layer in range(spec.num_layers):
         out = _out(spec)
+        total = int(((lay.context_lens.astype(np.int64) + 15) // 16).sum()) if pb < 0 else 0
         pkv.paged_decode_step(xs["k_new"][layer], xs["v_new"][layer], sm, xs["q"][layer], xs["k_cache"][layer],
                               xs["v_cache"][layer], xs["block_tables"], xs["context_lens"], spec.scale, out,
-                              partition_blocks=pb, window=window, sinks=sinks)
+                              partition_blocks=max(pb, 0), window=window, sinks=sinks, total_blocks=total)
         torch.cuda.synchronize()
         h = host_layer(x, layer)
         kc, vc, _, _ = oracle_append(h, spec, slots)
