@@ -696,6 +696,46 @@ def test_block_ids_outside_pool_are_ignored():
     assert (out[0] == 0).all() and torch.isfinite(out[1]).all()
 
 
+def test_lengths_past_the_table_are_clamped():
+    """Positions past max_blocks_per_seq * 16 are not attended; a negative
+    length is a zero row."""
+    say("[bounds] lengths past the table width, negative lengths")
+    spec = _ragged("clamp", "f16", "f16", "f16", 128, 4, [32, 32, 32, 20], 41)
+    lay = build_layout(spec)
+    x = make_host_inputs(lay)
+    xs = _to_dev(x)
+    assert lay.block_tables.shape[1] == 2
+    lens = torch.tensor([40, 33, -5, 20], dtype=torch.int32, device=DEV)   # table holds 32 positions
+    out = _out(spec)
+    pkv.paged_decode_attn(xs["q"][0], xs["k_cache"][0], xs["v_cache"][0], xs["block_tables"], lens,
+                          spec.scale, out)
+    torch.cuda.synchronize()
+    got = out_f64(out)
+    ref = oracle.paged_decode_attention(
+        host_storage(x["q"][0]), host_storage(x["k_cache"][0]), host_storage(x["v_cache"][0]),
+        lay.block_tables, np.array([32, 32, 0, 20]), spec.scale, q_tag="f16", kv_tag="f16")
+    assert (got[2] == 0).all()
+    assert err_beyond_rounding(got, ref, "f16") <= TOL["f16"]
+
+
+def test_group_descriptors_out_of_range_do_not_fault():
+    """Unsorted or out-of-range group starts and oversized block counts give
+    undefined numbers but every access stays in bounds (the counts are
+    clamped to the host bounds, the starts to [0, B])."""
+    spec, lay = _grouped_layout("prefix_groups_f16_g8_d128")
+    say("[bounds] group descriptors out of range")
+    xs = _to_dev(make_host_inputs(lay))
+    width = lay.block_tables.shape[1]
+    starts = torch.tensor([5, -3, 100, 2, 7], dtype=torch.int32, device=DEV)
+    blocks = torch.tensor([1000, -4, width, 3], dtype=torch.int32, device=DEV)
+    out = _out(spec)
+    pkv.paged_decode_attn(xs["q"][0], xs["k_cache"][0], xs["v_cache"][0], xs["block_tables"], xs["context_lens"],
+                          spec.scale, out, prefix_group_starts=starts, prefix_group_blocks=blocks,
+                          prefix_max_seqs=12, prefix_max_blocks=width)
+    torch.cuda.synchronize()
+    assert out.shape == (spec.num_seqs, spec.num_q_heads, spec.head_dim)
+
+
 def test_hbm_read_probe_reads_every_word():
     """The bandwidth probe folds every 16-byte word into its workgroup's sink."""
     say("[probe] plain read fold")
