@@ -62,8 +62,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
-
 // N 16-byte LDS reads (ds_read_b128) and the wait for them, in one asm
 // statement: the outputs are defined only when the statement ends, after
 // the wait, so the compiler cannot use them while they are in flight.  The
