@@ -108,7 +108,7 @@ def cpu_baseline(spec, lay, x, budget_s: float):
 
     nblk = -(-lay.context_lens.astype(int) // 16)
     done_bytes, elapsed, seqs = 0, 0.0, 0
-    order = [(layer, b) for layer in range(spec.num_layers) for b in range(spec.num_seqs)]
+    order = [(layer, b) for layer in range(x["k_cache"].shape[0]) for b in range(spec.num_seqs)]
     with threadpool_limits(limits=cores):
         for layer, b in order:
             used = lay.block_tables[b, : nblk[b]].astype(np.int64)
@@ -160,7 +160,7 @@ def cpu_baseline(spec, lay, x, budget_s: float):
         "cores": cores,
         "kind": "oracle",
         "sample": f"float64 numpy oracle (append + attention) on {seqs} (layer, sequence) pairs "
-                  f"of {spec.num_layers * spec.num_seqs}, all {spec.num_q_heads} query heads each; "
+                  f"of {x['k_cache'].shape[0] * spec.num_seqs}, all {spec.num_q_heads} query heads each; "
                   f"{done_bytes / 1e9:.3f} GB of K/V in {elapsed:.1f} s",
     }
 
@@ -385,6 +385,10 @@ def main():
                     help="untimed steps first (default: enough for >= 100 launches, at least 3); "
                          "the GPU needs a few dozen launches to reach its steady clocks")
     ap.add_argument("--workload", default="llama70b_f16_80l")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layers per step, each with its own cache (0: the workload's own count); "
+                         "several copies of a one-layer workload make every launch read cold data, "
+                         "as in a model with many layers")
     ap.add_argument("--partition-blocks", type=int, default=0)
     ap.add_argument("--window", type=int, default=0, help="sliding window W (0 = whole context)")
     ap.add_argument("--sinks", type=int, default=0, help="attention-sink tokens kept with a window")
@@ -438,18 +442,19 @@ def main():
     torch.cuda.set_device(dev)
     pkv.load_library()
     spec = WORKLOADS[args.workload]
+    layers = args.layers if args.layers > 0 else spec.num_layers
     if args.warmup < 0:
-        args.warmup = max(3, -(-100 // spec.num_layers))
+        args.warmup = max(3, -(-100 // layers))
     if args.steps <= 0:
-        args.steps = max(10, -(-200 // spec.num_layers))
+        args.steps = max(10, -(-200 // layers))
     if args.fp_sinks:
         spec = scaled(spec, fp_sinks=args.fp_sinks)
         args.sinks = args.fp_sinks
     lay = build_layout(spec)
     log(f"[bench] {spec.description}: generating inputs on the device")
-    x = make_device_inputs(lay, "cuda")
+    x = make_device_inputs(lay, "cuda", layers)
     torch.cuda.synchronize()
-    nl = spec.num_layers
+    nl = x["k_cache"].shape[0]
     odt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[spec.out_dtype]
     outs = torch.empty((nl, spec.num_seqs, spec.num_q_heads, spec.head_dim), dtype=odt, device=dev)
     # a scheduler knows its batch's lengths on the host: pass their block count

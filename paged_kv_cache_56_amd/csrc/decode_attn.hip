@@ -579,26 +579,43 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
       dma_off[i * VPT + v] = (uint32_t)(((i * R + r) * D + (v * LPT + c) * E) * C::EB);
-  auto tile_of = [&](int j) __attribute__((always_inline)) {
-    int phys = table[span.logical(j)];
-    phys = ((unsigned)phys < (unsigned)a.num_blocks) ? phys : 0;
+  // A block's table entry, read as raw (an id outside the pool masks the
+  // whole block), and its 8-bit scales.  The entry is read two steps before
+  // the step that computes the block and the scales one step before, so
+  // neither scalar load's latency sits between a step's wait and its next
+  // tile loads.
+  struct BlockRef {
+    int phys;
+    float ks, vs;
+  };
+  auto entry_of = [&](int j) __attribute__((always_inline)) { return table[span.logical(j)]; };
+  auto tile_of = [&](int phys_raw) __attribute__((always_inline)) {
+    const int phys = ((unsigned)phys_raw < (unsigned)a.num_blocks) ? phys_raw : 0;
     return ((int64_t)phys * a.num_kv_heads + h) * (int64_t)TILE_B;
   };
+  auto scales_of = [&](BlockRef& br) __attribute__((always_inline)) {
+    br.ks = 1.f;
+    br.vs = 1.f;
+    if constexpr (KQ) {
+      // uniform index, read-only data: scalar loads, which do not wait
+      // behind the tile copies in flight (those count on vmcnt)
+      const int phys = ((unsigned)br.phys < (unsigned)a.num_blocks) ? br.phys : 0;
+      const int64_t si = (int64_t)phys * a.num_kv_heads + h;
+      br.ks = ((const __attribute__((address_space(4))) float*)a.k_scales)[si];
+      br.vs = ((const __attribute__((address_space(4))) float*)a.v_scales)[si];
+    }
+  };
   // vr is consumed: tokens outside the sequence (or window) are zeroed in it.
-  auto compute_block = [&](int j, const TokWords<VPT> (&kr)[TPL], TokWords<VPT> (&vr)[TPL])
-                           __attribute__((always_inline)) {
+  auto compute_block = [&](int j, const BlockRef& br, const TokWords<VPT> (&kr)[TPL],
+                           TokWords<VPT> (&vr)[TPL]) __attribute__((always_inline)) {
     const int jl = span.logical(j);
-    const int phys_raw = table[jl];
-    const bool blk_ok = (unsigned)phys_raw < (unsigned)a.num_blocks;
+    const bool blk_ok = (unsigned)br.phys < (unsigned)a.num_blocks;
     const uint32_t vbits = blk_ok ? span.valid_bits(jl) : 0u;
     float cs = a.scale;  // scale * log2(e), folded on the host
     float vsc = 1.f;
     if constexpr (KQ) {
-      // uniform index, read-only data: scalar loads, which do not wait
-      // behind the tile copies in flight (those count on vmcnt)
-      const int64_t si = (int64_t)(blk_ok ? phys_raw : 0) * a.num_kv_heads + h;
-      cs *= ((const __attribute__((address_space(4))) float*)a.k_scales)[si];
-      vsc = ((const __attribute__((address_space(4))) float*)a.v_scales)[si];
+      cs *= br.ks;
+      vsc = br.vs;
     }
 
     // 1. partial scores: slot k = hs * TPL + i
@@ -722,10 +739,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
   };
 
   // Staging.  K tiles go through a two-slot per-wave LDS ring by LDS DMA; V
-  // tiles go straight to registers.  The LDS DMA path alone tops out near
-  // 6.0 TB/s on this chip while plain 16-byte loads reach ~6.7, and splitting
-  // the stream between the two paths reaches the latter.  Block t + 1's K
-  // copy and V loads are in flight while block t is computed.  The V loads
+  // tiles go straight to registers.  Scattered 4 KiB tiles stream at ~6.0
+  // TB/s on this chip under the default cache policy whichever path they
+  // take (LDS DMA or registers, one to three blocks in flight, two or four
+  // waves per SIMD all measured alike); non-temporal K copies lift a launch
+  // to ~6.2-6.3 TB/s.  Block t + 1's K copy and V loads are in flight while
+  // block t is computed.  The V loads
   // are ordinary loads, so the compiler knows when their registers are
   // valid; the one wait per block is a waitcnt it can see (vmcnt(0), which
   // also covers the K copies it cannot see), so it places no waits of its
@@ -738,8 +757,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
       roff[i][v] = (uint32_t)((((i ^ tmask) * R + r) * D + (v * LPT + c) * E) * C::EB);
-  auto issue_vregs = [&](int j, TokWords<VPT> (&vr)[TPL]) __attribute__((always_inline)) {
-    const char* src = vbase + tile_of(j);
+  // Ordinary loads: non-temporal V loads measured no faster on a uniform
+  // batch and about 40% slower on a batch of uneven lengths.
+  auto issue_vregs = [&](int phys_raw, TokWords<VPT> (&vr)[TPL]) __attribute__((always_inline)) {
+    const char* src = vbase + tile_of(phys_raw);
 #pragma unroll
     for (int i = 0; i < TPL; ++i)
 #pragma unroll
@@ -768,8 +789,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
   };
   {
     const uint32_t kslot0 = lds_offset(smem) + (uint32_t)(w * KR * TILE_B);
-    auto issue_k2 = [&](int j, int sk) __attribute__((always_inline)) {
-      const char* src = kbase + tile_of(j);
+    auto issue_k2 = [&](int phys_raw, int sk) __attribute__((always_inline)) {
+      const char* src = kbase + tile_of(phys_raw);
       const uint32_t dst = kslot0 + (uint32_t)(sk * TILE_B);
 #pragma unroll
       for (int n = 0; n < LPB; ++n) lds_dma16(src, dma_off[n], dst + n * 1024);
@@ -787,9 +808,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
       append_rows();
       if (n_my == 1) wait_vmcnt<0>();    // the new token's block is this wave's first
     }
+    // bcur: the block being computed; bnext: the next one, its entry read
+    BlockRef bcur{0, 1.f, 1.f}, bnext{0, 1.f, 1.f};
     if (n_my > 0) {
-      issue_vregs(first, va);
-      issue_k2(first, 0);
+      bcur.phys = entry_of(first);
+      issue_vregs(bcur.phys, va);
+      issue_k2(bcur.phys, 0);
+      scales_of(bcur);
+      if (n_my > 1) bnext.phys = entry_of(first + NW);
     }
     // Step t: K(t) and V(t) are the newest loads in flight, so wait for all.
     auto step = [&](int t, TokWords<VPT> (&vcur)[TPL], TokWords<VPT> (&vnext)[TPL])
@@ -798,12 +824,16 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
       wait_vmcnt<0>();                      // (asm, memory clobber) the LDS reads stay below
       TokWords<VPT> kr[TPL];
       read_k(t & 1, kr);                    // waits for its reads: K(t)'s slot may be refilled
+      const BlockRef b0 = bcur;
       if (t + 1 < n_my) {
-        issue_vregs(first + (t + 1) * NW, vnext);
-        issue_k2(first + (t + 1) * NW, (t + 1) & 1);
+        issue_vregs(bnext.phys, vnext);
+        issue_k2(bnext.phys, (t + 1) & 1);
+        scales_of(bnext);
+        bcur = bnext;
+        if (t + 2 < n_my) bnext.phys = entry_of(first + (t + 2) * NW);
       }
       __builtin_amdgcn_sched_barrier(0);    // the loads stay ahead of the compute
-      compute_block(first + t * NW, kr, vcur);
+      compute_block(first + t * NW, b0, kr, vcur);
     };
     int t = 0;
     for (; t + 1 < n_my; t += 2) {
