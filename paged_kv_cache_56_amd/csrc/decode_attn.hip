@@ -515,8 +515,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
   // power-of-two rescale for the whole KV group, from the largest |q * c|
   // over all g heads (every lane of a row sees all of them, so every lane
   // derives the same exponent), so the partial sums the rows combine agree.
+  // The query is loaded after the first tile loads are issued (below), so
+  // its latency overlaps theirs.
   QSlice<KT, EL> qs[G];
   int qexp = 0;
+  float qfac = 1.f;   // undoes the rescale on the scores
+  auto load_query = [&]() __attribute__((always_inline)) {
   if constexpr (KQ) {
     float cf[EL];
     if (a.k_chan) {
@@ -548,7 +552,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
 #pragma unroll
     for (int hs = 0; hs < G; ++hs) load_q<KT, QT, EL, LPT, E, VPT>(qs[hs], qrow_of(hs), c);
   }
-  const float qfac = __builtin_ldexpf(1.0f, -qexp);   // undoes the rescale on the scores
+  qfac = __builtin_ldexpf(1.0f, -qexp);
+  };
 
   float acc[G][EL];
   float mref[G];
@@ -798,11 +803,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
     const int first = j0 + w;
     const int n_my = first < j1 ? (j1 - first + NW - 1) / NW : 0;
     TokWords<VPT> va[TPL], vb[TPL];
-    // A wait the compiler sees: the query loads are complete, so it places
-    // none of its own inside the loop, where they would also wait for the
-    // prefetches in flight.
     constexpr unsigned kWaitVm0 = 0x0F70;     // vmcnt(0), expcnt(7), lgkmcnt(15)
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     static_assert(KR == 2, "one block in flight: K(t+1) and V(t+1) while t is computed");
     if (appends && w == append_wave) {
       append_rows();
@@ -817,17 +818,28 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
       scales_of(bcur);
       if (n_my > 1) bnext.phys = entry_of(first + NW);
     }
-    // Step t: K(t) and V(t) are the newest loads in flight, so wait for all.
+    load_query();
+    // A wait the compiler sees: the query loads are complete, so it places
+    // none of its own inside the loop, where they would also wait for the
+    // prefetches in flight.
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    // Step t: K(t) and V(t) are the newest loads in flight, so wait for all,
+    // then issue block t + 1 at once: its K slot and V registers held block
+    // t - 1, already consumed, so nothing of block t has to be read first.
     auto step = [&](int t, TokWords<VPT> (&vcur)[TPL], TokWords<VPT> (&vnext)[TPL])
                     __attribute__((always_inline)) {
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       wait_vmcnt<0>();                      // (asm, memory clobber) the LDS reads stay below
-      TokWords<VPT> kr[TPL];
-      read_k(t & 1, kr);                    // waits for its reads: K(t)'s slot may be refilled
       const BlockRef b0 = bcur;
-      if (t + 1 < n_my) {
+      const bool more = t + 1 < n_my;
+      if (more) {
         issue_vregs(bnext.phys, vnext);
         issue_k2(bnext.phys, (t + 1) & 1);
+      }
+      TokWords<VPT> kr[TPL];
+      read_k(t & 1, kr);                    // waits for its reads (lgkmcnt(0))
+      // scalar loads after that wait, which would otherwise cover them too
+      if (more) {
         scales_of(bnext);
         bcur = bnext;
         if (t + 2 < n_my) bnext.phys = entry_of(first + (t + 2) * NW);
