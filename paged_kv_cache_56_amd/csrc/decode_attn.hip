@@ -874,36 +874,59 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
 #pragma unroll
     for (int i = 0; i < TPL; ++i) lrow[hs] += la[hs * TPL + i];
   }
-  // rows of the wave: lanes with equal c hold the same heads and columns
+  // Rows of the wave: lanes with equal c hold the same heads and columns.
+  // Every row's partial is first moved to the wave's reference maximum.
+  constexpr int NA = G * EL;               // accumulators per lane, flat: hs * EL + el
+  float fa[NA];
 #pragma unroll
   for (int hs = 0; hs < G; ++hs) {
-    float mw = mref[hs];
-#pragma unroll
-    for (int d = LPT; d < 64; d <<= 1) mw = fmaxf(mw, __shfl_xor(mw, d));
+    const float mw = across_rows<LPT, true>(mref[hs]);
     const float f = mref[hs] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref[hs] - mw);
-    lrow[hs] *= f;
+    lrow[hs] = across_rows<LPT, false>(lrow[hs] * f);
 #pragma unroll
-    for (int e = 0; e < EL; ++e) acc[hs][e] *= f;
-#pragma unroll
-    for (int d = LPT; d < 64; d <<= 1) {
-      lrow[hs] += __shfl_xor(lrow[hs], d);
-#pragma unroll
-      for (int e = 0; e < EL; ++e) acc[hs][e] += __shfl_xor(acc[hs][e], d);
-    }
+    for (int e = 0; e < EL; ++e) fa[hs * EL + e] = acc[hs][e] * f;
     mref[hs] = mw;
   }
-  if (r == 0) {
+  // Rows inside a 16-lane DPP row (LPT < 16): summed in place.
+#pragma unroll
+  for (int k = 0; k < NA; ++k) {
+    if constexpr (LPT == 4) fa[k] += dpp<DPP_ROW_ROR4>(fa[k]);
+    if constexpr (LPT <= 8) fa[k] += dpp<DPP_ROW_ROR8>(fa[k]);
+  }
+  // Rows 16 and 32 lanes apart: a reduce-scatter with gfx950's lane swaps.
+  // v_permlane16_swap(X, Y) with X, Y the two halves of the accumulators
+  // leaves, in X' + Y', the pair's sum of X in even 16-lane rows and the
+  // pair's sum of Y in odd ones; v_permlane32_swap splits the result again
+  // between the lower and upper 32 lanes.  A lane ends with NA / 4 sums:
+  // flat indices base + k, base = (bit 5) * NA/4 + (bit 4) * NA/2.
+  constexpr int N2 = NA / 2, N4 = NA / 4;
+  float h1[N2], h2[N4];
+#pragma unroll
+  for (int k = 0; k < N2; ++k) {
+    const auto sw = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, fa[k]),
+                                                     __builtin_bit_cast(uint32_t, fa[k + N2]), false, false);
+    h1[k] = __builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]);
+  }
+#pragma unroll
+  for (int k = 0; k < N4; ++k) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, h1[k]),
+                                                     __builtin_bit_cast(uint32_t, h1[k + N4]), false, false);
+    h2[k] = __builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]);
+  }
+  // one lane of each in-row group (the rest hold copies) writes its sums
+  if (((lane & 15) / LPT) == 0) {
+    const int base = ((lane >> 5) & 1) * N4 + ((lane >> 4) & 1) * N2;
+#pragma unroll
+    for (int k = 0; k < N4; ++k) {
+      const int fi = base + k, hs = fi / EL, el = fi % EL;
+      red_acc[w][hs ^ hmask][((el / E) * LPT + c) * E + el % E] = h2[k];
+    }
+  }
+  if (r == 0 && c == 0) {
 #pragma unroll
     for (int hs = 0; hs < G; ++hs) {
-      const int ha = hs ^ hmask;
-#pragma unroll
-      for (int v = 0; v < VPT; ++v)
-#pragma unroll
-        for (int e = 0; e < E; ++e) red_acc[w][ha][(v * LPT + c) * E + e] = acc[hs][v * E + e];
-      if (c == 0) {
-        red_m[w][ha] = mref[hs];
-        red_l[w][ha] = lrow[hs];
-      }
+      red_m[w][hs ^ hmask] = mref[hs];
+      red_l[w][hs ^ hmask] = lrow[hs];
     }
   }
   __syncthreads();

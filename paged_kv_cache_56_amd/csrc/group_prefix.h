@@ -226,8 +226,7 @@ __device__ __forceinline__ void group_body(const DecodeArgs& a, int pp, int h, i
         mx = fmaxf(mx, sv[tt * 4 + i]);
       }
     if (__builtin_amdgcn_ballot_w64(mx > m + SLACK)) {         // uniform over the wave
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = across_rows<16, true>(mx);   // the query's four lane groups
       const float mn = fmaxf(m, mx);
       const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
       l *= alpha;
@@ -275,8 +274,7 @@ __device__ __forceinline__ void group_body(const DecodeArgs& a, int pp, int h, i
     if (i0 + s < nsteps) step(i0 + s, kreg[s], vreg[s], okb[s]);   // uniform over the workgroup
 
   // partial result of this piece: lane holds channels dt*16 + 4*lg + 0..3
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = across_rows<16, false>(l);
   if (wave_on && rv) {
     const int64_t slot =
         ((int64_t)b * a.num_q_heads + head) * a.part_stride + a.num_parts + pp;

@@ -41,6 +41,34 @@ __device__ __forceinline__ float dpp(float v) {
       float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
+// ---- combining the token rows of a wave ----------------------------------
+// Lanes l and l' hold the same quantity for different token rows when
+// l % LPT == l' % LPT (LPT lanes per row, 4, 8 or 16).  across_rows combines
+// the 64 / LPT copies and leaves the result in every lane.  Inside a 16-lane
+// DPP row the copies are LPT apart, and rotating the row by 4 and then by 8
+// visits all of them.  Across rows, gfx950's lane swaps do it without the
+// LDS round trip of a shuffle: with both operands equal to x, the two
+// results of v_permlane16_swap hold, in every lane, x and x from the lane 16
+// away (rows 0<->1, 2<->3), and v_permlane32_swap likewise for lanes 32
+// away, so combining the two results combines the pair.
+constexpr int DPP_ROW_ROR4 = 0x124;      // row_ror:4
+
+template <bool MAX>
+__device__ __forceinline__ float combine2(float a, float b) { return MAX ? fmaxf(a, b) : a + b; }
+
+template <int LPT, bool MAX>
+__device__ __forceinline__ float across_rows(float x) {
+  static_assert(LPT == 4 || LPT == 8 || LPT == 16, "lanes per token row");
+  if constexpr (LPT == 4) x = combine2<MAX>(x, dpp<DPP_ROW_ROR4>(x));
+  if constexpr (LPT <= 8) x = combine2<MAX>(x, dpp<DPP_ROW_ROR8>(x));
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = combine2<MAX>(__builtin_bit_cast(float, (uint32_t)s16[0]), __builtin_bit_cast(float, (uint32_t)s16[1]));
+  const uint32_t v = __builtin_bit_cast(uint32_t, x);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return combine2<MAX>(__builtin_bit_cast(float, (uint32_t)s32[0]), __builtin_bit_cast(float, (uint32_t)s32[1]));
+}
+
 // ---- asynchronous global -> LDS copies (gfx950 LDS DMA) --------------------
 // One instruction moves 16 bytes per lane from `gbase + voff` (per lane) into
 // LDS at `lds + 16 * lane`.  The copy is tracked by vmcnt only, so the waits
