@@ -947,8 +947,21 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
   }
 }
 
+// Waves per SIMD the register allocation must allow.  The GQA-4, D = 128
+// instantiations with 16-bit or fp8 K and V naturally land a few registers
+// above 168, the bound for three waves; holding them to it lets three
+// workgroups share a CU instead of two.  The 16-bit ones need no spill, the
+// fp8 ones one word kept across the loop; with int8 V the bound would put
+// reloads inside the loop, so those keep their natural allocation.
+template <KV KT, KV VT, int D, int G>
+struct MinWaves {
+  static constexpr bool fits = (KT == KV::F16 || KT == KV::BF16 || KT == KV::FP8) && VT == KT;
+  static constexpr int value = (G == 4 && D == 128 && fits) ? 3 : 1;
+};
+
 template <KV KT, KV VT, KV QT, KV OT, int D, int G>
-__global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MinWaves<KT, VT, D, G>::value)))
+decode_partition_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[Cfg<KT, D, G>::SMEM_B];
   decode_body<KT, VT, QT, OT, D, G>(a, blockIdx.x, blockIdx.y, blockIdx.z, smem);
 }
