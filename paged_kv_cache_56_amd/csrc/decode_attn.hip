@@ -74,7 +74,13 @@ __device__ __forceinline__ void static_for(F&& f) {
 template <KV KT, int D, int G>
 struct Cfg {
   static constexpr int EB = kv_bytes<KT>::value;
-  static constexpr int E = 16 / EB;                        // elements per 16-byte load
+  // Bytes a lane loads at a time.  16 in general; 8-bit caches serving 8
+  // query heads load 8, so that a lane owns 8 channels as with 16-bit caches
+  // (with 16 it would keep 16 channels x 8 heads of accumulators and query
+  // and fall to one wave per SIMD).
+  static constexpr int LW = (EB == 1 && G == 8) ? 8 : 16;
+  static constexpr int NWD = LW / 4;                       // words per load
+  static constexpr int E = LW / EB;                        // elements per load
   static constexpr int VPT = (D / E > 16) ? (D / E) / 16 : 1;  // loads per token per lane
   static constexpr int LPT = D / (E * VPT);                // lanes sharing one token
   static constexpr int R = 64 / LPT;                       // token rows per wave
@@ -85,15 +91,23 @@ struct Cfg {
   static constexpr int NF = NS >> NRS;                     // slots left after it
   static constexpr int EL = E * VPT;                       // elements per lane per token
   static constexpr int NW = 4;                             // waves per workgroup
-  static constexpr int LPB = TPL * VPT;                    // 16-byte loads per lane per tile
+  static constexpr int NWT = NWD * VPT;                    // words per token per lane
+  static constexpr int LPB = TPL * VPT;                    // loads per lane per tile
   static constexpr int TILE_B = 16 * D * EB;               // bytes of one (block, kv_head) tile
+  static constexpr int NDMA = TILE_B / 1024;               // 1 KiB LDS DMA copies per tile
   // K tiles are staged in LDS, two slots per wave (deeper rings measured
   // slower); V tiles go straight to registers.
   static constexpr int KR = 2;
-  static constexpr int KRING_B = NW * KR * TILE_B;
+  // Blocks per step: a step of a wave waits for, issues and computes BPS
+  // consecutive blocks.  Tiles of 8-bit caches with 8 query heads are small
+  // (2 KiB at D = 128) and their kernels hold two waves per SIMD, so one
+  // block per step would leave half the bytes in flight of a 16-bit step.
+  static constexpr int BPS = (EB == 1 && G == 8) ? 2 : 1;
+  static constexpr int KRING_B = NW * KR * BPS * TILE_B;
   static constexpr int RED_B = NW * G * (D + 2) * 4;       // end-of-partition combine
   static constexpr int SMEM_B = KRING_B > RED_B ? KRING_B : RED_B;
-  static_assert(LPB * 64 * 16 == TILE_B, "a tile is LPB wave-wide 16-byte loads");
+  static_assert(LPB * 64 * LW == TILE_B, "a tile is LPB wave-wide loads");
+  static_assert(LW == 16 || NWT == 2, "8-byte loads: one per token");
   static_assert(LPT >= 1 && LPT <= 16 && (LPT & (LPT - 1)) == 0, "lanes per token");
   static_assert(TPL >= 1, "tokens per lane");
 };
@@ -199,23 +213,21 @@ __device__ __forceinline__ void q8_pack(QSlice<KT, EL>& qs, const float (&f)[EL]
     qs.w[e / 2] = pack_f16x2(__builtin_ldexpf(f[e] * cf[e], qexp), __builtin_ldexpf(f[e + 1] * cf[e + 1], qexp));
 }
 
-// K/V words of one token for one lane: VPT * 4 dwords.
-template <int VPT> struct TokWords { uint4 x[VPT]; };
+// K/V words of one token for one lane: NWT dwords (VPT loads of 16 or 8 bytes).
+template <int NWT> struct TokWords { uint32_t w[NWT]; };
 
-template <int VPT>
-__device__ __forceinline__ void words_of(const TokWords<VPT>& t, uint32_t (&w)[4 * VPT]) {
+template <int NWT>
+__device__ __forceinline__ void words_of(const TokWords<NWT>& t, uint32_t (&w)[NWT]) {
 #pragma unroll
-  for (int v = 0; v < VPT; ++v) {
-    w[4 * v + 0] = t.x[v].x; w[4 * v + 1] = t.x[v].y; w[4 * v + 2] = t.x[v].z; w[4 * v + 3] = t.x[v].w;
-  }
+  for (int k = 0; k < NWT; ++k) w[k] = t.w[k];
 }
 
-template <KV KT, int EL, int VPT>
-__device__ __forceinline__ void to_f32(const TokWords<VPT>& t, float (&f)[EL]) {
-  uint32_t w[4 * VPT];
+template <KV KT, int EL, int NWT>
+__device__ __forceinline__ void to_f32(const TokWords<NWT>& t, float (&f)[EL]) {
+  uint32_t w[NWT];
   words_of(t, w);
 #pragma unroll
-  for (int k = 0; k < 4 * VPT; ++k) {
+  for (int k = 0; k < NWT; ++k) {
     if constexpr (KT == KV::F32) {
       f[k] = __builtin_bit_cast(float, w[k]);
     } else if constexpr (KT == KV::F16) {
@@ -236,12 +248,12 @@ __device__ __forceinline__ void to_f32(const TokWords<VPT>& t, float (&f)[EL]) {
 }
 
 // fp8 token words -> f16 pairs of adjacent elements (same token): EL / 2 words.
-template <int EL, int VPT>
-__device__ __forceinline__ void fp8_to_f16_pairs(const TokWords<VPT>& t, uint32_t (&h)[EL / 2]) {
-  uint32_t w[4 * VPT];
+template <int EL, int NWT>
+__device__ __forceinline__ void fp8_to_f16_pairs(const TokWords<NWT>& t, uint32_t (&h)[EL / 2]) {
+  uint32_t w[NWT];
   words_of(t, w);
 #pragma unroll
-  for (int k = 0; k < 4 * VPT; ++k) {
+  for (int k = 0; k < NWT; ++k) {
     h[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[k], 1.0f, false));
     h[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[k], 1.0f, true));
   }
@@ -273,20 +285,20 @@ __device__ __forceinline__ uint32_t i8_pair_to_f16(uint32_t lo, uint32_t hi) {
 #undef PKV_CVT_I8_HI
 
 // int8 token words -> f16 pairs of adjacent elements (same token): EL / 2 words.
-template <int EL, int VPT>
-__device__ __forceinline__ void int8_to_f16_pairs(const TokWords<VPT>& t, uint32_t (&h)[EL / 2]) {
-  uint32_t w[4 * VPT];
+template <int EL, int NWT>
+__device__ __forceinline__ void int8_to_f16_pairs(const TokWords<NWT>& t, uint32_t (&h)[EL / 2]) {
+  uint32_t w[NWT];
   words_of(t, w);
 #pragma unroll
-  for (int k = 0; k < 4 * VPT; ++k) {
+  for (int k = 0; k < NWT; ++k) {
     h[2 * k] = i8_pair_to_f16<0, 1>(w[k], w[k]);
     h[2 * k + 1] = i8_pair_to_f16<2, 3>(w[k], w[k]);
   }
 }
 
 // Partial <q_slice, K_slice> for one token.
-template <KV KT, int EL, int VPT>
-__device__ __forceinline__ float qk_partial(const QSlice<KT, EL>& qs, const TokWords<VPT>& t,
+template <KV KT, int EL, int NWT>
+__device__ __forceinline__ float qk_partial(const QSlice<KT, EL>& qs, const TokWords<NWT>& t,
                                             const float (&kf)[EL], const uint32_t (&kh)[EL / 2]) {
   float s;
   if constexpr (KT == KV::F16 || is_quantised<KT>()) {
@@ -319,14 +331,14 @@ __device__ __forceinline__ float qk_partial(const QSlice<KT, EL>& qs, const TokW
 }
 
 // V of two tokens -> per element, an f16 pair (token 0, token 1) for dot2.
-template <KV KT, int EL, int VPT>
-__device__ __forceinline__ void v_token_pairs(const TokWords<VPT>& t0, const TokWords<VPT>& t1,
+template <KV KT, int EL, int NWT>
+__device__ __forceinline__ void v_token_pairs(const TokWords<NWT>& t0, const TokWords<NWT>& t1,
                                               uint32_t (&vp)[EL]) {
-  uint32_t a[4 * VPT], b[4 * VPT];
+  uint32_t a[NWT], b[NWT];
   words_of(t0, a);
   words_of(t1, b);
 #pragma unroll
-  for (int k = 0; k < 4 * VPT; ++k) {
+  for (int k = 0; k < NWT; ++k) {
     if constexpr (KT == KV::F16) {
       // word k holds elements 2k, 2k+1 of each token
       vp[2 * k] = __builtin_amdgcn_perm(b[k], a[k], 0x05040100u);
@@ -419,7 +431,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
   static_assert(is_quantised<KT>() == is_quantised<VT>(), "8-bit K goes with 8-bit V");
   constexpr bool KQ = is_quantised<KT>();
   using C = Cfg<KT, D, G>;
-  constexpr int E = C::E, VPT = C::VPT, LPT = C::LPT, R = C::R, TPL = C::TPL;
+  constexpr int E = C::E, VPT = C::VPT, LPT = C::LPT, R = C::R, TPL = C::TPL, NWT = C::NWT, LW = C::LW;
   constexpr int NS = C::NS, NRS = C::NRS, NF = C::NF, EL = C::EL, NW = C::NW;
   constexpr int LEVELS = C::LEVELS;
   // P.V as f16 dot2 over pairs of tokens (probabilities rounded to f16)
@@ -454,7 +466,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
   // one below when that block is the wave's first).  No other workgroup
   // reads the block.  Partition 0 writes when nothing is attended.
   const bool appends = !KQ && a.new_slots != nullptr && p == (parts.n > 0 ? parts.n - 1 : 0);
-  const int append_wave = j1 > j0 ? (j1 - 1 - j0) % NW : 0;
+  constexpr int BPS = C::BPS;
+  const int append_wave = j1 > j0 ? ((j1 - 1 - j0) / BPS) % NW : 0;
   auto append_rows = [&]() __attribute__((always_inline)) {
     if constexpr (!KQ) {
       const int64_t slot = a.new_slots[b];
@@ -575,15 +588,24 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
   const __attribute__((address_space(4))) int32_t* table =
       (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)b * a.max_blocks);
 
-  constexpr int LPB = C::LPB, KR = C::KR, TILE_B = C::TILE_B;
-  // Copy n of a tile moves token rows n / VPT * R .. + R - 1, 16-byte column
-  // (n % VPT) * LPT + c, in lane order: every copy reads 1 KiB contiguously.
-  uint32_t dma_off[LPB];
+  constexpr int KR = C::KR, TILE_B = C::TILE_B, NDMA = C::NDMA;
+  // 16-byte lanes: copy n of a tile moves token rows n / VPT * R .. + R - 1,
+  // 16-byte column (n % VPT) * LPT + c, in lane order, so each lane later
+  // reads back exactly the bytes it copied.  8-byte lanes: the tile lands in
+  // LDS as it is in HBM (row-major) and lanes read their 8 bytes from there.
+  // Either way every copy reads 1 KiB contiguously.
+  uint32_t dma_off[NDMA];
+  if constexpr (LW == 16) {
+    static_assert(NDMA == C::LPB, "one copy per 16-byte load");
 #pragma unroll
-  for (int i = 0; i < TPL; ++i)
+    for (int i = 0; i < TPL; ++i)
 #pragma unroll
-    for (int v = 0; v < VPT; ++v)
-      dma_off[i * VPT + v] = (uint32_t)(((i * R + r) * D + (v * LPT + c) * E) * C::EB);
+      for (int v = 0; v < VPT; ++v)
+        dma_off[i * VPT + v] = (uint32_t)(((i * R + r) * D + (v * LPT + c) * E) * C::EB);
+  } else {
+#pragma unroll
+    for (int n = 0; n < NDMA; ++n) dma_off[n] = (uint32_t)(n * 1024 + lane * 16);
+  }
   // A block's table entry, read as raw (an id outside the pool masks the
   // whole block), and its 8-bit scales.  The entry is read two steps before
   // the step that computes the block and the scales one step before, so
@@ -611,8 +633,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
     }
   };
   // vr is consumed: tokens outside the sequence (or window) are zeroed in it.
-  auto compute_block = [&](int j, const BlockRef& br, const TokWords<VPT> (&kr)[TPL],
-                           TokWords<VPT> (&vr)[TPL]) __attribute__((always_inline)) {
+  auto compute_block = [&](int j, const BlockRef& br, const TokWords<NWT> (&kr)[TPL],
+                           TokWords<NWT> (&vr)[TPL]) __attribute__((always_inline)) {
     const int jl = span.logical(j);
     const bool blk_ok = (unsigned)br.phys < (unsigned)a.num_blocks;
     const uint32_t vbits = blk_ok ? span.valid_bits(jl) : 0u;
@@ -629,11 +651,11 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
     for (int i = 0; i < TPL; ++i) {
       float kf[EL];
       uint32_t kh[EL / 2];
-      if constexpr (KT == KV::F32) to_f32<KT, EL, VPT>(kr[i], kf);
-      if constexpr (KT == KV::FP8) fp8_to_f16_pairs<EL, VPT>(kr[i], kh);
-      if constexpr (KT == KV::INT8) int8_to_f16_pairs<EL, VPT>(kr[i], kh);
+      if constexpr (KT == KV::F32) to_f32<KT, EL, NWT>(kr[i], kf);
+      if constexpr (KT == KV::FP8) fp8_to_f16_pairs<EL, NWT>(kr[i], kh);
+      if constexpr (KT == KV::INT8) int8_to_f16_pairs<EL, NWT>(kr[i], kh);
 #pragma unroll
-      for (int hs = 0; hs < G; ++hs) s[hs * TPL + i] = qk_partial<KT, EL, VPT>(qs[hs], kr[i], kf, kh);
+      for (int hs = 0; hs < G; ++hs) s[hs * TPL + i] = qk_partial<KT, EL, NWT>(qs[hs], kr[i], kf, kh);
     }
     // 2. reduce-scatter over the row, then all-reduce for any levels left
     static_for<NRS>([&](auto l) {
@@ -651,7 +673,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
     for (int k = 0; k < NF; ++k) s[k] *= cs;
 
     // 3. mask the tail (and a block id outside the pool)
-    TokWords<VPT> (&vv)[TPL] = vr;
+    TokWords<NWT> (&vv)[TPL] = vr;
     if (vbits != 0xFFFFu) {
 #pragma unroll
       for (int k = 0; k < NF; ++k) {
@@ -662,7 +684,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
       for (int i = 0; i < TPL; ++i) {
         if (!((vbits >> ((i ^ tmask) * R + r)) & 1u)) {
 #pragma unroll
-          for (int v = 0; v < VPT; ++v) vv[i].x[v] = make_uint4(0, 0, 0, 0);
+          for (int k = 0; k < NWT; ++k) vv[i].w[k] = 0u;
         }
       }
     }
@@ -718,7 +740,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
 #pragma unroll
       for (int m2 = 0; m2 < TPL / 2; ++m2) {
         uint32_t vp[EL];
-        v_token_pairs<VT, EL, VPT>(vv[2 * m2], vv[2 * m2 + 1], vp);
+        v_token_pairs<VT, EL, NWT>(vv[2 * m2], vv[2 * m2 + 1], vp);
 #pragma unroll
         for (int hs = 0; hs < G; ++hs) {
           const half2_t pp = __builtin_bit_cast(
@@ -732,7 +754,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
 #pragma unroll
       for (int i = 0; i < TPL; ++i) {
         float vf[EL];
-        to_f32<VT, EL, VPT>(vv[i], vf);
+        to_f32<VT, EL, NWT>(vv[i], vf);
 #pragma unroll
         for (int hs = 0; hs < G; ++hs) {
           const float pw = pf[hs * TPL + i];
@@ -764,59 +786,103 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
       roff[i][v] = (uint32_t)((((i ^ tmask) * R + r) * D + (v * LPT + c) * E) * C::EB);
   // Ordinary loads: non-temporal V loads measured no faster on a uniform
   // batch and about 40% slower on a batch of uneven lengths.
-  auto issue_vregs = [&](int phys_raw, TokWords<VPT> (&vr)[TPL]) __attribute__((always_inline)) {
+  auto issue_vregs = [&](int phys_raw, TokWords<NWT> (&vr)[TPL]) __attribute__((always_inline)) {
     const char* src = vbase + tile_of(phys_raw);
 #pragma unroll
     for (int i = 0; i < TPL; ++i)
 #pragma unroll
-      for (int v = 0; v < VPT; ++v) vr[i].x[v] = *(const uint4*)(src + roff[i][v]);
+      for (int v = 0; v < VPT; ++v) {
+        if constexpr (LW == 16) {
+          const uint4 x = *(const uint4*)(src + roff[i][v]);
+          vr[i].w[4 * v + 0] = x.x; vr[i].w[4 * v + 1] = x.y; vr[i].w[4 * v + 2] = x.z; vr[i].w[4 * v + 3] = x.w;
+        } else {
+          const uint2 x = *(const uint2*)(src + roff[i][v]);
+          vr[i].w[0] = x.x; vr[i].w[1] = x.y;
+        }
+      }
   };
   // K(t) from its ring slot: the 16 bytes each lane's DMA copy wrote, read
   // back with ds_read_b128 (consecutive lanes, consecutive 16-byte columns:
   // no bank conflicts) and waited for in the same statement.
-  const uint32_t kread0 = lds_offset(smem) + (uint32_t)(w * KR * TILE_B + lane * 16);
-  auto read_k = [&](int sk, TokWords<VPT> (&kr)[TPL]) __attribute__((always_inline)) {
-    uint32_t addr[TPL * VPT];
+  // a wave's ring: KR slots of BPS tiles; tile sk of the ring at sk * TILE_B
+  const uint32_t kread0 = lds_offset(smem) + (uint32_t)(w * KR * BPS * TILE_B + lane * 16);
+  const uint32_t kread8 = lds_offset(smem) + (uint32_t)(w * KR * BPS * TILE_B + r * D * C::EB + c * 8);
+  auto read_k = [&](int sk, TokWords<NWT> (&kr)[TPL]) __attribute__((always_inline)) {
+    if constexpr (LW == 16) {
+      uint32_t addr[TPL * VPT];
 #pragma unroll
-    for (int i = 0; i < TPL; ++i)
+      for (int i = 0; i < TPL; ++i)
 #pragma unroll
-      for (int v = 0; v < VPT; ++v)
-        addr[i * VPT + v] = kread0 + (uint32_t)(sk * TILE_B + ((i ^ tmask) * VPT + v) * 1024);
-    u32x4_t got[TPL * VPT];
-    lds_read16_wait<TPL * VPT>(got, addr);
+        for (int v = 0; v < VPT; ++v)
+          addr[i * VPT + v] = kread0 + (uint32_t)(sk * TILE_B + ((i ^ tmask) * VPT + v) * 1024);
+      u32x4_t got[TPL * VPT];
+      lds_read16_wait<TPL * VPT>(got, addr);
 #pragma unroll
-    for (int i = 0; i < TPL; ++i)
+      for (int i = 0; i < TPL; ++i)
 #pragma unroll
-      for (int v = 0; v < VPT; ++v) {
-        const u32x4_t g = got[i * VPT + v];
-        kr[i].x[v] = make_uint4(g[0], g[1], g[2], g[3]);
+        for (int v = 0; v < VPT; ++v)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) kr[i].w[4 * v + k] = got[i * VPT + v][k];
+    } else {
+      // token row (i ^ tmask) * R + r, bytes [8c, 8c + 8) of the row-major tile
+      uint32_t addr[TPL];
+#pragma unroll
+      for (int i = 0; i < TPL; ++i)
+        addr[i] = kread8 + (uint32_t)(sk * TILE_B + (i ^ tmask) * R * D * C::EB);
+      u32x2_t got[TPL];
+      lds_read8_wait<TPL>(got, addr);
+#pragma unroll
+      for (int i = 0; i < TPL; ++i) {
+        kr[i].w[0] = got[i][0];
+        kr[i].w[1] = got[i][1];
       }
+    }
   };
   {
-    const uint32_t kslot0 = lds_offset(smem) + (uint32_t)(w * KR * TILE_B);
+    const uint32_t kslot0 = lds_offset(smem) + (uint32_t)(w * KR * BPS * TILE_B);
     auto issue_k2 = [&](int phys_raw, int sk) __attribute__((always_inline)) {
       const char* src = kbase + tile_of(phys_raw);
       const uint32_t dst = kslot0 + (uint32_t)(sk * TILE_B);
 #pragma unroll
-      for (int n = 0; n < LPB; ++n) lds_dma16(src, dma_off[n], dst + n * 1024);
+      for (int n = 0; n < NDMA; ++n) lds_dma16(src, dma_off[n], dst + n * 1024);
     };
-    const int first = j0 + w;
-    const int n_my = first < j1 ? (j1 - first + NW - 1) / NW : 0;
-    TokWords<VPT> va[TPL], vb[TPL];
+    // Step t of wave w covers unit w + t * NW: the BPS attended blocks from
+    // j0 + (w + t * NW) * BPS.  A block past j1 (the partition's last unit
+    // may be short) has entry -1: its loads read block 0 of the pool and it
+    // is masked like a block outside the pool.
+    const int nunits = (j1 - j0 + BPS - 1) / BPS;
+    const int n_my = w < nunits ? (nunits - w + NW - 1) / NW : 0;
+    auto blk = [&](int t, int b2) __attribute__((always_inline)) { return j0 + (w + t * NW) * BPS + b2; };
+    auto entry_at = [&](int t, int b2) __attribute__((always_inline)) {
+      const int j = blk(t, b2);
+      if constexpr (BPS == 1) return entry_of(j);   // every step's block is in range
+      else return j < j1 ? entry_of(j) : -1;
+    };
+    TokWords<NWT> va[BPS][TPL], vb[BPS][TPL];
     constexpr unsigned kWaitVm0 = 0x0F70;     // vmcnt(0), expcnt(7), lgkmcnt(15)
-    static_assert(KR == 2, "one block in flight: K(t+1) and V(t+1) while t is computed");
+    static_assert(KR == 2, "one step in flight: K(t+1) and V(t+1) while t is computed");
     if (appends && w == append_wave) {
       append_rows();
-      if (n_my == 1) wait_vmcnt<0>();    // the new token's block is this wave's first
+      if (n_my == 1) wait_vmcnt<0>();    // the new token's block is in this wave's first step
     }
-    // bcur: the block being computed; bnext: the next one, its entry read
-    BlockRef bcur{0, 1.f, 1.f}, bnext{0, 1.f, 1.f};
+    // bcur: the blocks being computed; bnext: the next step's, entries read
+    BlockRef bcur[BPS], bnext[BPS];
+#pragma unroll
+    for (int b2 = 0; b2 < BPS; ++b2) {
+      bcur[b2] = BlockRef{-1, 1.f, 1.f};
+      bnext[b2] = BlockRef{-1, 1.f, 1.f};
+    }
     if (n_my > 0) {
-      bcur.phys = entry_of(first);
-      issue_vregs(bcur.phys, va);
-      issue_k2(bcur.phys, 0);
-      scales_of(bcur);
-      if (n_my > 1) bnext.phys = entry_of(first + NW);
+#pragma unroll
+      for (int b2 = 0; b2 < BPS; ++b2) {
+        bcur[b2].phys = entry_at(0, b2);
+        issue_vregs(bcur[b2].phys, va[b2]);
+        issue_k2(bcur[b2].phys, b2);
+        scales_of(bcur[b2]);
+      }
+      if (n_my > 1)
+#pragma unroll
+        for (int b2 = 0; b2 < BPS; ++b2) bnext[b2].phys = entry_at(1, b2);
     }
     load_query();
     // A wait the compiler sees: the query loads are complete, so it places
@@ -824,28 +890,43 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
     // prefetches in flight.
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     // Step t: K(t) and V(t) are the newest loads in flight, so wait for all,
-    // then issue block t + 1 at once: its K slot and V registers held block
-    // t - 1, already consumed, so nothing of block t has to be read first.
-    auto step = [&](int t, TokWords<VPT> (&vcur)[TPL], TokWords<VPT> (&vnext)[TPL])
+    // then issue step t + 1 at once: its K slot and V registers held step
+    // t - 1, already consumed, so nothing of step t has to be read first.
+    auto step = [&](int t, TokWords<NWT> (&vcur)[BPS][TPL], TokWords<NWT> (&vnext)[BPS][TPL])
                     __attribute__((always_inline)) {
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       wait_vmcnt<0>();                      // (asm, memory clobber) the LDS reads stay below
-      const BlockRef b0 = bcur;
+      BlockRef b0[BPS];
+#pragma unroll
+      for (int b2 = 0; b2 < BPS; ++b2) b0[b2] = bcur[b2];
       const bool more = t + 1 < n_my;
       if (more) {
-        issue_vregs(bnext.phys, vnext);
-        issue_k2(bnext.phys, (t + 1) & 1);
+#pragma unroll
+        for (int b2 = 0; b2 < BPS; ++b2) {
+          issue_vregs(bnext[b2].phys, vnext[b2]);
+          issue_k2(bnext[b2].phys, ((t + 1) & 1) * BPS + b2);
+        }
       }
-      TokWords<VPT> kr[TPL];
-      read_k(t & 1, kr);                    // waits for its reads (lgkmcnt(0))
+      TokWords<NWT> kr[TPL];
+      read_k((t & 1) * BPS, kr);            // waits for its reads (lgkmcnt(0))
       // scalar loads after that wait, which would otherwise cover them too
       if (more) {
-        scales_of(bnext);
-        bcur = bnext;
-        if (t + 2 < n_my) bnext.phys = entry_of(first + (t + 2) * NW);
+#pragma unroll
+        for (int b2 = 0; b2 < BPS; ++b2) {
+          scales_of(bnext[b2]);
+          bcur[b2] = bnext[b2];
+          if (t + 2 < n_my) bnext[b2].phys = entry_at(t + 2, b2);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);    // the loads stay ahead of the compute
-      compute_block(first + t * NW, b0, kr, vcur);
+      compute_block(blk(t, 0), b0[0], kr, vcur[0]);
+      // further blocks of the step: K read from the ring just before use,
+      // so one block's K is held at a time
+#pragma unroll
+      for (int b2 = 1; b2 < BPS; ++b2) {
+        read_k((t & 1) * BPS + b2, kr);
+        compute_block(blk(t, b2), b0[b2], kr, vcur[b2]);
+      }
     };
     int t = 0;
     for (; t + 1 < n_my; t += 2) {
@@ -952,11 +1033,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
 // above 168, the bound for three waves; holding them to it lets three
 // workgroups share a CU instead of two.  The 16-bit ones need no spill, the
 // fp8 ones one word kept across the loop; with int8 V the bound would put
-// reloads inside the loop, so those keep their natural allocation.
+// reloads inside the loop, so those keep their natural allocation.  8-bit
+// caches with 8 query heads (two blocks per step) are held to two waves:
+// fp8 fits without spills, int8 V with a few words kept across the loop.
 template <KV KT, KV VT, int D, int G>
 struct MinWaves {
   static constexpr bool fits = (KT == KV::F16 || KT == KV::BF16 || KT == KV::FP8) && VT == KT;
-  static constexpr int value = (G == 4 && D == 128 && fits) ? 3 : 1;
+  static constexpr bool eight_bit = kv_bytes<KT>::value == 1;
+  static constexpr int value = (G == 4 && D == 128 && fits) ? 3 : ((G == 8 && eight_bit) ? 2 : 1);
 };
 
 template <KV KT, KV VT, KV QT, KV OT, int D, int G>

@@ -130,6 +130,27 @@ __device__ __forceinline__ void lds_read16_wait(u32x4_t (&out)[N], const uint32_
   }
 }
 
+// The same with 8-byte reads (ds_read_b64), 2 or 4 of them.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+template <int N>
+__device__ __forceinline__ void lds_read8_wait(u32x2_t (&out)[N], const uint32_t (&addr)[N]) {
+  static_assert(N == 2 || N == 4, "2 or 4 reads");
+  if constexpr (N == 2) {
+    asm volatile(
+        "ds_read_b64 %0, %2\n\tds_read_b64 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(out[0]), "=&v"(out[1])
+        : "v"(addr[0]), "v"(addr[1])
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64 %0, %4\n\tds_read_b64 %1, %5\n\tds_read_b64 %2, %6\n\tds_read_b64 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3])
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3])
+        : "memory");
+  }
+}
+
 // LDS byte offset of a __shared__ object (the low half of its flat address).
 __device__ __forceinline__ uint32_t lds_offset(const void* p) { return (uint32_t)(uintptr_t)p; }
 

@@ -328,6 +328,7 @@ SMALL = {
     "llama70b_f16_small": scaled(WORKLOADS["llama70b_f16_80l"], num_layers=2, num_seqs=3),
     "mha13b_prefix_small": scaled(WORKLOADS["mha13b_prefix_f16"], num_seqs=6),
     "long_fp8_small": scaled(WORKLOADS["long_fp8"], num_seqs=2, len_range=(8192, 8192)),
+    "llama70b_fp8_small": scaled(WORKLOADS["llama70b_fp8_80l"], num_layers=2, num_seqs=3),
     "ragged_f16_g8_d128": _ragged("r1", "f16", "f16", "f16", 128, 8, RAGGED, 1),
     "ragged_bf16_g4_d64": _ragged("r2", "bf16", "bf16", "bf16", 64, 4, RAGGED, 2),
     "ragged_f32_g8_d128": _ragged("r3", "f32", "f32", "f32", 128, 8, RAGGED, 3),
@@ -784,7 +785,7 @@ def _compact_rows(x, layer, lay, seqs):
 
 
 @pytest.mark.parametrize("name", ["llama3_8b_bf16", "mha13b_prefix_f16", "mha13b_prefix_f16:grouped", "long_fp8",
-                                  "llama70b_f16_80l", "long_fp8k_int8v", "long_int8_kchan"])
+                                  "llama70b_f16_80l", "llama70b_fp8_80l", "long_fp8k_int8v", "long_int8_kchan"])
 def test_full_size_sampled_rows(name):
     name, _, mode = name.partition(":")
     grouped = mode == "grouped"

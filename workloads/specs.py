@@ -112,6 +112,14 @@ WORKLOADS = {
         description="long-context int8 KV, 4 outlier K channels per head with per-channel K "
                     "factors, GQA-4, B=8 x 131072, bf16 q/out",
     ),
+    "llama70b_fp8_80l": DecodeWorkload(
+        name="llama70b_fp8_80l", seed=56007, num_layers=80, num_seqs=64,
+        num_q_heads=64, num_kv_heads=8, head_dim=128,
+        kv_dtype="fp8_e4m3", q_dtype="f16", out_dtype="f16",
+        context_lens=None, len_range=(4096, 4096), append=True,
+        description="70B-shaped step with an FP8 e4m3 cache, 80 layers, GQA-8, B=64 x 4096 tokens, "
+                    "f16 q/out",
+    ),
 }
 
 
