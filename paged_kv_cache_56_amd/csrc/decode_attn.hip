@@ -26,12 +26,16 @@
 //
 // Work split.  Grid = (partition p, kv head h, sequence b); a workgroup of
 // four waves owns the blocks [p*PB, (p+1)*PB) of (b, h); wave w takes every
-// fourth of them.  K tiles are copied by LDS DMA into a per-wave ring, each
-// copy reading 1 KiB contiguously; V tiles are loaded straight into
-// registers (see "Staging" below).  Inside a wave, lane l then takes token
-// rows of group r = l / LPT of every tile and the 16-byte column c = l % LPT,
-// and keeps its slice of all g query vectors in registers for the whole
-// partition.
+// fourth step of them, a step being one block (two for 8-bit caches with 8
+// query heads, whose tiles are small).  K tiles are copied by LDS DMA into
+// a per-wave ring, each copy reading 1 KiB contiguously; V tiles are loaded
+// straight into registers (see "Staging" below).  Inside a wave, lane l then
+// takes token rows of group r = l / LPT of every tile and the column c =
+// l % LPT of LW bytes (16; 8 for 8-bit caches with 8 query heads, so that a
+// lane owns 8 channels and its accumulators fit two waves per SIMD), and
+// keeps its slice of all g query vectors in registers for the whole
+// partition.  At the end the token rows of a wave are combined with lane
+// swaps (reduce-scatter), and the waves through LDS.
 //
 // Scores.  A lane's partial dot products (g heads x its tokens) are summed
 // over the LPT lanes of its row with a DPP reduce-scatter: at every level a
