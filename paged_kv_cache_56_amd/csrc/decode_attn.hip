@@ -1032,6 +1032,27 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
   }
 }
 
+}  // namespace pkv
+
+#include "decode_mfma.h"
+
+namespace pkv {
+
+// The per-sequence pass an instantiation runs, and its LDS.
+template <KV KT, KV VT, KV QT, KV OT, int D, int G>
+__device__ __forceinline__ void cache_pass(const DecodeArgs& a, int p, int h, int b, char* smem) {
+  if constexpr (UseMfma<KT, VT, D, G>::value) decode_body_mfma<KT, VT, QT, OT, G>(a, p, h, b, smem);
+  else decode_body<KT, VT, QT, OT, D, G>(a, p, h, b, smem);
+}
+template <KV KT, KV VT, int D, int G>
+struct PassLds {
+  static constexpr int bytes() {
+    if constexpr (UseMfma<KT, VT, D, G>::value) return MCfg<KT>::template smem_bytes<G>();
+    else return Cfg<KT, D, G>::SMEM_B;
+  }
+  static constexpr int value = bytes();
+};
+
 // Waves per SIMD the register allocation must allow.  The GQA-4, D = 128
 // instantiations with 16-bit or fp8 K and V naturally land a few registers
 // above 168, the bound for three waves; holding them to it lets three
@@ -1044,14 +1065,16 @@ template <KV KT, KV VT, int D, int G>
 struct MinWaves {
   static constexpr bool fits = (KT == KV::F16 || KT == KV::BF16 || KT == KV::FP8) && VT == KT;
   static constexpr bool eight_bit = kv_bytes<KT>::value == 1;
-  static constexpr int value = (G == 4 && D == 128 && fits) ? 3 : ((G == 8 && eight_bit) ? 2 : 1);
+  static constexpr int value = UseMfma<KT, VT, D, G>::value
+                                  ? 1
+                                  : ((G == 4 && D == 128 && fits) ? 3 : ((G == 8 && eight_bit) ? 2 : 1));
 };
 
 template <KV KT, KV VT, KV QT, KV OT, int D, int G>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MinWaves<KT, VT, D, G>::value)))
 decode_partition_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[Cfg<KT, D, G>::SMEM_B];
-  decode_body<KT, VT, QT, OT, D, G>(a, blockIdx.x, blockIdx.y, blockIdx.z, smem);
+  __shared__ __attribute__((aligned(16))) char smem[PassLds<KT, VT, D, G>::value];
+  cache_pass<KT, VT, QT, OT, D, G>(a, blockIdx.x, blockIdx.y, blockIdx.z, smem);
 }
 
 // Cache pass and shared-prefix group pass in one launch: the first
@@ -1060,8 +1083,8 @@ decode_partition_kernel(DecodeArgs a) {
 // waits for the other.  Both parts use the same LDS buffer.
 template <KV T, int D, int G>
 __global__ void __launch_bounds__(256) decode_group_kernel(DecodeArgs a) {
-  static_assert(Cfg<T, D, G>::SMEM_B >= GroupLds<D>::BYTES, "one LDS buffer serves both parts");
-  __shared__ __attribute__((aligned(16))) char smem[Cfg<T, D, G>::SMEM_B];
+  static_assert(PassLds<T, T, D, G>::value >= GroupLds<D>::BYTES, "one LDS buffer serves both parts");
+  __shared__ __attribute__((aligned(16))) char smem[PassLds<T, T, D, G>::value];
   const int id = blockIdx.x;
   if (id < a.group_wgs) {
     const int pp = id % a.group_num_parts, rest = id / a.group_num_parts;
@@ -1069,7 +1092,7 @@ __global__ void __launch_bounds__(256) decode_group_kernel(DecodeArgs a) {
   } else {
     const int k = id - a.group_wgs;
     const int p = k % a.num_parts, rest = k / a.num_parts;
-    decode_body<T, T, T, T, D, G>(a, p, rest % a.num_kv_heads, rest / a.num_kv_heads, smem);
+    cache_pass<T, T, T, T, D, G>(a, p, rest % a.num_kv_heads, rest / a.num_kv_heads, smem);
   }
 }
 

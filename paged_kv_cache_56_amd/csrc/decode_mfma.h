@@ -1,0 +1,505 @@
+// Per-sequence pass of paged decode attention on the matrix cores, for
+// head_dim 128 and 4 or 8 query heads per KV head (gfx950).
+//
+// Same result as the vector pass in decode_attn.hip ("KV Cache from first
+// principles" 2.1-2.2 and 4.3): for sequence b, KV head h and its g query
+// heads, softmax(scale * q K^T) V over the attended positions, K and V
+// gathered through the block table.  One (block, KV head) tile is still read
+// once from HBM for all g heads; what changes is where the arithmetic runs.
+// With 8 heads, and 8-bit tiles that must be widened first, the vector pass
+// spends as many VALU cycles per tile as the tile takes to stream, so here
+// the two products of a tile are matrix-core operations:
+//
+//   S^T (16 tokens x 16 columns) = K (16 x 128) . Q^T (128 x 16)
+//       four v_mfma_f32_16x16x32 over the head dimension; columns >= g are
+//       padding (a zero query), so a column is a query head;
+//   O^T (128 x 16) += V^T (128 x 16 tokens) . P^T (16 tokens x 16)
+//       eight v_mfma_f32_16x16x32, one per 16-channel slice of V.
+//
+// The matrix cores idle most of the time (12 operations per 4 KiB tile); the
+// point is that the VALU work per tile drops to the softmax of four scores
+// per lane, the widening of 8-bit codes and a byte shuffle of V.
+//
+// Lane layout (l = lane, lq = l % 16, lg = l / 16):
+//   * S^T leaves lane l with head lq and tokens 4 lg + i (i < 4) of the tile;
+//   * the K operand of lane l is token lq, channels 32 lg .. 32 lg + 31 (one
+//     8-channel slice per product), staged through LDS;
+//   * the P^T operand of lane l is exactly its four probabilities, twice:
+//     contraction slots 8 lg + j hold token 4 lg + (j % 4), rounded to the
+//     operand type for j < 4 (hi) and the rounding remainder for j >= 4 (lo),
+//     so each weight enters the sum to about 22 bits (f16) / 16 bits (bf16);
+//   * the V^T operand of lane l is channel 8 lq + c (slice c) of the same
+//     four tokens, twice: the lane loads 16 (8) bytes of each of its token
+//     rows straight into registers and pairs tokens with one byte permute;
+//   * O^T leaves lane l with head lq and channels 32 lg .. 32 lg + 31.
+// So the softmax state of a head lives in the four lanes lq + 16 k, which
+// keep identical reference maxima; a rescale stays in-lane.
+//
+// K staging.  Each K tile is copied into a per-wave two-slot LDS ring by
+// non-temporal LDS DMA, every copy reading 1 KiB of HBM contiguously.  The
+// copy places the 16-byte column x of token row r at column x ^ f(r) of the
+// LDS row (f(r) = r for 256-byte rows, r / 2 for 128-byte rows), so that
+// the 16 lanes of a lane group, which read the same column of 16 different
+// rows, hit 16 different bank groups.
+//
+// Masking, append, partitions and the end-of-partition combine behave as in
+// the vector pass: positions outside the sequence or window get score -inf
+// and a zeroed V operand; the step's append is written by the wave that
+// reads the new token's block; partial results go to the workspace when
+// the call is split.
+//
+// This file is part of decode_attn.hip's translation unit: it is included
+// there after the per-dtype helpers, SeqSpan and the vector pass, whose
+// pieces it uses.
+#pragma once
+
+namespace pkv {
+
+// Instantiations that run this pass (the others keep the vector pass).
+template <KV KT, KV VT, int D, int G>
+struct UseMfma {
+  static constexpr bool value = D == 128 && (G == 4 || G == 8) && KT != KV::F32;
+};
+
+template <KV KT>
+struct MCfg {
+  static constexpr int D = 128;
+  static constexpr int EB = kv_bytes<KT>::value;
+  static constexpr int ROW_B = D * EB;            // one token row of a tile
+  static constexpr int TILE_B = 16 * ROW_B;       // one (block, KV head) tile
+  static constexpr int NDMA = TILE_B / 1024;      // 1 KiB LDS DMA copies per tile
+  static constexpr int KREADS = 64 * EB / 16;     // 16-byte LDS reads: a lane's 32 channels
+  static constexpr int VW = 2 * EB;               // V dwords per token per lane (8 channels)
+  static constexpr int NW = 4;                    // waves per workgroup
+  static constexpr int KR = 2;                    // K ring slots per wave
+  static constexpr int KRING_B = NW * KR * TILE_B;
+  template <int G>
+  static constexpr int smem_bytes() {
+    constexpr int red = NW * G * (D + 2) * 4;     // end-of-partition combine
+    return KRING_B > red ? KRING_B : red;
+  }
+};
+
+// V rows of one tile held by a lane: token 4 lg + i, channels 8 lq .. + 7.
+template <int VW> struct VRows { uint32_t w[4][VW]; };
+
+// Probabilities of four tokens -> P^T operand: hi parts of tokens 0..3, then
+// the remainders p - hi, each rounded to the operand type (RNE).
+template <KV MV>
+__device__ __forceinline__ u32x4_t p_operand(const float (&pv)[4]) {
+  uint32_t hi[2], lo[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float p0 = pv[2 * k], p1 = pv[2 * k + 1];
+    if constexpr (MV == KV::F16) {
+      hi[k] = pack_f16x2(p0, p1);
+      lo[k] = pack_f16x2(p0 - f16lo(hi[k]), p1 - f16hi(hi[k]));
+    } else {
+      const uint32_t h0 = f32_to_bf16_rne(p0), h1 = f32_to_bf16_rne(p1);
+      const uint32_t l0 = f32_to_bf16_rne(p0 - __builtin_bit_cast(float, h0 << 16));
+      const uint32_t l1 = f32_to_bf16_rne(p1 - __builtin_bit_cast(float, h1 << 16));
+      hi[k] = h0 | (h1 << 16);
+      lo[k] = l0 | (l1 << 16);
+    }
+  }
+  return u32x4_t{hi[0], hi[1], lo[0], lo[1]};
+}
+
+// V^T operand of slice c (channel 8 lq + c of the lane's four tokens, as
+// f16/bf16 pairs (token 0, token 1), (token 2, token 3), then again).
+template <KV VT, int VW>
+__device__ __forceinline__ void v_operands(const VRows<VW>& v, u32x4_t (&op)[8]) {
+  static_for<8>([&](auto cc) {
+    constexpr int c = decltype(cc)::value;
+    uint32_t p01, p23;
+    if constexpr (VT == KV::F16 || VT == KV::BF16) {
+      // dword c / 2 holds channels c & ~1 (low half) and c | 1 (high half)
+      constexpr uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+      p01 = __builtin_amdgcn_perm(v.w[1][c / 2], v.w[0][c / 2], sel);
+      p23 = __builtin_amdgcn_perm(v.w[3][c / 2], v.w[2][c / 2], sel);
+    } else if constexpr (VT == KV::INT8) {
+      // dword c / 4 holds int8 channels 4 (c / 4) .. + 3
+      p01 = i8_pair_to_f16<c % 4, c % 4>(v.w[0][c / 4], v.w[1][c / 4]);
+      p23 = i8_pair_to_f16<c % 4, c % 4>(v.w[2][c / 4], v.w[3][c / 4]);
+    } else {
+      // fp8: interleave the bytes of channels (c, c + 1) of two tokens, widen
+      // each half; odd c takes the high half of its even neighbour's word
+      constexpr uint32_t sel = ((c & 2) ? 0x07030602u : 0x05010400u);
+      const uint32_t x01 = __builtin_amdgcn_perm(v.w[1][c / 4], v.w[0][c / 4], sel);
+      const uint32_t x23 = __builtin_amdgcn_perm(v.w[3][c / 4], v.w[2][c / 4], sel);
+      p01 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x01, 1.0f, (c & 1) != 0));
+      p23 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x23, 1.0f, (c & 1) != 0));
+    }
+    op[c] = u32x4_t{p01, p23, p01, p23};
+  });
+}
+
+// K operand of slice c from the lane's 32 staged channels (kr: 16-byte LDS
+// reads in channel order).  16-bit K is used as stored; 8-bit K is widened
+// to f16 exactly.
+template <KV KT, int KREADS>
+__device__ __forceinline__ void k_operands(const u32x4_t (&kr)[KREADS], u32x4_t (&op)[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if constexpr (KT == KV::F16 || KT == KV::BF16) {
+      op[c] = kr[c];
+    } else {
+      // channels 8c .. 8c + 7: dwords 2c, 2c + 1 of the 32 bytes
+      const uint32_t d0 = kr[c / 2][(c % 2) * 2], d1 = kr[c / 2][(c % 2) * 2 + 1];
+      if constexpr (KT == KV::FP8) {
+        op[c] = u32x4_t{
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true))};
+      } else {
+        op[c] = u32x4_t{i8_pair_to_f16<0, 1>(d0, d0), i8_pair_to_f16<2, 3>(d0, d0),
+                        i8_pair_to_f16<0, 1>(d1, d1), i8_pair_to_f16<2, 3>(d1, d1)};
+      }
+    }
+  }
+}
+
+// One workgroup: partition p of (sequence b, KV head h).  smem holds
+// MCfg<KT>::smem_bytes<G>() bytes.
+template <KV KT, KV VT, KV QT, KV OT, int G>
+__device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int h, int b, char* smem) {
+  static_assert(kv_bytes<KT>::value == kv_bytes<VT>::value, "K and V share the tile layout");
+  static_assert(is_quantised<KT>() == is_quantised<VT>(), "8-bit K goes with 8-bit V");
+  static_assert(G == 4 || G == 8, "4 or 8 query heads per KV head");
+  constexpr int D = 128;
+  using C = MCfg<KT>;
+  constexpr bool KQ = is_quantised<KT>();
+  constexpr int EB = C::EB, TILE_B = C::TILE_B, NDMA = C::NDMA, KREADS = C::KREADS, VW = C::VW;
+  constexpr int NW = C::NW, KR = C::KR;
+  constexpr KV MK = KQ ? KV::F16 : KT;                    // S^T operands
+  constexpr KV MV = VT == KV::BF16 ? KV::BF16 : KV::F16;  // O^T operands
+
+  float (*red_acc)[G][D] = reinterpret_cast<float (*)[G][D]>(smem);
+  float (*red_m)[G] = reinterpret_cast<float (*)[G]>(smem + NW * G * D * 4);
+  float (*red_l)[G] = reinterpret_cast<float (*)[G]>(smem + NW * G * D * 4 + NW * G * 4);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 15, lg = lane >> 4;
+  const bool hv = lq < G;                                 // the lane's column is a query head
+  const int Hq = a.num_kv_heads * G;
+
+  const int pre = a.sink_tiles ? 0 : prefix_blocks_of_seq(a, b);
+  const SeqSpan span(a.context_lens[b], a.max_blocks, a.window, a.sinks,
+                     a.sink_tiles ? a.sinks : 16 * pre);
+  const SeqParts parts(span.natt, a.part_blocks, a.num_parts, p);
+  const int j0 = parts.j0, j1 = parts.j1;
+
+  // The step's append, as in the vector pass: the partition holding the
+  // new token's block, and in it the wave that reads that block, writes
+  // head h's new K and V rows before its wait for the block.
+  const bool appends = !KQ && a.new_slots != nullptr && p == (parts.n > 0 ? parts.n - 1 : 0);
+  const int append_wave = j1 > j0 ? (j1 - 1 - j0) % NW : 0;
+  auto append_rows = [&]() __attribute__((always_inline)) {
+    if constexpr (!KQ) {
+      const int64_t slot = a.new_slots[b];
+      constexpr int ROWC = D * EB / 16;
+      if (slot >= 0 && slot < (int64_t)a.num_blocks * 16 && lane < 2 * ROWC) {
+        const bool isv = lane >= ROWC;
+        const int ch = isv ? lane - ROWC : lane;
+        const int64_t src = ((int64_t)b * a.num_kv_heads + h) * ROWC + ch;
+        const int64_t dst = (((slot >> 4) * a.num_kv_heads + h) * 16 + (slot & 15)) * ROWC + ch;
+        reinterpret_cast<u32x4_t*>(isv ? a.v_cache_rw : a.k_cache_rw)[dst] =
+            reinterpret_cast<const u32x4_t*>(isv ? a.v_new : a.k_new)[src];
+      }
+    }
+  };
+  auto finish = [&](int ha, int d, float m, float lsum, float o) __attribute__((always_inline)) {
+    const int64_t row = (int64_t)b * Hq + h * G + ha;
+    const float res = lsum > 0.f ? o / lsum : 0.f;
+    if (!a.split) {
+      store_out<OT>(a.out, row * D + d, res);
+    } else {
+      a.o_part[(row * a.part_stride + p) * D + d] = res;
+      if (d == 0) {
+        a.ml_part[(row * a.part_stride + p) * 2 + 0] = m;
+        a.ml_part[(row * a.part_stride + p) * 2 + 1] = lsum;
+      }
+    }
+  };
+  if (j0 >= j1) {
+    if (appends && w == 0) append_rows();
+    if (!a.split)
+      for (int idx = tid; idx < G * D; idx += 256) finish(idx / D, idx % D, -INFINITY, 0.f, 0.f);
+    return;
+  }
+
+  // Q^T operand: lane holds q[head lq][32 lg + 8c .. + 7] for slice c (zero
+  // for padding columns).  8-bit K: the query times K's channel factors,
+  // scaled by a power of two per head (from the head's largest |q c|, over
+  // its four lane groups) into f16; the scores undo it.
+  u32x4_t qop[4];
+  float qfac = 1.f;
+  const int64_t qoff = ((int64_t)b * Hq + h * G + (hv ? lq : 0)) * D + lg * 32;
+  auto load_query = [&]() __attribute__((always_inline)) {
+    if constexpr (!KQ) {
+      static_assert(QT == KT, "16-bit caches take a query of the same type");
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>((const uint16_t*)a.q + qoff);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qop[c] = hv ? src[c] : u32x4_t{0u, 0u, 0u, 0u};
+    } else {
+      float f[32], cf[32];
+      const void* qrow = (QT == KV::F32) ? (const void*)((const float*)a.q + qoff)
+                                         : (const void*)((const uint16_t*)a.q + qoff);
+      q_slice_f32<QT, 32, 1, 32, 1>(qrow, 0, f);
+      if (a.k_chan) {
+        q_slice_f32<KV::F32, 32, 1, 32, 1>(a.k_chan + (int64_t)h * D + lg * 32, 0, cf);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) cf[e] = 1.0f;
+      }
+      float m = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        f[e] = hv ? f[e] * cf[e] : 0.f;
+        m = fmaxf(m, fabsf(f[e]));
+      }
+      m = across_rows<16, true>(m);
+      int ex;
+      (void)__builtin_frexpf(m, &ex);
+      int qexp = m > 0.f ? 15 - ex : 0;              // largest element in [2^14, 2^15)
+      qexp = qexp > 100 ? 100 : (qexp < -100 ? -100 : qexp);
+      qfac = __builtin_ldexpf(1.0f, -qexp);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          qop[c][k] = pack_f16x2(__builtin_ldexpf(f[8 * c + 2 * k], qexp),
+                                 __builtin_ldexpf(f[8 * c + 2 * k + 1], qexp));
+    }
+  };
+
+  f32x4_t acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float mref = -INFINITY, lsum = 0.f;
+
+  const char* kbase = (const char*)a.k_cache;
+  const char* vbase = (const char*)a.v_cache;
+  const __attribute__((address_space(4))) int32_t* table =
+      (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)b * a.max_blocks);
+
+  // LDS DMA: copy n, lane l brings 16 bytes of token row r into LDS row r,
+  // column (l % per-row) -- i.e. HBM column (l % per-row) ^ f(r).
+  uint32_t dma_off[NDMA];
+#pragma unroll
+  for (int n = 0; n < NDMA; ++n) {
+    if constexpr (EB == 2) {
+      const int r = n * 4 + lg;
+      dma_off[n] = (uint32_t)(r * 256 + ((lq ^ r) & 15) * 16);
+    } else {
+      const int r = n * 8 + (lane >> 3);
+      dma_off[n] = (uint32_t)(r * 128 + (((lane & 7) ^ (r >> 1)) & 7) * 16);
+    }
+  }
+  // LDS reads: token row lq, HBM columns holding channels 32 lg .. + 31
+  const uint32_t ring0 = lds_offset(smem) + (uint32_t)(w * KR * TILE_B);
+  uint32_t kaddr[KREADS];
+#pragma unroll
+  for (int k = 0; k < KREADS; ++k) {
+    if constexpr (EB == 2) kaddr[k] = ring0 + (uint32_t)(lq * 256 + (((lg * 4 + k) ^ lq) & 15) * 16);
+    else kaddr[k] = ring0 + (uint32_t)(lq * 128 + (((lg * 2 + k) ^ (lq >> 1)) & 7) * 16);
+  }
+  // V loads: token rows 4 lg + i, bytes [8 lq EB, + 8 EB)
+  uint32_t voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)((lg * 4 + i) * C::ROW_B + lq * 8 * EB);
+
+  struct BlockRef {
+    int phys;
+    float ks, vs;
+  };
+  auto entry_of = [&](int j) __attribute__((always_inline)) { return table[span.logical(j)]; };
+  auto tile_of = [&](int phys_raw) __attribute__((always_inline)) {
+    const int phys = ((unsigned)phys_raw < (unsigned)a.num_blocks) ? phys_raw : 0;
+    return ((int64_t)phys * a.num_kv_heads + h) * (int64_t)TILE_B;
+  };
+  auto scales_of = [&](BlockRef& br) __attribute__((always_inline)) {
+    br.ks = 1.f;
+    br.vs = 1.f;
+    if constexpr (KQ) {
+      const int phys = ((unsigned)br.phys < (unsigned)a.num_blocks) ? br.phys : 0;
+      const int64_t si = (int64_t)phys * a.num_kv_heads + h;
+      br.ks = ((const __attribute__((address_space(4))) float*)a.k_scales)[si];
+      br.vs = ((const __attribute__((address_space(4))) float*)a.v_scales)[si];
+    }
+  };
+  auto issue_v = [&](int phys_raw, VRows<VW>& vr) __attribute__((always_inline)) {
+    const char* src = vbase + tile_of(phys_raw);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (VW == 4) {
+        const uint4 x = *(const uint4*)(src + voff[i]);
+        vr.w[i][0] = x.x; vr.w[i][1] = x.y; vr.w[i][2] = x.z; vr.w[i][3] = x.w;
+      } else {
+        const uint2 x = *(const uint2*)(src + voff[i]);
+        vr.w[i][0] = x.x; vr.w[i][1] = x.y;
+      }
+    }
+  };
+  const uint32_t kslot0 = lds_offset(smem) + (uint32_t)(w * KR * TILE_B);
+  auto issue_k = [&](int phys_raw, int sk) __attribute__((always_inline)) {
+    const char* src = kbase + tile_of(phys_raw);
+    const uint32_t dst = kslot0 + (uint32_t)(sk * TILE_B);
+#pragma unroll
+    for (int n = 0; n < NDMA; ++n) lds_dma16(src, dma_off[n], dst + n * 1024);
+  };
+  auto read_k = [&](int sk, u32x4_t (&kr)[KREADS]) __attribute__((always_inline)) {
+    uint32_t addr[KREADS];
+#pragma unroll
+    for (int k = 0; k < KREADS; ++k) addr[k] = kaddr[k] + (uint32_t)(sk * TILE_B);
+    lds_read16_wait<KREADS>(kr, addr);
+  };
+
+  // One tile: scores, online softmax, P.V.  vr is consumed (masked rows zeroed).
+  auto compute_block = [&](int j, const BlockRef& br, const u32x4_t (&kr)[KREADS], VRows<VW>& vr)
+                           __attribute__((always_inline)) {
+    const int jl = span.logical(j);
+    const bool blk_ok = (unsigned)br.phys < (unsigned)a.num_blocks;
+    const uint32_t vbits = blk_ok ? span.valid_bits(jl) : 0u;
+    float cs = a.scale;  // scale * log2(e), folded on the host
+    float vsc = 1.f;
+    if constexpr (KQ) {
+      cs *= br.ks * qfac;
+      vsc = br.vs;
+    }
+    u32x4_t kop[4];
+    k_operands<KT, KREADS>(kr, kop);
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s = Mma<MK>::run(kop[c], qop[c], s);
+
+    // this lane's tokens 4 lg + i, for a real head
+    const uint32_t mine = hv ? (vbits >> (lg * 4)) & 0xFu : 0u;
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = ((mine >> i) & 1u) ? s[i] * cs : -INFINITY;
+    if (vbits != 0xFFFFu) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!((vbits >> (lg * 4 + i)) & 1u)) {
+#pragma unroll
+          for (int k = 0; k < VW; ++k) vr.w[i][k] = 0u;
+        }
+    }
+
+    // move the head's reference maximum if a score passed it by > slack;
+    // the head's four lane groups agree on the new value
+    bool need = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) need |= sc[i] > mref + kLazyMaxSlack;
+    if (__any(need)) {
+      float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      bm = across_rows<16, true>(bm);
+      const float mnew = fmaxf(mref, bm);
+      const float f = exp2_safe_factor(mref, mnew);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] *= f;
+      lsum *= f;
+      mref = mnew;
+    }
+    const float mo = mref == -INFINITY ? 0.f : mref;
+    float pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pe = __builtin_amdgcn_exp2f(sc[i] - mo);
+      lsum += pe;
+      pv[i] = pe * vsc;
+    }
+    const u32x4_t pop = p_operand<MV>(pv);
+    u32x4_t vop[8];
+    v_operands<VT, VW>(vr, vop);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = Mma<MV>::run(vop[c], pop, acc[c]);
+  };
+
+  {
+    // wave w takes blocks j0 + w, j0 + w + NW, ...
+    const int nunits = j1 - j0;
+    const int n_my = w < nunits ? (nunits - w + NW - 1) / NW : 0;
+    auto blk = [&](int t) __attribute__((always_inline)) { return j0 + w + t * NW; };
+    VRows<VW> va, vb;
+    constexpr unsigned kWaitVm0 = 0x0F70;     // vmcnt(0), expcnt(7), lgkmcnt(15)
+    static_assert(KR == 2, "one step in flight: K(t+1) and V(t+1) while t is computed");
+    if (appends && w == append_wave) {
+      append_rows();
+      if (n_my == 1) wait_vmcnt<0>();
+    }
+    BlockRef bcur{-1, 1.f, 1.f}, bnext{-1, 1.f, 1.f};
+    if (n_my > 0) {
+      bcur.phys = entry_of(blk(0));
+      issue_v(bcur.phys, va);
+      issue_k(bcur.phys, 0);
+      scales_of(bcur);
+      if (n_my > 1) bnext.phys = entry_of(blk(1));
+    }
+    load_query();
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    auto step = [&](int t, VRows<VW>& vcur, VRows<VW>& vnext) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      wait_vmcnt<0>();
+      const BlockRef b0 = bcur;
+      const bool more = t + 1 < n_my;
+      if (more) {
+        issue_v(bnext.phys, vnext);
+        issue_k(bnext.phys, (t + 1) & 1);
+      }
+      u32x4_t kr[KREADS];
+      read_k(t & 1, kr);
+      if (more) {
+        scales_of(bnext);
+        bcur = bnext;
+        if (t + 2 < n_my) bnext.phys = entry_of(blk(t + 2));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      compute_block(blk(t), b0, kr, vcur);
+    };
+    int t = 0;
+    for (; t + 1 < n_my; t += 2) {
+      step(t, va, vb);
+      step(t + 1, vb, va);
+    }
+    if (t < n_my) step(t, va, vb);
+  }
+  __syncthreads();  // every wave is done with its ring: the LDS is reused below
+
+  // A head's sum over the wave's four lane groups; its accumulators are
+  // already complete per lane (lane lq + 16 lg owns channels 32 lg .. + 31).
+  const float lw = across_rows<16, false>(lsum);
+  if (hv) {
+    float* dst = &red_acc[w][lq][lg * 32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *(float4*)(dst + i * 8) = float4{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+      *(float4*)(dst + i * 8 + 4) = float4{acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
+    }
+    if (lg == 0) {
+      red_m[w][lq] = mref;
+      red_l[w][lq] = lw;
+    }
+  }
+  __syncthreads();
+
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int ha = idx / D, d = idx % D;
+    float m = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) m = fmaxf(m, red_m[ww][ha]);
+    float ls = 0.f, o = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float f = red_m[ww][ha] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(red_m[ww][ha] - m);
+      ls += red_l[ww][ha] * f;
+      o += red_acc[ww][ha][d] * f;
+    }
+    finish(ha, d, m, ls, o);
+  }
+}
+
+}  // namespace pkv
