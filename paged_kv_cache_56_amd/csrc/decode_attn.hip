@@ -1,6 +1,8 @@
 // Paged decode attention for gfx950 (CDNA4, wave64).  The per-sequence pass
-// below uses no MFMA; the shared-prefix group pass (group_prefix.h), which
-// it can carry in the same launch, does.
+// below does its arithmetic on the VALU; for head_dim 128 with 4 or 8 query
+// heads per KV head the kernels run its matrix-core form instead
+// (decode_mfma.h), and the shared-prefix group pass (group_prefix.h), which
+// the per-sequence pass can carry in the same launch, also uses MFMA.
 //
 // What is computed ("KV Cache from first principles" 2.1-2.2 and 4.3; "The
 // KV Cache memory ledger" 2 and 4): for every sequence b and query head i,

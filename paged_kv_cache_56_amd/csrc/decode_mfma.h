@@ -95,11 +95,10 @@ __device__ __forceinline__ u32x4_t p_operand(const float (&pv)[4]) {
       hi[k] = pack_f16x2(p0, p1);
       lo[k] = pack_f16x2(p0 - f16lo(hi[k]), p1 - f16hi(hi[k]));
     } else {
-      const uint32_t h0 = f32_to_bf16_rne(p0), h1 = f32_to_bf16_rne(p1);
-      const uint32_t l0 = f32_to_bf16_rne(p0 - __builtin_bit_cast(float, h0 << 16));
-      const uint32_t l1 = f32_to_bf16_rne(p1 - __builtin_bit_cast(float, h1 << 16));
-      hi[k] = h0 | (h1 << 16);
-      lo[k] = l0 | (l1 << 16);
+      // one v_cvt_pk_bf16_f32 (round to nearest even) per pair
+      hi[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{p0, p1}, bf162_t));
+      lo[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                                               float2_t{p0 - bf16lo(hi[k]), p1 - bf16hi(hi[k])}, bf162_t));
     }
   }
   return u32x4_t{hi[0], hi[1], lo[0], lo[1]};

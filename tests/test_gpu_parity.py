@@ -359,6 +359,9 @@ SMALL = {
                                                          [1, 2, 3, 4, 17, 100], 17, hkv=2, append=True,
                                                          v="int8", outliers=2, fp_sinks=3),
     "long_fp8_fpsinks_small": scaled(WORKLOADS["long_fp8"], num_seqs=2, len_range=(8192, 8192), fp_sinks=4),
+    # 8-bit caches on the matrix-core pass with an f32 query, or an f32 output
+    "ragged_fp8_g4_d128_f32": _ragged("r19", "fp8_e4m3", "f32", "f32", 128, 4, RAGGED, 19),
+    "ragged_fp8_g8_d128_bf16_f32out": _ragged("r20", "fp8_e4m3", "bf16", "f32", 128, 8, RAGGED, 20, hkv=3),
     # one long sequence among short ones: the batch-size hint changes the split plan
     "one_long_many_short_f16": _ragged("r18", "f16", "f16", "f16", 128, 4, [8192] + [20, 3, 47, 16] * 4, 18),
 }
