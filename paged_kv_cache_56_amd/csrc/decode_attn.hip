@@ -1115,6 +1115,22 @@ __global__ void __launch_bounds__(64) lse_merge_kernel(DecodeArgs a) {
   const int row = blockIdx.x;
   const int b = row / a.num_q_heads;
   const int lane = threadIdx.x;
+  const float* ml = a.ml_part + (int64_t)row * a.part_stride * 2;
+  const float* op = a.o_part + (int64_t)row * a.part_stride * D;
+  // The row's first U workspace slots are loaded before its length is known
+  // (which of them were written depends on it), so their round trip
+  // overlaps the lookups below; slots past the row's stride re-read the
+  // last one and are ignored.
+  constexpr int U = 4;
+  float mi0[U], li0[U], oi0[U][PER];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int sl = min(u, a.part_stride - 1);
+    mi0[u] = ml[2 * sl];
+    li0[u] = ml[2 * sl + 1];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) oi0[u][k] = op[(int64_t)sl * D + k * 64 + lane];
+  }
   const int pre = a.sink_tiles ? 0 : prefix_blocks_of_seq(a, b);
   const SeqSpan span(a.context_lens[b], a.max_blocks, a.window, a.sinks,
                      a.sink_tiles ? a.sinks : 16 * pre);
@@ -1122,8 +1138,9 @@ __global__ void __launch_bounds__(64) lse_merge_kernel(DecodeArgs a) {
   // those of the shared-prefix pass
   const int np = SeqParts(span.natt, a.part_blocks, a.num_parts, 0).n;
   const int ng = pre > 0 ? SeqParts(pre, a.group_part_blocks, a.group_num_parts, 0).n : 0;
-  const float* ml = a.ml_part + (int64_t)row * a.part_stride * 2;
-  const float* op = a.o_part + (int64_t)row * a.part_stride * D;
+  auto written = [&](int sl) __attribute__((always_inline)) {
+    return sl < np || (sl >= a.num_parts && sl < a.num_parts + ng);
+  };
 
   float ms = -INFINITY, ls = 0.f, os[PER];
 #pragma unroll
@@ -1157,17 +1174,32 @@ __global__ void __launch_bounds__(64) lse_merge_kernel(DecodeArgs a) {
 
   // One pass with a running reference (the sink term first): every
   // partition joins as l_p 2^(m_p - M) o_p, the sum rescaled when M moves.
-  // Slots are read four at a time with unconditional loads (an index past
-  // the end re-reads the last slot and is then ignored), so their latencies
-  // overlap.
-  const int n = np + ng;
   float m = ls > 0.f ? ms : -INFINITY;
   float wsum = ls > 0.f ? ls : 0.f;
   float o[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) o[k] = ls > 0.f ? os[k] : 0.f;
-  constexpr int U = 4;
-  for (int i0 = 0; i0 < n; i0 += U) {
+  auto join = [&](float mp, float lp, const float (&opp)[PER]) __attribute__((always_inline)) {
+    if (!(lp > 0.f)) return;
+    const float mn = fmaxf(m, mp);
+    const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+    const float g = lp * __builtin_amdgcn_exp2f(mp - mn);
+    wsum = __builtin_fmaf(wsum, f, g);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) o[k] = __builtin_fmaf(o[k], f, g * opp[k]);
+    m = mn;
+  };
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (u < a.part_stride && written(u)) join(mi0[u], li0[u], oi0[u]);
+  // The written slots from U on: the rest of the per-sequence pieces, then
+  // the group pieces, read U at a time with unconditional loads (an index
+  // past the end re-reads the last slot and is then ignored), so their
+  // latencies overlap.
+  const int n = np + ng;
+  int i0 = 0;
+  while (i0 < n && (i0 < np ? i0 : a.num_parts + (i0 - np)) < U) ++i0;
+  for (; i0 < n; i0 += U) {
     float mi[U], li[U], oi[U][PER];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -1180,14 +1212,9 @@ __global__ void __launch_bounds__(64) lse_merge_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (i0 + u >= n || !(li[u] > 0.f)) continue;
-      const float mn = fmaxf(m, mi[u]);
-      const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
-      const float g = li[u] * __builtin_amdgcn_exp2f(mi[u] - mn);
-      wsum = __builtin_fmaf(wsum, f, g);
-#pragma unroll
-      for (int k = 0; k < PER; ++k) o[k] = __builtin_fmaf(o[k], f, g * oi[u][k]);
-      m = mn;
+      const int i = i0 + u;
+      if (i >= n || (i < np ? i : a.num_parts + (i - np)) < U) continue;
+      join(mi[u], li[u], oi[u]);
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
