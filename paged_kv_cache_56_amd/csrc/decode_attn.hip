@@ -428,6 +428,112 @@ struct SeqSpan {
   }
 };
 
+// ---- pieces both per-sequence passes share --------------------------------
+// The step's append, when the call carries it ("KV Cache from first
+// principles" 2.3: the new token's K and V are written at the current
+// length before it is attended).  The partition holding the sequence's last
+// attended block -- the new token's -- writes head h's new rows into the
+// slot, and within it the wave that will read that block, so the write
+// needs no barrier: the wave's read of the block is issued after a wait for
+// all its memory operations (the per-step wait, or an explicit one when
+// that block is the wave's first).  No other workgroup reads the block.
+// Partition 0 writes when nothing is attended.  One wave: a K row and a V
+// row, 16 bytes per lane.
+template <int D, int EB>
+__device__ __forceinline__ void append_new_rows(const DecodeArgs& a, int b, int h, int lane) {
+  const int64_t slot = a.new_slots[b];
+  constexpr int ROWC = D * EB / 16;   // 16-byte chunks of one row
+  static_assert(2 * ROWC <= 64, "one wave copies a K row and a V row");
+  if (slot >= 0 && slot < (int64_t)a.num_blocks * 16 && lane < 2 * ROWC) {
+    const bool isv = lane >= ROWC;
+    const int ch = isv ? lane - ROWC : lane;
+    const int64_t src = ((int64_t)b * a.num_kv_heads + h) * ROWC + ch;
+    const int64_t dst = (((slot >> 4) * a.num_kv_heads + h) * 16 + (slot & 15)) * ROWC + ch;
+    reinterpret_cast<u32x4_t*>(isv ? a.v_cache_rw : a.k_cache_rw)[dst] =
+        reinterpret_cast<const u32x4_t*>(isv ? a.v_new : a.k_new)[src];
+  }
+}
+
+// Partition p's result for query head h * G + ha of sequence b, channel d,
+// from its (m, l, o), o being the unnormalised sum: the output element, or
+// the partition's workspace slot when the call is split.
+template <KV OT, int D, int G>
+__device__ __forceinline__ void finish_row(const DecodeArgs& a, int b, int h, int p, int ha, int d, float m,
+                                           float lsum, float o) {
+  const int64_t row = (int64_t)b * a.num_kv_heads * G + h * G + ha;
+  const float res = lsum > 0.f ? o / lsum : 0.f;
+  if (!a.split) {
+    store_out<OT>(a.out, row * D + d, res);
+  } else {
+    a.o_part[(row * a.part_stride + p) * D + d] = res;
+    if (d == 0) {
+      a.ml_part[(row * a.part_stride + p) * 2 + 0] = m;
+      a.ml_part[(row * a.part_stride + p) * 2 + 1] = lsum;
+    }
+  }
+}
+
+// A partition with nothing of the cache: a zero row (empty partitions of a
+// split call are skipped by the merge), and the append if it falls here.
+template <KV OT, int D, int G, int EB>
+__device__ __forceinline__ void finish_empty(const DecodeArgs& a, int b, int h, int p, int tid, bool append) {
+  if constexpr (EB > 1)
+    if (append) append_new_rows<D, EB>(a, b, h, tid & 63);
+  if (!a.split)
+    for (int idx = tid; idx < G * D; idx += 256) finish_row<OT, D, G>(a, b, h, p, idx / D, idx % D, -INFINITY, 0.f, 0.f);
+}
+
+// A block's table entry, as read (an id outside the pool masks the whole
+// block), and its 8-bit scales.
+struct BlockRef {
+  int phys;
+  float ks, vs;
+};
+
+// Byte offset of tile (block, KV head h) in a cache; an id outside the
+// pool reads block 0 (and is masked).
+__device__ __forceinline__ int64_t tile_offset(const DecodeArgs& a, int h, int phys_raw, int tile_bytes) {
+  const int phys = ((unsigned)phys_raw < (unsigned)a.num_blocks) ? phys_raw : 0;
+  return ((int64_t)phys * a.num_kv_heads + h) * (int64_t)tile_bytes;
+}
+
+// The block's K and V scales (8-bit caches; 1 otherwise).  Uniform index,
+// read-only data: scalar loads, which do not wait behind the tile copies in
+// flight (those count on vmcnt).
+template <bool KQ>
+__device__ __forceinline__ void block_scales(const DecodeArgs& a, int h, BlockRef& br) {
+  br.ks = 1.f;
+  br.vs = 1.f;
+  if constexpr (KQ) {
+    const int phys = ((unsigned)br.phys < (unsigned)a.num_blocks) ? br.phys : 0;
+    const int64_t si = (int64_t)phys * a.num_kv_heads + h;
+    br.ks = ((const __attribute__((address_space(4))) float*)a.k_scales)[si];
+    br.vs = ((const __attribute__((address_space(4))) float*)a.v_scales)[si];
+  }
+}
+
+// End of a partition: every wave's (reference maximum, sum, accumulators)
+// is in LDS; each thread combines them for G * D / 256 outputs.
+template <KV OT, int D, int G, int NW>
+__device__ __forceinline__ void combine_waves(const DecodeArgs& a, int b, int h, int p, int tid,
+                                              const float (*red_acc)[G][D], const float (*red_m)[G],
+                                              const float (*red_l)[G]) {
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int ha = idx / D, d = idx % D;
+    float m = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) m = fmaxf(m, red_m[ww][ha]);
+    float lsum = 0.f, o = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float f = red_m[ww][ha] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(red_m[ww][ha] - m);
+      lsum += red_l[ww][ha] * f;
+      o += red_acc[ww][ha][d] * f;
+    }
+    finish_row<OT, D, G>(a, b, h, p, ha, d, m, lsum, o);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // One workgroup of the cache pass: partition p of (sequence b, KV head h);
 // smem is the workgroup's LDS (Cfg::SMEM_B bytes).
@@ -462,55 +568,16 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
   const SeqParts parts(span.natt, a.part_blocks, a.num_parts, p);
   const int j0 = parts.j0, j1 = parts.j1;
 
-  // The step's append, when the call carries it ("KV Cache from first
-  // principles" 2.3: the new token's K and V are written at the current
-  // length before it is attended).  The partition holding the sequence's
-  // last attended block -- the new token's -- writes head h's new rows into
-  // the slot, and within it the wave that will read that block, so the
-  // write needs no barrier: the wave's read of the block is issued after a
-  // wait for all its memory operations (the per-step wait, or the explicit
-  // one below when that block is the wave's first).  No other workgroup
-  // reads the block.  Partition 0 writes when nothing is attended.
+  // the step's append (append_new_rows): by the partition holding the new
+  // token's block, and in it by the wave that reads that block
   const bool appends = !KQ && a.new_slots != nullptr && p == (parts.n > 0 ? parts.n - 1 : 0);
   constexpr int BPS = C::BPS;
   const int append_wave = j1 > j0 ? ((j1 - 1 - j0) / BPS) % NW : 0;
   auto append_rows = [&]() __attribute__((always_inline)) {
-    if constexpr (!KQ) {
-      const int64_t slot = a.new_slots[b];
-      constexpr int ROWC = D * C::EB / 16;   // 16-byte chunks of one row
-      static_assert(2 * ROWC <= 64, "one wave copies a K row and a V row");
-      if (slot >= 0 && slot < (int64_t)a.num_blocks * 16 && lane < 2 * ROWC) {
-        const bool isv = lane >= ROWC;
-        const int ch = isv ? lane - ROWC : lane;
-        const int64_t src = ((int64_t)b * a.num_kv_heads + h) * ROWC + ch;
-        const int64_t dst = (((slot >> 4) * a.num_kv_heads + h) * 16 + (slot & 15)) * ROWC + ch;
-        reinterpret_cast<u32x4_t*>(isv ? a.v_cache_rw : a.k_cache_rw)[dst] =
-            reinterpret_cast<const u32x4_t*>(isv ? a.v_new : a.k_new)[src];
-      }
-    }
-  };
-
-  // Writes row (b, h*G + ha), channel d, from this partition's (m, l, o),
-  // o being the unnormalised sum.
-  auto finish = [&](int ha, int d, float m, float lsum, float o) __attribute__((always_inline)) {
-    const int64_t row = (int64_t)b * Hq + h * G + ha;
-    const float res = lsum > 0.f ? o / lsum : 0.f;
-    if (!a.split) {
-      store_out<OT>(a.out, row * D + d, res);
-    } else {
-      a.o_part[(row * a.part_stride + p) * D + d] = res;
-      if (d == 0) {
-        a.ml_part[(row * a.part_stride + p) * 2 + 0] = m;
-        a.ml_part[(row * a.part_stride + p) * 2 + 1] = lsum;
-      }
-    }
+    if constexpr (!KQ) append_new_rows<D, C::EB>(a, b, h, lane);
   };
   if (j0 >= j1) {
-    // nothing of the cache here: a zero row; empty partitions of a split
-    // call are skipped by the merge
-    if (appends && w == 0) append_rows();
-    if (!a.split)
-      for (int idx = tid; idx < G * D; idx += 256) finish(idx / D, idx % D, -INFINITY, 0.f, 0.f);
+    finish_empty<OT, D, G, C::EB>(a, b, h, p, tid, appends && w == 0);
     return;
   }
 
@@ -612,32 +679,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
 #pragma unroll
     for (int n = 0; n < NDMA; ++n) dma_off[n] = (uint32_t)(n * 1024 + lane * 16);
   }
-  // A block's table entry, read as raw (an id outside the pool masks the
-  // whole block), and its 8-bit scales.  The entry is read two steps before
-  // the step that computes the block and the scales one step before, so
-  // neither scalar load's latency sits between a step's wait and its next
-  // tile loads.
-  struct BlockRef {
-    int phys;
-    float ks, vs;
-  };
+  // A block's table entry is read two steps before the step that computes
+  // the block and its scales one step before, so neither scalar load's
+  // latency sits between a step's wait and its next tile loads.
   auto entry_of = [&](int j) __attribute__((always_inline)) { return table[span.logical(j)]; };
-  auto tile_of = [&](int phys_raw) __attribute__((always_inline)) {
-    const int phys = ((unsigned)phys_raw < (unsigned)a.num_blocks) ? phys_raw : 0;
-    return ((int64_t)phys * a.num_kv_heads + h) * (int64_t)TILE_B;
-  };
-  auto scales_of = [&](BlockRef& br) __attribute__((always_inline)) {
-    br.ks = 1.f;
-    br.vs = 1.f;
-    if constexpr (KQ) {
-      // uniform index, read-only data: scalar loads, which do not wait
-      // behind the tile copies in flight (those count on vmcnt)
-      const int phys = ((unsigned)br.phys < (unsigned)a.num_blocks) ? br.phys : 0;
-      const int64_t si = (int64_t)phys * a.num_kv_heads + h;
-      br.ks = ((const __attribute__((address_space(4))) float*)a.k_scales)[si];
-      br.vs = ((const __attribute__((address_space(4))) float*)a.v_scales)[si];
-    }
-  };
+  auto tile_of = [&](int phys_raw) __attribute__((always_inline)) { return tile_offset(a, h, phys_raw, TILE_B); };
+  auto scales_of = [&](BlockRef& br) __attribute__((always_inline)) { block_scales<KQ>(a, h, br); };
   // vr is consumed: tokens outside the sequence (or window) are zeroed in it.
   auto compute_block = [&](int j, const BlockRef& br, const TokWords<NWT> (&kr)[TPL],
                            TokWords<NWT> (&vr)[TPL]) __attribute__((always_inline)) {
@@ -1017,21 +1064,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
     }
   }
   __syncthreads();
-
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int ha = idx / D, d = idx % D;
-    float m = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) m = fmaxf(m, red_m[ww][ha]);
-    float lsum = 0.f, o = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      const float f = red_m[ww][ha] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(red_m[ww][ha] - m);
-      lsum += red_l[ww][ha] * f;
-      o += red_acc[ww][ha][d] * f;
-    }
-    finish(ha, d, m, lsum, o);
-  }
+  combine_waves<OT, D, G, NW>(a, b, h, p, tid, red_acc, red_m, red_l);
 }
 
 }  // namespace pkv

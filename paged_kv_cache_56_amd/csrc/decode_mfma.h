@@ -184,48 +184,35 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
   const bool hv = lq < G;                                 // the lane's column is a query head
   const int Hq = a.num_kv_heads * G;
 
+  // The block table is read-only for the whole kernel: reading it through
+  // the constant address space makes every entry a scalar load, which never
+  // waits behind the tile copies in flight.  With 16-bit caches the wave's
+  // first two entries of partition 0 are read here, next to the sequence's
+  // length, so that a partition starting at block 0 with nothing skipped
+  // (every launch of an unsplit, unwindowed batch) does not wait for the
+  // length before them: 70B-shaped f16 step 173.4 -> 168.7 us per launch in
+  // a same-box A/B.  The 70B-shaped fp8 step measured ~1.5% slower with it.
+  constexpr bool EARLY = !KQ;
+  const __attribute__((address_space(4))) int32_t* table =
+      (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)b * a.max_blocks);
+  const int e0 = EARLY && w < a.max_blocks ? table[w] : -1;
+  const int e1 = EARLY && w + NW < a.max_blocks ? table[w + NW] : -1;
   const int pre = a.sink_tiles ? 0 : prefix_blocks_of_seq(a, b);
   const SeqSpan span(a.context_lens[b], a.max_blocks, a.window, a.sinks,
                      a.sink_tiles ? a.sinks : 16 * pre);
   const SeqParts parts(span.natt, a.part_blocks, a.num_parts, p);
   const int j0 = parts.j0, j1 = parts.j1;
+  const bool from_zero = EARLY && j0 == 0 && span.nsb == 0 && span.wb0 == 0;   // entry j is table[j]
 
-  // The step's append, as in the vector pass: the partition holding the
-  // new token's block, and in it the wave that reads that block, writes
-  // head h's new K and V rows before its wait for the block.
+  // the step's append (append_new_rows): by the partition holding the new
+  // token's block, and in it by the wave that reads that block
   const bool appends = !KQ && a.new_slots != nullptr && p == (parts.n > 0 ? parts.n - 1 : 0);
   const int append_wave = j1 > j0 ? (j1 - 1 - j0) % NW : 0;
   auto append_rows = [&]() __attribute__((always_inline)) {
-    if constexpr (!KQ) {
-      const int64_t slot = a.new_slots[b];
-      constexpr int ROWC = D * EB / 16;
-      if (slot >= 0 && slot < (int64_t)a.num_blocks * 16 && lane < 2 * ROWC) {
-        const bool isv = lane >= ROWC;
-        const int ch = isv ? lane - ROWC : lane;
-        const int64_t src = ((int64_t)b * a.num_kv_heads + h) * ROWC + ch;
-        const int64_t dst = (((slot >> 4) * a.num_kv_heads + h) * 16 + (slot & 15)) * ROWC + ch;
-        reinterpret_cast<u32x4_t*>(isv ? a.v_cache_rw : a.k_cache_rw)[dst] =
-            reinterpret_cast<const u32x4_t*>(isv ? a.v_new : a.k_new)[src];
-      }
-    }
-  };
-  auto finish = [&](int ha, int d, float m, float lsum, float o) __attribute__((always_inline)) {
-    const int64_t row = (int64_t)b * Hq + h * G + ha;
-    const float res = lsum > 0.f ? o / lsum : 0.f;
-    if (!a.split) {
-      store_out<OT>(a.out, row * D + d, res);
-    } else {
-      a.o_part[(row * a.part_stride + p) * D + d] = res;
-      if (d == 0) {
-        a.ml_part[(row * a.part_stride + p) * 2 + 0] = m;
-        a.ml_part[(row * a.part_stride + p) * 2 + 1] = lsum;
-      }
-    }
+    if constexpr (!KQ) append_new_rows<D, EB>(a, b, h, lane);
   };
   if (j0 >= j1) {
-    if (appends && w == 0) append_rows();
-    if (!a.split)
-      for (int idx = tid; idx < G * D; idx += 256) finish(idx / D, idx % D, -INFINITY, 0.f, 0.f);
+    finish_empty<OT, D, G, EB>(a, b, h, p, tid, appends && w == 0);
     return;
   }
 
@@ -281,8 +268,6 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
 
   const char* kbase = (const char*)a.k_cache;
   const char* vbase = (const char*)a.v_cache;
-  const __attribute__((address_space(4))) int32_t* table =
-      (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)b * a.max_blocks);
 
   // LDS DMA: copy n, lane l brings 16 bytes of token row r into LDS row r,
   // column (l % per-row) -- i.e. HBM column (l % per-row) ^ f(r).
@@ -310,25 +295,9 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
 #pragma unroll
   for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)((lg * 4 + i) * C::ROW_B + lq * 8 * EB);
 
-  struct BlockRef {
-    int phys;
-    float ks, vs;
-  };
   auto entry_of = [&](int j) __attribute__((always_inline)) { return table[span.logical(j)]; };
-  auto tile_of = [&](int phys_raw) __attribute__((always_inline)) {
-    const int phys = ((unsigned)phys_raw < (unsigned)a.num_blocks) ? phys_raw : 0;
-    return ((int64_t)phys * a.num_kv_heads + h) * (int64_t)TILE_B;
-  };
-  auto scales_of = [&](BlockRef& br) __attribute__((always_inline)) {
-    br.ks = 1.f;
-    br.vs = 1.f;
-    if constexpr (KQ) {
-      const int phys = ((unsigned)br.phys < (unsigned)a.num_blocks) ? br.phys : 0;
-      const int64_t si = (int64_t)phys * a.num_kv_heads + h;
-      br.ks = ((const __attribute__((address_space(4))) float*)a.k_scales)[si];
-      br.vs = ((const __attribute__((address_space(4))) float*)a.v_scales)[si];
-    }
-  };
+  auto tile_of = [&](int phys_raw) __attribute__((always_inline)) { return tile_offset(a, h, phys_raw, TILE_B); };
+  auto scales_of = [&](BlockRef& br) __attribute__((always_inline)) { block_scales<KQ>(a, h, br); };
   auto issue_v = [&](int phys_raw, VRows<VW>& vr) __attribute__((always_inline)) {
     const char* src = vbase + tile_of(phys_raw);
 #pragma unroll
@@ -432,11 +401,11 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
     }
     BlockRef bcur{-1, 1.f, 1.f}, bnext{-1, 1.f, 1.f};
     if (n_my > 0) {
-      bcur.phys = entry_of(blk(0));
+      bcur.phys = from_zero ? e0 : entry_of(blk(0));
       issue_v(bcur.phys, va);
       issue_k(bcur.phys, 0);
       scales_of(bcur);
-      if (n_my > 1) bnext.phys = entry_of(blk(1));
+      if (n_my > 1) bnext.phys = from_zero ? e1 : entry_of(blk(1));
     }
     load_query();
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -484,21 +453,7 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
     }
   }
   __syncthreads();
-
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int ha = idx / D, d = idx % D;
-    float m = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) m = fmaxf(m, red_m[ww][ha]);
-    float ls = 0.f, o = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      const float f = red_m[ww][ha] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(red_m[ww][ha] - m);
-      ls += red_l[ww][ha] * f;
-      o += red_acc[ww][ha][d] * f;
-    }
-    finish(ha, d, m, ls, o);
-  }
+  combine_waves<OT, D, G, NW>(a, b, h, p, tid, red_acc, red_m, red_l);
 }
 
 }  // namespace pkv
