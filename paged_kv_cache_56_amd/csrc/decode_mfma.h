@@ -184,25 +184,11 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
   const bool hv = lq < G;                                 // the lane's column is a query head
   const int Hq = a.num_kv_heads * G;
 
-  // The block table is read-only for the whole kernel: reading it through
-  // the constant address space makes every entry a scalar load, which never
-  // waits behind the tile copies in flight.  With 16-bit caches the wave's
-  // first two entries of partition 0 are read here, next to the sequence's
-  // length, so that a partition starting at block 0 with nothing skipped
-  // (every launch of an unsplit, unwindowed batch) does not wait for the
-  // length before them: 70B-shaped f16 step 173.4 -> 168.7 us per launch in
-  // a same-box A/B.  The 70B-shaped fp8 step measured ~1.5% slower with it.
-  constexpr bool EARLY = !KQ;
-  const __attribute__((address_space(4))) int32_t* table =
-      (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)b * a.max_blocks);
-  const int e0 = EARLY && w < a.max_blocks ? table[w] : -1;
-  const int e1 = EARLY && w + NW < a.max_blocks ? table[w + NW] : -1;
   const int pre = a.sink_tiles ? 0 : prefix_blocks_of_seq(a, b);
   const SeqSpan span(a.context_lens[b], a.max_blocks, a.window, a.sinks,
                      a.sink_tiles ? a.sinks : 16 * pre);
   const SeqParts parts(span.natt, a.part_blocks, a.num_parts, p);
   const int j0 = parts.j0, j1 = parts.j1;
-  const bool from_zero = EARLY && j0 == 0 && span.nsb == 0 && span.wb0 == 0;   // entry j is table[j]
 
   // the step's append (append_new_rows): by the partition holding the new
   // token's block, and in it by the wave that reads that block
@@ -268,6 +254,11 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
 
   const char* kbase = (const char*)a.k_cache;
   const char* vbase = (const char*)a.v_cache;
+  // The block table is read-only for the whole kernel: reading it through
+  // the constant address space makes every entry a scalar load, which never
+  // waits behind the tile copies in flight.
+  const __attribute__((address_space(4))) int32_t* table =
+      (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)b * a.max_blocks);
 
   // LDS DMA: copy n, lane l brings 16 bytes of token row r into LDS row r,
   // column (l % per-row) -- i.e. HBM column (l % per-row) ^ f(r).
@@ -290,7 +281,9 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
     if constexpr (EB == 2) kaddr[k] = ring0 + (uint32_t)(lq * 256 + (((lg * 4 + k) ^ lq) & 15) * 16);
     else kaddr[k] = ring0 + (uint32_t)(lq * 128 + (((lg * 2 + k) ^ (lq >> 1)) & 7) * 16);
   }
-  // V loads: token rows 4 lg + i, bytes [8 lq EB, + 8 EB)
+  // V loads: token rows 4 lg + i, bytes [8 lq EB, + 8 EB); non-temporal,
+  // like the K copies (streamed data, read once per step).  A wave
+  // instruction reads four whole rows 1 KiB apart.
   uint32_t voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)((lg * 4 + i) * C::ROW_B + lq * 8 * EB);
@@ -303,11 +296,11 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if constexpr (VW == 4) {
-        const uint4 x = *(const uint4*)(src + voff[i]);
-        vr.w[i][0] = x.x; vr.w[i][1] = x.y; vr.w[i][2] = x.z; vr.w[i][3] = x.w;
+        const u32x4_t x = __builtin_nontemporal_load((const u32x4_t*)(src + voff[i]));
+        vr.w[i][0] = x[0]; vr.w[i][1] = x[1]; vr.w[i][2] = x[2]; vr.w[i][3] = x[3];
       } else {
-        const uint2 x = *(const uint2*)(src + voff[i]);
-        vr.w[i][0] = x.x; vr.w[i][1] = x.y;
+        const u32x2_t x = __builtin_nontemporal_load((const u32x2_t*)(src + voff[i]));
+        vr.w[i][0] = x[0]; vr.w[i][1] = x[1];
       }
     }
   };
@@ -401,11 +394,11 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
     }
     BlockRef bcur{-1, 1.f, 1.f}, bnext{-1, 1.f, 1.f};
     if (n_my > 0) {
-      bcur.phys = from_zero ? e0 : entry_of(blk(0));
+      bcur.phys = entry_of(blk(0));
       issue_v(bcur.phys, va);
       issue_k(bcur.phys, 0);
       scales_of(bcur);
-      if (n_my > 1) bnext.phys = from_zero ? e1 : entry_of(blk(1));
+      if (n_my > 1) bnext.phys = entry_of(blk(1));
     }
     load_query();
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
