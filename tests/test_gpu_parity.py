@@ -618,11 +618,41 @@ def test_split_size_invariance(pb):
     assert max_err(out_f64(split), out_f64(whole)) <= 2e-6
 
 
-def test_shared_prefix_is_bit_identical_to_private_copies():
-    """Same values, once shared (refcount 6) and once copied into private
-    blocks: the kernel must give bit-identical outputs."""
-    spec = SMALL["mha13b_prefix_small"]
-    say("[prefix] shared vs private copies")
+@pytest.mark.parametrize("pb", [1, 3])
+def test_split_size_invariance_matrix_core(pb):
+    """The matrix-core pass (fp8 cache, 8 query heads, head_dim 128, f32
+    output): split into pieces of pb blocks and merged, or whole, the
+    results agree to fp32 rounding and both match the oracle."""
+    spec = SMALL["ragged_fp8_g8_d128_bf16_f32out"]
+    say(f"[split] {spec.name} partition_blocks={pb}")
+    lay = build_layout(spec)
+    x = make_host_inputs(lay)
+    xs = _to_dev(x)
+    whole = _out(spec)
+    run_step(xs, 0, spec, whole, partition_blocks=1000)
+    split = _out(spec)
+    run_step(xs, 0, spec, split, partition_blocks=pb, append=False)
+    torch.cuda.synchronize()
+    ref = oracle_rows(host_layer(x, 0), lay, spec)
+    assert max_err(out_f64(split), ref) <= 5e-2
+    assert max_err(out_f64(split), out_f64(whole)) <= 1e-5
+
+
+PRIVATE_COPY_CASES = {
+    "mha13b_prefix_small": SMALL["mha13b_prefix_small"],
+    # 64 query / 8 KV heads, head_dim 128: the matrix-core pass
+    "gqa8_prefix_small": scaled(WORKLOADS["mha13b_prefix_f16"], name="gqa8_prefix_small", num_seqs=4,
+                                num_q_heads=64, num_kv_heads=8),
+}
+
+
+@pytest.mark.parametrize("case", list(PRIVATE_COPY_CASES))
+def test_shared_prefix_is_bit_identical_to_private_copies(case):
+    """Same values, once shared (one block id in every table) and once
+    copied into private blocks: the kernel must give bit-identical
+    outputs."""
+    spec = PRIVATE_COPY_CASES[case]
+    say(f"[prefix] shared vs private copies: {case}")
     lay = build_layout(spec)
     x = make_host_inputs(lay)
     pb = spec.shared_prefix_tokens // 16
