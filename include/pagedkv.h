@@ -195,7 +195,11 @@ PKV_API int pkv_decode_num_partitions(const pkv_decode_dims* dims);
  * ids outside [0, num_blocks) and positions past max_blocks_per_seq * 16 are
  * ignored (the caller must not pass them).
  * Non-fp8 dtypes: q, caches and out all F32, or all F16, or all BF16.
- * Arithmetic is fp32; the output is rounded once (nearest-even).
+ * Sums are fp32 and the scores exact products of the stored values; each
+ * softmax weight enters the weighted sum of V with at least 11 significant
+ * bits (about 22 for f16 and 16 for bf16 caches at head_dim 128 with 4 or
+ * 8 query heads per KV head, where the products run on the matrix cores).
+ * The output is rounded once (nearest-even).
  * workspace: device buffer of at least pkv_decode_workspace_bytes(dims)
  * bytes (may be NULL when that is 0), used only during this call.
  */
