@@ -1088,21 +1088,17 @@ struct PassLds {
   static constexpr int value = bytes();
 };
 
-// Waves per SIMD the register allocation must allow.  The GQA-4, D = 128
-// instantiations with 16-bit or fp8 K and V naturally land a few registers
-// above 168, the bound for three waves; holding them to it lets three
-// workgroups share a CU instead of two.  The 16-bit ones need no spill, the
-// fp8 ones one word kept across the loop; with int8 V the bound would put
-// reloads inside the loop, so those keep their natural allocation.  8-bit
-// caches with 8 query heads (two blocks per step) are held to two waves:
-// fp8 fits without spills, int8 V with a few words kept across the loop.
+// Waves per SIMD the register allocation must allow.  The matrix-core
+// instantiations are held to three: the compiler then keeps their
+// accumulators in ordinary VGPRs (152 registers with 16-bit caches, 114
+// with 8-bit ones, no spills) instead of accumulator registers that the
+// per-tile rescale would copy out and back, 68 moves per tile.  Vector
+// instantiations for 8-bit caches with 8 query heads (two blocks per step)
+// are held to two; the others keep their natural allocation.
 template <KV KT, KV VT, int D, int G>
 struct MinWaves {
-  static constexpr bool fits = (KT == KV::F16 || KT == KV::BF16 || KT == KV::FP8) && VT == KT;
   static constexpr bool eight_bit = kv_bytes<KT>::value == 1;
-  static constexpr int value = UseMfma<KT, VT, D, G>::value
-                                  ? 1
-                                  : ((G == 4 && D == 128 && fits) ? 3 : ((G == 8 && eight_bit) ? 2 : 1));
+  static constexpr int value = UseMfma<KT, VT, D, G>::value ? 3 : ((G == 8 && eight_bit) ? 2 : 1);
 };
 
 template <KV KT, KV VT, KV QT, KV OT, int D, int G>
