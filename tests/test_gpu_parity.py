@@ -362,6 +362,10 @@ SMALL = {
     # 8-bit caches on the matrix-core pass with an f32 query, or an f32 output
     "ragged_fp8_g4_d128_f32": _ragged("r19", "fp8_e4m3", "f32", "f32", 128, 4, RAGGED, 19),
     "ragged_fp8_g8_d128_bf16_f32out": _ragged("r20", "fp8_e4m3", "bf16", "f32", 128, 8, RAGGED, 20, hkv=3),
+    # a table narrower than a workgroup's four waves (at most 3 blocks per
+    # sequence), append carried: most waves of the matrix-core pass idle
+    "narrow_table_f16_g8_d128_append": _ragged("r21", "f16", "f16", "f16", 128, 8, [1, 16, 17, 33, 2, 32],
+                                               21, hkv=2, append=True),
     # one long sequence among short ones: the batch-size hint changes the split plan
     "one_long_many_short_f16": _ragged("r18", "f16", "f16", "f16", 128, 4, [8192] + [20, 3, 47, 16] * 4, 18),
 }
