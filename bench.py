@@ -89,9 +89,19 @@ def attention_bytes(spec, lay, window: int = 0, sinks: int = 0):
     return kv, kv + q + out + meta + scales + chan, logical
 
 
-def cpu_baseline(spec, lay, x, budget_s: float):
+PARITY_TOL = {"f32": 1e-5, "f16": 1e-2, "bf16": 1e-2, "fp8_e4m3": 5e-2, "int8": 5e-2}
+
+
+def cpu_baseline(spec, lay, x, budget_s: float, outs=None):
     """Time the oracle on whole sequences (layer 0, then layer 1, ...) until
-    about budget_s seconds of CPU work have been spent."""
+    about budget_s seconds of CPU work have been spent.
+
+    The oracle's result for each (layer, sequence) it ran is also compared
+    with the GPU's output for that layer from the last timed step (`outs`):
+    the inputs are the caches as the timed steps left them (every step
+    appends the same new token to the same slot, so the oracle's own append
+    on top of them must change nothing), and the largest absolute difference
+    is reported next to the tolerance for the cache format."""
     import numpy as np
     import torch
 
@@ -108,6 +118,7 @@ def cpu_baseline(spec, lay, x, budget_s: float):
 
     nblk = -(-lay.context_lens.astype(int) // 16)
     done_bytes, elapsed, seqs = 0, 0.0, 0
+    max_err = 0.0
     order = [(layer, b) for layer in range(x["k_cache"].shape[0]) for b in range(spec.num_seqs)]
     with threadpool_limits(limits=cores):
         for layer, b in order:
@@ -145,16 +156,19 @@ def cpu_baseline(spec, lay, x, budget_s: float):
                 else:
                     kc = oracle.kv_append_bits(kc, kn, slot)
                     vc = oracle.kv_append_bits(vc, vn, slot)
-            oracle.paged_decode_attention(q, kc, vc, table, lens, spec.scale, q_tag=spec.q_dtype,
-                                          kv_tag=spec.kv_dtype, v_tag=spec.v_tag,
-                                          k_channel_scales=chan, **kw)
+            ref = oracle.paged_decode_attention(q, kc, vc, table, lens, spec.scale, q_tag=spec.q_dtype,
+                                                kv_tag=spec.kv_dtype, v_tag=spec.v_tag,
+                                                k_channel_scales=chan, **kw)
             elapsed += time.perf_counter() - t0
+            if outs is not None:
+                got = outs[layer][b].float().cpu().numpy().astype(np.float64)
+                max_err = max(max_err, float(np.abs(got - ref[0]).max()))
             done_bytes += int(lens[0]) * spec.num_kv_heads * spec.head_dim * (ELT[spec.kv_dtype] +
                                                                               ELT[spec.v_tag])
             seqs += 1
             if elapsed >= budget_s:
                 break
-    return {
+    rec = {
         "value": round(done_bytes / elapsed / 1e9, 4),
         "unit": "GB/s",
         "cores": cores,
@@ -163,6 +177,10 @@ def cpu_baseline(spec, lay, x, budget_s: float):
                   f"of {x['k_cache'].shape[0] * spec.num_seqs}, all {spec.num_q_heads} query heads each; "
                   f"{done_bytes / 1e9:.3f} GB of K/V in {elapsed:.1f} s",
     }
+    if outs is not None:
+        rec["max_abs_err_vs_gpu"] = max_err
+        rec["tol"] = PARITY_TOL[spec.kv_dtype]
+    return rec
 
 
 def read_probe(dev, gib: int = 4):
@@ -566,7 +584,9 @@ def main():
     cpu = None
     if args.cpu_seconds > 0:
         log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
-        cpu = cpu_baseline(spec, lay, x, args.cpu_seconds)
+        cpu = cpu_baseline(spec, lay, x, args.cpu_seconds, outs)
+        log(f"[bench] GPU output of the last step vs the oracle on the sampled (layer, sequence) "
+            f"pairs: max|err| = {cpu['max_abs_err_vs_gpu']:.3e} (tol {cpu['tol']})")
 
     rec = {
         "metric": METRIC,
@@ -616,6 +636,7 @@ def main():
             "frac_of_read_probe": None if probe is None else round(achieved / probe["gbs"], 4),
         },
         "cpu_baseline": cpu,
+        "max_abs_err": None if cpu is None else cpu["max_abs_err_vs_gpu"],
     }
     if copy_rec is not None:
         rec["copy_blocks"] = copy_rec

@@ -212,6 +212,17 @@ PKV_API int pkv_paged_decode_attn(const void* q, const void* k_cache, const void
  * FP8 variant ("The KV Cache memory ledger" 7: 8-bit K/V, one scale per head).
  * kv_dtype must be FP8_E4M3; q and out are F16, BF16 or F32.  The value of a
  * cached element is decode(code) * scale[block][kv_head].
+ * Precision: the codes are widened exactly; the query (times K's channel
+ * factors, where given) is multiplied by a power of two -- one per query
+ * head at head_dim 128 with 4 or 8 query heads per KV head, one per KV
+ * head's group of query heads otherwise -- chosen so that the largest
+ * element of the head (group) lands in [2^14, 2^15), then rounded to f16
+ * (nearest even); the scores undo the power of two.  So each query element
+ * keeps 11 significant bits (an f32 query loses its 13 lowest); elements
+ * more than 2^28 times smaller than that largest fall into f16's subnormal
+ * range and keep fewer, and those more than 2^39 times smaller become 0.  Scores and sums are fp32; each
+ * softmax weight enters the weighted sum of V with at least 11 significant
+ * bits (about 22 at head_dim 128 with 4 or 8 query heads per KV head).
  */
 PKV_API int pkv_paged_decode_attn_fp8(const void* q, const void* k_cache, const void* v_cache,
                               const float* k_scales, const float* v_scales,
@@ -250,7 +261,9 @@ typedef struct {
  * dims->sink_tiles = 1 the first dims->sinks positions are read as stored
  * from the side tiles (see pkv_quant_params); the attended positions are
  * those of pkv_paged_decode_attn, and the call always splits the context
- * (pkv_decode_workspace_bytes > 0).
+ * (pkv_decode_workspace_bytes > 0).  Precision: as for
+ * pkv_paged_decode_attn_fp8 (int8 codes are also widened exactly); the
+ * side tiles are read as stored and attended in fp32.
  */
 PKV_API int pkv_paged_decode_attn_quant(const void* q, const void* k_cache, const void* v_cache,
                                         const pkv_quant_params* p, const int32_t* block_tables,

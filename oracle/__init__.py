@@ -20,7 +20,7 @@ Pages cited (by title and section):
        example; decode reads history then appends; FP8 KV.
   [P5] "The KV Cache memory ledger: PagedAttention and continuous batching"
        (gcssc.sfwss.com/posts/kv-cache-budget.html): 1 bytes per token (70B);
-       2 GQA table; 4 block table and locate(); 4 prefix sharing; 7 quantized
+       2 GQA table; 4 block table; 4 prefix sharing; 7 quantized
        KV with per-head scales; sink tokens kept out of coarse quantisation.
 
 Readings taken where the pages are silent (each is also a test):
@@ -40,7 +40,7 @@ pages print); none is "parity unpinned".
 
 from .fp8_e4m3 import decode_e4m3fn, encode_e4m3fn_rne, E4M3_MAX, E4M3_NAN_CODES
 from .values import stored_to_f64
-from .paged_attention import locate, gather_sequence, paged_decode_attention, attended_positions
+from .paged_attention import page_of, gather_sequence, paged_decode_attention, attended_positions
 from .kv_append import kv_append_bits, kv_append_fp8, kv_append_int8, kv_append_quant
 from .kv_bytes import kv_bytes_per_token, kv_bytes
 
@@ -50,7 +50,7 @@ __all__ = [
     "E4M3_MAX",
     "E4M3_NAN_CODES",
     "stored_to_f64",
-    "locate",
+    "page_of",
     "gather_sequence",
     "paged_decode_attention",
     "attended_positions",

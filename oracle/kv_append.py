@@ -2,7 +2,7 @@
 
 [P1] section 2.3: each decode step writes the new token's K and V at the
 sequence's current length and then advances the length by one.  [P5]
-section 4 (locate()): with paging the write goes to the flat slot
+section 4 (block tables): with paging the write goes to the flat slot
 physical_block * block_size + offset.  A slot of -1 means "no token".
 
 The plain append is a pure copy, so it is done on the stored bit patterns

@@ -1,7 +1,7 @@
 """Single-query decode attention over a paged KV cache, in float64.
 
 What is computed, and where the pages state it:
-  * [P5] section 4 (block table and locate()): a sequence's tokens live in
+  * [P5] section 4 (block table): a sequence's tokens live in
     fixed blocks of `block_size` tokens; its block table lists the physical
     block of each logical block, so logical position `pos` is found in block
     table[pos // block_size] at offset pos % block_size.
@@ -40,11 +40,13 @@ import numpy as np
 from .values import stored_to_f64
 
 
-def locate(table_row, pos, block_size: int = 16):
-    """Physical block and in-block offset of logical position(s) `pos`."""
-    table_row = np.asarray(table_row)
-    pos = np.asarray(pos)
-    return table_row[pos // block_size], pos % block_size
+def page_of(table_row, pos, block_size):
+    """Where logical position(s) `pos` of a sequence are stored: the paging
+    definition splits a position into (logical page, offset in the page) and
+    the sequence's table maps the logical page to a physical one.
+    Returns (physical pages, offsets)."""
+    logical_page, offset = np.divmod(np.asarray(pos), int(block_size))
+    return np.asarray(table_row)[logical_page], offset
 
 
 def attended_positions(length: int, window: int = 0, sinks: int = 0) -> np.ndarray:
@@ -83,7 +85,7 @@ def gather_sequence(cache, table_row, length: int, kv_tag: str, kv_heads=None,
     pos = np.arange(int(length)) if positions is None else np.asarray(positions, dtype=np.int64)
     if len(pos) and (pos.min() < 0 or pos.max() >= length):
         raise IndexError("position outside the sequence")
-    blk, off = locate(table_row, pos, block_size)
+    blk, off = page_of(table_row, pos, block_size)
     if len(pos) and (blk.min() < 0 or blk.max() >= nb):
         raise IndexError("block table entry outside the pool for a position < length")
     raw = cache[blk[:, None], kv_heads[None, :], off[:, None], :]      # [L, h, D]

@@ -68,7 +68,7 @@ struct MCfg {
   static constexpr int ROW_B = D * EB;            // one token row of a tile
   static constexpr int TILE_B = 16 * ROW_B;       // one (block, KV head) tile
   static constexpr int NDMA = TILE_B / 1024;      // 1 KiB LDS DMA copies per tile
-  static constexpr int KREADS = 64 * EB / 16;     // 16-byte LDS reads: a lane's 32 channels
+  static constexpr int KREADS = 32 * EB / 16;     // 16-byte LDS reads: a lane's 32 channels
   static constexpr int VW = 2 * EB;               // V dwords per token per lane (8 channels)
   static constexpr int NW = 4;                    // waves per workgroup
   static constexpr int KR = 2;                    // K ring slots per wave

@@ -4,7 +4,10 @@ Tolerances (max-abs against the oracle run on the same stored values):
 fp32 1e-5, fp16/bf16 1e-2, 8-bit caches (fp8, int8, mixed) 5e-2; every
 append (plain or quantising) bit-exact.  The one final rounding of the
 result to the output type (half an ulp at the oracle's value) is not charged
-against the tolerance; it only matters where |out| > 1.
+against the tolerance only where half an ulp of the output type at the
+oracle's value is itself above the tolerance (bf16 outputs of 4 or more,
+from the full-precision sink tiles); everywhere else the raw max-abs error
+is what is asserted (gpu_common.parity_err).
 """
 
 import numpy as np
@@ -16,7 +19,7 @@ import paged_kv_cache_56_amd as pkv
 from workloads import (WORKLOADS, DecodeWorkload, build_layout, make_host_inputs, make_device_inputs, scaled,
                        share_prefixes)
 from gpu_common import (TOL, say, host_storage, run_step, oracle_rows, oracle_append, oracle_attend,
-                        host_layer, out_f64, max_err, err_beyond_rounding)
+                        host_layer, out_f64, max_err, parity_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -240,37 +243,51 @@ def test_copy_blocks_bit_exact(dt):
 
 def test_fork_copy_on_write_end_to_end():
     """A parent with a partial last block is forked three times; parent and
-    children then append different tokens.  The manager asks for copies, the
-    device copies and appends, and attention for every sequence equals the
-    oracle on each sequence's own contiguous history."""
+    children then append different tokens.  The native manager and the
+    oracle's reference manager (oracle.block_manager) are driven with the
+    same calls and must hand out the same slots and copies; the device runs
+    the copies and appends, the host applies the same copies and the
+    oracle's append to its own copy of the caches.  The caches must then be
+    bit-identical, and attention for every sequence must equal the oracle's
+    attention over the reference manager's tables."""
+    from oracle.block_manager import ReferenceBlockManager
+
     say("[cow] fork + copy-on-write + append + attention")
     rng = np.random.default_rng(12)
     NB, H, G, D = 24, 2, 4, 64
-    bm = pkv.BlockManager(NB, free_order=rng.permutation(NB).tolist())
+    order = rng.permutation(NB).tolist()
+    bm = pkv.BlockManager(NB, free_order=order)
+    ref_bm = ReferenceBlockManager(NB, free_order=order)
     kc = torch.full((NB, H, 16, D), float("nan"), dtype=torch.float16, device=DEV)
     vc = torch.full_like(kc, float("nan"))
-    hist_k, hist_v = {0: []}, {0: []}
+    hk, hv = host_storage(kc).copy(), host_storage(vc).copy()
     bm.add_sequence(0)
+    ref_bm.add_sequence(0)
+    gen = torch.Generator().manual_seed(12)
 
     def step(seqs):
         slots, copies = bm.append_slots(seqs)
+        rslots, rcopies = ref_bm.append_slots(seqs)
+        assert slots == rslots and copies == rcopies
         if copies:
             cs = torch.tensor([c[0] for c in copies], dtype=torch.int32, device=DEV)
             cd = torch.tensor([c[1] for c in copies], dtype=torch.int32, device=DEV)
             pkv.copy_blocks(kc, vc, cs, cd)
-        kn = torch.randn((len(seqs), H, D), dtype=torch.float16, device=DEV)
-        vn = torch.randn_like(kn)
-        pkv.kv_append(kn, vn, torch.tensor(slots, dtype=torch.int64, device=DEV), kc, vc)
-        for i, s_ in enumerate(seqs):
-            hist_k[s_].append(kn[i].cpu().float().numpy())
-            hist_v[s_].append(vn[i].cpu().float().numpy())
+            for src, dst in rcopies:
+                hk[dst], hv[dst] = hk[src], hv[src]
+        kn = torch.randn((len(seqs), H, D), generator=gen).to(torch.float16)
+        vn = torch.randn((len(seqs), H, D), generator=gen).to(torch.float16)
+        pkv.kv_append(kn.to(DEV), vn.to(DEV), torch.tensor(slots, dtype=torch.int64, device=DEV), kc, vc)
+        sl = np.array(rslots, dtype=np.int64)
+        hk[...] = oracle.kv_append_bits(hk, kn.numpy(), sl)
+        hv[...] = oracle.kv_append_bits(hv, vn.numpy(), sl)
         return copies
 
     for _ in range(20):
         step([0])
     for c in (1, 2, 3):
         bm.fork(0, c)
-        hist_k[c], hist_v[c] = list(hist_k[0]), list(hist_v[0])
+        ref_bm.fork(0, c)
     ncopies = 0
     for r in range(17):
         ncopies += len(step([3, 0, 1, 2] if r % 2 else [1, 2, 3, 0]))
@@ -279,21 +296,23 @@ def test_fork_copy_on_write_end_to_end():
     assert ncopies == 3
     seqs = [0, 1, 2, 3]
     tables, lens = bm.block_tables(seqs, 4)
-    q = torch.randn((4, H * G, D), dtype=torch.float16, device=DEV)
-    out = torch.empty_like(q)
-    pkv.paged_decode_attn(q, kc, vc, tables.to(DEV), lens.to(DEV), 0.125, out)
-    torch.cuda.synchronize()
-    got = out_f64(out)
+    ref_tables = np.full((4, 4), -1, dtype=np.int32)
     for i, s_ in enumerate(seqs):
-        K = np.stack(hist_k[s_]).astype(np.float64)          # [L, H, D]
-        V = np.stack(hist_v[s_]).astype(np.float64)
-        assert int(lens[i]) == len(K)
-        qv = q[i].cpu().double().numpy()
-        for hq in range(H * G):
-            sc = 0.125 * (K[:, hq // G, :] @ qv[hq])
-            w = np.exp(sc - sc.max())
-            ref = (w @ V[:, hq // G, :]) / w.sum()
-            assert np.abs(got[i, hq] - ref).max() <= TOL["f16"]
+        ref_tables[i, :len(ref_bm.tables[s_])] = ref_bm.tables[s_]
+    ref_lens = np.array([ref_bm.lens[s_] for s_ in seqs], dtype=np.int32)
+    assert np.array_equal(tables.numpy(), ref_tables) and np.array_equal(lens.numpy(), ref_lens)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_storage(kc).view(np.uint16), hk.view(np.uint16))
+    assert np.array_equal(host_storage(vc).view(np.uint16), hv.view(np.uint16))
+    q = torch.randn((4, H * G, D), generator=gen).to(torch.float16)
+    out = torch.empty((4, H * G, D), dtype=torch.float16, device=DEV)
+    pkv.paged_decode_attn(q.to(DEV), kc, vc, tables.to(DEV), lens.to(DEV), 0.125, out)
+    torch.cuda.synchronize()
+    ref = oracle.paged_decode_attention(q.numpy(), hk, hv, ref_tables, ref_lens, 0.125,
+                                        q_tag="f16", kv_tag="f16")
+    err = parity_err(out_f64(out), ref, "f16", TOL["f16"])
+    say(f"    max|err| = {err:.3e} (tol {TOL['f16']})")
+    assert err <= TOL["f16"]
     bm.close()
 
 
@@ -387,7 +406,7 @@ def test_decode_matches_oracle(name):
         got = out_f64(out)
         ref = oracle_rows(host_layer(x, layer), lay, spec)
         assert np.isfinite(got).all()
-        err = err_beyond_rounding(got, ref, spec.out_dtype)
+        err = parity_err(got, ref, spec.out_dtype, tol)
         say(f"    layer {layer}: max|err| = {err:.3e} (tol {tol})")
         assert err <= tol
         zero = lay.context_lens == 0
@@ -429,7 +448,7 @@ def test_balanced_split_with_window(case, window, sinks):
     torch.cuda.synchronize()
     got = out_f64(out)
     ref = oracle_rows(host_layer(x, 0), lay, spec, window=window, sinks=sinks)
-    err = err_beyond_rounding(got, ref, spec.out_dtype)
+    err = parity_err(got, ref, spec.out_dtype, TOL[spec.kv_dtype])
     say(f"    max|err| = {err:.3e} (tol {TOL[spec.kv_dtype]})")
     assert np.isfinite(got).all() and err <= TOL[spec.kv_dtype]
 
@@ -446,7 +465,7 @@ def test_sliding_window_and_sinks(case, window, sinks, pb):
     torch.cuda.synchronize()
     got = out_f64(out)
     ref = oracle_rows(host_layer(x, 0), lay, spec, window=window, sinks=sinks)
-    err = err_beyond_rounding(got, ref, spec.out_dtype)
+    err = parity_err(got, ref, spec.out_dtype, TOL[spec.kv_dtype])
     say(f"    max|err| = {err:.3e} (tol {TOL[spec.kv_dtype]})")
     assert np.isfinite(got).all()
     assert err <= TOL[spec.kv_dtype]
@@ -470,7 +489,7 @@ def test_balanced_plan_matches_oracle(name):
     torch.cuda.synchronize()
     got = out_f64(out)
     ref = oracle_rows(host_layer(x, 0), lay, spec)
-    err = err_beyond_rounding(got, ref, spec.out_dtype)
+    err = parity_err(got, ref, spec.out_dtype, TOL[spec.kv_dtype])
     say(f"    max|err| = {err:.3e} (tol {TOL[spec.kv_dtype]})")
     assert np.isfinite(got).all() and err <= TOL[spec.kv_dtype]
 
@@ -529,7 +548,7 @@ def test_prefix_groups_match_oracle(case):
     got = out_f64(grouped)
     ref = oracle_rows(host_layer(x, 0), lay, spec)
     tol = TOL[spec.kv_dtype]
-    err = err_beyond_rounding(got, ref, spec.out_dtype)
+    err = parity_err(got, ref, spec.out_dtype, tol)
     say(f"    max|err| = {err:.3e} (tol {tol})")
     assert np.isfinite(got).all() and err <= tol
     assert (got[lay.context_lens == 0] == 0).all()
@@ -600,7 +619,7 @@ def test_fused_step_matches_append_then_attend(case, pb, window, sinks, skip):
         ref = oracle_attend(h, spec, kc, vc, None, None, lay.block_tables, lay.context_lens, seqs=keep,
                             window=window, sinks=sinks)
         got = out_f64(out)[keep]
-        err = err_beyond_rounding(got, ref, spec.out_dtype)
+        err = parity_err(got, ref, spec.out_dtype, tol)
         say(f"    layer {layer}: max|err| = {err:.3e} (tol {tol})")
         assert np.isfinite(got).all() and err <= tol
 
@@ -753,7 +772,7 @@ def test_lengths_past_the_table_are_clamped():
         host_storage(x["q"][0]), host_storage(x["k_cache"][0]), host_storage(x["v_cache"][0]),
         lay.block_tables, np.array([32, 32, 0, 20]), spec.scale, q_tag="f16", kv_tag="f16")
     assert (got[2] == 0).all()
-    assert err_beyond_rounding(got, ref, "f16") <= TOL["f16"]
+    assert parity_err(got, ref, "f16", TOL["f16"]) <= TOL["f16"]
 
 
 def test_group_descriptors_out_of_range_do_not_fault():
@@ -849,7 +868,7 @@ def test_full_size_sampled_rows(name):
         kc, vc, ks, vs = oracle_append(h, spec, slots)
         ref = oracle_attend(h, spec, kc, vc, ks, vs, tables, lay.context_lens, seqs=seqs, q_heads=heads)
         got = out_f64(outs[layer])[seqs][:, heads]
-        err = err_beyond_rounding(got, ref, spec.out_dtype)
+        err = parity_err(got, ref, spec.out_dtype, tol)
         say(f"    layer {layer} seqs {seqs} heads {heads}: max|err| = {err:.3e} (tol {tol})")
         assert err <= tol
         assert torch.isfinite(outs[layer].float()).all()

@@ -3,7 +3,7 @@
 Nothing here retypes the oracle's formula.  The oracle is checked against
   * torch's scaled_dot_product_attention in float64 on contiguous K/V whose
     paged copy was laid down token by token by the block pool (so the pool's
-    incremental bookkeeping, not the oracle's locate(), decides where a token
+    incremental bookkeeping, not the oracle's page_of(), decides where a token
     lives);
   * closed forms (constant V, zero query, one token, one dominant key);
   * invariances (physical block permutation, GQA vs K/V heads duplicated,
@@ -20,7 +20,7 @@ import torch
 import torch.nn.functional as F
 
 import oracle
-from oracle import paged_decode_attention, locate
+from oracle import paged_decode_attention, page_of
 from workloads import BlockPool, build_layout, make_host_inputs, WORKLOADS, scaled
 
 BS = 16
@@ -277,8 +277,8 @@ def test_storage_dtypes_decode_like_torch():
     np.testing.assert_allclose(got, ref, atol=1e-12)
 
 
-def test_locate_matches_pool_bookkeeping_on_workloads():
-    """For every workload, locate() through the table finds each position at
+def test_page_of_matches_pool_bookkeeping_on_workloads():
+    """For every workload, page_of() through the table finds each position at
     the slot the pool handed out when that token was added."""
     for w in WORKLOADS.values():
         if w.num_seqs * (w.len_range[1] if w.len_range else 100) > 2_000_000:
@@ -287,7 +287,7 @@ def test_locate_matches_pool_bookkeeping_on_workloads():
         for b in range(w.num_seqs):
             slots = lay.seq_slots[b]
             pos = np.arange(len(slots))
-            blk, off = locate(lay.block_tables[b], pos, BS)
+            blk, off = page_of(lay.block_tables[b], pos, BS)
             assert np.array_equal(blk * BS + off, slots)
             assert len(slots) == lay.context_lens[b]
 
@@ -344,8 +344,8 @@ MUTANTS = {
     "head_map_modulo": ("h = col[kv_for[c]]", "h = col[kv_for[c]] if False else (q_heads[c] % Hkv) % len(kv_needed)"),
     "scale_dropped": ("s = scale * (K[:, h, :] @ qv[r, c])", "s = (K[:, h, :] @ qv[r, c])"),
     "length_off_by_one": ("L = int(context_lens[b])", "L = max(int(context_lens[b]) - 1, 0)"),
-    "offset_uses_block_index": ("return table_row[pos // block_size], pos % block_size",
-                                "return table_row[pos // block_size], (pos // block_size) % block_size"),
+    "offset_uses_block_index": ("return np.asarray(table_row)[logical_page], offset",
+                                "return np.asarray(table_row)[logical_page], logical_page % int(block_size)"),
     "k_v_swapped": ("out[r, c] = (w @ V[:, h, :]) / w.sum()", "out[r, c] = (w @ K[:, h, :]) / w.sum()"),
     "normalise_by_length": ("out[r, c] = (w @ V[:, h, :]) / w.sum()", "out[r, c] = (w @ V[:, h, :]) / len(w)"),
     "exponent_sign": ("w = np.exp(s - s.max())", "w = np.exp(s.max() - s)"),

@@ -32,7 +32,7 @@ Recipe (all seeded from the workload's seed):
     (poisons) the blocks that were replaced;
   * full-precision sinks (fp_sinks = S > 0): sequence b's first S positions
     live in side tile sink_tiles_of_seq[b] (a seeded permutation of the B
-    tiles), in q's dtype, drawn N(0, 1) x 8 (sink tokens stand apart in
+    tiles), in q's dtype, drawn N(0, 1) x 4 (sink tokens stand apart in
     magnitude); the rest of each tile, and the cache slots of those
     positions, are poisoned; a new token at a position < S goes to its tile
     (sink_slot_mapping = tile * 16 + position, else -1).
