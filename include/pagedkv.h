@@ -55,8 +55,10 @@ extern "C" {
 #define PKV_API
 #endif
 
-#define PKV_VERSION 150  /* 1.5.0 */
+#define PKV_VERSION 160  /* 1.6.0 */
 #define PKV_BLOCK_SIZE 16
+/* Device scratch held by pkv_paged_decode_attn_noalloc, per device. */
+#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 typedef enum {
   PKV_F32 = 0,
@@ -76,7 +78,9 @@ typedef enum {
   PKV_ERR_WORKSPACE = -4, /* workspace missing or smaller than required */
   PKV_ERR_LAUNCH = -5,    /* the HIP runtime refused a launch */
   PKV_ERR_NO_BLOCKS = -6, /* block manager: not enough free blocks (nothing changed) */
-  PKV_ERR_SEQUENCE = -7   /* block manager: unknown or duplicate sequence id */
+  PKV_ERR_SEQUENCE = -7,  /* block manager: unknown or duplicate sequence id */
+  PKV_ERR_SCRATCH = -8    /* pkv_paged_decode_attn_noalloc: the call's workspace would
+                             exceed PKV_NOALLOC_SCRATCH_BYTES (nothing ran) */
 } pkv_status;
 
 typedef struct {
@@ -207,6 +211,27 @@ PKV_API int pkv_paged_decode_attn(const void* q, const void* k_cache, const void
                           const int32_t* block_tables, const int32_t* context_lens, float scale,
                           void* out, const pkv_decode_dims* dims, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pkv_paged_decode_attn without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Arguments, results and errors
+ * are those of pkv_paged_decode_attn; when the context is split, the
+ * partial results go to a static device array of PKV_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every device it runs on (zero-filled when the
+ * library is loaded, kept until the process ends) instead of a caller
+ * workspace.  A call whose workspace (pkv_decode_workspace_bytes) would
+ * exceed that returns PKV_ERR_SCRATCH and runs nothing.  The call allocates
+ * nothing: the array's device address is looked up once per device, on
+ * the first call that splits.  Every call on a device shares that device's
+ * array and leaves its contents there, so calls on one device that may
+ * overlap (two streams, two host threads) race and must be ordered by the
+ * caller.
+ */
+PKV_API int pkv_paged_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                          const int32_t* block_tables, const int32_t* context_lens,
+                                          float scale, void* out, const pkv_decode_dims* dims,
+                                          hipStream_t stream);
 
 /*
  * FP8 variant ("The KV Cache memory ledger" 7: 8-bit K/V, one scale per head).

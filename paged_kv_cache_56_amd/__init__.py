@@ -135,6 +135,8 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_decode_num_partitions.restype = ctypes.c_int
     lib.pkv_paged_decode_attn.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp, sz, vp]
     lib.pkv_paged_decode_attn.restype = ctypes.c_int
+    lib.pkv_paged_decode_attn_noalloc.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp]
+    lib.pkv_paged_decode_attn_noalloc.restype = ctypes.c_int
     lib.pkv_paged_decode_attn_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
                                               dims_p, vp, sz, vp]
     lib.pkv_paged_decode_attn_fp8.restype = ctypes.c_int

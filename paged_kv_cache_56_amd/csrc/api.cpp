@@ -4,10 +4,45 @@
 #include "pkv_internal.h"
 
 #include <cmath>
+#include <mutex>
 
 using namespace pkv;
 
+// Device scratch of pkv_paged_decode_attn_noalloc: the split-context
+// workspace (partial results per query row and context piece) lives here
+// instead of in a caller buffer.  Each device that loads the library holds
+// its own copy, zero-filled at load, until the process ends.  In host code
+// `scratch` only names the symbol: its device address comes from
+// hipGetSymbolAddress, once per device (scratch_of_stream below).
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of `scratch` on the device `stream` belongs to, looked up
+// on the first call for that device with the device current.
+int scratch_of_stream(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return PKV_ERR_LAUNCH;
+  std::call_once(g_scratch_once[dev], [dev] {
+    int cur = -1;
+    g_scratch_err[dev] = hipGetDevice(&cur);
+    if (g_scratch_err[dev] != hipSuccess) return;
+    if (cur != dev && (g_scratch_err[dev] = hipSetDevice(dev)) != hipSuccess) return;
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+    if (cur != dev) (void)hipSetDevice(cur);
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return PKV_ERR_LAUNCH;
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
 
 int elem_bytes(int dt) {
   switch (dt) {
@@ -88,7 +123,8 @@ struct StepAppend {
 int decode_common(const void* q, const void* k_cache, const void* v_cache, const pkv_quant_params* qp,
                   const GroupPtrs* gp, const int32_t* block_tables, const int32_t* context_lens,
                   float scale, void* out, const pkv_decode_dims* dims, void* workspace,
-                  size_t workspace_bytes, hipStream_t stream, const StepAppend* ap = nullptr) {
+                  size_t workspace_bytes, hipStream_t stream, const StepAppend* ap = nullptr,
+                  bool use_scratch = false) {
   int st = check_dims(dims);
   if (st) return st;
   if (ap) {
@@ -118,7 +154,11 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
   plan_partitions(*dims, &pb, &np);
   if (dims->prefix_groups > 0) plan_groups(*dims, &gpb, &gnp, &qchunks);
   const size_t need = workspace_bytes_for(*dims);
-  if (need && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  if (use_scratch) {
+    if (need > PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_SCRATCH;
+  } else if (need && (!workspace || workspace_bytes < need)) {
+    return PKV_ERR_WORKSPACE;
+  }
 
   DecodeArgs a{};
   a.q = q;
@@ -178,6 +218,14 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
   a.kv_dtype = dims->kv_dtype;
   a.v_dtype = v_dtype >= 0 ? v_dtype : dims->kv_dtype;
   a.out_dtype = dims->out_dtype;
+  if (use_scratch && need) {
+    // every argument is valid: only now is the device touched
+    void* ws = nullptr;
+    st = scratch_of_stream(stream, &ws);
+    if (st) return st;
+    a.o_part = (float*)ws;
+    a.ml_part = (float*)ws + rows * (np + gnp) * dims->head_dim;
+  }
   return launch_decode(a, stream);
 }
 
@@ -282,6 +330,14 @@ int pkv_paged_decode_attn(const void* q, const void* k_cache, const void* v_cach
                        dims, workspace, workspace_bytes, stream);
 }
 
+int pkv_paged_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  float scale, void* out, const pkv_decode_dims* dims,
+                                  hipStream_t stream) {
+  return decode_common(q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens, scale, out,
+                       dims, nullptr, 0, stream, nullptr, true);
+}
+
 int pkv_paged_decode_attn_fp8(const void* q, const void* k_cache, const void* v_cache,
                               const float* k_scales, const float* v_scales,
                               const int32_t* block_tables, const int32_t* context_lens,
@@ -344,6 +400,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_LAUNCH: return "kernel launch failed";
     case PKV_ERR_NO_BLOCKS: return "block pool exhausted";
     case PKV_ERR_SEQUENCE: return "unknown or duplicate sequence id";
+    case PKV_ERR_SCRATCH: return "the call needs more scratch than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }

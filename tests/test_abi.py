@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
     lib = pkv.load_library()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pkv_version() == 150
+    assert lib.pkv_version() == 160
 
 
 def _dims(**kw):
@@ -289,3 +289,23 @@ def test_python_binding_rejects_host_tensors():
                               torch.ones(1, dtype=torch.int32), 0.125, torch.zeros_like(q))
     with pytest.raises(ValueError):
         pkv.kv_append(torch.zeros(1, 1, 64), torch.zeros(1, 1, 64), torch.zeros(1, dtype=torch.int64), kc, kc)
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch():
+    """pkv_paged_decode_attn_noalloc: invalid arguments give the usual status,
+    and a valid call whose split workspace would exceed the static scratch
+    gives PKV_ERR_SCRATCH (-8) before anything touches the device."""
+    lib = pkv.load_library()
+
+    def call(dims, q=FAKE):
+        return lib.pkv_paged_decode_attn_noalloc(q, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.088), FAKE,
+                                                 ctypes.byref(dims), None)
+
+    assert call(_dims(), q=None) == -1
+    assert call(_dims(block_size=8)) == -2
+    assert call(_dims(q_dtype=2)) == -3
+    # 4096 sequences x 64 query heads x 16 pieces x (128 + 2) floats > 32 MiB
+    big = _dims(num_seqs=4096, max_blocks_per_seq=256, partition_blocks=16)
+    assert pkv.decode_workspace_bytes(big) > 32 * 2**20
+    assert call(big) == -8
+    assert lib.pkv_status_string(-8)
