@@ -276,7 +276,8 @@ def _csv_rows(path):
         return list(csv.DictReader(f))
 
 
-def summarize_counters(fetch_csv, write_csv, stats_csv, workload, probe_gib, out_md, command):
+def summarize_counters(fetch_csv, write_csv, stats_csv, workload, probe_gib, out_md, command,
+                       kernel=ATTN_KERNEL, layers=0):
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench plus
     its --kernel-trace --stats run into the traffic summary bench.py reports.
 
@@ -300,14 +301,15 @@ def summarize_counters(fetch_csv, write_csv, stats_csv, workload, probe_gib, out
     copy_w = max(pick(write, CALIB_COPY_KERNEL))
     fetch_scale = probe_gib * 2**30 / probe_f
     write_scale = CALIB_COPY_BYTES / copy_w
-    attn_f = statistics.mean(pick(fetch, ATTN_KERNEL)) * fetch_scale
-    attn_w = statistics.mean(pick(write, ATTN_KERNEL)) * write_scale
+    attn_f = statistics.mean(pick(fetch, kernel)) * fetch_scale
+    attn_w = statistics.mean(pick(write, kernel)) * write_scale
     stats = [r for r in _csv_rows(stats_csv)]
     top = sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:6]
-    attn = [r for r in stats if ATTN_KERNEL in r["Name"]]
+    attn = [r for r in stats if kernel in r["Name"]]
     rec = {
         "workload": workload,
-        "kernel": ATTN_KERNEL,
+        "layers": layers or None,
+        "kernel": kernel,
         "kernel_source_sha": kernel_source_sha(),
         "fetch_bytes_per_launch": round(attn_f),
         "write_bytes_per_launch": round(attn_w),
@@ -319,7 +321,7 @@ def summarize_counters(fetch_csv, write_csv, stats_csv, workload, probe_gib, out
         "trace_calls": int(attn[0]["Calls"]) if attn else 0,
     }
     lines = [
-        f"# {ATTN_KERNEL} on {workload}: rocprofv3 summary",
+        f"# {kernel} on {workload}: rocprofv3 summary",
         "",
         "Commands (run from the repository root on one MI355X, `export TMPDIR=/tmp`):",
         "",
@@ -378,11 +380,13 @@ def summarize_trace(stats_csv, workload, out_md, command, kernel=ATTN_KERNEL):
     return rec
 
 
-def traffic_for(workload: str):
-    """Counter-measured bytes per attention launch, if taken on these sources."""
+def traffic_for(workload: str, kernel: str = "decode_partition_kernel", layers: int = 0):
+    """Counter-measured bytes per attention launch, if taken on these sources
+    with the same layer count (a one-layer workload re-read back to back is
+    partly served from the last-level cache; several layers read cold)."""
     import re
 
-    path = os.path.join(PROFILES, f"decode_partition_kernel__{workload}.md")
+    path = os.path.join(PROFILES, f"{kernel}__{workload}.md")
     if not os.path.exists(path):
         return None
     m = re.search(r"```json\n(.*?)\n```", open(path).read(), flags=re.S)
@@ -390,6 +394,8 @@ def traffic_for(workload: str):
         return None
     rec = json.loads(m.group(1))
     if rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    if layers and rec.get("layers") not in (None, layers):
         return None
     return rec
 
@@ -439,8 +445,9 @@ def main():
                                          args.trace_kernel)))
         return
     if args.summarize_counters:
-        out = os.path.join(PROFILES, f"decode_partition_kernel__{args.workload}.md")
-        rec = summarize_counters(*args.summarize_counters, args.workload, 4, out, args.command)
+        out = os.path.join(PROFILES, f"{args.trace_kernel.split('::')[-1]}__{args.workload}.md")
+        rec = summarize_counters(*args.summarize_counters, args.workload, 4, out, args.command,
+                                 args.trace_kernel, args.layers)
         print(json.dumps(rec))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -496,7 +503,7 @@ def main():
     chan = x.get("k_channel_scales")
     both_fp8 = spec.kv_dtype == spec.v_tag == "fp8_e4m3" and chan is None and not spec.fp_sinks
     # 16-bit and f32 caches: the append rides in the attention launch
-    fused = spec.append and not spec.quantised and not spec.fp_sinks and not grouped and not args.separate_append
+    fused = spec.append and not spec.quantised and not spec.fp_sinks and not args.separate_append
 
     def step(ev=None):
         for layer in range(nl):
@@ -527,7 +534,8 @@ def main():
                 pkv.paged_decode_step(x["k_new"][layer], x["v_new"][layer], x["slot_mapping"], x["q"][layer],
                                       kc, vc, x["block_tables"], x["context_lens"], spec.scale, outs[layer],
                                       workspace=ws, partition_blocks=args.partition_blocks,
-                                      window=args.window, sinks=args.sinks, total_blocks=total_blocks)
+                                      window=args.window, sinks=args.sinks, total_blocks=total_blocks,
+                                      **gkw)
             else:
                 pkv.paged_decode_attn(x["q"][layer], kc, vc, x["block_tables"], x["context_lens"],
                                       spec.scale, outs[layer], workspace=ws,
@@ -564,9 +572,10 @@ def main():
         alg_bytes += 4 * spec.num_seqs * spec.num_kv_heads * spec.head_dim * ELT[spec.kv_dtype]
     value = kv_bytes * nl / (ms_per_step / 1e3) / 1e9
     achieved = alg_bytes / mean_launch_s / 1e9
-    kernel = ("group_prefix_kernel+" if grouped else "") + "decode_partition_kernel" + (
+    kernel = ("decode_group_kernel" if grouped else "decode_partition_kernel") + (
         "+lse_merge_kernel" if (nparts > 1 or grouped) else "")
-    trec = traffic_for(spec.name) if (nparts == 1 and args.window == 0 and not grouped) else None
+    trec = (traffic_for(spec.name, kernel.split("+")[0], nl) if args.window == 0 and not args.fp_sinks
+            else None)
     traffic = None if trec is None else trec["traffic_bytes_per_launch"]
     log(f"[bench] {ms_per_step:.3f} ms/step; attention launch {mean_launch_s * 1e6:.1f} us "
         f"-> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of peak)")

@@ -177,9 +177,13 @@ PKV_API int pkv_kv_append_quant(const void* x_new, const int64_t* slot_mapping, 
                                 int32_t scale_mode, hipStream_t stream);
 
 /*
- * Bytes of workspace pkv_paged_decode_attn(_fp8, _quant) needs for `dims`; 0 when the
+ * Bytes of workspace the decode attention calls need for `dims`; 0 when the
  * context is not split.  Depends only on `dims` (never on the device or on
  * context_lens), so a caller can size it once.  Returns 0 for invalid dims.
+ * The workspace holds the partial results of the context pieces (per
+ * query row: output, reference maximum and sum of each piece), which a
+ * second kernel of the same call merges; calls sharing one workspace must
+ * not overlap in time (one stream, or synchronised).
  */
 PKV_API size_t pkv_decode_workspace_bytes(const pkv_decode_dims* dims);
 
@@ -342,6 +346,26 @@ PKV_API int pkv_paged_decode_step(const void* k_new, const void* v_new, const in
  */
 PKV_API int pkv_paged_decode_attn_prefix(const void* q, const void* k_cache, const void* v_cache,
                                          const int32_t* group_seq_start,
+                                         const int32_t* group_prefix_blocks,
+                                         const int32_t* block_tables, const int32_t* context_lens,
+                                         float scale, void* out, const pkv_decode_dims* dims,
+                                         void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
+
+/*
+ * One decode step for a batch with shared-prefix groups, in one launch: the
+ * append of pkv_paged_decode_step followed by pkv_paged_decode_attn_prefix
+ * ("KV Cache from first principles" 2.2-2.3; "The KV Cache memory ledger"
+ * 4).  Arguments are those two calls' together; caches, q and out all F16
+ * or all BF16.  Each sequence's new token must lie past its group's shared
+ * blocks (context_lens[b] - 1 >= 16 * group_prefix_blocks[g]: shared
+ * blocks are full, and a token is never appended into a block other
+ * sequences hold); otherwise the results are undefined (no out-of-bounds
+ * access).  Results and cache contents equal those of the two calls.
+ */
+PKV_API int pkv_paged_decode_step_prefix(const void* k_new, const void* v_new,
+                                         const int64_t* slot_mapping, const void* q, void* k_cache,
+                                         void* v_cache, const int32_t* group_seq_start,
                                          const int32_t* group_prefix_blocks,
                                          const int32_t* block_tables, const int32_t* context_lens,
                                          float scale, void* out, const pkv_decode_dims* dims,

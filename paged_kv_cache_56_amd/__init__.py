@@ -11,7 +11,8 @@ carry device memory and streams.
     kv_append_quant(x_new, slot_mapping, cache, scales, channel_scales=None)
     paged_decode_step(k_new, v_new, slot_mapping, q, k_cache, v_cache, block_tables,
                       context_lens, scale, out, workspace=None, partition_blocks=0,
-                      window=0, sinks=0, total_blocks=0)
+                      window=0, sinks=0, total_blocks=0, prefix_group_starts=None,
+                      prefix_group_blocks=None, prefix_max_seqs=0, prefix_max_blocks=0)
     paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, scale, out,
                       k_scales=None, v_scales=None, k_channel_scales=None,
                       sink_k=None, sink_v=None, sink_tiles_of_seq=None,
@@ -146,6 +147,9 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_paged_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp,
                                           sz, vp]
     lib.pkv_paged_decode_step.restype = ctypes.c_int
+    lib.pkv_paged_decode_step_prefix.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
+                                                 dims_p, vp, sz, vp]
+    lib.pkv_paged_decode_step_prefix.restype = ctypes.c_int
     lib.pkv_paged_decode_attn_prefix.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
                                                  dims_p, vp, sz, vp]
     lib.pkv_paged_decode_attn_prefix.restype = ctypes.c_int
@@ -515,15 +519,21 @@ def paged_decode_step(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: to
                       block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
                       out: torch.Tensor, *, workspace: Optional[torch.Tensor] = None,
                       partition_blocks: int = 0, window: int = 0, sinks: int = 0,
-                      total_blocks: int = 0) -> torch.Tensor:
+                      total_blocks: int = 0,
+                      prefix_group_starts: Optional[torch.Tensor] = None,
+                      prefix_group_blocks: Optional[torch.Tensor] = None,
+                      prefix_max_seqs: int = 0, prefix_max_blocks: int = 0) -> torch.Tensor:
     """kv_append of each sequence's new token, then paged_decode_attn, in one launch.
 
     k_new, v_new: [B, Hkv, D] (row b is sequence b's new token); slot_mapping:
     int64 [B], the slot of sequence b's last position (-1: none).  Caches and
-    q/out f32, f16 or bf16 of one type.  Returns `out`.
+    q/out f32, f16 or bf16 of one type.  Shared-prefix groups (f16/bf16) as in
+    paged_decode_attn; each new token must then lie past its group's shared
+    blocks.  Returns `out`.
     """
     lib = load_library()
-    _dev(k_new, v_new, slot_mapping, q, k_cache, v_cache, block_tables, context_lens, out, workspace)
+    _dev(k_new, v_new, slot_mapping, q, k_cache, v_cache, block_tables, context_lens, out, workspace,
+         prefix_group_starts, prefix_group_blocks)
     _need(q.dim() == 3 and out.shape == q.shape, "q and out must be [B, Hq, D]")
     _need(k_cache.shape == v_cache.shape and k_cache.dim() == 4, "caches must be [NB, Hkv, 16, D]")
     B = q.shape[0]
@@ -534,13 +544,31 @@ def paged_decode_step(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: to
     _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == B,
           "block_tables must be int32 [B, max_blocks]")
     _need(context_lens.dtype == torch.int32 and context_lens.shape == (B,), "context_lens must be int32 [B]")
-    dims = decode_dims(q, k_cache, block_tables, out, partition_blocks, window, sinks, False, total_blocks)
+    grouped = prefix_group_starts is not None or prefix_group_blocks is not None
+    G = 0
+    if grouped:
+        _need(prefix_group_starts is not None and prefix_group_blocks is not None,
+              "shared prefixes need prefix_group_starts and prefix_group_blocks")
+        G = prefix_group_blocks.numel()
+        _need(prefix_group_starts.dtype == prefix_group_blocks.dtype == torch.int32
+              and prefix_group_blocks.dim() == 1 and prefix_group_starts.shape == (G + 1,),
+              "prefix_group_starts must be int32 [G + 1] and prefix_group_blocks int32 [G]")
+    dims = decode_dims(q, k_cache, block_tables, out, partition_blocks, window, sinks, False, total_blocks,
+                       G, prefix_max_seqs if grouped else 0, prefix_max_blocks if grouped else 0)
     need = decode_workspace_bytes(dims)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _ptr(workspace) if need else None
     ws_bytes = workspace.numel() * workspace.element_size() if (need and workspace is not None) else 0
-    _check(lib.pkv_paged_decode_step(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(q), _ptr(k_cache),
-                                     _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), float(scale),
-                                     _ptr(out), ctypes.byref(dims), ws_ptr, ws_bytes, _stream(q)))
+    if grouped:
+        st = lib.pkv_paged_decode_step_prefix(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(q),
+                                              _ptr(k_cache), _ptr(v_cache), _ptr(prefix_group_starts),
+                                              _ptr(prefix_group_blocks), _ptr(block_tables),
+                                              _ptr(context_lens), float(scale), _ptr(out),
+                                              ctypes.byref(dims), ws_ptr, ws_bytes, _stream(q))
+    else:
+        st = lib.pkv_paged_decode_step(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(q), _ptr(k_cache),
+                                       _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), float(scale),
+                                       _ptr(out), ctypes.byref(dims), ws_ptr, ws_bytes, _stream(q))
+    _check(st)
     return out

@@ -128,7 +128,7 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
   int st = check_dims(dims);
   if (st) return st;
   if (ap) {
-    if (qp || gp || dims->sink_tiles) return PKV_ERR_SHAPE;   // 16-bit and f32 caches, no groups
+    if (qp || dims->sink_tiles) return PKV_ERR_SHAPE;   // 16-bit and f32 caches, no sink tiles
     if (is_q8(dims->kv_dtype)) return PKV_ERR_DTYPE;
     if (!ap->k_new || !ap->v_new || !ap->slots) return PKV_ERR_NULL;
   }
@@ -369,6 +369,18 @@ int pkv_paged_decode_step(const void* k_new, const void* v_new, const int64_t* s
                           hipStream_t stream) {
   const StepAppend ap{k_new, v_new, slot_mapping, k_cache, v_cache};
   return decode_common(q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens, scale, out,
+                       dims, workspace, workspace_bytes, stream, &ap);
+}
+
+int pkv_paged_decode_step_prefix(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                                 const void* q, void* k_cache, void* v_cache,
+                                 const int32_t* group_seq_start, const int32_t* group_prefix_blocks,
+                                 const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                 void* out, const pkv_decode_dims* dims, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  const StepAppend ap{k_new, v_new, slot_mapping, k_cache, v_cache};
+  const GroupPtrs gp{group_seq_start, group_prefix_blocks};
+  return decode_common(q, k_cache, v_cache, nullptr, &gp, block_tables, context_lens, scale, out,
                        dims, workspace, workspace_bytes, stream, &ap);
 }
 

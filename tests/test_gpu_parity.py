@@ -624,6 +624,79 @@ def test_fused_step_matches_append_then_attend(case, pb, window, sinks, skip):
         assert np.isfinite(got).all() and err <= tol
 
 
+@pytest.mark.parametrize("case", ["prefix_one_group_f16_g1", "prefix_groups_f16_g8_d128",
+                                  "prefix_two_chunks_f16_g8_d128", "prefix_groups_f16_g1_d64"])
+def test_fused_step_with_prefix_groups(case):
+    """pkv_paged_decode_step_prefix: the append carried by the launch that
+    reads shared prefixes once per group.  Every new token lies past its
+    group's shared blocks.  Caches equal the oracle's append bit for bit and
+    the output the oracle's attention over them (the oracle knows nothing
+    of groups)."""
+    from gpu_common import group_args
+    spec, lay = _grouped_layout(case)
+    assert spec.append
+    say(f"[step+groups] {case}: starts={list(lay.group_starts)} blocks={list(lay.group_blocks)} "
+        f"lens={list(lay.context_lens)}")
+    x = make_host_inputs(lay)
+    xs = _to_dev(x)
+    out = _out(spec)
+    pkv.paged_decode_step(xs["k_new"][0], xs["v_new"][0], xs["slot_mapping"], xs["q"][0], xs["k_cache"][0],
+                          xs["v_cache"][0], xs["block_tables"], xs["context_lens"], spec.scale, out,
+                          **group_args(xs))
+    torch.cuda.synchronize()
+    h = host_layer(x, 0)
+    kc, vc, _, _ = oracle_append(h, spec, lay.slot_mapping)
+    for name, ref in (("k_cache", kc), ("v_cache", vc)):
+        assert np.array_equal(host_storage(xs[name][0]).view(np.uint8), ref.view(np.uint8)), name
+    ref = oracle_attend(h, spec, kc, vc, None, None, lay.block_tables, lay.context_lens)
+    tol = TOL[spec.kv_dtype]
+    err = parity_err(out_f64(out), ref, spec.out_dtype, tol)
+    say(f"    max|err| = {err:.3e} (tol {tol})")
+    assert np.isfinite(out_f64(out)).all() and err <= tol
+
+
+@pytest.mark.parametrize("case", ["split", "groups"])
+def test_workspace_reused_across_calls(case):
+    """One workspace serves several calls in a row (each call's pieces
+    overwrite the previous call's): outputs are identical across the calls
+    and equal the oracle's."""
+    from gpu_common import group_args
+    if case == "split":
+        spec = SMALL["llama3_8b_bf16_small"]
+        lay = build_layout(spec)
+        kw = dict(partition_blocks=3)
+    else:
+        spec, lay = _grouped_layout("prefix_groups_f16_g8_d128")
+        kw = {}
+    say(f"[workspace reuse] {case}")
+    x = make_host_inputs(lay)
+    xs = _to_dev(x)
+    if case == "groups":
+        kw.update(group_args(xs))
+    first = _out(spec)
+    dims = pkv.decode_dims(xs["q"][0], xs["k_cache"][0], xs["block_tables"], first,
+                           kw.get("partition_blocks", 0), 0, 0, False, 0,
+                           len(lay.group_blocks) if case == "groups" else 0, kw.get("prefix_max_seqs", 0),
+                           kw.get("prefix_max_blocks", 0))
+    need = pkv.decode_workspace_bytes(dims)
+    assert need > 0
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)    # NaN-filled partial rows
+    if spec.append:
+        pkv.kv_append(xs["k_new"][0], xs["v_new"][0], xs["slot_mapping"], xs["k_cache"][0], xs["v_cache"][0])
+    outs = []
+    for i in range(3):
+        o = _out(spec)
+        pkv.paged_decode_attn(xs["q"][0], xs["k_cache"][0], xs["v_cache"][0], xs["block_tables"],
+                              xs["context_lens"], spec.scale, o, workspace=ws, **kw)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+    ref = oracle_rows(host_layer(x, 0), lay, spec)
+    err = parity_err(out_f64(outs[2]), ref, spec.out_dtype, TOL[spec.kv_dtype])
+    say(f"    max|err| = {err:.3e}")
+    assert err <= TOL[spec.kv_dtype]
+
+
 @pytest.mark.parametrize("pb", [1, 2, 3, 7])
 def test_split_size_invariance(pb):
     say(f"[split] tiny_f32 partition_blocks={pb}")
