@@ -59,13 +59,21 @@ def _encode(q: np.ndarray, code: str) -> np.ndarray:
 
 
 def kv_append_quant(cache_codes, scales, new_values, slot_mapping, *, code: str,
-                    first_write: bool, channel_scales=None, block_size: int = 16):
+                    first_write: bool, channel_scales=None, block_size: int = 16,
+                    granularity: str = "block"):
     """Quantise-on-write into an 8-bit cache; returns new (codes, scales).
 
     [P5] section 7: 8-bit K/V with one scale per head, and K in FP8 with V in
     INT8 as the mixed form; [P1] section 5.2: per-channel factors for K's
-    outlier channels.  `code` is "fp8_e4m3" (OCP e4m3fn, QMAX = 448) or
-    "int8" (symmetric, QMAX = 127, -128 unused).
+    outlier channels, or per-token scales.  `code` is "fp8_e4m3" (OCP
+    e4m3fn, QMAX = 448) or "int8" (symmetric, QMAX = 127, -128 unused).
+
+    granularity "token": scales is float32 [NB, Hkv, bs], one per (slot,
+    head), and every written token sets its own scales from its own row
+    before its codes are taken -- scale = float32(max_d |y[t, h, d]|) /
+    float32(QMAX) in fp32 (1.0 when that max is 0) -- so no value
+    saturates; `first_write` must then be False (it has no meaning).  The
+    rest of this docstring describes the default, granularity "block".
 
     cache_codes: [NB, Hkv, bs, D] codes; scales: float32 [NB, Hkv];
     new_values: float32 [T, Hkv, D] (the source values, widened exactly);
@@ -96,6 +104,18 @@ def kv_append_quant(cache_codes, scales, new_values, slot_mapping, *, code: str,
             raise ValueError("channel scales must be [Hkv, D]")
         x = x / c[None, :, :]                                                    # float32 quotient
     live = [(t, int(s)) for t, s in enumerate(slots) if 0 <= s < nb * bs]
+    if granularity == "token":
+        if first_write or sc.shape != (nb, hkv, bs):
+            raise ValueError("per-token scales are [NB, Hkv, bs] and always set by their token")
+        for t, s in live:
+            amax = np.abs(x[t]).max(axis=1)                                      # [Hkv], float32
+            tok = np.where(amax > 0, amax / qmax, np.float32(1.0))
+            sc[s // bs, :, s % bs] = tok
+            q = np.clip(x[t] / tok[:, None], -qmax, qmax)                        # float32 quotient
+            codes[s // bs, :, s % bs, :] = _encode(q, code)
+        return codes, sc
+    if granularity != "block" or sc.shape != (nb, hkv):
+        raise ValueError("granularity is 'block' (scales [NB, Hkv]) or 'token' (scales [NB, Hkv, bs])")
     if first_write:
         for t, s in live:
             if s % bs == 0:

@@ -16,6 +16,9 @@ What is computed, and where the pages state it:
     consecutive query heads share one K/V head (g = Hq / Hkv; MQA is Hkv = 1).
   * [P5] section 7: quantised K/V carry one scale per head; here one fp32
     scale per (physical block, KV head), and the value used is code * scale.
+    [P1] section 5.2 names finer granularities against K's outlier
+    channels: per channel (below) or per token -- one fp32 scale per
+    (slot, KV head) -- and quantising V alone with K kept in 16 bits.
   * [P5] section 7: K is the more sensitive of the two, so K may stay in FP8
     while V goes to INT8 (symmetric integer codes, value = code * scale);
     [P1] section 5.2: K has outlier channels, which per-channel scaling
@@ -72,9 +75,12 @@ def gather_sequence(cache, table_row, length: int, kv_tag: str, kv_heads=None,
     """Contiguous float64 [n, len(kv_heads), D] copy of one sequence's tokens.
 
     `cache` is the raw storage array [num_blocks, Hkv, block_size, D] (uint16
-    bits for bf16, uint8 codes for fp8, int8 codes for int8); `scales`
-    ([num_blocks, Hkv] fp32) is required for the quantised tags and multiplies
-    every element of its (block, head) tile; `channel_scales` ([Hkv, D] fp32,
+    bits for bf16, uint8 codes for fp8, int8 codes for int8); `scales` is
+    required for the quantised tags: fp32 [num_blocks, Hkv], one scale that
+    multiplies every element of its (block, head) tile, or fp32
+    [num_blocks, Hkv, block_size], one scale per (slot, head) -- the
+    per-token granularity of [P1] section 5.2 -- that multiplies the D
+    elements of that token's row; `channel_scales` ([Hkv, D] fp32,
     optional) multiplies channel d of head h.  The tokens are `positions`
     (default: 0 .. length-1), all < length.
     """
@@ -94,7 +100,12 @@ def gather_sequence(cache, table_row, length: int, kv_tag: str, kv_heads=None,
         if scales is None:
             raise ValueError("quantised caches need their per-(block, head) scales")
         s = np.asarray(scales, dtype=np.float32).astype(np.float64)
-        vals = vals * s[blk[:, None], kv_heads[None, :]][:, :, None]
+        if s.shape == (nb, cache.shape[1]):
+            vals = vals * s[blk[:, None], kv_heads[None, :]][:, :, None]
+        elif s.shape == (nb, cache.shape[1], block_size):
+            vals = vals * s[blk[:, None], kv_heads[None, :], off[:, None]][:, :, None]
+        else:
+            raise ValueError("scales must be [num_blocks, Hkv] or [num_blocks, Hkv, block_size]")
     elif scales is not None:
         raise ValueError("scales apply to quantised caches only")
     if channel_scales is not None:

@@ -266,3 +266,79 @@ def test_channel_scales_divide_before_quantising(code):
     others = [d for d in range(D) if d != 3]
     assert (np.abs(out_c[0, :, 0, others].astype(int)).max() >
             4 * np.abs(out_n[0, :, 0, others].astype(int)).max())
+
+
+# --------------------------------------------------------------------------
+# per-token scales ("KV Cache from first principles" 5.2: per-token granularity)
+# --------------------------------------------------------------------------
+
+def _token_case(code, seed=7, T=5, H=2, D=8, NB=4):
+    rng = np.random.default_rng(seed)
+    if code == "fp8_e4m3":
+        codes = rng.integers(0, 0x70, size=(NB, H, BS, D)).astype(np.uint8)
+    else:
+        codes = rng.integers(-127, 128, size=(NB, H, BS, D)).astype(np.int8)
+    scales = rng.uniform(0.01, 0.1, size=(NB, H, BS)).astype(np.float32)
+    x = (rng.standard_normal((T, H, D)) * 3).astype(np.float32)
+    x[1] *= 50                                     # one token far larger than the others
+    return codes, scales, x
+
+
+@pytest.mark.parametrize("code", ["fp8_e4m3", "int8"])
+def test_per_token_append_scales_each_token_by_its_own_row(code):
+    """Each written token's (slot, head) scale is its row's max |x| / QMAX;
+    its largest element lands exactly on +-QMAX; codes are torch's float8
+    cast (fp8) or the brute-force nearest integer (int8) of the fp32
+    quotient; no other slot or scale changes."""
+    codes, scales, x = _token_case(code)
+    slots = np.array([0, 17, 33, -1, 63])
+    out, sc = kv_append_quant(codes, scales, x, slots, code=code, first_write=False, granularity="token")
+    qmax = np.float32(448 if code == "fp8_e4m3" else 127)
+    touched = np.zeros(scales.shape, bool)
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        blk, off = s // BS, s % BS
+        amax = np.abs(x[t]).max(axis=1)
+        assert np.array_equal(sc[blk, :, off], (amax / qmax).astype(np.float32))
+        touched[blk, :, off] = True
+        q = np.clip(x[t] / sc[blk, :, off][:, None], -qmax, qmax).astype(np.float32)
+        got = out[blk, :, off, :]
+        if code == "fp8_e4m3":
+            ref = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(got, ref)
+            peak = np.abs(decode_e4m3fn(got)).max(axis=1)
+        else:
+            assert np.array_equal(got, _nearest_int8_brute(q))
+            peak = np.abs(got.astype(np.float64)).max(axis=1)
+        assert np.array_equal(peak, [float(qmax)] * x.shape[1])
+    assert np.array_equal(sc[~touched], scales[~touched])
+    mask = np.ones(codes.shape, bool)
+    for s in slots[slots >= 0]:
+        mask[s // BS, :, s % BS, :] = False
+    assert np.array_equal(out[mask], codes[mask])
+
+
+def test_per_token_append_round_trips_and_rejects_bad_calls():
+    """A row that is a code vector times a power of two with its largest
+    code at +-QMAX comes back as the same codes and that scale; a zero row
+    gets scale 1; first-write mode and block-shaped scales are refused."""
+    rng = np.random.default_rng(8)
+    c = rng.integers(-127, 128, size=(1, 2, 8)).astype(np.int8)
+    c[0, :, 0] = [127, -127]
+    x = (c.astype(np.float32) * np.float32(0.125))
+    codes = np.zeros((2, 2, BS, 8), np.int8)
+    scales = np.zeros((2, 2, BS), np.float32)
+    out, sc = kv_append_quant(codes, scales, x, np.array([21]), code="int8", first_write=False,
+                              granularity="token")
+    assert np.array_equal(out[1, :, 5, :], c[0]) and np.array_equal(sc[1, :, 5], [0.125, 0.125])
+    out, sc = kv_append_quant(codes, scales, np.zeros((1, 2, 8), np.float32), np.array([3]), code="int8",
+                              first_write=False, granularity="token")
+    assert np.all(sc[0, :, 3] == 1.0) and np.all(out[0, :, 3, :] == 0)
+    with pytest.raises(ValueError):
+        kv_append_quant(codes, scales, x, np.array([3]), code="int8", first_write=True, granularity="token")
+    with pytest.raises(ValueError):
+        kv_append_quant(codes, scales[:, :, 0], x, np.array([3]), code="int8", first_write=False,
+                        granularity="token")
+    with pytest.raises(ValueError):
+        kv_append_quant(codes, scales, x, np.array([3]), code="int8", first_write=False)

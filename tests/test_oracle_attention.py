@@ -361,6 +361,10 @@ MUTANTS = {
     "side_sinks_ignored": ("        if side and len(first):", "        if False:"),
     "side_sink_offset": ("[kv_needed][:, first, :].transpose(1, 0, 2)   # [n, h, D]",
                          "[kv_needed][:, first[::-1], :].transpose(1, 0, 2)   # [n, h, D]"),
+    "token_scale_offset_ignored": ("vals = vals * s[blk[:, None], kv_heads[None, :], off[:, None]][:, :, None]",
+                                   "vals = vals * s[blk[:, None], kv_heads[None, :], 0 * off[:, None]][:, :, None]"),
+    "token_scale_offset_reversed": ("vals = vals * s[blk[:, None], kv_heads[None, :], off[:, None]][:, :, None]",
+                                    "vals = vals * s[blk[:, None], kv_heads[None, :], (block_size - 1 - off)[:, None]][:, :, None]"),
     "query_head_index": ("qv = stored_to_f64(np.asarray(q)[seqs][:, q_heads], q_tag)",
                          "qv = stored_to_f64(np.asarray(q)[seqs][:, q_heads][:, ::-1], q_tag)"),
 }
@@ -430,6 +434,80 @@ def test_mixed_precision_pin():
     _mixed_pin(oracle)
 
 
+def _token_scale_pin(mod):
+    """fp8 K and int8 V with one scale per (slot, head): the dense reference
+    multiplies each token's row by the scale of its own slot, built
+    position by position."""
+    rng = np.random.default_rng(12)
+    lens = [21, 40]
+    Hkv, D = 2, 8
+    codes_k = [rng.integers(0, 0x70, size=(L, Hkv, D)).astype(np.uint8) for L in lens]
+    codes_v = [rng.integers(-127, 128, size=(L, Hkv, D)).astype(np.int8) for L in lens]
+    kc, _, t, Ls = paged_from_contiguous(codes_k, codes_k, 7, seed=22, storage=np.uint8, fill=0x7F)
+    vc, _, t2, _ = paged_from_contiguous(codes_v, codes_v, 7, seed=22, storage=np.int8, fill=0)
+    assert np.array_equal(t, t2)
+    ks = rng.uniform(0.001, 0.1, size=(7, Hkv, BS)).astype(np.float32)
+    vs = rng.uniform(0.001, 0.1, size=(7, Hkv, BS)).astype(np.float32)
+    q = rng.standard_normal((2, 4, D)).astype(np.float32)
+    got = mod.paged_decode_attention(q, kc, vc, t, Ls, 0.4, q_tag="f32", kv_tag="fp8_e4m3",
+                                     v_tag="int8", k_scales=ks, v_scales=vs)
+    dec = lambda a: torch.from_numpy(a).view(torch.float8_e4m3fn).double().numpy()
+    sk_d, sv_d = [], []
+    for b, L in enumerate(lens):
+        kd = np.zeros((L, Hkv, D)); vd = np.zeros_like(kd)
+        for pos in range(L):
+            blk, off = t[b][pos // BS], pos % BS
+            kd[pos] = dec(codes_k[b][pos]) * ks[blk, :, off][:, None]
+            vd[pos] = codes_v[b][pos].astype(np.float64) * vs[blk, :, off][:, None]
+        sk_d.append(kd); sv_d.append(vd)
+    ref = sdpa_reference(q.astype(np.float64), sk_d, sv_d, 0.4)
+    np.testing.assert_allclose(got, ref, atol=1e-12)
+
+
+def _k16_v8_pin(mod):
+    """K kept in f16 (as stored, no scale) with V in fp8 (block scales) or
+    int8 (per-token scales): the dense reference reads K as f16 values and
+    V as code times scale, position by position."""
+    rng = np.random.default_rng(13)
+    lens = [17, 33, 5]
+    Hkv, D = 1, 8
+    k16 = [rng.standard_normal((L, Hkv, D)).astype(np.float16) for L in lens]
+    codes_f8 = [rng.integers(0, 0x70, size=(L, Hkv, D)).astype(np.uint8) for L in lens]
+    codes_i8 = [rng.integers(-127, 128, size=(L, Hkv, D)).astype(np.int8) for L in lens]
+    kc, _, t, Ls = paged_from_contiguous(k16, k16, 6, seed=23, storage=np.float16, fill=np.nan)
+    v8, _, t2, _ = paged_from_contiguous(codes_f8, codes_f8, 6, seed=23, storage=np.uint8, fill=0x7F)
+    vi, _, t3, _ = paged_from_contiguous(codes_i8, codes_i8, 6, seed=23, storage=np.int8, fill=0)
+    assert np.array_equal(t, t2) and np.array_equal(t, t3)
+    vs_blk = rng.uniform(0.01, 0.1, size=(6, Hkv)).astype(np.float32)
+    vs_tok = rng.uniform(0.01, 0.1, size=(6, Hkv, BS)).astype(np.float32)
+    q = rng.standard_normal((3, 4, D)).astype(np.float16)
+    dec = lambda a: torch.from_numpy(a).view(torch.float8_e4m3fn).double().numpy()
+    for vcache, vtag, vs in ((v8, "fp8_e4m3", vs_blk), (vi, "int8", vs_tok)):
+        got = mod.paged_decode_attention(q, kc, vcache, t, Ls, 0.35, q_tag="f16", kv_tag="f16",
+                                         v_tag=vtag, v_scales=vs)
+        sk_d, sv_d = [], []
+        for b, L in enumerate(lens):
+            kd = np.zeros((L, Hkv, D)); vd = np.zeros_like(kd)
+            for pos in range(L):
+                blk, off = t[b][pos // BS], pos % BS
+                kd[pos] = k16[b][pos].astype(np.float64)
+                if vtag == "fp8_e4m3":
+                    vd[pos] = dec(codes_f8[b][pos]) * vs[blk][:, None]
+                else:
+                    vd[pos] = codes_i8[b][pos].astype(np.float64) * vs[blk, :, off][:, None]
+            sk_d.append(kd); sv_d.append(vd)
+        ref = sdpa_reference(q.astype(np.float64), sk_d, sv_d, 0.35)
+        np.testing.assert_allclose(got, ref, atol=1e-12)
+
+
+def test_per_token_scale_pin():
+    _token_scale_pin(oracle)
+
+
+def test_k16_with_v8_pin():
+    _k16_v8_pin(oracle)
+
+
 def _side_sink_pin(mod):
     """int8 cache with the first S positions of each sequence in f16 side
     tiles: the dense reference takes positions < S from the tile, as stored,
@@ -474,7 +552,7 @@ def test_full_precision_sink_pin():
 def test_planted_mistake_is_caught(name):
     mod = _mutant_module(name)
     caught = []
-    for pin in PINS + [_fp8_pin, _mixed_pin, _side_sink_pin]:
+    for pin in PINS + [_fp8_pin, _mixed_pin, _side_sink_pin, _token_scale_pin, _k16_v8_pin]:
         try:
             pin(mod)
         except (AssertionError, IndexError, ValueError, TypeError):
