@@ -84,7 +84,10 @@ def attention_bytes(spec, lay, window: int = 0, sinks: int = 0):
     q = spec.num_seqs * spec.num_q_heads * spec.head_dim * ELT[spec.q_dtype]
     out = spec.num_seqs * spec.num_q_heads * spec.head_dim * ELT[spec.out_dtype]
     meta = int(nblk.sum()) * 4 + spec.num_seqs * 4
-    scales = int(nblk.sum()) * spec.num_kv_heads * 4 * 2 if spec.quantised else 0
+    # 8-bit scales of every attended (block, KV head): one fp32, or 16 per-token ones
+    per_scale = lambda tok: int(nblk.sum()) * spec.num_kv_heads * 4 * (16 if tok else 1)
+    scales = ((per_scale(spec.k_scale_tok) if spec.k_quantised else 0) +
+              (per_scale(spec.v_scale_tok) if spec.v_tag in ("fp8_e4m3", "int8") else 0))
     chan = spec.num_kv_heads * spec.head_dim * 4 if spec.k_outliers else 0
     return kv, kv + q + out + meta + scales + chan, logical
 
@@ -130,9 +133,9 @@ def cpu_baseline(spec, lay, x, budget_s: float, outs=None):
             lens = lay.context_lens[b : b + 1]
             q = host(x["q"][layer][b : b + 1])
             kw = {}
-            if "k_scales" in x:
-                kw = dict(k_scales=host(x["k_scales"][layer].index_select(0, idx)),
-                          v_scales=host(x["v_scales"][layer].index_select(0, idx)))
+            for name in ("k_scales", "v_scales"):
+                if name in x:
+                    kw[name] = host(x[name][layer].index_select(0, idx))
             chan = host(x["k_channel_scales"]) if "k_channel_scales" in x else None
             if spec.fp_sinks:
                 tile = int(x["sink_tiles_of_seq"][b])
@@ -145,14 +148,20 @@ def cpu_baseline(spec, lay, x, budget_s: float, outs=None):
                 slot = np.array([int(np.nonzero(used == s // 16)[0][0]) * 16 + s % 16])
                 kn = host(x["k_new"][layer][b : b + 1])
                 vn = host(x["v_new"][layer][b : b + 1])
-                if "k_scales" in x:
-                    kn = oracle.stored_to_f64(kn, spec.q_dtype).astype(np.float32)
+                gran = lambda tok: "token" if tok else "block"
+                if spec.quantised:
+                    if spec.k_quantised:
+                        kn = oracle.stored_to_f64(kn, spec.q_dtype).astype(np.float32)
+                        kc, kw["k_scales"] = oracle.kv_append_quant(kc, kw["k_scales"], kn, slot,
+                                                                    code=spec.kv_dtype, first_write=False,
+                                                                    channel_scales=chan,
+                                                                    granularity=gran(spec.k_scale_tok))
+                    else:
+                        kc = oracle.kv_append_bits(kc, kn, slot)
                     vn = oracle.stored_to_f64(vn, spec.q_dtype).astype(np.float32)
-                    kc, kw["k_scales"] = oracle.kv_append_quant(kc, kw["k_scales"], kn, slot,
-                                                                code=spec.kv_dtype, first_write=False,
-                                                                channel_scales=chan)
                     vc, kw["v_scales"] = oracle.kv_append_quant(vc, kw["v_scales"], vn, slot,
-                                                                code=spec.v_tag, first_write=False)
+                                                                code=spec.v_tag, first_write=False,
+                                                                granularity=gran(spec.v_scale_tok))
                 else:
                     kc = oracle.kv_append_bits(kc, kn, slot)
                     vc = oracle.kv_append_bits(vc, vn, slot)
@@ -501,7 +510,8 @@ def main():
     ws_bytes = pkv.decode_workspace_bytes(dims)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     chan = x.get("k_channel_scales")
-    both_fp8 = spec.kv_dtype == spec.v_tag == "fp8_e4m3" and chan is None and not spec.fp_sinks
+    both_fp8 = (spec.kv_dtype == spec.v_tag == "fp8_e4m3" and chan is None and not spec.fp_sinks
+                and not (spec.k_scale_tok or spec.v_scale_tok))
     # 16-bit and f32 caches: the append rides in the attention launch
     fused = spec.append and not spec.quantised and not spec.fp_sinks and not args.separate_append
 
@@ -510,7 +520,9 @@ def main():
             kc, vc = x["k_cache"][layer], x["v_cache"][layer]
             kw = {}
             if spec.quantised:
-                kw = dict(k_scales=x["k_scales"][layer], v_scales=x["v_scales"][layer])
+                kw = dict(v_scales=x["v_scales"][layer])
+                if spec.k_quantised:
+                    kw["k_scales"] = x["k_scales"][layer]
                 if chan is not None:
                     kw["k_channel_scales"] = chan
             if spec.fp_sinks:
@@ -523,8 +535,11 @@ def main():
                 pkv.kv_append_fp8(x["k_new"][layer], x["v_new"][layer], x["slot_mapping"], kc, vc,
                                   kw["k_scales"], kw["v_scales"])
             elif spec.append and spec.quantised:
-                pkv.kv_append_quant(x["k_new"][layer], x["slot_mapping"], kc, kw["k_scales"],
-                                    channel_scales=chan)
+                if spec.k_quantised:
+                    pkv.kv_append_quant(x["k_new"][layer], x["slot_mapping"], kc, kw["k_scales"],
+                                        channel_scales=chan)
+                else:                               # a 16-bit K: a bit copy of K alone
+                    pkv.kv_append(x["k_new"][layer], None, x["slot_mapping"], kc, None)
                 pkv.kv_append_quant(x["v_new"][layer], x["slot_mapping"], vc, kw["v_scales"])
             elif spec.append and not fused:
                 pkv.kv_append(x["k_new"][layer], x["v_new"][layer], x["slot_mapping"], kc, vc)
@@ -609,6 +624,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": spec.kv_dtype if spec.v_tag == spec.kv_dtype else f"{spec.kv_dtype}+{spec.v_tag}",
+        "scales": None if not spec.quantised else ("per token" if (spec.k_scale_tok or spec.v_scale_tok)
+                                                   else "per block"),
         "data": "synthetic",
         "config": {
             "workload": spec.name,

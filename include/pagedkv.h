@@ -55,7 +55,7 @@ extern "C" {
 #define PKV_API
 #endif
 
-#define PKV_VERSION 160  /* 1.6.0 */
+#define PKV_VERSION 170  /* 1.7.0 */
 #define PKV_BLOCK_SIZE 16
 /* Device scratch held by pkv_paged_decode_attn_noalloc, per device. */
 #define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
@@ -121,6 +121,8 @@ typedef struct {
  *   Slots must be distinct (duplicates race).  Slots >= num_blocks * 16 are
  *   skipped like -1.  dtype: F32, F16 or BF16.  head_dim: any multiple of
  *   16 / sizeof(element) up to 1024 (the attention calls need 64 or 128).
+ *   v_new and v_cache may both be NULL: K alone is written (a 16-bit K next
+ *   to an 8-bit V, whose rows pkv_kv_append_quant writes).
  *   Does not touch context lengths: the caller advances them.
  */
 PKV_API int pkv_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
@@ -129,8 +131,10 @@ PKV_API int pkv_kv_append(const void* k_new, const void* v_new, const int64_t* s
                   hipStream_t stream);
 
 typedef enum {
-  PKV_SCALE_GIVEN = 0,      /* scales are set by the caller (e.g. calibrated) */
-  PKV_SCALE_FIRST_WRITE = 1 /* a block's first token (offset 0) sets its scale */
+  PKV_SCALE_GIVEN = 0,       /* scales are set by the caller (e.g. calibrated) */
+  PKV_SCALE_FIRST_WRITE = 1, /* a block's first token (offset 0) sets its scale */
+  PKV_SCALE_PER_TOKEN = 2    /* one scale per (slot, head): scales are fp32
+                                [NB][Hkv][16], and every token sets its own */
 } pkv_scale_mode;
 
 /*
@@ -156,15 +160,19 @@ PKV_API int pkv_kv_append_fp8(const void* k_new, const void* v_new, const int64_
 
 /*
  * 8-bit append into ONE cache (K or V), quantising on write, for the fp8,
- * int8 and mixed (K fp8, V int8) layouts ("The KV Cache memory ledger" 7;
- * "KV Cache from first principles" 5.2: per-channel factors for K).
+ * int8 and mixed (K fp8, V int8; K 16-bit, V 8-bit) layouts ("The KV Cache
+ * memory ledger" 7; "KV Cache from first principles" 5.2: per-channel
+ * factors for K, per-token scales).
  * cache: codes of cache_dtype (FP8_E4M3 or INT8) [NB][Hkv][16][D]; scales:
- * fp32 [NB][Hkv] (read and, in first-write mode, written); channel_scales:
- * NULL or fp32 [Hkv][D] (device).  x_new: [T][Hkv][D] of src_dtype.  With
+ * fp32 [NB][Hkv], or [NB][Hkv][16] with PKV_SCALE_PER_TOKEN (read and, in
+ * first-write and per-token modes, written); channel_scales: NULL or fp32
+ * [Hkv][D] (device).  x_new: [T][Hkv][D] of src_dtype.  With
  * QMAX = 448 (fp8) or 127 (int8), for every t with 0 <= slot < NB*16:
  *   - y = x / channel_scales[h][d] (correctly rounded fp32), or y = x;
  *   - PKV_SCALE_FIRST_WRITE and off == 0: scale[blk][h] = max_d |y| / QMAX
  *     (1.0 if that max is 0), set for all such tokens before any is quantised;
+ *   - PKV_SCALE_PER_TOKEN: scale[blk][h][off] = max_d |y| / QMAX (1.0 if
+ *     that max is 0) for every token, from its own row;
  *   - code = nearest code, ties to even, of clamp(y / scale, -QMAX, QMAX)
  *     (correctly rounded fp32 quotient); NaN stays NaN (fp8) or becomes 0
  *     (int8).
@@ -274,6 +282,11 @@ typedef struct {
   const void* v_sink;
   const int32_t* sink_tiles_of_seq;  /* int32 [num_seqs] */
   int32_t num_sink_tiles;
+  /* 1: the scales are fp32 [num_blocks][num_kv_heads][16], one per (slot,
+   * head) (written by pkv_kv_append_quant with PKV_SCALE_PER_TOKEN); 0: one
+   * per (block, head) as above.  K and V choose independently. */
+  int32_t k_scales_per_token;
+  int32_t v_scales_per_token;
 } pkv_quant_params;
 
 /*
@@ -283,10 +296,15 @@ typedef struct {
  * first principles" 5.2: per-channel factors for K's outlier channels).
  * dims->kv_dtype is K's format and p->v_dtype V's: (FP8_E4M3, FP8_E4M3) with
  * the q/out pairs of pkv_paged_decode_attn_fp8, or (FP8_E4M3, INT8) and
- * (INT8, INT8) with q and out both F16 or both BF16.  A cached K element is
- * decode(code) * k_scales[block][h] * k_channel_scales[h][d] (the last factor
- * 1 when k_channel_scales is NULL), a V element decode(code) *
- * v_scales[block][h]; int8 codes decode to their integer value.  With
+ * (INT8, INT8) with q and out both F16 or both BF16, or a 16-bit K with an
+ * 8-bit V ("KV Cache from first principles" 5.2: quantise only V, keep K in
+ * fp16): (F16 or BF16, FP8_E4M3 or INT8) with q and out of K's type, K read
+ * as stored, k_scales and k_channel_scales NULL.  A cached 8-bit K element
+ * is decode(code) * k_scales[block][h] * k_channel_scales[h][d] (the last
+ * factor 1 when k_channel_scales is NULL), a V element decode(code) *
+ * v_scales[block][h]; with per-token scales the scale is that of the
+ * element's own slot, [block][h][offset].  int8 codes decode to their
+ * integer value.  With
  * dims->sink_tiles = 1 the first dims->sinks positions are read as stored
  * from the side tiles (see pkv_quant_params); the attended positions are
  * those of pkv_paged_decode_attn, and the call always splits the context

@@ -102,6 +102,8 @@ class QuantParams(ctypes.Structure):
         ("v_sink", ctypes.c_void_p),
         ("sink_tiles_of_seq", ctypes.c_void_p),
         ("num_sink_tiles", ctypes.c_int32),
+        ("k_scales_per_token", ctypes.c_int32),
+        ("v_scales_per_token", ctypes.c_int32),
     ]
 
 
@@ -216,27 +218,31 @@ def _code(t: torch.Tensor) -> int:
     return DTYPE_CODES[t.dtype]
 
 
-def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
-              k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+def kv_append(k_new: torch.Tensor, v_new: Optional[torch.Tensor], slot_mapping: torch.Tensor,
+              k_cache: torch.Tensor, v_cache: Optional[torch.Tensor]) -> None:
     """Write token t's K/V rows into slot slot_mapping[t] (-1 = skip).
 
     k_new, v_new: [T, Hkv, D]; slot_mapping: int64 [T];
-    caches: [num_blocks, Hkv, 16, D] of the same dtype.
+    caches: [num_blocks, Hkv, 16, D] of the same dtype.  v_new and v_cache
+    both None: K alone (a 16-bit K next to an 8-bit V).
     """
     lib = load_library()
     _dev(k_new, v_new, slot_mapping, k_cache, v_cache)
-    _need(k_new.shape == v_new.shape and k_new.dim() == 3, "k_new/v_new must be [T, Hkv, D]")
-    _need(k_cache.shape == v_cache.shape and k_cache.dim() == 4, "caches must be [NB, Hkv, 16, D]")
+    _need((v_new is None) == (v_cache is None), "v_new and v_cache go together")
+    _need(k_new.dim() == 3 and (v_new is None or k_new.shape == v_new.shape), "k_new/v_new must be [T, Hkv, D]")
+    _need(k_cache.dim() == 4 and (v_cache is None or k_cache.shape == v_cache.shape),
+          "caches must be [NB, Hkv, 16, D]")
     T, H, D = k_new.shape
     _need(k_cache.shape[1] == H and k_cache.shape[3] == D, "cache and new-token shapes differ")
     _need(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (T,), "slot_mapping must be int64 [T]")
-    _need(k_new.dtype == v_new.dtype == k_cache.dtype == v_cache.dtype, "dtype mismatch")
+    _need(k_new.dtype == k_cache.dtype and (v_new is None or v_new.dtype == v_cache.dtype == k_cache.dtype),
+          "dtype mismatch")
     _check(lib.pkv_kv_append(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache),
                              _ptr(v_cache), T, H, D, k_cache.shape[0], k_cache.shape[2],
                              _code(k_cache), _stream(k_cache)))
 
 
-SCALE_GIVEN, SCALE_FIRST_WRITE = 0, 1
+SCALE_GIVEN, SCALE_FIRST_WRITE, SCALE_PER_TOKEN = 0, 1, 2
 
 
 def kv_append_fp8(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
@@ -271,9 +277,10 @@ def kv_append_quant(x_new: torch.Tensor, slot_mapping: torch.Tensor, cache: torc
     """Quantise token t's rows (f32/f16/bf16) into ONE 8-bit cache at its slot.
 
     x_new: [T, Hkv, D]; cache: fp8 (uint8 / float8_e4m3fn) or int8 [NB, Hkv, 16, D];
-    scales: fp32 [NB, Hkv]; channel_scales: optional fp32 [Hkv, D] that each
-    element is divided by first.  first_write as in kv_append_fp8 (QMAX 448 for
-    fp8, 127 for int8).
+    scales: fp32 [NB, Hkv], or fp32 [NB, Hkv, 16] for one scale per (slot, head)
+    (every token then sets its own from its row); channel_scales: optional fp32
+    [Hkv, D] that each element is divided by first.  first_write as in
+    kv_append_fp8 (QMAX 448 for fp8, 127 for int8).
     """
     lib = load_library()
     _dev(x_new, slot_mapping, cache, scales, channel_scales)
@@ -282,14 +289,18 @@ def kv_append_quant(x_new: torch.Tensor, slot_mapping: torch.Tensor, cache: torc
     T, H, D = x_new.shape
     _need(cache.shape[1] == H and cache.shape[3] == D, "cache and new-token shapes differ")
     _need(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (T,), "slot_mapping must be int64 [T]")
-    _need(scales.dtype == torch.float32 and scales.shape == cache.shape[:2], "scales must be fp32 [NB, Hkv]")
+    per_token = scales.dim() == 3
+    _need(scales.dtype == torch.float32 and scales.shape in (cache.shape[:2], cache.shape[:3]),
+          "scales must be fp32 [NB, Hkv] or [NB, Hkv, 16]")
+    _need(not (per_token and first_write), "per-token scales are always set by their token")
     _need(channel_scales is None or (channel_scales.dtype == torch.float32 and
                                      channel_scales.shape == (H, D)), "channel_scales must be fp32 [Hkv, D]")
     _need(_code(x_new) in (0, 1, 2), "x_new must be f32/f16/bf16")
     _check(lib.pkv_kv_append_quant(_ptr(x_new), _ptr(slot_mapping), _ptr(cache), _ptr(scales),
                                    _ptr(channel_scales), T, H, D, cache.shape[0], cache.shape[2],
                                    _code(x_new), _code(cache),
-                                   SCALE_FIRST_WRITE if first_write else SCALE_GIVEN, _stream(cache)))
+                                   SCALE_PER_TOKEN if per_token else
+                                   (SCALE_FIRST_WRITE if first_write else SCALE_GIVEN), _stream(cache)))
 
 
 def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src: torch.Tensor, dst: torch.Tensor,
@@ -424,8 +435,10 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
 
     q, out: [B, Hq, D]; caches: [NB, Hkv, 16, D]; block_tables: int32 [B, max_blocks];
     context_lens: int32 [B].  8-bit caches -- fp8 (uint8 or float8_e4m3fn) or
-    int8, K fp8 with V int8 allowed -- need k_scales and v_scales: fp32 [NB, Hkv],
-    and may give k_channel_scales: fp32 [Hkv, D] for K, and full-precision sink
+    int8, K fp8 with V int8 allowed, or a 16-bit K (q's dtype) with an 8-bit V --
+    need k_scales (8-bit K only) and v_scales: fp32 [NB, Hkv], or [NB, Hkv, 16]
+    for one scale per (slot, head); an 8-bit K may give k_channel_scales: fp32
+    [Hkv, D], and the caller may give full-precision sink
     tiles sink_k, sink_v: [num_tiles, Hkv, 16, D] of q's dtype with
     sink_tiles_of_seq: int32 [B] (positions < sinks of sequence b are read from
     its tile; 1 <= sinks <= 16, with or without a window).  total_blocks (the
@@ -447,7 +460,8 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     _need(q.dim() == 3 and out.shape == q.shape, "q and out must be [B, Hq, D]")
     _need(k_cache.shape == v_cache.shape and k_cache.dim() == 4, "caches must be [NB, Hkv, 16, D]")
     kc, vc = _code(k_cache), _code(v_cache)
-    _need(kc == vc or (kc in _Q8 and vc in _Q8), "K and V caches differ in dtype")
+    _need(kc == vc or (vc in _Q8 and (kc in _Q8 or kc in (1, 2))),
+          "K and V caches differ in dtype (an 8-bit V may go with an 8-bit or a 16-bit K)")
     _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
           and block_tables.shape[0] == q.shape[0], "block_tables must be int32 [B, max_blocks]")
     _need(context_lens.dtype == torch.int32 and context_lens.shape == (q.shape[0],),
@@ -469,7 +483,7 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         _need(prefix_group_starts.dtype == prefix_group_blocks.dtype == torch.int32
               and prefix_group_blocks.dim() == 1 and prefix_group_starts.shape == (G + 1,),
               "prefix_group_starts must be int32 [G + 1] and prefix_group_blocks int32 [G]")
-        _need(kc in (1, 2), "shared prefixes need f16 or bf16 caches")
+        _need(kc == vc and kc in (1, 2), "shared prefixes need f16 or bf16 caches")
     dims = decode_dims(q, k_cache, block_tables, out, partition_blocks, window, sinks, side, total_blocks,
                        G, prefix_max_seqs if grouped else 0, prefix_max_blocks if grouped else 0)
     need = decode_workspace_bytes(dims)
@@ -477,14 +491,20 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _ptr(workspace) if need else None
     ws_bytes = workspace.numel() * workspace.element_size() if (need and workspace is not None) else 0
-    if kc in _Q8:
-        _need(k_scales is not None and v_scales is not None, "8-bit caches need k_scales and v_scales")
-        _need(k_scales.dtype == v_scales.dtype == torch.float32 and
-              k_scales.shape == v_scales.shape == k_cache.shape[:2], "scales must be fp32 [NB, Hkv]")
-        _need(k_channel_scales is None or (k_channel_scales.dtype == torch.float32 and
+    if vc in _Q8:
+        k8 = kc in _Q8
+        _need(v_scales is not None and (k_scales is not None) == k8,
+              "an 8-bit V needs v_scales, an 8-bit K k_scales (a 16-bit K takes none)")
+        for sc in (k_scales, v_scales):
+            _need(sc is None or (sc.dtype == torch.float32 and
+                                 sc.shape in (k_cache.shape[:2], k_cache.shape[:3])),
+                  "scales must be fp32 [NB, Hkv], or [NB, Hkv, 16] for one per (slot, head)")
+        k_tok = int(k_scales is not None and k_scales.dim() == 3)
+        v_tok = int(v_scales.dim() == 3)
+        _need(k_channel_scales is None or (k8 and k_channel_scales.dtype == torch.float32 and
                                            k_channel_scales.shape == (k_cache.shape[1], k_cache.shape[3])),
-              "k_channel_scales must be fp32 [Hkv, D]")
-        if kc == vc == 3 and k_channel_scales is None and not side:
+              "k_channel_scales must be fp32 [Hkv, D], for an 8-bit K")
+        if kc == vc == 3 and k_channel_scales is None and not side and not (k_tok or v_tok):
             st = lib.pkv_paged_decode_attn_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales),
                                                _ptr(v_scales), _ptr(block_tables), _ptr(context_lens),
                                                float(scale), _ptr(out), ctypes.byref(dims), ws_ptr,
@@ -492,7 +512,7 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         else:
             qp = QuantParams(_ptr(k_scales), _ptr(v_scales), _ptr(k_channel_scales), vc,
                              _ptr(sink_k), _ptr(sink_v), _ptr(sink_tiles_of_seq),
-                             sink_k.shape[0] if side else 0)
+                             sink_k.shape[0] if side else 0, k_tok, v_tok)
             st = lib.pkv_paged_decode_attn_quant(_ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(qp),
                                                  _ptr(block_tables), _ptr(context_lens), float(scale),
                                                  _ptr(out), ctypes.byref(dims), ws_ptr, ws_bytes,

@@ -90,6 +90,8 @@ int check_dtypes(const pkv_decode_dims* d, int v_dtype) {
   if (v_dtype >= 0) {
     const int k = d->kv_dtype, q = d->q_dtype, o = d->out_dtype;
     if (is_q8(q) || is_q8(o)) return PKV_ERR_DTYPE;
+    if (k == PKV_F16 || k == PKV_BF16)   // 16-bit K with 8-bit V: q and out of K's type
+      return is_q8(v_dtype) && q == k && o == k ? PKV_OK : PKV_ERR_DTYPE;
     if (k == PKV_FP8_E4M3 && v_dtype == PKV_FP8_E4M3) {
       const bool ok = (q == o) || (o == PKV_F32 && (q == PKV_BF16 || q == PKV_F16));
       return ok ? PKV_OK : PKV_ERR_DTYPE;
@@ -139,7 +141,15 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
     if (dims->kv_dtype != PKV_F16 && dims->kv_dtype != PKV_BF16) return PKV_ERR_DTYPE;
   }
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
-  if (qp && (!qp->k_scales || !qp->v_scales)) return PKV_ERR_NULL;
+  if (qp) {
+    const bool k8 = is_q8(dims->kv_dtype);
+    if (!qp->v_scales || (k8 && !qp->k_scales)) return PKV_ERR_NULL;
+    if (!k8 && (qp->k_scales || qp->k_channel_scales || qp->k_scales_per_token))
+      return PKV_ERR_DTYPE;                    // a 16-bit K is read as stored
+    if ((qp->k_scales_per_token != 0 && qp->k_scales_per_token != 1) ||
+        (qp->v_scales_per_token != 0 && qp->v_scales_per_token != 1))
+      return PKV_ERR_SHAPE;
+  }
   if (dims->sink_tiles) {
     if (!qp) return PKV_ERR_SHAPE;            // side tiles exist for 8-bit caches only
     if (!qp->k_sink || !qp->v_sink || !qp->sink_tiles_of_seq) return PKV_ERR_NULL;
@@ -167,6 +177,8 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
   a.k_scales = qp ? qp->k_scales : nullptr;
   a.v_scales = qp ? qp->v_scales : nullptr;
   a.k_chan = qp ? qp->k_channel_scales : nullptr;
+  a.k_tok = qp ? qp->k_scales_per_token : 0;
+  a.v_tok = qp ? qp->v_scales_per_token : 0;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.scale = scale * 1.4426950408889634f;  // scores are kept in log2 units
@@ -235,7 +247,9 @@ int check_q8_append(int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, 
     return PKV_ERR_SHAPE;
   if (block_size != PKV_BLOCK_SIZE || head_dim % 16 || head_dim > 1024) return PKV_ERR_SHAPE;
   if (src_dtype != PKV_F32 && src_dtype != PKV_F16 && src_dtype != PKV_BF16) return PKV_ERR_DTYPE;
-  if (scale_mode != PKV_SCALE_GIVEN && scale_mode != PKV_SCALE_FIRST_WRITE) return PKV_ERR_SHAPE;
+  if (scale_mode != PKV_SCALE_GIVEN && scale_mode != PKV_SCALE_FIRST_WRITE &&
+      scale_mode != PKV_SCALE_PER_TOKEN)
+    return PKV_ERR_SHAPE;
   return PKV_OK;
 }
 
@@ -254,7 +268,8 @@ int pkv_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapp
   const int row_bytes = head_dim * elem_bytes(dtype);
   if (row_bytes % 16 || head_dim > 1024) return PKV_ERR_SHAPE;
   if (num_tokens == 0) return PKV_OK;
-  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKV_ERR_NULL;
+  const bool k_only = !v_new && !v_cache;   // a 16-bit K next to an 8-bit V
+  if (!k_new || !slot_mapping || !k_cache || (!k_only && (!v_new || !v_cache))) return PKV_ERR_NULL;
   return launch_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, num_tokens,
                           num_kv_heads, row_bytes, num_blocks, stream);
 }
@@ -267,12 +282,13 @@ int pkv_kv_append_fp8(const void* k_new, const void* v_new, const int64_t* slot_
   const int st = check_q8_append(num_tokens, num_kv_heads, head_dim, num_blocks, block_size,
                                  src_dtype, scale_mode);
   if (st) return st;
+  if (scale_mode == PKV_SCALE_PER_TOKEN) return PKV_ERR_SHAPE;   // per-token: pkv_kv_append_quant
   if (num_tokens == 0) return PKV_OK;
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache || !k_scales || !v_scales)
     return PKV_ERR_NULL;
   const QTargetArgs tg[2] = {{k_new, k_cache, k_scales, nullptr}, {v_new, v_cache, v_scales, nullptr}};
   return launch_kv_append_q8(tg, 2, slot_mapping, num_tokens, num_kv_heads, head_dim, num_blocks,
-                             src_dtype, PKV_FP8_E4M3, scale_mode == PKV_SCALE_FIRST_WRITE, stream);
+                             src_dtype, PKV_FP8_E4M3, scale_mode, stream);
 }
 
 int pkv_kv_append_quant(const void* x_new, const int64_t* slot_mapping, void* cache, float* scales,
@@ -288,7 +304,7 @@ int pkv_kv_append_quant(const void* x_new, const int64_t* slot_mapping, void* ca
   if (!x_new || !slot_mapping || !cache || !scales) return PKV_ERR_NULL;
   const QTargetArgs tg[1] = {{x_new, cache, scales, channel_scales}};
   return launch_kv_append_q8(tg, 1, slot_mapping, num_tokens, num_kv_heads, head_dim, num_blocks,
-                             src_dtype, cache_dtype, scale_mode == PKV_SCALE_FIRST_WRITE, stream);
+                             src_dtype, cache_dtype, scale_mode, stream);
 }
 
 int pkv_copy_blocks(void* k_cache, void* v_cache, float* k_scales, float* v_scales,

@@ -110,8 +110,11 @@ struct Cfg {
   // block per step would leave half the bytes in flight of a 16-bit step.
   static constexpr int BPS = (EB == 1 && G == 8) ? 2 : 1;
   static constexpr int KRING_B = NW * KR * BPS * TILE_B;
+  // per-token scales of a ring tile's block: 16 K scales, then 16 V scales
+  static constexpr int TOKS_B = 128;
+  static constexpr int TOKRING_B = NW * KR * BPS * TOKS_B;
   static constexpr int RED_B = NW * G * (D + 2) * 4;       // end-of-partition combine
-  static constexpr int SMEM_B = KRING_B > RED_B ? KRING_B : RED_B;
+  static constexpr int SMEM_B = KRING_B + TOKRING_B > RED_B ? KRING_B + TOKRING_B : RED_B;
   static_assert(LPB * 64 * LW == TILE_B, "a tile is LPB wave-wide loads");
   static_assert(LW == 16 || NWT == 2, "8-byte loads: one per token");
   static_assert(LPT >= 1 && LPT <= 16 && (LPT & (LPT - 1)) == 0, "lanes per token");
@@ -497,19 +500,20 @@ __device__ __forceinline__ int64_t tile_offset(const DecodeArgs& a, int h, int p
   return ((int64_t)phys * a.num_kv_heads + h) * (int64_t)tile_bytes;
 }
 
-// The block's K and V scales (8-bit caches; 1 otherwise).  Uniform index,
-// read-only data: scalar loads, which do not wait behind the tile copies in
-// flight (those count on vmcnt).
-template <bool KQ>
+// The block's K and V scales (8-bit caches with one scale per (block, head);
+// 1 otherwise, and with per-token scales, which are read per lane).
+// Uniform index, read-only data: scalar loads, which do not wait behind the
+// tile copies in flight (those count on vmcnt).
+template <bool KQ, bool VQ>
 __device__ __forceinline__ void block_scales(const DecodeArgs& a, int h, BlockRef& br) {
   br.ks = 1.f;
   br.vs = 1.f;
-  if constexpr (KQ) {
-    const int phys = ((unsigned)br.phys < (unsigned)a.num_blocks) ? br.phys : 0;
-    const int64_t si = (int64_t)phys * a.num_kv_heads + h;
-    br.ks = ((const __attribute__((address_space(4))) float*)a.k_scales)[si];
-    br.vs = ((const __attribute__((address_space(4))) float*)a.v_scales)[si];
-  }
+  const int phys = ((unsigned)br.phys < (unsigned)a.num_blocks) ? br.phys : 0;
+  const int64_t si = (int64_t)phys * a.num_kv_heads + h;
+  if constexpr (KQ)
+    if (!a.k_tok) br.ks = ((const __attribute__((address_space(4))) float*)a.k_scales)[si];
+  if constexpr (VQ)
+    if (!a.v_tok) br.vs = ((const __attribute__((address_space(4))) float*)a.v_scales)[si];
 }
 
 // End of a partition: every wave's (reference maximum, sum, accumulators)
@@ -539,11 +543,16 @@ __device__ __forceinline__ void combine_waves(const DecodeArgs& a, int b, int h,
 // smem is the workgroup's LDS (Cfg::SMEM_B bytes).
 template <KV KT, KV VT, KV QT, KV OT, int D, int G>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, int b, char* smem) {
-  static_assert(kv_bytes<KT>::value == kv_bytes<VT>::value, "K and V share the tile layout");
-  static_assert(is_quantised<KT>() == is_quantised<VT>(), "8-bit K goes with 8-bit V");
-  constexpr bool KQ = is_quantised<KT>();
+  static_assert(kv_bytes<VT>::value <= kv_bytes<KT>::value, "V is no wider than K");
+  static_assert(is_quantised<VT>() || !is_quantised<KT>(), "an 8-bit K goes with an 8-bit V");
+  constexpr bool KQ = is_quantised<KT>(), VQ = is_quantised<VT>();
   using C = Cfg<KT, D, G>;
   constexpr int E = C::E, VPT = C::VPT, LPT = C::LPT, R = C::R, TPL = C::TPL, NWT = C::NWT, LW = C::LW;
+  // V tiles use K's lane layout (same tokens and channels per lane); a
+  // narrower V (16-bit K with 8-bit V) is loaded in proportionally smaller
+  // pieces: VEB bytes per element, NWTV words per token per lane.
+  constexpr int VEB = kv_bytes<VT>::value, VLW = LW * VEB / C::EB, NWTV = NWT * VEB / C::EB;
+  static_assert(VLW == 16 || VLW == 8, "V loads of 16 or 8 bytes");
   constexpr int NS = C::NS, NRS = C::NRS, NF = C::NF, EL = C::EL, NW = C::NW;
   constexpr int LEVELS = C::LEVELS;
   // P.V as f16 dot2 over pairs of tokens (probabilities rounded to f16)
@@ -570,14 +579,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
 
   // the step's append (append_new_rows): by the partition holding the new
   // token's block, and in it by the wave that reads that block
-  const bool appends = !KQ && a.new_slots != nullptr && p == (parts.n > 0 ? parts.n - 1 : 0);
+  const bool appends = !KQ && !VQ && a.new_slots != nullptr && p == (parts.n > 0 ? parts.n - 1 : 0);
   constexpr int BPS = C::BPS;
   const int append_wave = j1 > j0 ? ((j1 - 1 - j0) / BPS) % NW : 0;
   auto append_rows = [&]() __attribute__((always_inline)) {
-    if constexpr (!KQ) append_new_rows<D, C::EB>(a, b, h, lane);
+    if constexpr (!KQ && !VQ) append_new_rows<D, C::EB>(a, b, h, lane);
   };
   if (j0 >= j1) {
-    finish_empty<OT, D, G, C::EB>(a, b, h, p, tid, appends && w == 0);
+    finish_empty<OT, D, G, (KQ || VQ) ? 1 : C::EB>(a, b, h, p, tid, appends && w == 0);
     return;
   }
 
@@ -684,18 +693,44 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
   // latency sits between a step's wait and its next tile loads.
   auto entry_of = [&](int j) __attribute__((always_inline)) { return table[span.logical(j)]; };
   auto tile_of = [&](int phys_raw) __attribute__((always_inline)) { return tile_offset(a, h, phys_raw, TILE_B); };
-  auto scales_of = [&](BlockRef& br) __attribute__((always_inline)) { block_scales<KQ>(a, h, br); };
+  auto vtile_of = [&](int phys_raw) __attribute__((always_inline)) {
+    return tile_offset(a, h, phys_raw, 16 * D * VEB);
+  };
+  auto scales_of = [&](BlockRef& br) __attribute__((always_inline)) { block_scales<KQ, VQ>(a, h, br); };
+  // Per-token scales ("KV Cache from first principles" 5.2): the 16 K and
+  // 16 V scales of a block's slots are copied by LDS DMA (four lanes of 16
+  // bytes each) into the ring tile's scale area, waited for with its K
+  // tile; a lane reads those of its own token rows.
+  const char* toks_area = smem + C::KRING_B + w * KR * BPS * C::TOKS_B;
+  auto issue_tok = [&](int phys_raw, int sk) __attribute__((always_inline)) {
+    if constexpr (KQ || VQ) {
+      const int64_t si = tile_offset(a, h, phys_raw, 16);   // (block, head) * 16 scales
+      const uint32_t dst = lds_offset(toks_area) + (uint32_t)(sk * C::TOKS_B);
+      if (KQ && a.k_tok && lane < 4) lds_dma16(a.k_scales + si, (uint32_t)(lane * 16), dst);
+      if (VQ && a.v_tok && lane < 4) lds_dma16(a.v_scales + si, (uint32_t)(lane * 16), dst + 64);
+    }
+  };
   // vr is consumed: tokens outside the sequence (or window) are zeroed in it.
-  auto compute_block = [&](int j, const BlockRef& br, const TokWords<NWT> (&kr)[TPL],
-                           TokWords<NWT> (&vr)[TPL]) __attribute__((always_inline)) {
+  auto compute_block = [&](int j, int sk, const BlockRef& br, const TokWords<NWT> (&kr)[TPL],
+                           TokWords<NWTV> (&vr)[TPL]) __attribute__((always_inline)) {
     const int jl = span.logical(j);
     const bool blk_ok = (unsigned)br.phys < (unsigned)a.num_blocks;
     const uint32_t vbits = blk_ok ? span.valid_bits(jl) : 0u;
     float cs = a.scale;  // scale * log2(e), folded on the host
     float vsc = 1.f;
-    if constexpr (KQ) {
-      cs *= br.ks;
-      vsc = br.vs;
+    if constexpr (KQ) cs *= br.ks;   // br.ks, br.vs: 1 with per-token scales
+    if constexpr (VQ) vsc = br.vs;
+    // per-token scales of the lane's token rows (i ^ tmask) * R + r (1 otherwise)
+    float kt[TPL], vt[TPL];
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+      kt[i] = 1.f;
+      vt[i] = 1.f;
+      if constexpr (KQ || VQ) {
+        const float* ts = (const float*)(toks_area + sk * C::TOKS_B) + ((i ^ tmask) * R + r);
+        if (KQ && a.k_tok) kt[i] = ts[0];
+        if (VQ && a.v_tok) vt[i] = ts[16];
+      }
     }
 
     // 1. partial scores: slot k = hs * TPL + i
@@ -723,10 +758,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
     });
     if constexpr (KQ) cs *= qfac;
 #pragma unroll
-    for (int k = 0; k < NF; ++k) s[k] *= cs;
+    for (int k = 0; k < NF; ++k) s[k] *= cs * kt[k % TPL];
 
     // 3. mask the tail (and a block id outside the pool)
-    TokWords<NWT> (&vv)[TPL] = vr;
+    TokWords<NWTV> (&vv)[TPL] = vr;
     if (vbits != 0xFFFFu) {
 #pragma unroll
       for (int k = 0; k < NF; ++k) {
@@ -737,7 +772,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
       for (int i = 0; i < TPL; ++i) {
         if (!((vbits >> ((i ^ tmask) * R + r)) & 1u)) {
 #pragma unroll
-          for (int k = 0; k < NWT; ++k) vv[i].w[k] = 0u;
+          for (int k = 0; k < NWTV; ++k) vv[i].w[k] = 0u;
         }
       }
     }
@@ -779,7 +814,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
       const float m = mref[k / TPL];
       const float pk = __builtin_amdgcn_exp2f(s[k] - (m == -INFINITY ? 0.f : m));
       lpart[k] += pk;
-      pf[k] = pk * vsc;
+      pf[k] = pk * vsc * vt[k % TPL];
     }
     static_for<NRS>([&](auto l) {
       constexpr int lv = NRS - 1 - decltype(l)::value;
@@ -793,7 +828,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
 #pragma unroll
       for (int m2 = 0; m2 < TPL / 2; ++m2) {
         uint32_t vp[EL];
-        v_token_pairs<VT, EL, NWT>(vv[2 * m2], vv[2 * m2 + 1], vp);
+        v_token_pairs<VT, EL, NWTV>(vv[2 * m2], vv[2 * m2 + 1], vp);
 #pragma unroll
         for (int hs = 0; hs < G; ++hs) {
           const half2_t pp = __builtin_bit_cast(
@@ -807,7 +842,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
 #pragma unroll
       for (int i = 0; i < TPL; ++i) {
         float vf[EL];
-        to_f32<VT, EL, NWT>(vv[i], vf);
+        to_f32<VT, EL, NWTV>(vv[i], vf);
 #pragma unroll
         for (int hs = 0; hs < G; ++hs) {
           const float pw = pf[hs * TPL + i];
@@ -836,21 +871,21 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
   for (int i = 0; i < TPL; ++i)
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
-      roff[i][v] = (uint32_t)((((i ^ tmask) * R + r) * D + (v * LPT + c) * E) * C::EB);
+      roff[i][v] = (uint32_t)((((i ^ tmask) * R + r) * D + (v * LPT + c) * E) * VEB);
   // Ordinary loads: non-temporal V loads measured no faster on a uniform
   // batch and about 40% slower on a batch of uneven lengths.
-  auto issue_vregs = [&](int phys_raw, TokWords<NWT> (&vr)[TPL]) __attribute__((always_inline)) {
-    const char* src = vbase + tile_of(phys_raw);
+  auto issue_vregs = [&](int phys_raw, TokWords<NWTV> (&vr)[TPL]) __attribute__((always_inline)) {
+    const char* src = vbase + vtile_of(phys_raw);
 #pragma unroll
     for (int i = 0; i < TPL; ++i)
 #pragma unroll
       for (int v = 0; v < VPT; ++v) {
-        if constexpr (LW == 16) {
+        if constexpr (VLW == 16) {
           const uint4 x = *(const uint4*)(src + roff[i][v]);
           vr[i].w[4 * v + 0] = x.x; vr[i].w[4 * v + 1] = x.y; vr[i].w[4 * v + 2] = x.z; vr[i].w[4 * v + 3] = x.w;
         } else {
           const uint2 x = *(const uint2*)(src + roff[i][v]);
-          vr[i].w[0] = x.x; vr[i].w[1] = x.y;
+          vr[i].w[2 * v + 0] = x.x; vr[i].w[2 * v + 1] = x.y;
         }
       }
   };
@@ -911,7 +946,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
       if constexpr (BPS == 1) return entry_of(j);   // every step's block is in range
       else return j < j1 ? entry_of(j) : -1;
     };
-    TokWords<NWT> va[BPS][TPL], vb[BPS][TPL];
+    TokWords<NWTV> va[BPS][TPL], vb[BPS][TPL];
     constexpr unsigned kWaitVm0 = 0x0F70;     // vmcnt(0), expcnt(7), lgkmcnt(15)
     static_assert(KR == 2, "one step in flight: K(t+1) and V(t+1) while t is computed");
     if (appends && w == append_wave) {
@@ -931,6 +966,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
         bcur[b2].phys = entry_at(0, b2);
         issue_vregs(bcur[b2].phys, va[b2]);
         issue_k2(bcur[b2].phys, b2);
+        issue_tok(bcur[b2].phys, b2);
         scales_of(bcur[b2]);
       }
       if (n_my > 1)
@@ -945,7 +981,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
     // Step t: K(t) and V(t) are the newest loads in flight, so wait for all,
     // then issue step t + 1 at once: its K slot and V registers held step
     // t - 1, already consumed, so nothing of step t has to be read first.
-    auto step = [&](int t, TokWords<NWT> (&vcur)[BPS][TPL], TokWords<NWT> (&vnext)[BPS][TPL])
+    auto step = [&](int t, TokWords<NWTV> (&vcur)[BPS][TPL], TokWords<NWTV> (&vnext)[BPS][TPL])
                     __attribute__((always_inline)) {
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       wait_vmcnt<0>();                      // (asm, memory clobber) the LDS reads stay below
@@ -958,6 +994,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
         for (int b2 = 0; b2 < BPS; ++b2) {
           issue_vregs(bnext[b2].phys, vnext[b2]);
           issue_k2(bnext[b2].phys, ((t + 1) & 1) * BPS + b2);
+          issue_tok(bnext[b2].phys, ((t + 1) & 1) * BPS + b2);
         }
       }
       TokWords<NWT> kr[TPL];
@@ -972,13 +1009,13 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
         }
       }
       __builtin_amdgcn_sched_barrier(0);    // the loads stay ahead of the compute
-      compute_block(blk(t, 0), b0[0], kr, vcur[0]);
+      compute_block(blk(t, 0), (t & 1) * BPS, b0[0], kr, vcur[0]);
       // further blocks of the step: K read from the ring just before use,
       // so one block's K is held at a time
 #pragma unroll
       for (int b2 = 1; b2 < BPS; ++b2) {
         read_k((t & 1) * BPS + b2, kr);
-        compute_block(blk(t, b2), b0[b2], kr, vcur[b2]);
+        compute_block(blk(t, b2), (t & 1) * BPS + b2, b0[b2], kr, vcur[b2]);
       }
     };
     int t = 0;
@@ -1371,6 +1408,15 @@ static int dispatch_d(const DecodeArgs& a, hipStream_t s) {
 
 int launch_decode(const DecodeArgs& a, hipStream_t s) {
   const KV kt = (KV)a.kv_dtype, vt = (KV)a.v_dtype, qt = (KV)a.q_dtype, ot = (KV)a.out_dtype;
+  if ((kt == KV::F16 || kt == KV::BF16) && (vt == KV::FP8 || vt == KV::INT8)) {
+    // 16-bit K with an 8-bit V: q and out of K's type
+    if (qt != kt || ot != kt) return PKV_ERR_DTYPE;
+    if (kt == KV::F16)
+      return vt == KV::FP8 ? dispatch_d<KV::F16, KV::FP8, KV::F16, KV::F16>(a, s)
+                           : dispatch_d<KV::F16, KV::INT8, KV::F16, KV::F16>(a, s);
+    return vt == KV::FP8 ? dispatch_d<KV::BF16, KV::FP8, KV::BF16, KV::BF16>(a, s)
+                         : dispatch_d<KV::BF16, KV::INT8, KV::BF16, KV::BF16>(a, s);
+  }
   if (kt == KV::F32 || kt == KV::F16 || kt == KV::BF16) {
     if (vt != kt || qt != kt || ot != kt) return PKV_ERR_DTYPE;
     switch (kt) {

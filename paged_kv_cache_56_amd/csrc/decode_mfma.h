@@ -61,10 +61,11 @@ struct UseMfma {
   static constexpr bool value = D == 128 && (G == 4 || G == 8) && KT != KV::F32;
 };
 
-template <KV KT>
+// Tile geometry of one cache (K's or V's: a 16-bit K may go with an 8-bit V).
+template <KV T>
 struct MCfg {
   static constexpr int D = 128;
-  static constexpr int EB = kv_bytes<KT>::value;
+  static constexpr int EB = kv_bytes<T>::value;
   static constexpr int ROW_B = D * EB;            // one token row of a tile
   static constexpr int TILE_B = 16 * ROW_B;       // one (block, KV head) tile
   static constexpr int NDMA = TILE_B / 1024;      // 1 KiB LDS DMA copies per tile
@@ -73,10 +74,13 @@ struct MCfg {
   static constexpr int NW = 4;                    // waves per workgroup
   static constexpr int KR = 2;                    // K ring slots per wave
   static constexpr int KRING_B = NW * KR * TILE_B;
+  // per-token scales of a ring slot's block: 16 K scales, then 16 V scales
+  static constexpr int TOKS_B = 128;
+  static constexpr int TOKRING_B = NW * KR * TOKS_B;
   template <int G>
   static constexpr int smem_bytes() {
     constexpr int red = NW * G * (D + 2) * 4;     // end-of-partition combine
-    return KRING_B > red ? KRING_B : red;
+    return KRING_B + TOKRING_B > red ? KRING_B + TOKRING_B : red;
   }
 };
 
@@ -163,13 +167,14 @@ __device__ __forceinline__ void k_operands(const u32x4_t (&kr)[KREADS], u32x4_t 
 // MCfg<KT>::smem_bytes<G>() bytes.
 template <KV KT, KV VT, KV QT, KV OT, int G>
 __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int h, int b, char* smem) {
-  static_assert(kv_bytes<KT>::value == kv_bytes<VT>::value, "K and V share the tile layout");
-  static_assert(is_quantised<KT>() == is_quantised<VT>(), "8-bit K goes with 8-bit V");
+  static_assert(kv_bytes<VT>::value <= kv_bytes<KT>::value, "V is no wider than K");
+  static_assert(is_quantised<VT>() || !is_quantised<KT>(), "an 8-bit K goes with an 8-bit V");
   static_assert(G == 4 || G == 8, "4 or 8 query heads per KV head");
   constexpr int D = 128;
-  using C = MCfg<KT>;
-  constexpr bool KQ = is_quantised<KT>();
-  constexpr int EB = C::EB, TILE_B = C::TILE_B, NDMA = C::NDMA, KREADS = C::KREADS, VW = C::VW;
+  using C = MCfg<KT>;     // K tiles
+  using CV = MCfg<VT>;    // V tiles
+  constexpr bool KQ = is_quantised<KT>(), VQ = is_quantised<VT>();
+  constexpr int EB = C::EB, TILE_B = C::TILE_B, NDMA = C::NDMA, KREADS = C::KREADS, VW = CV::VW;
   constexpr int NW = C::NW, KR = C::KR;
   constexpr KV MK = KQ ? KV::F16 : KT;                    // S^T operands
   constexpr KV MV = VT == KV::BF16 ? KV::BF16 : KV::F16;  // O^T operands
@@ -192,13 +197,13 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
 
   // the step's append (append_new_rows): by the partition holding the new
   // token's block, and in it by the wave that reads that block
-  const bool appends = !KQ && a.new_slots != nullptr && p == (parts.n > 0 ? parts.n - 1 : 0);
+  const bool appends = !KQ && !VQ && a.new_slots != nullptr && p == (parts.n > 0 ? parts.n - 1 : 0);
   const int append_wave = j1 > j0 ? (j1 - 1 - j0) % NW : 0;
   auto append_rows = [&]() __attribute__((always_inline)) {
-    if constexpr (!KQ) append_new_rows<D, EB>(a, b, h, lane);
+    if constexpr (!KQ && !VQ) append_new_rows<D, EB>(a, b, h, lane);
   };
   if (j0 >= j1) {
-    finish_empty<OT, D, G, EB>(a, b, h, p, tid, appends && w == 0);
+    finish_empty<OT, D, G, (KQ || VQ) ? 1 : EB>(a, b, h, p, tid, appends && w == 0);
     return;
   }
 
@@ -286,13 +291,29 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
   // instruction reads four whole rows 1 KiB apart.
   uint32_t voff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)((lg * 4 + i) * C::ROW_B + lq * 8 * EB);
+  for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)((lg * 4 + i) * CV::ROW_B + lq * 8 * CV::EB);
 
   auto entry_of = [&](int j) __attribute__((always_inline)) { return table[span.logical(j)]; };
   auto tile_of = [&](int phys_raw) __attribute__((always_inline)) { return tile_offset(a, h, phys_raw, TILE_B); };
-  auto scales_of = [&](BlockRef& br) __attribute__((always_inline)) { block_scales<KQ>(a, h, br); };
+  auto vtile_of = [&](int phys_raw) __attribute__((always_inline)) {
+    return tile_offset(a, h, phys_raw, CV::TILE_B);
+  };
+  auto scales_of = [&](BlockRef& br) __attribute__((always_inline)) { block_scales<KQ, VQ>(a, h, br); };
+  // Per-token scales ("KV Cache from first principles" 5.2): the 16 K and
+  // 16 V scales of a block's slots are copied by LDS DMA (four lanes of 16
+  // bytes each) into the ring slot's scale area next to its K tile, and
+  // waited for with it; a lane then reads the four of its tokens.
+  const uint32_t toks0 = lds_offset(smem) + (uint32_t)(C::KRING_B + w * KR * C::TOKS_B);
+  auto issue_tok = [&](int phys_raw, int sk) __attribute__((always_inline)) {
+    if constexpr (KQ || VQ) {
+      const int64_t si = tile_offset(a, h, phys_raw, 16);   // (block, head) * 16 scales
+      const uint32_t dst = toks0 + (uint32_t)(sk * C::TOKS_B);
+      if (KQ && a.k_tok && lane < 4) lds_dma16(a.k_scales + si, (uint32_t)(lane * 16), dst);
+      if (VQ && a.v_tok && lane < 4) lds_dma16(a.v_scales + si, (uint32_t)(lane * 16), dst + 64);
+    }
+  };
   auto issue_v = [&](int phys_raw, VRows<VW>& vr) __attribute__((always_inline)) {
-    const char* src = vbase + tile_of(phys_raw);
+    const char* src = vbase + vtile_of(phys_raw);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if constexpr (VW == 4) {
@@ -319,16 +340,21 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
   };
 
   // One tile: scores, online softmax, P.V.  vr is consumed (masked rows zeroed).
-  auto compute_block = [&](int j, const BlockRef& br, const u32x4_t (&kr)[KREADS], VRows<VW>& vr)
+  auto compute_block = [&](int j, int sk, const BlockRef& br, const u32x4_t (&kr)[KREADS], VRows<VW>& vr)
                            __attribute__((always_inline)) {
     const int jl = span.logical(j);
     const bool blk_ok = (unsigned)br.phys < (unsigned)a.num_blocks;
     const uint32_t vbits = blk_ok ? span.valid_bits(jl) : 0u;
     float cs = a.scale;  // scale * log2(e), folded on the host
     float vsc = 1.f;
-    if constexpr (KQ) {
-      cs *= br.ks * qfac;
-      vsc = br.vs;
+    if constexpr (KQ) cs *= br.ks * qfac;   // br.ks, br.vs: 1 with per-token scales
+    if constexpr (VQ) vsc = br.vs;
+    // per-token scales of the lane's tokens 4 lg .. + 3 (1 otherwise)
+    f32x4_t kt = {1.f, 1.f, 1.f, 1.f}, vt = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (KQ || VQ) {
+      const char* ts = smem + C::KRING_B + (w * KR + sk) * C::TOKS_B + lg * 16;
+      if (KQ && a.k_tok) kt = *(const f32x4_t*)ts;
+      if (VQ && a.v_tok) vt = *(const f32x4_t*)(ts + 64);
     }
     u32x4_t kop[4];
     k_operands<KT, KREADS>(kr, kop);
@@ -340,7 +366,7 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
     const uint32_t mine = hv ? (vbits >> (lg * 4)) & 0xFu : 0u;
     float sc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = ((mine >> i) & 1u) ? s[i] * cs : -INFINITY;
+    for (int i = 0; i < 4; ++i) sc[i] = ((mine >> i) & 1u) ? s[i] * cs * kt[i] : -INFINITY;
     if (vbits != 0xFFFFu) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -371,7 +397,7 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
     for (int i = 0; i < 4; ++i) {
       const float pe = __builtin_amdgcn_exp2f(sc[i] - mo);
       lsum += pe;
-      pv[i] = pe * vsc;
+      pv[i] = pe * vsc * vt[i];
     }
     const u32x4_t pop = p_operand<MV>(pv);
     u32x4_t vop[8];
@@ -397,6 +423,7 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
       bcur.phys = entry_of(blk(0));
       issue_v(bcur.phys, va);
       issue_k(bcur.phys, 0);
+      issue_tok(bcur.phys, 0);
       scales_of(bcur);
       if (n_my > 1) bnext.phys = entry_of(blk(1));
     }
@@ -410,6 +437,7 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
       if (more) {
         issue_v(bnext.phys, vnext);
         issue_k(bnext.phys, (t + 1) & 1);
+        issue_tok(bnext.phys, (t + 1) & 1);
       }
       u32x4_t kr[KREADS];
       read_k(t & 1, kr);
@@ -419,7 +447,7 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
         if (t + 2 < n_my) bnext.phys = entry_of(blk(t + 2));
       }
       __builtin_amdgcn_sched_barrier(0);
-      compute_block(blk(t), b0, kr, vcur);
+      compute_block(blk(t), t & 1, b0, kr, vcur);
     };
     int t = 0;
     for (; t + 1 < n_my; t += 2) {

@@ -42,11 +42,14 @@ __global__ void __launch_bounds__(256) kv_append_kernel(
 // with one scale per head, K in FP8 with V in INT8 as the mixed form; "Why
 // does KV Cache eat GPU memory?": FP8 KV needs calibrated scales; "KV Cache
 // from first principles" 5.2: per-channel factors for K's outlier channels).
-// Scales are per (block, KV head).  With channel factors the source is first
-// divided by its channel's factor.  In first-write mode the token that opens
-// a block (offset 0) sets that block's scale to max|y| / QMAX of its own row;
-// the pass that does so runs before the one that quantises, so tokens of one
-// call that land later in the same block already see it.  Codes are the
+// Scales are per (block, KV head), or per (slot, KV head) ("KV Cache from
+// first principles" 5.2: per-token granularity).  With channel factors the
+// source is first divided by its channel's factor.  In first-write mode the
+// token that opens a block (offset 0) sets that block's scale to
+// max|y| / QMAX of its own row; in per-token mode every token sets its own
+// slot's scale that way.  The pass that sets scales runs before the one
+// that quantises, so tokens of one call that land later in the same block
+// already see it.  Codes are the
 // nearest code (ties to even) of clamp(y / scale, +-QMAX), every quotient a
 // correctly rounded fp32 division: for fp8 the hardware's round-to-nearest-
 // even e4m3 (OCP) convert, for int8 rint (NaN gives 0).
@@ -78,20 +81,26 @@ __device__ __forceinline__ float scaled_src(const QTarget& q, int64_t row, int h
   return q.chan ? x / q.chan[(int64_t)h * head_dim + d] : x;
 }
 
+// Index of the scale a token uses: per (block, head), or per (slot, head).
+__device__ __forceinline__ int64_t scale_index(int64_t slot, int h, int num_kv_heads, int per_token) {
+  const int64_t bh = (slot / PKV_BLOCK_SIZE) * num_kv_heads + h;
+  return per_token ? bh * PKV_BLOCK_SIZE + slot % PKV_BLOCK_SIZE : bh;
+}
+
 template <KV ST, KV CT>
 __global__ void __launch_bounds__(256) q8_first_write_scale_kernel(
     QTargets tg, const int64_t* __restrict__ slot_mapping, int num_tokens, int num_kv_heads,
-    int head_dim, int64_t num_slots) {
+    int head_dim, int64_t num_slots, int per_token) {
   const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // t * Hkv + h
   if (row >= (int64_t)num_tokens * num_kv_heads) return;
   const QTarget q = blockIdx.y ? tg.t[1] : tg.t[0];   // uniform: no indexed copy
   const int64_t t = row / num_kv_heads;
   const int h = (int)(row % num_kv_heads);
   const int64_t slot = slot_mapping[t];
-  if (slot < 0 || slot >= num_slots || slot % PKV_BLOCK_SIZE != 0) return;
+  if (slot < 0 || slot >= num_slots || (!per_token && slot % PKV_BLOCK_SIZE != 0)) return;
   float amax = 0.f;
   for (int d = 0; d < head_dim; ++d) amax = fmaxf(amax, fabsf(scaled_src<ST>(q, row, h, d, head_dim)));
-  q.scales[(slot / PKV_BLOCK_SIZE) * num_kv_heads + h] = amax > 0.f ? amax / qmax<CT>() : 1.0f;
+  q.scales[scale_index(slot, h, num_kv_heads, per_token)] = amax > 0.f ? amax / qmax<CT>() : 1.0f;
 }
 
 // Four clamped quotients -> four codes in one word (element 0 in the low byte).
@@ -114,7 +123,7 @@ __device__ __forceinline__ uint32_t encode4(const float (&v)[4]) {
 template <KV ST, KV CT>
 __global__ void __launch_bounds__(256) q8_quantize_append_kernel(
     QTargets tg, const int64_t* __restrict__ slot_mapping, int num_tokens, int num_kv_heads,
-    int head_dim, int64_t num_slots) {
+    int head_dim, int64_t num_slots, int per_token) {
   const int groups = head_dim / 16;                         // 16 elements per thread
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)num_tokens * num_kv_heads * groups) return;
@@ -126,7 +135,7 @@ __global__ void __launch_bounds__(256) q8_quantize_append_kernel(
   const int64_t slot = slot_mapping[t];
   if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot / PKV_BLOCK_SIZE, off = slot % PKV_BLOCK_SIZE;
-  const float scale = q.scales[blk * num_kv_heads + h];
+  const float scale = q.scales[scale_index(slot, h, num_kv_heads, per_token)];
   constexpr float QM = qmax<CT>();
   uint32_t packed[4];
 #pragma unroll
@@ -145,7 +154,9 @@ __global__ void __launch_bounds__(256) q8_quantize_append_kernel(
 
 int launch_kv_append_q8(const QTargetArgs* targets, int num_targets, const int64_t* slot_mapping,
                         int num_tokens, int num_kv_heads, int head_dim, int num_blocks,
-                        int src_dtype, int code_dtype, bool first_write, hipStream_t stream) {
+                        int src_dtype, int code_dtype, int scale_mode, hipStream_t stream) {
+  const bool first_write = scale_mode == PKV_SCALE_FIRST_WRITE;
+  const int per_token = scale_mode == PKV_SCALE_PER_TOKEN ? 1 : 0;
   const int64_t rows = (int64_t)num_tokens * num_kv_heads;
   if (rows == 0) return PKV_OK;
   const int64_t slots = (int64_t)num_blocks * PKV_BLOCK_SIZE;
@@ -158,11 +169,11 @@ int launch_kv_append_q8(const QTargetArgs* targets, int num_targets, const int64
   const dim3 g2((unsigned)((threads + 255) / 256), num_targets);
 #define PKV_Q8_APPEND(ST, CT)                                                                     \
   do {                                                                                            \
-    if (first_write)                                                                              \
+    if (first_write || per_token)                                                                 \
       hipLaunchKernelGGL((q8_first_write_scale_kernel<ST, CT>), g1, dim3(256), 0, stream, tg,     \
-                         slot_mapping, num_tokens, num_kv_heads, head_dim, slots);                \
+                         slot_mapping, num_tokens, num_kv_heads, head_dim, slots, per_token);     \
     hipLaunchKernelGGL((q8_quantize_append_kernel<ST, CT>), g2, dim3(256), 0, stream, tg,        \
-                       slot_mapping, num_tokens, num_kv_heads, head_dim, slots);                  \
+                       slot_mapping, num_tokens, num_kv_heads, head_dim, slots, per_token);       \
   } while (0)
 #define PKV_Q8_SRC(CT)                                       \
   switch ((KV)src_dtype) {                                   \
@@ -192,7 +203,8 @@ int launch_kv_append(const void* k_new, const void* v_new, const int64_t* slot_m
   const int threads = 256;
   const int64_t blocks = (per_tensor + threads - 1) / threads;
   if (blocks > 0x7FFFFFFF) return PKV_ERR_SHAPE;
-  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)blocks, 2), dim3(threads), 0, stream,
+  const unsigned tensors = v_cache ? 2 : 1;   // K and V, or K alone
+  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)blocks, tensors), dim3(threads), 0, stream,
                      (const uint4*)k_new, (const uint4*)v_new, slot_mapping, (uint4*)k_cache,
                      (uint4*)v_cache, num_tokens, num_kv_heads, chunks,
                      (int64_t)num_blocks * PKV_BLOCK_SIZE);

@@ -19,10 +19,11 @@ struct QTargetArgs {
   const float* chan;
 };
 
-// 8-bit append into one or two caches of the same code set (grid.y picks).
+// 8-bit append into one or two caches of the same code set (grid.y picks);
+// scale_mode is a pkv_scale_mode.
 int launch_kv_append_q8(const QTargetArgs* targets, int num_targets, const int64_t* slot_mapping,
                         int num_tokens, int num_kv_heads, int head_dim, int num_blocks,
-                        int src_dtype, int code_dtype, bool first_write, hipStream_t stream);
+                        int src_dtype, int code_dtype, int scale_mode, hipStream_t stream);
 
 int launch_copy_blocks(void* k_cache, void* v_cache, float* k_scales, float* v_scales,
                        const int32_t* src, const int32_t* dst, int n, int num_kv_heads,
@@ -32,8 +33,9 @@ struct DecodeArgs {
   const void* q;
   const void* k_cache;
   const void* v_cache;
-  const float* k_scales;   // 8-bit caches only: [num_blocks][num_kv_heads]
-  const float* v_scales;   // 8-bit caches only
+  const float* k_scales;   // 8-bit K only: [num_blocks][num_kv_heads] (x 16 per token)
+  const float* v_scales;   // 8-bit V only: likewise
+  int k_tok, v_tok;        // 1: the scales are per (slot, head): [num_blocks][num_kv_heads][16]
   const float* k_chan;     // 8-bit K only, may be NULL: [num_kv_heads][head_dim]
   const int32_t* block_tables;
   const int32_t* context_lens;

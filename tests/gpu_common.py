@@ -53,7 +53,9 @@ def run_step(x, layer: int, spec, out: torch.Tensor, partition_blocks: int = 0,
     kw = {}
     chan = x.get("k_channel_scales")
     if spec.quantised:
-        kw = dict(k_scales=x["k_scales"][layer], v_scales=x["v_scales"][layer])
+        kw = dict(v_scales=x["v_scales"][layer])
+        if spec.k_quantised:
+            kw["k_scales"] = x["k_scales"][layer]
         if chan is not None:
             kw["k_channel_scales"] = chan
     if spec.fp_sinks:
@@ -64,12 +66,16 @@ def run_step(x, layer: int, spec, out: torch.Tensor, partition_blocks: int = 0,
             pkv.kv_append(x["k_new"][layer], x["v_new"][layer], x["sink_slot_mapping"],
                           x["sink_k"][layer], x["sink_v"][layer])
     if spec.append and append:
-        if spec.kv_dtype == spec.v_tag == "fp8_e4m3" and chan is None:
+        if (spec.kv_dtype == spec.v_tag == "fp8_e4m3" and chan is None
+                and not (spec.k_scale_tok or spec.v_scale_tok)):
             pkv.kv_append_fp8(x["k_new"][layer], x["v_new"][layer], x["slot_mapping"], kc, vc,
                               kw["k_scales"], kw["v_scales"])
         elif spec.quantised:
-            pkv.kv_append_quant(x["k_new"][layer], x["slot_mapping"], kc, kw["k_scales"],
-                                channel_scales=chan)
+            if spec.k_quantised:
+                pkv.kv_append_quant(x["k_new"][layer], x["slot_mapping"], kc, kw["k_scales"],
+                                    channel_scales=chan)
+            else:                                   # a 16-bit K: a bit copy of K alone
+                pkv.kv_append(x["k_new"][layer], None, x["slot_mapping"], kc, None)
             pkv.kv_append_quant(x["v_new"][layer], x["slot_mapping"], vc, kw["v_scales"])
         else:
             pkv.kv_append(x["k_new"][layer], x["v_new"][layer], x["slot_mapping"], kc, vc)
@@ -115,13 +121,18 @@ def oracle_append(h, spec, slot_mapping):
     ks, vs = h.get("k_scales"), h.get("v_scales")
     if spec.append:
         if spec.quantised:
-            kn = oracle.stored_to_f64(h["k_new"], spec.q_dtype).astype(np.float32)
+            gran = lambda tok: "token" if tok else "block"
+            if spec.k_quantised:
+                kn = oracle.stored_to_f64(h["k_new"], spec.q_dtype).astype(np.float32)
+                kc, ks = oracle.kv_append_quant(kc, ks, kn, slot_mapping, code=spec.kv_dtype,
+                                                first_write=False,
+                                                channel_scales=h.get("k_channel_scales"),
+                                                granularity=gran(spec.k_scale_tok))
+            else:
+                kc = oracle.kv_append_bits(kc, h["k_new"], slot_mapping)
             vn = oracle.stored_to_f64(h["v_new"], spec.q_dtype).astype(np.float32)
-            kc, ks = oracle.kv_append_quant(kc, ks, kn, slot_mapping, code=spec.kv_dtype,
-                                            first_write=False,
-                                            channel_scales=h.get("k_channel_scales"))
             vc, vs = oracle.kv_append_quant(vc, vs, vn, slot_mapping, code=spec.v_tag,
-                                            first_write=False)
+                                            first_write=False, granularity=gran(spec.v_scale_tok))
         else:
             kc = oracle.kv_append_bits(kc, h["k_new"], slot_mapping)
             vc = oracle.kv_append_bits(vc, h["v_new"], slot_mapping)

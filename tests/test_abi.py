@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
     lib = pkv.load_library()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pkv_version() == 160
+    assert lib.pkv_version() == 170
 
 
 def _dims(**kw):
@@ -208,7 +208,7 @@ def test_append_quant_status_codes():
     assert call(FAKE, FAKE, FAKE, FAKE, None, 4, 8, 128, 64, 16, 2, 1, 0) == -3    # f16 cache
     assert call(FAKE, FAKE, FAKE, FAKE, None, 4, 8, 128, 64, 16, 3, 4, 0) == -3    # fp8 source
     assert call(FAKE, FAKE, FAKE, FAKE, None, 4, 8, 120, 64, 16, 2, 4, 0) == -2    # D % 16
-    assert call(FAKE, FAKE, FAKE, FAKE, None, 4, 8, 128, 64, 16, 2, 4, 2) == -2    # scale mode
+    assert call(FAKE, FAKE, FAKE, FAKE, None, 4, 8, 128, 64, 16, 2, 4, 3) == -2    # scale mode
     assert call(FAKE, FAKE, FAKE, None, None, 4, 8, 128, 64, 16, 2, 4, 0) == -1    # no scales
     assert call(None, None, None, None, None, 0, 8, 128, 64, 16, 2, 4, 0) == 0     # nothing to do
 
@@ -309,3 +309,32 @@ def test_noalloc_rejects_calls_beyond_its_scratch():
     assert pkv.decode_workspace_bytes(big) > 32 * 2**20
     assert call(big) == -8
     assert lib.pkv_status_string(-8)
+
+
+def test_k16_v8_and_per_token_status_codes():
+    """A 16-bit K with an 8-bit V takes q and out of K's type, v_scales, and
+    no K scales or channel factors; per-token flags are 0 or 1 and apply to
+    an 8-bit K only.  All refused before any launch."""
+    lib = pkv.load_library()
+
+    def call(dims, v_dtype, ks=None, vs=FAKE, chan=None, k_tok=0, v_tok=0):
+        qp = pkv.QuantParams(ks and ks.value, vs and vs.value, chan and chan.value, v_dtype, None, None,
+                             None, 0, k_tok, v_tok)
+        return lib.pkv_paged_decode_attn_quant(FAKE, FAKE, FAKE, ctypes.byref(qp), FAKE, FAKE,
+                                               ctypes.c_float(0.088), FAKE, ctypes.byref(dims), None, 0,
+                                               None)
+
+    base = dict(num_q_heads=32, max_blocks_per_seq=16)
+    f16 = _dims(**base, q_dtype=1, kv_dtype=1, out_dtype=1)
+    bf16 = _dims(**base, q_dtype=2, kv_dtype=2, out_dtype=2)
+    assert call(f16, 3, vs=None) == -1                       # V scales missing
+    assert call(f16, 3, ks=FAKE) == -3                       # a 16-bit K takes no scales
+    assert call(f16, 4, chan=FAKE) == -3                     # nor channel factors
+    assert call(f16, 3, k_tok=1) == -3                       # nor per-token K scales
+    assert call(bf16, 1) == -3                               # V must be 8-bit
+    assert call(_dims(**base, q_dtype=2, kv_dtype=1, out_dtype=1), 3) == -3    # q of K's type
+    assert call(_dims(**base, q_dtype=1, kv_dtype=1, out_dtype=0), 3) == -3    # out of K's type
+    fp8 = _dims(**base, q_dtype=2, kv_dtype=3, out_dtype=2)
+    assert call(fp8, 3, ks=FAKE, v_tok=2) == -2              # flags are 0 or 1
+    assert call(fp8, 3, ks=FAKE, k_tok=-1) == -2
+    assert call(fp8, 3, ks=None) == -1                       # an 8-bit K needs its scales

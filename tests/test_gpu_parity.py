@@ -156,6 +156,53 @@ def test_kv_append_quant_bit_exact(code, src, first_write, chan):
     assert np.array_equal(ds.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
 
 
+@pytest.mark.parametrize("code", ["int8", "fp8_e4m3"])
+@pytest.mark.parametrize("src", ["f16", "bf16"])
+@pytest.mark.parametrize("chan", [False, True])
+def test_kv_append_quant_per_token_bit_exact(code, src, chan):
+    """One scale per (slot, head): every written token sets its own scales
+    from its row; codes and scales equal the oracle's bit for bit, and no
+    other slot's scale changes."""
+    say(f"[kv_append_quant per token] code={code} src={src} chan={chan}")
+    rng = np.random.default_rng(12)
+    NB, H, D, T = 10, 3, 128, 19
+    npdt = np.uint8 if code == "fp8_e4m3" else np.int8
+    codes = rng.integers(0, 0x7E, size=(NB, H, 16, D)).astype(npdt)
+    scales = rng.uniform(0.002, 0.05, size=(NB, H, 16)).astype(np.float32)
+    cs = None
+    if chan:
+        cs = rng.uniform(0.25, 20.0, size=(H, D)).astype(np.float32)
+    x = torch.from_numpy(rng.standard_normal((T, H, D)).astype(np.float32) * 2).to(TORCH_DT[src])
+    x[3] *= 40
+    x[5] = 0                                       # a zero row: scale 1
+    slots = np.array([0, 1, 2, 3, 4, 5, 16, 33, -1, 48, 49, 50, 51, 52, 53, 54, 55, 159,
+                      NB * 16 + 3], dtype=np.int64)
+    xf = oracle.stored_to_f64(host_storage(x), src).astype(np.float32)
+    ref_c, ref_s = oracle.kv_append_quant(codes, scales, xf, slots, code=code, first_write=False,
+                                          channel_scales=cs, granularity="token")
+    dc = torch.from_numpy(codes).to(DEV)
+    ds = torch.from_numpy(scales).to(DEV)
+    dcs = None if cs is None else torch.from_numpy(cs).to(DEV)
+    pkv.kv_append_quant(x.to(DEV), torch.from_numpy(slots).to(DEV), dc, ds, channel_scales=dcs)
+    torch.cuda.synchronize()
+    assert np.array_equal(dc.cpu().numpy(), ref_c)
+    assert np.array_equal(ds.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+
+
+def test_kv_append_k_alone():
+    """pkv_kv_append with no V: the K rows are bit-copied, nothing else moves."""
+    say("[kv_append] K alone")
+    rng = np.random.default_rng(13)
+    kc = torch.from_numpy(rng.standard_normal((6, 2, 16, 128)).astype(np.float32)).to(torch.bfloat16)
+    new = torch.from_numpy(rng.standard_normal((4, 2, 128)).astype(np.float32)).to(torch.bfloat16)
+    slots = np.array([3, 17, -1, 95], dtype=np.int64)
+    ref = oracle.kv_append_bits(host_storage(kc), host_storage(new), slots)
+    dk = kc.to(DEV)
+    pkv.kv_append(new.to(DEV), None, torch.from_numpy(slots).to(DEV), dk, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_storage(dk), ref)
+
+
 def test_int8_quantise_ties_saturation_and_nan():
     """Scale 1: every half-integer tie in range, both fp32 neighbours of it,
     +-127.5 and beyond, infinities and NaN."""
@@ -333,11 +380,12 @@ def test_kv_append_skips_out_of_pool_slots():
 # decode attention, oracle-sized cases
 # --------------------------------------------------------------------------
 
-def _ragged(name, kv, q, out, D, G, lens, seed, hkv=2, append=False, v=None, outliers=0, fp_sinks=0):
+def _ragged(name, kv, q, out, D, G, lens, seed, hkv=2, append=False, v=None, outliers=0, fp_sinks=0,
+            ktok=False, vtok=False):
     return DecodeWorkload(name=name, seed=seed, num_layers=1, num_seqs=len(lens), num_q_heads=hkv * G,
                           num_kv_heads=hkv, head_dim=D, kv_dtype=kv, q_dtype=q, out_dtype=out,
                           context_lens=tuple(lens), append=append, v_dtype=v, k_outliers=outliers,
-                          fp_sinks=fp_sinks)
+                          fp_sinks=fp_sinks, k_scale_tok=ktok, v_scale_tok=vtok)
 
 
 RAGGED = [1, 15, 16, 17, 31, 33, 100, 257, 0, 64, 511]
@@ -387,6 +435,29 @@ SMALL = {
                                                21, hkv=2, append=True),
     # one long sequence among short ones: the batch-size hint changes the split plan
     "one_long_many_short_f16": _ragged("r18", "f16", "f16", "f16", 128, 4, [8192] + [20, 3, 47, 16] * 4, 18),
+    # V alone quantised, K kept in 16 bits (matrix-core and vector passes)
+    "ragged_bf16k_fp8v_g4_d128": _ragged("r22", "bf16", "bf16", "bf16", 128, 4, RAGGED, 22, v="fp8_e4m3"),
+    "ragged_f16k_int8v_g8_d128_append": _ragged("r23", "f16", "f16", "f16", 128, 8, [1, 16, 17, 200, 33, 48, 49],
+                                                23, hkv=3, append=True, v="int8"),
+    "ragged_f16k_fp8v_g2_d64": _ragged("r24", "f16", "f16", "f16", 64, 2, RAGGED, 24, v="fp8_e4m3"),
+    "ragged_bf16k_int8v_g1_d128_vtok_append": _ragged("r25", "bf16", "bf16", "bf16", 128, 1,
+                                                      [2, 15, 16, 64, 65, 300], 25, append=True, v="int8",
+                                                      vtok=True),
+    "ragged_f16k_fp8v_g4_d128_vtok": _ragged("r26", "f16", "f16", "f16", 128, 4, RAGGED, 26, v="fp8_e4m3",
+                                             vtok=True),
+    "long_bf16k_fp8v_small": scaled(WORKLOADS["long_bf16k_fp8v"], num_seqs=2, len_range=(8192, 8192)),
+    # one scale per (token, KV head)
+    "ragged_fp8_tok_g4_d128_append": _ragged("r27", "fp8_e4m3", "bf16", "bf16", 128, 4,
+                                             [1, 16, 17, 200, 33, 48, 49], 27, append=True, ktok=True,
+                                             vtok=True),
+    "ragged_int8_tok_g8_d64_chan": _ragged("r28", "int8", "f16", "f16", 64, 8, RAGGED, 28, outliers=3,
+                                           ktok=True, vtok=True),
+    "ragged_fp8k_int8v_ktok_g8_d128": _ragged("r29", "fp8_e4m3", "bf16", "bf16", 128, 8, RAGGED, 29, hkv=3,
+                                              v="int8", ktok=True),
+    "ragged_fp8_vtok_g2_d128_f32": _ragged("r30", "fp8_e4m3", "f32", "f32", 128, 2, RAGGED, 30, vtok=True),
+    "ragged_int8_tok_g4_d128_fpsinks4": _ragged("r31", "int8", "bf16", "bf16", 128, 4, RAGGED, 31, fp_sinks=4,
+                                                ktok=True, vtok=True),
+    "long_fp8_tok_small": scaled(WORKLOADS["long_fp8_tok"], num_seqs=2, len_range=(8192, 8192)),
 }
 
 
@@ -894,9 +965,9 @@ def _compact_rows(x, layer, lay, seqs):
     h = {"q": host_storage(x["q"][layer]),
          "k_cache": host_storage(x["k_cache"][layer].index_select(0, idx)),
          "v_cache": host_storage(x["v_cache"][layer].index_select(0, idx))}
-    if "k_scales" in x:
-        h["k_scales"] = host_storage(x["k_scales"][layer].index_select(0, idx))
-        h["v_scales"] = host_storage(x["v_scales"][layer].index_select(0, idx))
+    for name in ("k_scales", "v_scales"):
+        if name in x:
+            h[name] = host_storage(x[name][layer].index_select(0, idx))
     if "k_channel_scales" in x:
         h["k_channel_scales"] = host_storage(x["k_channel_scales"])
     tables = np.full_like(lay.block_tables, -1)
@@ -914,7 +985,8 @@ def _compact_rows(x, layer, lay, seqs):
 
 
 @pytest.mark.parametrize("name", ["llama3_8b_bf16", "mha13b_prefix_f16", "mha13b_prefix_f16:grouped", "long_fp8",
-                                  "llama70b_f16_80l", "llama70b_fp8_80l", "long_fp8k_int8v", "long_int8_kchan"])
+                                  "llama70b_f16_80l", "llama70b_fp8_80l", "long_fp8k_int8v", "long_int8_kchan",
+                                  "long_bf16k_fp8v", "long_fp8_tok"])
 def test_full_size_sampled_rows(name):
     name, _, mode = name.partition(":")
     grouped = mode == "grouped"

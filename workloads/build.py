@@ -21,6 +21,11 @@ Recipe (all seeded from the workload's seed):
     slots hold 0x7F (fp8 NaN) or -128 (the unused int8 code); the new token's
     K/V are drawn in the query dtype and quantised on write, with its block's
     existing scale, by the step itself;
+  * per-token scales (k_scale_tok / v_scale_tok): the same, with one scale
+    per (slot, kv_head), amax|x| / QMAX over that token's row; the new
+    token sets its own slot's scale when it is written;
+  * a 16-bit K with an 8-bit V (kv_dtype f16/bf16, v_dtype fp8/int8): K is
+    drawn as for a 16-bit cache, V quantised as above;
   * K outlier channels (k_outliers > 0): in each KV head that many channels,
     chosen at random, are 16x larger, in the history and in the new token
     alike; K then has per-channel factors c[h][d] (16 on those channels, 1
@@ -240,6 +245,18 @@ def quantize_blocks(x: torch.Tensor, valid: Optional[torch.Tensor] = None, code:
     return torch.round(y).to(torch.int8), scales          # round: halves to even
 
 
+def quantize_tokens(x: torch.Tensor, code: str = "fp8_e4m3"):
+    """x: fp32 [NB, H, bs, D] -> (codes same shape, scales fp32 [NB, H, bs]):
+    one scale per (slot, head), the row's amax / QMAX (1.0 for a zero row)."""
+    qmax = _QMAX[code]
+    amax = x.abs().amax(dim=3)
+    scales = torch.where(amax > 0, amax / qmax, torch.ones_like(amax)).to(torch.float32)
+    y = (x / scales[..., None]).clamp_(-qmax, qmax)
+    if code == "fp8_e4m3":
+        return y.to(torch.float8_e4m3fn).view(torch.uint8), scales
+    return torch.round(y).to(torch.int8), scales          # round: halves to even
+
+
 def fp8_quantize_blocks(x: torch.Tensor, valid: Optional[torch.Tensor] = None):
     return quantize_blocks(x, valid, "fp8_e4m3")
 
@@ -286,12 +303,13 @@ def _make_inputs(layout: DecodeLayout, device: str, layers: Optional[int]) -> Di
     for name, cache in (("k", k_cache), ("v", v_cache)):
         tag = tags[name]
         if tag in _QMAX:
-            sc = torch.empty((nl, NB, Hkv), dtype=torch.float32, device=device)
+            tok = spec.k_scale_tok if name == "k" else spec.v_scale_tok
+            sc = torch.empty((nl, NB, Hkv) + ((bs,) if tok else ()), dtype=torch.float32, device=device)
             for layer in range(nl):
                 x = torch.randn((NB, Hkv, bs, D), generator=gen, device=device, dtype=torch.float32)
                 # with outlier channels x is already K / c: the history's K is
                 # code * scale * c, its outliers carried by c
-                codes, s = quantize_blocks(x, valid, tag)
+                codes, s = quantize_tokens(x, tag) if tok else quantize_blocks(x, valid, tag)
                 del x
                 codes.masked_fill_(poison, _POISON[tag])
                 cache[layer].copy_(codes)
@@ -305,8 +323,9 @@ def _make_inputs(layout: DecodeLayout, device: str, layers: Optional[int]) -> Di
                 del x
                 cache[layer].masked_fill_(poison, float("nan"))
     out["k_cache"], out["v_cache"] = k_cache, v_cache
-    if spec.quantised:
-        out["k_scales"], out["v_scales"] = scales["k"], scales["v"]
+    for name in ("k", "v"):
+        if name in scales:
+            out[f"{name}_scales"] = scales[name]
     if chan is not None:
         out["k_channel_scales"] = chan
     if spec.fp_sinks:

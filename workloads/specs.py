@@ -43,14 +43,23 @@ class DecodeWorkload:
     # 8-bit caches: the first this-many positions (<= 16) of every sequence
     # live in full-precision side tiles (q's dtype) instead of the cache
     fp_sinks: int = 0
+    # 8-bit caches: one scale per (slot, KV head) instead of per (block, KV
+    # head), for K and for V independently (per-token granularity)
+    k_scale_tok: bool = False
+    v_scale_tok: bool = False
 
     @property
     def v_tag(self) -> str:
         return self.v_dtype or self.kv_dtype
 
     @property
-    def quantised(self) -> bool:
+    def k_quantised(self) -> bool:
         return self.kv_dtype in ("fp8_e4m3", "int8")
+
+    @property
+    def quantised(self) -> bool:
+        """Some cache is 8-bit (K, or V next to a 16-bit K)."""
+        return self.k_quantised or self.v_tag in ("fp8_e4m3", "int8")
 
     @property
     def group(self) -> int:
@@ -111,6 +120,22 @@ WORKLOADS = {
         len_range=(131072, 131072), append=True, k_outliers=4,
         description="long-context int8 KV, 4 outlier K channels per head with per-channel K "
                     "factors, GQA-4, B=8 x 131072, bf16 q/out",
+    ),
+    "long_bf16k_fp8v": DecodeWorkload(
+        name="long_bf16k_fp8v", seed=56008, num_layers=1, num_seqs=8,
+        num_q_heads=32, num_kv_heads=8, head_dim=128,
+        kv_dtype="bf16", v_dtype="fp8_e4m3", q_dtype="bf16", out_dtype="bf16",
+        len_range=(131072, 131072), append=True,
+        description="long-context KV with V alone quantised: K bf16, V fp8 e4m3, GQA-4, "
+                    "B=8 x 131072, bf16 q/out",
+    ),
+    "long_fp8_tok": DecodeWorkload(
+        name="long_fp8_tok", seed=56009, num_layers=1, num_seqs=8,
+        num_q_heads=32, num_kv_heads=8, head_dim=128,
+        kv_dtype="fp8_e4m3", q_dtype="bf16", out_dtype="bf16",
+        len_range=(131072, 131072), append=True, k_scale_tok=True, v_scale_tok=True,
+        description="long-context FP8 e4m3 KV with one scale per (token, KV head), GQA-4, "
+                    "B=8 x 131072, bf16 q/out",
     ),
     "llama70b_fp8_80l": DecodeWorkload(
         name="llama70b_fp8_80l", seed=56007, num_layers=80, num_seqs=64,
