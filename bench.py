@@ -512,8 +512,9 @@ def main():
     chan = x.get("k_channel_scales")
     both_fp8 = (spec.kv_dtype == spec.v_tag == "fp8_e4m3" and chan is None and not spec.fp_sinks
                 and not (spec.k_scale_tok or spec.v_scale_tok))
-    # 16-bit and f32 caches: the append rides in the attention launch
-    fused = spec.append and not spec.quantised and not spec.fp_sinks and not args.separate_append
+    # the append rides in the attention launch (8-bit caches: quantised there,
+    # with the blocks' given scales or per-token scales); not with sink tiles
+    fused = spec.append and not spec.fp_sinks and not args.separate_append
 
     def step(ev=None):
         for layer in range(nl):
@@ -531,7 +532,9 @@ def main():
                 if spec.append:
                     pkv.kv_append(x["k_new"][layer], x["v_new"][layer], x["sink_slot_mapping"],
                                   x["sink_k"][layer], x["sink_v"][layer])
-            if spec.append and both_fp8:
+            if spec.append and fused:
+                pass                                # written by the attention launch
+            elif spec.append and both_fp8:
                 pkv.kv_append_fp8(x["k_new"][layer], x["v_new"][layer], x["slot_mapping"], kc, vc,
                                   kw["k_scales"], kw["v_scales"])
             elif spec.append and spec.quantised:
@@ -541,7 +544,7 @@ def main():
                 else:                               # a 16-bit K: a bit copy of K alone
                     pkv.kv_append(x["k_new"][layer], None, x["slot_mapping"], kc, None)
                 pkv.kv_append_quant(x["v_new"][layer], x["slot_mapping"], vc, kw["v_scales"])
-            elif spec.append and not fused:
+            elif spec.append:
                 pkv.kv_append(x["k_new"][layer], x["v_new"][layer], x["slot_mapping"], kc, vc)
             if ev is not None and layer in ev:
                 ev[layer][0].record()
@@ -550,7 +553,7 @@ def main():
                                       kc, vc, x["block_tables"], x["context_lens"], spec.scale, outs[layer],
                                       workspace=ws, partition_blocks=args.partition_blocks,
                                       window=args.window, sinks=args.sinks, total_blocks=total_blocks,
-                                      **gkw)
+                                      **gkw, **kw)
             else:
                 pkv.paged_decode_attn(x["q"][layer], kc, vc, x["block_tables"], x["context_lens"],
                                       spec.scale, outs[layer], workspace=ws,
@@ -583,8 +586,12 @@ def main():
 
     kv_bytes, alg_bytes, logical_bytes = attention_bytes(spec, lay, args.window, args.sinks)
     if fused:
-        # the launch also reads each new K/V row and writes it to its slot
-        alg_bytes += 4 * spec.num_seqs * spec.num_kv_heads * spec.head_dim * ELT[spec.kv_dtype]
+        # the launch also reads each new K/V row (q's dtype for an 8-bit cache)
+        # and writes it to its slot, with its per-token scale where there is one
+        rows = spec.num_seqs * spec.num_kv_heads
+        src = ELT[spec.q_dtype] if spec.quantised else ELT[spec.kv_dtype]
+        alg_bytes += rows * spec.head_dim * (2 * src + ELT[spec.kv_dtype] + ELT[spec.v_tag])
+        alg_bytes += rows * 4 * (int(spec.k_scale_tok) + int(spec.v_scale_tok))
     value = kv_bytes * nl / (ms_per_step / 1e3) / 1e9
     achieved = alg_bytes / mean_launch_s / 1e9
     kernel = ("decode_group_kernel" if grouped else "decode_partition_kernel") + (

@@ -371,6 +371,33 @@ PKV_API int pkv_paged_decode_attn_prefix(const void* q, const void* k_cache, con
                                          hipStream_t stream);
 
 /*
+ * One decode step with an 8-bit cache in one launch: the quantise-on-write
+ * append of each sequence's new token followed by pkv_paged_decode_attn_quant
+ * ("KV Cache from first principles" 2.2-2.3: write the new token at the
+ * current length, then attend to every position, its own included; "The KV
+ * Cache memory ledger" 7: 8-bit K/V with scales; "KV Cache from first
+ * principles" 5.2: per-token scales, or V alone quantised).
+ *   k_new, v_new: [num_seqs][num_kv_heads][head_dim] of q's dtype: token b
+ *     is sequence b's new token; slot_mapping: int64 [num_seqs], the slot of
+ *     sequence b's position context_lens[b] - 1, or -1 for none (slots
+ *     outside the pool are skipped; a slot elsewhere gives undefined
+ *     results).
+ *   p, dims, caches and the remaining arguments as for
+ *     pkv_paged_decode_attn_quant, without sink tiles (dims->sink_tiles 0).
+ * The new rows are written as pkv_kv_append_quant writes them with
+ * PKV_SCALE_GIVEN (the block's scale in k_scales / v_scales is read) or,
+ * for a cache with per-token scales, PKV_SCALE_PER_TOKEN (the token's slot
+ * scale is written first); a 16-bit K is copied as pkv_kv_append copies it.
+ * Codes, scales, output: those of the separate calls.
+ */
+PKV_API int pkv_paged_decode_step_quant(const void* k_new, const void* v_new,
+                                        const int64_t* slot_mapping, const void* q, void* k_cache,
+                                        void* v_cache, const pkv_quant_params* p,
+                                        const int32_t* block_tables, const int32_t* context_lens,
+                                        float scale, void* out, const pkv_decode_dims* dims,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * One decode step for a batch with shared-prefix groups, in one launch: the
  * append of pkv_paged_decode_step followed by pkv_paged_decode_attn_prefix
  * ("KV Cache from first principles" 2.2-2.3; "The KV Cache memory ledger"

@@ -149,6 +149,9 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_paged_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp,
                                           sz, vp]
     lib.pkv_paged_decode_step.restype = ctypes.c_int
+    lib.pkv_paged_decode_step_quant.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(QuantParams), vp, vp,
+                                                ctypes.c_float, vp, dims_p, vp, sz, vp]
+    lib.pkv_paged_decode_step_quant.restype = ctypes.c_int
     lib.pkv_paged_decode_step_prefix.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
                                                  dims_p, vp, sz, vp]
     lib.pkv_paged_decode_step_prefix.restype = ctypes.c_int
@@ -542,23 +545,57 @@ def paged_decode_step(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: to
                       total_blocks: int = 0,
                       prefix_group_starts: Optional[torch.Tensor] = None,
                       prefix_group_blocks: Optional[torch.Tensor] = None,
-                      prefix_max_seqs: int = 0, prefix_max_blocks: int = 0) -> torch.Tensor:
+                      prefix_max_seqs: int = 0, prefix_max_blocks: int = 0,
+                      k_scales: Optional[torch.Tensor] = None, v_scales: Optional[torch.Tensor] = None,
+                      k_channel_scales: Optional[torch.Tensor] = None) -> torch.Tensor:
     """kv_append of each sequence's new token, then paged_decode_attn, in one launch.
 
     k_new, v_new: [B, Hkv, D] (row b is sequence b's new token); slot_mapping:
     int64 [B], the slot of sequence b's last position (-1: none).  Caches and
     q/out f32, f16 or bf16 of one type.  Shared-prefix groups (f16/bf16) as in
     paged_decode_attn; each new token must then lie past its group's shared
-    blocks.  Returns `out`.
+    blocks.  8-bit caches (as in paged_decode_attn, no sink tiles): k_new and
+    v_new in q's dtype, quantised on write with the blocks' given scales, or
+    setting their own slot's scale when the scales are per token.  Returns
+    `out`.
     """
     lib = load_library()
     _dev(k_new, v_new, slot_mapping, q, k_cache, v_cache, block_tables, context_lens, out, workspace,
-         prefix_group_starts, prefix_group_blocks)
+         prefix_group_starts, prefix_group_blocks, k_scales, v_scales, k_channel_scales)
     _need(q.dim() == 3 and out.shape == q.shape, "q and out must be [B, Hq, D]")
     _need(k_cache.shape == v_cache.shape and k_cache.dim() == 4, "caches must be [NB, Hkv, 16, D]")
     B = q.shape[0]
     _need(k_new.shape == v_new.shape == (B, k_cache.shape[1], k_cache.shape[3]),
           "k_new/v_new must be [B, Hkv, D]")
+    kc, vc = _code(k_cache), _code(v_cache)
+    if vc in _Q8:
+        _need(k_new.dtype == v_new.dtype == q.dtype, "new rows of an 8-bit cache come in q's dtype")
+        _need(prefix_group_starts is None and prefix_group_blocks is None, "shared prefixes need 16-bit caches")
+        k8 = kc in _Q8
+        _need(kc in _Q8 or kc == _code(q), "K and V caches differ in dtype")
+        _need(v_scales is not None and (k_scales is not None) == k8,
+              "an 8-bit V needs v_scales, an 8-bit K k_scales (a 16-bit K takes none)")
+        for sc in (k_scales, v_scales):
+            _need(sc is None or (sc.dtype == torch.float32 and
+                                 sc.shape in (k_cache.shape[:2], k_cache.shape[:3])),
+                  "scales must be fp32 [NB, Hkv], or [NB, Hkv, 16] for one per (slot, head)")
+        _need(k_channel_scales is None or (k8 and k_channel_scales.dtype == torch.float32 and
+                                           k_channel_scales.shape == (k_cache.shape[1], k_cache.shape[3])),
+              "k_channel_scales must be fp32 [Hkv, D], for an 8-bit K")
+        dims = decode_dims(q, k_cache, block_tables, out, partition_blocks, window, sinks, False, total_blocks)
+        need = decode_workspace_bytes(dims)
+        if need and workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        qp = QuantParams(_ptr(k_scales), _ptr(v_scales), _ptr(k_channel_scales), vc, None, None, None, 0,
+                         int(k_scales is not None and k_scales.dim() == 3), int(v_scales.dim() == 3))
+        _check(lib.pkv_paged_decode_step_quant(
+            _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+            ctypes.byref(qp), _ptr(block_tables), _ptr(context_lens), float(scale), _ptr(out),
+            ctypes.byref(dims), _ptr(workspace) if need else None,
+            workspace.numel() * workspace.element_size() if need else 0, _stream(q)))
+        return out
+    _need(k_scales is None and v_scales is None and k_channel_scales is None,
+          "scales apply to 8-bit caches only")
     _need(k_new.dtype == v_new.dtype == k_cache.dtype == v_cache.dtype, "dtype mismatch")
     _need(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (B,), "slot_mapping must be int64 [B]")
     _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == B,

@@ -130,8 +130,8 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
   int st = check_dims(dims);
   if (st) return st;
   if (ap) {
-    if (qp || dims->sink_tiles) return PKV_ERR_SHAPE;   // 16-bit and f32 caches, no sink tiles
-    if (is_q8(dims->kv_dtype)) return PKV_ERR_DTYPE;
+    if (dims->sink_tiles) return PKV_ERR_SHAPE;          // no full-precision sink tiles
+    if (!qp && is_q8(dims->kv_dtype)) return PKV_ERR_DTYPE;
     if (!ap->k_new || !ap->v_new || !ap->slots) return PKV_ERR_NULL;
   }
   if (!gp && dims->prefix_groups != 0) return PKV_ERR_SHAPE;   // groups: the _prefix entry point
@@ -386,6 +386,17 @@ int pkv_paged_decode_step(const void* k_new, const void* v_new, const int64_t* s
   const StepAppend ap{k_new, v_new, slot_mapping, k_cache, v_cache};
   return decode_common(q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens, scale, out,
                        dims, workspace, workspace_bytes, stream, &ap);
+}
+
+int pkv_paged_decode_step_quant(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                                const void* q, void* k_cache, void* v_cache, const pkv_quant_params* p,
+                                const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                void* out, const pkv_decode_dims* dims, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  if (!p) return PKV_ERR_NULL;
+  const StepAppend ap{k_new, v_new, slot_mapping, k_cache, v_cache};
+  return decode_common(q, k_cache, v_cache, p, nullptr, block_tables, context_lens, scale, out, dims,
+                       workspace, workspace_bytes, stream, &ap);
 }
 
 int pkv_paged_decode_step_prefix(const void* k_new, const void* v_new, const int64_t* slot_mapping,

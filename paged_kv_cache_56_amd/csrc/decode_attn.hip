@@ -457,6 +457,81 @@ __device__ __forceinline__ void append_new_rows(const DecodeArgs& a, int b, int 
   }
 }
 
+// The step's append into a layout with an 8-bit cache: K (8-bit, or a
+// 16-bit K, which is copied) and V (8-bit) of sequence b's new token, head
+// h, written at its slot exactly as pkv_kv_append_quant (8-bit) and
+// pkv_kv_append (16-bit) write them: y = x / channel factor (8-bit K, when
+// given), then with per-token scales the slot's scale max|y| / QMAX (1 for
+// a zero row) is written first, otherwise the block's given scale is read;
+// codes are the nearest (ties to even) of clamp(y / scale, +-QMAX).  One
+// wave: lanes 0..31 take K, 32..63 V, D / 32 consecutive elements each.
+template <KV KT, KV VT, KV QT, int D>
+__device__ __forceinline__ void append_new_rows_q8(const DecodeArgs& a, int b, int h, int lane) {
+  static_assert(is_quantised<VT>(), "an 8-bit V");
+  constexpr int EPL = D / 32;
+  static_assert(EPL == 2 || EPL == 4, "head_dim 64 or 128");
+  const int64_t slot = a.new_slots[b];
+  if (!(slot >= 0 && slot < (int64_t)a.num_blocks * 16)) return;   // uniform over the wave
+  const bool isv = lane >= 32;
+  const int e0 = (lane & 31) * EPL;
+  const int64_t bh = (slot >> 4) * a.num_kv_heads + h;             // (block, head)
+  const int64_t src = ((int64_t)b * a.num_kv_heads + h) * D + e0;  // element of k_new / v_new
+  const int64_t dst = (bh * 16 + (slot & 15)) * D + e0;            // element of the cache
+  if constexpr (!is_quantised<KT>()) {
+    static_assert(QT == KT, "a 16-bit K takes rows of its own type");
+    if (!isv) {                                                     // K: a bit copy
+      const uint16_t* from = (const uint16_t*)a.k_new + src;
+      uint16_t* to = (uint16_t*)a.k_cache_rw + dst;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) to[e] = from[e];
+    }
+  }
+  float y[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    y[e] = load_elem_f32<QT>(isv ? a.v_new : a.k_new, src + e);
+    if (is_quantised<KT>() && !isv && a.k_chan) y[e] = y[e] / a.k_chan[(int64_t)h * D + e0 + e];
+  }
+  const bool tok = isv ? a.v_tok : a.k_tok;
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(y[e]));
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));   // over the half
+  auto write = [&](auto ct) __attribute__((always_inline)) {
+    constexpr KV CT = decltype(ct)::value;
+    constexpr float QM = qmax<CT>();
+    float* scales = const_cast<float*>(isv ? a.v_scales : a.k_scales);
+    float scale;
+    if (tok) {
+      scale = amax > 0.f ? amax / QM : 1.0f;
+      if ((lane & 31) == 0) scales[bh * 16 + (slot & 15)] = scale;
+    } else {
+      scale = scales[bh];
+    }
+    float v[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float q = y[e] / scale;
+      v[e] = q > QM ? QM : (q < -QM ? -QM : q);   // NaN passes through
+    }
+    const uint32_t codes = encode_codes<CT, EPL>(v);
+    uint8_t* to = (uint8_t*)(isv ? a.v_cache_rw : a.k_cache_rw) + dst;
+    if constexpr (EPL == 4) *(uint32_t*)to = codes;
+    else *(uint16_t*)to = (uint16_t)codes;
+  };
+  if (isv) write(std::integral_constant<KV, VT>{});
+  else if constexpr (is_quantised<KT>()) write(std::integral_constant<KV, KT>{});
+}
+
+// The step's append for any cache layout (see append_new_rows and
+// append_new_rows_q8), by one wave.
+template <KV KT, KV VT, KV QT, int D>
+__device__ __forceinline__ void append_step_rows(const DecodeArgs& a, int b, int h, int lane) {
+  if constexpr (is_quantised<VT>()) append_new_rows_q8<KT, VT, QT, D>(a, b, h, lane);
+  else append_new_rows<D, kv_bytes<KT>::value>(a, b, h, lane);
+}
+
 // Partition p's result for query head h * G + ha of sequence b, channel d,
 // from its (m, l, o), o being the unnormalised sum: the output element, or
 // the partition's workspace slot when the call is split.
@@ -478,10 +553,9 @@ __device__ __forceinline__ void finish_row(const DecodeArgs& a, int b, int h, in
 
 // A partition with nothing of the cache: a zero row (empty partitions of a
 // split call are skipped by the merge), and the append if it falls here.
-template <KV OT, int D, int G, int EB>
+template <KV KT, KV VT, KV QT, KV OT, int D, int G>
 __device__ __forceinline__ void finish_empty(const DecodeArgs& a, int b, int h, int p, int tid, bool append) {
-  if constexpr (EB > 1)
-    if (append) append_new_rows<D, EB>(a, b, h, tid & 63);
+  if (append) append_step_rows<KT, VT, QT, D>(a, b, h, tid & 63);
   if (!a.split)
     for (int idx = tid; idx < G * D; idx += 256) finish_row<OT, D, G>(a, b, h, p, idx / D, idx % D, -INFINITY, 0.f, 0.f);
 }
@@ -579,14 +653,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
 
   // the step's append (append_new_rows): by the partition holding the new
   // token's block, and in it by the wave that reads that block
-  const bool appends = !KQ && !VQ && a.new_slots != nullptr && p == (parts.n > 0 ? parts.n - 1 : 0);
+  const bool appends = a.new_slots != nullptr && p == (parts.n > 0 ? parts.n - 1 : 0);
   constexpr int BPS = C::BPS;
   const int append_wave = j1 > j0 ? ((j1 - 1 - j0) / BPS) % NW : 0;
-  auto append_rows = [&]() __attribute__((always_inline)) {
-    if constexpr (!KQ && !VQ) append_new_rows<D, C::EB>(a, b, h, lane);
-  };
+  auto append_rows = [&]() __attribute__((always_inline)) { append_step_rows<KT, VT, QT, D>(a, b, h, lane); };
   if (j0 >= j1) {
-    finish_empty<OT, D, G, (KQ || VQ) ? 1 : C::EB>(a, b, h, p, tid, appends && w == 0);
+    finish_empty<KT, VT, QT, OT, D, G>(a, b, h, p, tid, appends && w == 0);
     return;
   }
 

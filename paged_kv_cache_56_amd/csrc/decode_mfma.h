@@ -197,13 +197,11 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
 
   // the step's append (append_new_rows): by the partition holding the new
   // token's block, and in it by the wave that reads that block
-  const bool appends = !KQ && !VQ && a.new_slots != nullptr && p == (parts.n > 0 ? parts.n - 1 : 0);
+  const bool appends = a.new_slots != nullptr && p == (parts.n > 0 ? parts.n - 1 : 0);
   const int append_wave = j1 > j0 ? (j1 - 1 - j0) % NW : 0;
-  auto append_rows = [&]() __attribute__((always_inline)) {
-    if constexpr (!KQ && !VQ) append_new_rows<D, EB>(a, b, h, lane);
-  };
+  auto append_rows = [&]() __attribute__((always_inline)) { append_step_rows<KT, VT, QT, D>(a, b, h, lane); };
   if (j0 >= j1) {
-    finish_empty<OT, D, G, (KQ || VQ) ? 1 : EB>(a, b, h, p, tid, appends && w == 0);
+    finish_empty<KT, VT, QT, OT, D, G>(a, b, h, p, tid, appends && w == 0);
     return;
   }
 

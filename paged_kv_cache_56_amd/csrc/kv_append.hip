@@ -72,8 +72,6 @@ __device__ __forceinline__ float src_elem(const void* base, int64_t i) {
   else return __builtin_bit_cast(float, ((uint32_t)((const uint16_t*)base)[i]) << 16);
 }
 
-template <KV CT> constexpr float qmax() { return CT == KV::FP8 ? 448.0f : 127.0f; }
-
 // Source element divided by its channel factor (if any).
 template <KV ST>
 __device__ __forceinline__ float scaled_src(const QTarget& q, int64_t row, int h, int d, int head_dim) {
@@ -103,23 +101,6 @@ __global__ void __launch_bounds__(256) q8_first_write_scale_kernel(
   q.scales[scale_index(slot, h, num_kv_heads, per_token)] = amax > 0.f ? amax / qmax<CT>() : 1.0f;
 }
 
-// Four clamped quotients -> four codes in one word (element 0 in the low byte).
-template <KV CT>
-__device__ __forceinline__ uint32_t encode4(const float (&v)[4]) {
-  if constexpr (CT == KV::FP8) {
-    int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
-  } else {
-    uint32_t word = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float r = v[e] == v[e] ? __builtin_rintf(v[e]) : 0.f;   // ties to even; NaN -> 0
-      word |= ((uint32_t)(int)r & 0xFFu) << (8 * e);
-    }
-    return word;
-  }
-}
-
 template <KV ST, KV CT>
 __global__ void __launch_bounds__(256) q8_quantize_append_kernel(
     QTargets tg, const int64_t* __restrict__ slot_mapping, int num_tokens, int num_kv_heads,
@@ -146,7 +127,7 @@ __global__ void __launch_bounds__(256) q8_quantize_append_kernel(
       float v = scaled_src<ST>(q, row, h, gi * 16 + w * 4 + e, head_dim) / scale;
       v4[e] = v > QM ? QM : (v < -QM ? -QM : v);   // NaN passes through
     }
-    packed[w] = encode4<CT>(v4);
+    packed[w] = encode_codes<CT, 4>(v4);
   }
   uint8_t* dst = q.cache + ((blk * num_kv_heads + h) * PKV_BLOCK_SIZE + off) * head_dim + gi * 16;
   *(uint4*)dst = make_uint4(packed[0], packed[1], packed[2], packed[3]);

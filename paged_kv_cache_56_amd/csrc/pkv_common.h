@@ -172,4 +172,29 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return (uint16_t)(u >> 16);
 }
 
+// ---- 8-bit codes (quantise on write) ---------------------------------------
+// Largest code magnitude: 448 for OCP e4m3fn, 127 for symmetric int8.
+template <KV CT> constexpr float qmax() { return CT == KV::FP8 ? 448.0f : 127.0f; }
+
+// N (2 or 4) clamped quotients -> N codes in one word, element 0 in the low
+// byte: fp8 by the hardware's round-to-nearest-even e4m3 convert, int8 by
+// rint (ties to even; NaN gives 0).
+template <KV CT, int N>
+__device__ __forceinline__ uint32_t encode_codes(const float (&v)[N]) {
+  static_assert(N == 2 || N == 4, "two or four codes");
+  if constexpr (CT == KV::FP8) {
+    int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    if constexpr (N == 4) word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
+    return (uint32_t)word & (N == 4 ? 0xFFFFFFFFu : 0xFFFFu);
+  } else {
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      const float r = v[e] == v[e] ? __builtin_rintf(v[e]) : 0.f;
+      word |= ((uint32_t)(int)r & 0xFFu) << (8 * e);
+    }
+    return word;
+  }
+}
+
 }  // namespace pkv

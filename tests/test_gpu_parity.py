@@ -458,6 +458,11 @@ SMALL = {
     "ragged_int8_tok_g4_d128_fpsinks4": _ragged("r31", "int8", "bf16", "bf16", 128, 4, RAGGED, 31, fp_sinks=4,
                                                 ktok=True, vtok=True),
     "long_fp8_tok_small": scaled(WORKLOADS["long_fp8_tok"], num_seqs=2, len_range=(8192, 8192)),
+    "ragged_int8_g8_d64_chan_ktok_append": _ragged("r32", "int8", "bf16", "bf16", 64, 8,
+                                                   [1, 16, 17, 200, 33, 48, 49], 32, hkv=3, append=True,
+                                                   outliers=3, ktok=True),
+    "ragged_fp8_g8_d64_append_f32out": _ragged("r33", "fp8_e4m3", "f16", "f32", 64, 8, [5, 16, 17, 80, 33], 33,
+                                               append=True),
 }
 
 
@@ -766,6 +771,63 @@ def test_workspace_reused_across_calls(case):
     err = parity_err(out_f64(outs[2]), ref, spec.out_dtype, TOL[spec.kv_dtype])
     say(f"    max|err| = {err:.3e}")
     assert err <= TOL[spec.kv_dtype]
+
+
+QUANT_STEP_CASES = [
+    ("long_fp8_small", 0, None),
+    ("llama70b_fp8_small", 0, 1),
+    ("ragged_int8_g2_d128_chan_append", 0, None),
+    ("ragged_fp8k_int8v_g4_d128_chan_append", 2, 3),
+    ("ragged_f16k_int8v_g8_d128_append", 0, None),
+    ("ragged_bf16k_int8v_g1_d128_vtok_append", 1, None),
+    ("ragged_fp8_tok_g4_d128_append", 0, 2),
+    ("ragged_int8_g8_d64_chan_ktok_append", 0, None),
+    ("ragged_fp8_g8_d64_append_f32out", 3, None),
+]
+
+
+@pytest.mark.parametrize("case,pb,skip", QUANT_STEP_CASES)
+def test_fused_quant_step_matches_oracle(case, pb, skip):
+    """pkv_paged_decode_step_quant: the new token quantised on write inside
+    the attention launch (given block scales, or per-token scales the token
+    sets; a 16-bit K copied): codes and scales equal the oracle's append bit
+    for bit, the output the oracle's attention over them."""
+    spec = SMALL[case]
+    assert spec.append and spec.quantised
+    lay = build_layout(spec)
+    say(f"[step q8] {case}: pb={pb} skip={skip} k={spec.kv_dtype} v={spec.v_tag} "
+        f"tok={spec.k_scale_tok},{spec.v_scale_tok} lens={list(lay.context_lens[:12])}")
+    x = make_host_inputs(lay)
+    xs = _to_dev(x)
+    slots = lay.slot_mapping.copy()
+    if skip is not None:
+        slots[skip] = -1
+    sm = torch.from_numpy(slots).to(DEV)
+    tol = TOL[spec.kv_dtype]
+    for layer in range(spec.num_layers):
+        out = _out(spec)
+        kw = dict(v_scales=xs["v_scales"][layer])
+        if spec.k_quantised:
+            kw["k_scales"] = xs["k_scales"][layer]
+        if "k_channel_scales" in xs:
+            kw["k_channel_scales"] = xs["k_channel_scales"]
+        pkv.paged_decode_step(xs["k_new"][layer], xs["v_new"][layer], sm, xs["q"][layer], xs["k_cache"][layer],
+                              xs["v_cache"][layer], xs["block_tables"], xs["context_lens"], spec.scale, out,
+                              partition_blocks=pb, **kw)
+        torch.cuda.synchronize()
+        h = host_layer(x, layer)
+        kc, vc, ks, vs = oracle_append(h, spec, slots)
+        for name, ref in (("k_cache", kc), ("v_cache", vc), ("k_scales", ks), ("v_scales", vs)):
+            if ref is None:
+                continue
+            got = host_storage(xs[name][layer])
+            assert np.array_equal(got.view(np.uint8), ref.view(np.uint8)), (layer, name)
+        keep = [b for b in range(spec.num_seqs) if b != skip]
+        ref = oracle_attend(h, spec, kc, vc, ks, vs, lay.block_tables, lay.context_lens, seqs=keep)
+        got = out_f64(out)[keep]
+        err = parity_err(got, ref, spec.out_dtype, tol)
+        say(f"    layer {layer}: max|err| = {err:.3e} (tol {tol})")
+        assert np.isfinite(got).all() and err <= tol
 
 
 @pytest.mark.parametrize("pb", [1, 2, 3, 7])
