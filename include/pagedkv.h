@@ -348,7 +348,9 @@ PKV_API int pkv_paged_decode_step(const void* k_new, const void* v_new, const in
  * changes: a group's shared blocks are read once and scored against the
  * queries of all its sequences together (a matrix product on the matrix
  * cores), the rest of each sequence as usual, and the two parts are merged
- * by log-sum-exp.
+ * by log-sum-exp.  The shared part keeps the precision stated for
+ * pkv_paged_decode_attn's matrix-core products: each softmax weight enters
+ * the sum of V with about 22 (f16) or 16 (bf16) significant bits.
  *   group_seq_start: int32 device [G + 1], nondecreasing: group g is the
  *     sequences [group_seq_start[g], group_seq_start[g + 1]);
  *   group_prefix_blocks: int32 device [G]: every sequence of group g has the

@@ -34,11 +34,11 @@
 // leaves lane l with query l % 16, so the softmax rescale stays in-lane.
 //
 // Precision.  q, K and V are read as stored; products accumulate in fp32.
-// The probabilities exp2(s - m) (m: a reference at most 8 below the largest
-// score so far, so they stay <= 256) are rounded once to the operand type
-// (f16 or bf16), and the running sum adds the rounded values, so the result
-// is an exact convex combination of V rows with weights off by at most half
-// an ulp of that type.
+// Each probability exp2(s - m) (m: a reference at most 8 below the largest
+// score so far, so they stay <= 256) enters P.V as its value rounded to the
+// operand type plus the rounding remainder, itself rounded: about 22
+// significant bits with f16 operands, 16 with bf16.  The running sum adds
+// the fp32 probabilities.
 #pragma once
 
 #include "pkv_internal.h"
@@ -235,19 +235,26 @@ __device__ __forceinline__ void group_body(const DecodeArgs& a, int pp, int h, i
       m = mn;
     }
 
-    // B operand of O^T = V^T P^T: the lane's 8 tokens of query lq, rounded
-    uint32_t pw[4];
+    // B operands of O^T = V^T P^T: the lane's 8 tokens of query lq, each
+    // probability as its value rounded to the operand type (hi) plus the
+    // rounding remainder, rounded too (lo), in two products
+    uint32_t pw[4], pr[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      float r0, r1;
+      float r0, r1, e0, e1;
       const float p0 = sv[2 * k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[2 * k] - m);
       const float p1 = sv[2 * k + 1] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[2 * k + 1] - m);
       pw[k] = Mma<T>::round(p0, &r0) | (Mma<T>::round(p1, &r1) << 16);
-      l += r0 + r1;
+      pr[k] = Mma<T>::round(p0 - r0, &e0) | (Mma<T>::round(p1 - r1, &e1) << 16);
+      l += p0 + p1;
     }
     const u32x4_t pb = {pw[0], pw[1], pw[2], pw[3]};
+    const u32x4_t pl = {pr[0], pr[1], pr[2], pr[3]};
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[dt] = Mma<T>::run(*(const u32x4_t*)&vt[(dt * 16 + lq) * VS + 8 * lg], pb, acc[dt]);
+    for (int dt = 0; dt < DT; ++dt) {
+      const u32x4_t va = *(const u32x4_t*)&vt[(dt * 16 + lq) * VS + 8 * lg];
+      acc[dt] = Mma<T>::run(va, pl, Mma<T>::run(va, pb, acc[dt]));
+    }
   };
 
   // step i uses ring slot i % PF and refills it with step i + PF

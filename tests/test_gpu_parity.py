@@ -1048,7 +1048,7 @@ def _compact_rows(x, layer, lay, seqs):
 
 @pytest.mark.parametrize("name", ["llama3_8b_bf16", "mha13b_prefix_f16", "mha13b_prefix_f16:grouped", "long_fp8",
                                   "llama70b_f16_80l", "llama70b_fp8_80l", "long_fp8k_int8v", "long_int8_kchan",
-                                  "long_bf16k_fp8v", "long_fp8_tok"])
+                                  "long_bf16k_fp8v", "long_fp8_tok", "mha13b_prefix_bf16:grouped"])
 def test_full_size_sampled_rows(name):
     name, _, mode = name.partition(":")
     grouped = mode == "grouped"
