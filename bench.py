@@ -224,6 +224,41 @@ def read_probe(dev, gib: int = 4):
     return {"gbs": best, "bytes": gib * 2**30}
 
 
+def pattern_probe(x, lay, spec, dims, layers: int, launches: int, stride: int):
+    """The attention launch's access pattern without its arithmetic (the
+    library's paged_read_probe: same grid, tables, LDS-DMA K ring and V
+    register loads) on the same caches, launched like the attention calls
+    (layer after layer, HIP events around every `stride`-th launch).
+    Returns its mean launch time and K/V bytes per launch."""
+    import torch
+
+    import paged_kv_cache_56_amd as pkv
+
+    P = pkv.decode_num_partitions(dims)
+    sink = torch.zeros(spec.num_seqs * spec.num_kv_heads * P, dtype=torch.int32, device=x["q"].device)
+    for layer in range(layers):                   # warm
+        pkv.paged_read_probe(x["k_cache"][layer], x["v_cache"][layer], x["block_tables"], x["context_lens"],
+                             dims, sink)
+    torch.cuda.synchronize()
+    ev = []
+    for k in range(launches):
+        layer = k % layers
+        timed = k % stride == 0
+        if timed:
+            e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            e[0].record()
+        pkv.paged_read_probe(x["k_cache"][layer], x["v_cache"][layer], x["block_tables"], x["context_lens"],
+                             dims, sink)
+        if timed:
+            e[1].record()
+            ev.append(e)
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    nblk = -(-lay.context_lens.astype(np.int64) // 16)
+    tile = 16 * spec.head_dim * (ELT[spec.kv_dtype] + ELT[spec.v_tag])
+    return us, int(nblk.sum()) * spec.num_kv_heads * tile
+
+
 def copy_blocks_rate(x, spec, pairs: int):
     """Copy-on-write block copies on layer 0's caches: `pairs` random
     (src, dst) pairs with distinct destinations, each moving a whole block of
@@ -607,6 +642,14 @@ def main():
         copy_rec = copy_blocks_rate(x, spec, args.copy_pairs)
         log(f"[bench] copy-on-write copies: {copy_rec['pairs']} block pairs, {copy_rec['gbs']:.0f} GB/s")
 
+    pat = None
+    if (not args.no_probe and args.window == 0 and not spec.fp_sinks and not grouped and spec.head_dim == 128
+            and ELT[spec.kv_dtype] == ELT[spec.v_tag]):
+        pat_us, pat_bytes = pattern_probe(x, lay, spec, dims, nl, max(40, len(launch_ms) * stride), stride)
+        pat = {"us": pat_us, "gbs": pat_bytes / (pat_us / 1e6) / 1e9}
+        log(f"[bench] access-pattern probe: {pat_us:.1f} us per launch, {pat['gbs']:.0f} GB/s; the attention "
+            f"launch takes {mean_launch_s * 1e6 / pat_us:.3f}x as long")
+
     probe = None
     if not args.no_probe:
         probe = read_probe(dev)
@@ -667,6 +710,10 @@ def main():
             "kernel_source_sha": kernel_source_sha(),
             "read_probe_gbs": None if probe is None else round(probe["gbs"], 1),
             "frac_of_read_probe": None if probe is None else round(achieved / probe["gbs"], 4),
+            # the same K/V tiles through the same grid and staging, no arithmetic
+            "pattern_probe_us": None if pat is None else round(pat["us"], 2),
+            "pattern_probe_gbs": None if pat is None else round(pat["gbs"], 1),
+            "frac_of_pattern_probe": None if pat is None else round(pat["us"] / (mean_launch_s * 1e6), 4),
         },
         "cpu_baseline": cpu,
         "max_abs_err": None if cpu is None else cpu["max_abs_err_vs_gpu"],

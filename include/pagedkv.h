@@ -432,6 +432,24 @@ PKV_API int pkv_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, in
                                hipStream_t stream);
 
 /*
+ * The memory traffic of pkv_paged_decode_attn without its arithmetic, as a
+ * bandwidth reference for that access pattern ("KV Cache from first
+ * principles" 4.1, 4.3: decode is bound by the bytes it moves, fetched
+ * through the block table from scattered places).  Same grid and
+ * partition plan as the attention call for `dims`, the same per-wave
+ * order of blocks, K tiles copied into LDS by non-temporal DMA and V tiles
+ * read into registers by non-temporal loads one block ahead; each
+ * workgroup folds what it read into sink[(b * Hkv + h) * P + p]
+ * (uint32 device array of num_seqs * num_kv_heads *
+ * pkv_decode_num_partitions(dims) words, caller-zeroed if the value
+ * matters).  head_dim 128; kv_dtype F16, BF16, FP8_E4M3 or INT8 for both
+ * caches; no window, sink tiles or groups.  Computes nothing else.
+ */
+PKV_API int pkv_paged_read_probe(const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                 const int32_t* context_lens, const pkv_decode_dims* dims,
+                                 uint32_t* sink, hipStream_t stream);
+
+/*
  * Copy-on-write block copies ("Large-model inference KV Cache memory
  * optimisation" 3.2: copy a shared block before writing into it).  For every
  * i < num_pairs, block dst_blocks[i] of both caches receives a bit copy of

@@ -44,6 +44,7 @@ __all__ = [
     "decode_workspace_bytes",
     "decode_num_partitions",
     "hbm_read_probe",
+    "paged_read_probe",
     "DTYPE_CODES",
     "BLOCK_SIZE",
 ]
@@ -158,6 +159,8 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_paged_decode_attn_prefix.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
                                                  dims_p, vp, sz, vp]
     lib.pkv_paged_decode_attn_prefix.restype = ctypes.c_int
+    lib.pkv_paged_read_probe.argtypes = [vp, vp, vp, vp, dims_p, vp, vp]
+    lib.pkv_paged_read_probe.restype = ctypes.c_int
     lib.pkv_hbm_read_probe.argtypes = [vp, sz, vp, i32, vp]
     lib.pkv_hbm_read_probe.restype = ctypes.c_int
     i64, i32p, i64p = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
@@ -418,6 +421,19 @@ def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
     _need(sink.dtype == torch.int32 and sink.dim() == 1, "sink must be int32 [workgroups]")
     _check(load_library().pkv_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                              sink.numel(), _stream(buf)))
+
+
+def paged_read_probe(k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                     context_lens: torch.Tensor, dims: DecodeDims, sink: torch.Tensor) -> None:
+    """The attention call's memory traffic for `dims` without its arithmetic
+    (bandwidth reference); sink: int32 [B * Hkv * partitions] on the device."""
+    _dev(k_cache, v_cache, block_tables, context_lens, sink)
+    _need(sink.dtype == torch.int32 and sink.dim() == 1 and
+          sink.numel() >= dims.num_seqs * dims.num_kv_heads * decode_num_partitions(dims),
+          "sink must be int32 [B * Hkv * partitions]")
+    _check(load_library().pkv_paged_read_probe(_ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                               _ptr(context_lens), ctypes.byref(dims), _ptr(sink),
+                                               _stream(k_cache)))
 
 
 def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

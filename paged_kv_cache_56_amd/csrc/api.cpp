@@ -429,6 +429,35 @@ int pkv_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t si
   return launch_hbm_read(buf, bytes, sink, sink_words, stream);
 }
 
+int pkv_paged_read_probe(const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, const pkv_decode_dims* dims, uint32_t* sink,
+                         hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (dims->head_dim != 128 || dims->window != 0 || dims->sink_tiles || dims->prefix_groups)
+    return PKV_ERR_SHAPE;
+  const int eb = elem_bytes(dims->kv_dtype);
+  if (eb != 1 && eb != 2) return PKV_ERR_DTYPE;
+  if (!k_cache || !v_cache || !block_tables || !context_lens || !sink) return PKV_ERR_NULL;
+  int pb, np;
+  plan_partitions(*dims, &pb, &np);
+  DecodeArgs a{};
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = dims->num_seqs;
+  a.num_q_heads = dims->num_q_heads;
+  a.num_kv_heads = dims->num_kv_heads;
+  a.head_dim = dims->head_dim;
+  a.num_blocks = dims->num_blocks;
+  a.max_blocks = dims->max_blocks_per_seq;
+  a.part_blocks = pb;
+  a.num_parts = np;
+  a.kv_dtype = dims->kv_dtype;
+  return launch_paged_read_probe(a, sink, stream);
+}
+
 const char* pkv_status_string(int status) {
   switch (status) {
     case PKV_OK: return "ok";

@@ -1214,7 +1214,8 @@ template <KV KT, KV VT, KV QT, KV OT, int D, int G>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MinWaves<KT, VT, D, G>::value)))
 decode_partition_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[PassLds<KT, VT, D, G>::value];
-  cache_pass<KT, VT, QT, OT, D, G>(a, blockIdx.x, blockIdx.y, blockIdx.z, smem);
+  const Unit u = unit_of(a, blockIdx.x);
+  cache_pass<KT, VT, QT, OT, D, G>(a, u.p, u.h, u.b, smem);
 }
 
 // Cache pass and shared-prefix group pass in one launch: the first
@@ -1230,9 +1231,8 @@ __global__ void __launch_bounds__(256) decode_group_kernel(DecodeArgs a) {
     const int pp = id % a.group_num_parts, rest = id / a.group_num_parts;
     group_body<T, D>(a, pp, rest % a.num_kv_heads, rest / a.num_kv_heads, smem);
   } else {
-    const int k = id - a.group_wgs;
-    const int p = k % a.num_parts, rest = k / a.num_parts;
-    cache_pass<T, T, T, T, D, G>(a, p, rest % a.num_kv_heads, rest / a.num_kv_heads, smem);
+    const Unit u = unit_of(a, id - a.group_wgs);
+    cache_pass<T, T, T, T, D, G>(a, u.p, u.h, u.b, smem);
   }
 }
 
@@ -1447,8 +1447,9 @@ static int launch_typed(const DecodeArgs& a, hipStream_t stream) {
     }
   }
   if (a.group_wgs > 0) return PKV_ERR_DTYPE;   // groups run with 16-bit caches only
-  dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((decode_partition_kernel<KT, VT, QT, OT, D, G>), grid, dim3(256), 0, stream, a);
+  const int64_t n = (int64_t)a.num_parts * a.num_kv_heads * a.num_seqs;
+  if (n > 0x7FFFFFFF) return PKV_ERR_SHAPE;
+  hipLaunchKernelGGL((decode_partition_kernel<KT, VT, QT, OT, D, G>), dim3((unsigned)n), dim3(256), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return PKV_ERR_LAUNCH;
   if (a.split) {
     hipLaunchKernelGGL((lse_merge_kernel<QT, OT, D>), dim3(a.num_seqs * a.num_q_heads), dim3(64), 0,

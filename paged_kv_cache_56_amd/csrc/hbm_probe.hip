@@ -42,4 +42,125 @@ int launch_hbm_read(const void* buf, size_t bytes, uint32_t* sink, int sink_word
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
+// ---------------------------------------------------------------------------
+// The decode kernel's memory traffic without its arithmetic: the reference
+// for how fast this access pattern can stream on the device.  Same grid
+// (partition, KV head, sequence) and partition plan as the attention
+// launch; in a workgroup wave w takes the blocks j0 + w, j0 + w + 4, ...;
+// per block, K's (block, head) tile is copied into a two-slot per-wave LDS
+// ring by non-temporal LDS DMA, 1 KiB per wave instruction, and V's tile
+// is read into registers by non-temporal loads, four rows per wave
+// instruction, one block ahead of the one being consumed; the table entry
+// of the next block is read as a scalar load.  Consuming a block is
+// reading the lane's 32 channels of K back from LDS and folding them and
+// the V words into one word, which each wave adds to sink[workgroup].
+// head_dim 128; tiles of 16-bit (EB = 2) or 8-bit (EB = 1) elements.
+template <int EB>
+__global__ void __launch_bounds__(256) paged_read_probe_kernel(DecodeArgs a, uint32_t* __restrict__ sink) {
+  constexpr int D = 128, ROW_B = D * EB, TILE_B = 16 * ROW_B, NDMA = TILE_B / 1024;
+  constexpr int KREADS = 2 * EB, VW = 2 * EB, NW = 4, KR = 2;
+  __shared__ __attribute__((aligned(16))) char ring[NW * KR * TILE_B];
+  const Unit u = unit_of(a, blockIdx.x);
+  const int p = u.p, h = u.h, b = u.b;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lq = lane & 15, lg = lane >> 4;
+  int L = a.context_lens[b];
+  L = L < 0 ? 0 : (L > a.max_blocks * 16 ? a.max_blocks * 16 : L);
+  const SeqParts parts((L + 15) >> 4, a.part_blocks, a.num_parts, p);
+  const int nunits = parts.j1 - parts.j0;
+  const int n_my = w < nunits ? (nunits - w + NW - 1) / NW : 0;
+  const __attribute__((address_space(4))) int32_t* table =
+      (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)b * a.max_blocks);
+  auto tile = [&](int j) __attribute__((always_inline)) {
+    const int phys = table[j];
+    return ((int64_t)(((unsigned)phys < (unsigned)a.num_blocks) ? phys : 0) * a.num_kv_heads + h) * TILE_B;
+  };
+  // the decode pass's LDS placement of K: HBM column x of row r at LDS
+  // column x ^ f(r), so that a lane group's reads of one column of 16 rows
+  // hit 16 bank groups
+  uint32_t dma_off[NDMA], kaddr[KREADS];
+  const uint32_t slot0 = lds_offset(ring) + (uint32_t)(w * KR * TILE_B);
+#pragma unroll
+  for (int n = 0; n < NDMA; ++n) {
+    if constexpr (EB == 2) {
+      const int r = n * 4 + lg;
+      dma_off[n] = (uint32_t)(r * 256 + ((lq ^ r) & 15) * 16);
+    } else {
+      const int r = n * 8 + (lane >> 3);
+      dma_off[n] = (uint32_t)(r * 128 + (((lane & 7) ^ (r >> 1)) & 7) * 16);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < KREADS; ++k) {
+    if constexpr (EB == 2) kaddr[k] = slot0 + (uint32_t)(lq * 256 + (((lg * 4 + k) ^ lq) & 15) * 16);
+    else kaddr[k] = slot0 + (uint32_t)(lq * 128 + (((lg * 2 + k) ^ (lq >> 1)) & 7) * 16);
+  }
+  typedef uint32_t VRow[4][VW];
+  auto issue = [&](int64_t off, int sk, VRow& v) __attribute__((always_inline)) {
+    const char* k = (const char*)a.k_cache + off;
+#pragma unroll
+    for (int n = 0; n < NDMA; ++n) lds_dma16(k, dma_off[n], slot0 + sk * TILE_B + n * 1024);
+    const char* vsrc = (const char*)a.v_cache + off;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t o = (uint32_t)((lg * 4 + i) * ROW_B + lq * 8 * EB);
+      if constexpr (VW == 4) {
+        const u32x4_t x = __builtin_nontemporal_load((const u32x4_t*)(vsrc + o));
+        v[i][0] = x[0]; v[i][1] = x[1]; v[i][2] = x[2]; v[i][3] = x[3];
+      } else {
+        const u32x2_t x = __builtin_nontemporal_load((const u32x2_t*)(vsrc + o));
+        v[i][0] = x[0]; v[i][1] = x[1];
+      }
+    }
+  };
+  constexpr unsigned kWaitVm0 = 0x0F70;     // vmcnt(0), expcnt(7), lgkmcnt(15)
+  uint32_t acc = 0;
+  int64_t next = 0;
+  VRow va, vb;
+  if (n_my > 0) {
+    issue(tile(parts.j0 + w), 0, va);
+    if (n_my > 1) next = tile(parts.j0 + w + NW);
+  }
+  // step t: wait for everything (block t is the newest load in flight),
+  // issue block t + 1 into the other ring slot and register set, consume t
+  auto step = [&](int t, VRow& vcur, VRow& vnext) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    wait_vmcnt<0>();
+    if (t + 1 < n_my) {
+      issue(next, (t + 1) & 1, vnext);
+      if (t + 2 < n_my) next = tile(parts.j0 + w + (t + 2) * NW);
+    }
+    uint32_t addr[KREADS];
+#pragma unroll
+    for (int k = 0; k < KREADS; ++k) addr[k] = kaddr[k] + (uint32_t)((t & 1) * TILE_B);
+    u32x4_t kr[KREADS];
+    lds_read16_wait<KREADS>(kr, addr);
+#pragma unroll
+    for (int k = 0; k < KREADS; ++k) acc ^= kr[k][0] ^ kr[k][1] ^ kr[k][2] ^ kr[k][3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < VW; ++k) acc ^= vcur[i][k];
+  };
+  int t = 0;
+  for (; t + 1 < n_my; t += 2) {
+    step(t, va, vb);
+    step(t + 1, vb, va);
+  }
+  if (t < n_my) step(t, va, vb);
+  for (int d = 32; d >= 1; d >>= 1) acc ^= __shfl_xor(acc, d);
+  if (lane == 0) atomicXor(sink + ((int64_t)b * a.num_kv_heads + h) * a.num_parts + p, acc);
+}
+
+int launch_paged_read_probe(const DecodeArgs& a, uint32_t* sink, hipStream_t stream) {
+  const int64_t n = (int64_t)a.num_parts * a.num_kv_heads * a.num_seqs;
+  if (n > 0x7FFFFFFF) return PKV_ERR_SHAPE;
+  const dim3 grid((unsigned)n);
+  if (a.kv_dtype == PKV_FP8_E4M3 || a.kv_dtype == PKV_INT8)
+    hipLaunchKernelGGL((paged_read_probe_kernel<1>), grid, dim3(256), 0, stream, a, sink);
+  else
+    hipLaunchKernelGGL((paged_read_probe_kernel<2>), grid, dim3(256), 0, stream, a, sink);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
 }  // namespace pkv

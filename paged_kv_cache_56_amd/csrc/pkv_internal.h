@@ -92,6 +92,22 @@ struct SeqParts {
   }
 };
 
+// (partition, KV head, sequence) of the k-th workgroup of the cache pass:
+// the partition varies fastest, then the KV head.  (Workgroups go to the
+// XCDs round robin, so with one partition an XCD takes one KV head of
+// every sequence.  The sequence varying fastest instead, so that every XCD
+// takes all heads, measured no faster on the 70B-shaped step and 7-10 us
+// slower on the uneven Llama-3-8B and shared-prefix layers.)
+struct Unit { int p, h, b; };
+__device__ __forceinline__ Unit unit_of(const DecodeArgs& a, int k) {
+  Unit u;
+  u.p = k % a.num_parts;
+  const int rest = k / a.num_parts;
+  u.h = rest % a.num_kv_heads;
+  u.b = rest / a.num_kv_heads;
+  return u;
+}
+
 // One group as both passes see it, clamped so that they always agree on
 // which blocks of which sequence the group pass covers.
 struct PrefixGroup {
@@ -133,5 +149,9 @@ int launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 int launch_hbm_read(const void* buf, size_t bytes, uint32_t* sink, int sink_words,
                     hipStream_t stream);
+
+// The attention launch's access pattern without its arithmetic (head_dim
+// 128; K and V of one element width): sink has one word per workgroup.
+int launch_paged_read_probe(const DecodeArgs& a, uint32_t* sink, hipStream_t stream);
 
 }  // namespace pkv

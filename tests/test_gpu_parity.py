@@ -1046,6 +1046,44 @@ def _compact_rows(x, layer, lay, seqs):
     return h, tables, slots
 
 
+@pytest.mark.parametrize("case,pb", [("ragged_f16_g8_d128", 1000), ("ragged_f16_g8_d128", 3),
+                                     ("long_fp8_small", 64), ("ragged_bf16k_fp8v_g4_d128", 5)])
+def test_paged_read_probe_reads_exactly_the_attended_tiles(case, pb):
+    """The access-pattern probe reads, per workgroup (sequence, KV head,
+    partition), every 32-bit word of the K and V tiles of the blocks that
+    partition covers and nothing else: its sink equals the XOR of exactly
+    those words, computed on the host."""
+    spec = SMALL[case]
+    if spec.kv_dtype != spec.v_tag:
+        spec = scaled(spec, v_dtype=None)            # the probe reads K and V of one width
+    lay = build_layout(spec)
+    say(f"[probe] {case}: pb={pb} lens={list(lay.context_lens[:12])}")
+    x = make_host_inputs(lay)
+    xs = _to_dev(x)
+    out = _out(spec)
+    dims = pkv.decode_dims(xs["q"][0], xs["k_cache"][0], xs["block_tables"], out, partition_blocks=pb)
+    P = pkv.decode_num_partitions(dims)
+    sink = torch.zeros(spec.num_seqs * spec.num_kv_heads * P, dtype=torch.int32, device=DEV)
+    pkv.paged_read_probe(xs["k_cache"][0], xs["v_cache"][0], xs["block_tables"], xs["context_lens"], dims, sink)
+    torch.cuda.synchronize()
+    kw = x["k_cache"][0].contiguous().view(torch.int32).numpy()
+    vw = x["v_cache"][0].contiguous().view(torch.int32).numpy()
+    pbk = min(pb, lay.max_blocks_per_seq)           # the plan's piece size
+    want = np.zeros_like(sink.cpu().numpy())
+    for b in range(spec.num_seqs):
+        natt = -(-int(lay.context_lens[b]) // 16)
+        n = min(-(-natt // pbk), P) if natt else 0
+        per = -(-natt // n) if n else 0
+        for h in range(spec.num_kv_heads):
+            for p in range(P):
+                acc = np.int32(0)
+                for j in range(p * per, min(p * per + per, natt)):
+                    blk = int(lay.block_tables[b, j])
+                    acc ^= np.bitwise_xor.reduce(kw[blk, h].ravel()) ^ np.bitwise_xor.reduce(vw[blk, h].ravel())
+                want[(b * spec.num_kv_heads + h) * P + p] = acc
+    assert np.array_equal(sink.cpu().numpy(), want)
+
+
 @pytest.mark.parametrize("name", ["llama3_8b_bf16", "mha13b_prefix_f16", "mha13b_prefix_f16:grouped", "long_fp8",
                                   "llama70b_f16_80l", "llama70b_fp8_80l", "long_fp8k_int8v", "long_int8_kchan",
                                   "long_bf16k_fp8v", "long_fp8_tok", "mha13b_prefix_bf16:grouped"])
