@@ -224,21 +224,61 @@ def read_probe(dev, gib: int = 4):
     return {"gbs": best, "bytes": gib * 2**30}
 
 
-def pattern_probe(x, lay, spec, dims, layers: int, launches: int, stride: int):
+def grouped_probe_rows(lay, group_pieces: int):
+    """Block-table rows and lengths whose plain per-sequence reading is the
+    unique traffic of a shared-prefix launch: each group's shared blocks cut
+    into `group_pieces` equal pieces (one row each, read once, and first, as
+    the group pass's workgroups lead the launch), then every sequence's
+    blocks after its group's shared ones.  Host-side bookkeeping only."""
+    tab, lens = lay.block_tables, lay.context_lens.astype(np.int64)
+    B, maxb = tab.shape
+    skip = np.zeros(B, dtype=np.int64)
+    rows, rlens = [], []
+    for g in range(len(lay.group_blocks)):
+        s0, s1 = int(lay.group_starts[g]), int(lay.group_starts[g + 1])
+        nb = int(lay.group_blocks[g])
+        if s1 <= s0 or nb <= 0:
+            continue
+        skip[s0:s1] = nb
+        pb = -(-nb // max(1, group_pieces))
+        for j0 in range(0, nb, pb):
+            j1 = min(j0 + pb, nb)
+            r = np.zeros(maxb, dtype=np.int32)
+            r[:j1 - j0] = tab[s0, j0:j1]
+            rows.append(r)
+            rlens.append((j1 - j0) * 16)
+    for b in range(B):
+        r = np.zeros(maxb, dtype=np.int32)
+        k = int(skip[b])
+        r[:maxb - k] = tab[b, k:]
+        rows.append(r)
+        rlens.append(int(lens[b]) - 16 * k)
+    return np.stack(rows).astype(np.int32), np.array(rlens, dtype=np.int32)
+
+
+def pattern_probe(x, lay, spec, dims, layers: int, launches: int, stride: int, rows=None):
     """The attention launch's access pattern without its arithmetic (the
     library's paged_read_probe: same grid, tables, LDS-DMA K ring and V
     register loads) on the same caches, launched like the attention calls
-    (layer after layer, HIP events around every `stride`-th launch).
+    (layer after layer, HIP events around every `stride`-th launch).  With
+    `rows` = (block tables, lengths, dims) the probe reads those rows instead
+    (a shared-prefix launch's unique blocks).
     Returns its mean launch time and K/V bytes per launch."""
     import torch
 
     import paged_kv_cache_56_amd as pkv
 
+    tables, lens = x["block_tables"], x["context_lens"]
+    nblk = -(-lay.context_lens.astype(np.int64) // 16)
+    if rows is not None:
+        tab_np, lens_np, dims = rows
+        tables = torch.from_numpy(tab_np).to(x["q"].device)
+        lens = torch.from_numpy(lens_np).to(x["q"].device)
+        nblk = -(-lens_np.astype(np.int64) // 16)
     P = pkv.decode_num_partitions(dims)
-    sink = torch.zeros(spec.num_seqs * spec.num_kv_heads * P, dtype=torch.int32, device=x["q"].device)
+    sink = torch.zeros(dims.num_seqs * spec.num_kv_heads * P, dtype=torch.int32, device=x["q"].device)
     for layer in range(layers):                   # warm
-        pkv.paged_read_probe(x["k_cache"][layer], x["v_cache"][layer], x["block_tables"], x["context_lens"],
-                             dims, sink)
+        pkv.paged_read_probe(x["k_cache"][layer], x["v_cache"][layer], tables, lens, dims, sink)
     torch.cuda.synchronize()
     ev = []
     for k in range(launches):
@@ -247,14 +287,12 @@ def pattern_probe(x, lay, spec, dims, layers: int, launches: int, stride: int):
         if timed:
             e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             e[0].record()
-        pkv.paged_read_probe(x["k_cache"][layer], x["v_cache"][layer], x["block_tables"], x["context_lens"],
-                             dims, sink)
+        pkv.paged_read_probe(x["k_cache"][layer], x["v_cache"][layer], tables, lens, dims, sink)
         if timed:
             e[1].record()
             ev.append(e)
     torch.cuda.synchronize()
     us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
-    nblk = -(-lay.context_lens.astype(np.int64) // 16)
     tile = 16 * spec.head_dim * (ELT[spec.kv_dtype] + ELT[spec.v_tag])
     return us, int(nblk.sum()) * spec.num_kv_heads * tile
 
@@ -643,9 +681,24 @@ def main():
         log(f"[bench] copy-on-write copies: {copy_rec['pairs']} block pairs, {copy_rec['gbs']:.0f} GB/s")
 
     pat = None
-    if (not args.no_probe and args.window == 0 and not spec.fp_sinks and not grouped and spec.head_dim == 128
+    if (not args.no_probe and args.window == 0 and not spec.fp_sinks and spec.head_dim == 128
             and ELT[spec.kv_dtype] == ELT[spec.v_tag]):
-        pat_us, pat_bytes = pattern_probe(x, lay, spec, dims, nl, max(40, len(launch_ms) * stride), stride)
+        rows = None
+        if grouped:
+            # the group pass's pieces per group, from the workspace it is given
+            # (a partial result per query row per piece)
+            row_b = spec.num_seqs * spec.num_q_heads * (spec.head_dim + 2) * 4
+            gpieces = ws_bytes // row_b - nparts
+            tab_np, lens_np = grouped_probe_rows(lay, gpieces)
+            qd = torch.empty((len(lens_np), spec.num_q_heads, spec.head_dim), dtype=x["q"].dtype, device=dev)
+            tb = torch.from_numpy(tab_np)
+            pdims = pkv.decode_dims(qd, x["k_cache"][0], tb, qd, args.partition_blocks, 0, 0, False,
+                                    int((-(-lens_np.astype(np.int64) // 16)).sum()))
+            rows = (tab_np, lens_np, pdims)
+            log(f"[bench] access-pattern probe rows: {gpieces} prefix pieces per group + the suffixes "
+                f"({pkv.decode_num_partitions(pdims)} partitions per row)")
+        pat_us, pat_bytes = pattern_probe(x, lay, spec, dims, nl, max(40, len(launch_ms) * stride), stride,
+                                          rows)
         pat = {"us": pat_us, "gbs": pat_bytes / (pat_us / 1e6) / 1e9}
         log(f"[bench] access-pattern probe: {pat_us:.1f} us per launch, {pat['gbs']:.0f} GB/s; the attention "
             f"launch takes {mean_launch_s * 1e6 / pat_us:.3f}x as long")

@@ -415,6 +415,14 @@ struct SeqSpan {
     natt = nsb + nblk - wb0;
   }
   __device__ __forceinline__ int logical(int cidx) const { return cidx < nsb ? cidx : cidx - nsb + wb0; }
+  // token rows of logical block j that hold a token: 16, but fewer in the
+  // last block.  Rows past them are never fetched: their scores are masked
+  // and their V rows zeroed whatever the staging holds there, so the
+  // kernels read the bytes of the sequence's tokens and no more.
+  __device__ __forceinline__ int rows(int j) const {
+    const int n = L - j * 16;
+    return n < 0 ? 0 : (n > 16 ? 16 : n);
+  }
   // bit t set: token t of logical block j is attended
   __device__ __forceinline__ uint32_t valid_bits(int j) const {
     const int base = j * 16;
@@ -946,20 +954,31 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
       roff[i][v] = (uint32_t)((((i ^ tmask) * R + r) * D + (v * LPT + c) * E) * VEB);
   // Ordinary loads: non-temporal V loads measured no faster on a uniform
   // batch and about 40% slower on a batch of uneven lengths.
-  auto issue_vregs = [&](int phys_raw, TokWords<NWTV> (&vr)[TPL]) __attribute__((always_inline)) {
+  // nv: token rows of the block to fetch (rows_of); lanes of rows past it
+  // load nothing.
+  auto issue_vregs = [&](int phys_raw, TokWords<NWTV> (&vr)[TPL], int nv) __attribute__((always_inline)) {
     const char* src = vbase + vtile_of(phys_raw);
-#pragma unroll
-    for (int i = 0; i < TPL; ++i)
-#pragma unroll
-      for (int v = 0; v < VPT; ++v) {
-        if constexpr (VLW == 16) {
-          const uint4 x = *(const uint4*)(src + roff[i][v]);
-          vr[i].w[4 * v + 0] = x.x; vr[i].w[4 * v + 1] = x.y; vr[i].w[4 * v + 2] = x.z; vr[i].w[4 * v + 3] = x.w;
-        } else {
-          const uint2 x = *(const uint2*)(src + roff[i][v]);
-          vr[i].w[2 * v + 0] = x.x; vr[i].w[2 * v + 1] = x.y;
-        }
+    auto load = [&](int i, int v) __attribute__((always_inline)) {
+      if constexpr (VLW == 16) {
+        const uint4 x = *(const uint4*)(src + roff[i][v]);
+        vr[i].w[4 * v + 0] = x.x; vr[i].w[4 * v + 1] = x.y; vr[i].w[4 * v + 2] = x.z; vr[i].w[4 * v + 3] = x.w;
+      } else {
+        const uint2 x = *(const uint2*)(src + roff[i][v]);
+        vr[i].w[2 * v + 0] = x.x; vr[i].w[2 * v + 1] = x.y;
       }
+    };
+    if (nv >= 16) {
+#pragma unroll
+      for (int i = 0; i < TPL; ++i)
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) load(i, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < TPL; ++i)
+#pragma unroll
+        for (int v = 0; v < VPT; ++v)
+          if (((i ^ tmask) * R + r) < nv) load(i, v);
+    }
   };
   // K(t) from its ring slot: the 16 bytes each lane's DMA copy wrote, read
   // back with ds_read_b128 (consecutive lanes, consecutive 16-byte columns:
@@ -1000,11 +1019,22 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
   };
   {
     const uint32_t kslot0 = lds_offset(smem) + (uint32_t)(w * KR * BPS * TILE_B);
-    auto issue_k2 = [&](int phys_raw, int sk) __attribute__((always_inline)) {
+    // nv as for issue_vregs: a copy's lanes of rows past it copy nothing
+    // (the slot keeps older bytes there, which compute_block never uses).
+    auto issue_k2 = [&](int phys_raw, int sk, int nv) __attribute__((always_inline)) {
       const char* src = kbase + tile_of(phys_raw);
       const uint32_t dst = kslot0 + (uint32_t)(sk * TILE_B);
+      if (nv >= 16) {
 #pragma unroll
-      for (int n = 0; n < NDMA; ++n) lds_dma16(src, dma_off[n], dst + n * 1024);
+        for (int n = 0; n < NDMA; ++n) lds_dma16(src, dma_off[n], dst + n * 1024);
+      } else {
+#pragma unroll
+        for (int n = 0; n < NDMA; ++n) {
+          // token row of this lane's 16 bytes in copy n
+          const int row = LW == 16 ? (n / VPT) * R + r : (n * 1024 + lane * 16) / (D * C::EB);
+          if (row < nv) lds_dma16(src, dma_off[n], dst + n * 1024);
+        }
+      }
     };
     // Step t of wave w covers unit w + t * NW: the BPS attended blocks from
     // j0 + (w + t * NW) * BPS.  A block past j1 (the partition's last unit
@@ -1017,6 +1047,11 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
       const int j = blk(t, b2);
       if constexpr (BPS == 1) return entry_of(j);   // every step's block is in range
       else return j < j1 ? entry_of(j) : -1;
+    };
+    auto rows_at = [&](int t, int b2) __attribute__((always_inline)) {
+      const int j = blk(t, b2);
+      if constexpr (BPS == 1) return span.rows(span.logical(j));
+      else return j < j1 ? span.rows(span.logical(j)) : 0;
     };
     TokWords<NWTV> va[BPS][TPL], vb[BPS][TPL];
     constexpr unsigned kWaitVm0 = 0x0F70;     // vmcnt(0), expcnt(7), lgkmcnt(15)
@@ -1036,8 +1071,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
 #pragma unroll
       for (int b2 = 0; b2 < BPS; ++b2) {
         bcur[b2].phys = entry_at(0, b2);
-        issue_vregs(bcur[b2].phys, va[b2]);
-        issue_k2(bcur[b2].phys, b2);
+        issue_vregs(bcur[b2].phys, va[b2], rows_at(0, b2));
+        issue_k2(bcur[b2].phys, b2, rows_at(0, b2));
         issue_tok(bcur[b2].phys, b2);
         scales_of(bcur[b2]);
       }
@@ -1064,8 +1099,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
       if (more) {
 #pragma unroll
         for (int b2 = 0; b2 < BPS; ++b2) {
-          issue_vregs(bnext[b2].phys, vnext[b2]);
-          issue_k2(bnext[b2].phys, ((t + 1) & 1) * BPS + b2);
+          issue_vregs(bnext[b2].phys, vnext[b2], rows_at(t + 1, b2));
+          issue_k2(bnext[b2].phys, ((t + 1) & 1) * BPS + b2, rows_at(t + 1, b2));
           issue_tok(bnext[b2].phys, ((t + 1) & 1) * BPS + b2);
         }
       }

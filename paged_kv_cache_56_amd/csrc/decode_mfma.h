@@ -315,10 +315,11 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
       if (VQ && a.v_tok && lane < 4) lds_dma16(a.v_scales + si, (uint32_t)(lane * 16), dst + 64);
     }
   };
-  auto issue_v = [&](int phys_raw, VRows<VW>& vr) __attribute__((always_inline)) {
+  // nv: token rows of the block to fetch (SeqSpan::rows); lanes of rows
+  // past it load nothing.
+  auto issue_v = [&](int phys_raw, VRows<VW>& vr, int nv) __attribute__((always_inline)) {
     const char* src = vbase + vtile_of(phys_raw);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    auto load = [&](int i) __attribute__((always_inline)) {
       if constexpr (VW == 4) {
         const u32x4_t x = __builtin_nontemporal_load((const u32x4_t*)(src + voff[i]));
         vr.w[i][0] = x[0]; vr.w[i][1] = x[1]; vr.w[i][2] = x[2]; vr.w[i][3] = x[3];
@@ -326,14 +327,32 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
         const u32x2_t x = __builtin_nontemporal_load((const u32x2_t*)(src + voff[i]));
         vr.w[i][0] = x[0]; vr.w[i][1] = x[1];
       }
+    };
+    if (nv >= 16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load(i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (lg * 4 + i < nv) load(i);
     }
   };
   const uint32_t kslot0 = lds_offset(smem) + (uint32_t)(w * KR * TILE_B);
-  auto issue_k = [&](int phys_raw, int sk) __attribute__((always_inline)) {
+  // nv as for issue_v: a copy's lanes of rows past it copy nothing (the
+  // slot keeps older bytes there, which compute_block never uses).
+  auto issue_k = [&](int phys_raw, int sk, int nv) __attribute__((always_inline)) {
     const char* src = kbase + tile_of(phys_raw);
     const uint32_t dst = kslot0 + (uint32_t)(sk * TILE_B);
+    if (nv >= 16) {
 #pragma unroll
-    for (int n = 0; n < NDMA; ++n) lds_dma16(src, dma_off[n], dst + n * 1024);
+      for (int n = 0; n < NDMA; ++n) lds_dma16(src, dma_off[n], dst + n * 1024);
+    } else {
+#pragma unroll
+      for (int n = 0; n < NDMA; ++n) {
+        const int row = EB == 2 ? n * 4 + lg : n * 8 + (lane >> 3);   // as in dma_off
+        if (row < nv) lds_dma16(src, dma_off[n], dst + n * 1024);
+      }
+    }
   };
   auto read_k = [&](int sk, u32x4_t (&kr)[KREADS]) __attribute__((always_inline)) {
     uint32_t addr[KREADS];
@@ -424,8 +443,9 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
     BlockRef bcur{-1, 1.f, 1.f}, bnext{-1, 1.f, 1.f};
     if (n_my > 0) {
       bcur.phys = entry_of(blk(0));
-      issue_v(bcur.phys, va);
-      issue_k(bcur.phys, 0);
+      const int nv = span.rows(span.logical(blk(0)));
+      issue_v(bcur.phys, va, nv);
+      issue_k(bcur.phys, 0, nv);
       issue_tok(bcur.phys, 0);
       scales_of(bcur);
       if (n_my > 1) bnext.phys = entry_of(blk(1));
@@ -438,8 +458,9 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
       const BlockRef b0 = bcur;
       const bool more = t + 1 < n_my;
       if (more) {
-        issue_v(bnext.phys, vnext);
-        issue_k(bnext.phys, (t + 1) & 1);
+        const int nv = span.rows(span.logical(blk(t + 1)));
+        issue_v(bnext.phys, vnext, nv);
+        issue_k(bnext.phys, (t + 1) & 1, nv);
         issue_tok(bnext.phys, (t + 1) & 1);
       }
       u32x4_t kr[KREADS];

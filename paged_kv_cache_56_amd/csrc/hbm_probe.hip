@@ -51,9 +51,11 @@ int launch_hbm_read(const void* buf, size_t bytes, uint32_t* sink, int sink_word
 // ring by non-temporal LDS DMA, 1 KiB per wave instruction, and V's tile
 // is read into registers by non-temporal loads, four rows per wave
 // instruction, one block ahead of the one being consumed; the table entry
-// of the next block is read as a scalar load.  Consuming a block is
-// reading the lane's 32 channels of K back from LDS and folding them and
-// the V words into one word, which each wave adds to sink[workgroup].
+// of the next block is read as a scalar load.  Only the token rows that
+// hold a token are fetched (all 16 but in a sequence's last block).
+// Consuming a block is reading the lane's 32 channels of K back from LDS
+// and folding them and the V words of those rows into one word, which
+// each wave adds to sink[workgroup].
 // head_dim 128; tiles of 16-bit (EB = 2) or 8-bit (EB = 1) elements.
 template <int EB>
 __global__ void __launch_bounds__(256) paged_read_probe_kernel(DecodeArgs a, uint32_t* __restrict__ sink) {
@@ -96,13 +98,27 @@ __global__ void __launch_bounds__(256) paged_read_probe_kernel(DecodeArgs a, uin
     else kaddr[k] = slot0 + (uint32_t)(lq * 128 + (((lg * 2 + k) ^ (lq >> 1)) & 7) * 16);
   }
   typedef uint32_t VRow[4][VW];
-  auto issue = [&](int64_t off, int sk, VRow& v) __attribute__((always_inline)) {
+  // rows of block j that hold a token: only those are fetched, as the
+  // decode pass does
+  auto rows_of = [&](int j) __attribute__((always_inline)) {
+    const int n = L - j * 16;
+    return n < 0 ? 0 : (n > 16 ? 16 : n);
+  };
+  auto issue = [&](int64_t off, int sk, VRow& v, int nv) __attribute__((always_inline)) {
     const char* k = (const char*)a.k_cache + off;
 #pragma unroll
-    for (int n = 0; n < NDMA; ++n) lds_dma16(k, dma_off[n], slot0 + sk * TILE_B + n * 1024);
+    for (int n = 0; n < NDMA; ++n) {
+      const int row = EB == 2 ? n * 4 + lg : n * 8 + (lane >> 3);   // as in dma_off
+      if (nv >= 16 || row < nv) lds_dma16(k, dma_off[n], slot0 + sk * TILE_B + n * 1024);
+    }
     const char* vsrc = (const char*)a.v_cache + off;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      if (nv < 16 && lg * 4 + i >= nv) {
+#pragma unroll
+        for (int q = 0; q < VW; ++q) v[i][q] = 0u;
+        continue;
+      }
       const uint32_t o = (uint32_t)((lg * 4 + i) * ROW_B + lq * 8 * EB);
       if constexpr (VW == 4) {
         const u32x4_t x = __builtin_nontemporal_load((const u32x4_t*)(vsrc + o));
@@ -118,7 +134,7 @@ __global__ void __launch_bounds__(256) paged_read_probe_kernel(DecodeArgs a, uin
   int64_t next = 0;
   VRow va, vb;
   if (n_my > 0) {
-    issue(tile(parts.j0 + w), 0, va);
+    issue(tile(parts.j0 + w), 0, va, rows_of(parts.j0 + w));
     if (n_my > 1) next = tile(parts.j0 + w + NW);
   }
   // step t: wait for everything (block t is the newest load in flight),
@@ -127,7 +143,7 @@ __global__ void __launch_bounds__(256) paged_read_probe_kernel(DecodeArgs a, uin
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     wait_vmcnt<0>();
     if (t + 1 < n_my) {
-      issue(next, (t + 1) & 1, vnext);
+      issue(next, (t + 1) & 1, vnext, rows_of(parts.j0 + w + (t + 1) * NW));
       if (t + 2 < n_my) next = tile(parts.j0 + w + (t + 2) * NW);
     }
     uint32_t addr[KREADS];
@@ -135,8 +151,9 @@ __global__ void __launch_bounds__(256) paged_read_probe_kernel(DecodeArgs a, uin
     for (int k = 0; k < KREADS; ++k) addr[k] = kaddr[k] + (uint32_t)((t & 1) * TILE_B);
     u32x4_t kr[KREADS];
     lds_read16_wait<KREADS>(kr, addr);
+    if (lq < rows_of(parts.j0 + w + t * NW))        // the lane's K row holds a token
 #pragma unroll
-    for (int k = 0; k < KREADS; ++k) acc ^= kr[k][0] ^ kr[k][1] ^ kr[k][2] ^ kr[k][3];
+      for (int k = 0; k < KREADS; ++k) acc ^= kr[k][0] ^ kr[k][1] ^ kr[k][2] ^ kr[k][3];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll

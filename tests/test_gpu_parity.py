@@ -1050,9 +1050,9 @@ def _compact_rows(x, layer, lay, seqs):
                                      ("long_fp8_small", 64), ("ragged_bf16k_fp8v_g4_d128", 5)])
 def test_paged_read_probe_reads_exactly_the_attended_tiles(case, pb):
     """The access-pattern probe reads, per workgroup (sequence, KV head,
-    partition), every 32-bit word of the K and V tiles of the blocks that
-    partition covers and nothing else: its sink equals the XOR of exactly
-    those words, computed on the host."""
+    partition), every 32-bit word of the K and V rows that hold a token in
+    the blocks that partition covers and nothing else: its sink equals the
+    XOR of exactly those words, computed on the host."""
     spec = SMALL[case]
     if spec.kv_dtype != spec.v_tag:
         spec = scaled(spec, v_dtype=None)            # the probe reads K and V of one width
@@ -1079,7 +1079,9 @@ def test_paged_read_probe_reads_exactly_the_attended_tiles(case, pb):
                 acc = np.int32(0)
                 for j in range(p * per, min(p * per + per, natt)):
                     blk = int(lay.block_tables[b, j])
-                    acc ^= np.bitwise_xor.reduce(kw[blk, h].ravel()) ^ np.bitwise_xor.reduce(vw[blk, h].ravel())
+                    nv = min(16, int(lay.context_lens[b]) - 16 * j)     # rows holding a token
+                    acc ^= (np.bitwise_xor.reduce(kw[blk, h, :nv].ravel()) ^
+                            np.bitwise_xor.reduce(vw[blk, h, :nv].ravel()))
                 want[(b * spec.num_kv_heads + h) * P + p] = acc
     assert np.array_equal(sink.cpu().numpy(), want)
 
