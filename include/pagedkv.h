@@ -438,8 +438,12 @@ PKV_API int pkv_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, in
  * through the block table from scattered places).  Same grid and
  * partition plan as the attention call for `dims`, the same per-wave
  * order of blocks, K tiles copied into LDS by non-temporal DMA and V tiles
- * read into registers by non-temporal loads one block ahead; each
- * workgroup folds what it read into sink[(b * Hkv + h) * P + p]
+ * read into registers one block ahead (non-temporal loads when the
+ * attention call takes its matrix-core pass, head_dim 128 with 4 or 8
+ * query heads per KV head; ordinary loads otherwise, as its vector pass
+ * does); only the token rows that hold a token are fetched (all 16 but in
+ * a sequence's last block).  Each workgroup folds what it read into
+ * sink[(b * Hkv + h) * P + p]
  * (uint32 device array of num_seqs * num_kv_heads *
  * pkv_decode_num_partitions(dims) words, caller-zeroed if the value
  * matters).  head_dim 128; kv_dtype F16, BF16, FP8_E4M3 or INT8 for both

@@ -56,8 +56,13 @@ int launch_hbm_read(const void* buf, size_t bytes, uint32_t* sink, int sink_word
 // Consuming a block is reading the lane's 32 channels of K back from LDS
 // and folding them and the V words of those rows into one word, which
 // each wave adds to sink[workgroup].
-// head_dim 128; tiles of 16-bit (EB = 2) or 8-bit (EB = 1) elements.
-template <int EB>
+// head_dim 128; tiles of 16-bit (EB = 2) or 8-bit (EB = 1) elements.  V's
+// loads take the cache policy of the pass the attention launch runs for
+// the same shape: non-temporal (NTV) for the matrix-core pass (4 or 8
+// query heads per KV head), the default policy for the vector pass, whose
+// V loads are ordinary (a repeated batch then finds part of V in the
+// last-level cache).
+template <int EB, bool NTV>
 __global__ void __launch_bounds__(256) paged_read_probe_kernel(DecodeArgs a, uint32_t* __restrict__ sink) {
   constexpr int D = 128, ROW_B = D * EB, TILE_B = 16 * ROW_B, NDMA = TILE_B / 1024;
   constexpr int KREADS = 2 * EB, VW = 2 * EB, NW = 4, KR = 2;
@@ -121,10 +126,12 @@ __global__ void __launch_bounds__(256) paged_read_probe_kernel(DecodeArgs a, uin
       }
       const uint32_t o = (uint32_t)((lg * 4 + i) * ROW_B + lq * 8 * EB);
       if constexpr (VW == 4) {
-        const u32x4_t x = __builtin_nontemporal_load((const u32x4_t*)(vsrc + o));
+        const u32x4_t x = NTV ? __builtin_nontemporal_load((const u32x4_t*)(vsrc + o))
+                              : *(const u32x4_t*)(vsrc + o);
         v[i][0] = x[0]; v[i][1] = x[1]; v[i][2] = x[2]; v[i][3] = x[3];
       } else {
-        const u32x2_t x = __builtin_nontemporal_load((const u32x2_t*)(vsrc + o));
+        const u32x2_t x = NTV ? __builtin_nontemporal_load((const u32x2_t*)(vsrc + o))
+                              : *(const u32x2_t*)(vsrc + o);
         v[i][0] = x[0]; v[i][1] = x[1];
       }
     }
@@ -173,10 +180,17 @@ int launch_paged_read_probe(const DecodeArgs& a, uint32_t* sink, hipStream_t str
   const int64_t n = (int64_t)a.num_parts * a.num_kv_heads * a.num_seqs;
   if (n > 0x7FFFFFFF) return PKV_ERR_SHAPE;
   const dim3 grid((unsigned)n);
-  if (a.kv_dtype == PKV_FP8_E4M3 || a.kv_dtype == PKV_INT8)
-    hipLaunchKernelGGL((paged_read_probe_kernel<1>), grid, dim3(256), 0, stream, a, sink);
+  const int g = a.num_kv_heads > 0 ? a.num_q_heads / a.num_kv_heads : 0;
+  const bool matrix_core_pass = a.head_dim == 128 && (g == 4 || g == 8);
+  const bool eight_bit = a.kv_dtype == PKV_FP8_E4M3 || a.kv_dtype == PKV_INT8;
+  if (eight_bit && matrix_core_pass)
+    hipLaunchKernelGGL((paged_read_probe_kernel<1, true>), grid, dim3(256), 0, stream, a, sink);
+  else if (eight_bit)
+    hipLaunchKernelGGL((paged_read_probe_kernel<1, false>), grid, dim3(256), 0, stream, a, sink);
+  else if (matrix_core_pass)
+    hipLaunchKernelGGL((paged_read_probe_kernel<2, true>), grid, dim3(256), 0, stream, a, sink);
   else
-    hipLaunchKernelGGL((paged_read_probe_kernel<2>), grid, dim3(256), 0, stream, a, sink);
+    hipLaunchKernelGGL((paged_read_probe_kernel<2, false>), grid, dim3(256), 0, stream, a, sink);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
