@@ -1234,8 +1234,8 @@ struct PassLds {
 
 // Waves per SIMD the register allocation must allow.  The matrix-core
 // instantiations are held to three: the compiler then keeps their
-// accumulators in ordinary VGPRs (152 registers with 16-bit caches, 114
-// with 8-bit ones, no spills) instead of accumulator registers that the
+// accumulators in ordinary VGPRs (138 registers with 16-bit caches, 123
+// with 8-bit ones) instead of accumulator registers that the
 // per-tile rescale would copy out and back, 68 moves per tile.  Vector
 // instantiations for 8-bit caches with 8 query heads (two blocks per step)
 // are held to two; the others keep their natural allocation.
