@@ -800,16 +800,21 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
     float vsc = 1.f;
     if constexpr (KQ) cs *= br.ks;   // br.ks, br.vs: 1 with per-token scales
     if constexpr (VQ) vsc = br.vs;
-    // per-token scales of the lane's token rows (i ^ tmask) * R + r (1 otherwise)
+    // per-token scales of the lane's token rows (i ^ tmask) * R + r (1
+    // otherwise, and for a row that holds no attended token: its slot's
+    // scale may never have been written, and a NaN there would survive the
+    // zero probability it is multiplied with)
     float kt[TPL], vt[TPL];
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
       kt[i] = 1.f;
       vt[i] = 1.f;
       if constexpr (KQ || VQ) {
-        const float* ts = (const float*)(toks_area + sk * C::TOKS_B) + ((i ^ tmask) * R + r);
-        if (KQ && a.k_tok) kt[i] = ts[0];
-        if (VQ && a.v_tok) vt[i] = ts[16];
+        const int row = (i ^ tmask) * R + r;
+        const float* ts = (const float*)(toks_area + sk * C::TOKS_B) + row;
+        const bool live = (vbits >> row) & 1u;
+        if (KQ && a.k_tok && live) kt[i] = ts[0];
+        if (VQ && a.v_tok && live) vt[i] = ts[16];
       }
     }
 

@@ -371,7 +371,10 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
     float vsc = 1.f;
     if constexpr (KQ) cs *= br.ks * qfac;   // br.ks, br.vs: 1 with per-token scales
     if constexpr (VQ) vsc = br.vs;
-    // per-token scales of the lane's tokens 4 lg .. + 3 (1 otherwise)
+    // per-token scales of the lane's tokens 4 lg .. + 3 (1 otherwise).  A
+    // token outside the attended ones may have a scale slot never written:
+    // its score is selected to -inf below, its weight to 0, so a NaN there
+    // reaches neither.
     f32x4_t kt = {1.f, 1.f, 1.f, 1.f}, vt = {1.f, 1.f, 1.f, 1.f};
     if constexpr (KQ || VQ) {
       const char* ts = smem + C::KRING_B + (w * KR + sk) * C::TOKS_B + lg * 16;
@@ -420,6 +423,7 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
       const float pe = __builtin_amdgcn_exp2f(sc[i] - mo);
       lsum += pe;
       pv[i] = pe * vsc * vt[i];
+      if constexpr (VQ) pv[i] = ((mine >> i) & 1u) ? pv[i] : 0.f;
     }
     const u32x4_t pop = p_operand<MV>(pv);
     u32x4_t vop[8];

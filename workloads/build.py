@@ -22,7 +22,8 @@ Recipe (all seeded from the workload's seed):
     K/V are drawn in the query dtype and quantised on write, with its block's
     existing scale, by the step itself;
   * per-token scales (k_scale_tok / v_scale_tok): the same, with one scale
-    per (slot, kv_head), amax|x| / QMAX over that token's row; the new
+    per (slot, kv_head), amax|x| / QMAX over that token's row; a slot that
+    holds no token has a NaN scale (poisoned like its codes); the new
     token sets its own slot's scale when it is written;
   * a 16-bit K with an 8-bit V (kv_dtype f16/bf16, v_dtype fp8/int8): K is
     drawn as for a 16-bit cache, V quantised as above;
@@ -312,6 +313,8 @@ def _make_inputs(layout: DecodeLayout, device: str, layers: Optional[int]) -> Di
                 codes, s = quantize_tokens(x, tag) if tok else quantize_blocks(x, valid, tag)
                 del x
                 codes.masked_fill_(poison, _POISON[tag])
+                if tok:                       # a slot with no token has no scale either
+                    s.masked_fill_(~valid.view(NB, 1, bs), float("nan"))
                 cache[layer].copy_(codes)
                 sc[layer].copy_(s)
                 del codes
