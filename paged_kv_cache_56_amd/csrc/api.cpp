@@ -455,6 +455,7 @@ int pkv_paged_read_probe(const void* k_cache, const void* v_cache, const int32_t
   a.part_blocks = pb;
   a.num_parts = np;
   a.kv_dtype = dims->kv_dtype;
+  a.v_dtype = dims->kv_dtype;
   return launch_paged_read_probe(a, sink, stream);
 }
 
