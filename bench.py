@@ -568,8 +568,13 @@ def main():
     # so the split plan can balance uneven sequences
     total_blocks = int((-(-lay.context_lens.astype(np.int64) // 16)).sum())
     # shared prefixes: read once per group (the scheduler knows the groups)
-    grouped = (lay.group_starts is not None and not args.no_groups and args.window == 0
-               and spec.kv_dtype in ("f16", "bf16"))
+    # (16-bit caches, or K and V of one 8-bit format with per-block scales,
+    # a 16-bit q and out of one type, head_dim 128)
+    group_ok = spec.kv_dtype in ("f16", "bf16") or (
+        spec.k_quantised and spec.v_tag == spec.kv_dtype and not spec.k_outliers and not spec.fp_sinks
+        and not (spec.k_scale_tok or spec.v_scale_tok) and spec.q_dtype == spec.out_dtype
+        and spec.q_dtype in ("f16", "bf16") and spec.head_dim == 128)
+    grouped = (lay.group_starts is not None and not args.no_groups and args.window == 0 and group_ok)
     gkw = {}
     if grouped:
         gkw = dict(prefix_group_starts=x["group_starts"], prefix_group_blocks=x["group_blocks"],

@@ -55,7 +55,7 @@ extern "C" {
 #define PKV_API
 #endif
 
-#define PKV_VERSION 170  /* 1.7.0 */
+#define PKV_VERSION 180  /* 1.8.0 */
 #define PKV_BLOCK_SIZE 16
 /* Device scratch held by pkv_paged_decode_attn_noalloc, per device. */
 #define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
@@ -105,7 +105,7 @@ typedef struct {
                                   ceil(context_len / 16).  When the batch is much lighter
                                   than max_blocks_per_seq suggests, the split plan sizes
                                   its pieces from it; results do not depend on it */
-  int32_t prefix_groups;       /* G >= 0 shared-prefix groups (pkv_paged_decode_attn_prefix
+  int32_t prefix_groups;       /* G >= 0 shared-prefix groups (the _prefix entry points
                                   only; 0 everywhere else) */
   int32_t prefix_max_seqs;     /* with G > 0: >= the sequence count of every group */
   int32_t prefix_max_blocks;   /* with G > 0: >= every group's shared block count,
@@ -418,6 +418,52 @@ PKV_API int pkv_paged_decode_step_prefix(const void* k_new, const void* v_new,
                                          float scale, void* out, const pkv_decode_dims* dims,
                                          void* workspace, size_t workspace_bytes,
                                          hipStream_t stream);
+
+/*
+ * pkv_paged_decode_attn_prefix for an 8-bit cache ("The KV Cache memory
+ * ledger" 4 and 7: shared prefix blocks, and 8-bit K/V with one scale per
+ * (block, head)).  K and V both FP8_E4M3 or both INT8 (p->v_dtype =
+ * dims->kv_dtype) with one scale per (block, KV head) in p->k_scales and
+ * p->v_scales; no channel factors, per-token scales or sink tiles
+ * (p->k_channel_scales NULL, the per-token flags 0, dims->sink_tiles 0:
+ * -3 / -2 otherwise); q and out both F16 or both BF16; head_dim 128 (-2
+ * otherwise).  Groups as for pkv_paged_decode_attn_prefix.  The result is
+ * that of pkv_paged_decode_attn_quant.  Precision: the sequences' own
+ * blocks as stated for pkv_paged_decode_attn_fp8; in the shared part the
+ * codes are widened to f16 exactly, the query is rounded to f16 after a
+ * power-of-two rescale per query row (its largest element in [2^14, 2^15),
+ * so 11 significant bits for each element within 2^28 of that one), and
+ * each softmax weight times V's block scale enters the sum of V with about
+ * 22 significant bits.  Always splits (workspace > 0).
+ */
+PKV_API int pkv_paged_decode_attn_quant_prefix(const void* q, const void* k_cache, const void* v_cache,
+                                               const pkv_quant_params* p, const int32_t* group_seq_start,
+                                               const int32_t* group_prefix_blocks,
+                                               const int32_t* block_tables, const int32_t* context_lens,
+                                               float scale, void* out, const pkv_decode_dims* dims,
+                                               void* workspace, size_t workspace_bytes,
+                                               hipStream_t stream);
+
+/*
+ * One decode step for an 8-bit cache with shared-prefix groups, in one
+ * launch: the quantise-on-write append of pkv_paged_decode_step_quant
+ * (given block scales) followed by pkv_paged_decode_attn_quant_prefix
+ * ("KV Cache from first principles" 2.2-2.3; "The KV Cache memory ledger"
+ * 4 and 7).  Arguments are those two calls' together, with the limits of
+ * the latter; k_new and v_new are of q's dtype.  Each sequence's new token
+ * must lie past its group's shared blocks, as for
+ * pkv_paged_decode_step_prefix.  Codes and output equal those of the two
+ * calls.
+ */
+PKV_API int pkv_paged_decode_step_quant_prefix(const void* k_new, const void* v_new,
+                                               const int64_t* slot_mapping, const void* q, void* k_cache,
+                                               void* v_cache, const pkv_quant_params* p,
+                                               const int32_t* group_seq_start,
+                                               const int32_t* group_prefix_blocks,
+                                               const int32_t* block_tables, const int32_t* context_lens,
+                                               float scale, void* out, const pkv_decode_dims* dims,
+                                               void* workspace, size_t workspace_bytes,
+                                               hipStream_t stream);
 
 /*
  * Bandwidth reference ("KV Cache from first principles" 4.1: decode time is

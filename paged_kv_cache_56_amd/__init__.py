@@ -159,6 +159,12 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_paged_decode_attn_prefix.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
                                                  dims_p, vp, sz, vp]
     lib.pkv_paged_decode_attn_prefix.restype = ctypes.c_int
+    lib.pkv_paged_decode_attn_quant_prefix.argtypes = [vp, vp, vp, ctypes.POINTER(QuantParams), vp, vp, vp, vp,
+                                                       ctypes.c_float, vp, dims_p, vp, sz, vp]
+    lib.pkv_paged_decode_attn_quant_prefix.restype = ctypes.c_int
+    lib.pkv_paged_decode_step_quant_prefix.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(QuantParams), vp,
+                                                       vp, vp, vp, ctypes.c_float, vp, dims_p, vp, sz, vp]
+    lib.pkv_paged_decode_step_quant_prefix.restype = ctypes.c_int
     lib.pkv_paged_read_probe.argtypes = [vp, vp, vp, vp, dims_p, vp, vp]
     lib.pkv_paged_read_probe.restype = ctypes.c_int
     lib.pkv_hbm_read_probe.argtypes = [vp, sz, vp, i32, vp]
@@ -466,12 +472,15 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     when the call splits the context and none is given.  window > 0 limits each
     query to the last `window` positions plus the first `sinks` positions.
 
-    Shared prefixes (f16 or bf16 throughout): prefix_group_starts int32 [G + 1]
-    (nondecreasing; group g = sequences [starts[g], starts[g + 1])) and
-    prefix_group_blocks int32 [G] (the group's shared leading table entries,
-    full blocks) on the device, with host bounds prefix_max_seqs (>= every
-    group's size) and prefix_max_blocks (>= every count); the shared blocks
-    are then read once per group.  The result is the same attention.
+    Shared prefixes: prefix_group_starts int32 [G + 1] (nondecreasing; group g
+    = sequences [starts[g], starts[g + 1])) and prefix_group_blocks int32 [G]
+    (the group's shared leading table entries, full blocks) on the device,
+    with host bounds prefix_max_seqs (>= every group's size) and
+    prefix_max_blocks (>= every count); the shared blocks are then read once
+    per group.  The result is the same attention.  Caches f16 or bf16 with q
+    and out alike, or K and V of one 8-bit format with per-(block, head)
+    scales, q and out f16 or bf16, head_dim 128 (no channel factors,
+    per-token scales or sink tiles).
     """
     lib = load_library()
     _dev(q, k_cache, v_cache, block_tables, context_lens, out, k_scales, v_scales, k_channel_scales,
@@ -502,7 +511,8 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         _need(prefix_group_starts.dtype == prefix_group_blocks.dtype == torch.int32
               and prefix_group_blocks.dim() == 1 and prefix_group_starts.shape == (G + 1,),
               "prefix_group_starts must be int32 [G + 1] and prefix_group_blocks int32 [G]")
-        _need(kc == vc and kc in (1, 2), "shared prefixes need f16 or bf16 caches")
+        _need(kc == vc and (kc in (1, 2) or kc in _Q8),
+              "shared prefixes need f16 or bf16 caches, or K and V of one 8-bit format")
     dims = decode_dims(q, k_cache, block_tables, out, partition_blocks, window, sinks, side, total_blocks,
                        G, prefix_max_seqs if grouped else 0, prefix_max_blocks if grouped else 0)
     need = decode_workspace_bytes(dims)
@@ -523,7 +533,15 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         _need(k_channel_scales is None or (k8 and k_channel_scales.dtype == torch.float32 and
                                            k_channel_scales.shape == (k_cache.shape[1], k_cache.shape[3])),
               "k_channel_scales must be fp32 [Hkv, D], for an 8-bit K")
-        if kc == vc == 3 and k_channel_scales is None and not side and not (k_tok or v_tok):
+        if grouped:
+            qp = QuantParams(_ptr(k_scales), _ptr(v_scales), _ptr(k_channel_scales), vc,
+                             None, None, None, 0, k_tok, v_tok)
+            st = lib.pkv_paged_decode_attn_quant_prefix(_ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(qp),
+                                                        _ptr(prefix_group_starts), _ptr(prefix_group_blocks),
+                                                        _ptr(block_tables), _ptr(context_lens), float(scale),
+                                                        _ptr(out), ctypes.byref(dims), ws_ptr, ws_bytes,
+                                                        _stream(q))
+        elif kc == vc == 3 and k_channel_scales is None and not side and not (k_tok or v_tok):
             st = lib.pkv_paged_decode_attn_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales),
                                                _ptr(v_scales), _ptr(block_tables), _ptr(context_lens),
                                                float(scale), _ptr(out), ctypes.byref(dims), ws_ptr,
@@ -572,8 +590,9 @@ def paged_decode_step(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: to
     paged_decode_attn; each new token must then lie past its group's shared
     blocks.  8-bit caches (as in paged_decode_attn, no sink tiles): k_new and
     v_new in q's dtype, quantised on write with the blocks' given scales, or
-    setting their own slot's scale when the scales are per token.  Returns
-    `out`.
+    setting their own slot's scale when the scales are per token; with
+    shared-prefix groups, the limits paged_decode_attn states for them.
+    Returns `out`.
     """
     lib = load_library()
     _dev(k_new, v_new, slot_mapping, q, k_cache, v_cache, block_tables, context_lens, out, workspace,
@@ -584,9 +603,18 @@ def paged_decode_step(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: to
     _need(k_new.shape == v_new.shape == (B, k_cache.shape[1], k_cache.shape[3]),
           "k_new/v_new must be [B, Hkv, D]")
     kc, vc = _code(k_cache), _code(v_cache)
+    grouped = prefix_group_starts is not None or prefix_group_blocks is not None
+    G = 0
+    if grouped:
+        _need(prefix_group_starts is not None and prefix_group_blocks is not None,
+              "shared prefixes need prefix_group_starts and prefix_group_blocks")
+        G = prefix_group_blocks.numel()
+        _need(prefix_group_starts.dtype == prefix_group_blocks.dtype == torch.int32
+              and prefix_group_blocks.dim() == 1 and prefix_group_starts.shape == (G + 1,),
+              "prefix_group_starts must be int32 [G + 1] and prefix_group_blocks int32 [G]")
     if vc in _Q8:
         _need(k_new.dtype == v_new.dtype == q.dtype, "new rows of an 8-bit cache come in q's dtype")
-        _need(prefix_group_starts is None and prefix_group_blocks is None, "shared prefixes need 16-bit caches")
+        _need(not grouped or kc == vc, "shared prefixes need K and V of one 8-bit format")
         k8 = kc in _Q8
         _need(kc in _Q8 or kc == _code(q), "K and V caches differ in dtype")
         _need(v_scales is not None and (k_scales is not None) == k8,
@@ -598,17 +626,26 @@ def paged_decode_step(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: to
         _need(k_channel_scales is None or (k8 and k_channel_scales.dtype == torch.float32 and
                                            k_channel_scales.shape == (k_cache.shape[1], k_cache.shape[3])),
               "k_channel_scales must be fp32 [Hkv, D], for an 8-bit K")
-        dims = decode_dims(q, k_cache, block_tables, out, partition_blocks, window, sinks, False, total_blocks)
+        dims = decode_dims(q, k_cache, block_tables, out, partition_blocks, window, sinks, False, total_blocks,
+                           G, prefix_max_seqs if grouped else 0, prefix_max_blocks if grouped else 0)
         need = decode_workspace_bytes(dims)
         if need and workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         qp = QuantParams(_ptr(k_scales), _ptr(v_scales), _ptr(k_channel_scales), vc, None, None, None, 0,
                          int(k_scales is not None and k_scales.dim() == 3), int(v_scales.dim() == 3))
-        _check(lib.pkv_paged_decode_step_quant(
-            _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-            ctypes.byref(qp), _ptr(block_tables), _ptr(context_lens), float(scale), _ptr(out),
-            ctypes.byref(dims), _ptr(workspace) if need else None,
-            workspace.numel() * workspace.element_size() if need else 0, _stream(q)))
+        ws_ptr = _ptr(workspace) if need else None
+        ws_bytes = workspace.numel() * workspace.element_size() if need else 0
+        if grouped:
+            st = lib.pkv_paged_decode_step_quant_prefix(
+                _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                ctypes.byref(qp), _ptr(prefix_group_starts), _ptr(prefix_group_blocks), _ptr(block_tables),
+                _ptr(context_lens), float(scale), _ptr(out), ctypes.byref(dims), ws_ptr, ws_bytes, _stream(q))
+        else:
+            st = lib.pkv_paged_decode_step_quant(
+                _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                ctypes.byref(qp), _ptr(block_tables), _ptr(context_lens), float(scale), _ptr(out),
+                ctypes.byref(dims), ws_ptr, ws_bytes, _stream(q))
+        _check(st)
         return out
     _need(k_scales is None and v_scales is None and k_channel_scales is None,
           "scales apply to 8-bit caches only")
@@ -617,15 +654,6 @@ def paged_decode_step(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: to
     _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == B,
           "block_tables must be int32 [B, max_blocks]")
     _need(context_lens.dtype == torch.int32 and context_lens.shape == (B,), "context_lens must be int32 [B]")
-    grouped = prefix_group_starts is not None or prefix_group_blocks is not None
-    G = 0
-    if grouped:
-        _need(prefix_group_starts is not None and prefix_group_blocks is not None,
-              "shared prefixes need prefix_group_starts and prefix_group_blocks")
-        G = prefix_group_blocks.numel()
-        _need(prefix_group_starts.dtype == prefix_group_blocks.dtype == torch.int32
-              and prefix_group_blocks.dim() == 1 and prefix_group_starts.shape == (G + 1,),
-              "prefix_group_starts must be int32 [G + 1] and prefix_group_blocks int32 [G]")
     dims = decode_dims(q, k_cache, block_tables, out, partition_blocks, window, sinks, False, total_blocks,
                        G, prefix_max_seqs if grouped else 0, prefix_max_blocks if grouped else 0)
     need = decode_workspace_bytes(dims)

@@ -137,8 +137,18 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache, const
   if (!gp && dims->prefix_groups != 0) return PKV_ERR_SHAPE;   // groups: the _prefix entry point
   if (gp) {
     if (dims->prefix_groups > 0 && (!gp->seq_start || !gp->blocks)) return PKV_ERR_NULL;
-    if (qp) return PKV_ERR_DTYPE;
-    if (dims->kv_dtype != PKV_F16 && dims->kv_dtype != PKV_BF16) return PKV_ERR_DTYPE;
+    if (qp) {
+      // the group pass on 8-bit caches: K and V of one 8-bit format with one
+      // scale per (block, KV head), a 16-bit query and output of one type,
+      // head_dim 128, no full-precision sink tiles
+      if (!is_q8(dims->kv_dtype) || qp->v_dtype != dims->kv_dtype) return PKV_ERR_DTYPE;
+      if (qp->k_channel_scales || qp->k_scales_per_token || qp->v_scales_per_token) return PKV_ERR_DTYPE;
+      if (dims->q_dtype != dims->out_dtype || (dims->q_dtype != PKV_F16 && dims->q_dtype != PKV_BF16))
+        return PKV_ERR_DTYPE;
+      if (dims->head_dim != 128 || dims->sink_tiles) return PKV_ERR_SHAPE;
+    } else if (dims->kv_dtype != PKV_F16 && dims->kv_dtype != PKV_BF16) {
+      return PKV_ERR_DTYPE;
+    }
   }
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
   if (qp) {
@@ -419,6 +429,31 @@ int pkv_paged_decode_attn_prefix(const void* q, const void* k_cache, const void*
   const GroupPtrs gp{group_seq_start, group_prefix_blocks};
   return decode_common(q, k_cache, v_cache, nullptr, &gp, block_tables, context_lens, scale, out,
                        dims, workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_decode_attn_quant_prefix(const void* q, const void* k_cache, const void* v_cache,
+                                       const pkv_quant_params* p, const int32_t* group_seq_start,
+                                       const int32_t* group_prefix_blocks, const int32_t* block_tables,
+                                       const int32_t* context_lens, float scale, void* out,
+                                       const pkv_decode_dims* dims, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  if (!p) return PKV_ERR_NULL;
+  const GroupPtrs gp{group_seq_start, group_prefix_blocks};
+  return decode_common(q, k_cache, v_cache, p, &gp, block_tables, context_lens, scale, out, dims, workspace,
+                       workspace_bytes, stream);
+}
+
+int pkv_paged_decode_step_quant_prefix(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                                       const void* q, void* k_cache, void* v_cache, const pkv_quant_params* p,
+                                       const int32_t* group_seq_start, const int32_t* group_prefix_blocks,
+                                       const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                       void* out, const pkv_decode_dims* dims, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  if (!p) return PKV_ERR_NULL;
+  const StepAppend ap{k_new, v_new, slot_mapping, k_cache, v_cache};
+  const GroupPtrs gp{group_seq_start, group_prefix_blocks};
+  return decode_common(q, k_cache, v_cache, p, &gp, block_tables, context_lens, scale, out, dims, workspace,
+                       workspace_bytes, stream, &ap);
 }
 
 int pkv_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t sink_words,

@@ -159,11 +159,6 @@ __device__ __forceinline__ float load_elem_f32(const void* base, int64_t idx) {
   else return __builtin_bit_cast(float, ((uint32_t)((const uint16_t*)base)[idx]) << 16);
 }
 
-__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  const half2_t h = {(_Float16)lo, (_Float16)hi};   // one v_cvt_pk_f16_f32 (round to nearest even)
-  return __builtin_bit_cast(uint32_t, h);
-}
-
 // The lane's slice of one query row as fp32: elements (v * LPT + c) * E + e
 // for v < VPT, e < E (E consecutive elements per v, read 16 bytes at a time).
 template <KV QT, int EL, int LPT, int E, int VPT>
@@ -1261,18 +1256,23 @@ decode_partition_kernel(DecodeArgs a) {
 // Cache pass and shared-prefix group pass in one launch: the first
 // group_wgs workgroups run the group pass (matrix cores, latency-bound at
 // this size) while the rest stream the sequences' own blocks, so neither
-// waits for the other.  Both parts use the same LDS buffer.
-template <KV T, int D, int G>
+// waits for the other.  Both parts use the same LDS buffer.  T: the caches'
+// element type (K and V alike); QT: the query's and the output's.
+template <KV T, KV QT, int D, int G>
+struct GroupKernelLds {
+  static constexpr int value =
+      PassLds<T, T, D, G>::value > GroupLds<D>::BYTES ? PassLds<T, T, D, G>::value : GroupLds<D>::BYTES;
+};
+template <KV T, KV QT, int D, int G>
 __global__ void __launch_bounds__(256) decode_group_kernel(DecodeArgs a) {
-  static_assert(PassLds<T, T, D, G>::value >= GroupLds<D>::BYTES, "one LDS buffer serves both parts");
-  __shared__ __attribute__((aligned(16))) char smem[PassLds<T, T, D, G>::value];
+  __shared__ __attribute__((aligned(16))) char smem[GroupKernelLds<T, QT, D, G>::value];
   const int id = blockIdx.x;
   if (id < a.group_wgs) {
     const int pp = id % a.group_num_parts, rest = id / a.group_num_parts;
-    group_body<T, D>(a, pp, rest % a.num_kv_heads, rest / a.num_kv_heads, smem);
+    group_body<T, QT, D>(a, pp, rest % a.num_kv_heads, rest / a.num_kv_heads, smem);
   } else {
     const Unit u = unit_of(a, id - a.group_wgs);
-    cache_pass<T, T, T, T, D, G>(a, u.p, u.h, u.b, smem);
+    cache_pass<T, T, QT, QT, D, G>(a, u.p, u.h, u.b, smem);
   }
 }
 
@@ -1476,17 +1476,21 @@ size_t workspace_bytes_for(const pkv_decode_dims& d) {
 template <KV KT, KV VT, KV QT, KV OT, int D, int G>
 static int launch_typed(const DecodeArgs& a, hipStream_t stream) {
   constexpr bool plain16 = (KT == KV::F16 || KT == KV::BF16) && VT == KT && QT == KT && OT == KT;
-  if constexpr (plain16) {
+  // 8-bit caches with groups: K and V of one format, a 16-bit query and
+  // output of one type, head_dim 128
+  constexpr bool q8group = is_quantised<KT>() && VT == KT && QT == OT && (QT == KV::F16 || QT == KV::BF16) &&
+                           D == 128;
+  if constexpr (plain16 || q8group) {
     if (a.group_wgs > 0) {
       const int64_t n = (int64_t)a.group_wgs + (int64_t)a.num_parts * a.num_kv_heads * a.num_seqs;
-      hipLaunchKernelGGL((decode_group_kernel<KT, D, G>), dim3((unsigned)n), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((decode_group_kernel<KT, QT, D, G>), dim3((unsigned)n), dim3(256), 0, stream, a);
       if (hipGetLastError() != hipSuccess) return PKV_ERR_LAUNCH;
       hipLaunchKernelGGL((lse_merge_kernel<QT, OT, D>), dim3(a.num_seqs * a.num_q_heads), dim3(64), 0,
                          stream, a);
       return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
     }
   }
-  if (a.group_wgs > 0) return PKV_ERR_DTYPE;   // groups run with 16-bit caches only
+  if (a.group_wgs > 0) return PKV_ERR_DTYPE;   // no group pass for this type combination
   const int64_t n = (int64_t)a.num_parts * a.num_kv_heads * a.num_seqs;
   if (n > 0x7FFFFFFF) return PKV_ERR_SHAPE;
   hipLaunchKernelGGL((decode_partition_kernel<KT, VT, QT, OT, D, G>), dim3((unsigned)n), dim3(256), 0, stream, a);

@@ -39,6 +39,15 @@
 // operand type plus the rounding remainder, itself rounded: about 22
 // significant bits with f16 operands, 16 with bf16.  The running sum adds
 // the fp32 probabilities.
+//
+// 8-bit caches ("The KV Cache memory ledger" 7: FP8 K/V with one scale per
+// (block, head); e4m3 or int8 codes, K and V of one format).  The codes
+// are widened to f16 exactly as a step is staged in LDS, and both products
+// run on f16 operands.  The query is held in f16 after a power-of-two
+// rescale per query row (its largest element lands in [2^14, 2^15)); the
+// scores undo it together with the block's K scale, and each probability
+// enters P.V times the block's V scale (the running sum adds the
+// probabilities themselves).
 #pragma once
 
 #include "pkv_internal.h"
@@ -100,13 +109,42 @@ template <int D> struct GroupLds {
   static constexpr int BYTES = (32 * KS + D * VS) * 2;
 };
 
+// 16 codes (one 16-byte chunk of an 8-bit tile row) -> 16 f16 values, two
+// to a word, element 0 in the low half of word 0.  Exact: every e4m3 value
+// and every integer of magnitude <= 128 is an f16 value.
+template <KV T>
+__device__ __forceinline__ void widen16(const u32x4_t& c, uint32_t (&h)[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if constexpr (T == KV::FP8) {
+      h[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[k], 1.0f, false));
+      h[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[k], 1.0f, true));
+    } else {
+      uint16_t e[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        e[u] = __builtin_bit_cast(uint16_t, (_Float16)(int8_t)(uint8_t)(c[k] >> (8 * u)));
+      h[2 * k] = e[0] | ((uint32_t)e[1] << 16);
+      h[2 * k + 1] = e[2] | ((uint32_t)e[3] << 16);
+    }
+  }
+}
+
 // One workgroup of the group pass: piece pp of the shared blocks of group
 // z / group_qchunks, KV head h, query chunk z % group_qchunks; smem holds
-// at least GroupLds<D>::BYTES bytes.
-template <KV T, int D>
+// at least GroupLds<D>::BYTES bytes.  T: the caches' element type (f16,
+// bf16, or 8-bit codes with one scale per (block, KV head)); QT: the
+// query's (T itself for 16-bit caches; f16 or bf16 for 8-bit ones).
+template <KV T, KV QT, int D>
 __device__ __forceinline__ void group_body(const DecodeArgs& a, int pp, int h, int z, char* smem) {
+  constexpr bool Q8 = is_quantised<T>();
+  static_assert(Q8 || QT == T, "a 16-bit cache takes a query of its own type");
+  static_assert(QT == KV::F16 || QT == KV::BF16, "a 16-bit query");
+  constexpr KV MT = Q8 ? KV::F16 : T;  // operand type of both products
+  constexpr int EB = kv_bytes<T>::value;
+  constexpr int EPC = 16 / EB;         // elements per 16-byte chunk
   constexpr int KS = GroupLds<D>::KS, VS = GroupLds<D>::VS;
-  constexpr int CH = D / 8;            // 16-byte chunks per token row
+  constexpr int CH = D / EPC;          // 16-byte chunks per token row
   constexpr int NL = 32 * CH / 256;    // chunks per thread per 32-token step
   constexpr int KK = D / 32;           // contraction steps over the head dimension
   constexpr int DT = D / 16;           // 16-channel output tiles
@@ -133,12 +171,37 @@ __device__ __forceinline__ void group_body(const DecodeArgs& a, int pp, int h, i
   const int L = rv ? max(a.context_lens[b], 0) : 0;
 
   // B operand of S^T = K Q^T: lane holds q[row lq][kk*32 + 8*lg .. +7]
+  // (8-bit caches: rescaled by 2^qexp into f16, and qinv = 2^-qexp)
   u32x4_t qf[KK];
+  float qinv = 1.f;
   {
     const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)b * a.num_q_heads + head) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       qf[kk] = rv ? *(const u32x4_t*)(qrow + kk * 32 + 8 * lg) : u32x4_t{0u, 0u, 0u, 0u};
+    if constexpr (Q8) {
+      float f[KK][8];
+      float mq = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          f[kk][2 * k] = QT == KV::F16 ? f16lo(qf[kk][k]) : bf16lo(qf[kk][k]);
+          f[kk][2 * k + 1] = QT == KV::F16 ? f16hi(qf[kk][k]) : bf16hi(qf[kk][k]);
+          mq = fmaxf(mq, fmaxf(fabsf(f[kk][2 * k]), fabsf(f[kk][2 * k + 1])));
+        }
+      mq = across_rows<16, true>(mq);          // the row's four lane groups
+      int ex;
+      (void)__builtin_frexpf(mq, &ex);
+      int qexp = mq > 0.f ? 15 - ex : 0;
+      qexp = qexp > 100 ? 100 : (qexp < -100 ? -100 : qexp);
+      qinv = __builtin_ldexpf(1.0f, -qexp);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          qf[kk][k] = pack_f16x2(__builtin_ldexpf(f[kk][2 * k], qexp), __builtin_ldexpf(f[kk][2 * k + 1], qexp));
+    }
   }
 
   const int32_t* table = a.block_tables + (int64_t)pg.s0 * a.max_blocks;
@@ -156,21 +219,36 @@ __device__ __forceinline__ void group_body(const DecodeArgs& a, int pp, int h, i
   // block, bit 1: second), taken when its table entries are read, so that
   // no table read (a scalar load, counted with the LDS reads) sits in the
   // compute.
+  // 8-bit caches: the step's two K and two V block scales travel with it
+  // (scalar loads next to its table entries).
+  struct StepScales { float k[2], v[2]; };
   u32x4_t kreg[PF][NL], vreg[PF][NL];
   int okb[PF];
-  auto load_step = [&](int i, u32x4_t (&kr)[NL], u32x4_t (&vr)[NL], int& ok) __attribute__((always_inline)) {
+  StepScales scb[PF];
+  auto load_step = [&](int i, u32x4_t (&kr)[NL], u32x4_t (&vr)[NL], int& ok, StepScales& sc)
+                       __attribute__((always_inline)) {
     const int j = parts.j0 + 2 * min(i, nsteps - 1);
     const int ph0 = table[j];
     const int ph1 = j + 1 < parts.j1 ? table[j + 1] : -1;
     ok = ((unsigned)ph0 < (unsigned)a.num_blocks ? 1 : 0) | ((unsigned)ph1 < (unsigned)a.num_blocks ? 2 : 0);
+    if constexpr (Q8) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        int ph = u == 0 ? ph0 : ph1;
+        ph = (unsigned)ph < (unsigned)a.num_blocks ? ph : 0;
+        const int64_t si = (int64_t)ph * a.num_kv_heads + h;
+        sc.k[u] = ((const __attribute__((address_space(4))) float*)a.k_scales)[si];
+        sc.v[u] = ((const __attribute__((address_space(4))) float*)a.v_scales)[si];
+      }
+    }
 #pragma unroll
     for (int e = 0; e < NL; ++e) {
       const int c = tid + 256 * e, t = c & 31, col = c >> 5;
       int ph = t < 16 ? ph0 : ph1;
       ph = (unsigned)ph < (unsigned)a.num_blocks ? ph : 0;
-      const int64_t off = (((int64_t)ph * a.num_kv_heads + h) * 16 + (t & 15)) * D + col * 8;
-      kr[e] = *(const u32x4_t*)((const uint16_t*)a.k_cache + off);
-      vr[e] = *(const u32x4_t*)((const uint16_t*)a.v_cache + off);
+      const int64_t off = ((((int64_t)ph * a.num_kv_heads + h) * 16 + (t & 15)) * D + col * EPC) * EB;
+      kr[e] = *(const u32x4_t*)((const char*)a.k_cache + off);
+      vr[e] = *(const u32x4_t*)((const char*)a.v_cache + off);
     }
   };
   auto store_step = [&](int ok, const u32x4_t (&kr)[NL], const u32x4_t (&vr)[NL]) __attribute__((always_inline)) {
@@ -180,13 +258,27 @@ __device__ __forceinline__ void group_body(const DecodeArgs& a, int pp, int h, i
     for (int e = 0; e < NL; ++e) {
       const int c = tid + 256 * e, t = c & 31, col = c >> 5;
       const bool ok = t < 16 ? ok0 : ok1;            // a missing block: zeros, never NaN
-      *(u32x4_t*)&ks[t * KS + col * 8] = ok ? kr[e] : zero;
-      const u32x4_t v = ok ? vr[e] : zero;
       const int vc = vt_col(t);
+      if constexpr (!Q8) {
+        *(u32x4_t*)&ks[t * KS + col * 8] = ok ? kr[e] : zero;
+        const u32x4_t v = ok ? vr[e] : zero;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        vt[(col * 8 + 2 * k) * VS + vc] = (uint16_t)(v[k] & 0xFFFFu);
-        vt[(col * 8 + 2 * k + 1) * VS + vc] = (uint16_t)(v[k] >> 16);
+        for (int k = 0; k < 4; ++k) {
+          vt[(col * 8 + 2 * k) * VS + vc] = (uint16_t)(v[k] & 0xFFFFu);
+          vt[(col * 8 + 2 * k + 1) * VS + vc] = (uint16_t)(v[k] >> 16);
+        }
+      } else {
+        // 16 codes: channels col * 16 .. + 15 of token t, widened to f16
+        uint32_t hk[8], hv[8];
+        widen16<T>(ok ? kr[e] : zero, hk);
+        widen16<T>(ok ? vr[e] : zero, hv);
+        *(u32x4_t*)&ks[t * KS + col * 16] = u32x4_t{hk[0], hk[1], hk[2], hk[3]};
+        *(u32x4_t*)&ks[t * KS + col * 16 + 8] = u32x4_t{hk[4], hk[5], hk[6], hk[7]};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          vt[(col * 16 + 2 * k) * VS + vc] = (uint16_t)(hv[k] & 0xFFFFu);
+          vt[(col * 16 + 2 * k + 1) * VS + vc] = (uint16_t)(hv[k] >> 16);
+        }
       }
     }
   };
@@ -202,7 +294,7 @@ __device__ __forceinline__ void group_body(const DecodeArgs& a, int pp, int h, i
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute_step = [&](int j, int ok) __attribute__((always_inline)) {
+  auto compute_step = [&](int j, int ok, const StepScales& sc) __attribute__((always_inline)) {
 
     // S^T tiles: lane holds (token 16*tt + 4*lg + i, query lq) in s[tt][i]
     f32x4_t s[2];
@@ -211,20 +303,23 @@ __device__ __forceinline__ void group_body(const DecodeArgs& a, int pp, int h, i
       s[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        s[tt] = Mma<T>::run(*(const u32x4_t*)&ks[(tt * 16 + lq) * KS + kk * 32 + 8 * lg], qf[kk], s[tt]);
+        s[tt] = Mma<MT>::run(*(const u32x4_t*)&ks[(tt * 16 + lq) * KS + kk * 32 + 8 * lg], qf[kk], s[tt]);
     }
     const bool ok0 = ok & 1, ok1 = ok & 2;
     float sv[8];
     float mx = -INFINITY;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < 2; ++tt) {
+      float cs = a.scale;                                      // log2 units
+      if constexpr (Q8) cs *= sc.k[tt] * qinv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int pos = (j + tt) * 16 + 4 * lg + i;
         const bool ok = (tt == 0 ? ok0 : ok1) && pos < L;
-        sv[tt * 4 + i] = ok ? s[tt][i] * a.scale : -INFINITY;   // log2 units
+        sv[tt * 4 + i] = ok ? s[tt][i] * cs : -INFINITY;
         mx = fmaxf(mx, sv[tt * 4 + i]);
       }
+    }
     if (__builtin_amdgcn_ballot_w64(mx > m + SLACK)) {         // uniform over the wave
       mx = across_rows<16, true>(mx);   // the query's four lane groups
       const float mn = fmaxf(m, mx);
@@ -244,41 +339,46 @@ __device__ __forceinline__ void group_body(const DecodeArgs& a, int pp, int h, i
       float r0, r1, e0, e1;
       const float p0 = sv[2 * k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[2 * k] - m);
       const float p1 = sv[2 * k + 1] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[2 * k + 1] - m);
-      pw[k] = Mma<T>::round(p0, &r0) | (Mma<T>::round(p1, &r1) << 16);
-      pr[k] = Mma<T>::round(p0 - r0, &e0) | (Mma<T>::round(p1 - r1, &e1) << 16);
       l += p0 + p1;
+      // weights of P.V: tokens 2k, 2k + 1 of the lane's 8 lie in tile k / 2
+      const float vsc = Q8 ? sc.v[k >> 1] : 1.f;
+      const float w0 = p0 * vsc, w1 = p1 * vsc;
+      pw[k] = Mma<MT>::round(w0, &r0) | (Mma<MT>::round(w1, &r1) << 16);
+      pr[k] = Mma<MT>::round(w0 - r0, &e0) | (Mma<MT>::round(w1 - r1, &e1) << 16);
     }
     const u32x4_t pb = {pw[0], pw[1], pw[2], pw[3]};
     const u32x4_t pl = {pr[0], pr[1], pr[2], pr[3]};
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const u32x4_t va = *(const u32x4_t*)&vt[(dt * 16 + lq) * VS + 8 * lg];
-      acc[dt] = Mma<T>::run(va, pl, Mma<T>::run(va, pb, acc[dt]));
+      acc[dt] = Mma<MT>::run(va, pl, Mma<MT>::run(va, pb, acc[dt]));
     }
   };
 
   // step i uses ring slot i % PF and refills it with step i + PF
-  auto step = [&](int i, u32x4_t (&kr)[NL], u32x4_t (&vr)[NL], int& okr) __attribute__((always_inline)) {
+  auto step = [&](int i, u32x4_t (&kr)[NL], u32x4_t (&vr)[NL], int& okr, StepScales& scr)
+                  __attribute__((always_inline)) {
     const int j = parts.j0 + 2 * i;
     const int ok = okr;
+    const StepScales sc = scr;
     __syncthreads();                      // the previous step's LDS reads are done
     store_step(ok, kr, vr);
     __syncthreads();
-    load_step(i + PF, kr, vr, okr);
-    if (wave_on) compute_step(j, ok);
+    load_step(i + PF, kr, vr, okr, scr);
+    if (wave_on) compute_step(j, ok, sc);
   };
 #pragma unroll
-  for (int s = 0; s < PF; ++s) load_step(s, kreg[s], vreg[s], okb[s]);
+  for (int s = 0; s < PF; ++s) load_step(s, kreg[s], vreg[s], okb[s], scb[s]);
   // whole rounds of PF steps carry no conditions, so every wait for a ring
   // slot leaves the PF - 1 younger slots in flight
   int i0 = 0;
   for (; i0 + PF <= nsteps; i0 += PF) {
 #pragma unroll
-    for (int s = 0; s < PF; ++s) step(i0 + s, kreg[s], vreg[s], okb[s]);
+    for (int s = 0; s < PF; ++s) step(i0 + s, kreg[s], vreg[s], okb[s], scb[s]);
   }
 #pragma unroll
   for (int s = 0; s < PF - 1; ++s)
-    if (i0 + s < nsteps) step(i0 + s, kreg[s], vreg[s], okb[s]);   // uniform over the workgroup
+    if (i0 + s < nsteps) step(i0 + s, kreg[s], vreg[s], okb[s], scb[s]);   // uniform over the workgroup
 
   // partial result of this piece: lane holds channels dt*16 + 4*lg + 0..3
   l = across_rows<16, false>(l);

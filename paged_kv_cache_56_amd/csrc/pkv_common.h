@@ -164,6 +164,13 @@ __device__ __forceinline__ float f16hi(uint32_t w) {
   return (float)__builtin_bit_cast(half2_t, w).y;
 }
 
+// Two fp32 values -> an f16 pair in one word (one v_cvt_pk_f16_f32, round to
+// nearest even), lo in the low half.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const half2_t h = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 // fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   uint32_t u = __builtin_bit_cast(uint32_t, x);

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
     lib = pkv.load_library()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pkv_version() == 170
+    assert lib.pkv_version() == 180
 
 
 def _dims(**kw):
@@ -338,3 +338,41 @@ def test_k16_v8_and_per_token_status_codes():
     assert call(fp8, 3, ks=FAKE, v_tok=2) == -2              # flags are 0 or 1
     assert call(fp8, 3, ks=FAKE, k_tok=-1) == -2
     assert call(fp8, 3, ks=None) == -1                       # an 8-bit K needs its scales
+
+
+def test_quant_prefix_status_codes():
+    """The group pass on 8-bit caches: K and V of one 8-bit format with
+    per-(block, head) scales, q and out f16 or bf16 alike, head_dim 128; no
+    channel factors, per-token scales or sink tiles.  All refused before
+    any launch; a valid call asks for its workspace."""
+    lib = pkv.load_library()
+
+    def call(dims, v_dtype, ks=FAKE, vs=FAKE, chan=None, k_tok=0, v_tok=0, starts=FAKE, step=False):
+        qp = pkv.QuantParams(ks and ks.value, vs and vs.value, chan and chan.value, v_dtype, None, None,
+                             None, 0, k_tok, v_tok)
+        if step:
+            return lib.pkv_paged_decode_step_quant_prefix(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(qp),
+                                                          starts, FAKE, FAKE, FAKE, ctypes.c_float(0.088),
+                                                          FAKE, ctypes.byref(dims), None, 0, None)
+        return lib.pkv_paged_decode_attn_quant_prefix(FAKE, FAKE, FAKE, ctypes.byref(qp), starts, FAKE, FAKE,
+                                                      FAKE, ctypes.c_float(0.088), FAKE, ctypes.byref(dims),
+                                                      None, 0, None)
+
+    ok = dict(num_seqs=64, num_q_heads=40, num_kv_heads=40, max_blocks_per_seq=100, prefix_groups=1,
+              prefix_max_seqs=64, prefix_max_blocks=75, kv_dtype=3, q_dtype=2, out_dtype=2)
+    d = _dims(**ok)
+    for step in (False, True):
+        assert call(d, 3, step=step) == -4                          # valid, but no workspace
+        assert call(d, 3, starts=None, step=step) == -1
+        assert call(d, 3, ks=None, step=step) == -1
+        assert call(d, 4, step=step) == -3                          # K fp8 with V int8
+        assert call(d, 3, chan=FAKE, step=step) == -3
+        assert call(d, 3, k_tok=1, step=step) == -3
+        assert call(d, 3, v_tok=1, step=step) == -3
+        assert call(_dims(**dict(ok, out_dtype=0)), 3, step=step) == -3        # out not q's type
+        assert call(_dims(**dict(ok, q_dtype=0, out_dtype=0)), 3, step=step) == -3
+        assert call(_dims(**dict(ok, head_dim=64)), 3, step=step) == -2
+        assert call(_dims(**dict(ok, kv_dtype=1, q_dtype=1, out_dtype=1)), 3, step=step) == -3
+    assert call(_dims(**dict(ok, kv_dtype=4)), 4) == -4             # int8 K and V: valid
+    # the same plan and workspace as the 16-bit group pass
+    assert pkv.decode_workspace_bytes(d) == 64 * 40 * (1 + 3) * (128 + 2) * 4

@@ -593,6 +593,21 @@ GROUPED = {
     "prefix_groups_f16_g1_d64": (
         _ragged("p5", "f16", "f16", "f16", 64, 1, [130, 145, 161, 177, 193, 1], 35, hkv=5, append=True),
         [0, 5, 5], [8, 0]),
+    # 8-bit caches: codes widened in the group pass, block scales on the scores and weights
+    "prefix_groups_fp8_g1_d128": (
+        _ragged("p6", "fp8_e4m3", "bf16", "bf16", 128, 1, [300, 200, 180, 50, 260, 90, 40, 20, 600, 17],
+                36, hkv=5, append=True),
+        [0, 3, 3, 7], [10, 0, 1]),
+    "prefix_groups_int8_g4_d128": (
+        _ragged("p7", "int8", "f16", "f16", 128, 4, [700, 650, 601, 599, 1000, 70, 35, 17, 16], 37, hkv=3),
+        [0, 4, 6], [37, 2]),
+    "prefix_two_chunks_fp8_g8_d128": (       # 10 sequences x 8 heads = 80 query rows
+        _ragged("p8", "fp8_e4m3", "f16", "f16", 128, 8, [400 + 37 * i for i in range(10)] + [5, 300],
+                38, append=True),
+        [0, 10], [23]),
+    "prefix_groups_int8_g2_d128_one_seq": (  # a one-sequence group and a 1-block group
+        _ragged("p9", "int8", "bf16", "bf16", 128, 2, [90, 130, 33, 34, 18, 257], 39, hkv=4, append=True),
+        [0, 1, 2, 6], [5, 1, 1]),
 }
 
 
@@ -701,13 +716,16 @@ def test_fused_step_matches_append_then_attend(case, pb, window, sinks, skip):
 
 
 @pytest.mark.parametrize("case", ["prefix_one_group_f16_g1", "prefix_groups_f16_g8_d128",
-                                  "prefix_two_chunks_f16_g8_d128", "prefix_groups_f16_g1_d64"])
+                                  "prefix_two_chunks_f16_g8_d128", "prefix_groups_f16_g1_d64",
+                                  "prefix_groups_fp8_g1_d128", "prefix_two_chunks_fp8_g8_d128",
+                                  "prefix_groups_int8_g2_d128_one_seq"])
 def test_fused_step_with_prefix_groups(case):
-    """pkv_paged_decode_step_prefix: the append carried by the launch that
-    reads shared prefixes once per group.  Every new token lies past its
-    group's shared blocks.  Caches equal the oracle's append bit for bit and
-    the output the oracle's attention over them (the oracle knows nothing
-    of groups)."""
+    """pkv_paged_decode_step_prefix (pkv_paged_decode_step_quant_prefix for
+    8-bit caches, quantising on write with the blocks' scales): the append
+    carried by the launch that reads shared prefixes once per group.  Every
+    new token lies past its group's shared blocks.  Caches (and scales)
+    equal the oracle's append bit for bit and the output the oracle's
+    attention over them (the oracle knows nothing of groups)."""
     from gpu_common import group_args
     spec, lay = _grouped_layout(case)
     assert spec.append
@@ -716,15 +734,20 @@ def test_fused_step_with_prefix_groups(case):
     x = make_host_inputs(lay)
     xs = _to_dev(x)
     out = _out(spec)
+    kw = {}
+    if spec.quantised:
+        kw = dict(k_scales=xs["k_scales"][0], v_scales=xs["v_scales"][0])
     pkv.paged_decode_step(xs["k_new"][0], xs["v_new"][0], xs["slot_mapping"], xs["q"][0], xs["k_cache"][0],
                           xs["v_cache"][0], xs["block_tables"], xs["context_lens"], spec.scale, out,
-                          **group_args(xs))
+                          **group_args(xs), **kw)
     torch.cuda.synchronize()
     h = host_layer(x, 0)
-    kc, vc, _, _ = oracle_append(h, spec, lay.slot_mapping)
-    for name, ref in (("k_cache", kc), ("v_cache", vc)):
+    kc, vc, ks, vs = oracle_append(h, spec, lay.slot_mapping)
+    for name, ref in (("k_cache", kc), ("v_cache", vc), ("k_scales", ks), ("v_scales", vs)):
+        if ref is None:
+            continue
         assert np.array_equal(host_storage(xs[name][0]).view(np.uint8), ref.view(np.uint8)), name
-    ref = oracle_attend(h, spec, kc, vc, None, None, lay.block_tables, lay.context_lens)
+    ref = oracle_attend(h, spec, kc, vc, ks, vs, lay.block_tables, lay.context_lens)
     tol = TOL[spec.kv_dtype]
     err = parity_err(out_f64(out), ref, spec.out_dtype, tol)
     say(f"    max|err| = {err:.3e} (tol {tol})")
@@ -1088,7 +1111,8 @@ def test_paged_read_probe_reads_exactly_the_attended_tiles(case, pb):
 
 @pytest.mark.parametrize("name", ["llama3_8b_bf16", "mha13b_prefix_f16", "mha13b_prefix_f16:grouped", "long_fp8",
                                   "llama70b_f16_80l", "llama70b_fp8_80l", "long_fp8k_int8v", "long_int8_kchan",
-                                  "long_bf16k_fp8v", "long_fp8_tok", "mha13b_prefix_bf16:grouped"])
+                                  "long_bf16k_fp8v", "long_fp8_tok", "mha13b_prefix_bf16:grouped",
+                                  "mha13b_prefix_fp8:grouped"])
 def test_full_size_sampled_rows(name):
     name, _, mode = name.partition(":")
     grouped = mode == "grouped"

@@ -106,6 +106,14 @@ WORKLOADS = {
         len_range=(50, 400), shared_prefix_tokens=1200, append=True,
         description="13B MHA bf16 layer, 64 seqs sharing a 1200-token prefix + U[50,400] suffix",
     ),
+    "mha13b_prefix_fp8": DecodeWorkload(
+        name="mha13b_prefix_fp8", seed=56011, num_layers=1, num_seqs=64,
+        num_q_heads=40, num_kv_heads=40, head_dim=128,
+        kv_dtype="fp8_e4m3", q_dtype="bf16", out_dtype="bf16",
+        len_range=(50, 400), shared_prefix_tokens=1200, append=True,
+        description="13B MHA layer with an FP8 e4m3 cache, bf16 q/out, 64 seqs sharing a 1200-token "
+                    "prefix + U[50,400] suffix",
+    ),
     "long_fp8": DecodeWorkload(
         name="long_fp8", seed=56004, num_layers=1, num_seqs=8,
         num_q_heads=32, num_kv_heads=8, head_dim=128,
