@@ -1263,8 +1263,20 @@ struct GroupKernelLds {
   static constexpr int value =
       PassLds<T, T, D, G>::value > GroupLds<D>::BYTES ? PassLds<T, T, D, G>::value : GroupLds<D>::BYTES;
 };
+// Waves per SIMD the group launch's registers must allow.  With 8-bit
+// caches its per-sequence workgroups are short chains of dependent round
+// trips moving half the bytes of 16-bit ones, so more of them resident pay:
+// held to four waves per SIMD (no spills; 13B MHA layer with an fp8 cache
+// 58.7 -> 53.2 us per layer cold, balanced A/B).  With 16-bit caches four
+// waves measured slower (63.0 -> 64.0 us), so they keep their natural
+// allocation (three).
+template <KV T>
+struct GroupMinWaves {
+  static constexpr int value = is_quantised<T>() ? 4 : 1;
+};
 template <KV T, KV QT, int D, int G>
-__global__ void __launch_bounds__(256) decode_group_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GroupMinWaves<T>::value)))
+decode_group_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[GroupKernelLds<T, QT, D, G>::value];
   const int id = blockIdx.x;
   if (id < a.group_wgs) {
