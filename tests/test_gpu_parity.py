@@ -647,9 +647,12 @@ def test_prefix_groups_match_oracle(case):
         assert max_err(got, out_f64(plain)) <= tol
 
 
-def test_prefix_groups_deterministic():
-    spec, lay = _grouped_layout("prefix_groups_f16_g8_d128")
-    say("[groups] run-to-run")
+@pytest.mark.parametrize("case", ["prefix_groups_f16_g8_d128", "prefix_groups_fp8_g1_d128"])
+def test_prefix_groups_deterministic(case):
+    """Two calls on the same inputs give bit-identical outputs (16-bit and
+    8-bit caches)."""
+    spec, lay = _grouped_layout(case)
+    say(f"[groups] run-to-run: {case}")
     xs = _to_dev(make_host_inputs(lay))
     outs = []
     for i in range(3):
