@@ -260,6 +260,9 @@ PKV_API int pkv_paged_decode_attn_noalloc(const void* q, const void* k_cache, co
  * range and keep fewer, and those more than 2^39 times smaller become 0.  Scores and sums are fp32; each
  * softmax weight enters the weighted sum of V with at least 11 significant
  * bits (about 22 at head_dim 128 with 4 or 8 query heads per KV head).
+ * Weights are formed as (probability <= 256) * V's scale and held in f16,
+ * so V's scales must stay below 255 (with scale = amax / 448: |V| below
+ * about 114000); beyond that a weight can overflow.
  */
 PKV_API int pkv_paged_decode_attn_fp8(const void* q, const void* k_cache, const void* v_cache,
                               const float* k_scales, const float* v_scales,
