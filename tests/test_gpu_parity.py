@@ -1007,20 +1007,23 @@ def test_lengths_past_the_table_are_clamped():
     assert parity_err(got, ref, "f16", TOL["f16"]) <= TOL["f16"]
 
 
-def test_group_descriptors_out_of_range_do_not_fault():
+@pytest.mark.parametrize("case", ["prefix_groups_f16_g8_d128", "prefix_two_chunks_fp8_g8_d128"])
+def test_group_descriptors_out_of_range_do_not_fault(case):
     """Unsorted or out-of-range group starts and oversized block counts give
     undefined numbers but every access stays in bounds (the counts are
-    clamped to the host bounds, the starts to [0, B])."""
-    spec, lay = _grouped_layout("prefix_groups_f16_g8_d128")
-    say("[bounds] group descriptors out of range")
+    clamped to the host bounds, the starts to [0, B]; with an 8-bit cache
+    the block scales are read through the same clamped ids)."""
+    spec, lay = _grouped_layout(case)
+    say(f"[bounds] group descriptors out of range: {case}")
     xs = _to_dev(make_host_inputs(lay))
     width = lay.block_tables.shape[1]
     starts = torch.tensor([5, -3, 100, 2, 7], dtype=torch.int32, device=DEV)
     blocks = torch.tensor([1000, -4, width, 3], dtype=torch.int32, device=DEV)
     out = _out(spec)
+    kw = dict(k_scales=xs["k_scales"][0], v_scales=xs["v_scales"][0]) if spec.quantised else {}
     pkv.paged_decode_attn(xs["q"][0], xs["k_cache"][0], xs["v_cache"][0], xs["block_tables"], xs["context_lens"],
                           spec.scale, out, prefix_group_starts=starts, prefix_group_blocks=blocks,
-                          prefix_max_seqs=12, prefix_max_blocks=width)
+                          prefix_max_seqs=12, prefix_max_blocks=width, **kw)
     torch.cuda.synchronize()
     assert out.shape == (spec.num_seqs, spec.num_q_heads, spec.head_dim)
 
