@@ -495,7 +495,10 @@ __device__ __forceinline__ void append_new_rows_q8(const DecodeArgs& a, int b, i
     y[e] = load_elem_f32<QT>(isv ? a.v_new : a.k_new, src + e);
     if (is_quantised<KT>() && !isv && a.k_chan) y[e] = y[e] / a.k_chan[(int64_t)h * D + e0 + e];
   }
-  const bool tok = isv ? a.v_tok : a.k_tok;
+  // both flags read, then a bit picked: a select between the two fields'
+  // addresses would put them in per-lane scratch memory
+  const int tok_bits = (a.k_tok ? 1 : 0) | (a.v_tok ? 2 : 0);
+  const bool tok = (tok_bits >> (isv ? 1 : 0)) & 1;
   float amax = 0.f;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(y[e]));
