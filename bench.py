@@ -687,7 +687,7 @@ def main():
 
     pat = None
     if (not args.no_probe and args.window == 0 and not spec.fp_sinks and spec.head_dim == 128
-            and ELT[spec.kv_dtype] == ELT[spec.v_tag]):
+            and ELT[spec.v_tag] <= ELT[spec.kv_dtype] <= 2):
         rows = None
         if grouped:
             # the group pass's pieces per group, from the workspace it is given

@@ -55,7 +55,7 @@ extern "C" {
 #define PKV_API
 #endif
 
-#define PKV_VERSION 180  /* 1.8.0 */
+#define PKV_VERSION 181  /* 1.8.1 */
 #define PKV_BLOCK_SIZE 16
 /* Device scratch held by pkv_paged_decode_attn_noalloc, per device. */
 #define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
@@ -495,12 +495,17 @@ PKV_API int pkv_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, in
  * sink[(b * Hkv + h) * P + p]
  * (uint32 device array of num_seqs * num_kv_heads *
  * pkv_decode_num_partitions(dims) words, caller-zeroed if the value
- * matters).  head_dim 128; kv_dtype F16, BF16, FP8_E4M3 or INT8 for both
- * caches; no window, sink tiles or groups.  Computes nothing else.
+ * matters).  head_dim 128; dims->kv_dtype is K's format and v_dtype V's,
+ * each F16, BF16, FP8_E4M3 or INT8, V no wider than K (a 16-bit K with an
+ * 8-bit V reads 2-byte K tiles and 1-byte V tiles, as the attention call
+ * does; per-token scales are not read); no window, sink tiles or groups.
+ * Computes nothing else.
+ * Errors: head_dim != 128, a window, sink tiles or groups -> PKV_ERR_SHAPE;
+ * a format outside that list or V wider than K -> PKV_ERR_DTYPE.
  */
 PKV_API int pkv_paged_read_probe(const void* k_cache, const void* v_cache, const int32_t* block_tables,
                                  const int32_t* context_lens, const pkv_decode_dims* dims,
-                                 uint32_t* sink, hipStream_t stream);
+                                 int32_t v_dtype, uint32_t* sink, hipStream_t stream);
 
 /*
  * Copy-on-write block copies ("Large-model inference KV Cache memory

@@ -165,7 +165,7 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_paged_decode_step_quant_prefix.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(QuantParams), vp,
                                                        vp, vp, vp, ctypes.c_float, vp, dims_p, vp, sz, vp]
     lib.pkv_paged_decode_step_quant_prefix.restype = ctypes.c_int
-    lib.pkv_paged_read_probe.argtypes = [vp, vp, vp, vp, dims_p, vp, vp]
+    lib.pkv_paged_read_probe.argtypes = [vp, vp, vp, vp, dims_p, i32, vp, vp]
     lib.pkv_paged_read_probe.restype = ctypes.c_int
     lib.pkv_hbm_read_probe.argtypes = [vp, sz, vp, i32, vp]
     lib.pkv_hbm_read_probe.restype = ctypes.c_int
@@ -432,14 +432,16 @@ def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
 def paged_read_probe(k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
                      context_lens: torch.Tensor, dims: DecodeDims, sink: torch.Tensor) -> None:
     """The attention call's memory traffic for `dims` without its arithmetic
-    (bandwidth reference); sink: int32 [B * Hkv * partitions] on the device."""
+    (bandwidth reference); sink: int32 [B * Hkv * partitions] on the device.
+    dims.kv_dtype is K's format; V's is taken from v_cache's dtype (a 16-bit
+    K may go with an 8-bit V)."""
     _dev(k_cache, v_cache, block_tables, context_lens, sink)
     _need(sink.dtype == torch.int32 and sink.dim() == 1 and
           sink.numel() >= dims.num_seqs * dims.num_kv_heads * decode_num_partitions(dims),
           "sink must be int32 [B * Hkv * partitions]")
     _check(load_library().pkv_paged_read_probe(_ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                                               _ptr(context_lens), ctypes.byref(dims), _ptr(sink),
-                                               _stream(k_cache)))
+                                               _ptr(context_lens), ctypes.byref(dims), _code(v_cache),
+                                               _ptr(sink), _stream(k_cache)))
 
 
 def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

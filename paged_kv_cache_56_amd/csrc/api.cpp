@@ -465,14 +465,14 @@ int pkv_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t si
 }
 
 int pkv_paged_read_probe(const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                         const int32_t* context_lens, const pkv_decode_dims* dims, uint32_t* sink,
-                         hipStream_t stream) {
+                         const int32_t* context_lens, const pkv_decode_dims* dims, int32_t v_dtype,
+                         uint32_t* sink, hipStream_t stream) {
   int st = check_dims(dims);
   if (st) return st;
   if (dims->head_dim != 128 || dims->window != 0 || dims->sink_tiles || dims->prefix_groups)
     return PKV_ERR_SHAPE;
-  const int eb = elem_bytes(dims->kv_dtype);
-  if (eb != 1 && eb != 2) return PKV_ERR_DTYPE;
+  const int eb = elem_bytes(dims->kv_dtype), veb = elem_bytes(v_dtype);
+  if ((eb != 1 && eb != 2) || (veb != 1 && veb != 2) || veb > eb) return PKV_ERR_DTYPE;
   if (!k_cache || !v_cache || !block_tables || !context_lens || !sink) return PKV_ERR_NULL;
   int pb, np;
   plan_partitions(*dims, &pb, &np);
@@ -490,7 +490,7 @@ int pkv_paged_read_probe(const void* k_cache, const void* v_cache, const int32_t
   a.part_blocks = pb;
   a.num_parts = np;
   a.kv_dtype = dims->kv_dtype;
-  a.v_dtype = dims->kv_dtype;
+  a.v_dtype = v_dtype;
   return launch_paged_read_probe(a, sink, stream);
 }
 

@@ -56,16 +56,19 @@ int launch_hbm_read(const void* buf, size_t bytes, uint32_t* sink, int sink_word
 // Consuming a block is reading the lane's 32 channels of K back from LDS
 // and folding them and the V words of those rows into one word, which
 // each wave adds to sink[workgroup].
-// head_dim 128; tiles of 16-bit (EB = 2) or 8-bit (EB = 1) elements.  V's
-// loads take the cache policy of the pass the attention launch runs for
+// head_dim 128; K tiles of 16-bit (KEB = 2) or 8-bit (KEB = 1) elements,
+// V tiles likewise (VEB), V no wider than K (a 16-bit K may go with an
+// 8-bit V, as the attention call allows).  V's loads take the cache policy of the pass the attention launch runs for
 // the same shape: non-temporal (NTV) for the matrix-core pass (4 or 8
 // query heads per KV head), the default policy for the vector pass, whose
 // V loads are ordinary (a repeated batch then finds part of V in the
 // last-level cache).
-template <int EB, bool NTV>
+template <int EB, int VEB, bool NTV>
 __global__ void __launch_bounds__(256) paged_read_probe_kernel(DecodeArgs a, uint32_t* __restrict__ sink) {
+  static_assert(VEB <= EB, "V is no wider than K");
   constexpr int D = 128, ROW_B = D * EB, TILE_B = 16 * ROW_B, NDMA = TILE_B / 1024;
-  constexpr int KREADS = 2 * EB, VW = 2 * EB, NW = 4, KR = 2;
+  constexpr int VROW_B = D * VEB, VTILE_B = 16 * VROW_B;
+  constexpr int KREADS = 2 * EB, VW = 2 * VEB, NW = 4, KR = 2;
   __shared__ __attribute__((aligned(16))) char ring[NW * KR * TILE_B];
   const Unit u = unit_of(a, blockIdx.x);
   const int p = u.p, h = u.h, b = u.b;
@@ -78,9 +81,11 @@ __global__ void __launch_bounds__(256) paged_read_probe_kernel(DecodeArgs a, uin
   const int n_my = w < nunits ? (nunits - w + NW - 1) / NW : 0;
   const __attribute__((address_space(4))) int32_t* table =
       (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)b * a.max_blocks);
+  // (block, head) index of logical block j; a tile's offset is that times
+  // the cache's tile bytes
   auto tile = [&](int j) __attribute__((always_inline)) {
     const int phys = table[j];
-    return ((int64_t)(((unsigned)phys < (unsigned)a.num_blocks) ? phys : 0) * a.num_kv_heads + h) * TILE_B;
+    return (int64_t)(((unsigned)phys < (unsigned)a.num_blocks) ? phys : 0) * a.num_kv_heads + h;
   };
   // the decode pass's LDS placement of K: HBM column x of row r at LDS
   // column x ^ f(r), so that a lane group's reads of one column of 16 rows
@@ -109,14 +114,14 @@ __global__ void __launch_bounds__(256) paged_read_probe_kernel(DecodeArgs a, uin
     const int n = L - j * 16;
     return n < 0 ? 0 : (n > 16 ? 16 : n);
   };
-  auto issue = [&](int64_t off, int sk, VRow& v, int nv) __attribute__((always_inline)) {
-    const char* k = (const char*)a.k_cache + off;
+  auto issue = [&](int64_t bh, int sk, VRow& v, int nv) __attribute__((always_inline)) {
+    const char* k = (const char*)a.k_cache + bh * TILE_B;
 #pragma unroll
     for (int n = 0; n < NDMA; ++n) {
       const int row = EB == 2 ? n * 4 + lg : n * 8 + (lane >> 3);   // as in dma_off
       if (nv >= 16 || row < nv) lds_dma16(k, dma_off[n], slot0 + sk * TILE_B + n * 1024);
     }
-    const char* vsrc = (const char*)a.v_cache + off;
+    const char* vsrc = (const char*)a.v_cache + bh * VTILE_B;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (nv < 16 && lg * 4 + i >= nv) {
@@ -124,7 +129,7 @@ __global__ void __launch_bounds__(256) paged_read_probe_kernel(DecodeArgs a, uin
         for (int q = 0; q < VW; ++q) v[i][q] = 0u;
         continue;
       }
-      const uint32_t o = (uint32_t)((lg * 4 + i) * ROW_B + lq * 8 * EB);
+      const uint32_t o = (uint32_t)((lg * 4 + i) * VROW_B + lq * 8 * VEB);
       if constexpr (VW == 4) {
         const u32x4_t x = NTV ? __builtin_nontemporal_load((const u32x4_t*)(vsrc + o))
                               : *(const u32x4_t*)(vsrc + o);
@@ -182,15 +187,26 @@ int launch_paged_read_probe(const DecodeArgs& a, uint32_t* sink, hipStream_t str
   const dim3 grid((unsigned)n);
   const int g = a.num_kv_heads > 0 ? a.num_q_heads / a.num_kv_heads : 0;
   const bool matrix_core_pass = a.head_dim == 128 && (g == 4 || g == 8);
-  const bool eight_bit = a.kv_dtype == PKV_FP8_E4M3 || a.kv_dtype == PKV_INT8;
-  if (eight_bit && matrix_core_pass)
-    hipLaunchKernelGGL((paged_read_probe_kernel<1, true>), grid, dim3(256), 0, stream, a, sink);
-  else if (eight_bit)
-    hipLaunchKernelGGL((paged_read_probe_kernel<1, false>), grid, dim3(256), 0, stream, a, sink);
-  else if (matrix_core_pass)
-    hipLaunchKernelGGL((paged_read_probe_kernel<2, true>), grid, dim3(256), 0, stream, a, sink);
-  else
-    hipLaunchKernelGGL((paged_read_probe_kernel<2, false>), grid, dim3(256), 0, stream, a, sink);
+  auto width = [](int dt) { return dt == PKV_FP8_E4M3 || dt == PKV_INT8 ? 1 : 2; };
+  const int keb = width(a.kv_dtype), veb = width(a.v_dtype);
+  if (keb == 1 && veb == 1) {
+    if (matrix_core_pass)
+      hipLaunchKernelGGL((paged_read_probe_kernel<1, 1, true>), grid, dim3(256), 0, stream, a, sink);
+    else
+      hipLaunchKernelGGL((paged_read_probe_kernel<1, 1, false>), grid, dim3(256), 0, stream, a, sink);
+  } else if (veb == 1) {
+    if (matrix_core_pass)
+      hipLaunchKernelGGL((paged_read_probe_kernel<2, 1, true>), grid, dim3(256), 0, stream, a, sink);
+    else
+      hipLaunchKernelGGL((paged_read_probe_kernel<2, 1, false>), grid, dim3(256), 0, stream, a, sink);
+  } else if (keb == 2) {
+    if (matrix_core_pass)
+      hipLaunchKernelGGL((paged_read_probe_kernel<2, 2, true>), grid, dim3(256), 0, stream, a, sink);
+    else
+      hipLaunchKernelGGL((paged_read_probe_kernel<2, 2, false>), grid, dim3(256), 0, stream, a, sink);
+  } else {
+    return PKV_ERR_DTYPE;   // V wider than K
+  }
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
     lib = pkv.load_library()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pkv_version() == 180
+    assert lib.pkv_version() == 181
 
 
 def _dims(**kw):
@@ -376,3 +376,20 @@ def test_quant_prefix_status_codes():
     assert call(_dims(**dict(ok, kv_dtype=4)), 4) == -4             # int8 K and V: valid
     # the same plan and workspace as the 16-bit group pass
     assert pkv.decode_workspace_bytes(d) == 64 * 40 * (1 + 3) * (128 + 2) * 4
+
+
+@pytest.mark.parametrize("kw,v_dtype,status", [
+    (dict(head_dim=64), 1, -2),                        # the probe is for head_dim 128
+    (dict(window=64), 1, -2),
+    (dict(kv_dtype=0, q_dtype=0, out_dtype=0), 0, -3),  # f32 tiles
+    (dict(kv_dtype=3), 1, -3),                         # V wider than K
+    (dict(kv_dtype=1), 7, -3),                         # no such format
+])
+def test_paged_read_probe_status_codes(kw, v_dtype, status):
+    lib = pkv.load_library()
+    dims = _dims(**kw)
+    assert lib.pkv_paged_read_probe(FAKE, FAKE, FAKE, FAKE, ctypes.byref(dims), v_dtype, FAKE, None) == status
+    if status == -3:
+        return
+    dims = _dims()
+    assert lib.pkv_paged_read_probe(None, FAKE, FAKE, FAKE, ctypes.byref(dims), 1, FAKE, None) == -1

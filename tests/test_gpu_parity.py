@@ -1076,15 +1076,14 @@ def _compact_rows(x, layer, lay, seqs):
 
 
 @pytest.mark.parametrize("case,pb", [("ragged_f16_g8_d128", 1000), ("ragged_f16_g8_d128", 3),
-                                     ("long_fp8_small", 64), ("ragged_bf16k_fp8v_g4_d128", 5)])
+                                     ("long_fp8_small", 64), ("ragged_bf16k_fp8v_g4_d128", 5),
+                                     ("ragged_bf16k_int8v_g1_d128_vtok_append", 4)])
 def test_paged_read_probe_reads_exactly_the_attended_tiles(case, pb):
     """The access-pattern probe reads, per workgroup (sequence, KV head,
     partition), every 32-bit word of the K and V rows that hold a token in
     the blocks that partition covers and nothing else: its sink equals the
     XOR of exactly those words, computed on the host."""
     spec = SMALL[case]
-    if spec.kv_dtype != spec.v_tag:
-        spec = scaled(spec, v_dtype=None)            # the probe reads K and V of one width
     lay = build_layout(spec)
     say(f"[probe] {case}: pb={pb} lens={list(lay.context_lens[:12])}")
     x = make_host_inputs(lay)
