@@ -98,11 +98,15 @@ struct SeqParts {
 // every sequence.  The sequence varying fastest instead, so that every XCD
 // takes all heads, measured no faster on the 70B-shaped step and 7-10 us
 // slower on the uneven Llama-3-8B and shared-prefix layers.)  The
-// exception is an 8-bit cache with one partition: there the sequence
-// varies fastest, so that one XCD reads every KV head of a block and each
-// 64-byte line of per-(block, head) scales once, where eight XCDs would
-// each fetch it for 4 bytes (70B-shaped fp8 step: 88.0 -> 86.9 us, HBM
-// traffic 1.03 -> 1.00 of the algorithmic bytes).
+// exception is an 8-bit cache with one partition and at most 8 KV heads:
+// there the sequence varies fastest, so that one XCD reads every KV head
+// of a block and each 64-byte line of per-(block, head) scales once, where
+// eight XCDs would each fetch it for 4 bytes (70B-shaped fp8 step: 88.0 ->
+// 86.9 us, HBM traffic 1.03 -> 1.00 of the algorithmic bytes).  With many
+// KV heads a block's tiles are better read together, by consecutive
+// workgroups, than the scale lines are shared (13B-shaped fp8 layer, 40
+// KV heads: 109.5 -> 92.2 us per layer, and 52.4 -> 48.0 us with the
+// shared-prefix pass).
 struct Unit { int p, h, b; };
 __device__ __forceinline__ Unit unit_of(const DecodeArgs& a, int k) {
   Unit u;
@@ -110,7 +114,7 @@ __device__ __forceinline__ Unit unit_of(const DecodeArgs& a, int k) {
   const int rest = k / a.num_parts;
   const bool eight_bit = a.kv_dtype == PKV_FP8_E4M3 || a.kv_dtype == PKV_INT8 ||
                          a.v_dtype == PKV_FP8_E4M3 || a.v_dtype == PKV_INT8;
-  if (eight_bit && a.num_parts == 1) {
+  if (eight_bit && a.num_parts == 1 && a.num_kv_heads <= 8) {
     u.b = rest % a.num_seqs;
     u.h = rest / a.num_seqs;
     return u;
