@@ -463,6 +463,12 @@ SMALL = {
                                                    outliers=3, ktok=True),
     "ragged_fp8_g8_d64_append_f32out": _ragged("r33", "fp8_e4m3", "f16", "f32", 64, 8, [5, 16, 17, 80, 33], 33,
                                                append=True),
+    # more than 8 KV heads with an 8-bit cache and one partition (the KV head
+    # is then the fastest workgroup index, as for 16-bit caches)
+    "ragged_fp8_g1_d128_h12_append": _ragged("r34", "fp8_e4m3", "f16", "f16", 128, 1,
+                                             [1, 16, 17, 200, 33, 48, 49], 51, hkv=12, append=True),
+    "ragged_int8_g2_d64_h10": _ragged("r35", "int8", "bf16", "bf16", 64, 2, [1, 15, 16, 17, 31, 33, 100, 0, 64, 130],
+                                      52, hkv=10),
 }
 
 
