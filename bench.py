@@ -375,12 +375,22 @@ def summarize_counters(fetch_csv, write_csv, stats_csv, workload, probe_gib, out
                 d.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
         return d
 
-    fetch = per_kernel(_csv_rows(fetch_csv), "FETCH_SIZE")
-    write = per_kernel(_csv_rows(write_csv), "WRITE_SIZE")
+    def calib_copy(rows, counter):
+        # the 512 MiB copy read_probe() makes: the first copy dispatched after
+        # the last read-probe dispatch (input generation makes other copies,
+        # some larger)
+        rows = sorted((r for r in rows if r["Counter_Name"] == counter), key=lambda r: int(r["Dispatch_Id"]))
+        last = max(i for i, r in enumerate(rows) if PROBE_KERNEL in r["Kernel_Name"])
+        return next(float(r["Counter_Value"]) * 1024.0 for r in rows[last + 1:]
+                    if r["Kernel_Name"].startswith(CALIB_COPY_KERNEL))
+
+    fetch_rows, write_rows = _csv_rows(fetch_csv), _csv_rows(write_csv)
+    fetch = per_kernel(fetch_rows, "FETCH_SIZE")
+    write = per_kernel(write_rows, "WRITE_SIZE")
     pick = lambda d, key: [v for k, vals in d.items() if k.startswith(key) or key in k for v in vals]
     probe_f = max(pick(fetch, PROBE_KERNEL))
-    copy_f = max(pick(fetch, CALIB_COPY_KERNEL))
-    copy_w = max(pick(write, CALIB_COPY_KERNEL))
+    copy_f = calib_copy(fetch_rows, "FETCH_SIZE")
+    copy_w = calib_copy(write_rows, "WRITE_SIZE")
     fetch_scale = probe_gib * 2**30 / probe_f
     write_scale = CALIB_COPY_BYTES / copy_w
     attn_f = statistics.mean(pick(fetch, kernel)) * fetch_scale
