@@ -1241,11 +1241,17 @@ struct PassLds {
 // with 8-bit ones) instead of accumulator registers that the
 // per-tile rescale would copy out and back, 68 moves per tile.  Vector
 // instantiations for 8-bit caches with 8 query heads (two blocks per step)
-// are held to two; the others keep their natural allocation.
+// are held to two.  The fp8 vector instantiations with one query head per
+// KV head are held to five (96 registers, no spills, against a natural
+// 100 and four): their workgroups are short chains of dependent round
+// trips, which more resident waves overlap (13B-shaped fp8 layer without
+// groups: 92.4 -> 87.6 us per layer, balanced A/B).  The others keep their
+// natural allocation.
 template <KV KT, KV VT, int D, int G>
 struct MinWaves {
   static constexpr bool eight_bit = kv_bytes<KT>::value == 1;
-  static constexpr int value = UseMfma<KT, VT, D, G>::value ? 3 : ((G == 8 && eight_bit) ? 2 : 1);
+  static constexpr bool fp8_mha = G == 1 && KT == KV::FP8 && VT == KV::FP8;
+  static constexpr int value = UseMfma<KT, VT, D, G>::value ? 3 : ((G == 8 && eight_bit) ? 2 : (fp8_mha ? 5 : 1));
 };
 
 template <KV KT, KV VT, KV QT, KV OT, int D, int G>
@@ -1270,15 +1276,16 @@ struct GroupKernelLds {
 // caches its per-sequence workgroups are short chains of dependent round
 // trips moving half the bytes of 16-bit ones, so more of them resident pay:
 // held to four waves per SIMD (no spills; 13B MHA layer with an fp8 cache
-// 58.7 -> 53.2 us per layer cold, balanced A/B).  With 16-bit caches four
-// waves measured slower (63.0 -> 64.0 us), so they keep their natural
-// allocation (three).
-template <KV T>
+// 58.7 -> 53.2 us per layer cold, balanced A/B), and with fp8 and one query
+// head per KV head to five (96 registers, no spills; 48.3 -> 46.3 us).
+// With 16-bit caches four waves measured slower (63.0 -> 64.0 us), so they
+// keep their natural allocation (three).
+template <KV T, int G>
 struct GroupMinWaves {
-  static constexpr int value = is_quantised<T>() ? 4 : 1;
+  static constexpr int value = is_quantised<T>() ? ((T == KV::FP8 && G == 1) ? 5 : 4) : 1;
 };
 template <KV T, KV QT, int D, int G>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GroupMinWaves<T>::value)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GroupMinWaves<T, G>::value)))
 decode_group_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[GroupKernelLds<T, QT, D, G>::value];
   const int id = blockIdx.x;
