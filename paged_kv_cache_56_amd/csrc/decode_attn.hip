@@ -445,9 +445,20 @@ struct SeqSpan {
 // that block is the wave's first).  No other workgroup reads the block.
 // Partition 0 writes when nothing is attended.  One wave: a K row and a V
 // row, 16 bytes per lane.
+//
+// The copy comes in two halves, so that a caller can overlap its round trip
+// with other loads: append_rows_load issues the load of the lane's 16 bytes
+// and append_rows_store writes them.  In between the caller must not read
+// the new token's block; the store is complete after the caller's next
+// wait for all its memory operations.
+struct PendingRow {
+  u32x4_t x;
+  u32x4_t* dst;   // null: the lane writes nothing
+};
 template <int D, int EB>
-__device__ __forceinline__ void append_new_rows(const DecodeArgs& a, int b, int h, int lane) {
-  const int64_t slot = a.new_slots[b];
+__device__ __forceinline__ PendingRow append_rows_load(const DecodeArgs& a, int b, int h, int lane, int64_t slot) {
+  PendingRow r;
+  r.dst = nullptr;
   constexpr int ROWC = D * EB / 16;   // 16-byte chunks of one row
   static_assert(2 * ROWC <= 64, "one wave copies a K row and a V row");
   if (slot >= 0 && slot < (int64_t)a.num_blocks * 16 && lane < 2 * ROWC) {
@@ -455,9 +466,17 @@ __device__ __forceinline__ void append_new_rows(const DecodeArgs& a, int b, int 
     const int ch = isv ? lane - ROWC : lane;
     const int64_t src = ((int64_t)b * a.num_kv_heads + h) * ROWC + ch;
     const int64_t dst = (((slot >> 4) * a.num_kv_heads + h) * 16 + (slot & 15)) * ROWC + ch;
-    reinterpret_cast<u32x4_t*>(isv ? a.v_cache_rw : a.k_cache_rw)[dst] =
-        reinterpret_cast<const u32x4_t*>(isv ? a.v_new : a.k_new)[src];
+    r.x = reinterpret_cast<const u32x4_t*>(isv ? a.v_new : a.k_new)[src];
+    r.dst = reinterpret_cast<u32x4_t*>(isv ? a.v_cache_rw : a.k_cache_rw) + dst;
   }
+  return r;
+}
+__device__ __forceinline__ void append_rows_store(const PendingRow& r) {
+  if (r.dst) *r.dst = r.x;
+}
+template <int D, int EB>
+__device__ __forceinline__ void append_new_rows(const DecodeArgs& a, int b, int h, int lane, int64_t slot) {
+  append_rows_store(append_rows_load<D, EB>(a, b, h, lane, slot));
 }
 
 // The step's append into a layout with an 8-bit cache: K (8-bit, or a
@@ -469,11 +488,10 @@ __device__ __forceinline__ void append_new_rows(const DecodeArgs& a, int b, int 
 // codes are the nearest (ties to even) of clamp(y / scale, +-QMAX).  One
 // wave: lanes 0..31 take K, 32..63 V, D / 32 consecutive elements each.
 template <KV KT, KV VT, KV QT, int D>
-__device__ __forceinline__ void append_new_rows_q8(const DecodeArgs& a, int b, int h, int lane) {
+__device__ __forceinline__ void append_new_rows_q8(const DecodeArgs& a, int b, int h, int lane, int64_t slot) {
   static_assert(is_quantised<VT>(), "an 8-bit V");
   constexpr int EPL = D / 32;
   static_assert(EPL == 2 || EPL == 4, "head_dim 64 or 128");
-  const int64_t slot = a.new_slots[b];
   if (!(slot >= 0 && slot < (int64_t)a.num_blocks * 16)) return;   // uniform over the wave
   const bool isv = lane >= 32;
   const int e0 = (lane & 31) * EPL;
@@ -531,11 +549,11 @@ __device__ __forceinline__ void append_new_rows_q8(const DecodeArgs& a, int b, i
 }
 
 // The step's append for any cache layout (see append_new_rows and
-// append_new_rows_q8), by one wave.
+// append_new_rows_q8), by one wave; slot = new_slots[b].
 template <KV KT, KV VT, KV QT, int D>
-__device__ __forceinline__ void append_step_rows(const DecodeArgs& a, int b, int h, int lane) {
-  if constexpr (is_quantised<VT>()) append_new_rows_q8<KT, VT, QT, D>(a, b, h, lane);
-  else append_new_rows<D, kv_bytes<KT>::value>(a, b, h, lane);
+__device__ __forceinline__ void append_step_rows(const DecodeArgs& a, int b, int h, int lane, int64_t slot) {
+  if constexpr (is_quantised<VT>()) append_new_rows_q8<KT, VT, QT, D>(a, b, h, lane, slot);
+  else append_new_rows<D, kv_bytes<KT>::value>(a, b, h, lane, slot);
 }
 
 // Partition p's result for query head h * G + ha of sequence b, channel d,
@@ -560,8 +578,9 @@ __device__ __forceinline__ void finish_row(const DecodeArgs& a, int b, int h, in
 // A partition with nothing of the cache: a zero row (empty partitions of a
 // split call are skipped by the merge), and the append if it falls here.
 template <KV KT, KV VT, KV QT, KV OT, int D, int G>
-__device__ __forceinline__ void finish_empty(const DecodeArgs& a, int b, int h, int p, int tid, bool append) {
-  if (append) append_step_rows<KT, VT, QT, D>(a, b, h, tid & 63);
+__device__ __forceinline__ void finish_empty(const DecodeArgs& a, int b, int h, int p, int tid, bool append,
+                                             int64_t slot) {
+  if (append) append_step_rows<KT, VT, QT, D>(a, b, h, tid & 63, slot);
   if (!a.split)
     for (int idx = tid; idx < G * D; idx += 256) finish_row<OT, D, G>(a, b, h, p, idx / D, idx % D, -INFINITY, 0.f, 0.f);
 }
@@ -648,6 +667,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int Hq = a.num_kv_heads * G;
 
+  // the new token's slot, when the step's append is carried: read next to
+  // the sequence's length, so that the append does not wait for it later
+  const int64_t new_slot = a.new_slots ? a.new_slots[b] : -1;
   // positions covered elsewhere (sink tiles, or a shared prefix read by the
   // group pass) are skipped here
   const int pre = a.sink_tiles ? 0 : prefix_blocks_of_seq(a, b);
@@ -662,9 +684,11 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
   const bool appends = a.new_slots != nullptr && p == (parts.n > 0 ? parts.n - 1 : 0);
   constexpr int BPS = C::BPS;
   const int append_wave = j1 > j0 ? ((j1 - 1 - j0) / BPS) % NW : 0;
-  auto append_rows = [&]() __attribute__((always_inline)) { append_step_rows<KT, VT, QT, D>(a, b, h, lane); };
+  auto append_rows = [&]() __attribute__((always_inline)) {
+    append_step_rows<KT, VT, QT, D>(a, b, h, lane, new_slot);
+  };
   if (j0 >= j1) {
-    finish_empty<KT, VT, QT, OT, D, G>(a, b, h, p, tid, appends && w == 0);
+    finish_empty<KT, VT, QT, OT, D, G>(a, b, h, p, tid, appends && w == 0, new_slot);
     return;
   }
 
@@ -1059,9 +1083,23 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
     TokWords<NWTV> va[BPS][TPL], vb[BPS][TPL];
     constexpr unsigned kWaitVm0 = 0x0F70;     // vmcnt(0), expcnt(7), lgkmcnt(15)
     static_assert(KR == 2, "one step in flight: K(t+1) and V(t+1) while t is computed");
+    // A plain copy of the new rows is loaded here and stored in step 0 once
+    // step 1's loads are issued, so that its round trip overlaps the first
+    // tiles' instead of delaying them.  Step 1's wait completes the store
+    // before the wave issues any later block's loads, the new token's block
+    // (its last step, n_my - 1 >= 2) among them.  Otherwise the rows are
+    // written before the first loads.
+    const bool defer = !is_quantised<VT>() && appends && w == append_wave && n_my >= 3;
+    PendingRow pend;
+    pend.dst = nullptr;
     if (appends && w == append_wave) {
-      append_rows();
-      if (n_my == 1) wait_vmcnt<0>();    // the new token's block is in this wave's first step
+      if constexpr (!is_quantised<VT>()) {
+        if (defer) pend = append_rows_load<D, kv_bytes<KT>::value>(a, b, h, lane, new_slot);
+      }
+      if (!defer) {
+        append_rows();
+        if (n_my == 1) wait_vmcnt<0>();    // the new token's block is in this wave's first step
+      }
     }
     // bcur: the blocks being computed; bnext: the next step's, entries read
     BlockRef bcur[BPS], bnext[BPS];
@@ -1107,6 +1145,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
           issue_tok(bnext[b2].phys, ((t + 1) & 1) * BPS + b2);
         }
       }
+      if (defer && t == 0) append_rows_store(pend);
       TokWords<NWT> kr[TPL];
       read_k((t & 1) * BPS, kr);            // waits for its reads (lgkmcnt(0))
       // scalar loads after that wait, which would otherwise cover them too

@@ -194,6 +194,7 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
   const bool hv = lq < G;                                 // the lane's column is a query head
   const int Hq = a.num_kv_heads * G;
 
+  const int64_t new_slot = a.new_slots ? a.new_slots[b] : -1;   // read next to the length
   const int pre = a.sink_tiles ? 0 : prefix_blocks_of_seq(a, b);
   const SeqSpan span(a.context_lens[b], a.max_blocks, a.window, a.sinks,
                      a.sink_tiles ? a.sinks : 16 * pre);
@@ -204,9 +205,11 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
   // token's block, and in it by the wave that reads that block
   const bool appends = a.new_slots != nullptr && p == (parts.n > 0 ? parts.n - 1 : 0);
   const int append_wave = j1 > j0 ? (j1 - 1 - j0) % NW : 0;
-  auto append_rows = [&]() __attribute__((always_inline)) { append_step_rows<KT, VT, QT, D>(a, b, h, lane); };
+  auto append_rows = [&]() __attribute__((always_inline)) {
+    append_step_rows<KT, VT, QT, D>(a, b, h, lane, new_slot);
+  };
   if (j0 >= j1) {
-    finish_empty<KT, VT, QT, OT, D, G>(a, b, h, p, tid, appends && w == 0);
+    finish_empty<KT, VT, QT, OT, D, G>(a, b, h, p, tid, appends && w == 0, new_slot);
     return;
   }
 
@@ -440,9 +443,20 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
     VRows<VW> va, vb;
     constexpr unsigned kWaitVm0 = 0x0F70;     // vmcnt(0), expcnt(7), lgkmcnt(15)
     static_assert(KR == 2, "one step in flight: K(t+1) and V(t+1) while t is computed");
+    // a plain copy of the new rows: loaded here, stored in step 0 after step
+    // 1's loads are issued, complete at step 1's wait, before the wave loads
+    // its last block, the new token's (n_my >= 3); as in the vector pass
+    const bool defer = !is_quantised<VT>() && appends && w == append_wave && n_my >= 3;
+    PendingRow pend;
+    pend.dst = nullptr;
     if (appends && w == append_wave) {
-      append_rows();
-      if (n_my == 1) wait_vmcnt<0>();
+      if constexpr (!is_quantised<VT>()) {
+        if (defer) pend = append_rows_load<D, EB>(a, b, h, lane, new_slot);
+      }
+      if (!defer) {
+        append_rows();
+        if (n_my == 1) wait_vmcnt<0>();
+      }
     }
     BlockRef bcur{-1, 1.f, 1.f}, bnext{-1, 1.f, 1.f};
     if (n_my > 0) {
@@ -467,6 +481,7 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
         issue_k(bnext.phys, (t + 1) & 1, nv);
         issue_tok(bnext.phys, (t + 1) & 1);
       }
+      if (defer && t == 0) append_rows_store(pend);
       u32x4_t kr[KREADS];
       read_k(t & 1, kr);
       if (more) {
