@@ -389,6 +389,7 @@ def _ragged(name, kv, q, out, D, G, lens, seed, hkv=2, append=False, v=None, out
 
 
 RAGGED = [1, 15, 16, 17, 31, 33, 100, 257, 0, 64, 511]
+APPEND_STEPS = [129, 144, 177, 192, 113, 128, 33, 48, 49, 65]
 SMALL = {
     "tiny_f32": WORKLOADS["tiny_f32"],
     "llama3_8b_bf16_small": scaled(WORKLOADS["llama3_8b_bf16"], num_seqs=4, len_range=(512, 2100)),
@@ -469,6 +470,14 @@ SMALL = {
                                              [1, 16, 17, 200, 33, 48, 49], 51, hkv=12, append=True),
     "ragged_int8_g2_d64_h10": _ragged("r35", "int8", "bf16", "bf16", 64, 2, [1, 15, 16, 17, 31, 33, 100, 0, 64, 130],
                                       52, hkv=10),
+    # the carried plain-copy append at the boundary where it moves behind the
+    # first loads: lengths whose last piece gives the wave reading the new
+    # token's block 1, 2 or exactly 3 steps (one partition), in the
+    # matrix-core pass, the vector pass and with 4-byte elements
+    "append_steps_f16_g8_d128": _ragged("r36", "f16", "f16", "f16", 128, 8, APPEND_STEPS, 53, append=True),
+    "append_steps_bf16_g1_d128": _ragged("r37", "bf16", "bf16", "bf16", 128, 1, APPEND_STEPS, 54, hkv=3,
+                                         append=True),
+    "append_steps_f32_g2_d64": _ragged("r38", "f32", "f32", "f32", 64, 2, APPEND_STEPS, 55, append=True),
 }
 
 
@@ -685,6 +694,11 @@ STEP_CASES = [
     ("mha13b_prefix_small", -1, 0, 0, None),
     ("llama3_8b_bf16_small", 3, 700, 4, None),
     ("llama3_8b_bf16_small", -1, 0, 0, None),
+    # the copying wave with 1, 2 or 3 steps (its copy moves behind the first
+    # loads at 3), a skipped token among the latter
+    ("append_steps_f16_g8_d128", 0, 0, 0, None),
+    ("append_steps_bf16_g1_d128", 0, 0, 0, 0),
+    ("append_steps_f32_g2_d64", 0, 0, 0, 2),
 ]
 
 
