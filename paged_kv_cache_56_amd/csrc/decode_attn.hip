@@ -487,31 +487,100 @@ __device__ __forceinline__ void append_new_rows(const DecodeArgs& a, int b, int 
 // a zero row) is written first, otherwise the block's given scale is read;
 // codes are the nearest (ties to even) of clamp(y / scale, +-QMAX).  One
 // wave: lanes 0..31 take K, 32..63 V, D / 32 consecutive elements each.
+// The quantising append comes in two halves as well (see append_rows_load):
+// append_q8_load issues the loads -- the lane's elements of the new row as
+// stored and the block's given scale -- and append_q8_store does the rest
+// (K's channel factors, when given, are read there).
+template <KV QT, int D>
+struct PendingQ8 {
+  static constexpr int EPL = D / 32;                            // elements per lane
+  static constexpr int RW = EPL * (QT == KV::F32 ? 4 : 2) / 4;  // their dwords: 1, 2 or 4
+  uint32_t raw[RW];
+  float given;        // the block's scale for the lane's half (one per block and head)
+  bool on;            // the slot is in the pool (uniform over the wave)
+};
 template <KV KT, KV VT, KV QT, int D>
-__device__ __forceinline__ void append_new_rows_q8(const DecodeArgs& a, int b, int h, int lane, int64_t slot) {
+__device__ __forceinline__ PendingQ8<QT, D> append_q8_load(const DecodeArgs& a, int b, int h, int lane,
+                                                           int64_t slot) {
   static_assert(is_quantised<VT>(), "an 8-bit V");
-  constexpr int EPL = D / 32;
+  using P = PendingQ8<QT, D>;
+  constexpr int EPL = P::EPL, RW = P::RW;
   static_assert(EPL == 2 || EPL == 4, "head_dim 64 or 128");
-  if (!(slot >= 0 && slot < (int64_t)a.num_blocks * 16)) return;   // uniform over the wave
+  P r;
+  r.on = slot >= 0 && slot < (int64_t)a.num_blocks * 16;
+  r.given = 1.0f;
+#pragma unroll
+  for (int k = 0; k < RW; ++k) r.raw[k] = 0u;
+  if (!r.on) return r;
+  const bool isv = lane >= 32;
+  const int e0 = (lane & 31) * EPL;
+  const int64_t bh = (slot >> 4) * a.num_kv_heads + h;             // (block, head), uniform
+  const int64_t src = ((int64_t)b * a.num_kv_heads + h) * D + e0;  // element of k_new / v_new
+  const char* from = (const char*)(isv ? a.v_new : a.k_new) + src * (RW * 4 / EPL);
+  if constexpr (RW == 1) {
+    r.raw[0] = *(const uint32_t*)from;
+  } else if constexpr (RW == 2) {
+    const u32x2_t x = *(const u32x2_t*)from;
+    r.raw[0] = x[0]; r.raw[1] = x[1];
+  } else {
+    const u32x4_t x = *(const u32x4_t*)from;
+    r.raw[0] = x[0]; r.raw[1] = x[1]; r.raw[2] = x[2]; r.raw[3] = x[3];
+  }
+  // each half's given scale by a load of its own (uniform addresses), then
+  // a choice of values: a choice of pointers per lane would put both in
+  // per-lane scratch memory
+  float gv = 1.0f, gk = 1.0f;
+  if (!a.v_tok) gv = a.v_scales[bh];
+  if constexpr (is_quantised<KT>()) {
+    if (!a.k_tok) gk = a.k_scales[bh];
+  }
+  r.given = isv ? gv : gk;
+  return r;
+}
+
+// Element e of the lane's loaded row, as fp32.
+template <KV QT, int D>
+__device__ __forceinline__ float pending_elem(const PendingQ8<QT, D>& r, int e) {
+  if constexpr (QT == KV::F32) return __builtin_bit_cast(float, r.raw[e]);
+  else {
+    const uint32_t hbits = (r.raw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+    if constexpr (QT == KV::F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)hbits);
+    else return __builtin_bit_cast(float, hbits << 16);
+  }
+}
+
+// The step's append into a layout with an 8-bit cache: K (8-bit, or a
+// 16-bit K, which is copied) and V (8-bit) of sequence b's new token, head
+// h, written at its slot exactly as pkv_kv_append_quant (8-bit) and
+// pkv_kv_append (16-bit) write them: y = x / channel factor (8-bit K, when
+// given), then with per-token scales the slot's scale max|y| / QMAX (1 for
+// a zero row) is written first, otherwise the block's given scale is used;
+// codes are the nearest (ties to even) of clamp(y / scale, +-QMAX).  One
+// wave: lanes 0..31 take K, 32..63 V, D / 32 consecutive elements each.
+template <KV KT, KV VT, KV QT, int D>
+__device__ __forceinline__ void append_q8_store(const DecodeArgs& a, int h, int lane, int64_t slot,
+                                                const PendingQ8<QT, D>& r) {
+  constexpr int EPL = PendingQ8<QT, D>::EPL, RW = PendingQ8<QT, D>::RW;
+  if (!r.on) return;                                                // uniform over the wave
   const bool isv = lane >= 32;
   const int e0 = (lane & 31) * EPL;
   const int64_t bh = (slot >> 4) * a.num_kv_heads + h;             // (block, head)
-  const int64_t src = ((int64_t)b * a.num_kv_heads + h) * D + e0;  // element of k_new / v_new
   const int64_t dst = (bh * 16 + (slot & 15)) * D + e0;            // element of the cache
   if constexpr (!is_quantised<KT>()) {
     static_assert(QT == KT, "a 16-bit K takes rows of its own type");
     if (!isv) {                                                     // K: a bit copy
-      const uint16_t* from = (const uint16_t*)a.k_new + src;
-      uint16_t* to = (uint16_t*)a.k_cache_rw + dst;
+      uint32_t* to = (uint32_t*)((uint16_t*)a.k_cache_rw + dst);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) to[e] = from[e];
+      for (int k = 0; k < RW; ++k) to[k] = r.raw[k];
     }
   }
   float y[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    y[e] = load_elem_f32<QT>(isv ? a.v_new : a.k_new, src + e);
-    if (is_quantised<KT>() && !isv && a.k_chan) y[e] = y[e] / a.k_chan[(int64_t)h * D + e0 + e];
+  for (int e = 0; e < EPL; ++e) y[e] = pending_elem<QT, D>(r, e);
+  if constexpr (is_quantised<KT>()) {
+    if (!isv && a.k_chan)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) y[e] = y[e] / a.k_chan[(int64_t)h * D + e0 + e];
   }
   // both flags read, then a bit picked: a select between the two fields'
   // addresses would put them in per-lane scratch memory
@@ -525,13 +594,11 @@ __device__ __forceinline__ void append_new_rows_q8(const DecodeArgs& a, int b, i
   auto write = [&](auto ct) __attribute__((always_inline)) {
     constexpr KV CT = decltype(ct)::value;
     constexpr float QM = qmax<CT>();
-    float* scales = const_cast<float*>(isv ? a.v_scales : a.k_scales);
-    float scale;
+    float scale = r.given;
     if (tok) {
       scale = amax > 0.f ? amax / QM : 1.0f;
+      float* scales = const_cast<float*>(isv ? a.v_scales : a.k_scales);
       if ((lane & 31) == 0) scales[bh * 16 + (slot & 15)] = scale;
-    } else {
-      scale = scales[bh];
     }
     float v[EPL];
 #pragma unroll
@@ -548,12 +615,29 @@ __device__ __forceinline__ void append_new_rows_q8(const DecodeArgs& a, int b, i
   else if constexpr (is_quantised<KT>()) write(std::integral_constant<KV, KT>{});
 }
 
+template <KV KT, KV VT, KV QT, int D>
+__device__ __forceinline__ void append_new_rows_q8(const DecodeArgs& a, int b, int h, int lane, int64_t slot) {
+  append_q8_store<KT, VT, QT, D>(a, h, lane, slot, append_q8_load<KT, VT, QT, D>(a, b, h, lane, slot));
+}
+
 // The step's append for any cache layout (see append_new_rows and
 // append_new_rows_q8), by one wave; slot = new_slots[b].
 template <KV KT, KV VT, KV QT, int D>
 __device__ __forceinline__ void append_step_rows(const DecodeArgs& a, int b, int h, int lane, int64_t slot) {
   if constexpr (is_quantised<VT>()) append_new_rows_q8<KT, VT, QT, D>(a, b, h, lane, slot);
   else append_new_rows<D, kv_bytes<KT>::value>(a, b, h, lane, slot);
+}
+// The same in two halves (append_rows_load / append_q8_load, then the
+// matching store).
+template <KV KT, KV VT, KV QT, int D>
+__device__ __forceinline__ auto append_step_load(const DecodeArgs& a, int b, int h, int lane, int64_t slot) {
+  if constexpr (is_quantised<VT>()) return append_q8_load<KT, VT, QT, D>(a, b, h, lane, slot);
+  else return append_rows_load<D, kv_bytes<KT>::value>(a, b, h, lane, slot);
+}
+template <KV KT, KV VT, KV QT, int D, class P>
+__device__ __forceinline__ void append_step_store(const DecodeArgs& a, int h, int lane, int64_t slot, const P& r) {
+  if constexpr (is_quantised<VT>()) append_q8_store<KT, VT, QT, D>(a, h, lane, slot, r);
+  else append_rows_store(r);
 }
 
 // Partition p's result for query head h * G + ha of sequence b, channel d,
@@ -1083,12 +1167,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int p, int h, i
     TokWords<NWTV> va[BPS][TPL], vb[BPS][TPL];
     constexpr unsigned kWaitVm0 = 0x0F70;     // vmcnt(0), expcnt(7), lgkmcnt(15)
     static_assert(KR == 2, "one step in flight: K(t+1) and V(t+1) while t is computed");
-    // A plain copy of the new rows is loaded here and stored in step 0 once
-    // step 1's loads are issued, so that its round trip overlaps the first
-    // tiles' instead of delaying them.  Step 1's wait completes the store
+    // A plain copy of the new rows is loaded here, so that its round trip
+    // overlaps the first tiles' instead of delaying them, and stored in step
+    // 0 once step 1's loads are issued: step 1's wait completes the store
     // before the wave issues any later block's loads, the new token's block
-    // (its last step, n_my - 1 >= 2) among them.  Otherwise the rows are
-    // written before the first loads.
+    // (its last step, n_my - 1 >= 2) among them.  (A later step would keep
+    // the rows' registers live through the loop, which costs the head_dim-64
+    // instantiations a wave per SIMD.)  With fewer than three steps the rows
+    // are written before the first loads.
     const bool defer = !is_quantised<VT>() && appends && w == append_wave && n_my >= 3;
     PendingRow pend;
     pend.dst = nullptr;
@@ -1284,13 +1370,16 @@ struct PassLds {
 // KV head are held to five (96 registers, no spills, against a natural
 // 100 and four): their workgroups are short chains of dependent round
 // trips, which more resident waves overlap (13B-shaped fp8 layer without
-// groups: 92.4 -> 87.6 us per layer, balanced A/B).  The others keep their
-// natural allocation.
+// groups: 92.4 -> 87.6 us per layer, balanced A/B).  Those with two are
+// held to four, which they fit without spills (a natural 129 registers
+// would allow three).  The others keep their natural allocation.
 template <KV KT, KV VT, int D, int G>
 struct MinWaves {
   static constexpr bool eight_bit = kv_bytes<KT>::value == 1;
-  static constexpr bool fp8_mha = G == 1 && KT == KV::FP8 && VT == KV::FP8;
-  static constexpr int value = UseMfma<KT, VT, D, G>::value ? 3 : ((G == 8 && eight_bit) ? 2 : (fp8_mha ? 5 : 1));
+  static constexpr bool fp8 = KT == KV::FP8 && VT == KV::FP8;
+  static constexpr int value =
+      UseMfma<KT, VT, D, G>::value ? 3
+                                   : ((G == 8 && eight_bit) ? 2 : ((G == 1 && fp8) ? 5 : ((G == 2 && fp8) ? 4 : 1)));
 };
 
 template <KV KT, KV VT, KV QT, KV OT, int D, int G>

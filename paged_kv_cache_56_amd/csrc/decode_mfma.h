@@ -443,17 +443,23 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
     VRows<VW> va, vb;
     constexpr unsigned kWaitVm0 = 0x0F70;     // vmcnt(0), expcnt(7), lgkmcnt(15)
     static_assert(KR == 2, "one step in flight: K(t+1) and V(t+1) while t is computed");
-    // a plain copy of the new rows: loaded here, stored in step 0 after step
-    // 1's loads are issued, complete at step 1's wait, before the wave loads
-    // its last block, the new token's (n_my >= 3); as in the vector pass
-    const bool defer = !is_quantised<VT>() && appends && w == append_wave && n_my >= 3;
-    PendingRow pend;
-    pend.dst = nullptr;
+    // the new rows (copied, or quantised for an fp8 cache): loaded here and
+    // stored once the next step's loads are issued -- a copy in step
+    // n_my - 3 (in step 0, as the vector pass does, the 70B-shaped step was
+    // 1.3 us slower per layer), quantised rows in step 0 (in step n_my - 3
+    // the 131072-token fp8 layer was 2.4 us slower) -- and complete at the
+    // following step's wait, before the wave loads its last block, the new
+    // token's.  The int8 and mixed-format instantiations would need more
+    // registers than their waves per SIMD allow, so they write before their
+    // first loads.
+    constexpr bool kDefer = !is_quantised<VT>() || (KT == KV::FP8 && VT == KV::FP8);
+    const bool defer = kDefer && appends && w == append_wave && n_my >= 3;
+    const int store_step = is_quantised<VT>() ? 0 : n_my - 3;
+    decltype(append_step_load<KT, VT, QT, D>(a, b, h, lane, new_slot)) pend{};
     if (appends && w == append_wave) {
-      if constexpr (!is_quantised<VT>()) {
-        if (defer) pend = append_rows_load<D, EB>(a, b, h, lane, new_slot);
-      }
-      if (!defer) {
+      if (defer) {
+        pend = append_step_load<KT, VT, QT, D>(a, b, h, lane, new_slot);
+      } else {
         append_rows();
         if (n_my == 1) wait_vmcnt<0>();
       }
@@ -481,7 +487,7 @@ __device__ __forceinline__ void decode_body_mfma(const DecodeArgs& a, int p, int
         issue_k(bnext.phys, (t + 1) & 1, nv);
         issue_tok(bnext.phys, (t + 1) & 1);
       }
-      if (defer && t == 0) append_rows_store(pend);
+      if (defer && t == store_step) append_step_store<KT, VT, QT, D>(a, h, lane, new_slot, pend);
       u32x4_t kr[KREADS];
       read_k(t & 1, kr);
       if (more) {
