@@ -478,6 +478,11 @@ SMALL = {
     "append_steps_bf16_g1_d128": _ragged("r37", "bf16", "bf16", "bf16", 128, 1, APPEND_STEPS, 54, hkv=3,
                                          append=True),
     "append_steps_f32_g2_d64": _ragged("r38", "f32", "f32", "f32", 64, 2, APPEND_STEPS, 55, append=True),
+    # the same boundary for quantised rows (fp8, matrix-core pass), with
+    # block scales and with per-token scales the new token sets
+    "append_steps_fp8_g4_d128": _ragged("r39", "fp8_e4m3", "bf16", "bf16", 128, 4, APPEND_STEPS, 56, append=True),
+    "append_steps_fp8_tok_g8_d128": _ragged("r40", "fp8_e4m3", "f16", "f16", 128, 8, APPEND_STEPS, 57,
+                                            append=True, ktok=True, vtok=True),
 }
 
 
@@ -829,6 +834,8 @@ QUANT_STEP_CASES = [
     ("ragged_fp8_tok_g4_d128_append", 0, 2),
     ("ragged_int8_g8_d64_chan_ktok_append", 0, None),
     ("ragged_fp8_g8_d64_append_f32out", 3, None),
+    ("append_steps_fp8_g4_d128", 0, None),
+    ("append_steps_fp8_tok_g8_d128", 0, 3),
 ]
 
 
