@@ -205,7 +205,7 @@ def read_probe(dev, gib: int = 4):
     buf = torch.empty(gib * 2**30, dtype=torch.uint8, device=dev)
     buf.fill_(1)
     best = 0.0
-    for wgs in (1024, 2048, 4096, 8192):
+    for wgs in (512, 1024, 2048, 4096):
         sink = torch.zeros(wgs, dtype=torch.int32, device=dev)
         pkv.hbm_read_probe(buf, sink)            # warm
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

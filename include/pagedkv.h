@@ -472,9 +472,10 @@ PKV_API int pkv_paged_decode_step_quant_prefix(const void* k_new, const void* v_
  * Bandwidth reference ("KV Cache from first principles" 4.1: decode time is
  * set by the bytes moved).  Reads the first `bytes` (rounded down to a
  * multiple of 16) of device buffer `buf` once with 16-byte loads, using
- * `sink_words` workgroups; each workgroup XORs what it read into
- * sink[workgroup] (device, caller-zeroed if the value matters).  The rate
- * of this call is what a read-only kernel achieves on the device.
+ * `sink_words` workgroups: workgroup k reads the 16-byte words
+ * [k * c, (k + 1) * c), c = ceil(words / sink_words), and XORs them into
+ * sink[k] (device, caller-zeroed if the value matters).  The rate of this
+ * call is what a read-only kernel achieves on the device.
  * Errors: NULL buf/sink with bytes >= 16, sink_words < 1 -> status.
  */
 PKV_API int pkv_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t sink_words,

@@ -11,21 +11,28 @@ namespace pkv {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Workgroup k reads the k-th of gridDim.x contiguous chunks, its 256
+// threads 16 bytes apart, eight loads in flight per thread, non-temporal.
+// Long contiguous chunks per workgroup stream faster on this chip than a
+// grid-wide stride over the buffer (7.1 against 6.8 TB/s over 4 GiB at the
+// best grid size of each form).
 __global__ void __launch_bounds__(256) hbm_read_kernel(const u32x4* __restrict__ src, int64_t n16,
                                                        uint32_t* __restrict__ sink) {
   constexpr int UNROLL = 8;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * per;
+  const int64_t hi = lo + per < n16 ? lo + per : n16;
+  int64_t j = lo + threadIdx.x;
   uint32_t acc = 0;
-  for (; i + (UNROLL - 1) * stride < n16; i += UNROLL * stride) {
+  for (; j + (UNROLL - 1) * 256 < hi; j += UNROLL * 256) {
     u32x4 x[UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) x[u] = __builtin_nontemporal_load(src + i + u * stride);
+    for (int u = 0; u < UNROLL; ++u) x[u] = __builtin_nontemporal_load(src + j + u * 256);
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) acc ^= x[u].x ^ x[u].y ^ x[u].z ^ x[u].w;
   }
-  for (; i < n16; i += stride) {
-    const u32x4 x = src[i];
+  for (; j < hi; j += 256) {
+    const u32x4 x = src[j];
     acc ^= x.x ^ x.y ^ x.z ^ x.w;
   }
   // fold the workgroup: any lane's value reaches the sink through the wave xor

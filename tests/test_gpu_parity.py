@@ -1065,7 +1065,7 @@ def test_hbm_read_probe_reads_every_word():
     torch.cuda.synchronize()
     words = x.cpu().numpy().view(np.uint32).reshape(n16, 4)
     f = words[:, 0] ^ words[:, 1] ^ words[:, 2] ^ words[:, 3]
-    wg = (np.arange(n16) % (W * 256)) // 256
+    wg = np.arange(n16) // (-(-n16 // W))         # contiguous chunks of ceil(n16 / W) words
     exp = [int(np.bitwise_xor.reduce(f[wg == w])) for w in range(W)]
     assert sink.cpu().numpy().view(np.uint32).tolist() == exp
 
